@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the 3D-RoPE sparse + low-rank attention layer forward on one
+MI355X: ms/layer and effective TFLOP/s, with the dominant kernel's roofline,
+per-stage times, the in-library dense flash kernel and the CPU oracle.
+
+    python bench.py [--steps K] [--warmup W] [--workload wan13b|wan14b|hunyuan13b]
+
+One step = one slr_attention_fwd over the whole layer (rotate + pool, block
+top-k, low-rank summary, block-sparse flash + low-rank readout + gated
+combine). Inputs are seeded synthetic layers already resident in HBM.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def _hip():
+    h = ctypes.CDLL("libamdhip64.so")
+    h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return h
+
+
+def _event(h):
+    e = ctypes.c_void_p()
+    assert h.hipEventCreate(ctypes.byref(e)) == 0
+    return e.value
+
+
+def _elapsed(h, a, b) -> float:
+    ms = ctypes.c_float()
+    assert h.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+    return ms.value
+
+
+def make_device_inputs(cfg, torch):
+    from sparse_rank_attention_rope3d_amd import synth
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    shp = (cfg.B, cfg.H, cfg.L, cfg.D)
+    q, k, v = (torch.empty(shp, dtype=tdt, device="cuda") for _ in range(3))
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            for dst, arr in zip((q, k, v), synth.qkv_slice(cfg, b, h)):
+                if cfg.dtype == "bf16":
+                    bits = synth.f32_to_bf16_bits(arr)
+                    dst[b, h] = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+                else:
+                    dst[b, h] = torch.from_numpy(arr).cuda()
+    params = {kk: torch.from_numpy(vv).cuda() for kk, vv in synth.lowrank_params(cfg).items()}
+    return q, k, v, params
+
+
+def cpu_baseline(cfg, blocks: int):
+    """The CPU oracle (one thread, fp64) on one (b, h) slice: the whole
+    selection and summary plus `blocks` sampled query blocks of the sparse
+    branch and readout, extrapolated linearly to the full layer."""
+    import oracle
+    from sparse_rank_attention_rope3d_amd import synth
+    q, k, v = synth.qkv_slice(cfg, 0, 0)
+    p = synth.lowrank_params(cfg)
+    E = (p["et"], p["eh"], p["ew"]) if cfg.lr_mode == "abspe" else None
+    rng = np.random.default_rng([cfg.seed, synth.TID_SAMPLE, 0, 0])
+    qblocks = np.sort(rng.choice(cfg.nblk, size=min(blocks, cfg.nblk), replace=False)).astype(np.int32)
+    grid = (cfg.T, cfg.Hg, cfg.Wg)
+    t0 = time.perf_counter()
+    qr = oracle.rope3d(q, grid, cfg.base, cfg.pairs)
+    kr = oracle.rope3d(k, grid, cfg.base, cfg.pairs)
+    s = oracle.block_scores(oracle.block_mean(qr, cfg.block), oracle.block_mean(kr, cfg.block))
+    idx, _, _ = oracle.topk_blocks(s, cfg.keep)
+    if cfg.lr_mode == "rola":
+        u, w = oracle.lowrank_features(k, p["wk"][0], grid), oracle.lowrank_features(q, p["wq"][0], grid)
+        fk = oracle.lowrank_rotate(u, grid, cfg.base, cfg.pairs, cfg.lr_pairs)
+        fq = oracle.lowrank_rotate(w, grid, cfg.base, cfg.pairs, cfg.lr_pairs)
+    else:
+        u, w = oracle.lowrank_features(k, p["wk"][0], grid, E), oracle.lowrank_features(q, p["wq"][0], grid, E)
+        fk, fq = u, w
+    S, z = oracle.lowrank_summary(fk, u, v)
+    t1 = time.perf_counter()
+    rows = (qblocks[:, None].astype(np.int64) * cfg.block + np.arange(cfg.block)[None, :]).reshape(-1)
+    rows = rows[rows < cfg.L]
+    oracle.block_sparse_attention(qr, kr, v, cfg.block, idx, qblocks)
+    oracle.lowrank_readout(fq, w, S, z, cfg.eps, rows)
+    t2 = time.perf_counter()
+    per_slice = (t1 - t0) + (t2 - t1) * cfg.nblk / len(qblocks)
+    layer_s = per_slice * cfg.B * cfg.H
+    return layer_s, {"measured_s": round(t2 - t0, 2), "sampled_blocks": int(len(qblocks))}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan13b", choices=["wan13b", "wan14b", "hunyuan13b"])
+    ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--cpu-blocks", type=int, default=160, help="query blocks the CPU oracle samples")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus} GPUs, world size {world}): "
+              "the layer shards over (batch, head) with no exchange, so there is no multi-GPU path to time.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from sparse_rank_attention_rope3d_amd import binding as B
+    from sparse_rank_attention_rope3d_amd import synth
+
+    cfg = synth.by_name(args.workload)
+    print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    q, k, v, params = make_device_inputs(cfg, torch)
+    shape, rope, sparse = B.shape_of(cfg), B.rope_of(cfg), B.sparse_of(cfg)
+    lowrank = B.lowrank_of(cfg, params)
+    ws = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lowrank), "cuda")
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+
+    hip = _hip()
+    events = [[_event(hip) for _ in range(5)] for _ in range(args.steps)]
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        B.slr_attention_fwd(q, k, v, shape, rope, sparse, lowrank, out=out, ws=ws)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        B.slr_attention_fwd_staged(q, k, v, shape, rope, sparse, lowrank, out, ws, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    stage_names = ["rope_pool", "select", "lowrank_summary", "sparse_flash"]
+    stages = {n: [] for n in stage_names}
+    for ev in events:
+        for j, n in enumerate(stage_names):
+            stages[n].append(_elapsed(hip, ev[j], ev[j + 1]))
+    stage_ms = {n: float(np.mean(vs)) for n, vs in stages.items()}
+
+    F = cfg.flops()
+    f_total = F["sparse"] + F["lowrank"] + F["select"]
+    tflops = f_total / (ms_step * 1e-3) / 1e12
+    flash_ms = stage_ms["sparse_flash"]
+    flash_tf = F["sparse"] / (flash_ms * 1e-3) / 1e12
+    es = 2 if cfg.dtype == "bf16" else 4
+    BHLD = cfg.B * cfg.H * cfg.L * cfg.D
+    rows_pad = cfg.B * cfg.H * cfg.nblk * cfg.block * cfg.D
+    rope_bytes = 2 * BHLD * es + 2 * rows_pad * es + 2 * cfg.B * cfg.H * cfg.nblk * cfg.D * 4
+    summ_bytes = 2 * BHLD * es
+    hbm = {
+        "rope_pool": {"GB/s": rope_bytes / (stage_ms["rope_pool"] * 1e-3) / 1e9},
+        "lowrank_summary": {"GB/s": summ_bytes / (stage_ms["lowrank_summary"] * 1e-3) / 1e9},
+    }
+    for d in hbm.values():
+        d["frac"] = d["GB/s"] / PEAK_HBM_GBS
+        d["GB/s"] = round(d["GB/s"], 1)
+        d["frac"] = round(d["frac"], 4)
+    sel_tf = F["select"] / (stage_ms["select"] * 1e-3) / 1e12
+
+    # in-library dense flash attention (RoPE inside) at the same shape
+    dense = None
+    if args.dense_reps > 0:
+        print("[bench] dense flash baseline", file=sys.stderr, flush=True)
+        wsd = B.workspace(B.slr_workspace_bytes(B.SLR_OP_DENSE, shape, rope), "cuda")
+        B.slr_dense_attention_fwd(q, k, v, shape, rope, out=out, ws=wsd)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.dense_reps):
+            B.slr_dense_attention_fwd(q, k, v, shape, rope, out=out, ws=wsd)
+        e1.record()
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / args.dense_reps
+        dtf = F["dense"] / (dms * 1e-3) / 1e12
+        dense = {"ms": round(dms, 3), "TFLOP/s": round(dtf, 1), "frac_bf16_peak": round(dtf / PEAK_BF16_TFLOPS, 4),
+                 "speedup_of_slr_layer": round(dms / ms_step, 2)}
+        del wsd
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        layer_s, info = cpu_baseline(cfg, args.cpu_blocks)
+        cpu = {"value": f_total / layer_s / 1e12, "unit": "TFLOP/s (effective)", "cores": 1, "kind": "oracle",
+               "ms_per_layer": round(layer_s * 1e3, 1),
+               "sample": f"one (b,h) slice of {cfg.B * cfg.H}: full selection and summary, "
+                         f"{info['sampled_blocks']} of {cfg.nblk} query blocks of the sparse branch and readout, "
+                         f"fp64 single thread, {info['measured_s']} s measured, extrapolated linearly to the layer"}
+
+    line = {
+        "metric": "SLR attn fwd ms/layer + effective TFLOP/s at L=32760/75600/118800, 1 GPU",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s (effective)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded clustered Q/K, Gaussian V; random-init projections)",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "D": cfg.D, "L": cfg.L,
+                   "grid": [cfg.T, cfg.Hg, cfg.Wg], "block": cfg.block, "keep": cfg.keep, "nblk": cfg.nblk,
+                   "rank": cfg.rank, "lowrank": cfg.lr_mode, "parallelism": "single GPU"},
+        "roofline": {"kernel": "k_flash_bf16 (block-sparse flash + low-rank readout + combine)",
+                     "bound": "mfma", "achieved": round(flash_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flash_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": F["sparse"], "avg_launch_ms": round(flash_ms, 4)},
+        "stages_ms": {n: round(vv, 4) for n, vv in stage_ms.items()},
+        "hbm_stages": hbm,
+        "select": {"TFLOP/s": round(sel_tf, 2), "frac_fp32_peak": round(sel_tf / PEAK_FP32_TFLOPS, 4)},
+        "dense_flash": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+    for ev in events:
+        for e in ev:
+            hip.hipEventDestroy(ctypes.c_void_p(e))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

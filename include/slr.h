@@ -1,0 +1,181 @@
+/*
+ * slr.h -- C ABI of the MI355X (gfx950) 3D-RoPE sparse + low-rank hybrid
+ * attention forward library (libslr.so).
+ *
+ * The layer (RoLA, arXiv 2609.06712v3, App. A Algorithm 1 and Fig. 2;
+ * RoPeSLR, arXiv 2605.20659, abstract) combines
+ *   - a block-sparse softmax branch: 3D RoPE of q and k, block mean-pool,
+ *     per-query-block top-k key blocks, exact softmax over the kept blocks;
+ *   - a head-wise rank-r linear-attention branch: phi(x W) with phi = elu+1,
+ *     and either the backbone's rotary schedule truncated to r dims applied
+ *     after phi (RoLA §4.2-4.3) or learnable per-axis absolute embeddings
+ *     added before phi (RoPeSLR abstract), read out through one reusable
+ *     per-head summary S = sum rho(phi(k)) v^T, z = sum phi(k);
+ *   - an additive per-head gated combine  O = O_sparse + g_h * O_lowrank.
+ *
+ * Conventions shared by every entry point
+ *   Tensors q, k, v, out are [B, H, L, D] contiguous, L = T*Hg*Wg tokens
+ *   flattened t-major, then h, then w. Element type is fp32 (SLR_F32) or
+ *   bf16 stored as raw 16-bit patterns (SLR_BF16). Every pointer argument
+ *   is a DEVICE pointer (including weights, gate and tables), 16-byte
+ *   aligned, owned by the caller; the library never allocates, frees or
+ *   retains memory and keeps no state between calls. Scratch comes from the
+ *   caller's workspace (size from slr_workspace_bytes, 256-byte aligned).
+ *   All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *   stream) with no host synchronisation; SLR_OK means "enqueued". Calls
+ *   that share a workspace must be ordered on one stream.
+ *   Every argument is checked on the host before anything is launched; a
+ *   failed check returns a negative status and touches no memory. A HIP
+ *   launch failure returns SLR_EHIP. Nothing throws across the ABI.
+ *
+ * Readings of points the pages leave open (fixed here, documented with the
+ * design notes): rotary pairs are adjacent dims (2i, 2i+1) in contiguous
+ * t | h | w chunks; pair j of an axis with n pairs turns by
+ * p * base^(-2j/(2n)) at integer coordinate p; block scores are
+ * mean(rotated q) . mean(rotated k) / sqrt(D) over valid tokens; ties go to
+ * the lower block index; kept indices are stored ascending; the softmax
+ * scale is 1/sqrt(D); the normaliser is phi(q W_q) . z + eps with the
+ * un-rotated features.
+ */
+#ifndef SLR_H
+#define SLR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define SLR_OK 0
+#define SLR_EINVAL (-1)        /* bad shape, config, pointer or alignment */
+#define SLR_EUNSUPPORTED (-2)  /* valid but not built (e.g. D not 64/128) */
+#define SLR_EWORKSPACE (-3)    /* workspace missing or too small          */
+#define SLR_EHIP (-4)          /* a HIP call or kernel launch failed      */
+
+/* element types */
+#define SLR_F32 0
+#define SLR_BF16 1
+
+/* low-rank branch variants */
+#define SLR_LR_ROPE_OUTSIDE 0  /* RoLA: truncated rotary schedule after phi      */
+#define SLR_LR_ABS_PE 1        /* RoPeSLR: E_t[t]+E_h[h]+E_w[w] added before phi */
+
+/* operations, for slr_workspace_bytes */
+#define SLR_OP_ROPE3D 0
+#define SLR_OP_SELECT 1
+#define SLR_OP_LOWRANK_SUMMARY 2
+#define SLR_OP_ATTENTION 3
+#define SLR_OP_DENSE 4
+
+typedef struct {
+    int32_t B, H, D;       /* batch, heads, head dim (64 or 128)      */
+    int32_t T, Hg, Wg;     /* token grid; L = T*Hg*Wg                 */
+    int32_t dtype;         /* SLR_F32 or SLR_BF16                     */
+} slr_shape;
+
+typedef struct {
+    double base;                         /* rotary base, > 1           */
+    int32_t pairs_t, pairs_h, pairs_w;   /* sum = D/2, each >= 0        */
+} slr_rope_cfg;
+
+typedef struct {
+    int32_t block;   /* tokens per block: 32 or 64; nblk = ceil(L/block) */
+    int32_t keep;    /* kept key blocks per query block, 1..nblk         */
+} slr_sparse_cfg;
+
+typedef struct {
+    int32_t rank;                /* r: 8, 16, 32 or 64                              */
+    int32_t mode;                /* SLR_LR_ROPE_OUTSIDE or SLR_LR_ABS_PE            */
+    int32_t lr_pairs_t, lr_pairs_h, lr_pairs_w; /* ROPE_OUTSIDE: sum = r/2, each
+                                    <= the backbone pairs of its axis; ignored for ABS_PE */
+    float eps;                   /* normaliser epsilon (> 0), e.g. 1e-6             */
+    const float *Wq, *Wk;        /* [H, D, r] fp32; bf16 layers use them rounded to bf16 */
+    const float *gate;           /* [H] fp32, the per-head gate g_h                 */
+    const float *Et, *Eh, *Ew;   /* ABS_PE only: [T, r], [Hg, r], [Wg, r] fp32; else NULL */
+} slr_lowrank_cfg;
+
+/*
+ * Workspace size in bytes for operation `op` (SLR_OP_*) at this shape.
+ * `sparse` may be NULL for SLR_OP_ROPE3D / SLR_OP_LOWRANK_SUMMARY /
+ * SLR_OP_DENSE; `lowrank` may be NULL unless op is SLR_OP_ATTENTION or
+ * SLR_OP_LOWRANK_SUMMARY. Pure host arithmetic: no HIP call.
+ */
+int slr_workspace_bytes(int op, const slr_shape *shape, const slr_rope_cfg *rope,
+                        const slr_sparse_cfg *sparse, const slr_lowrank_cfg *lowrank,
+                        size_t *bytes);
+
+/*
+ * 3D RoPE (RoLA §3 "3D RoPE", eq. 1): x_rot = R(t,h,w) x for every token.
+ * x, x_rot: [B,H,L,D] of shape->dtype (x_rot may not alias x). Rotation in
+ * fp32 with fp32 cos/sin tables built from fp64 values.
+ */
+int slr_rope3d(const slr_shape *shape, const slr_rope_cfg *rope, const void *x, void *x_rot,
+               void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Block selection of the sparse branch (RoLA Fig. 2 "sparse top-k spikes",
+ * §4.1): rotate q and k, mean-pool each block over its valid tokens (from
+ * the fp32 rotated values), score s_ij = qbar_i . kbar_j / sqrt(D) in fp32
+ * and keep the `keep` largest per query block (ties: lower index).
+ * idx: int32 [B,H,nblk,keep], ascending per row.
+ * q_rot, k_rot: optional [B,H,L,D] outputs of the rotated q, k (NULL to skip).
+ */
+int slr_select_blocks(const slr_shape *shape, const slr_rope_cfg *rope, const slr_sparse_cfg *sparse,
+                      const void *q, const void *k, int32_t *idx, void *q_rot, void *k_rot,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The low-rank branch's reusable per-head summary (RoLA §4.1, App. B.1):
+ *   S = sum_l f_l v_l^T  [B,H,r,D] fp32,   z = sum_l u_l  [B,H,r] fp32,
+ * u_l = phi(k_l W_k [+ E]) from the raw (un-rotated) k, f_l = rho_l(u_l)
+ * (ROPE_OUTSIDE) or u_l (ABS_PE); sums over the L valid tokens, reduced in
+ * a fixed order (bitwise reproducible).
+ */
+int slr_lowrank_summary(const slr_shape *shape, const slr_rope_cfg *rope, const slr_lowrank_cfg *lowrank,
+                        const void *k, const void *v, float *S, float *z,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The whole hybrid layer forward (RoLA App. A, Algorithm 1):
+ *   out = O_sparse + g_h * (rho(w)^T S) / (w . z + eps),  w = phi(q W_q [+ E]).
+ * out: [B,H,L,D] of shape->dtype. Optional outputs (NULL to skip):
+ *   idx_out [B,H,nblk,keep] int32 (the selection used),
+ *   o_sparse_out, o_lowrank_out [B,H,L,D] of shape->dtype (the two branches
+ *   before the combine; for tests and diagnostics).
+ */
+int slr_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, const slr_sparse_cfg *sparse,
+                      const slr_lowrank_cfg *lowrank, const void *q, const void *k, const void *v,
+                      void *out, int32_t *idx_out, void *o_sparse_out, void *o_lowrank_out,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * slr_attention_fwd, plus timing marks: events[0..4] are hipEvent_t handles
+ * created by the caller; they are recorded on `stream` before the first
+ * launch, after the rotate + pool step, after the block selection, after the
+ * low-rank summary (projection prep, split-L partials, reduce) and after the
+ * fused sparse flash + readout + combine kernel. Same results, same errors.
+ */
+int slr_attention_fwd_staged(const slr_shape *shape, const slr_rope_cfg *rope, const slr_sparse_cfg *sparse,
+                             const slr_lowrank_cfg *lowrank, const void *q, const void *k, const void *v,
+                             void *out, int32_t *idx_out, void *o_sparse_out, void *o_lowrank_out,
+                             void *ws, size_t ws_bytes, void *const events[5], void *stream);
+
+/*
+ * Dense softmax attention with 3D RoPE applied inside (RoLA §3 "Full
+ * attention"; the baseline the sparse branch is measured against):
+ *   out = softmax(R q (R k)^T / sqrt(D)) v  over all L keys.
+ */
+int slr_dense_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, const void *q,
+                            const void *k, const void *v, void *out,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *slr_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLR_H */

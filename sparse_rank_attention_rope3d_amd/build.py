@@ -1,0 +1,54 @@
+"""Build libslr.so (HIP, gfx950 only) in-tree with hipcc.
+
+    python -m sparse_rank_attention_rope3d_amd.build
+
+Each source compiles to an object under csrc/_build/, then they link into
+sparse_rank_attention_rope3d_amd/libslr.so. Packed fp32 VALU instructions are
+disabled for the device code.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+OUT = os.path.join(PKG, "libslr.so")
+SOURCES = ["k_rope.hip", "k_select.hip", "k_lowrank.hip", "k_flash.hip", "slr_api.cpp"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _compile(src: str, obj: str, extra) -> None:
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    # the host pass does not know the packed-fp32 feature; nothing else is expected
+    noise = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+    if noise:
+        sys.stderr.write("\n".join(noise) + "\n")
+
+
+def build(extra=(), jobs: int = 8) -> str:
+    bdir = os.path.join(CSRC, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
+        list(ex.map(lambda so: _compile(so[0], so[1], list(extra)), zip(SOURCES, objs)))
+    tmp = OUT + ".tmp%d" % os.getpid()
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(sys.argv[1:]))

@@ -1,0 +1,469 @@
+// Block-sparse (and dense) flash attention with the low-rank readout and the
+// gated combine fused into the epilogue.
+//
+// RoLA (arXiv 2609.06712v3) §4.1: exact softmax attention of each query
+// block over the tokens of its kept key blocks; App. A Algorithm 1: the
+// layer output adds the gated low-rank readout rho(w)^T S / (w . z + eps),
+// w = phi(q W_q) from the raw q (§4.3); App. F: the sparse branch dominates
+// the cost. Dense attention (§3 "Full attention") is the same loop over
+// every key block.
+//
+// bf16 layers, per workgroup = one query block of BS rows, BS/32 waves of
+// 32 query rows each. Scores are computed transposed, S^T = K Q^T, with the
+// 32x32x16 bf16 MFMA: each lane then owns one query row (l % 32) and 16 of
+// its keys per 32-key sub-block, so the online softmax (fp32, exp2 domain)
+// needs one cross-lane step (lane ^ 32) per tile. O^T = V^T P^T is the
+// second MFMA; the probabilities go straight from the score accumulator
+// into the B operand because V^T is staged in LDS with keys in the same
+// slot16 order. K and V^T tiles live in LDS (padded rows: conflict-free
+// 16-byte reads); the next kept tile is fetched into registers while the
+// current one is consumed.
+#include "slr_common.h"
+#include "slr_launch.h"
+
+namespace slr {
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float2 lr_cossin_q(const float2* __restrict__ tab, const LrGeom& g, int pr,
+                                              const int* crd) {
+    int a, j;
+    if (pr < g.lp[0]) { a = 0; j = pr; }
+    else if (pr < g.lp[0] + g.lp[1]) { a = 1; j = pr - g.lp[0]; }
+    else { a = 2; j = pr - g.lp[0] - g.lp[1]; }
+    return tab[g.rope.tab_off[a] + crd[a] * g.rope.np[a] + j];
+}
+
+// Work-item order that keeps each XCD on a contiguous range of
+// (slice, query block): hardware hands workgroup p to XCD p % 8.
+__device__ __forceinline__ long xcd_remap(long p, long n) {
+    const long per = n / 8, rem = n % 8, x = p % 8, loc = p / 8;
+    return x * per + (x < rem ? x : rem) + loc;
+}
+
+template <int D, int BS, int RP, int LR, bool DENSE>
+__global__ __launch_bounds__(BS * 2) void k_flash_bf16(FlashArgs a) {
+    constexpr int NT = BS * 2;          // threads (BS/32 waves)
+    constexpr int KLD = D + 8;          // K tile row stride (elements)
+    constexpr int VLD = BS + 8;         // V^T tile row stride (elements)
+    constexpr int NKB = BS / 32;        // 32-key sub-blocks per tile
+    constexpr int NS = D / 16;          // k-steps over d
+    constexpr int NDB = D / 32;         // 32-dim blocks of the output
+    constexpr int KCH = D / 8;          // 16-byte chunks per row
+    constexpr int KRPP = NT / KCH;      // K rows loaded per pass
+    constexpr int KPASS = BS / KRPP;
+    constexpr int VBLK = (BS / 8) * (D / 8);  // 8x8 V blocks per tile
+    static_assert(VBLK <= NT, "one 8x8 V block per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[BS * KLD];
+    __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VLD];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const long wid = xcd_remap(blockIdx.x, a.nwg);
+    const long bh = wid / a.nblk;
+    const int qb = (int)(wid % a.nblk);
+    const int head = (int)(bh % a.H);
+    const long rows = (long)a.nblk * BS;
+    const long L = a.L;
+
+    const uint16_t* qr = (const uint16_t*)a.qr + (bh * rows + (long)qb * BS + 32 * wave) * D;
+    const uint16_t* kr = (const uint16_t*)a.kr + bh * rows * D;
+    const uint16_t* vg = (const uint16_t*)a.v + bh * L * D;
+    const int32_t* ix = DENSE ? nullptr : a.idx + (bh * a.nblk + qb) * (long)a.keep;
+    const int ntile = DENSE ? a.nblk : a.keep;
+
+    // B operand of S^T = K Q^T: q row l32, dims 16s + 8hf + e
+    u32x4_t qop[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qop[s] = ldg16(qr + l32 * D + 16 * s + 8 * hf);
+
+    // tile loader assignment
+    const int kc = tid % KCH, kr0 = tid / KCH;
+    const int vc = tid % (D / 8), vgp = tid / (D / 8);
+    const int vG = vgp >> 1, vh = vgp & 1;
+    const bool vload = tid < VBLK;
+    u32x4_t kreg[KPASS], vreg[8];
+
+    auto fetch = [&](int j) {
+        const uint16_t* kt = kr + (long)j * BS * D;
+#pragma unroll
+        for (int i = 0; i < KPASS; ++i) kreg[i] = ldg16(kt + (long)(kr0 + KRPP * i) * D + 8 * kc);
+        if (vload) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const long row = (long)j * BS + 16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2);
+                vreg[e] = row < L ? ldg16(vg + row * D + 8 * vc) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int i = 0; i < KPASS; ++i)
+            *reinterpret_cast<u32x4_t*>(k_lds + (kr0 + KRPP * i) * KLD + 8 * kc) = kreg[i];
+        if (vload) {
+#pragma unroll
+            for (int f = 0; f < 8; ++f) {
+                u32x4_t o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t a0 = vreg[2 * i][f >> 1], a1 = vreg[2 * i + 1][f >> 1];
+                    o[i] = (f & 1) ? __builtin_amdgcn_perm(a1, a0, 0x07060302u)
+                                   : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+                }
+                *reinterpret_cast<u32x4_t*>(vt_lds + (8 * vc + f) * VLD + 16 * vG + 8 * vh) = o;
+            }
+        }
+    };
+
+    f32x16_t oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    const float sl2 = a.scale * kLog2e;
+    const bool ragged = (L % BS) != 0;
+
+    int j = DENSE ? 0 : ix[0];
+    fetch(j);
+    stash();
+    __syncthreads();
+
+    for (int n = 0; n < ntile; ++n) {
+        const int jn = (n + 1 < ntile) ? (DENSE ? n + 1 : ix[n + 1]) : -1;
+        if (jn >= 0) fetch(jn);
+
+        // ---- S^T = K Q^T over this tile
+        f32x16_t sacc[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(k_lds + (32 * kb + l32) * KLD + 16 * s + 8 * hf);
+                sacc[kb] = mfma32(ka, qop[s], sacc[kb]);
+            }
+        }
+        // ---- online softmax (log2 domain); lane holds query l32
+        const bool mask = ragged && j == a.nblk - 1;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float x = sacc[kb][i] * sl2;
+                if (mask) {
+                    const long key = (long)j * BS + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
+                    if (key >= L) x = -INFINITY;
+                }
+                sacc[kb][i] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = fmaxf(mx, wave_xor32(mx));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        u32x4_t pop[NKB][2];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p0 = fast_exp2(sacc[kb][8 * h2 + 2 * i] - m_new);
+                    const float p1 = fast_exp2(sacc[kb][8 * h2 + 2 * i + 1] - m_new);
+                    l_run += p0 + p1;
+                    pop[kb][h2][i] = pack_bf2(p0, p1);
+                }
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const u32x4_t va =
+                        *reinterpret_cast<const u32x4_t*>(vt_lds + (32 * db + l32) * VLD + 32 * kb + 16 * h2 + 8 * hf);
+                    oacc[db] = mfma32(va, pop[kb][h2], oacc[db]);
+                }
+        __syncthreads();
+        if (jn >= 0) {
+            stash();
+            j = jn;
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane owns query row qrow, dims 32db + 8(i/4) + 4hf + i%4
+    const long qrow = (long)qb * BS + 32 * wave + l32;
+    const bool qval = qrow < L;
+    const float inv = 1.f / (l_run + wave_xor32(l_run));
+    float gsc = 0.f, rden = 0.f;
+    f32x16_t nacc[NDB];
+    if (LR != 0) {
+        constexpr int NRB = RP / 32;
+        const uint16_t* qraw = (const uint16_t*)a.q + (bh * L + (qval ? qrow : 0)) * D;
+        f32x16_t wacc[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) wacc[rb][i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const u32x4_t qo2 = qval ? ldg16(qraw + 16 * s + 8 * hf) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                const u32x4_t wa = ldg16(a.wqt + ((long)head * RP + 32 * rb + l32) * D + 16 * s + 8 * hf);
+                wacc[rb] = mfma32(wa, qo2, wacc[rb]);
+            }
+        }
+        int crd[3] = {0, 0, 0};
+        if (qval) token_coords(qrow, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
+        const float* zp = a.zp + bh * RP;
+        float den = 0.f;
+        u32x4_t whi[NRB][2], wlo[NRB][2];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            float w[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 32 * rb + 8 * (i >> 2) + 4 * hf + (i & 3);
+                const bool ok = qval && r < a.g.R;
+                float x = wacc[rb][i];
+                if (LR == 2 && ok) x += a.Et[crd[0] * a.g.R + r] + a.Eh[crd[1] * a.g.R + r] + a.Ew[crd[2] * a.g.R + r];
+                w[i] = ok ? phi_elu1(x) : 0.f;
+                den += w[i] * zp[r];
+            }
+            if (LR == 1) {
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    const int r = 32 * rb + 8 * (i >> 2) + 4 * hf + (i & 3);
+                    if (qval && r < a.g.R) {
+                        const float2 cs = lr_cossin_q(a.tab, a.g, r >> 1, crd);
+                        const float w0 = w[i], w1 = w[i + 1];
+                        w[i] = w0 * cs.x - w1 * cs.y;
+                        w[i + 1] = w0 * cs.y + w1 * cs.x;
+                    }
+                }
+            }
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float a0 = w[8 * h2 + 2 * i], a1 = w[8 * h2 + 2 * i + 1];
+                    const uint32_t hi = pack_bf2(a0, a1);
+                    whi[rb][h2][i] = hi;
+                    wlo[rb][h2][i] = pack_bf2(a0 - bf_lo(hi), a1 - bf_hi(hi));
+                }
+        }
+        den += wave_xor32(den);
+        rden = 1.f / (den + a.eps);
+        gsc = a.gate[head];
+        // num^T = S^T rho(w)^T: m = d, k = r, n = query
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) nacc[db][i] = 0.f;
+            const long so = (bh * D + 32 * db + l32) * RP + 8 * hf;
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const u32x4_t sh = ldg16(a.st_hi + so + 32 * rb + 16 * h2);
+                    const u32x4_t sl = ldg16(a.st_lo + so + 32 * rb + 16 * h2);
+                    nacc[db] = mfma32(sh, whi[rb][h2], nacc[db]);
+                    nacc[db] = mfma32(sh, wlo[rb][h2], nacc[db]);
+                    nacc[db] = mfma32(sl, whi[rb][h2], nacc[db]);
+                }
+        }
+    }
+    if (!qval) return;
+    uint16_t* out = (uint16_t*)a.out + (bh * L + qrow) * D;
+    uint16_t* osp = a.o_sp ? (uint16_t*)a.o_sp + (bh * L + qrow) * D : nullptr;
+    uint16_t* olr = a.o_lr ? (uint16_t*)a.o_lr + (bh * L + qrow) * D : nullptr;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int d0 = 32 * db + 8 * g4 + 4 * hf;
+            float vs[4], vl[4], vo[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vs[i] = oacc[db][4 * g4 + i] * inv;
+                vl[i] = LR != 0 ? nacc[db][4 * g4 + i] * rden : 0.f;
+                vo[i] = vs[i] + gsc * vl[i];
+            }
+            *reinterpret_cast<u32x2_t*>(out + d0) = u32x2_t{pack_bf2(vo[0], vo[1]), pack_bf2(vo[2], vo[3])};
+            if (osp) *reinterpret_cast<u32x2_t*>(osp + d0) = u32x2_t{pack_bf2(vs[0], vs[1]), pack_bf2(vs[2], vs[3])};
+            if (olr) *reinterpret_cast<u32x2_t*>(olr + d0) = u32x2_t{pack_bf2(vl[0], vl[1]), pack_bf2(vl[2], vl[3])};
+        }
+}
+
+// fp32 layers: one thread per query row, K / V tiles staged in LDS, fp32
+// VALU throughout (the precision the tiny fp32 check layer asks for).
+template <int D, int RP, int LR, bool DENSE>
+__global__ __launch_bounds__(64) void k_flash_f32(FlashArgs a, int BS) {
+    __shared__ float k_lds[64][D + 1];
+    __shared__ float v_lds[64][D];
+    const int tid = threadIdx.x;
+    const long wid = xcd_remap(blockIdx.x, a.nwg);
+    const long bh = wid / a.nblk;
+    const int qb = (int)(wid % a.nblk);
+    const int head = (int)(bh % a.H);
+    const long rows = (long)a.nblk * BS;
+    const long L = a.L;
+    const float* qr = (const float*)a.qr + (bh * rows + (long)qb * BS) * D;
+    const float* kr = (const float*)a.kr + bh * rows * D;
+    const float* vv = (const float*)a.v + bh * L * D;
+    const int32_t* ix = DENSE ? nullptr : a.idx + (bh * a.nblk + qb) * (long)a.keep;
+    const int ntile = DENSE ? a.nblk : a.keep;
+    const bool act = tid < BS;
+
+    float q[D], o[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) { q[d] = act ? qr[(long)tid * D + d] : 0.f; o[d] = 0.f; }
+    float m_run = -INFINITY, l_run = 0.f;
+    for (int n = 0; n < ntile; ++n) {
+        const int j = DENSE ? n : ix[n];
+        __syncthreads();
+        for (int e = tid; e < BS * D; e += 64) {
+            const int r = e / D, d = e % D;
+            const long row = (long)j * BS + r;
+            k_lds[r][d] = kr[row * D + d];
+            v_lds[r][d] = row < L ? vv[row * D + d] : 0.f;
+        }
+        __syncthreads();
+        float s[64];
+        float mx = -INFINITY;
+        for (int r = 0; r < BS; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int d = 0; d < D; ++d) acc += q[d] * k_lds[r][d];
+            acc *= a.scale;
+            if ((long)j * BS + r >= L) acc = -INFINITY;
+            s[r] = acc;
+            mx = fmaxf(mx, acc);
+        }
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = expf(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < D; ++d) o[d] *= alpha;
+        for (int r = 0; r < BS; ++r) {
+            const float p = expf(s[r] - m_new);
+            l_run += p;
+#pragma unroll
+            for (int d = 0; d < D; ++d) o[d] += p * v_lds[r][d];
+        }
+        m_run = m_new;
+    }
+    const long qrow = (long)qb * BS + tid;
+    if (!act || qrow >= L) return;
+    const float inv = 1.f / l_run;
+    float* out = (float*)a.out + (bh * L + qrow) * D;
+    float* osp = a.o_sp ? (float*)a.o_sp + (bh * L + qrow) * D : nullptr;
+    float* olr = a.o_lr ? (float*)a.o_lr + (bh * L + qrow) * D : nullptr;
+    if (LR == 0) {
+        for (int d = 0; d < D; ++d) {
+            out[d] = o[d] * inv;
+            if (osp) osp[d] = o[d] * inv;
+        }
+        return;
+    }
+    const int R = a.g.R;
+    const float* qraw = (const float*)a.q + (bh * L + qrow) * D;
+    const float* W = a.wq + (long)head * D * R;
+    int crd[3];
+    token_coords(qrow, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
+    float w[RP], f[RP];
+    float den = 0.f;
+    for (int r = 0; r < RP; ++r) {
+        float x = 0.f;
+        if (r < R) {
+            for (int d = 0; d < D; ++d) x += qraw[d] * W[d * R + r];
+            if (LR == 2) x += a.Et[crd[0] * R + r] + a.Eh[crd[1] * R + r] + a.Ew[crd[2] * R + r];
+        }
+        w[r] = r < R ? phi_elu1(x) : 0.f;
+        den += r < R ? w[r] * a.zp[bh * R + r] : 0.f;
+    }
+    for (int r = 0; r < RP; r += 2) {
+        if (LR == 1 && r < R) {
+            const float2 cs = lr_cossin_q(a.tab, a.g, r >> 1, crd);
+            f[r] = w[r] * cs.x - w[r + 1] * cs.y;
+            f[r + 1] = w[r] * cs.y + w[r + 1] * cs.x;
+        } else {
+            f[r] = w[r];
+            f[r + 1] = w[r + 1];
+        }
+    }
+    const float rd = 1.f / (den + a.eps);
+    const float gs = a.gate[head];
+    const float* S = a.S + bh * (long)R * D;
+    for (int d = 0; d < D; ++d) {
+        float num = 0.f;
+        for (int r = 0; r < R; ++r) num += f[r] * S[(long)r * D + d];
+        const float sp = o[d] * inv, lr = num * rd;
+        out[d] = sp + gs * lr;
+        if (osp) osp[d] = sp;
+        if (olr) olr[d] = lr;
+    }
+}
+
+// ---- launcher ------------------------------------------------------------
+template <int D, int BS, int RP, int LR, bool DENSE>
+static hipError_t flash_bf16_t(const FlashArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((k_flash_bf16<D, BS, RP, LR, DENSE>), dim3((unsigned)a.nwg), dim3(BS * 2), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int D, int BS, int RP>
+static hipError_t flash_bf16_mode(int lr_mode, bool dense, const FlashArgs& a, hipStream_t st) {
+    if (dense) return flash_bf16_t<D, BS, RP, 0, true>(a, st);
+    if (lr_mode == 1) return flash_bf16_t<D, BS, RP, 1, false>(a, st);
+    if (lr_mode == 2) return flash_bf16_t<D, BS, RP, 2, false>(a, st);
+    return flash_bf16_t<D, BS, RP, 0, false>(a, st);
+}
+
+template <int D, int RP>
+static hipError_t flash_f32_t(int lr_mode, bool dense, const FlashArgs& a, int BS, hipStream_t st) {
+    dim3 grid((unsigned)a.nwg);
+    if (dense)
+        hipLaunchKernelGGL((k_flash_f32<D, RP, 0, true>), grid, dim3(64), 0, st, a, BS);
+    else if (lr_mode == 1)
+        hipLaunchKernelGGL((k_flash_f32<D, RP, 1, false>), grid, dim3(64), 0, st, a, BS);
+    else if (lr_mode == 2)
+        hipLaunchKernelGGL((k_flash_f32<D, RP, 2, false>), grid, dim3(64), 0, st, a, BS);
+    else
+        hipLaunchKernelGGL((k_flash_f32<D, RP, 0, false>), grid, dim3(64), 0, st, a, BS);
+    return hipGetLastError();
+}
+
+hipError_t launch_flash(int dtype_bf16, int D, int BS, int RP, int lr_mode, bool dense, const FlashArgs& a, long BH,
+                        hipStream_t st) {
+    (void)BH;
+    if (!dtype_bf16) {
+        if (D == 64) return RP == 64 ? flash_f32_t<64, 64>(lr_mode, dense, a, BS, st)
+                                     : flash_f32_t<64, 32>(lr_mode, dense, a, BS, st);
+        return RP == 64 ? flash_f32_t<128, 64>(lr_mode, dense, a, BS, st)
+                        : flash_f32_t<128, 32>(lr_mode, dense, a, BS, st);
+    }
+    if (D == 128 && BS == 64)
+        return RP == 64 ? flash_bf16_mode<128, 64, 64>(lr_mode, dense, a, st)
+                        : flash_bf16_mode<128, 64, 32>(lr_mode, dense, a, st);
+    if (D == 128 && BS == 32)
+        return RP == 64 ? flash_bf16_mode<128, 32, 64>(lr_mode, dense, a, st)
+                        : flash_bf16_mode<128, 32, 32>(lr_mode, dense, a, st);
+    if (D == 64 && BS == 64)
+        return RP == 64 ? flash_bf16_mode<64, 64, 64>(lr_mode, dense, a, st)
+                        : flash_bf16_mode<64, 64, 32>(lr_mode, dense, a, st);
+    return RP == 64 ? flash_bf16_mode<64, 32, 64>(lr_mode, dense, a, st)
+                    : flash_bf16_mode<64, 32, 32>(lr_mode, dense, a, st);
+}
+
+}  // namespace slr

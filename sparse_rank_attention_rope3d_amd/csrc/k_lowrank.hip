@@ -1,0 +1,384 @@
+// Low-rank global branch: the reusable per-head summary.
+//
+// RoLA (arXiv 2609.06712v3) §4.1 / App. B.1: the global context is one
+// query-independent sum per head, O(L r D). §4.2-4.3: features are
+// u = phi(k W_k) (phi = elu + 1, position-free content), rotated after phi
+// by the backbone's first rotary pairs of each axis; RoPeSLR (arXiv
+// 2605.20659) abstract: the absolute-PE variant adds E_t[t]+E_h[h]+E_w[w]
+// before phi and does not rotate. S = sum f v^T, z = sum u over the L valid
+// tokens.
+//
+// bf16 layers: u = K W_k on bf16 MFMA (exact products, fp32 sums); phi, the
+// rotation and z in fp32; S = sum f v^T on bf16 MFMA with f split into
+// bf16 hi + lo parts (about 16 mantissa bits), fp32 accumulation.
+// Split-L partials [BH][nsplit][RP*D + RP] are reduced in a fixed order, so
+// results are bitwise reproducible.
+#include "slr_common.h"
+#include "slr_launch.h"
+
+namespace slr {
+
+// W [H][D][R] fp32 -> Wt [H][RP][D] bf16 (transposed, rows r >= R zero).
+__global__ void k_lr_prep(const float* __restrict__ W, uint16_t* __restrict__ Wt, int H, int D, int R, int RP) {
+    const long n = (long)H * RP * D;
+    for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < n; e += (long)gridDim.x * blockDim.x) {
+        const int d = (int)(e % D);
+        const int r = (int)((e / D) % RP);
+        const long h = e / ((long)D * RP);
+        Wt[e] = r < R ? f2bf(W[(h * D + d) * R + r]) : (uint16_t)0;
+    }
+}
+
+// Rotation of low-rank feature pair index pr (0 .. R/2-1) at token coords.
+__device__ __forceinline__ float2 lr_cossin(const float2* __restrict__ tab, const LrGeom& g, int pr, const int* crd) {
+    int a, j;
+    if (pr < g.lp[0]) { a = 0; j = pr; }
+    else if (pr < g.lp[0] + g.lp[1]) { a = 1; j = pr - g.lp[0]; }
+    else { a = 2; j = pr - g.lp[0] - g.lp[1]; }
+    return tab[g.rope.tab_off[a] + crd[a] * g.rope.np[a] + j];
+}
+
+// One workgroup (4 waves) = `chunk` consecutive tokens of one (b, h) slice;
+// each wave takes 32-token sub-tiles. Per sub-tile:
+//   U (32 tok x RP) = K_sub W_k              MFMA m=tok, n=r, k=d
+//   U -> E, phi, rotation (pairs are adjacent lanes), z partial
+//   S (RP x D) += U^T V_sub                  MFMA m=r, n=d, k=tok
+// The U accumulator already has the token slots a 32x32x16 A operand needs
+// (slot16 order), so V is staged in LDS transposed [d][slot16(tok)].
+template <int D, int RP, bool ABSPE>
+__global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v,
+                                                         const uint16_t* __restrict__ wkt,
+                                                         const float* __restrict__ Et,
+                                                         const float* __restrict__ Eh,
+                                                         const float* __restrict__ Ew,
+                                                         const float2* __restrict__ tab, LrGeom g, long L,
+                                                         int H, int chunk, int nsplit, float* __restrict__ part) {
+    constexpr int NRB = RP / 32;   // r blocks
+    constexpr int NDB = D / 32;    // d blocks
+    constexpr int NKS = D / 16;    // k steps over d
+    constexpr int VLD = 32 + 8;    // LDS row stride (elements) of V^T
+    __shared__ __attribute__((aligned(16))) uint16_t vt[4][D * VLD];
+    __shared__ float red[RP * D + RP];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const long bh = blockIdx.y;
+    const int head = (int)(bh % H);
+    const int split = blockIdx.x;
+    const long tok_lo = (long)split * chunk;
+    const long tok_hi = tok_lo + chunk < L ? tok_lo + chunk : L;
+    const uint16_t* ks = k + bh * L * D;
+    const uint16_t* vs = v + bh * L * D;
+
+    // B operand of U = K W: W[d = 16s + 8hf + e][r = 32rb + l32]
+    u32x4_t wop[NRB][NKS];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+            wop[rb][s] = ldg16(wkt + ((long)head * RP + 32 * rb + l32) * D + 16 * s + 8 * hf);
+
+    f32x16_t sacc[NRB][NDB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[rb][db][i] = 0.f;
+    float zacc[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) zacc[rb] = 0.f;
+
+    // V transpose assignment: 8 tokens x 8 dims per lane
+    constexpr int VCH = D / 8;                 // dim chunks
+    const int vc = lane % VCH, vg = lane / VCH;  // vg: 8-token group (valid if < 4)
+    const int vG = vg >> 1, vh = vg & 1;
+    uint16_t* myvt = vt[wave];
+
+    // every wave runs the same number of steps (the loop holds barriers)
+    const int nsteps = (int)((tok_hi - tok_lo + 127) / 128);
+    for (int step = 0; step < nsteps; ++step) {
+        const long t0 = tok_lo + 128L * step + 32 * wave;
+        // ---- U = K_sub W_k
+        const long tk = t0 + l32;
+        const bool tval = t0 < tok_hi && tk < tok_hi;
+        f32x16_t uacc[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) uacc[rb][i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            u32x4_t kop = tval ? ldg16(ks + tk * D + 16 * s + 8 * hf) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) uacc[rb] = mfma32(kop, wop[rb][s], uacc[rb]);
+        }
+        // ---- V sub-tile -> LDS, transposed to [d][slot16(tok)]
+        if (vg < 4) {
+            uint32_t rows[8][4];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int tl = 16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2);  // token within sub-tile
+                const long tv = t0 + tl;
+                u32x4_t w = (t0 < tok_hi && tv < tok_hi) ? ldg16(vs + tv * D + 8 * vc) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rows[e][i] = w[i];
+            }
+#pragma unroll
+            for (int f = 0; f < 8; ++f) {
+                u32x4_t o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t a0 = rows[2 * i][f >> 1], a1 = rows[2 * i + 1][f >> 1];
+                    o[i] = (f & 1) ? __builtin_amdgcn_perm(a1, a0, 0x07060302u)
+                                   : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+                }
+                stg16(myvt + (8 * vc + f) * VLD + 16 * vG + 8 * vh, o);
+            }
+        }
+        // ---- features: lane holds r = 32rb + l32, tokens 8(v/4) + 4hf + v%4
+        u32x4_t fhi[NRB][2], flo[NRB][2];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            const int r = 32 * rb + l32;
+            float f[16];
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv) {
+                const long tt = t0 + 8 * (vv >> 2) + 4 * hf + (vv & 3);
+                const bool ok = t0 < tok_hi && tt < tok_hi && r < g.R;
+                float x = uacc[rb][vv];
+                int crd[3] = {0, 0, 0};
+                if (ok) token_coords(tt, g.rope.Hg, g.rope.Wg, crd[0], crd[1], crd[2]);
+                if (ABSPE && ok) x += Et[crd[0] * g.R + r] + Eh[crd[1] * g.R + r] + Ew[crd[2] * g.R + r];
+                float u = ok ? phi_elu1(x) : 0.f;
+                zacc[rb] += u;
+                if (!ABSPE) {
+                    const float p = lane_swap1(u);  // partner dim r ^ 1
+                    float2 cs = make_float2(1.f, 0.f);
+                    if (ok) cs = lr_cossin(tab, g, r >> 1, crd);
+                    u = (r & 1) ? (p * cs.y + u * cs.x) : (u * cs.x - p * cs.y);
+                }
+                f[vv] = u;
+            }
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float a0 = f[8 * ks2 + 2 * i], a1 = f[8 * ks2 + 2 * i + 1];
+                    const uint32_t hi = pack_bf2(a0, a1);
+                    fhi[rb][ks2][i] = hi;
+                    flo[rb][ks2][i] = pack_bf2(a0 - bf_lo(hi), a1 - bf_hi(hi));
+                }
+        }
+        __syncthreads();
+        // ---- S += F^T V
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2) {
+                const u32x4_t vb = *reinterpret_cast<const u32x4_t*>(myvt + (32 * db + l32) * VLD + 16 * ks2 + 8 * hf);
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb) {
+                    sacc[rb][db] = mfma32(fhi[rb][ks2], vb, sacc[rb][db]);
+                    sacc[rb][db] = mfma32(flo[rb][ks2], vb, sacc[rb][db]);
+                }
+            }
+        __syncthreads();
+    }
+
+    // ---- reduce the 4 waves in a fixed order, then write the partial
+    // sacc[rb][db][vv]: r = 32rb + 8(vv/4) + 4hf + vv%4, d = 32db + l32
+    for (int w = 0; w < 4; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int vv = 0; vv < 16; ++vv) {
+                        const int r = 32 * rb + 8 * (vv >> 2) + 4 * hf + (vv & 3);
+                        const int e = r * D + 32 * db + l32;
+                        red[e] = (w == 0 ? 0.f : red[e]) + sacc[rb][db][vv];
+                    }
+            // z: lanes l32 and l32+32 hold the same r, different tokens
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                const float zz = zacc[rb] + wave_xor32(zacc[rb]);
+                if (hf == 0) {
+                    const int e = RP * D + 32 * rb + l32;
+                    red[e] = (w == 0 ? 0.f : red[e]) + zz;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    float* dst = part + (bh * nsplit + split) * (long)(RP * D + RP);
+    for (int e = tid; e < RP * D + RP; e += 256) dst[e] = red[e];
+}
+
+// fp32 layers: the same sums on fp32 VALU (tokens staged through LDS).
+template <int D, int RP>
+__global__ __launch_bounds__(256) void k_lr_summary_f32(const float* __restrict__ k, const float* __restrict__ v,
+                                                        const float* __restrict__ W, const float* __restrict__ Et,
+                                                        const float* __restrict__ Eh, const float* __restrict__ Ew,
+                                                        const float2* __restrict__ tab, LrGeom g, long L, int H,
+                                                        int absPE, int chunk, int nsplit, float* __restrict__ part) {
+    constexpr int TS = 16;  // tokens per step
+    __shared__ float ksh[TS][D], vsh[TS][D], fsh[TS][RP], ush[TS][RP];
+    const int tid = threadIdx.x;
+    const long bh = blockIdx.y;
+    const int head = (int)(bh % H);
+    const int split = blockIdx.x;
+    const long tok_lo = (long)split * chunk;
+    const long tok_hi = tok_lo + chunk < L ? tok_lo + chunk : L;
+    const int R = g.R;
+    const float* Wh = W + (long)head * D * R;
+    constexpr int NE = (RP * D + 255) / 256;
+    float sacc[NE];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) sacc[i] = 0.f;
+    float zacc = 0.f;
+
+    for (long t0 = tok_lo; t0 < tok_hi; t0 += TS) {
+        for (int e = tid; e < TS * D; e += 256) {
+            const int tl = e / D, d = e % D;
+            const long t = t0 + tl;
+            ksh[tl][d] = t < tok_hi ? k[(bh * L + t) * D + d] : 0.f;
+            vsh[tl][d] = t < tok_hi ? v[(bh * L + t) * D + d] : 0.f;
+        }
+        __syncthreads();
+        // features, one (token, pair) per thread
+        for (int e = tid; e < TS * (RP / 2); e += 256) {
+            const int tl = e / (RP / 2), pr = e % (RP / 2);
+            const long t = t0 + tl;
+            float u[2] = {0.f, 0.f};
+            int crd[3] = {0, 0, 0};
+            const bool tv = t < tok_hi;
+            if (tv) token_coords(t, g.rope.Hg, g.rope.Wg, crd[0], crd[1], crd[2]);
+            for (int q = 0; q < 2; ++q) {
+                const int r = 2 * pr + q;
+                if (!tv || r >= R) continue;
+                float acc = 0.f;
+                for (int d = 0; d < D; ++d) acc += ksh[tl][d] * Wh[d * R + r];
+                if (absPE) acc += Et[crd[0] * R + r] + Eh[crd[1] * R + r] + Ew[crd[2] * R + r];
+                u[q] = phi_elu1(acc);
+            }
+            ush[tl][2 * pr] = u[0];
+            ush[tl][2 * pr + 1] = u[1];
+            if (!absPE && tv && 2 * pr < R) {
+                const float2 cs = lr_cossin(tab, g, pr, crd);
+                fsh[tl][2 * pr] = u[0] * cs.x - u[1] * cs.y;
+                fsh[tl][2 * pr + 1] = u[0] * cs.y + u[1] * cs.x;
+            } else {
+                fsh[tl][2 * pr] = u[0];
+                fsh[tl][2 * pr + 1] = u[1];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const int e = tid + 256 * i;
+            if (e < RP * D) {
+                const int r = e / D, d = e % D;
+                float s = sacc[i];
+                for (int tl = 0; tl < TS; ++tl) s += fsh[tl][r] * vsh[tl][d];
+                sacc[i] = s;
+            }
+        }
+        if (tid < RP)
+            for (int tl = 0; tl < TS; ++tl) zacc += ush[tl][tid];
+        __syncthreads();
+    }
+    float* dst = part + (bh * nsplit + split) * (long)(RP * D + RP);
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        const int e = tid + 256 * i;
+        if (e < RP * D) dst[e] = sacc[i];
+    }
+    if (tid < RP) dst[RP * D + tid] = zacc;
+}
+
+// Sum the split partials in split order. Writes S [BH][R][D] and z [BH][R]
+// (fp32), and for bf16 layers the readout operand St_hi/St_lo [BH][D][RP]
+// (bf16 hi + lo of S, r in slot16 order inside each 16-group) and zp [BH][RP].
+__global__ __launch_bounds__(256) void k_lr_reduce(const float* __restrict__ part, int nsplit, int D, int R, int RP,
+                                                   float* __restrict__ S, float* __restrict__ z,
+                                                   uint16_t* __restrict__ st_hi, uint16_t* __restrict__ st_lo,
+                                                   float* __restrict__ zp) {
+    const long bh = blockIdx.y;
+    const int n = RP * D + RP;
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= n) return;
+    const float* p = part + bh * nsplit * (long)n + e;
+    float s = 0.f;
+    for (int i = 0; i < nsplit; ++i) s += p[(long)i * n];
+    if (e < RP * D) {
+        const int r = e / D, d = e % D;
+        if (r < R && S) S[(bh * R + r) * D + d] = s;
+        if (st_hi) {
+            const uint16_t hi = f2bf(s);
+            const uint16_t lo = f2bf(s - bf2f(hi));
+            const long o = (bh * D + d) * RP + 16 * (r >> 4) + slot16(r & 15);
+            st_hi[o] = hi;
+            st_lo[o] = lo;
+        }
+    } else {
+        const int r = e - RP * D;
+        if (r < R && z) z[bh * R + r] = s;
+        if (zp) zp[bh * RP + r] = s;
+    }
+}
+
+// ---- launchers ----------------------------------------------------------
+hipError_t launch_lr_prep(const float* W, uint16_t* Wt, int H, int D, int R, int RP, hipStream_t st) {
+    const long n = (long)H * RP * D;
+    hipLaunchKernelGGL(k_lr_prep, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, W, Wt, H, D, R, RP);
+    return hipGetLastError();
+}
+
+template <int D, int RP>
+static hipError_t summary_bf16_t(bool abspe, const void* k, const void* v, const uint16_t* wkt, const float* Et,
+                                 const float* Eh, const float* Ew, const float2* tab, const LrGeom& g, long BH,
+                                 long L, int H, int chunk, int nsplit, float* part, hipStream_t st) {
+    dim3 grid((unsigned)nsplit, (unsigned)BH);
+    if (abspe)
+        hipLaunchKernelGGL((k_lr_summary_bf16<D, RP, true>), grid, dim3(256), 0, st, (const uint16_t*)k,
+                           (const uint16_t*)v, wkt, Et, Eh, Ew, tab, g, L, H, chunk, nsplit, part);
+    else
+        hipLaunchKernelGGL((k_lr_summary_bf16<D, RP, false>), grid, dim3(256), 0, st, (const uint16_t*)k,
+                           (const uint16_t*)v, wkt, Et, Eh, Ew, tab, g, L, H, chunk, nsplit, part);
+    return hipGetLastError();
+}
+
+hipError_t launch_lr_summary(int dtype_bf16, int D, int RP, bool abspe, const void* k, const void* v,
+                             const float* W, const uint16_t* wkt, const float* Et, const float* Eh,
+                             const float* Ew, const float2* tab, const LrGeom& g, long BH, long L, int H, int chunk,
+                             int nsplit, float* part, hipStream_t st) {
+    if (dtype_bf16) {
+        if (D == 64 && RP == 32) return summary_bf16_t<64, 32>(abspe, k, v, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk, nsplit, part, st);
+        if (D == 64) return summary_bf16_t<64, 64>(abspe, k, v, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk, nsplit, part, st);
+        if (RP == 32) return summary_bf16_t<128, 32>(abspe, k, v, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk, nsplit, part, st);
+        return summary_bf16_t<128, 64>(abspe, k, v, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk, nsplit, part, st);
+    }
+    dim3 grid((unsigned)nsplit, (unsigned)BH);
+#define SLR_SUMF32(DD, RR)                                                                                     \
+    hipLaunchKernelGGL((k_lr_summary_f32<DD, RR>), grid, dim3(256), 0, st, (const float*)k, (const float*)v, W, \
+                       Et, Eh, Ew, tab, g, L, H, (int)abspe, chunk, nsplit, part)
+    if (D == 64 && RP == 32) SLR_SUMF32(64, 32);
+    else if (D == 64) SLR_SUMF32(64, 64);
+    else if (RP == 32) SLR_SUMF32(128, 32);
+    else SLR_SUMF32(128, 64);
+#undef SLR_SUMF32
+    return hipGetLastError();
+}
+
+hipError_t launch_lr_reduce(const float* part, long BH, int nsplit, int D, int R, int RP, float* S, float* z,
+                            uint16_t* st_hi, uint16_t* st_lo, float* zp, hipStream_t st) {
+    const int n = RP * D + RP;
+    dim3 grid((unsigned)((n + 255) / 256), (unsigned)BH);
+    hipLaunchKernelGGL(k_lr_reduce, grid, dim3(256), 0, st, part, nsplit, D, R, RP, S, z, st_hi, st_lo, zp);
+    return hipGetLastError();
+}
+
+}  // namespace slr

@@ -1,0 +1,185 @@
+// 3D RoPE tables and the fused rotate + block mean-pool kernel.
+//
+// RoLA (arXiv 2609.06712v3) §3 "3D RoPE", eq. 1: the head is split across
+// the t, h, w axes; each axis rotates its own pairs by (coordinate) x
+// (its frequency), so scores depend on per-axis offsets only. §4.2 reuses
+// the backbone's cos/sin tensors in the low-rank branch, so the tables
+// built here serve both branches.
+#include "slr_common.h"
+#include "slr_launch.h"
+
+namespace slr {
+
+// (cos, sin) of p * base^(-2j/(2n)) for every axis coordinate p and pair j,
+// evaluated in fp64 and rounded once to fp32.
+__global__ void k_rope_tables(float2* __restrict__ tab, int T, int Hg, int Wg, int nt, int nh, int nw,
+                              double base) {
+    const int n_t = T * nt, n_h = Hg * nh, n_w = Wg * nw;
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n_t + n_h + n_w; e += gridDim.x * blockDim.x) {
+        int p, j, n;
+        if (e < n_t) {
+            p = e / nt; j = e % nt; n = nt;
+        } else if (e < n_t + n_h) {
+            p = (e - n_t) / nh; j = (e - n_t) % nh; n = nh;
+        } else {
+            p = (e - n_t - n_h) / nw; j = (e - n_t - n_h) % nw; n = nw;
+        }
+        double theta = pow(base, -2.0 * (double)j / (2.0 * (double)n));
+        double a = (double)p * theta;
+        tab[e] = make_float2((float)cos(a), (float)sin(a));
+    }
+}
+
+template <typename TIO> struct Io8;
+template <> struct Io8<uint16_t> {
+    // 8 bf16 values as fp32
+    static __device__ __forceinline__ void load(const uint16_t* p, float* x) {
+        u32x4_t w = ldg16(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[2 * i] = bf_lo(w[i]); x[2 * i + 1] = bf_hi(w[i]); }
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, const float* x) {
+        u32x4_t w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = pack_bf2(x[2 * i], x[2 * i + 1]);
+        stg16(p, w);
+    }
+};
+template <> struct Io8<float> {
+    static __device__ __forceinline__ void load(const float* p, float* x) {
+        f32x4_t a = *reinterpret_cast<const f32x4_t*>(p), b = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+    }
+    static __device__ __forceinline__ void store(float* p, const float* x) {
+        f32x4_t a, b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { a[i] = x[i]; b[i] = x[4 + i]; }
+        *reinterpret_cast<f32x4_t*>(p) = a;
+        *reinterpret_cast<f32x4_t*>(p + 4) = b;
+    }
+};
+
+// One workgroup = one block of `bs` tokens of one (b, h) slice, for q and
+// (optionally) k. Thread layout: 8 consecutive dims (4 pairs) of one token
+// row per thread, D/8 threads per row, 256/(D/8) rows per pass.
+// Writes the rotated rows when q_out / k_out are non-null (rows in
+// [L, out_rows) of the block are written as zeros, which pads the workspace
+// copy to whole blocks) and, when qbar is non-null, the block means of the
+// fp32 rotated values over valid tokens.
+template <typename TIO, int D>
+__global__ __launch_bounds__(256) void k_rope_pool(const TIO* __restrict__ q, const TIO* __restrict__ k,
+                                                   TIO* __restrict__ q_out, TIO* __restrict__ k_out,
+                                                   float* __restrict__ qbar, float* __restrict__ kbar,
+                                                   const float2* __restrict__ tab, RopeGeom g, long L,
+                                                   long out_rows, int bs, int nblk) {
+    constexpr int CH = D / 8;          // threads per row
+    constexpr int RPP = 256 / CH;      // rows per pass
+    const int tid = threadIdx.x;
+    const int c = tid % CH, rsub = tid / CH;
+    const int blk = blockIdx.x;
+    const long bh = blockIdx.y;
+    const bool two = (k != nullptr);
+
+    // axis and in-axis index of the 4 pairs this thread owns
+    int ax[4], jj[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        int p = 4 * c + e;
+        if (p < g.np[0]) { ax[e] = 0; jj[e] = p; }
+        else if (p < g.np[0] + g.np[1]) { ax[e] = 1; jj[e] = p - g.np[0]; }
+        else { ax[e] = 2; jj[e] = p - g.np[0] - g.np[1]; }
+    }
+
+    float sq[8], sk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { sq[i] = 0.f; sk[i] = 0.f; }
+
+    const TIO* qs = q + bh * L * D;
+    const TIO* ks = two ? k + bh * L * D : nullptr;
+    TIO* qo = q_out ? q_out + bh * out_rows * D : nullptr;
+    TIO* ko = (two && k_out) ? k_out + bh * out_rows * D : nullptr;
+
+    for (int r0 = 0; r0 < bs; r0 += RPP) {
+        const long l = (long)blk * bs + r0 + rsub;
+        if (l >= out_rows) continue;
+        float xq[8], xk[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xk[i] = 0.f;
+        if (l < L) {
+            int crd[3];
+            token_coords(l, g.Hg, g.Wg, crd[0], crd[1], crd[2]);
+            Io8<TIO>::load(qs + l * D + 8 * c, xq);
+            if (two) Io8<TIO>::load(ks + l * D + 8 * c, xk);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int a = ax[e];
+                const float2 cs = tab[g.tab_off[a] + crd[a] * g.np[a] + jj[e]];
+                float x0 = xq[2 * e], x1 = xq[2 * e + 1];
+                xq[2 * e] = x0 * cs.x - x1 * cs.y;
+                xq[2 * e + 1] = x0 * cs.y + x1 * cs.x;
+                if (two) {
+                    x0 = xk[2 * e]; x1 = xk[2 * e + 1];
+                    xk[2 * e] = x0 * cs.x - x1 * cs.y;
+                    xk[2 * e + 1] = x0 * cs.y + x1 * cs.x;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) { sq[i] += xq[i]; sk[i] += xk[i]; }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xq[i] = 0.f;
+        }
+        if (qo) Io8<TIO>::store(qo + l * D + 8 * c, xq);
+        if (ko) Io8<TIO>::store(ko + l * D + 8 * c, xk);
+    }
+
+    if (qbar == nullptr) return;
+    // block means: reduce the RPP row groups through LDS, fixed order
+    __shared__ float red[2][RPP][D];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { red[0][rsub][8 * c + i] = sq[i]; red[1][rsub][8 * c + i] = sk[i]; }
+    __syncthreads();
+    const long lo = (long)blk * bs;
+    const long hi = lo + bs < L ? lo + bs : L;
+    const float inv = 1.f / (float)(hi - lo);
+    for (int e = tid; e < (two ? 2 : 1) * D; e += 256) {
+        const int which = e / D, d = e % D;
+        float s = 0.f;
+        for (int r = 0; r < RPP; ++r) s += red[which][r][d];
+        float* dst = which ? kbar : qbar;
+        dst[(bh * nblk + blk) * D + d] = s * inv;
+    }
+}
+
+// ---- launchers ----------------------------------------------------------
+hipError_t launch_rope_tables(float2* tab, const RopeGeom& g, double base, hipStream_t st) {
+    const int n = g.T * g.np[0] + g.Hg * g.np[1] + g.Wg * g.np[2];
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_rope_tables, dim3((n + 255) / 256), dim3(256), 0, st, tab, g.T, g.Hg, g.Wg, g.np[0],
+                       g.np[1], g.np[2], base);
+    return hipGetLastError();
+}
+
+template <typename TIO, int D>
+static hipError_t rope_pool_t(const void* q, const void* k, void* qo, void* ko, float* qbar, float* kbar,
+                              const float2* tab, const RopeGeom& g, long BH, long L, long out_rows, int bs,
+                              int nblk, hipStream_t st) {
+    dim3 grid((unsigned)nblk, (unsigned)BH);
+    hipLaunchKernelGGL((k_rope_pool<TIO, D>), grid, dim3(256), 0, st, (const TIO*)q, (const TIO*)k, (TIO*)qo,
+                       (TIO*)ko, qbar, kbar, tab, g, L, out_rows, bs, nblk);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_pool(int dtype_bf16, int D, const void* q, const void* k, void* qo, void* ko, float* qbar,
+                            float* kbar, const float2* tab, const RopeGeom& g, long BH, long L, long out_rows,
+                            int bs, int nblk, hipStream_t st) {
+    if (dtype_bf16) {
+        if (D == 64) return rope_pool_t<uint16_t, 64>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
+        return rope_pool_t<uint16_t, 128>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
+    }
+    if (D == 64) return rope_pool_t<float, 64>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
+    return rope_pool_t<float, 128>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
+}
+
+}  // namespace slr

@@ -1,0 +1,432 @@
+// libslr C ABI: argument checks, workspace layout and the launch sequence.
+//
+// Every check runs on the host before the first HIP call, so a rejected call
+// has no side effect. Launch order of the layer forward (one stream):
+//   rope tables -> (bf16) projection prep -> rotate + pool q, k -> block
+//   top-k -> low-rank split-L summary -> fixed-order reduce -> fused
+//   sparse flash + low-rank readout + gated combine.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/slr.h"
+#include "slr_launch.h"
+
+using namespace slr;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Dims {
+    long B, H, BH, D, L;
+    int T, Hg, Wg, bf16, es;
+};
+
+int check_shape(const slr_shape* s, Dims* d) {
+    if (!s) return SLR_EINVAL;
+    if (s->B < 1 || s->H < 1 || s->T < 1 || s->Hg < 1 || s->Wg < 1) return SLR_EINVAL;
+    if (s->dtype != SLR_F32 && s->dtype != SLR_BF16) return SLR_EINVAL;
+    if (s->D < 2 || (s->D & 1)) return SLR_EINVAL;
+    if (s->D != 64 && s->D != 128) return SLR_EUNSUPPORTED;
+    const long L = (long)s->T * s->Hg * s->Wg;
+    if (L > 0x7fffffffL || (long)s->Hg * s->Wg > 0x7fffffffL) return SLR_EUNSUPPORTED;
+    const long BH = (long)s->B * s->H;
+    if (BH > 65535) return SLR_EUNSUPPORTED;
+    d->B = s->B; d->H = s->H; d->BH = BH; d->D = s->D; d->L = L;
+    d->T = s->T; d->Hg = s->Hg; d->Wg = s->Wg;
+    d->bf16 = s->dtype == SLR_BF16;
+    d->es = d->bf16 ? 2 : 4;
+    return SLR_OK;
+}
+
+int check_rope(const slr_rope_cfg* r, const Dims& d, RopeGeom* g) {
+    if (!r) return SLR_EINVAL;
+    if (!std::isfinite(r->base) || !(r->base > 1.0)) return SLR_EINVAL;
+    if (r->pairs_t < 0 || r->pairs_h < 0 || r->pairs_w < 0) return SLR_EINVAL;
+    if ((long)r->pairs_t + r->pairs_h + r->pairs_w != d.D / 2) return SLR_EINVAL;
+    g->T = d.T; g->Hg = d.Hg; g->Wg = d.Wg;
+    g->np[0] = r->pairs_t; g->np[1] = r->pairs_h; g->np[2] = r->pairs_w;
+    g->tab_off[0] = 0;
+    g->tab_off[1] = d.T * r->pairs_t;
+    g->tab_off[2] = g->tab_off[1] + d.Hg * r->pairs_h;
+    return SLR_OK;
+}
+
+long rope_tab_entries(const RopeGeom& g) { return (long)g.T * g.np[0] + (long)g.Hg * g.np[1] + (long)g.Wg * g.np[2]; }
+
+int check_sparse(const slr_sparse_cfg* sp, const Dims& d, int* nblk) {
+    if (!sp) return SLR_EINVAL;
+    if (sp->block != 32 && sp->block != 64) return SLR_EINVAL;
+    const long nb = (d.L + sp->block - 1) / sp->block;
+    if (sp->keep < 1 || sp->keep > nb) return SLR_EINVAL;
+    if (nb > 16383 || d.BH * nb > 0x7fffffffL) return SLR_EUNSUPPORTED;
+    *nblk = (int)nb;
+    return SLR_OK;
+}
+
+int check_lowrank(const slr_lowrank_cfg* lr, const slr_rope_cfg* rope, const Dims& d, bool need_q, LrGeom* lg,
+                  int* RP) {
+    if (!lr) return SLR_EINVAL;
+    if (lr->rank != 8 && lr->rank != 16 && lr->rank != 32 && lr->rank != 64) return SLR_EINVAL;
+    if (lr->mode != SLR_LR_ROPE_OUTSIDE && lr->mode != SLR_LR_ABS_PE) return SLR_EINVAL;
+    if (!std::isfinite(lr->eps) || !(lr->eps > 0.f)) return SLR_EINVAL;
+    if (!lr->Wk || !aligned(lr->Wk, 4)) return SLR_EINVAL;
+    if (need_q && (!lr->Wq || !aligned(lr->Wq, 4) || !lr->gate || !aligned(lr->gate, 4))) return SLR_EINVAL;
+    lg->lp[0] = lg->lp[1] = lg->lp[2] = 0;
+    if (lr->mode == SLR_LR_ROPE_OUTSIDE) {
+        if (lr->lr_pairs_t < 0 || lr->lr_pairs_h < 0 || lr->lr_pairs_w < 0) return SLR_EINVAL;
+        if (lr->lr_pairs_t + lr->lr_pairs_h + lr->lr_pairs_w != lr->rank / 2) return SLR_EINVAL;
+        if (lr->lr_pairs_t > rope->pairs_t || lr->lr_pairs_h > rope->pairs_h || lr->lr_pairs_w > rope->pairs_w)
+            return SLR_EINVAL;
+        lg->lp[0] = lr->lr_pairs_t; lg->lp[1] = lr->lr_pairs_h; lg->lp[2] = lr->lr_pairs_w;
+    } else {
+        if (!lr->Et || !lr->Eh || !lr->Ew) return SLR_EINVAL;
+        if (!aligned(lr->Et, 4) || !aligned(lr->Eh, 4) || !aligned(lr->Ew, 4)) return SLR_EINVAL;
+    }
+    lg->R = lr->rank;
+    *RP = lr->rank <= 32 ? 32 : 64;
+    (void)d;
+    return SLR_OK;
+}
+
+bool tensor_ok(const void* p) { return p && aligned(p, 16); }
+
+// Split-L chunk of the summary: a multiple of 128 tokens, aiming at about
+// 1024 workgroups over all slices.
+void summary_split(const Dims& d, int* chunk, int* nsplit) {
+    long c = (d.BH * d.L + 1023) / 1024;
+    c = (c + 127) / 128 * 128;
+    if (c < 512) c = 512;
+    *chunk = (int)c;
+    *nsplit = (int)((d.L + c - 1) / c);
+}
+
+// Workspace layout (byte offsets, each 256-byte aligned).
+struct Layout {
+    size_t tab, qr, kr, qbar, kbar, idx, wqt, wkt, part, S, z, sthi, stlo, zp, total;
+};
+
+Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int keep, int R, int RP) {
+    Layout w;
+    std::memset(&w, 0, sizeof(w));
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+    w.tab = take(sizeof(float2) * (size_t)rope_tab_entries(g));
+    if (op == SLR_OP_SELECT || op == SLR_OP_ATTENTION) {
+        w.qbar = take(4ul * d.BH * nblk * d.D);
+        w.kbar = take(4ul * d.BH * nblk * d.D);
+        w.idx = take(4ul * d.BH * nblk * keep);
+    }
+    if (op == SLR_OP_ATTENTION || op == SLR_OP_DENSE) {
+        const size_t rows = (size_t)nblk * bs;
+        w.qr = take((size_t)d.es * d.BH * rows * d.D);
+        w.kr = take((size_t)d.es * d.BH * rows * d.D);
+    }
+    if (op == SLR_OP_ATTENTION || op == SLR_OP_LOWRANK_SUMMARY) {
+        int chunk, nsplit;
+        summary_split(d, &chunk, &nsplit);
+        if (d.bf16) {
+            w.wqt = take(2ul * d.H * RP * d.D);
+            w.wkt = take(2ul * d.H * RP * d.D);
+        }
+        w.part = take(4ul * d.BH * nsplit * (RP * d.D + RP));
+        w.S = take(4ul * d.BH * R * d.D);
+        w.z = take(4ul * d.BH * R);
+        if (d.bf16) {
+            w.sthi = take(2ul * d.BH * d.D * RP);
+            w.stlo = take(2ul * d.BH * d.D * RP);
+            w.zp = take(4ul * d.BH * RP);
+        }
+    }
+    w.total = off;
+    return w;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return SLR_OK;
+    if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return SLR_EWORKSPACE;
+    return SLR_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+#define SLR_TRY(expr)                                  \
+    do {                                               \
+        if ((expr) != hipSuccess) return SLR_EHIP;     \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* slr_status_string(int status) {
+    switch (status) {
+        case SLR_OK: return "SLR_OK: success";
+        case SLR_EINVAL: return "SLR_EINVAL: invalid shape, configuration, pointer or alignment";
+        case SLR_EUNSUPPORTED: return "SLR_EUNSUPPORTED: valid arguments outside the built kernel set";
+        case SLR_EWORKSPACE: return "SLR_EWORKSPACE: workspace missing, misaligned or too small";
+        case SLR_EHIP: return "SLR_EHIP: a HIP runtime call or kernel launch failed";
+        default: return "unknown slr status";
+    }
+}
+
+int slr_workspace_bytes(int op, const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
+                        const slr_lowrank_cfg* lowrank, size_t* bytes) {
+    if (!bytes) return SLR_EINVAL;
+    Dims d;
+    RopeGeom g;
+    int st = check_shape(shape, &d);
+    if (st) return st;
+    if ((st = check_rope(rope, d, &g))) return st;
+    int nblk = 0, keep = 0, bs = 64, R = 0, RP = 32;
+    switch (op) {
+        case SLR_OP_ROPE3D:
+        case SLR_OP_DENSE:
+            nblk = (int)((d.L + bs - 1) / bs);
+            break;
+        case SLR_OP_SELECT:
+        case SLR_OP_ATTENTION:
+            if ((st = check_sparse(sparse, d, &nblk))) return st;
+            bs = sparse->block;
+            keep = sparse->keep;
+            break;
+        case SLR_OP_LOWRANK_SUMMARY:
+            break;
+        default:
+            return SLR_EINVAL;
+    }
+    if (op == SLR_OP_ATTENTION || op == SLR_OP_LOWRANK_SUMMARY) {
+        if (!lowrank) return SLR_EINVAL;
+        LrGeom lg;
+        // pointer fields are not needed for sizing
+        slr_lowrank_cfg probe = *lowrank;
+        float dummy[4] __attribute__((aligned(16)));
+        probe.Wq = probe.Wk = probe.gate = dummy;
+        probe.Et = probe.Eh = probe.Ew = dummy;
+        if ((st = check_lowrank(&probe, rope, d, op == SLR_OP_ATTENTION, &lg, &RP))) return st;
+        R = lowrank->rank;
+    }
+    *bytes = layout(op, d, g, bs, nblk, keep, R, RP).total;
+    return SLR_OK;
+}
+
+int slr_rope3d(const slr_shape* shape, const slr_rope_cfg* rope, const void* x, void* x_rot, void* ws,
+               size_t ws_bytes, void* stream) {
+    Dims d;
+    RopeGeom g;
+    int st = check_shape(shape, &d);
+    if (st) return st;
+    if ((st = check_rope(rope, d, &g))) return st;
+    if (!tensor_ok(x) || !tensor_ok(x_rot) || x == x_rot) return SLR_EINVAL;
+    const int bs = 64;
+    const int nblk = (int)((d.L + bs - 1) / bs);
+    Layout w = layout(SLR_OP_ROPE3D, d, g, bs, nblk, 0, 0, 32);
+    if ((st = check_ws(ws, ws_bytes, w.total))) return st;
+    hipStream_t s = (hipStream_t)stream;
+    float2* tab = at<float2>(ws, w.tab);
+    SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
+    SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, x, nullptr, x_rot, nullptr, nullptr, nullptr, tab, g, d.BH, d.L, d.L,
+                             bs, nblk, s));
+    return SLR_OK;
+}
+
+int slr_select_blocks(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse, const void* q,
+                      const void* k, int32_t* idx, void* q_rot, void* k_rot, void* ws, size_t ws_bytes,
+                      void* stream) {
+    Dims d;
+    RopeGeom g;
+    int nblk;
+    int st = check_shape(shape, &d);
+    if (st) return st;
+    if ((st = check_rope(rope, d, &g))) return st;
+    if ((st = check_sparse(sparse, d, &nblk))) return st;
+    if (!tensor_ok(q) || !tensor_ok(k) || !idx || !aligned(idx, 4)) return SLR_EINVAL;
+    if ((q_rot && !tensor_ok(q_rot)) || (k_rot && !tensor_ok(k_rot))) return SLR_EINVAL;
+    Layout w = layout(SLR_OP_SELECT, d, g, sparse->block, nblk, sparse->keep, 0, 32);
+    if ((st = check_ws(ws, ws_bytes, w.total))) return st;
+    hipStream_t s = (hipStream_t)stream;
+    float2* tab = at<float2>(ws, w.tab);
+    float* qbar = at<float>(ws, w.qbar);
+    float* kbar = at<float>(ws, w.kbar);
+    SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
+    SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, q_rot, k_rot, qbar, kbar, tab, g, d.BH, d.L, d.L, sparse->block,
+                             nblk, s));
+    SLR_TRY(launch_select((int)d.D, qbar, kbar, idx, d.BH, nblk, sparse->keep, s));
+    return SLR_OK;
+}
+
+namespace {
+
+// Shared by the summary entry point and the layer forward.
+int run_summary(const Dims& d, const RopeGeom& g, const LrGeom& lg, int RP, const slr_lowrank_cfg* lr, const void* k,
+                const void* v, void* ws, const Layout& w, float* S, float* z, bool want_st, hipStream_t s) {
+    int chunk, nsplit;
+    summary_split(d, &chunk, &nsplit);
+    const float2* tab = at<float2>(ws, w.tab);
+    uint16_t* wkt = d.bf16 ? at<uint16_t>(ws, w.wkt) : nullptr;
+    if (d.bf16) SLR_TRY(launch_lr_prep(lr->Wk, wkt, (int)d.H, (int)d.D, lg.R, RP, s));
+    const bool abspe = lr->mode == SLR_LR_ABS_PE;
+    float* part = at<float>(ws, w.part);
+    SLR_TRY(launch_lr_summary(d.bf16, (int)d.D, RP, abspe, k, v, lr->Wk, wkt, lr->Et, lr->Eh, lr->Ew, tab, lg, d.BH,
+                              d.L, (int)d.H, chunk, nsplit, part, s));
+    uint16_t* sthi = want_st ? at<uint16_t>(ws, w.sthi) : nullptr;
+    uint16_t* stlo = want_st ? at<uint16_t>(ws, w.stlo) : nullptr;
+    float* zp = want_st ? at<float>(ws, w.zp) : nullptr;
+    SLR_TRY(launch_lr_reduce(part, d.BH, nsplit, (int)d.D, lg.R, RP, S, z, sthi, stlo, zp, s));
+    (void)g;
+    return SLR_OK;
+}
+
+}  // namespace
+
+int slr_lowrank_summary(const slr_shape* shape, const slr_rope_cfg* rope, const slr_lowrank_cfg* lowrank,
+                        const void* k, const void* v, float* S, float* z, void* ws, size_t ws_bytes, void* stream) {
+    Dims d;
+    RopeGeom g;
+    LrGeom lg;
+    int RP;
+    int st = check_shape(shape, &d);
+    if (st) return st;
+    if ((st = check_rope(rope, d, &g))) return st;
+    if ((st = check_lowrank(lowrank, rope, d, false, &lg, &RP))) return st;
+    if (!tensor_ok(k) || !tensor_ok(v) || !S || !z || !aligned(S, 4) || !aligned(z, 4)) return SLR_EINVAL;
+    lg.rope = g;
+    Layout w = layout(SLR_OP_LOWRANK_SUMMARY, d, g, 64, 0, 0, lowrank->rank, RP);
+    if ((st = check_ws(ws, ws_bytes, w.total))) return st;
+    hipStream_t s = (hipStream_t)stream;
+    SLR_TRY(launch_rope_tables(at<float2>(ws, w.tab), g, rope->base, s));
+    return run_summary(d, g, lg, RP, lowrank, k, v, ws, w, S, z, false, s);
+}
+
+namespace {
+
+int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
+                  const slr_lowrank_cfg* lowrank, const void* q, const void* k, const void* v, void* out,
+                  int32_t* idx_out, void* o_sparse_out, void* o_lowrank_out, void* ws, size_t ws_bytes,
+                  void* const* events, void* stream) {
+    Dims d;
+    RopeGeom g;
+    LrGeom lg;
+    int nblk, RP;
+    int st = check_shape(shape, &d);
+    if (st) return st;
+    if ((st = check_rope(rope, d, &g))) return st;
+    if ((st = check_sparse(sparse, d, &nblk))) return st;
+    if ((st = check_lowrank(lowrank, rope, d, true, &lg, &RP))) return st;
+    if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out)) return SLR_EINVAL;
+    if (idx_out && !aligned(idx_out, 4)) return SLR_EINVAL;
+    if ((o_sparse_out && !tensor_ok(o_sparse_out)) || (o_lowrank_out && !tensor_ok(o_lowrank_out)))
+        return SLR_EINVAL;
+    lg.rope = g;
+    const int bs = sparse->block;
+    Layout w = layout(SLR_OP_ATTENTION, d, g, bs, nblk, sparse->keep, lowrank->rank, RP);
+    if ((st = check_ws(ws, ws_bytes, w.total))) return st;
+    hipStream_t s = (hipStream_t)stream;
+
+    float2* tab = at<float2>(ws, w.tab);
+    void* qr = at<void>(ws, w.qr);
+    void* kr = at<void>(ws, w.kr);
+    float* qbar = at<float>(ws, w.qbar);
+    float* kbar = at<float>(ws, w.kbar);
+    int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, w.idx);
+    float* S = at<float>(ws, w.S);
+    float* z = at<float>(ws, w.z);
+
+    auto mark = [&](int i) { return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess; };
+    SLR_TRY(mark(0));
+    SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
+    SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, qr, kr, qbar, kbar, tab, g, d.BH, d.L, (long)nblk * bs, bs, nblk,
+                             s));
+    SLR_TRY(mark(1));
+    SLR_TRY(launch_select((int)d.D, qbar, kbar, idx, d.BH, nblk, sparse->keep, s));
+    SLR_TRY(mark(2));
+    if ((st = run_summary(d, g, lg, RP, lowrank, k, v, ws, w, S, z, d.bf16 != 0, s))) return st;
+    uint16_t* wqt = nullptr;
+    if (d.bf16) {
+        wqt = at<uint16_t>(ws, w.wqt);
+        SLR_TRY(launch_lr_prep(lowrank->Wq, wqt, (int)d.H, (int)d.D, lg.R, RP, s));
+    }
+    SLR_TRY(mark(3));
+
+    FlashArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.qr = qr; a.kr = kr; a.v = v; a.idx = idx; a.q = q;
+    a.wqt = wqt; a.wq = lowrank->Wq;
+    a.st_hi = d.bf16 ? at<uint16_t>(ws, w.sthi) : nullptr;
+    a.st_lo = d.bf16 ? at<uint16_t>(ws, w.stlo) : nullptr;
+    a.S = S;
+    a.zp = d.bf16 ? at<float>(ws, w.zp) : z;
+    a.gate = lowrank->gate;
+    a.Et = lowrank->Et; a.Eh = lowrank->Eh; a.Ew = lowrank->Ew;
+    a.tab = tab;
+    a.g = lg;
+    a.out = out; a.o_sp = o_sparse_out; a.o_lr = o_lowrank_out;
+    a.L = d.L; a.H = (int)d.H; a.nblk = nblk; a.keep = sparse->keep;
+    a.scale = (float)(1.0 / std::sqrt((double)d.D));
+    a.eps = lowrank->eps;
+    a.nwg = d.BH * nblk;
+    const int lr_mode = lowrank->mode == SLR_LR_ABS_PE ? 2 : 1;
+    SLR_TRY(launch_flash(d.bf16, (int)d.D, bs, RP, lr_mode, false, a, d.BH, s));
+    SLR_TRY(mark(4));
+    return SLR_OK;
+}
+
+}  // namespace
+
+int slr_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
+                      const slr_lowrank_cfg* lowrank, const void* q, const void* k, const void* v, void* out,
+                      int32_t* idx_out, void* o_sparse_out, void* o_lowrank_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+    return attention_fwd(shape, rope, sparse, lowrank, q, k, v, out, idx_out, o_sparse_out, o_lowrank_out, ws,
+                         ws_bytes, nullptr, stream);
+}
+
+int slr_attention_fwd_staged(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
+                             const slr_lowrank_cfg* lowrank, const void* q, const void* k, const void* v, void* out,
+                             int32_t* idx_out, void* o_sparse_out, void* o_lowrank_out, void* ws, size_t ws_bytes,
+                             void* const events[5], void* stream) {
+    if (!events) return SLR_EINVAL;
+    for (int i = 0; i < 5; ++i)
+        if (!events[i]) return SLR_EINVAL;
+    return attention_fwd(shape, rope, sparse, lowrank, q, k, v, out, idx_out, o_sparse_out, o_lowrank_out, ws,
+                         ws_bytes, events, stream);
+}
+
+int slr_dense_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const void* q, const void* k,
+                            const void* v, void* out, void* ws, size_t ws_bytes, void* stream) {
+    Dims d;
+    RopeGeom g;
+    int st = check_shape(shape, &d);
+    if (st) return st;
+    if ((st = check_rope(rope, d, &g))) return st;
+    if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out)) return SLR_EINVAL;
+    const int bs = 64;
+    const long nb = (d.L + bs - 1) / bs;
+    if (d.BH * nb > 0x7fffffffL) return SLR_EUNSUPPORTED;
+    const int nblk = (int)nb;
+    Layout w = layout(SLR_OP_DENSE, d, g, bs, nblk, 0, 0, 32);
+    if ((st = check_ws(ws, ws_bytes, w.total))) return st;
+    hipStream_t s = (hipStream_t)stream;
+    float2* tab = at<float2>(ws, w.tab);
+    void* qr = at<void>(ws, w.qr);
+    void* kr = at<void>(ws, w.kr);
+    SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
+    SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, qr, kr, nullptr, nullptr, tab, g, d.BH, d.L, (long)nblk * bs, bs,
+                             nblk, s));
+    FlashArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.qr = qr; a.kr = kr; a.v = v; a.out = out;
+    a.L = d.L; a.H = (int)d.H; a.nblk = nblk; a.keep = nblk;
+    a.scale = (float)(1.0 / std::sqrt((double)d.D));
+    a.nwg = d.BH * nblk;
+    SLR_TRY(launch_flash(d.bf16, (int)d.D, bs, 32, 0, true, a, d.BH, s));
+    return SLR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Host-side launch wrappers of the libslr kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "slr_common.h"
+
+namespace slr {
+
+struct LrGeom {
+    RopeGeom rope;
+    int lp[3];
+    int R;
+};
+
+// Everything the fused sparse/dense flash kernel reads.
+struct FlashArgs {
+    const void* qr;          // [BH][nblk*BS][D] rotated q, zero rows past L
+    const void* kr;          // same layout, rotated k
+    const void* v;           // [BH][L][D]
+    const int32_t* idx;      // [BH][nblk][keep] (sparse only)
+    const void* q;           // raw q [BH][L][D] (low-rank readout)
+    const uint16_t* wqt;     // bf16 layers: W_q^T [H][RP][D]
+    const float* wq;         // fp32 layers: W_q [H][D][R]
+    const uint16_t* st_hi;   // bf16 layers: S^T hi/lo [BH][D][RP], r in slot16 order
+    const uint16_t* st_lo;
+    const float* S;          // fp32 layers: S [BH][R][D]
+    const float* zp;         // [BH][RP] (bf16 layers) or [BH][R] (fp32 layers)
+    const float* gate;       // [H]
+    const float *Et, *Eh, *Ew;
+    const float2* tab;
+    LrGeom g;
+    void* out;               // [BH][L][D]
+    void* o_sp;              // optional debug outputs, same layout
+    void* o_lr;
+    long L;
+    int H, nblk, keep;
+    float scale;             // 1/sqrt(D)
+    float eps;
+    long nwg;                // workgroups in the grid
+};
+
+hipError_t launch_rope_tables(float2* tab, const RopeGeom& g, double base, hipStream_t st);
+hipError_t launch_rope_pool(int dtype_bf16, int D, const void* q, const void* k, void* qo, void* ko, float* qbar,
+                            float* kbar, const float2* tab, const RopeGeom& g, long BH, long L, long out_rows,
+                            int bs, int nblk, hipStream_t st);
+int select_rows_per_wg(int nblk);
+size_t select_lds_bytes(int nblk);
+hipError_t launch_select(int D, const float* qbar, const float* kbar, int32_t* idx, long BH, int nblk, int keep,
+                         hipStream_t st);
+hipError_t launch_lr_prep(const float* W, uint16_t* Wt, int H, int D, int R, int RP, hipStream_t st);
+hipError_t launch_lr_summary(int dtype_bf16, int D, int RP, bool abspe, const void* k, const void* v,
+                             const float* W, const uint16_t* wkt, const float* Et, const float* Eh,
+                             const float* Ew, const float2* tab, const LrGeom& g, long BH, long L, int H, int chunk,
+                             int nsplit, float* part, hipStream_t st);
+hipError_t launch_lr_reduce(const float* part, long BH, int nsplit, int D, int R, int RP, float* S, float* z,
+                            uint16_t* st_hi, uint16_t* st_lo, float* zp, hipStream_t st);
+// lr_mode: 0 = no low-rank term (plain attention), 1 = rotary after phi, 2 = absolute PE
+hipError_t launch_flash(int dtype_bf16, int D, int BS, int RP, int lr_mode, bool dense, const FlashArgs& a,
+                        long BH, hipStream_t st);
+
+}  // namespace slr

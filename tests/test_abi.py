@@ -1,0 +1,145 @@
+"""The C ABI library loads, exports what include/slr.h declares, and rejects
+bad arguments on the host before any HIP call (so these run without a GPU).
+Pointers below are never dereferenced: every call is rejected first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_rank_attention_rope3d_amd import binding as B
+from sparse_rank_attention_rope3d_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "slr.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libslr.so not built")
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+MISALIGNED = 0x10008
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(slr_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert set(names) == set(B.EXPORTS)
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in (B.SLR_OK, B.SLR_EINVAL, B.SLR_EUNSUPPORTED, B.SLR_EWORKSPACE, B.SLR_EHIP):
+        assert B.status_string(code).startswith("SLR_")
+    assert "unknown" in B.status_string(12345)
+
+
+def _cfgs(layer=None):
+    layer = layer or synth.wan13b()
+    shape, rope, sparse = B.shape_of(layer), B.rope_of(layer), B.sparse_of(layer)
+    lr = B.SlrLowrankCfg(layer.rank, B.SLR_LR_ROPE_OUTSIDE, *layer.lr_pairs, 1e-6, FAKE, FAKE, FAKE, None, None, None)
+    return shape, rope, sparse, lr
+
+
+def _attn(shape, rope, sparse, lr, q=FAKE, k=FAKE, v=FAKE, out=FAKE, ws=None, ws_bytes=0, idx=None):
+    r = ctypes.byref
+    return B.lib().slr_attention_fwd(r(shape), r(rope), r(sparse), r(lr), q, k, v, out, idx, None, None, ws,
+                                     ws_bytes, None)
+
+
+def test_workspace_bytes_matches_layout_size():
+    shape, rope, sparse, lr = _cfgs()
+    n = B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lr)
+    layer = synth.wan13b()
+    rot = 2 * (layer.B * layer.H * layer.nblk * layer.block * layer.D * 2)   # q, k rotated copies
+    assert rot < n < rot + 64 * 2 ** 20
+    assert B.slr_workspace_bytes(B.SLR_OP_ROPE3D, shape, rope) < 2 ** 20
+    assert B.slr_workspace_bytes(B.SLR_OP_DENSE, shape, rope) >= rot
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("D", 96, B.SLR_EUNSUPPORTED), ("D", 7, B.SLR_EINVAL), ("B", 0, B.SLR_EINVAL), ("T", 0, B.SLR_EINVAL),
+    ("dtype", 5, B.SLR_EINVAL), ("H", 70000, B.SLR_EUNSUPPORTED)])
+def test_bad_shape(field, value, code):
+    shape, rope, sparse, lr = _cfgs()
+    setattr(shape, field, value)
+    assert _attn(shape, rope, sparse, lr) == code
+
+
+@pytest.mark.parametrize("pairs", [(22, 21, 20), (23, 21, 21), (-1, 33, 32)])
+def test_bad_rotary_pairs(pairs):
+    shape, rope, sparse, lr = _cfgs()
+    rope.pairs_t, rope.pairs_h, rope.pairs_w = pairs
+    assert _attn(shape, rope, sparse, lr) == B.SLR_EINVAL
+
+
+def test_bad_base():
+    shape, rope, sparse, lr = _cfgs()
+    rope.base = 1.0
+    assert _attn(shape, rope, sparse, lr) == B.SLR_EINVAL
+    rope.base = float("nan")
+    assert _attn(shape, rope, sparse, lr) == B.SLR_EINVAL
+
+
+@pytest.mark.parametrize("block,keep", [(48, 52), (64, 0), (64, 513), (16, 4)])
+def test_bad_sparse(block, keep):
+    shape, rope, sparse, lr = _cfgs()
+    sparse.block, sparse.keep = block, keep
+    assert _attn(shape, rope, sparse, lr) == B.SLR_EINVAL
+
+
+@pytest.mark.parametrize("change", ["rank", "pairs_sum", "pairs_axis", "mode", "eps", "wq", "abspe_tables"])
+def test_bad_lowrank(change):
+    shape, rope, sparse, lr = _cfgs()
+    if change == "rank":
+        lr.rank = 24
+    elif change == "pairs_sum":
+        lr.lr_pairs_t = 9
+    elif change == "pairs_axis":
+        rope.pairs_t, rope.pairs_h, rope.pairs_w = 2, 31, 31   # lr t pairs 8 > 2
+    elif change == "mode":
+        lr.mode = 3
+    elif change == "eps":
+        lr.eps = 0.0
+    elif change == "wq":
+        lr.Wq = None
+    elif change == "abspe_tables":
+        lr.mode = B.SLR_LR_ABS_PE
+    assert _attn(shape, rope, sparse, lr) == B.SLR_EINVAL
+
+
+def test_null_and_misaligned_tensors():
+    shape, rope, sparse, lr = _cfgs()
+    assert _attn(shape, rope, sparse, lr, q=None) == B.SLR_EINVAL
+    assert _attn(shape, rope, sparse, lr, v=MISALIGNED) == B.SLR_EINVAL
+    assert _attn(shape, rope, sparse, lr, out=None) == B.SLR_EINVAL
+    assert _attn(shape, rope, sparse, lr, idx=FAKE + 2) == B.SLR_EINVAL
+
+
+def test_workspace_missing_or_short():
+    shape, rope, sparse, lr = _cfgs()
+    need = B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lr)
+    assert _attn(shape, rope, sparse, lr) == B.SLR_EWORKSPACE
+    assert _attn(shape, rope, sparse, lr, ws=FAKE, ws_bytes=need - 1) == B.SLR_EWORKSPACE
+    assert _attn(shape, rope, sparse, lr, ws=FAKE + 16, ws_bytes=need) == B.SLR_EWORKSPACE  # not 256-aligned
+
+
+def test_other_entry_points_validate():
+    shape, rope, sparse, lr = _cfgs()
+    r = ctypes.byref
+    L = B.lib()
+    assert L.slr_rope3d(r(shape), r(rope), FAKE, FAKE, None, 0, None) == B.SLR_EINVAL      # aliasing
+    assert L.slr_rope3d(r(shape), r(rope), FAKE, FAKE + 16, None, 0, None) == B.SLR_EWORKSPACE
+    assert L.slr_select_blocks(r(shape), r(rope), r(sparse), FAKE, FAKE, None, None, None, None, 0,
+                               None) == B.SLR_EINVAL
+    assert L.slr_lowrank_summary(r(shape), r(rope), r(lr), FAKE, FAKE, None, FAKE, None, 0, None) == B.SLR_EINVAL
+    assert L.slr_dense_attention_fwd(r(shape), r(rope), FAKE, FAKE, MISALIGNED, FAKE, None, 0,
+                                     None) == B.SLR_EINVAL
+    n = ctypes.c_size_t()
+    assert L.slr_workspace_bytes(9, r(shape), r(rope), None, None, r(n)) == B.SLR_EINVAL
+    assert L.slr_workspace_bytes(B.SLR_OP_ATTENTION, r(shape), r(rope), None, r(lr), r(n)) == B.SLR_EINVAL
