@@ -160,7 +160,11 @@ def main() -> int:
     es = 2 if cfg.dtype == "bf16" else 4
     BHLD = cfg.B * cfg.H * cfg.L * cfg.D
     rows_pad = cfg.B * cfg.H * cfg.nblk * cfg.block * cfg.D
-    rope_bytes = 2 * BHLD * es + 2 * rows_pad * es + 2 * cfg.B * cfg.H * cfg.nblk * cfg.D * 4
+    # rotate + pool: read q, k (and v, for the [K | V^T] tiles of the bf16 D=128 path), write the
+    # rotated q, the k and V^T tiles (or rotated k) and the block means
+    tiled = cfg.dtype == "bf16" and cfg.D == 128 and cfg.block == 64
+    n_io = 3 if tiled else 2
+    rope_bytes = n_io * BHLD * es + n_io * rows_pad * es + 2 * cfg.B * cfg.H * cfg.nblk * cfg.D * 4
     summ_bytes = 2 * BHLD * es
     hbm = {
         "rope_pool": {"GB/s": rope_bytes / (stage_ms["rope_pool"] * 1e-3) / 1e9},

@@ -41,6 +41,125 @@ __device__ __forceinline__ long xcd_remap(long p, long n) {
     return x * per + (x < rem ? x : rem) + loc;
 }
 
+// Epilogue shared by the flash kernels: lane owns query row q0 + l32 and the
+// O^T accumulator dims 32db + 8(i/4) + 4hf + i%4. Normalises the sparse
+// branch, evaluates the low-rank readout rho(w)^T S / (w . z + eps) with
+// w = phi(q W_q [+ E]) on MFMA (hi/lo bf16 splits of w and S for ~fp32
+// accuracy), combines with the per-head gate and stores bf16 rows.
+template <int D, int RP, int LR>
+__device__ __forceinline__ void flash_epilogue(const FlashArgs& a, long bh, int head, long q0, float lsum,
+                                               const f32x16_t* oacc) {
+    constexpr int NS = D / 16;
+    constexpr int NDB = D / 32;
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
+    const long L = a.L;
+    const long qrow = q0 + l32;
+    const bool qval = qrow < L;
+    const float inv = 1.f / lsum;
+    float gsc = 0.f, rden = 0.f;
+    constexpr int NRB = RP / 32;
+    u32x4_t whi[NRB][2], wlo[NRB][2];
+    if (LR != 0) {
+        const uint16_t* qraw = (const uint16_t*)a.q + (bh * L + (qval ? qrow : 0)) * D;
+        f32x16_t wacc[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) wacc[rb][i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const u32x4_t qo2 = qval ? ldg16(qraw + 16 * s + 8 * hf) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                const u32x4_t wa = ldg16(a.wqt + ((long)head * RP + 32 * rb + l32) * D + 16 * s + 8 * hf);
+                wacc[rb] = mfma32(wa, qo2, wacc[rb]);
+            }
+        }
+        int crd[3] = {0, 0, 0};
+        if (qval) token_coords(qrow, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
+        const float* zp = a.zp + bh * RP;
+        float den = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            float w[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 32 * rb + 8 * (i >> 2) + 4 * hf + (i & 3);
+                const bool ok = qval && r < a.g.R;
+                float x = wacc[rb][i];
+                if (LR == 2 && ok) x += a.Et[crd[0] * a.g.R + r] + a.Eh[crd[1] * a.g.R + r] + a.Ew[crd[2] * a.g.R + r];
+                w[i] = ok ? phi_elu1(x) : 0.f;
+                den += w[i] * zp[r];
+            }
+            if (LR == 1) {
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    const int r = 32 * rb + 8 * (i >> 2) + 4 * hf + (i & 3);
+                    if (qval && r < a.g.R) {
+                        const float2 cs = lr_cossin_q(a.tab, a.g, r >> 1, crd);
+                        const float w0 = w[i], w1 = w[i + 1];
+                        w[i] = w0 * cs.x - w1 * cs.y;
+                        w[i + 1] = w0 * cs.y + w1 * cs.x;
+                    }
+                }
+            }
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float a0 = w[8 * h2 + 2 * i], a1 = w[8 * h2 + 2 * i + 1];
+                    const uint32_t hi = pack_bf2(a0, a1);
+                    whi[rb][h2][i] = hi;
+                    wlo[rb][h2][i] = pack_bf2(a0 - bf_lo(hi), a1 - bf_hi(hi));
+                }
+        }
+        den += wave_xor32(den);
+        rden = 1.f / (den + a.eps);
+        gsc = a.gate[head];
+    }
+    uint16_t* out = (uint16_t*)a.out + (bh * L + (qval ? qrow : 0)) * D;
+    uint16_t* osp = a.o_sp ? (uint16_t*)a.o_sp + (bh * L + (qval ? qrow : 0)) * D : nullptr;
+    uint16_t* olr = a.o_lr ? (uint16_t*)a.o_lr + (bh * L + (qval ? qrow : 0)) * D : nullptr;
+    // one 32-dim block at a time: num^T = S^T rho(w)^T (m = d, k = r, n = query), combine, store
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        f32x16_t nacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) nacc[i] = 0.f;
+        if (LR != 0) {
+            const long so = (bh * D + 32 * db + l32) * RP + 8 * hf;
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const u32x4_t sh = ldg16(a.st_hi + so + 32 * rb + 16 * h2);
+                    const u32x4_t sl = ldg16(a.st_lo + so + 32 * rb + 16 * h2);
+                    nacc = mfma32(sh, whi[rb][h2], nacc);
+                    nacc = mfma32(sh, wlo[rb][h2], nacc);
+                    nacc = mfma32(sl, whi[rb][h2], nacc);
+                }
+        }
+        if (qval) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = 32 * db + 8 * g4 + 4 * hf;
+                float vs[4], vl[4], vo[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    vs[i] = oacc[db][4 * g4 + i] * inv;
+                    vl[i] = LR != 0 ? nacc[4 * g4 + i] * rden : 0.f;
+                    vo[i] = vs[i] + gsc * vl[i];
+                }
+                *reinterpret_cast<u32x2_t*>(out + d0) = u32x2_t{pack_bf2(vo[0], vo[1]), pack_bf2(vo[2], vo[3])};
+                if (osp)
+                    *reinterpret_cast<u32x2_t*>(osp + d0) = u32x2_t{pack_bf2(vs[0], vs[1]), pack_bf2(vs[2], vs[3])};
+                if (olr)
+                    *reinterpret_cast<u32x2_t*>(olr + d0) = u32x2_t{pack_bf2(vl[0], vl[1]), pack_bf2(vl[2], vl[3])};
+            }
+        }
+    }
+}
+
 template <int D, int BS, int RP, int LR, bool DENSE>
 __global__ __launch_bounds__(BS * 2) void k_flash_bf16(FlashArgs a) {
     constexpr int NT = BS * 2;          // threads (BS/32 waves)
@@ -200,109 +319,199 @@ __global__ __launch_bounds__(BS * 2) void k_flash_bf16(FlashArgs a) {
         __syncthreads();
     }
 
-    // ---- epilogue: lane owns query row qrow, dims 32db + 8(i/4) + 4hf + i%4
-    const long qrow = (long)qb * BS + 32 * wave + l32;
-    const bool qval = qrow < L;
-    const float inv = 1.f / (l_run + wave_xor32(l_run));
-    float gsc = 0.f, rden = 0.f;
-    f32x16_t nacc[NDB];
-    if (LR != 0) {
-        constexpr int NRB = RP / 32;
-        const uint16_t* qraw = (const uint16_t*)a.q + (bh * L + (qval ? qrow : 0)) * D;
-        f32x16_t wacc[NRB];
+    flash_epilogue<D, RP, LR>(a, bh, head, (long)qb * BS + 32 * wave, l_run + wave_xor32(l_run), oacc);
+}
+
+
+// ---------------------------------------------------------------------------
+// Streaming variant for bf16, D = 128, 64-token blocks (every workload shape).
+//
+// Workgroup = 4 waves = one 64-row query block; wave w takes query rows
+// 32*(w&1).. and keys 32*(w>>1).. of every tile (two row halves x two key
+// halves), keeping its own running max / sum; the two key halves of a row
+// half are merged once at the end. Each kept key block is one contiguous
+// 32 KB tile [K | V^T] (written by the rotate kernel, bank-swizzled) that is
+// copied straight into LDS with 16-byte global->LDS loads; two LDS buffers
+// let the next tile stream in while the current one is consumed, so the
+// workgroup needs 64 KB and two workgroups (8 waves, 2 per SIMD) share a CU.
+// The running max is only raised when it grows by more than 2^8 (the
+// probabilities then stay <= 256, exact after the final normalisation), so
+// the accumulator rescale is rare.
+
+// s_waitcnt with only the vector-memory counter constrained (<= n outstanding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One kept tile: scores, online softmax and P V for this wave's quarter.
+// Kt / Vt point at the LDS copy of the tile.
+template <int NDB, int NS>
+__device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ Vt,
+                                          const u32x4_t* qop, f32x16_t* oacc, float& m_run, float& l_run,
+                                          float sl2, int kh, int l32, int hf, bool mask, long key0, long L) {
+    constexpr int D = 128, BS = 64;
+    f32x16_t sacc;
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+    const int key = 32 * kh + l32;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) wacc[rb][i] = 0.f;
+    for (int s = 0; s < NS; ++s) {
+        const int c = 2 * s + hf;
+        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(Kt + key * D + 8 * (c ^ (key & 15)));
+        sacc = mfma32(ka, qop[s], sacc);
+    }
+    if (mask) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const u32x4_t qo2 = qval ? ldg16(qraw + 16 * s + 8 * hf) : u32x4_t{0u, 0u, 0u, 0u};
+        for (int i = 0; i < 16; ++i)
+            if (key0 + 32 * kh + 8 * (i >> 2) + 4 * hf + (i & 3) >= L) sacc[i] = -INFINITY;
+    }
+    float mx = sacc[0];
 #pragma unroll
-            for (int rb = 0; rb < NRB; ++rb) {
-                const u32x4_t wa = ldg16(a.wqt + ((long)head * RP + 32 * rb + l32) * D + 16 * s + 8 * hf);
-                wacc[rb] = mfma32(wa, qo2, wacc[rb]);
-            }
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+    mx = fmaxf(mx, wave_xor32(mx)) * sl2;
+    if (__ballot(mx > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+    u32x4_t pop[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p0 = fast_exp2(fmaf(sacc[8 * h2 + 2 * i], sl2, -m_run));
+            const float p1 = fast_exp2(fmaf(sacc[8 * h2 + 2 * i + 1], sl2, -m_run));
+            l_run += p0 + p1;
+            pop[h2][i] = pack_bf2(p0, p1);
         }
-        int crd[3] = {0, 0, 0};
-        if (qval) token_coords(qrow, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
-        const float* zp = a.zp + bh * RP;
-        float den = 0.f;
-        u32x4_t whi[NRB][2], wlo[NRB][2];
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            float w[16];
+    for (int db = 0; db < NDB; ++db) {
+        const int d = 32 * db + l32;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = 32 * rb + 8 * (i >> 2) + 4 * hf + (i & 3);
-                const bool ok = qval && r < a.g.R;
-                float x = wacc[rb][i];
-                if (LR == 2 && ok) x += a.Et[crd[0] * a.g.R + r] + a.Eh[crd[1] * a.g.R + r] + a.Ew[crd[2] * a.g.R + r];
-                w[i] = ok ? phi_elu1(x) : 0.f;
-                den += w[i] * zp[r];
-            }
-            if (LR == 1) {
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) {
-                    const int r = 32 * rb + 8 * (i >> 2) + 4 * hf + (i & 3);
-                    if (qval && r < a.g.R) {
-                        const float2 cs = lr_cossin_q(a.tab, a.g, r >> 1, crd);
-                        const float w0 = w[i], w1 = w[i + 1];
-                        w[i] = w0 * cs.x - w1 * cs.y;
-                        w[i + 1] = w0 * cs.y + w1 * cs.x;
-                    }
-                }
-            }
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float a0 = w[8 * h2 + 2 * i], a1 = w[8 * h2 + 2 * i + 1];
-                    const uint32_t hi = pack_bf2(a0, a1);
-                    whi[rb][h2][i] = hi;
-                    wlo[rb][h2][i] = pack_bf2(a0 - bf_lo(hi), a1 - bf_hi(hi));
-                }
-        }
-        den += wave_xor32(den);
-        rden = 1.f / (den + a.eps);
-        gsc = a.gate[head];
-        // num^T = S^T rho(w)^T: m = d, k = r, n = query
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) nacc[db][i] = 0.f;
-            const long so = (bh * D + 32 * db + l32) * RP + 8 * hf;
-#pragma unroll
-            for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const u32x4_t sh = ldg16(a.st_hi + so + 32 * rb + 16 * h2);
-                    const u32x4_t sl = ldg16(a.st_lo + so + 32 * rb + 16 * h2);
-                    nacc[db] = mfma32(sh, whi[rb][h2], nacc[db]);
-                    nacc[db] = mfma32(sh, wlo[rb][h2], nacc[db]);
-                    nacc[db] = mfma32(sl, whi[rb][h2], nacc[db]);
-                }
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int kc = 4 * kh + 2 * h2 + hf;
+            const u32x4_t va = *reinterpret_cast<const u32x4_t*>(Vt + d * BS + 8 * (kc ^ ((d >> 1) & 7)));
+            oacc[db] = mfma32(va, pop[h2], oacc[db]);
         }
     }
-    if (!qval) return;
-    uint16_t* out = (uint16_t*)a.out + (bh * L + qrow) * D;
-    uint16_t* osp = a.o_sp ? (uint16_t*)a.o_sp + (bh * L + qrow) * D : nullptr;
-    uint16_t* olr = a.o_lr ? (uint16_t*)a.o_lr + (bh * L + qrow) * D : nullptr;
+}
+
+template <int RP, int LR, bool DENSE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_flash_tiled(
+    FlashArgs a, const int32_t* __restrict__ idx_all, const uint16_t* __restrict__ kvt_all) {
+    constexpr int D = 128, BS = 64;
+    constexpr int NS = D / 16;
+    constexpr int NDB = D / 32;
+    constexpr int LOADS = kTileElems * 2 / (256 * 16);  // 16-byte loads per thread per tile (8)
+    __shared__ __attribute__((aligned(16))) uint16_t buf0[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t buf1[kTileElems];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rh = wave & 1, kh = wave >> 1;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const long wid = xcd_remap(blockIdx.x, a.nwg);
+    const long bh = wid / a.nblk;
+    const int qb = (int)(wid % a.nblk);
+    const int head = (int)(bh % a.H);
+    const long L = a.L;
+    const int nblk = a.nblk;
+    const uint16_t* tiles = kvt_all + bh * (long)nblk * kTileElems + (long)tid * 8;
+    const int32_t* ix = DENSE ? nullptr : idx_all + (bh * nblk + qb) * (long)a.keep;
+    const int ntile = DENSE ? nblk : a.keep;
+    auto tile_of = [&](int n) -> int { return DENSE ? n : ix[n]; };
+
+    // B operand of S^T = K Q^T: query row 32rh + l32 of the block
+    const uint16_t* qr = (const uint16_t*)a.qr + (bh * (long)nblk * BS + (long)qb * BS + 32 * rh + l32) * D;
+    u32x4_t qop[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qop[s] = ldg16(qr + 16 * s + 8 * hf);
+
+    // the tile image in LDS equals its image in memory: thread tid moves
+    // 16-byte chunks tid, tid + 256, ...
+    u32x4_t stage[LOADS];
+    auto fetch = [&](int j) {
+        const uint16_t* src = tiles + (long)j * kTileElems;
+#pragma unroll
+        for (int m = 0; m < LOADS; ++m) stage[m] = ldg16(src + m * 256 * 8);
+    };
+    auto stash = [&](uint16_t* dst) {
+#pragma unroll
+        for (int m = 0; m < LOADS; ++m) *reinterpret_cast<u32x4_t*>(dst + (m * 256 + tid) * 8) = stage[m];
+    };
+
+    f32x16_t oacc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const int d0 = 32 * db + 8 * g4 + 4 * hf;
-            float vs[4], vl[4], vo[4];
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    float m_run = -1e30f, l_run = 0.f;   // log2-domain running max (scaled), partial row sum
+    const float sl2 = a.scale * kLog2e;
+    const bool ragged = (L % BS) != 0;
+
+    int jcur = tile_of(0);
+    fetch(jcur);
+    stash(buf0);
+    int jnext = 0;
+    if (ntile > 1) {
+        jnext = tile_of(1);
+        fetch(jnext);
+    }
+    __syncthreads();
+
+    // two tiles per trip: buf0 holds even tiles, buf1 odd ones; registers hold
+    // the tile after the one being consumed
+    for (int n = 0; n < ntile; n += 2) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                vs[i] = oacc[db][4 * g4 + i] * inv;
-                vl[i] = LR != 0 ? nacc[db][4 * g4 + i] * rden : 0.f;
-                vo[i] = vs[i] + gsc * vl[i];
+        for (int half = 0; half < 2; ++half) {
+            const int t = n + half;
+            if (t < ntile) {
+                uint16_t* cur = half ? buf1 : buf0;
+                uint16_t* nxt = half ? buf0 : buf1;
+                tile_step<NDB, NS>(cur, cur + BS * D, qop, oacc, m_run, l_run, sl2, kh, l32, hf,
+                                   ragged && jcur == nblk - 1, (long)jcur * BS, L);
+                if (t + 1 < ntile) stash(nxt);
+                __syncthreads();
+                if (t + 2 < ntile) {
+                    const int jfar = tile_of(t + 2);
+                    fetch(jfar);
+                    jcur = jnext;
+                    jnext = jfar;
+                } else {
+                    jcur = jnext;
+                }
             }
-            *reinterpret_cast<u32x2_t*>(out + d0) = u32x2_t{pack_bf2(vo[0], vo[1]), pack_bf2(vo[2], vo[3])};
-            if (osp) *reinterpret_cast<u32x2_t*>(osp + d0) = u32x2_t{pack_bf2(vs[0], vs[1]), pack_bf2(vs[2], vs[3])};
-            if (olr) *reinterpret_cast<u32x2_t*>(olr + d0) = u32x2_t{pack_bf2(vl[0], vl[1]), pack_bf2(vl[2], vl[3])};
         }
+    }
+
+    // ---- merge the two key halves of each row half through LDS
+    float* mrg = reinterpret_cast<float*>(buf0) + rh * (66 * 64);
+    if (kh == 1) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mrg[(16 * db + i) * 64 + lane] = oacc[db][i];
+        mrg[64 * 64 + lane] = m_run;
+        mrg[65 * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = mrg[64 * 64 + lane], l1 = mrg[65 * 64 + lane];
+    const float m = fmaxf(m_run, m1);
+    const float f0 = fast_exp2(m_run - m), f1 = fast_exp2(m1 - m);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = oacc[db][i] * f0 + mrg[(16 * db + i) * 64 + lane] * f1;
+    const float lsum = l_run * f0 + l1 * f1;
+    flash_epilogue<D, RP, LR>(a, bh, head, (long)qb * BS + 32 * rh, lsum + wave_xor32(lsum), oacc);
 }
 
 // fp32 layers: one thread per query row, K / V tiles staged in LDS, fp32
@@ -444,9 +653,21 @@ static hipError_t flash_f32_t(int lr_mode, bool dense, const FlashArgs& a, int B
     return hipGetLastError();
 }
 
+template <int RP>
+static hipError_t flash_tiled_t(int lr_mode, bool dense, const FlashArgs& a, hipStream_t st) {
+    dim3 grid((unsigned)a.nwg), blk(256);
+    if (dense) hipLaunchKernelGGL((k_flash_tiled<RP, 0, true>), grid, blk, 0, st, a, a.idx, a.kvt);
+    else if (lr_mode == 1) hipLaunchKernelGGL((k_flash_tiled<RP, 1, false>), grid, blk, 0, st, a, a.idx, a.kvt);
+    else if (lr_mode == 2) hipLaunchKernelGGL((k_flash_tiled<RP, 2, false>), grid, blk, 0, st, a, a.idx, a.kvt);
+    else hipLaunchKernelGGL((k_flash_tiled<RP, 0, false>), grid, blk, 0, st, a, a.idx, a.kvt);
+    return hipGetLastError();
+}
+
 hipError_t launch_flash(int dtype_bf16, int D, int BS, int RP, int lr_mode, bool dense, const FlashArgs& a, long BH,
                         hipStream_t st) {
     (void)BH;
+    if (dtype_bf16 && D == 128 && BS == 64 && a.kvt)
+        return RP == 64 ? flash_tiled_t<64>(lr_mode, dense, a, st) : flash_tiled_t<32>(lr_mode, dense, a, st);
     if (!dtype_bf16) {
         if (D == 64) return RP == 64 ? flash_f32_t<64, 64>(lr_mode, dense, a, BS, st)
                                      : flash_f32_t<64, 32>(lr_mode, dense, a, BS, st);

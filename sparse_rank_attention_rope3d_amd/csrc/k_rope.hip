@@ -67,12 +67,21 @@ template <> struct Io8<float> {
 // [L, out_rows) of the block are written as zeros, which pads the workspace
 // copy to whole blocks) and, when qbar is non-null, the block means of the
 // fp32 rotated values over valid tokens.
-template <typename TIO, int D>
+//
+// Tiled mode (bf16, D = 128, 64-token blocks; the layout the block-sparse
+// flash kernel streams): instead of a plain copy, rotated k and the
+// transposed v of every block go to one contiguous 32 KB tile
+// kv_tiles[bh][blk] = [ K (64 keys x 128 dims) | V^T (128 dims x 64 keys) ],
+// 16-byte chunks XOR-swizzled so the flash kernel's 16-byte LDS reads are
+// bank-conflict free, V^T keys in slot16 order (the MFMA accumulator's row
+// order), rows past L zero.
+template <typename TIO, int D, bool TILED>
 __global__ __launch_bounds__(256) void k_rope_pool(const TIO* __restrict__ q, const TIO* __restrict__ k,
                                                    TIO* __restrict__ q_out, TIO* __restrict__ k_out,
                                                    float* __restrict__ qbar, float* __restrict__ kbar,
                                                    const float2* __restrict__ tab, RopeGeom g, long L,
-                                                   long out_rows, int bs, int nblk) {
+                                                   long out_rows, int bs, int nblk, const TIO* __restrict__ v,
+                                                   uint16_t* __restrict__ kv_tiles) {
     constexpr int CH = D / 8;          // threads per row
     constexpr int RPP = 256 / CH;      // rows per pass
     const int tid = threadIdx.x;
@@ -99,6 +108,7 @@ __global__ __launch_bounds__(256) void k_rope_pool(const TIO* __restrict__ q, co
     const TIO* ks = two ? k + bh * L * D : nullptr;
     TIO* qo = q_out ? q_out + bh * out_rows * D : nullptr;
     TIO* ko = (two && k_out) ? k_out + bh * out_rows * D : nullptr;
+    uint16_t* tile = TILED ? kv_tiles + (bh * nblk + blk) * (long)kTileElems : nullptr;
 
     for (int r0 = 0; r0 < bs; r0 += RPP) {
         const long l = (long)blk * bs + r0 + rsub;
@@ -131,7 +141,44 @@ __global__ __launch_bounds__(256) void k_rope_pool(const TIO* __restrict__ q, co
             for (int i = 0; i < 8; ++i) xq[i] = 0.f;
         }
         if (qo) Io8<TIO>::store(qo + l * D + 8 * c, xq);
-        if (ko) Io8<TIO>::store(ko + l * D + 8 * c, xk);
+        if (TILED) {
+            const int r = r0 + rsub;
+            Io8<TIO>::store(reinterpret_cast<TIO*>(tile + r * D + 8 * (c ^ (r & 15))), xk);
+        } else if (ko) {
+            Io8<TIO>::store(ko + l * D + 8 * c, xk);
+        }
+    }
+
+    if (TILED) {
+        // V^T: thread takes 8 keys x 8 dims (keys = slots 8vh..8vh+7 of 16-group vG), transposes in
+        // registers and stores 8 rows of 16 bytes.
+        static_assert(!TILED || (D == 128 && sizeof(TIO) == 2), "tiled layout is bf16, D = 128");
+        if (tid < 128) {
+            const int vc = tid & 15, vg = tid >> 4, vG = vg >> 1, vh = vg & 1;
+            const uint16_t* vs = reinterpret_cast<const uint16_t*>(v) + bh * L * D;
+            uint32_t rows[8][4];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const long l = (long)blk * 64 + 16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2);
+                const u32x4_t w = l < L ? ldg16(vs + l * D + 8 * vc) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rows[e][i] = w[i];
+            }
+            uint16_t* vt = tile + 64 * D;
+            const int kc = 2 * vG + vh;
+#pragma unroll
+            for (int f = 0; f < 8; ++f) {
+                u32x4_t o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t a0 = rows[2 * i][f >> 1], a1 = rows[2 * i + 1][f >> 1];
+                    o[i] = (f & 1) ? __builtin_amdgcn_perm(a1, a0, 0x07060302u)
+                                   : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+                }
+                const int d = 8 * vc + f;
+                stg16(vt + d * 64 + 8 * (kc ^ ((d >> 1) & 7)), o);
+            }
+        }
     }
 
     if (qbar == nullptr) return;
@@ -166,8 +213,18 @@ static hipError_t rope_pool_t(const void* q, const void* k, void* qo, void* ko, 
                               const float2* tab, const RopeGeom& g, long BH, long L, long out_rows, int bs,
                               int nblk, hipStream_t st) {
     dim3 grid((unsigned)nblk, (unsigned)BH);
-    hipLaunchKernelGGL((k_rope_pool<TIO, D>), grid, dim3(256), 0, st, (const TIO*)q, (const TIO*)k, (TIO*)qo,
-                       (TIO*)ko, qbar, kbar, tab, g, L, out_rows, bs, nblk);
+    hipLaunchKernelGGL((k_rope_pool<TIO, D, false>), grid, dim3(256), 0, st, (const TIO*)q, (const TIO*)k, (TIO*)qo,
+                       (TIO*)ko, qbar, kbar, tab, g, L, out_rows, bs, nblk, (const TIO*)nullptr, (uint16_t*)nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_pool_tiled(const void* q, const void* k, const void* v, void* qo, uint16_t* kv_tiles,
+                                  float* qbar, float* kbar, const float2* tab, const RopeGeom& g, long BH, long L,
+                                  int nblk, hipStream_t st) {
+    dim3 grid((unsigned)nblk, (unsigned)BH);
+    hipLaunchKernelGGL((k_rope_pool<uint16_t, 128, true>), grid, dim3(256), 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (uint16_t*)qo, (uint16_t*)nullptr, qbar, kbar, tab, g, L, (long)nblk * 64,
+                       64, nblk, (const uint16_t*)v, kv_tiles);
     return hipGetLastError();
 }
 

@@ -108,8 +108,13 @@ void summary_split(const Dims& d, int* chunk, int* nsplit) {
 
 // Workspace layout (byte offsets, each 256-byte aligned).
 struct Layout {
-    size_t tab, qr, kr, qbar, kbar, idx, wqt, wkt, part, S, z, sthi, stlo, zp, total;
+    size_t tab, qr, kr, kvt, qbar, kbar, idx, wqt, wkt, part, S, z, sthi, stlo, zp, total;
+    bool tiled;
 };
+
+// bf16, D = 128, 64-token blocks: K and V^T go to contiguous per-block tiles
+// that the streaming flash kernel copies straight into LDS.
+bool use_tiles(const Dims& d, int bs) { return d.bf16 && d.D == 128 && bs == 64; }
 
 Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int keep, int R, int RP) {
     Layout w;
@@ -122,10 +127,16 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         w.kbar = take(4ul * d.BH * nblk * d.D);
         w.idx = take(4ul * d.BH * nblk * keep);
     }
+    w.tiled = false;
     if (op == SLR_OP_ATTENTION || op == SLR_OP_DENSE) {
         const size_t rows = (size_t)nblk * bs;
         w.qr = take((size_t)d.es * d.BH * rows * d.D);
-        w.kr = take((size_t)d.es * d.BH * rows * d.D);
+        if (use_tiles(d, bs)) {
+            w.tiled = true;
+            w.kvt = take(2ul * d.BH * nblk * kTileElems);
+        } else {
+            w.kr = take((size_t)d.es * d.BH * rows * d.D);
+        }
     }
     if (op == SLR_OP_ATTENTION || op == SLR_OP_LOWRANK_SUMMARY) {
         int chunk, nsplit;
@@ -331,7 +342,8 @@ int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sp
 
     float2* tab = at<float2>(ws, w.tab);
     void* qr = at<void>(ws, w.qr);
-    void* kr = at<void>(ws, w.kr);
+    void* kr = w.tiled ? nullptr : at<void>(ws, w.kr);
+    uint16_t* kvt = w.tiled ? at<uint16_t>(ws, w.kvt) : nullptr;
     float* qbar = at<float>(ws, w.qbar);
     float* kbar = at<float>(ws, w.kbar);
     int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, w.idx);
@@ -341,8 +353,11 @@ int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sp
     auto mark = [&](int i) { return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess; };
     SLR_TRY(mark(0));
     SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
-    SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, qr, kr, qbar, kbar, tab, g, d.BH, d.L, (long)nblk * bs, bs, nblk,
-                             s));
+    if (w.tiled)
+        SLR_TRY(launch_rope_pool_tiled(q, k, v, qr, kvt, qbar, kbar, tab, g, d.BH, d.L, nblk, s));
+    else
+        SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, qr, kr, qbar, kbar, tab, g, d.BH, d.L, (long)nblk * bs, bs,
+                                 nblk, s));
     SLR_TRY(mark(1));
     SLR_TRY(launch_select((int)d.D, qbar, kbar, idx, d.BH, nblk, sparse->keep, s));
     SLR_TRY(mark(2));
@@ -356,7 +371,7 @@ int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sp
 
     FlashArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.qr = qr; a.kr = kr; a.v = v; a.idx = idx; a.q = q;
+    a.qr = qr; a.kr = kr; a.kvt = kvt; a.v = v; a.idx = idx; a.q = q;
     a.wqt = wqt; a.wq = lowrank->Wq;
     a.st_hi = d.bf16 ? at<uint16_t>(ws, w.sthi) : nullptr;
     a.st_lo = d.bf16 ? at<uint16_t>(ws, w.stlo) : nullptr;
@@ -415,13 +430,17 @@ int slr_dense_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, co
     hipStream_t s = (hipStream_t)stream;
     float2* tab = at<float2>(ws, w.tab);
     void* qr = at<void>(ws, w.qr);
-    void* kr = at<void>(ws, w.kr);
+    void* kr = w.tiled ? nullptr : at<void>(ws, w.kr);
+    uint16_t* kvt = w.tiled ? at<uint16_t>(ws, w.kvt) : nullptr;
     SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
-    SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, qr, kr, nullptr, nullptr, tab, g, d.BH, d.L, (long)nblk * bs, bs,
-                             nblk, s));
+    if (w.tiled)
+        SLR_TRY(launch_rope_pool_tiled(q, k, v, qr, kvt, nullptr, nullptr, tab, g, d.BH, d.L, nblk, s));
+    else
+        SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, qr, kr, nullptr, nullptr, tab, g, d.BH, d.L, (long)nblk * bs,
+                                 bs, nblk, s));
     FlashArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.qr = qr; a.kr = kr; a.v = v; a.out = out;
+    a.qr = qr; a.kr = kr; a.kvt = kvt; a.v = v; a.out = out;
     a.L = d.L; a.H = (int)d.H; a.nblk = nblk; a.keep = nblk;
     a.scale = (float)(1.0 / std::sqrt((double)d.D));
     a.nwg = d.BH * nblk;

@@ -19,6 +19,7 @@ struct LrGeom {
 struct FlashArgs {
     const void* qr;          // [BH][nblk*BS][D] rotated q, zero rows past L
     const void* kr;          // same layout, rotated k
+    const uint16_t* kvt;     // tiled K / V^T (bf16, D = 128, 64-token blocks)
     const void* v;           // [BH][L][D]
     const int32_t* idx;      // [BH][nblk][keep] (sparse only)
     const void* q;           // raw q [BH][L][D] (low-rank readout)
@@ -46,6 +47,11 @@ hipError_t launch_rope_tables(float2* tab, const RopeGeom& g, double base, hipSt
 hipError_t launch_rope_pool(int dtype_bf16, int D, const void* q, const void* k, void* qo, void* ko, float* qbar,
                             float* kbar, const float2* tab, const RopeGeom& g, long BH, long L, long out_rows,
                             int bs, int nblk, hipStream_t st);
+// Tiled K / V^T layout of the block-sparse flash kernel (bf16, D = 128, 64-token blocks).
+constexpr int kTileElems = 2 * 64 * 128;
+hipError_t launch_rope_pool_tiled(const void* q, const void* k, const void* v, void* qo, uint16_t* kv_tiles,
+                                  float* qbar, float* kbar, const float2* tab, const RopeGeom& g, long BH, long L,
+                                  int nblk, hipStream_t st);
 int select_rows_per_wg(int nblk);
 size_t select_lds_bytes(int nblk);
 hipError_t launch_select(int D, const float* qbar, const float* kbar, int32_t* idx, long BH, int nblk, int keep,

@@ -56,10 +56,17 @@ def test_workspace_bytes_matches_layout_size():
     shape, rope, sparse, lr = _cfgs()
     n = B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lr)
     layer = synth.wan13b()
-    rot = 2 * (layer.B * layer.H * layer.nblk * layer.block * layer.D * 2)   # q, k rotated copies
+    # bf16, D = 128, 64-token blocks: rotated q plus per-block [K | V^T] tiles
+    rot = 3 * (layer.B * layer.H * layer.nblk * layer.block * layer.D * 2)
     assert rot < n < rot + 64 * 2 ** 20
     assert B.slr_workspace_bytes(B.SLR_OP_ROPE3D, shape, rope) < 2 ** 20
     assert B.slr_workspace_bytes(B.SLR_OP_DENSE, shape, rope) >= rot
+    # other shapes keep plain rotated q and k copies
+    small = synth.tiny()
+    n32 = B.slr_workspace_bytes(B.SLR_OP_ATTENTION, B.shape_of(small), B.rope_of(small), B.sparse_of(small),
+                                B.SlrLowrankCfg(small.rank, 0, *small.lr_pairs, 1e-6, FAKE, FAKE, FAKE, None, None,
+                                                None))
+    assert n32 >= 2 * small.B * small.H * small.nblk * small.block * small.D * 4
 
 
 @pytest.mark.parametrize("field,value,code", [
