@@ -111,6 +111,9 @@ def main() -> int:
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--cpu-blocks", type=int, default=160, help="query blocks the CPU oracle samples")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; used to scale "
+                         "the FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -122,6 +125,16 @@ def main() -> int:
     import torch
     from sparse_rank_attention_rope3d_amd import binding as B
     from sparse_rank_attention_rope3d_amd import synth
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * 2 ** 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "reps": 3}))
+        return 0
 
     cfg = synth.by_name(args.workload)
     print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)

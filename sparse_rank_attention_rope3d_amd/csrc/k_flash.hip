@@ -113,7 +113,7 @@ __device__ __forceinline__ void flash_epilogue(const FlashArgs& a, long bh, int 
                     wlo[rb][h2][i] = pack_bf2(a0 - bf_lo(hi), a1 - bf_hi(hi));
                 }
         }
-        den += wave_xor32(den);
+        den = sum_xor32(den);
         rden = 1.f / (den + a.eps);
         gsc = a.gate[head];
     }
@@ -326,62 +326,47 @@ __global__ __launch_bounds__(BS * 2) void k_flash_bf16(FlashArgs a) {
 // ---------------------------------------------------------------------------
 // Streaming variant for bf16, D = 128, 64-token blocks (every workload shape).
 //
-// Workgroup = 4 waves = one 64-row query block; wave w takes query rows
-// 32*(w&1).. and keys 32*(w>>1).. of every tile (two row halves x two key
-// halves), keeping its own running max / sum; the two key halves of a row
-// half are merged once at the end. Each kept key block is one contiguous
-// 32 KB tile [K | V^T] (written by the rotate kernel, bank-swizzled) that is
-// copied straight into LDS with 16-byte global->LDS loads; two LDS buffers
-// let the next tile stream in while the current one is consumed, so the
-// workgroup needs 64 KB and two workgroups (8 waves, 2 per SIMD) share a CU.
+// Each kept key block is one contiguous 32 KB tile in operand order (see the
+// rotate kernel): every 1 KB chunk is a wave's MFMA operand, so operands go
+// from memory straight into registers with fully coalesced 16-byte loads and
+// the loop needs neither LDS nor barriers. Workgroup = 2 waves = one 64-row
+// query block; wave kh takes the 32 keys of half kh of every tile for all 64
+// query rows, as two independent 32-row blocks (two MFMA chains to overlap
+// with the other block's softmax). Operands of the next tile are requested
+// while the current one is consumed. The two key halves of every row are
+// merged once at the end through LDS; each wave then finishes one row block.
 // The running max is only raised when it grows by more than 2^8 (the
 // probabilities then stay <= 256, exact after the final normalisation), so
 // the accumulator rescale is rare.
 
-// s_waitcnt with only the vector-memory counter constrained (<= n outstanding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+__device__ __forceinline__ void load_k_ops(u32x4_t* k, const uint16_t* __restrict__ tile, int kh, int lane) {
+    const uint16_t* kp = tile + ((kh * 8) * 64 + lane) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) k[i] = ldg16(kp + i * 512);
+}
+__device__ __forceinline__ void load_v_ops(u32x4_t* v, const uint16_t* __restrict__ tile, int kh, int lane) {
+    const uint16_t* vp = tile + 64 * 128 + ((kh * 8) * 64 + lane) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ldg16(vp + i * 512);
 }
 
-// One kept tile: scores, online softmax and P V for this wave's quarter.
-// Kt / Vt point at the LDS copy of the tile.
-template <int NDB, int NS>
-__device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ Vt,
-                                          const u32x4_t* qop, f32x16_t* oacc, float& m_run, float& l_run,
-                                          float sl2, int kh, int l32, int hf, bool mask, long key0, long L) {
-    constexpr int D = 128, BS = 64;
-    f32x16_t sacc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-    const int key = 32 * kh + l32;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const int c = 2 * s + hf;
-        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(Kt + key * D + 8 * (c ^ (key & 15)));
-        sacc = mfma32(ka, qop[s], sacc);
-    }
-    if (mask) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if (key0 + 32 * kh + 8 * (i >> 2) + 4 * hf + (i & 3) >= L) sacc[i] = -INFINITY;
-    }
+// online softmax of one 32-row block's scores -> bf16 probabilities
+__device__ __forceinline__ void softmax_block(f32x16_t& sacc, f32x16_t* oacc, float& m_run, float& l_run, float sl2,
+                                              u32x4_t* pop) {
     float mx = sacc[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-    mx = fmaxf(mx, wave_xor32(mx)) * sl2;
+    mx = max_xor32(mx) * sl2;
     if (__ballot(mx > m_run + 8.f)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = fast_exp2(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
     }
-    u32x4_t pop[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -391,25 +376,33 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Kt, const
             l_run += p0 + p1;
             pop[h2][i] = pack_bf2(p0, p1);
         }
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-        const int d = 32 * db + l32;
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            const int kc = 4 * kh + 2 * h2 + hf;
-            const u32x4_t va = *reinterpret_cast<const u32x4_t*>(Vt + d * BS + 8 * (kc ^ ((d >> 1) & 7)));
-            oacc[db] = mfma32(va, pop[h2], oacc[db]);
-        }
-    }
+}
+
+// Eight 16-byte LDS reads (1 KB apart) into registers; the block waits for
+// them itself, so no read is left in flight when it ends.
+__device__ __forceinline__ void lds_read8(u32x4_t* r, const uint16_t* lds_base) {
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds_base;
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %4, %8 offset:4096\n\t"
+        "ds_read_b128 %5, %8 offset:5120\n\t"
+        "ds_read_b128 %6, %8 offset:6144\n\t"
+        "ds_read_b128 %7, %8 offset:7168\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7])
+        : "v"(a)
+        : "memory");
 }
 
 template <int RP, int LR, bool DENSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_flash_tiled(
     FlashArgs a, const int32_t* __restrict__ idx_all, const uint16_t* __restrict__ kvt_all) {
     constexpr int D = 128, BS = 64;
-    constexpr int NS = D / 16;
-    constexpr int NDB = D / 32;
-    constexpr int LOADS = kTileElems * 2 / (256 * 16);  // 16-byte loads per thread per tile (8)
+    constexpr int LOADS = kTileElems * 2 / (256 * 16);  // 16-byte copies per thread per tile (8)
+    // two tile buffers; the first is reused as the key-half exchange area at the end
     __shared__ __attribute__((aligned(16))) uint16_t buf0[kTileElems];
     __shared__ __attribute__((aligned(16))) uint16_t buf1[kTileElems];
 
@@ -429,89 +422,95 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto tile_of = [&](int n) -> int { return DENSE ? n : ix[n]; };
 
     // B operand of S^T = K Q^T: query row 32rh + l32 of the block
-    const uint16_t* qr = (const uint16_t*)a.qr + (bh * (long)nblk * BS + (long)qb * BS + 32 * rh + l32) * D;
-    u32x4_t qop[NS];
+    u32x4_t qop[8];
+    const uint16_t* qr = (const uint16_t*)a.qr + (bh * (long)nblk * BS + (long)qb * BS + 32 * rh + l32) * D + 8 * hf;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qop[s] = ldg16(qr + 16 * s + 8 * hf);
+    for (int s = 0; s < 8; ++s) qop[s] = ldg16(qr + 16 * s);
+    wait_vmcnt<0>();
 
-    // the tile image in LDS equals its image in memory: thread tid moves
-    // 16-byte chunks tid, tid + 256, ...
-    u32x4_t stage[LOADS];
-    auto fetch = [&](int j) {
+    // tile j -> LDS: the LDS image equals the memory image (operand order)
+    auto issue = [&](int j, uint16_t* dst) {
         const uint16_t* src = tiles + (long)j * kTileElems;
 #pragma unroll
-        for (int m = 0; m < LOADS; ++m) stage[m] = ldg16(src + m * 256 * 8);
-    };
-    auto stash = [&](uint16_t* dst) {
-#pragma unroll
-        for (int m = 0; m < LOADS; ++m) *reinterpret_cast<u32x4_t*>(dst + (m * 256 + tid) * 8) = stage[m];
+        for (int m = 0; m < LOADS; ++m)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(src + m * 256 * 8),
+                (__attribute__((address_space(3))) void*)(dst + (m * 256 + wave * 64) * 8), 16, 0, 0);
     };
 
-    f32x16_t oacc[NDB];
+    f32x16_t oacc[4];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    float m_run = -1e30f, l_run = 0.f;   // log2-domain running max (scaled), partial row sum
+    float m_run = -1e30f, l_run = 0.f;   // log2-domain (scaled) running max, partial row sum
     const float sl2 = a.scale * kLog2e;
     const bool ragged = (L % BS) != 0;
 
     int jcur = tile_of(0);
-    fetch(jcur);
-    stash(buf0);
-    int jnext = 0;
-    if (ntile > 1) {
-        jnext = tile_of(1);
-        fetch(jnext);
-    }
-    __syncthreads();
+    issue(jcur, buf0);
+    if (ntile > 1) issue(tile_of(1), buf1);
 
-    // two tiles per trip: buf0 holds even tiles, buf1 odd ones; registers hold
-    // the tile after the one being consumed
+    // two tiles per trip: buf0 holds even tiles, buf1 odd ones; tile t + 2 is
+    // requested as soon as every wave is done with tile t's buffer
     for (int n = 0; n < ntile; n += 2) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int t = n + half;
             if (t < ntile) {
                 uint16_t* cur = half ? buf1 : buf0;
-                uint16_t* nxt = half ? buf0 : buf1;
-                tile_step<NDB, NS>(cur, cur + BS * D, qop, oacc, m_run, l_run, sl2, kh, l32, hf,
-                                   ragged && jcur == nblk - 1, (long)jcur * BS, L);
-                if (t + 1 < ntile) stash(nxt);
-                __syncthreads();
-                if (t + 2 < ntile) {
-                    const int jfar = tile_of(t + 2);
-                    fetch(jfar);
-                    jcur = jnext;
-                    jnext = jfar;
-                } else {
-                    jcur = jnext;
+                if (t + 1 < ntile) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
+                __builtin_amdgcn_s_barrier();
+                u32x4_t op[8];
+                lds_read8(op, cur + ((kh * 8) * 64 + lane) * 8);                 // K chunks (kh, s)
+                f32x16_t sacc;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) sacc = mfma32(op[s], qop[s], sacc);
+                if (ragged && jcur == nblk - 1) {
+                    const long key0 = (long)jcur * BS + 32 * kh;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (key0 + 8 * (i >> 2) + 4 * hf + (i & 3) >= L) sacc[i] = -INFINITY;
                 }
+                u32x4_t pop[2];
+                softmax_block(sacc, oacc, m_run, l_run, sl2, pop);
+                lds_read8(op, cur + 64 * 128 + ((kh * 8) * 64 + lane) * 8);      // V^T chunks (kh, db, h2)
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) oacc[db] = mfma32(op[db * 2 + h2], pop[h2], oacc[db]);
+                __builtin_amdgcn_s_barrier();   // every wave is done with this buffer
+                if (t + 2 < ntile) issue(tile_of(t + 2), cur);
+                if (t + 1 < ntile) jcur = tile_of(t + 1);
             }
         }
     }
+    __syncthreads();
+    float (*mrg)[66 * 64] = reinterpret_cast<float (*)[66 * 64]>(&buf0[0]);
 
     // ---- merge the two key halves of each row half through LDS
-    float* mrg = reinterpret_cast<float*>(buf0) + rh * (66 * 64);
+    float* m_lds = mrg[rh];
     if (kh == 1) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mrg[(16 * db + i) * 64 + lane] = oacc[db][i];
-        mrg[64 * 64 + lane] = m_run;
-        mrg[65 * 64 + lane] = l_run;
+            for (int i = 0; i < 16; ++i) m_lds[(16 * db + i) * 64 + lane] = oacc[db][i];
+        m_lds[64 * 64 + lane] = m_run;
+        m_lds[65 * 64 + lane] = l_run;
     }
     __syncthreads();
     if (kh == 1) return;
-    const float m1 = mrg[64 * 64 + lane], l1 = mrg[65 * 64 + lane];
+    const float m1 = m_lds[64 * 64 + lane], l1 = m_lds[65 * 64 + lane];
     const float m = fmaxf(m_run, m1);
     const float f0 = fast_exp2(m_run - m), f1 = fast_exp2(m1 - m);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] = oacc[db][i] * f0 + mrg[(16 * db + i) * 64 + lane] * f1;
+        for (int i = 0; i < 16; ++i) oacc[db][i] = oacc[db][i] * f0 + m_lds[(16 * db + i) * 64 + lane] * f1;
     const float lsum = l_run * f0 + l1 * f1;
-    flash_epilogue<D, RP, LR>(a, bh, head, (long)qb * BS + 32 * rh, lsum + wave_xor32(lsum), oacc);
+    flash_epilogue<D, RP, LR>(a, bh, head, (long)qb * BS + 32 * rh, sum_xor32(lsum), oacc);
 }
 
 // fp32 layers: one thread per query row, K / V tiles staged in LDS, fp32

@@ -71,10 +71,13 @@ template <> struct Io8<float> {
 // Tiled mode (bf16, D = 128, 64-token blocks; the layout the block-sparse
 // flash kernel streams): instead of a plain copy, rotated k and the
 // transposed v of every block go to one contiguous 32 KB tile
-// kv_tiles[bh][blk] = [ K (64 keys x 128 dims) | V^T (128 dims x 64 keys) ],
-// 16-byte chunks XOR-swizzled so the flash kernel's 16-byte LDS reads are
-// bank-conflict free, V^T keys in slot16 order (the MFMA accumulator's row
-// order), rows past L zero.
+// kv_tiles[bh][blk] = [ K part 16 KB | V^T part 16 KB ] in operand order:
+// every 1 KB chunk is one wave's MFMA operand, lane l's 16 bytes at l * 16.
+//   K chunk (kh, s), kh = key half, s = 16-dim step:
+//       lane l holds K[key 32kh + l%32][dims 16s + 8(l/32) .. +7]
+//   V^T chunk (kh, db, h2), db = 32-dim block, h2 = 16-key group of the half:
+//       lane l holds V[keys (slot16 order) 32kh + 16h2 + 8(l/32) .. +7][dim 32db + l%32]
+// Keys past L are zero.
 template <typename TIO, int D, bool TILED>
 __global__ __launch_bounds__(256) void k_rope_pool(const TIO* __restrict__ q, const TIO* __restrict__ k,
                                                    TIO* __restrict__ q_out, TIO* __restrict__ k_out,
@@ -142,8 +145,9 @@ __global__ __launch_bounds__(256) void k_rope_pool(const TIO* __restrict__ q, co
         }
         if (qo) Io8<TIO>::store(qo + l * D + 8 * c, xq);
         if (TILED) {
-            const int r = r0 + rsub;
-            Io8<TIO>::store(reinterpret_cast<TIO*>(tile + r * D + 8 * (c ^ (r & 15))), xk);
+            const int r = r0 + rsub;   // key within the block; dims 8c .. 8c+7 = step c/2, lane half c%2
+            const int kh = r >> 5, ln = (r & 31) + 32 * (c & 1);
+            Io8<TIO>::store(reinterpret_cast<TIO*>(tile + ((kh * 8 + (c >> 1)) * 64 + ln) * 8), xk);
         } else if (ko) {
             Io8<TIO>::store(ko + l * D + 8 * c, xk);
         }
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(256) void k_rope_pool(const TIO* __restrict__ q, co
                 for (int i = 0; i < 4; ++i) rows[e][i] = w[i];
             }
             uint16_t* vt = tile + 64 * D;
-            const int kc = 2 * vG + vh;
+            const int kh = vG >> 1, h2 = vG & 1;   // 16-key group vG = 2kh + h2, lane half vh
 #pragma unroll
             for (int f = 0; f < 8; ++f) {
                 u32x4_t o;
@@ -176,7 +180,8 @@ __global__ __launch_bounds__(256) void k_rope_pool(const TIO* __restrict__ q, co
                                    : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
                 }
                 const int d = 8 * vc + f;
-                stg16(vt + d * 64 + 8 * (kc ^ ((d >> 1) & 7)), o);
+                const int ln = (d & 31) + 32 * vh;
+                stg16(vt + ((kh * 8 + (d >> 5) * 2 + h2) * 64 + ln) * 8, o);
             }
         }
     }

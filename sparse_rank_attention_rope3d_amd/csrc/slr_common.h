@@ -45,6 +45,17 @@ __device__ __forceinline__ f32x4_t mfma16f32(float a, float b, f32x4_t c) {
 
 // ---- wave helpers --------------------------------------------------------
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Pairwise reductions of lanes l and l ^ 32 with v_permlane32_swap (a VALU
+// op, no LDS round trip): the swap exchanges one 32-lane half between its
+// two operands, so combining both results gives every lane f(x[l], x[l^32]).
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ __forceinline__ int wave_sum_int(int x) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
@@ -53,6 +64,13 @@ __device__ __forceinline__ int wave_sum_int(int x) {
 // Swap with the adjacent lane (l ^ 1) through DPP quad_perm [1,0,3,2].
 __device__ __forceinline__ float lane_swap1(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
+// s_waitcnt with only the vector-memory counter constrained (<= N outstanding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // Order-preserving key of a float (larger float -> larger key); -0 maps to +0.
