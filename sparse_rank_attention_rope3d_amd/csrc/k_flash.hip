@@ -466,8 +466,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 f32x16_t sacc;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+                __builtin_amdgcn_s_setprio(1);   // matrix phase first when two waves share a SIMD
 #pragma unroll
                 for (int s = 0; s < 8; ++s) sacc = mfma32(op[s], qop[s], sacc);
+                __builtin_amdgcn_s_setprio(0);
                 if (ragged && jcur == nblk - 1) {
                     const long key0 = (long)jcur * BS + 32 * kh;
 #pragma unroll
@@ -477,10 +479,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 u32x4_t pop[2];
                 softmax_block(sacc, oacc, m_run, l_run, sl2, pop);
                 lds_read8(op, cur + 64 * 128 + ((kh * 8) * 64 + lane) * 8);      // V^T chunks (kh, db, h2)
+                __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                 for (int db = 0; db < 4; ++db)
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) oacc[db] = mfma32(op[db * 2 + h2], pop[h2], oacc[db]);
+                __builtin_amdgcn_s_setprio(0);
                 __builtin_amdgcn_s_barrier();   // every wave is done with this buffer
                 if (t + 2 < ntile) issue(tile_of(t + 2), cur);
                 if (t + 1 < ntile) jcur = tile_of(t + 1);

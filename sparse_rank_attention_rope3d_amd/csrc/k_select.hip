@@ -2,113 +2,172 @@
 //
 // RoLA (arXiv 2609.06712v3) Fig. 2 / §4.1: the sparse branch keeps the
 // top-k key blocks of every query block. Scores are
-// s_ij = qbar_i . kbar_j / sqrt(D) of the fp32 block means, computed in fp32
-// (fp32 MFMA); the k-th largest is found exactly with a bitwise search over
-// order-preserving 32-bit keys, ties go to the lower block index, and the
-// kept indices are written in ascending order.
+// s_ij = qbar_i . kbar_j / sqrt(D) of the fp32 block means; the k-th largest
+// is found exactly by bisection over order-preserving 32-bit keys, ties go to
+// the lower block index, and the kept indices are written in ascending order.
+//
+// Two kernels: a tiled score GEMM per (b, h) slice and a one-wave-per-row
+// top-k. The GEMM runs on bf16 MFMA with each fp32 operand split into a bf16
+// hi + lo pair (three products: hi*hi + hi*lo + lo*hi, fp32 accumulation);
+// the dropped lo*lo term and the residual of the split are ~2^-16 relative,
+// about 1e-7 on these scores -- two orders below the near-tie window the
+// selection is specified with.
 #include "slr_common.h"
 #include "slr_launch.h"
 
 namespace slr {
 
-// One workgroup (4 waves) = `qt` consecutive query blocks of one (b, h)
-// slice. Phase 1 fills an LDS score tile [qt][nblk] with 16x16x4 fp32 MFMAs
-// (rows beyond qt are zero operands); phase 2 gives each wave whole rows.
+// 8 fp32 values -> bf16 hi and lo parts (packed pairs)
+__device__ __forceinline__ void split8(const float* x, u32x4_t& hi, u32x4_t& lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t h = pack_bf2(x[2 * i], x[2 * i + 1]);
+        hi[i] = h;
+        lo[i] = pack_bf2(x[2 * i] - bf_lo(h), x[2 * i + 1] - bf_hi(h));
+    }
+}
+
+// One workgroup (4 waves) = a 64 x 64 tile of the score matrix of one slice;
+// wave (wi, wj) owns the 32 x 32 sub-tile. A = qbar rows (m = i, k = d),
+// B = kbar rows (k = d, n = j), both read straight from global memory.
 template <int D>
-__global__ __launch_bounds__(256) void k_select(const float* __restrict__ qbar, const float* __restrict__ kbar,
-                                                int32_t* __restrict__ idx, int nblk, int keep, int qt,
-                                                int ld, float scale) {
-    extern __shared__ float sc[];  // [qt][ld]
+__global__ __launch_bounds__(256) void k_block_scores(const float* __restrict__ qbar, const float* __restrict__ kbar,
+                                                      float* __restrict__ scores, int nblk, float scale) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const long bh = blockIdx.y;
-    const int i0 = blockIdx.x * qt;
-    const float* qb = qbar + bh * nblk * D;
-    const float* kb = kbar + bh * nblk * D;
-
-    // A operand: query block i0 + lane%16, dims 16p + 4*(lane/16) + {0..3}
-    const int arow = lane & 15, kq = 4 * (lane >> 4);
-    const bool aval = arow < qt && i0 + arow < nblk;
-    f32x4_t a[D / 16];
+    const int l32 = lane & 31, hf = lane >> 5;
+    const long bh = blockIdx.z;
+    const int i0 = blockIdx.y * 64 + 32 * (wave & 1);
+    const int j0 = blockIdx.x * 64 + 32 * (wave >> 1);
+    const float* qb = qbar + bh * (long)nblk * D;
+    const float* kb = kbar + bh * (long)nblk * D;
+    const int ia = i0 + l32, jb = j0 + l32;
+    f32x16_t acc;
 #pragma unroll
-    for (int p = 0; p < D / 16; ++p) {
-        a[p] = aval ? *reinterpret_cast<const f32x4_t*>(qb + (long)(i0 + arow) * D + 16 * p + kq)
-                    : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int c0 = wave * 16; c0 < nblk; c0 += 64) {
-        const int col = c0 + (lane & 15);
-        const bool bval = col < nblk;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-        for (int p = 0; p < D / 16; ++p) {
-            f32x4_t b = bval ? *reinterpret_cast<const f32x4_t*>(kb + (long)col * D + 16 * p + kq)
-                             : f32x4_t{0.f, 0.f, 0.f, 0.f};
-            acc = mfma16f32(a[p][0], b[0], acc);
-            acc = mfma16f32(a[p][1], b[1], acc);
-            acc = mfma16f32(a[p][2], b[2], acc);
-            acc = mfma16f32(a[p][3], b[3], acc);
+    for (int s = 0; s < D / 16; ++s) {
+        float xa[8], xb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { xa[e] = 0.f; xb[e] = 0.f; }
+        if (ia < nblk) {
+            const f32x4_t* p = reinterpret_cast<const f32x4_t*>(qb + (long)ia * D + 16 * s + 8 * hf);
+            const f32x4_t u = p[0], w = p[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { xa[e] = u[e]; xa[4 + e] = w[e]; }
         }
+        if (jb < nblk) {
+            const f32x4_t* p = reinterpret_cast<const f32x4_t*>(kb + (long)jb * D + 16 * s + 8 * hf);
+            const f32x4_t u = p[0], w = p[1];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int row = 4 * (lane >> 4) + v;
-            if (row < qt && bval) sc[row * ld + col] = acc[v] * scale;
+            for (int e = 0; e < 4; ++e) { xb[e] = u[e]; xb[4 + e] = w[e]; }
+        }
+        u32x4_t ah, al, bhi, blo;
+        split8(xa, ah, al);
+        split8(xb, bhi, blo);
+        acc = mfma32(ah, bhi, acc);
+        acc = mfma32(ah, blo, acc);
+        acc = mfma32(al, bhi, acc);
+    }
+    // lane holds rows i0 + 8(v/4) + 4hf + v%4 of column j0 + l32
+    if (jb < nblk) {
+        float* out = scores + bh * (long)nblk * nblk + jb;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int i = i0 + 8 * (v >> 2) + 4 * hf + (v & 3);
+            if (i < nblk) out[(long)i * nblk] = acc[v] * scale;
         }
     }
-    __syncthreads();
+}
 
+// Top-k of one score row per wave. KPL = keys per lane held in registers
+// (column j = 64 m + lane); KPL = 0 reads the row from memory on every pass.
+template <int KPL>
+__global__ __launch_bounds__(256) void k_topk_rows(const float* __restrict__ scores, int32_t* __restrict__ idx,
+                                                   long nrows, int nblk, int keep) {
+    const int lane = threadIdx.x & 63;
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= nrows) return;
+    const float* s = scores + row * nblk;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int row = wave; row < qt; row += 4) {
-        const int i = i0 + row;
-        if (i >= nblk) break;
-        const float* s = sc + row * ld;
-        // largest key value t with #(key >= t) >= keep, built bit by bit
-        uint32_t thr = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = thr | (1u << bit);
-            int cnt = 0;
-            for (int j = lane; j < nblk; j += 64) cnt += ordered_key(s[j]) >= cand;
-            if (wave_sum_int(cnt) >= keep) thr = cand;
+    uint32_t key[KPL > 0 ? KPL : 1];
+    if (KPL > 0) {
+#pragma unroll
+        for (int m = 0; m < KPL; ++m) {
+            const int j = 64 * m + lane;
+            key[m] = j < nblk ? ordered_key(s[j]) : 0u;   // 0 is below every finite key
         }
-        int gt = 0;
-        for (int j = lane; j < nblk; j += 64) gt += ordered_key(s[j]) > thr;
-        const int need = keep - wave_sum_int(gt);  // ties at the threshold to keep, lowest index first
-        int pos = 0, eqseen = 0;
-        int32_t* out = idx + (bh * nblk + i) * (long)keep;
+    }
+    auto count_ge = [&](uint32_t cand) -> int {
+        int cnt = 0;
+        if (KPL > 0) {
+#pragma unroll
+            for (int m = 0; m < KPL; ++m) cnt += __popcll(__ballot(key[m] >= cand));
+        } else {
+            for (int j0 = 0; j0 < nblk; j0 += 64) {
+                const int j = j0 + lane;
+                cnt += __popcll(__ballot(j < nblk && ordered_key(s[j]) >= cand));
+            }
+        }
+        return cnt;
+    };
+    // largest key value t with #(key >= t) >= keep, built bit by bit
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = thr | (1u << bit);
+        if (count_ge(cand) >= keep) thr = cand;
+    }
+    const int need = keep - (thr == 0xffffffffu ? 0 : count_ge(thr + 1));  // ties at thr, lowest index first
+    int32_t* out = idx + row * (long)keep;
+    int pos = 0, eqseen = 0;
+    auto emit = [&](int j, uint32_t k) {
+        const bool valid = j < nblk;
+        const bool isgt = valid && k > thr;
+        const bool iseq = valid && k == thr;
+        const uint64_t eqm = __ballot(iseq);
+        const bool sel = isgt || (iseq && eqseen + __popcll(eqm & below) < need);
+        const uint64_t selm = __ballot(sel);
+        if (sel) out[pos + __popcll(selm & below)] = j;
+        pos += __popcll(selm);
+        eqseen += __popcll(eqm);
+    };
+    if (KPL > 0) {
+#pragma unroll
+        for (int m = 0; m < (KPL > 0 ? KPL : 1); ++m)
+            if (64 * m < nblk) emit(64 * m + lane, key[m]);
+    } else {
         for (int j0 = 0; j0 < nblk; j0 += 64) {
             const int j = j0 + lane;
-            const uint32_t key = j < nblk ? ordered_key(s[j]) : 0u;
-            const bool isgt = j < nblk && key > thr;
-            const bool iseq = j < nblk && key == thr;
-            const uint64_t eqm = __ballot(iseq);
-            const bool sel = isgt || (iseq && eqseen + __popcll(eqm & below) < need);
-            const uint64_t selm = __ballot(sel);
-            if (sel) out[pos + __popcll(selm & below)] = j;
-            pos += __popcll(selm);
-            eqseen += __popcll(eqm);
+            emit(j, j < nblk ? ordered_key(s[j]) : 0u);
         }
     }
 }
 
-// rows per workgroup: as many as fit 64 KB of scores, at most 16
-int select_rows_per_wg(int nblk) {
-    const int ld = nblk + 1;
-    int qt = 16;
-    while (qt > 1 && (size_t)qt * ld * sizeof(float) > 64 * 1024) qt >>= 1;
-    return qt;
-}
+size_t select_scores_bytes(long BH, int nblk) { return sizeof(float) * (size_t)BH * nblk * nblk; }
 
-size_t select_lds_bytes(int nblk) { return (size_t)select_rows_per_wg(nblk) * (nblk + 1) * sizeof(float); }
-
-hipError_t launch_select(int D, const float* qbar, const float* kbar, int32_t* idx, long BH, int nblk, int keep,
-                         hipStream_t st) {
-    const int qt = select_rows_per_wg(nblk);
-    const int ld = nblk + 1;
-    const size_t lds = (size_t)qt * ld * sizeof(float);
-    dim3 grid((unsigned)((nblk + qt - 1) / qt), (unsigned)BH);
+hipError_t launch_select(int D, const float* qbar, const float* kbar, float* scores, int32_t* idx, long BH, int nblk,
+                         int keep, hipStream_t st) {
     const float scale = 1.0f / sqrtf((float)D);
+    const int nt = (nblk + 63) / 64;
+    dim3 g1((unsigned)nt, (unsigned)nt, (unsigned)BH);
     if (D == 64)
-        hipLaunchKernelGGL(k_select<64>, grid, dim3(256), lds, st, qbar, kbar, idx, nblk, keep, qt, ld, scale);
+        hipLaunchKernelGGL(k_block_scores<64>, g1, dim3(256), 0, st, qbar, kbar, scores, nblk, scale);
     else
-        hipLaunchKernelGGL(k_select<128>, grid, dim3(256), lds, st, qbar, kbar, idx, nblk, keep, qt, ld, scale);
+        hipLaunchKernelGGL(k_block_scores<128>, g1, dim3(256), 0, st, qbar, kbar, scores, nblk, scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long rows = BH * nblk;
+    dim3 g2((unsigned)((rows + 3) / 4));
+    const int kpl = (nblk + 63) / 64;
+    if (kpl <= 8)
+        hipLaunchKernelGGL(k_topk_rows<8>, g2, dim3(256), 0, st, scores, idx, rows, nblk, keep);
+    else if (kpl <= 16)
+        hipLaunchKernelGGL(k_topk_rows<16>, g2, dim3(256), 0, st, scores, idx, rows, nblk, keep);
+    else if (kpl <= 32)
+        hipLaunchKernelGGL(k_topk_rows<32>, g2, dim3(256), 0, st, scores, idx, rows, nblk, keep);
+    else if (kpl <= 64)
+        hipLaunchKernelGGL(k_topk_rows<64>, g2, dim3(256), 0, st, scores, idx, rows, nblk, keep);
+    else
+        hipLaunchKernelGGL(k_topk_rows<0>, g2, dim3(256), 0, st, scores, idx, rows, nblk, keep);
     return hipGetLastError();
 }
 

@@ -108,7 +108,7 @@ void summary_split(const Dims& d, int* chunk, int* nsplit) {
 
 // Workspace layout (byte offsets, each 256-byte aligned).
 struct Layout {
-    size_t tab, qr, kr, kvt, qbar, kbar, idx, wqt, wkt, part, S, z, sthi, stlo, zp, total;
+    size_t tab, qr, kr, kvt, qbar, kbar, scores, idx, wqt, wkt, part, S, z, sthi, stlo, zp, total;
     bool tiled;
 };
 
@@ -125,6 +125,7 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
     if (op == SLR_OP_SELECT || op == SLR_OP_ATTENTION) {
         w.qbar = take(4ul * d.BH * nblk * d.D);
         w.kbar = take(4ul * d.BH * nblk * d.D);
+        w.scores = take(select_scores_bytes(d.BH, nblk));
         w.idx = take(4ul * d.BH * nblk * keep);
     }
     w.tiled = false;
@@ -268,7 +269,7 @@ int slr_select_blocks(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
     SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, q_rot, k_rot, qbar, kbar, tab, g, d.BH, d.L, d.L, sparse->block,
                              nblk, s));
-    SLR_TRY(launch_select((int)d.D, qbar, kbar, idx, d.BH, nblk, sparse->keep, s));
+    SLR_TRY(launch_select((int)d.D, qbar, kbar, at<float>(ws, w.scores), idx, d.BH, nblk, sparse->keep, s));
     return SLR_OK;
 }
 
@@ -359,7 +360,7 @@ int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sp
         SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, qr, kr, qbar, kbar, tab, g, d.BH, d.L, (long)nblk * bs, bs,
                                  nblk, s));
     SLR_TRY(mark(1));
-    SLR_TRY(launch_select((int)d.D, qbar, kbar, idx, d.BH, nblk, sparse->keep, s));
+    SLR_TRY(launch_select((int)d.D, qbar, kbar, at<float>(ws, w.scores), idx, d.BH, nblk, sparse->keep, s));
     SLR_TRY(mark(2));
     if ((st = run_summary(d, g, lg, RP, lowrank, k, v, ws, w, S, z, d.bf16 != 0, s))) return st;
     uint16_t* wqt = nullptr;

@@ -52,10 +52,9 @@ constexpr int kTileElems = 2 * 64 * 128;
 hipError_t launch_rope_pool_tiled(const void* q, const void* k, const void* v, void* qo, uint16_t* kv_tiles,
                                   float* qbar, float* kbar, const float2* tab, const RopeGeom& g, long BH, long L,
                                   int nblk, hipStream_t st);
-int select_rows_per_wg(int nblk);
-size_t select_lds_bytes(int nblk);
-hipError_t launch_select(int D, const float* qbar, const float* kbar, int32_t* idx, long BH, int nblk, int keep,
-                         hipStream_t st);
+size_t select_scores_bytes(long BH, int nblk);
+hipError_t launch_select(int D, const float* qbar, const float* kbar, float* scores, int32_t* idx, long BH, int nblk,
+                         int keep, hipStream_t st);
 hipError_t launch_lr_prep(const float* W, uint16_t* Wt, int H, int D, int R, int RP, hipStream_t st);
 hipError_t launch_lr_summary(int dtype_bf16, int D, int RP, bool abspe, const void* k, const void* v,
                              const float* W, const uint16_t* wkt, const float* Et, const float* Eh,
