@@ -162,6 +162,10 @@ hipError_t launch_select(int D, const float* qbar, const float* kbar, float* sco
         hipLaunchKernelGGL(k_topk_rows<8>, g2, dim3(256), 0, st, scores, idx, rows, nblk, keep);
     else if (kpl <= 16)
         hipLaunchKernelGGL(k_topk_rows<16>, g2, dim3(256), 0, st, scores, idx, rows, nblk, keep);
+    else if (kpl <= 20)
+        hipLaunchKernelGGL(k_topk_rows<20>, g2, dim3(256), 0, st, scores, idx, rows, nblk, keep);
+    else if (kpl <= 24)
+        hipLaunchKernelGGL(k_topk_rows<24>, g2, dim3(256), 0, st, scores, idx, rows, nblk, keep);
     else if (kpl <= 32)
         hipLaunchKernelGGL(k_topk_rows<32>, g2, dim3(256), 0, st, scores, idx, rows, nblk, keep);
     else if (kpl <= 64)
