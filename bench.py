@@ -102,6 +102,49 @@ def cpu_baseline(cfg, blocks: int):
     return layer_s, {"measured_s": round(t2 - t0, 2), "sampled_blocks": int(len(qblocks))}
 
 
+def _time_ms(torch, fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def run_sweep(args, torch, B, synth):
+    """Keep fraction x rank sweep at the Wan2.1-1.3B shape: layer time of
+    every point and the dense kernel's time on the same inputs."""
+    points = synth.sweep()
+    base = points[0]
+    q, k, v, _ = make_device_inputs(base, torch)
+    shape, rope = B.shape_of(base), B.rope_of(base)
+    wsd = B.workspace(B.slr_workspace_bytes(B.SLR_OP_DENSE, shape, rope), "cuda")
+    out = torch.empty_like(q)
+    dense_ms = _time_ms(torch, lambda: B.slr_dense_attention_fwd(q, k, v, shape, rope, out=out, ws=wsd), 3)
+    del wsd
+    rows = []
+    for cfg in points:
+        params = {kk: torch.from_numpy(vv).cuda() for kk, vv in synth.lowrank_params(cfg).items()}
+        sparse, lowrank = B.sparse_of(cfg), B.lowrank_of(cfg, params)
+        ws = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lowrank), "cuda")
+        ms = _time_ms(torch, lambda: B.slr_attention_fwd(q, k, v, shape, rope, sparse, lowrank, out=out, ws=ws),
+                      args.steps)
+        F = cfg.flops()
+        row = {"keep": cfg.keep, "keep_pct": round(100.0 * cfg.keep / cfg.nblk, 1), "rank": cfg.rank,
+               "layer_ms": round(ms, 4), "dense_ms": round(dense_ms, 3), "speedup_vs_dense": round(dense_ms / ms, 2),
+               "effective_tflops": round((F["sparse"] + F["lowrank"] + F["select"]) / (ms * 1e-3) / 1e12, 1)}
+        rows.append(row)
+        print(f"[sweep] {row}", file=sys.stderr, flush=True)
+        del ws
+    with open(args.sweep, "w") as f:
+        for row in rows:
+            f.write(json.dumps(row) + "\n")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,8 +152,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan13b", choices=["wan13b", "wan14b", "hunyuan13b"])
     ap.add_argument("--dense-reps", type=int, default=3)
-    ap.add_argument("--cpu-blocks", type=int, default=160, help="query blocks the CPU oracle samples")
+    ap.add_argument("--cpu-blocks", type=int, default=512, help="query blocks the CPU oracle samples")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", metavar="JSONL", default=None,
+                    help="time every keep-fraction x rank point of the Wan2.1-1.3B sweep against the dense "
+                         "kernel, write one JSON object per point to JSONL and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; used to scale "
                          "the FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -135,6 +181,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "reps": 3}))
         return 0
+
+    if args.sweep:
+        return run_sweep(args, torch, B, synth)
 
     cfg = synth.by_name(args.workload)
     print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)

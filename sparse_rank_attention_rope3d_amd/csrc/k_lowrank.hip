@@ -13,6 +13,8 @@
 // bf16 hi + lo parts (about 16 mantissa bits), fp32 accumulation.
 // Split-L partials [BH][nsplit][RP*D + RP] are reduced in a fixed order, so
 // results are bitwise reproducible.
+#include <atomic>
+
 #include "slr_common.h"
 #include "slr_launch.h"
 
@@ -45,9 +47,15 @@ __device__ __forceinline__ float2 lr_cossin(const float2* __restrict__ tab, cons
 //   S (RP x D) += U^T V_sub                  MFMA m=r, n=d, k=tok
 // The U accumulator already has the token slots a 32x32x16 A operand needs
 // (slot16 order), so V is staged in LDS transposed [d][slot16(tok)].
-template <int D, int RP, bool ABSPE>
+//
+// TILEDV (D = 128, used inside the layer forward): V is not read from v but
+// from the rotate kernel's [K | V^T] tiles, whose V^T chunks already hold a
+// wave's B operand in this kernel's token-slot order, so no LDS transpose is
+// needed (the tail block's padded keys are zero there).
+template <int D, int RP, bool ABSPE, bool TILEDV>
 __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
+                                                         const uint16_t* __restrict__ kv_tiles, int nblk,
                                                          const uint16_t* __restrict__ wkt,
                                                          const float* __restrict__ Et,
                                                          const float* __restrict__ Eh,
@@ -58,7 +66,7 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
     constexpr int NDB = D / 32;    // d blocks
     constexpr int NKS = D / 16;    // k steps over d
     constexpr int VLD = 32 + 8;    // LDS row stride (elements) of V^T
-    __shared__ __attribute__((aligned(16))) uint16_t vt[4][D * VLD];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[TILEDV ? 1 : 4][TILEDV ? 8 : D * VLD];
     __shared__ float red[RP * D + RP];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -94,15 +102,26 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
     constexpr int VCH = D / 8;                 // dim chunks
     const int vc = lane % VCH, vg = lane / VCH;  // vg: 8-token group (valid if < 4)
     const int vG = vg >> 1, vh = vg & 1;
-    uint16_t* myvt = vt[wave];
+    uint16_t* myvt = vt[TILEDV ? 0 : wave];
+    const uint16_t* tiles = TILEDV ? kv_tiles + bh * (long)nblk * kTileElems : nullptr;
 
-    // every wave runs the same number of steps (the loop holds barriers)
-    const int nsteps = (int)((tok_hi - tok_lo + 127) / 128);
-    for (int step = 0; step < nsteps; ++step) {
-        const long t0 = tok_lo + 128L * step + 32 * wave;
+    // each wave walks its own 32-token sub-tiles (wave, wave + 4, ...) with
+    // its own LDS area, so the loop has no workgroup barrier
+    // rotation of this lane's feature pair (r = 32rb + l32 is fixed per lane)
+    int rax[NRB], rtab[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+        const int pr = (32 * rb + l32) >> 1;
+        int a = 0, j = pr;
+        if (pr >= g.lp[0] + g.lp[1]) { a = 2; j = pr - g.lp[0] - g.lp[1]; }
+        else if (pr >= g.lp[0]) { a = 1; j = pr - g.lp[0]; }
+        rax[rb] = a;
+        rtab[rb] = g.rope.tab_off[a] + j;
+    }
+    for (long t0 = tok_lo + 32 * wave; t0 < tok_hi; t0 += 128) {
         // ---- U = K_sub W_k
         const long tk = t0 + l32;
-        const bool tval = t0 < tok_hi && tk < tok_hi;
+        const bool tval = tk < tok_hi;
         f32x16_t uacc[NRB];
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
@@ -114,14 +133,19 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) uacc[rb] = mfma32(kop, wop[rb][s], uacc[rb]);
         }
-        // ---- V sub-tile -> LDS, transposed to [d][slot16(tok)]
-        if (vg < 4) {
+        // ---- V sub-tile -> this wave's LDS area, transposed to [d][slot16(tok)]
+        u32x4_t vop[TILEDV ? 8 : 1];
+        if (TILEDV) {
+            // sub-tile = key half ((t0 / 32) & 1) of block t0 / 64; chunk (kh, db, h2)
+            const uint16_t* vp = tiles + (t0 >> 6) * (long)kTileElems + 64 * 128 + ((((t0 >> 5) & 1) * 8) * 64 + lane) * 8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vop[i] = ldg16(vp + i * 512);
+        } else if (vg < 4) {
             uint32_t rows[8][4];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int tl = 16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2);  // token within sub-tile
-                const long tv = t0 + tl;
-                u32x4_t w = (t0 < tok_hi && tv < tok_hi) ? ldg16(vs + tv * D + 8 * vc) : u32x4_t{0u, 0u, 0u, 0u};
+                const long tv = t0 + 16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2);
+                const u32x4_t w = tv < tok_hi ? ldg16(vs + tv * D + 8 * vc) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) rows[e][i] = w[i];
             }
@@ -137,55 +161,77 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
                 stg16(myvt + (8 * vc + f) * VLD + 16 * vG + 8 * vh, o);
             }
         }
-        // ---- features: lane holds r = 32rb + l32, tokens 8(v/4) + 4hf + v%4
-        u32x4_t fhi[NRB][2], flo[NRB][2];
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            const int r = 32 * rb + l32;
-            float f[16];
+        // ---- features: lane holds r = 32rb + l32 for tokens t0 + 4hf + {0..3, 8..11, 16..19, 24..27}
+        int crd0[3];
+        token_coords(t0 + 4 * hf, g.rope.Hg, g.rope.Wg, crd0[0], crd0[1], crd0[2]);
+        float fv[NRB][16];
+        {
+            int ct = crd0[0], chh = crd0[1], cw = crd0[2];
+            int prev = 0;
 #pragma unroll
             for (int vv = 0; vv < 16; ++vv) {
-                const long tt = t0 + 8 * (vv >> 2) + 4 * hf + (vv & 3);
-                const bool ok = t0 < tok_hi && tt < tok_hi && r < g.R;
-                float x = uacc[rb][vv];
-                int crd[3] = {0, 0, 0};
-                if (ok) token_coords(tt, g.rope.Hg, g.rope.Wg, crd[0], crd[1], crd[2]);
-                if (ABSPE && ok) x += Et[crd[0] * g.R + r] + Eh[crd[1] * g.R + r] + Ew[crd[2] * g.R + r];
-                float u = ok ? phi_elu1(x) : 0.f;
-                zacc[rb] += u;
-                if (!ABSPE) {
-                    const float p = lane_swap1(u);  // partner dim r ^ 1
-                    float2 cs = make_float2(1.f, 0.f);
-                    if (ok) cs = lr_cossin(tab, g, r >> 1, crd);
-                    u = (r & 1) ? (p * cs.y + u * cs.x) : (u * cs.x - p * cs.y);
+                const int off = 8 * (vv >> 2) + (vv & 3);
+                coords_advance(ct, chh, cw, off - prev, g.rope.Hg, g.rope.Wg);
+                prev = off;
+                const long tt = t0 + 4 * hf + off;
+                const int crd[3] = {ct, chh, cw};
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb) {
+                    const int r = 32 * rb + l32;
+                    const bool ok = tt < tok_hi && r < g.R;
+                    float x = uacc[rb][vv];
+                    if (ABSPE && ok) x += Et[ct * g.R + r] + Eh[chh * g.R + r] + Ew[cw * g.R + r];
+                    float u = ok ? phi_elu1_fast(x) : 0.f;
+                    zacc[rb] += u;
+                    if (!ABSPE) {
+                        const float p = lane_swap1(u);  // partner dim r ^ 1
+                        float2 cs = make_float2(1.f, 0.f);
+                        if (ok) cs = tab[rtab[rb] + crd[rax[rb]] * g.rope.np[rax[rb]]];
+                        u = (r & 1) ? (p * cs.y + u * cs.x) : (u * cs.x - p * cs.y);
+                    }
+                    fv[rb][vv] = u;
                 }
-                f[vv] = u;
             }
+        }
+        u32x4_t fhi[NRB][2], flo[NRB][2];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
             for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float a0 = f[8 * ks2 + 2 * i], a1 = f[8 * ks2 + 2 * i + 1];
+                    const float a0 = fv[rb][8 * ks2 + 2 * i], a1 = fv[rb][8 * ks2 + 2 * i + 1];
                     const uint32_t hi = pack_bf2(a0, a1);
                     fhi[rb][ks2][i] = hi;
                     flo[rb][ks2][i] = pack_bf2(a0 - bf_lo(hi), a1 - bf_hi(hi));
                 }
+        // this wave's LDS writes before its reads (lanes read other lanes' data)
+        if (!TILEDV) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-        __syncthreads();
         // ---- S += F^T V
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int ks2 = 0; ks2 < 2; ++ks2) {
-                const u32x4_t vb = *reinterpret_cast<const u32x4_t*>(myvt + (32 * db + l32) * VLD + 16 * ks2 + 8 * hf);
+                const u32x4_t vb = TILEDV ? vop[(db * 2 + ks2) & (TILEDV ? 7 : 0)]
+                                          : *reinterpret_cast<const u32x4_t*>(myvt + (32 * db + l32) * VLD + 16 * ks2 + 8 * hf);
 #pragma unroll
                 for (int rb = 0; rb < NRB; ++rb) {
                     sacc[rb][db] = mfma32(fhi[rb][ks2], vb, sacc[rb][db]);
                     sacc[rb][db] = mfma32(flo[rb][ks2], vb, sacc[rb][db]);
                 }
             }
-        __syncthreads();
+        // reads done before the next sub-tile overwrites the area
+        if (!TILEDV) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
     }
+    __syncthreads();
 
     // ---- reduce the 4 waves in a fixed order, then write the partial
     // sacc[rb][db][vv]: r = 32rb + 8(vv/4) + 4hf + vv%4, d = 32db + l32
@@ -337,29 +383,88 @@ hipError_t launch_lr_prep(const float* W, uint16_t* Wt, int H, int D, int R, int
     return hipGetLastError();
 }
 
-template <int D, int RP>
-static hipError_t summary_bf16_t(bool abspe, const void* k, const void* v, const uint16_t* wkt, const float* Et,
-                                 const float* Eh, const float* Ew, const float2* tab, const LrGeom& g, long BH,
-                                 long L, int H, int chunk, int nsplit, float* part, hipStream_t st) {
+template <int D, int RP, bool TILEDV>
+static hipError_t summary_bf16_t(bool abspe, const void* k, const void* v, const uint16_t* kvt, int nblk,
+                                 const uint16_t* wkt, const float* Et, const float* Eh, const float* Ew,
+                                 const float2* tab, const LrGeom& g, long BH, long L, int H, int chunk, int nsplit,
+                                 float* part, hipStream_t st) {
     dim3 grid((unsigned)nsplit, (unsigned)BH);
     if (abspe)
-        hipLaunchKernelGGL((k_lr_summary_bf16<D, RP, true>), grid, dim3(256), 0, st, (const uint16_t*)k,
-                           (const uint16_t*)v, wkt, Et, Eh, Ew, tab, g, L, H, chunk, nsplit, part);
+        hipLaunchKernelGGL((k_lr_summary_bf16<D, RP, true, TILEDV>), grid, dim3(256), 0, st, (const uint16_t*)k,
+                           (const uint16_t*)v, kvt, nblk, wkt, Et, Eh, Ew, tab, g, L, H, chunk, nsplit, part);
     else
-        hipLaunchKernelGGL((k_lr_summary_bf16<D, RP, false>), grid, dim3(256), 0, st, (const uint16_t*)k,
-                           (const uint16_t*)v, wkt, Et, Eh, Ew, tab, g, L, H, chunk, nsplit, part);
+        hipLaunchKernelGGL((k_lr_summary_bf16<D, RP, false, TILEDV>), grid, dim3(256), 0, st, (const uint16_t*)k,
+                           (const uint16_t*)v, kvt, nblk, wkt, Et, Eh, Ew, tab, g, L, H, chunk, nsplit, part);
     return hipGetLastError();
 }
 
-hipError_t launch_lr_summary(int dtype_bf16, int D, int RP, bool abspe, const void* k, const void* v,
-                             const float* W, const uint16_t* wkt, const float* Et, const float* Eh,
-                             const float* Ew, const float2* tab, const LrGeom& g, long BH, long L, int H, int chunk,
-                             int nsplit, float* part, hipStream_t st) {
+// The kernel instance launch_lr_summary picks for these arguments.
+static const void* summary_kernel(int dtype_bf16, int D, int RP, bool abspe, bool tiled) {
+#define SLR_PICK(...) return reinterpret_cast<const void*>(&__VA_ARGS__)
     if (dtype_bf16) {
-        if (D == 64 && RP == 32) return summary_bf16_t<64, 32>(abspe, k, v, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk, nsplit, part, st);
-        if (D == 64) return summary_bf16_t<64, 64>(abspe, k, v, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk, nsplit, part, st);
-        if (RP == 32) return summary_bf16_t<128, 32>(abspe, k, v, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk, nsplit, part, st);
-        return summary_bf16_t<128, 64>(abspe, k, v, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk, nsplit, part, st);
+        if (tiled && D == 128) {
+            if (RP == 32) { if (abspe) SLR_PICK(k_lr_summary_bf16<128, 32, true, true>); SLR_PICK(k_lr_summary_bf16<128, 32, false, true>); }
+            if (abspe) SLR_PICK(k_lr_summary_bf16<128, 64, true, true>);
+            SLR_PICK(k_lr_summary_bf16<128, 64, false, true>);
+        }
+        if (D == 64 && RP == 32) { if (abspe) SLR_PICK(k_lr_summary_bf16<64, 32, true, false>); SLR_PICK(k_lr_summary_bf16<64, 32, false, false>); }
+        if (D == 64) { if (abspe) SLR_PICK(k_lr_summary_bf16<64, 64, true, false>); SLR_PICK(k_lr_summary_bf16<64, 64, false, false>); }
+        if (RP == 32) { if (abspe) SLR_PICK(k_lr_summary_bf16<128, 32, true, false>); SLR_PICK(k_lr_summary_bf16<128, 32, false, false>); }
+        if (abspe) SLR_PICK(k_lr_summary_bf16<128, 64, true, false>);
+        SLR_PICK(k_lr_summary_bf16<128, 64, false, false>);
+    }
+    if (D == 64 && RP == 32) SLR_PICK(k_lr_summary_f32<64, 32>);
+    if (D == 64) SLR_PICK(k_lr_summary_f32<64, 64>);
+    if (RP == 32) SLR_PICK(k_lr_summary_f32<128, 32>);
+    SLR_PICK(k_lr_summary_f32<128, 64>);
+#undef SLR_PICK
+}
+
+hipError_t lr_summary_slots(int dtype_bf16, int D, int RP, bool abspe, bool tiled, int* slots) {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cache[kMaxDev][32];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const int key = (dtype_bf16 ? 16 : 0) | (D == 128 ? 8 : 0) | (RP == 64 ? 4 : 0) | (abspe ? 2 : 0) | (tiled ? 1 : 0);
+    if (dev >= 0 && dev < kMaxDev) {
+        const int c = cache[dev][key].load(std::memory_order_relaxed);
+        if (c > 0) { *slots = c; return hipSuccess; }
+    }
+    int cus = 0, per = 0;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, summary_kernel(dtype_bf16, D, RP, abspe, tiled), 256,
+                                                          0)) != hipSuccess)
+        return e;
+    const int n = (cus > 0 ? cus : 1) * (per > 0 ? per : 1);
+    if (dev >= 0 && dev < kMaxDev) cache[dev][key].store(n, std::memory_order_relaxed);
+    *slots = n;
+    return hipSuccess;
+}
+
+hipError_t launch_lr_summary(int dtype_bf16, int D, int RP, bool abspe, const void* k, const void* v,
+                             const uint16_t* kvt, int nblk, const float* W, const uint16_t* wkt, const float* Et,
+                             const float* Eh, const float* Ew, const float2* tab, const LrGeom& g, long BH, long L,
+                             int H, int chunk, int nsplit, float* part, hipStream_t st) {
+    if (dtype_bf16) {
+        if (kvt && D == 128) {
+            if (RP == 32)
+                return summary_bf16_t<128, 32, true>(abspe, k, v, kvt, nblk, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk,
+                                                     nsplit, part, st);
+            return summary_bf16_t<128, 64, true>(abspe, k, v, kvt, nblk, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk,
+                                                 nsplit, part, st);
+        }
+        if (D == 64 && RP == 32)
+            return summary_bf16_t<64, 32, false>(abspe, k, v, nullptr, 0, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk,
+                                                 nsplit, part, st);
+        if (D == 64)
+            return summary_bf16_t<64, 64, false>(abspe, k, v, nullptr, 0, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk,
+                                                 nsplit, part, st);
+        if (RP == 32)
+            return summary_bf16_t<128, 32, false>(abspe, k, v, nullptr, 0, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk,
+                                                  nsplit, part, st);
+        return summary_bf16_t<128, 64, false>(abspe, k, v, nullptr, 0, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk,
+                                              nsplit, part, st);
     }
     dim3 grid((unsigned)nsplit, (unsigned)BH);
 #define SLR_SUMF32(DD, RR)                                                                                     \

@@ -96,14 +96,37 @@ int check_lowrank(const slr_lowrank_cfg* lr, const slr_rope_cfg* rope, const Dim
 
 bool tensor_ok(const void* p) { return p && aligned(p, 16); }
 
-// Split-L chunk of the summary: a multiple of 128 tokens, aiming at about
-// 1024 workgroups over all slices.
-void summary_split(const Dims& d, int* chunk, int* nsplit) {
-    long c = (d.BH * d.L + 1023) / 1024;
-    c = (c + 127) / 128 * 128;
-    if (c < 512) c = 512;
-    *chunk = (int)c;
-    *nsplit = (int)((d.L + c - 1) / c);
+// Split-L partition of the summary: each of the BH slices is cut into nsplit
+// chunks of a multiple of 128 tokens, one workgroup per chunk. At most
+// max(1, 2048 / BH) splits (this bounds the partial-sum workspace).
+int summary_split_cap(const Dims& d) {
+    long cap = 2048 / d.BH;
+    const long most = (d.L + 127) / 128;
+    if (cap > most) cap = most;
+    return cap < 1 ? 1 : (int)cap;
+}
+
+// The split that minimises the modelled time when `slots` workgroups run at
+// once: rounds of workgroups x (128-token steps per workgroup + a fixed
+// per-workgroup cost of about three steps); ties go to fewer splits.
+// slots = 0 gives the cap.
+void summary_split(const Dims& d, int slots, int* chunk, int* nsplit) {
+    const int cap = summary_split_cap(d);
+    long best_cost = -1, best_c = 0, best_n = 0;
+    for (int n = 1; n <= cap; ++n) {
+        const long c = ((d.L + n - 1) / n + 127) / 128 * 128;
+        const long ne = (d.L + c - 1) / c;
+        if (ne != n) continue;
+        const long rounds = slots > 0 ? (d.BH * ne + slots - 1) / slots : 1;
+        const long cost = rounds * (c / 128 + 3);
+        if (slots <= 0 || best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best_c = c;
+            best_n = ne;
+        }
+    }
+    *chunk = (int)best_c;
+    *nsplit = (int)best_n;
 }
 
 // Workspace layout (byte offsets, each 256-byte aligned).
@@ -140,8 +163,7 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         }
     }
     if (op == SLR_OP_ATTENTION || op == SLR_OP_LOWRANK_SUMMARY) {
-        int chunk, nsplit;
-        summary_split(d, &chunk, &nsplit);
+        const int nsplit = summary_split_cap(d);
         if (d.bf16) {
             w.wqt = take(2ul * d.H * RP * d.D);
             w.wkt = take(2ul * d.H * RP * d.D);
@@ -277,16 +299,18 @@ namespace {
 
 // Shared by the summary entry point and the layer forward.
 int run_summary(const Dims& d, const RopeGeom& g, const LrGeom& lg, int RP, const slr_lowrank_cfg* lr, const void* k,
-                const void* v, void* ws, const Layout& w, float* S, float* z, bool want_st, hipStream_t s) {
-    int chunk, nsplit;
-    summary_split(d, &chunk, &nsplit);
+                const void* v, const uint16_t* kvt, int nblk, void* ws, const Layout& w, float* S, float* z,
+                bool want_st, hipStream_t s) {
+    const bool abspe = lr->mode == SLR_LR_ABS_PE;
+    int slots = 0, chunk, nsplit;
+    SLR_TRY(lr_summary_slots(d.bf16, (int)d.D, RP, abspe, kvt != nullptr, &slots));
+    summary_split(d, slots, &chunk, &nsplit);
     const float2* tab = at<float2>(ws, w.tab);
     uint16_t* wkt = d.bf16 ? at<uint16_t>(ws, w.wkt) : nullptr;
     if (d.bf16) SLR_TRY(launch_lr_prep(lr->Wk, wkt, (int)d.H, (int)d.D, lg.R, RP, s));
-    const bool abspe = lr->mode == SLR_LR_ABS_PE;
     float* part = at<float>(ws, w.part);
-    SLR_TRY(launch_lr_summary(d.bf16, (int)d.D, RP, abspe, k, v, lr->Wk, wkt, lr->Et, lr->Eh, lr->Ew, tab, lg, d.BH,
-                              d.L, (int)d.H, chunk, nsplit, part, s));
+    SLR_TRY(launch_lr_summary(d.bf16, (int)d.D, RP, abspe, k, v, kvt, nblk, lr->Wk, wkt, lr->Et, lr->Eh, lr->Ew, tab,
+                              lg, d.BH, d.L, (int)d.H, chunk, nsplit, part, s));
     uint16_t* sthi = want_st ? at<uint16_t>(ws, w.sthi) : nullptr;
     uint16_t* stlo = want_st ? at<uint16_t>(ws, w.stlo) : nullptr;
     float* zp = want_st ? at<float>(ws, w.zp) : nullptr;
@@ -313,7 +337,7 @@ int slr_lowrank_summary(const slr_shape* shape, const slr_rope_cfg* rope, const 
     if ((st = check_ws(ws, ws_bytes, w.total))) return st;
     hipStream_t s = (hipStream_t)stream;
     SLR_TRY(launch_rope_tables(at<float2>(ws, w.tab), g, rope->base, s));
-    return run_summary(d, g, lg, RP, lowrank, k, v, ws, w, S, z, false, s);
+    return run_summary(d, g, lg, RP, lowrank, k, v, nullptr, 0, ws, w, S, z, false, s);
 }
 
 namespace {
@@ -362,7 +386,7 @@ int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sp
     SLR_TRY(mark(1));
     SLR_TRY(launch_select((int)d.D, qbar, kbar, at<float>(ws, w.scores), idx, d.BH, nblk, sparse->keep, s));
     SLR_TRY(mark(2));
-    if ((st = run_summary(d, g, lg, RP, lowrank, k, v, ws, w, S, z, d.bf16 != 0, s))) return st;
+    if ((st = run_summary(d, g, lg, RP, lowrank, k, v, kvt, nblk, ws, w, S, z, d.bf16 != 0, s))) return st;
     uint16_t* wqt = nullptr;
     if (d.bf16) {
         wqt = at<uint16_t>(ws, w.wqt);

@@ -82,6 +82,20 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
 
 // phi(x) = elu(x) + 1
 __device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : expf(x); }
+// the same with the hardware exp2 (relative error ~1e-7 for the x <= 0 branch; bf16 paths)
+__device__ __forceinline__ float phi_elu1_fast(float x) {
+    return x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// Grid coordinates of token l + delta given those of token l (t-major, then
+// h, then w), without divisions.
+__device__ __forceinline__ void coords_advance(int& t, int& h, int& w, int delta, int Hg, int Wg) {
+    w += delta;
+    while (w >= Wg) {
+        w -= Wg;
+        if (++h == Hg) { h = 0; ++t; }
+    }
+}
 
 // Position of key/token x (0..15) inside a 16-slot group in the order
 // {0,1,2,3,8,9,10,11,4,5,6,7,12,13,14,15}: lane half h of a 32x32x16 MFMA

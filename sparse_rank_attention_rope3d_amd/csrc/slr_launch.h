@@ -56,10 +56,15 @@ size_t select_scores_bytes(long BH, int nblk);
 hipError_t launch_select(int D, const float* qbar, const float* kbar, float* scores, int32_t* idx, long BH, int nblk,
                          int keep, hipStream_t st);
 hipError_t launch_lr_prep(const float* W, uint16_t* Wt, int H, int D, int R, int RP, hipStream_t st);
+// Workgroups of the summary kernel chosen for these arguments that the
+// current device holds at once (CUs x resident workgroups per CU; cached).
+hipError_t lr_summary_slots(int dtype_bf16, int D, int RP, bool abspe, bool tiled, int* slots);
+
+// kvt: when non-null (bf16, D = 128, 64-token blocks), V operands come from the [K | V^T] tiles
 hipError_t launch_lr_summary(int dtype_bf16, int D, int RP, bool abspe, const void* k, const void* v,
-                             const float* W, const uint16_t* wkt, const float* Et, const float* Eh,
-                             const float* Ew, const float2* tab, const LrGeom& g, long BH, long L, int H, int chunk,
-                             int nsplit, float* part, hipStream_t st);
+                             const uint16_t* kvt, int nblk, const float* W, const uint16_t* wkt, const float* Et,
+                             const float* Eh, const float* Ew, const float2* tab, const LrGeom& g, long BH, long L,
+                             int H, int chunk, int nsplit, float* part, hipStream_t st);
 hipError_t launch_lr_reduce(const float* part, long BH, int nsplit, int D, int R, int RP, float* S, float* z,
                             uint16_t* st_hi, uint16_t* st_lo, float* zp, hipStream_t st);
 // lr_mode: 0 = no low-rank term (plain attention), 1 = rotary after phi, 2 = absolute PE
