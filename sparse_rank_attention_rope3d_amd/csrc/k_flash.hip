@@ -447,50 +447,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float sl2 = a.scale * kLog2e;
     const bool ragged = (L % BS) != 0;
 
-    int jcur = tile_of(0);
-    issue(jcur, buf0);
-    if (ntile > 1) issue(tile_of(1), buf1);
+    issue(tile_of(0), buf0);
 
-    // two tiles per trip: buf0 holds even tiles, buf1 odd ones; tile t + 2 is
-    // requested as soon as every wave is done with tile t's buffer
-    for (int n = 0; n < ntile; n += 2) {
+    // two buffers: tile t lives in buffer t % 2. After the barrier that opens
+    // tile t every wave is done with tile t - 1, so tile t + 1 is requested
+    // into that buffer right away and lands while tile t is consumed.
+    auto step = [&](const int t, const uint16_t* cur, uint16_t* nxt) {
+        const int jcur = tile_of(t);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (t + 1 < ntile) issue(tile_of(t + 1), nxt);
+        u32x4_t op[8], vop[8];
+        lds_read8(op, cur + ((kh * 8) * 64 + lane) * 8);                 // K chunks (kh, s)
+        f32x16_t sacc;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int t = n + half;
-            if (t < ntile) {
-                uint16_t* cur = half ? buf1 : buf0;
-                if (t + 1 < ntile) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
-                __builtin_amdgcn_s_barrier();
-                u32x4_t op[8];
-                lds_read8(op, cur + ((kh * 8) * 64 + lane) * 8);                 // K chunks (kh, s)
-                f32x16_t sacc;
+        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+        __builtin_amdgcn_s_setprio(1);   // matrix phase first when two waves share a SIMD
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-                __builtin_amdgcn_s_setprio(1);   // matrix phase first when two waves share a SIMD
+        for (int s = 0; s < 8; ++s) sacc = mfma32(op[s], qop[s], sacc);
+        __builtin_amdgcn_s_setprio(0);
+        // V^T chunks (kh, db, h2): read while the score MFMAs run, into
+        // registers other than the K operands those MFMAs still read
+        lds_read8(vop, cur + 64 * 128 + ((kh * 8) * 64 + lane) * 8);
+        asm volatile("" ::"v"(op[0]), "v"(op[1]), "v"(op[2]), "v"(op[3]), "v"(op[4]), "v"(op[5]), "v"(op[6]),
+                     "v"(op[7]));
+        if (ragged && jcur == nblk - 1) {
+            const long key0 = (long)jcur * BS + 32 * kh;
 #pragma unroll
-                for (int s = 0; s < 8; ++s) sacc = mfma32(op[s], qop[s], sacc);
-                __builtin_amdgcn_s_setprio(0);
-                if (ragged && jcur == nblk - 1) {
-                    const long key0 = (long)jcur * BS + 32 * kh;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (key0 + 8 * (i >> 2) + 4 * hf + (i & 3) >= L) sacc[i] = -INFINITY;
-                }
-                u32x4_t pop[2];
-                softmax_block(sacc, oacc, m_run, l_run, sl2, pop);
-                lds_read8(op, cur + 64 * 128 + ((kh * 8) * 64 + lane) * 8);      // V^T chunks (kh, db, h2)
-                __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) oacc[db] = mfma32(op[db * 2 + h2], pop[h2], oacc[db]);
-                __builtin_amdgcn_s_setprio(0);
-                __builtin_amdgcn_s_barrier();   // every wave is done with this buffer
-                if (t + 2 < ntile) issue(tile_of(t + 2), cur);
-                if (t + 1 < ntile) jcur = tile_of(t + 1);
-            }
+            for (int i = 0; i < 16; ++i)
+                if (key0 + 8 * (i >> 2) + 4 * hf + (i & 3) >= L) sacc[i] = -INFINITY;
         }
+        u32x4_t pop[2];
+        softmax_block(sacc, oacc, m_run, l_run, sl2, pop);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) oacc[db] = mfma32(vop[db * 2 + h2], pop[h2], oacc[db]);
+        __builtin_amdgcn_s_setprio(0);
+    };
+    int n = 0;
+    for (; n + 1 < ntile; n += 2) {
+        step(n, buf0, buf1);
+        step(n + 1, buf1, buf0);
     }
+    if (n < ntile) step(n, buf0, buf1);
     __syncthreads();
     float (*mrg)[66 * 64] = reinterpret_cast<float (*)[66 * 64]>(&buf0[0]);
 
