@@ -327,28 +327,16 @@ __global__ __launch_bounds__(BS * 2) void k_flash_bf16(FlashArgs a) {
 // Streaming variant for bf16, D = 128, 64-token blocks (every workload shape).
 //
 // Each kept key block is one contiguous 32 KB tile in operand order (see the
-// rotate kernel): every 1 KB chunk is a wave's MFMA operand, so operands go
-// from memory straight into registers with fully coalesced 16-byte loads and
-// the loop needs neither LDS nor barriers. Workgroup = 2 waves = one 64-row
-// query block; wave kh takes the 32 keys of half kh of every tile for all 64
-// query rows, as two independent 32-row blocks (two MFMA chains to overlap
-// with the other block's softmax). Operands of the next tile are requested
-// while the current one is consumed. The two key halves of every row are
-// merged once at the end through LDS; each wave then finishes one row block.
-// The running max is only raised when it grows by more than 2^8 (the
-// probabilities then stay <= 256, exact after the final normalisation), so
-// the accumulator rescale is rare.
-
-__device__ __forceinline__ void load_k_ops(u32x4_t* k, const uint16_t* __restrict__ tile, int kh, int lane) {
-    const uint16_t* kp = tile + ((kh * 8) * 64 + lane) * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) k[i] = ldg16(kp + i * 512);
-}
-__device__ __forceinline__ void load_v_ops(u32x4_t* v, const uint16_t* __restrict__ tile, int kh, int lane) {
-    const uint16_t* vp = tile + 64 * 128 + ((kh * 8) * 64 + lane) * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = ldg16(vp + i * 512);
-}
+// rotate kernel): a 16 KB K part and a 16 KB V^T part whose 1 KB chunks are
+// each one wave's MFMA operand, so the LDS image equals the memory image and
+// is filled by direct global-to-LDS copies with no repacking. Workgroup = 4
+// waves = one 64-row query block; wave (rh, kh) owns query rows 32rh.. and
+// keys 32kh.. of every tile, with S^T = K Q^T computed so that each lane holds
+// one query row. The K and V^T parts stream through separate LDS rings (K
+// three deep, V^T two deep; one barrier per tile). The key halves of each row
+// are merged once at the end through LDS. The running max is only raised when
+// it grows by more than 2^8 (the probabilities then stay <= 256, exact after
+// the final normalisation), so the accumulator rescale is rare.
 
 // online softmax of one 32-row block's scores -> bf16 probabilities
 __device__ __forceinline__ void softmax_block(f32x16_t& sacc, f32x16_t* oacc, float& m_run, float& l_run, float sl2,
@@ -401,10 +389,11 @@ template <int RP, int LR, bool DENSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_flash_tiled(
     FlashArgs a, const int32_t* __restrict__ idx_all, const uint16_t* __restrict__ kvt_all) {
     constexpr int D = 128, BS = 64;
-    constexpr int LOADS = kTileElems * 2 / (256 * 16);  // 16-byte copies per thread per tile (8)
-    // two tile buffers; the first is reused as the key-half exchange area at the end
-    __shared__ __attribute__((aligned(16))) uint16_t buf0[kTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t buf1[kTileElems];
+    constexpr int PART = kTileElems / 2;                 // K or V^T part of a tile (elements)
+    constexpr int PLOADS = PART * 2 / (256 * 16);        // 16-byte copies per thread per part (4)
+    // K ring (3 parts) | V^T ring (2 parts), 80 KB; the start is reused as the
+    // key-half exchange area at the end
+    __shared__ __attribute__((aligned(16))) uint16_t lds[5 * PART];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -428,15 +417,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int s = 0; s < 8; ++s) qop[s] = ldg16(qr + 16 * s);
     wait_vmcnt<0>();
 
-    // tile j -> LDS: the LDS image equals the memory image (operand order)
-    auto issue = [&](int j, uint16_t* dst) {
-        const uint16_t* src = tiles + (long)j * kTileElems;
+    // part (0 = K, 1 = V^T) of tile j -> LDS: the LDS image equals the memory
+    // image (operand order)
+    auto issue = [&](int j, int part, uint16_t* dst) {
+        const uint16_t* src = tiles + (long)j * kTileElems + part * PART;
 #pragma unroll
-        for (int m = 0; m < LOADS; ++m)
+        for (int m = 0; m < PLOADS; ++m)
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void*)(src + m * 256 * 8),
                 (__attribute__((address_space(3))) void*)(dst + (m * 256 + wave * 64) * 8), 16, 0, 0);
     };
+    const int rd = ((kh * 8) * 64 + lane) * 8;   // this lane's operand chunks (kh, 0..7) within a part
 
     f32x16_t oacc[4];
 #pragma unroll
@@ -447,18 +438,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float sl2 = a.scale * kLog2e;
     const bool ragged = (L % BS) != 0;
 
-    issue(tile_of(0), buf0);
-
-    // two buffers: tile t lives in buffer t % 2. After the barrier that opens
-    // tile t every wave is done with tile t - 1, so tile t + 1 is requested
-    // into that buffer right away and lands while tile t is consumed.
-    auto step = [&](const int t, const uint16_t* cur, uint16_t* nxt) {
+    // K of tile t lives in K slot t % 3, V^T in V slot t % 2. The barrier that
+    // opens tile t also certifies that every wave is done with tile t - 1, so
+    // V^T of t + 1 and K of t + 2 are requested into those slots right away:
+    // K parts land two tiles ahead (they are needed first), V^T parts one.
+    issue(tile_of(0), 0, lds);
+    issue(tile_of(0), 1, lds + 3 * PART);
+    if (ntile > 1) issue(tile_of(1), 0, lds + PART);
+    int ks = 0;   // K slot of tile t
+    for (int t = 0; t < ntile; ++t) {
         const int jcur = tile_of(t);
-        wait_vmcnt<0>();
+        // outstanding in issue order: ..., V^T(t), K(t + 1) -> keep K(t + 1) in flight
+        if (t + 1 < ntile) wait_vmcnt<PLOADS>(); else wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        if (t + 1 < ntile) issue(tile_of(t + 1), nxt);
+        if (t + 1 < ntile) issue(tile_of(t + 1), 1, lds + (3 + ((t + 1) & 1)) * PART);
+        if (t + 2 < ntile) issue(tile_of(t + 2), 0, lds + (ks == 0 ? 2 : ks - 1) * PART);
+        const uint16_t* kcur = lds + ks * PART;
+        const uint16_t* vcur = lds + (3 + (t & 1)) * PART;
+        ks = ks == 2 ? 0 : ks + 1;
         u32x4_t op[8], vop[8];
-        lds_read8(op, cur + ((kh * 8) * 64 + lane) * 8);                 // K chunks (kh, s)
+        lds_read8(op, kcur + rd);                 // K chunks (kh, s)
         f32x16_t sacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
@@ -468,7 +467,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_s_setprio(0);
         // V^T chunks (kh, db, h2): read while the score MFMAs run, into
         // registers other than the K operands those MFMAs still read
-        lds_read8(vop, cur + 64 * 128 + ((kh * 8) * 64 + lane) * 8);
+        lds_read8(vop, vcur + rd);
         asm volatile("" ::"v"(op[0]), "v"(op[1]), "v"(op[2]), "v"(op[3]), "v"(op[4]), "v"(op[5]), "v"(op[6]),
                      "v"(op[7]));
         if (ragged && jcur == nblk - 1) {
@@ -485,15 +484,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) oacc[db] = mfma32(vop[db * 2 + h2], pop[h2], oacc[db]);
         __builtin_amdgcn_s_setprio(0);
-    };
-    int n = 0;
-    for (; n + 1 < ntile; n += 2) {
-        step(n, buf0, buf1);
-        step(n + 1, buf1, buf0);
     }
-    if (n < ntile) step(n, buf0, buf1);
     __syncthreads();
-    float (*mrg)[66 * 64] = reinterpret_cast<float (*)[66 * 64]>(&buf0[0]);
+    float (*mrg)[66 * 64] = reinterpret_cast<float (*)[66 * 64]>(&lds[0]);
 
     // ---- merge the two key halves of each row half through LDS
     float* m_lds = mrg[rh];
