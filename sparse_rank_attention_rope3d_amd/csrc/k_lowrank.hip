@@ -108,7 +108,8 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
     // each wave walks its own 32-token sub-tiles (wave, wave + 4, ...) with
     // its own LDS area, so the loop has no workgroup barrier
     // rotation of this lane's feature pair (r = 32rb + l32 is fixed per lane)
-    int rax[NRB], rtab[NRB];
+    // table row of this lane's pair: entry = base + (its axis coordinate) * stride
+    int rax[NRB], rbase[NRB], rstride[NRB];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
         const int pr = (32 * rb + l32) >> 1;
@@ -116,12 +117,19 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
         if (pr >= g.lp[0] + g.lp[1]) { a = 2; j = pr - g.lp[0] - g.lp[1]; }
         else if (pr >= g.lp[0]) { a = 1; j = pr - g.lp[0]; }
         rax[rb] = a;
-        rtab[rb] = g.rope.tab_off[a] + j;
+        rbase[rb] = (a == 0 ? g.rope.tab_off[0] : a == 1 ? g.rope.tab_off[1] : g.rope.tab_off[2]) + j;
+        rstride[rb] = a == 0 ? g.rope.np[0] : a == 1 ? g.rope.np[1] : g.rope.np[2];
     }
+    // Every load below is unconditional: rows past the chunk are clamped to
+    // its last token (their features are zeroed), so the loads of a sub-tile
+    // issue back to back instead of one predicated round trip each.
     for (long t0 = tok_lo + 32 * wave; t0 < tok_hi; t0 += 128) {
         // ---- U = K_sub W_k
         const long tk = t0 + l32;
-        const bool tval = tk < tok_hi;
+        const long tkc = tk < tok_hi ? tk : tok_hi - 1;
+        u32x4_t kop[NKS];
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) kop[s] = ldg16(ks + tkc * D + 16 * s + 8 * hf);
         f32x16_t uacc[NRB];
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
@@ -129,9 +137,8 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
             for (int i = 0; i < 16; ++i) uacc[rb][i] = 0.f;
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-            u32x4_t kop = tval ? ldg16(ks + tk * D + 16 * s + 8 * hf) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int rb = 0; rb < NRB; ++rb) uacc[rb] = mfma32(kop, wop[rb][s], uacc[rb]);
+            for (int rb = 0; rb < NRB; ++rb) uacc[rb] = mfma32(kop[s], wop[rb][s], uacc[rb]);
         }
         // ---- V sub-tile -> this wave's LDS area, transposed to [d][slot16(tok)]
         u32x4_t vop[TILEDV ? 8 : 1];
@@ -145,7 +152,7 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const long tv = t0 + 16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2);
-                const u32x4_t w = tv < tok_hi ? ldg16(vs + tv * D + 8 * vc) : u32x4_t{0u, 0u, 0u, 0u};
+                const u32x4_t w = ldg16(vs + (tv < tok_hi ? tv : tok_hi - 1) * D + 8 * vc);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) rows[e][i] = w[i];
             }
@@ -162,35 +169,60 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
             }
         }
         // ---- features: lane holds r = 32rb + l32 for tokens t0 + 4hf + {0..3, 8..11, 16..19, 24..27}
-        int crd0[3];
-        token_coords(t0 + 4 * hf, g.rope.Hg, g.rope.Wg, crd0[0], crd0[1], crd0[2]);
-        float fv[NRB][16];
+        // coordinates of the 16 tokens (division free after the first): the three
+        // axes for the absolute embeddings, else this lane's rotation axis only
+        int cT[16], cH[16], cW[16], cA[NRB][16];
         {
-            int ct = crd0[0], chh = crd0[1], cw = crd0[2];
-            int prev = 0;
+            int ct, chh, cw;
+            token_coords(t0 + 4 * hf, g.rope.Hg, g.rope.Wg, ct, chh, cw);
+            if (g.rope.Wg > 5) {   // steps are at most 5 tokens: one wrap of w at most
+#pragma unroll
+                for (int vv = 0; vv < 16; ++vv) {
+                    if (vv > 0) coords_step(ct, chh, cw, (vv & 3) ? 1 : 5, g.rope.Hg, g.rope.Wg);
+                    cT[vv] = ct; cH[vv] = chh; cW[vv] = cw;
+                }
+            } else {
+                for (int vv = 0; vv < 16; ++vv) {
+                    if (vv > 0) coords_advance(ct, chh, cw, (vv & 3) ? 1 : 5, g.rope.Hg, g.rope.Wg);
+                    cT[vv] = ct; cH[vv] = chh; cW[vv] = cw;
+                }
+            }
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv)
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb)
+                    cA[rb][vv] = rax[rb] == 2 ? cW[vv] : (rax[rb] == 1 ? cH[vv] : cT[vv]);
+        }
+        float fv[NRB][16];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            const int r = 32 * rb + l32;
+            // gathers first (all independent), arithmetic after
+            float2 cs[16];
+            float ev[16];
 #pragma unroll
             for (int vv = 0; vv < 16; ++vv) {
-                const int off = 8 * (vv >> 2) + (vv & 3);
-                coords_advance(ct, chh, cw, off - prev, g.rope.Hg, g.rope.Wg);
-                prev = off;
-                const long tt = t0 + 4 * hf + off;
-                const int crd[3] = {ct, chh, cw};
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) {
-                    const int r = 32 * rb + l32;
-                    const bool ok = tt < tok_hi && r < g.R;
-                    float x = uacc[rb][vv];
-                    if (ABSPE && ok) x += Et[ct * g.R + r] + Eh[chh * g.R + r] + Ew[cw * g.R + r];
-                    float u = ok ? phi_elu1_fast(x) : 0.f;
-                    zacc[rb] += u;
-                    if (!ABSPE) {
-                        const float p = lane_swap1(u);  // partner dim r ^ 1
-                        float2 cs = make_float2(1.f, 0.f);
-                        if (ok) cs = tab[rtab[rb] + crd[rax[rb]] * g.rope.np[rax[rb]]];
-                        u = (r & 1) ? (p * cs.y + u * cs.x) : (u * cs.x - p * cs.y);
-                    }
-                    fv[rb][vv] = u;
+                const bool ok = t0 + 4 * hf + 8 * (vv >> 2) + (vv & 3) < tok_hi && r < g.R;
+                if (ABSPE) {
+                    const int rr = r < g.R ? r : 0;
+                    const int it = ok ? cT[vv] : 0, ih = ok ? cH[vv] : 0, iw = ok ? cW[vv] : 0;
+                    ev[vv] = Et[it * g.R + rr] + Eh[ih * g.R + rr] + Ew[iw * g.R + rr];
+                } else {
+                    cs[vv] = tab[rbase[rb] + (ok ? cA[rb][vv] : 0) * rstride[rb]];
                 }
+            }
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv) {
+                const bool ok = t0 + 4 * hf + 8 * (vv >> 2) + (vv & 3) < tok_hi && r < g.R;
+                float x = uacc[rb][vv];
+                if (ABSPE) x += ev[vv];
+                float u = ok ? phi_elu1_fast(x) : 0.f;
+                zacc[rb] += u;
+                if (!ABSPE) {
+                    const float p = lane_swap1(u);  // partner dim r ^ 1
+                    u = (r & 1) ? (p * cs[vv].y + u * cs[vv].x) : (u * cs[vv].x - p * cs[vv].y);
+                }
+                fv[rb][vv] = u;
             }
         }
         u32x4_t fhi[NRB][2], flo[NRB][2];

@@ -97,6 +97,17 @@ __device__ __forceinline__ void coords_advance(int& t, int& h, int& w, int delta
     }
 }
 
+// The same for 0 <= delta < Wg (at most one wrap of w), branch free.
+__device__ __forceinline__ void coords_step(int& t, int& h, int& w, int delta, int Hg, int Wg) {
+    w += delta;
+    const bool ww = w >= Wg;
+    w -= ww ? Wg : 0;
+    h += ww ? 1 : 0;
+    const bool hw = h >= Hg;
+    h -= hw ? Hg : 0;
+    t += hw ? 1 : 0;
+}
+
 // Position of key/token x (0..15) inside a 16-slot group in the order
 // {0,1,2,3,8,9,10,11,4,5,6,7,12,13,14,15}: lane half h of a 32x32x16 MFMA
 // holds slots 8h..8h+7, which is the order the 32x32 accumulator keeps rows
