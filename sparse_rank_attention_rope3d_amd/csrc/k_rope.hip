@@ -78,29 +78,33 @@ template <> struct Io8<float> {
 //   V^T chunk (kh, db, h2), db = 32-dim block, h2 = 16-key group of the half:
 //       lane l holds V[keys (slot16 order) 32kh + 16h2 + 8(l/32) .. +7][dim 32db + l%32]
 // Keys past L are zero.
-template <typename TIO, int D, bool TILED>
+template <typename TIO, int D, int BS, bool TWO, bool TILED>
 __global__ __launch_bounds__(256) void k_rope_pool(const TIO* __restrict__ q, const TIO* __restrict__ k,
                                                    TIO* __restrict__ q_out, TIO* __restrict__ k_out,
                                                    float* __restrict__ qbar, float* __restrict__ kbar,
                                                    const float2* __restrict__ tab, RopeGeom g, long L,
-                                                   long out_rows, int bs, int nblk, const TIO* __restrict__ v,
+                                                   long out_rows, int nblk, const TIO* __restrict__ v,
                                                    uint16_t* __restrict__ kv_tiles) {
     constexpr int CH = D / 8;          // threads per row
     constexpr int RPP = 256 / CH;      // rows per pass
+    constexpr int bs = BS;
+    constexpr bool two = TWO;
     const int tid = threadIdx.x;
     const int c = tid % CH, rsub = tid / CH;
     const int blk = blockIdx.x;
     const long bh = blockIdx.y;
-    const bool two = (k != nullptr);
 
-    // axis and in-axis index of the 4 pairs this thread owns
-    int ax[4], jj[4];
+    // table entry of the 4 pairs this thread owns: base + (axis coordinate) * stride
+    int pax[4], pbase[4], pstride[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        int p = 4 * c + e;
-        if (p < g.np[0]) { ax[e] = 0; jj[e] = p; }
-        else if (p < g.np[0] + g.np[1]) { ax[e] = 1; jj[e] = p - g.np[0]; }
-        else { ax[e] = 2; jj[e] = p - g.np[0] - g.np[1]; }
+        const int p = 4 * c + e;
+        int a = 0, j = p;
+        if (p >= g.np[0] + g.np[1]) { a = 2; j = p - g.np[0] - g.np[1]; }
+        else if (p >= g.np[0]) { a = 1; j = p - g.np[0]; }
+        pax[e] = a;
+        pbase[e] = (a == 0 ? g.tab_off[0] : a == 1 ? g.tab_off[1] : g.tab_off[2]) + j;
+        pstride[e] = a == 0 ? g.np[0] : a == 1 ? g.np[1] : g.np[2];
     }
 
     float sq[8], sk[8];
@@ -113,76 +117,101 @@ __global__ __launch_bounds__(256) void k_rope_pool(const TIO* __restrict__ q, co
     TIO* ko = (two && k_out) ? k_out + bh * out_rows * D : nullptr;
     uint16_t* tile = TILED ? kv_tiles + (bh * nblk + blk) * (long)kTileElems : nullptr;
 
-    for (int r0 = 0; r0 < bs; r0 += RPP) {
-        const long l = (long)blk * bs + r0 + rsub;
-        if (l >= out_rows) continue;
-        float xq[8], xk[8];
+    // All loads of the block first (rows past L are clamped to row L - 1 and
+    // zeroed after), then the table gathers, then the arithmetic: no load
+    // waits on another.
+    constexpr int MAXP = BS / RPP;   // passes over the block
+    constexpr int npass = MAXP;
+    float xq[MAXP][8], xk[MAXP][8];
+    float2 cs[MAXP][4];
+    // V^T (tiled mode): thread tid < 128 takes 8 keys x 8 dims (keys = slots
+    // 8vh..8vh+7 of 16-group vG); it transposes them in registers and stores
+    // 8 rows of 16 bytes at the end
+    // (threads 128..255 load the same rows as tid - 128, so the loads are not
+    // under a divergent branch; those repeats are served by the caches)
+    const int vc = tid & 15, vg = (tid >> 4) & 7, vG = vg >> 1, vh = vg & 1;
+    uint32_t vrows[TILED ? 8 : 1][4];
+    if (TILED) {
+        const uint16_t* vs = reinterpret_cast<const uint16_t*>(v) + bh * L * D;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xk[i] = 0.f;
-        if (l < L) {
-            int crd[3];
-            token_coords(l, g.Hg, g.Wg, crd[0], crd[1], crd[2]);
-            Io8<TIO>::load(qs + l * D + 8 * c, xq);
-            if (two) Io8<TIO>::load(ks + l * D + 8 * c, xk);
+        for (int e = 0; e < 8; ++e) {
+            const long l = (long)blk * 64 + 16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2);
+            const u32x4_t w = ldg16(vs + (l < L ? l : L - 1) * D + 8 * vc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vrows[e][i] = l < L ? w[i] : 0u;
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+        if (p < npass) {
+            const long l = (long)blk * bs + p * RPP + rsub;
+            const long lc = l < L ? l : L - 1;
+            Io8<TIO>::load(qs + lc * D + 8 * c, xq[p]);
+            if (two) Io8<TIO>::load(ks + lc * D + 8 * c, xk[p]);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+        if (p < npass) {
+            const long l = (long)blk * bs + p * RPP + rsub;
+            int ct, chh, cw;
+            token_coords(l < L ? l : L - 1, g.Hg, g.Wg, ct, chh, cw);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int a = ax[e];
-                const float2 cs = tab[g.tab_off[a] + crd[a] * g.np[a] + jj[e]];
-                float x0 = xq[2 * e], x1 = xq[2 * e + 1];
-                xq[2 * e] = x0 * cs.x - x1 * cs.y;
-                xq[2 * e + 1] = x0 * cs.y + x1 * cs.x;
+                const int cv = pax[e] == 2 ? cw : (pax[e] == 1 ? chh : ct);
+                cs[p][e] = tab[pbase[e] + cv * pstride[e]];
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+        if (p < npass) {
+            const long l = (long)blk * bs + p * RPP + rsub;
+            if (l >= out_rows) continue;
+            const bool valid = l < L;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float x0 = xq[p][2 * e], x1 = xq[p][2 * e + 1];
+                xq[p][2 * e] = valid ? x0 * cs[p][e].x - x1 * cs[p][e].y : 0.f;
+                xq[p][2 * e + 1] = valid ? x0 * cs[p][e].y + x1 * cs[p][e].x : 0.f;
                 if (two) {
-                    x0 = xk[2 * e]; x1 = xk[2 * e + 1];
-                    xk[2 * e] = x0 * cs.x - x1 * cs.y;
-                    xk[2 * e + 1] = x0 * cs.y + x1 * cs.x;
+                    x0 = xk[p][2 * e]; x1 = xk[p][2 * e + 1];
+                    xk[p][2 * e] = valid ? x0 * cs[p][e].x - x1 * cs[p][e].y : 0.f;
+                    xk[p][2 * e + 1] = valid ? x0 * cs[p][e].y + x1 * cs[p][e].x : 0.f;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) xk[p][2 * e + i] = 0.f;
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) { sq[i] += xq[i]; sk[i] += xk[i]; }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) xq[i] = 0.f;
-        }
-        if (qo) Io8<TIO>::store(qo + l * D + 8 * c, xq);
-        if (TILED) {
-            const int r = r0 + rsub;   // key within the block; dims 8c .. 8c+7 = step c/2, lane half c%2
-            const int kh = r >> 5, ln = (r & 31) + 32 * (c & 1);
-            Io8<TIO>::store(reinterpret_cast<TIO*>(tile + ((kh * 8 + (c >> 1)) * 64 + ln) * 8), xk);
-        } else if (ko) {
-            Io8<TIO>::store(ko + l * D + 8 * c, xk);
+            for (int i = 0; i < 8; ++i) { sq[i] += xq[p][i]; sk[i] += xk[p][i]; }
+            if (qo) Io8<TIO>::store(qo + l * D + 8 * c, xq[p]);
+            if (TILED) {
+                const int r = p * RPP + rsub;   // key within the block; dims 8c .. 8c+7 = step c/2, lane half c%2
+                const int kh = r >> 5, ln = (r & 31) + 32 * (c & 1);
+                Io8<TIO>::store(reinterpret_cast<TIO*>(tile + ((kh * 8 + (c >> 1)) * 64 + ln) * 8), xk[p]);
+            } else if (ko) {
+                Io8<TIO>::store(ko + l * D + 8 * c, xk[p]);
+            }
         }
     }
 
-    if (TILED) {
-        // V^T: thread takes 8 keys x 8 dims (keys = slots 8vh..8vh+7 of 16-group vG), transposes in
-        // registers and stores 8 rows of 16 bytes.
+    if (TILED && tid < 128) {
         static_assert(!TILED || (D == 128 && sizeof(TIO) == 2), "tiled layout is bf16, D = 128");
-        if (tid < 128) {
-            const int vc = tid & 15, vg = tid >> 4, vG = vg >> 1, vh = vg & 1;
-            const uint16_t* vs = reinterpret_cast<const uint16_t*>(v) + bh * L * D;
-            uint32_t rows[8][4];
+        uint16_t* vt = tile + 64 * D;
+        const int kh = vG >> 1, h2 = vG & 1;   // 16-key group vG = 2kh + h2, lane half vh
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const long l = (long)blk * 64 + 16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2);
-                const u32x4_t w = l < L ? ldg16(vs + l * D + 8 * vc) : u32x4_t{0u, 0u, 0u, 0u};
+        for (int f = 0; f < 8; ++f) {
+            u32x4_t o;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) rows[e][i] = w[i];
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t a0 = vrows[2 * i][f >> 1], a1 = vrows[2 * i + 1][f >> 1];
+                o[i] = (f & 1) ? __builtin_amdgcn_perm(a1, a0, 0x07060302u)
+                               : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
             }
-            uint16_t* vt = tile + 64 * D;
-            const int kh = vG >> 1, h2 = vG & 1;   // 16-key group vG = 2kh + h2, lane half vh
-#pragma unroll
-            for (int f = 0; f < 8; ++f) {
-                u32x4_t o;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t a0 = rows[2 * i][f >> 1], a1 = rows[2 * i + 1][f >> 1];
-                    o[i] = (f & 1) ? __builtin_amdgcn_perm(a1, a0, 0x07060302u)
-                                   : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-                }
-                const int d = 8 * vc + f;
-                const int ln = (d & 31) + 32 * vh;
-                stg16(vt + ((kh * 8 + (d >> 5) * 2 + h2) * 64 + ln) * 8, o);
-            }
+            const int d = 8 * vc + f;
+            const int ln = (d & 31) + 32 * vh;
+            stg16(vt + ((kh * 8 + (d >> 5) * 2 + h2) * 64 + ln) * 8, o);
         }
     }
 
@@ -213,23 +242,35 @@ hipError_t launch_rope_tables(float2* tab, const RopeGeom& g, double base, hipSt
     return hipGetLastError();
 }
 
-template <typename TIO, int D>
+template <typename TIO, int D, int BS, bool TWO>
 static hipError_t rope_pool_t(const void* q, const void* k, void* qo, void* ko, float* qbar, float* kbar,
+                              const float2* tab, const RopeGeom& g, long BH, long L, long out_rows, int nblk,
+                              hipStream_t st) {
+    dim3 grid((unsigned)nblk, (unsigned)BH);
+    hipLaunchKernelGGL((k_rope_pool<TIO, D, BS, TWO, false>), grid, dim3(256), 0, st, (const TIO*)q, (const TIO*)k,
+                       (TIO*)qo, (TIO*)ko, qbar, kbar, tab, g, L, out_rows, nblk, (const TIO*)nullptr,
+                       (uint16_t*)nullptr);
+    return hipGetLastError();
+}
+
+template <typename TIO, int D>
+static hipError_t rope_pool_d(const void* q, const void* k, void* qo, void* ko, float* qbar, float* kbar,
                               const float2* tab, const RopeGeom& g, long BH, long L, long out_rows, int bs,
                               int nblk, hipStream_t st) {
-    dim3 grid((unsigned)nblk, (unsigned)BH);
-    hipLaunchKernelGGL((k_rope_pool<TIO, D, false>), grid, dim3(256), 0, st, (const TIO*)q, (const TIO*)k, (TIO*)qo,
-                       (TIO*)ko, qbar, kbar, tab, g, L, out_rows, bs, nblk, (const TIO*)nullptr, (uint16_t*)nullptr);
-    return hipGetLastError();
+    if (bs == 32)
+        return k ? rope_pool_t<TIO, D, 32, true>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, nblk, st)
+                 : rope_pool_t<TIO, D, 32, false>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, nblk, st);
+    return k ? rope_pool_t<TIO, D, 64, true>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, nblk, st)
+             : rope_pool_t<TIO, D, 64, false>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, nblk, st);
 }
 
 hipError_t launch_rope_pool_tiled(const void* q, const void* k, const void* v, void* qo, uint16_t* kv_tiles,
                                   float* qbar, float* kbar, const float2* tab, const RopeGeom& g, long BH, long L,
                                   int nblk, hipStream_t st) {
     dim3 grid((unsigned)nblk, (unsigned)BH);
-    hipLaunchKernelGGL((k_rope_pool<uint16_t, 128, true>), grid, dim3(256), 0, st, (const uint16_t*)q,
-                       (const uint16_t*)k, (uint16_t*)qo, (uint16_t*)nullptr, qbar, kbar, tab, g, L, (long)nblk * 64,
-                       64, nblk, (const uint16_t*)v, kv_tiles);
+    hipLaunchKernelGGL((k_rope_pool<uint16_t, 128, 64, true, true>), grid, dim3(256), 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (uint16_t*)qo, (uint16_t*)nullptr, qbar, kbar, tab, g, L,
+                       (long)nblk * 64, nblk, (const uint16_t*)v, kv_tiles);
     return hipGetLastError();
 }
 
@@ -237,11 +278,11 @@ hipError_t launch_rope_pool(int dtype_bf16, int D, const void* q, const void* k,
                             float* kbar, const float2* tab, const RopeGeom& g, long BH, long L, long out_rows,
                             int bs, int nblk, hipStream_t st) {
     if (dtype_bf16) {
-        if (D == 64) return rope_pool_t<uint16_t, 64>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
-        return rope_pool_t<uint16_t, 128>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
+        if (D == 64) return rope_pool_d<uint16_t, 64>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
+        return rope_pool_d<uint16_t, 128>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
     }
-    if (D == 64) return rope_pool_t<float, 64>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
-    return rope_pool_t<float, 128>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
+    if (D == 64) return rope_pool_d<float, 64>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
+    return rope_pool_d<float, 128>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
 }
 
 }  // namespace slr

@@ -125,11 +125,12 @@ struct RopeGeom {
 };
 
 __device__ __forceinline__ void token_coords(long l, int Hg, int Wg, int& t, int& h, int& w) {
-    int hw = Hg * Wg;
-    t = (int)(l / hw);
-    int rem = (int)(l - (long)t * hw);
-    h = rem / Wg;
-    w = rem - h * Wg;
+    // token indices (padded rows included) stay below 2^32: 32-bit unsigned division
+    const uint32_t lu = (uint32_t)l, hw = (uint32_t)Hg * (uint32_t)Wg;
+    const uint32_t tq = lu / hw, rem = lu - tq * hw, hq = rem / (uint32_t)Wg;
+    t = (int)tq;
+    h = (int)hq;
+    w = (int)(rem - hq * (uint32_t)Wg);
 }
 
 // Fully pipelined global loads / LDS access as 16-byte vectors.
