@@ -34,12 +34,6 @@ __device__ __forceinline__ float2 lr_cossin_q(const float2* __restrict__ tab, co
     return tab[g.rope.tab_off[a] + crd[a] * g.rope.np[a] + j];
 }
 
-// Work-item order that keeps each XCD on a contiguous range of
-// (slice, query block): hardware hands workgroup p to XCD p % 8.
-__device__ __forceinline__ long xcd_remap(long p, long n) {
-    const long per = n / 8, rem = n % 8, x = p % 8, loc = p / 8;
-    return x * per + (x < rem ? x : rem) + loc;
-}
 
 // Epilogue shared by the flash kernels: lane owns query row q0 + l32 and the
 // O^T accumulator dims 32db + 8(i/4) + 4hf + i%4. Normalises the sparse

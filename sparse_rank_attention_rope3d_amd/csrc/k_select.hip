@@ -27,74 +27,98 @@ __device__ __forceinline__ void split8(const float* x, u32x4_t& hi, u32x4_t& lo)
     }
 }
 
-// One workgroup (4 waves) = a 64 x 64 tile of the score matrix of one slice;
-// wave (wi, wj) owns the 32 x 32 sub-tile. A = qbar rows (m = i, k = d),
-// B = kbar rows (k = d, n = j), both read straight from global memory.
+// One workgroup (4 waves) = 32 complete rows of the score matrix of one
+// slice, so its output is one contiguous stretch of memory. A = qbar rows
+// (m = i, k = d), split once and kept in registers; the waves take the 32-key
+// column tiles round robin, B = kbar rows (k = d, n = j) from L2. The grid is
+// remapped so that all row blocks of a slice run on one XCD.
 template <int D>
 __global__ __launch_bounds__(256) void k_block_scores(const float* __restrict__ qbar, const float* __restrict__ kbar,
-                                                      float* __restrict__ scores, int nblk, float scale) {
+                                                      float* __restrict__ scores, int nblk, float scale, int nrb,
+                                                      long nwg) {
+    constexpr int NS = D / 16;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
-    const long bh = blockIdx.z;
-    const int i0 = blockIdx.y * 64 + 32 * (wave & 1);
-    const int j0 = blockIdx.x * 64 + 32 * (wave >> 1);
+    const long wg = xcd_remap(blockIdx.x, nwg);
+    const long bh = wg / nrb;
+    const int i0 = (int)(wg % nrb) * 32;
     const float* qb = qbar + bh * (long)nblk * D;
     const float* kb = kbar + bh * (long)nblk * D;
-    const int ia = i0 + l32, jb = j0 + l32;
-    f32x16_t acc;
+    // rows / columns past nblk read the last one; they are never stored
+    const int ia = i0 + l32 < nblk ? i0 + l32 : nblk - 1;
+    u32x4_t ahi[NS], alo[NS];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int s = 0; s < NS; ++s) {
+        const f32x4_t* p = reinterpret_cast<const f32x4_t*>(qb + (long)ia * D + 16 * s + 8 * hf);
+        const f32x4_t u = p[0], w = p[1];
+        float x[8];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-        float xa[8], xb[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { xa[e] = 0.f; xb[e] = 0.f; }
-        if (ia < nblk) {
-            const f32x4_t* p = reinterpret_cast<const f32x4_t*>(qb + (long)ia * D + 16 * s + 8 * hf);
-            const f32x4_t u = p[0], w = p[1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { xa[e] = u[e]; xa[4 + e] = w[e]; }
-        }
-        if (jb < nblk) {
-            const f32x4_t* p = reinterpret_cast<const f32x4_t*>(kb + (long)jb * D + 16 * s + 8 * hf);
-            const f32x4_t u = p[0], w = p[1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { xb[e] = u[e]; xb[4 + e] = w[e]; }
-        }
-        u32x4_t ah, al, bhi, blo;
-        split8(xa, ah, al);
-        split8(xb, bhi, blo);
-        acc = mfma32(ah, bhi, acc);
-        acc = mfma32(ah, blo, acc);
-        acc = mfma32(al, bhi, acc);
+        for (int e = 0; e < 4; ++e) { x[e] = u[e]; x[4 + e] = w[e]; }
+        split8(x, ahi[s], alo[s]);
     }
-    // lane holds rows i0 + 8(v/4) + 4hf + v%4 of column j0 + l32
-    if (jb < nblk) {
-        float* out = scores + bh * (long)nblk * nblk + jb;
+    const int ntile = (nblk + 31) / 32;
+    float* out_rows = scores + bh * (long)nblk * nblk;
+    for (int jt = wave; jt < ntile; jt += 4) {
+        const int j0 = jt * 32;
+        const int jb = j0 + l32 < nblk ? j0 + l32 : nblk - 1;
+        f32x4_t braw[2 * NS];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int i = i0 + 8 * (v >> 2) + 4 * hf + (v & 3);
-            if (i < nblk) out[(long)i * nblk] = acc[v] * scale;
+        for (int s = 0; s < NS; ++s) {
+            const f32x4_t* p = reinterpret_cast<const f32x4_t*>(kb + (long)jb * D + 16 * s + 8 * hf);
+            braw[2 * s] = p[0];
+            braw[2 * s + 1] = p[1];
+        }
+        f32x16_t acc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { x[e] = braw[2 * s][e]; x[4 + e] = braw[2 * s + 1][e]; }
+            u32x4_t bhi, blo;
+            split8(x, bhi, blo);
+            acc = mfma32(ahi[s], bhi, acc);
+            acc = mfma32(ahi[s], blo, acc);
+            acc = mfma32(alo[s], bhi, acc);
+        }
+        // lane holds rows i0 + 8(v/4) + 4hf + v%4 of column j0 + l32
+        if (j0 + l32 < nblk) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int i = i0 + 8 * (v >> 2) + 4 * hf + (v & 3);
+                if (i < nblk) out_rows[(long)i * nblk + j0 + l32] = acc[v] * scale;
+            }
         }
     }
 }
 
 // Top-k of one score row per wave. KPL = keys per lane held in registers
 // (column j = 64 m + lane); KPL = 0 reads the row from memory on every pass.
+//
+// The k-th largest key is found exactly, bit by bit from the top. With keys
+// in registers this runs in two phases: the upper 16 bits over all keys, then
+// the lower 16 bits over only the keys that share the upper 16 bits with the
+// threshold (compacted into LDS), since every other key is decided by then.
 template <int KPL>
 __global__ __launch_bounds__(256) void k_topk_rows(const float* __restrict__ scores, int32_t* __restrict__ idx,
                                                    long nrows, int nblk, int keep) {
-    const int lane = threadIdx.x & 63;
-    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    constexpr int CMAX = KPL > 0 ? 64 * KPL : 1;
+    __shared__ uint32_t cand_all[4][CMAX];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const long row = (long)blockIdx.x * 4 + wave;
     if (row >= nrows) return;
     const float* s = scores + row * nblk;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t key[KPL > 0 ? KPL : 1];
     if (KPL > 0) {
+        // unconditional loads (columns past nblk read the last one, then get
+        // key 0, which is below every finite key)
 #pragma unroll
         for (int m = 0; m < KPL; ++m) {
             const int j = 64 * m + lane;
-            key[m] = j < nblk ? ordered_key(s[j]) : 0u;   // 0 is below every finite key
+            const uint32_t kk = ordered_key(s[j < nblk ? j : nblk - 1]);
+            key[m] = j < nblk ? kk : 0u;
         }
     }
     auto count_ge = [&](uint32_t cand) -> int {
@@ -110,11 +134,45 @@ __global__ __launch_bounds__(256) void k_topk_rows(const float* __restrict__ sco
         }
         return cnt;
     };
-    // largest key value t with #(key >= t) >= keep, built bit by bit
+    // thr = the largest key value t with #(key >= t) >= keep
     uint32_t thr = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = thr | (1u << bit);
-        if (count_ge(cand) >= keep) thr = cand;
+    if (KPL > 0) {
+        // phase 1: upper 16 bits
+        uint32_t hi = 0;
+        for (int bit = 15; bit >= 0; --bit) {
+            const uint32_t c = hi | (1u << bit);
+            if (count_ge(c << 16) >= keep) hi = c;
+        }
+        const int n_above = hi == 0xffffu ? 0 : count_ge((hi + 1) << 16);
+        // keys in bucket hi -> this wave's LDS list
+        uint32_t* cand = cand_all[wave];
+        int nc = 0;
+#pragma unroll
+        for (int m = 0; m < KPL; ++m) {
+            const bool in = (key[m] >> 16) == hi;
+            const uint64_t msk = __ballot(in);
+            if (in) cand[nc + __popcll(msk & below)] = key[m];
+            nc += __popcll(msk);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // phase 2: lower 16 bits, counting the bucket only
+        thr = hi << 16;
+        for (int bit = 15; bit >= 0; --bit) {
+            const uint32_t c = thr | (1u << bit);
+            int cnt = n_above;
+            for (int j0 = 0; j0 < nc; j0 += 64) {
+                const int j = j0 + lane;
+                cnt += __popcll(__ballot(j < nc && cand[j < nc ? j : 0] >= c));
+            }
+            if (cnt >= keep) thr = c;
+        }
+    } else {
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = thr | (1u << bit);
+            if (count_ge(cand) >= keep) thr = cand;
+        }
     }
     const int need = keep - (thr == 0xffffffffu ? 0 : count_ge(thr + 1));  // ties at thr, lowest index first
     int32_t* out = idx + row * (long)keep;
@@ -147,12 +205,13 @@ size_t select_scores_bytes(long BH, int nblk) { return sizeof(float) * (size_t)B
 hipError_t launch_select(int D, const float* qbar, const float* kbar, float* scores, int32_t* idx, long BH, int nblk,
                          int keep, hipStream_t st) {
     const float scale = 1.0f / sqrtf((float)D);
-    const int nt = (nblk + 63) / 64;
-    dim3 g1((unsigned)nt, (unsigned)nt, (unsigned)BH);
+    const int nrb = (nblk + 31) / 32;
+    const long nwg = (long)nrb * BH;
+    dim3 g1((unsigned)nwg);
     if (D == 64)
-        hipLaunchKernelGGL(k_block_scores<64>, g1, dim3(256), 0, st, qbar, kbar, scores, nblk, scale);
+        hipLaunchKernelGGL(k_block_scores<64>, g1, dim3(256), 0, st, qbar, kbar, scores, nblk, scale, nrb, nwg);
     else
-        hipLaunchKernelGGL(k_block_scores<128>, g1, dim3(256), 0, st, qbar, kbar, scores, nblk, scale);
+        hipLaunchKernelGGL(k_block_scores<128>, g1, dim3(256), 0, st, qbar, kbar, scores, nblk, scale, nrb, nwg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long rows = BH * nblk;

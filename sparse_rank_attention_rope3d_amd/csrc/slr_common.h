@@ -133,6 +133,13 @@ __device__ __forceinline__ void token_coords(long l, int Hg, int Wg, int& t, int
     w = (int)(rem - hq * (uint32_t)Wg);
 }
 
+// Work-item order that keeps each XCD on a contiguous range of
+// (slice, query block): hardware hands workgroup p to XCD p % 8.
+__device__ __forceinline__ long xcd_remap(long p, long n) {
+    const long per = n / 8, rem = n % 8, x = p % 8, loc = p / 8;
+    return x * per + (x < rem ? x : rem) + loc;
+}
+
 // Fully pipelined global loads / LDS access as 16-byte vectors.
 __device__ __forceinline__ u32x4_t ldg16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ void stg16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
