@@ -28,6 +28,31 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch of the sparse flash kernel, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch, scaled x2 and x1 by what the same counters read
+# for a plain 1 GiB copy). They hold only for the kernel source they were taken
+# on, identified by the sha256 of its files; any other source reports null.
+FLASH_TRAFFIC_SOURCES = ["k_flash.hip", "slr_common.h", "slr_launch.h"]
+FLASH_TRAFFIC = {
+    "sha256": "d9a9f84660e65111535d058264f8c47d7ba1dea842c551dde6ef03b39a08e933",
+    "bytes_per_launch": {"wan13b": 8521.1e6 + 201.9e6, "wan14b": 226550.7e6 + 1568.6e6},
+}
+
+
+def flash_traffic(workload: str):
+    import hashlib
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_rank_attention_rope3d_amd", "csrc")
+    h = hashlib.sha256()
+    try:
+        for f in FLASH_TRAFFIC_SOURCES:
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    except OSError:
+        return None
+    if h.hexdigest() != FLASH_TRAFFIC["sha256"]:
+        return None
+    return FLASH_TRAFFIC["bytes_per_launch"].get(workload)
+
 
 def _hip():
     h = ctypes.CDLL("libamdhip64.so")
@@ -283,9 +308,9 @@ def main() -> int:
         "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "D": cfg.D, "L": cfg.L,
                    "grid": [cfg.T, cfg.Hg, cfg.Wg], "block": cfg.block, "keep": cfg.keep, "nblk": cfg.nblk,
                    "rank": cfg.rank, "lowrank": cfg.lr_mode, "parallelism": "single GPU"},
-        "roofline": {"kernel": "k_flash_bf16 (block-sparse flash + low-rank readout + combine)",
+        "roofline": {"kernel": "k_flash_tiled (block-sparse flash + low-rank readout + combine)",
                      "bound": "mfma", "achieved": round(flash_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(flash_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(flash_tf / PEAK_BF16_TFLOPS, 4), "traffic": flash_traffic(args.workload),
                      "algorithmic_flops_per_launch": F["sparse"], "avg_launch_ms": round(flash_ms, 4)},
         "stages_ms": {n: round(vv, 4) for n, vv in stage_ms.items()},
         "hbm_stages": hbm,
