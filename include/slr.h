@@ -115,7 +115,7 @@ int slr_rope3d(const slr_shape *shape, const slr_rope_cfg *rope, const void *x, 
                void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Block selection of the sparse branch (RoLA Fig. 2 "sparse top-k spikes",
+ * Block selection of the sparse branch (RoLA Fig. 2, the top-k spike blocks of the sparse branch;
  * §4.1): rotate q and k, mean-pool each block over its valid tokens (from
  * the fp32 rotated values), score s_ij = qbar_i . kbar_j / sqrt(D) in fp32
  * and keep the `keep` largest per query block (ties: lower index).

@@ -134,7 +134,7 @@ static int ascending_int(const void *pa, const void *pb)
 }
 
 /*
- * Per-query-block top-k ([RoLA] Fig. 2 "sparse top-k spikes"; §4.1): keep
+ * Per-query-block top-k ([RoLA] Fig. 2, the top-k spike blocks; §4.1): keep
  * the k key blocks with the largest scores. idx[i, 0..k) ascending;
  * thr[i] = the k-th largest score of row i; next[i] = the (k+1)-th (or
  * -inf when k = nblk), so callers can tell how close the cut is.

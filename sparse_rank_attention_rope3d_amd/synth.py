@@ -62,7 +62,7 @@ class Layer:
     lr_mode: str                   # "rola" (rotation after phi) or "abspe"
     lr_pairs: Tuple[int, int, int] # rotary pairs the rank-r branch reuses (sum = r/2)
     seed: int
-    gen: str                       # "normal" or "clustered"
+    gen: str                       # "normal", "clustered" or "zero_qk" (q = k = 0: every block score ties)
     eps: float = 1e-6
 
     @property
@@ -179,6 +179,9 @@ def qkv_slice(cfg: Layer, b: int, h: int, L: Optional[int] = None) -> Tuple[np.n
     if cfg.gen == "normal":
         q = _rng(cfg.seed, TID_Q, b, h).standard_normal((L, D), dtype=np.float32)
         k = _rng(cfg.seed, TID_K, b, h).standard_normal((L, D), dtype=np.float32)
+    elif cfg.gen == "zero_qk":
+        q = np.zeros((L, D), dtype=np.float32)
+        k = np.zeros((L, D), dtype=np.float32)
     else:
         cent = centroids(cfg, h) * np.float32(CENTROID_SCALE)
         cl = _rng(cfg.seed, TID_CLUSTER, b, h).integers(0, N_CENTROIDS, size=L)

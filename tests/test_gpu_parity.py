@@ -74,6 +74,8 @@ SMALL = [
     (128, 64, 32, "rola", (2, 4, 16), 2, "bf16"),     # L = 128, no tail
     (128, 64, 32, "rola", (5, 9, 13), 3, "f32"),
     (64, 64, 16, "abspe", (3, 6, 7), 2, "f32"),
+    (128, 64, 32, "rola", (20, 7, 2), 2, "bf16"),     # grid rows of 2 tokens (coordinate steps wrap often)
+    (128, 64, 32, "abspe", (9, 4, 3), 2, "bf16"),
 ]
 
 
@@ -86,6 +88,24 @@ def test_small_layers_full(D, bs, r, mode, grid, keep, dtype):
                    T=grid[0], Hg=grid[1], Wg=grid[2], block=bs, keep=keep, rank=r, lr_mode=mode, lr_pairs=lp,
                    pairs=pairs, dtype=dtype, seed=7)
     _full_check(cfg)
+
+
+@pytest.mark.parametrize("grid,keep", [((5, 9, 13), 3), ((5, 30, 30), 7)])
+def test_exact_ties_pick_lowest_blocks(grid, keep):
+    """q = k = 0: every block score is exactly 0, so every query block keeps
+    blocks 0 .. keep-1 (ties go to the lower index); 71 blocks put the keys
+    of a row in two register slots per lane."""
+    cfg = T.custom(synth.wan13b(), name=f"ties {grid}", B=1, H=2, T=grid[0], Hg=grid[1], Wg=grid[2], keep=keep,
+                   gen="zero_qk", seed=11)
+    T.log(f"  case {cfg.name}: nblk={cfg.nblk} keep={keep}")
+    inp = T.make_inputs(cfg)
+    out, idx, o_sp, o_lr = T.run_layer(inp)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    want = np.broadcast_to(np.arange(keep, dtype=got.dtype), got.shape)
+    assert np.array_equal(got, want)
+    res = T.check_layer(inp, out, idx, o_sp, o_lr)
+    assert res["differ"] == 0
 
 
 def test_gate_zero_gives_sparse_branch():
