@@ -220,7 +220,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     hip = _hip()
-    events = [[_event(hip) for _ in range(6)] for _ in range(args.steps)]
+    events = [[_event(hip) for _ in range(5)] for _ in range(args.steps)]
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         B.slr_attention_fwd(q, k, v, shape, rope, sparse, lowrank, out=out, ws=ws)
@@ -232,7 +232,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    stage_names = ["rope_pool", "select", "lowrank_summary", "sparse_flash", "lr_apply"]
+    stage_names = ["rope_pool", "select", "lowrank_summary", "sparse_flash"]
     stages = {n: [] for n in stage_names}
     for ev in events:
         for j, n in enumerate(stage_names):

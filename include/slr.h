@@ -151,19 +151,16 @@ int slr_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, const sl
                       void *ws, size_t ws_bytes, void *stream);
 
 /*
- * slr_attention_fwd, plus timing marks: events[0..5] are hipEvent_t handles
+ * slr_attention_fwd, plus timing marks: events[0..4] are hipEvent_t handles
  * created by the caller; they are recorded on `stream` before the first
- * launch, after the rotate + pool step, after the block selection (with the
- * key-range segments), after the low-rank summary (split-L partials, reduce,
- * projection prep), after the block-sparse flash kernel and after the partial
- * merge + low-rank readout + combine. On shapes where the readout is fused
- * into the flash kernel, events 4 and 5 are recorded back to back.
- * Same results, same errors.
+ * launch, after the rotate + pool step, after the block selection, after the
+ * low-rank summary (projection prep, split-L partials, reduce) and after the
+ * fused sparse flash + readout + combine kernel. Same results, same errors.
  */
 int slr_attention_fwd_staged(const slr_shape *shape, const slr_rope_cfg *rope, const slr_sparse_cfg *sparse,
                              const slr_lowrank_cfg *lowrank, const void *q, const void *k, const void *v,
                              void *out, int32_t *idx_out, void *o_sparse_out, void *o_lowrank_out,
-                             void *ws, size_t ws_bytes, void *const events[6], void *stream);
+                             void *ws, size_t ws_bytes, void *const events[5], void *stream);
 
 /*
  * Dense softmax attention with 3D RoPE applied inside (RoLA §3 "Full

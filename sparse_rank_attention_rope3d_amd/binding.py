@@ -202,9 +202,9 @@ def slr_attention_fwd(q, k, v, shape: SlrShape, rope: SlrRopeCfg, sparse: SlrSpa
 
 def slr_attention_fwd_staged(q, k, v, shape: SlrShape, rope: SlrRopeCfg, sparse: SlrSparseCfg,
                              lowrank: SlrLowrankCfg, out: torch.Tensor, ws: torch.Tensor, events) -> None:
-    """slr_attention_fwd recording six caller-created hipEvent_t handles
+    """slr_attention_fwd recording five caller-created hipEvent_t handles
     (integers) at the stage boundaries on the current stream."""
-    ev = (ctypes.c_void_p * 6)(*events)
+    ev = (ctypes.c_void_p * 5)(*events)
     _check(lib().slr_attention_fwd_staged(ctypes.byref(shape), ctypes.byref(rope), ctypes.byref(sparse),
                                           ctypes.byref(lowrank), _ptr(q), _ptr(k), _ptr(v), _ptr(out), None, None,
                                           None, _ptr(ws), ws.numel(), ev, _stream()), "slr_attention_fwd_staged")

@@ -1,6 +1,5 @@
 // Block-sparse (and dense) flash attention with the low-rank readout and the
-// gated combine fused into the epilogue, for the layer shapes outside the
-// persistent tiled kernel (fp32 layers; bf16 with D = 64 or 32-token blocks).
+// gated combine fused into the epilogue.
 //
 // RoLA (arXiv 2609.06712v3) §4.1: exact softmax attention of each query
 // block over the tokens of its kept key blocks; App. A Algorithm 1: the
@@ -20,10 +19,140 @@
 // 16-byte reads); the next kept tile is fetched into registers while the
 // current one is consumed.
 #include "slr_common.h"
-#include "slr_epilogue.h"
 #include "slr_launch.h"
 
 namespace slr {
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float2 lr_cossin_q(const float2* __restrict__ tab, const LrGeom& g, int pr,
+                                              const int* crd) {
+    int a, j;
+    if (pr < g.lp[0]) { a = 0; j = pr; }
+    else if (pr < g.lp[0] + g.lp[1]) { a = 1; j = pr - g.lp[0]; }
+    else { a = 2; j = pr - g.lp[0] - g.lp[1]; }
+    return tab[g.rope.tab_off[a] + crd[a] * g.rope.np[a] + j];
+}
+
+
+// Epilogue shared by the flash kernels: lane owns query row q0 + l32 and the
+// O^T accumulator dims 32db + 8(i/4) + 4hf + i%4. Normalises the sparse
+// branch, evaluates the low-rank readout rho(w)^T S / (w . z + eps) with
+// w = phi(q W_q [+ E]) on MFMA (hi/lo bf16 splits of w and S for ~fp32
+// accuracy), combines with the per-head gate and stores bf16 rows.
+template <int D, int RP, int LR>
+__device__ __forceinline__ void flash_epilogue(const FlashArgs& a, long bh, int head, long q0, float lsum,
+                                               const f32x16_t* oacc) {
+    constexpr int NS = D / 16;
+    constexpr int NDB = D / 32;
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
+    const long L = a.L;
+    const long qrow = q0 + l32;
+    const bool qval = qrow < L;
+    const float inv = 1.f / lsum;
+    float gsc = 0.f, rden = 0.f;
+    constexpr int NRB = RP / 32;
+    u32x4_t whi[NRB][2], wlo[NRB][2];
+    if (LR != 0) {
+        const uint16_t* qraw = (const uint16_t*)a.q + (bh * L + (qval ? qrow : 0)) * D;
+        f32x16_t wacc[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) wacc[rb][i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const u32x4_t qo2 = qval ? ldg16(qraw + 16 * s + 8 * hf) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                const u32x4_t wa = ldg16(a.wqt + ((long)head * RP + 32 * rb + l32) * D + 16 * s + 8 * hf);
+                wacc[rb] = mfma32(wa, qo2, wacc[rb]);
+            }
+        }
+        int crd[3] = {0, 0, 0};
+        if (qval) token_coords(qrow, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
+        const float* zp = a.zp + bh * RP;
+        float den = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            float w[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 32 * rb + 8 * (i >> 2) + 4 * hf + (i & 3);
+                const bool ok = qval && r < a.g.R;
+                float x = wacc[rb][i];
+                if (LR == 2 && ok) x += a.Et[crd[0] * a.g.R + r] + a.Eh[crd[1] * a.g.R + r] + a.Ew[crd[2] * a.g.R + r];
+                w[i] = ok ? phi_elu1(x) : 0.f;
+                den += w[i] * zp[r];
+            }
+            if (LR == 1) {
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    const int r = 32 * rb + 8 * (i >> 2) + 4 * hf + (i & 3);
+                    if (qval && r < a.g.R) {
+                        const float2 cs = lr_cossin_q(a.tab, a.g, r >> 1, crd);
+                        const float w0 = w[i], w1 = w[i + 1];
+                        w[i] = w0 * cs.x - w1 * cs.y;
+                        w[i + 1] = w0 * cs.y + w1 * cs.x;
+                    }
+                }
+            }
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float a0 = w[8 * h2 + 2 * i], a1 = w[8 * h2 + 2 * i + 1];
+                    const uint32_t hi = pack_bf2(a0, a1);
+                    whi[rb][h2][i] = hi;
+                    wlo[rb][h2][i] = pack_bf2(a0 - bf_lo(hi), a1 - bf_hi(hi));
+                }
+        }
+        den = sum_xor32(den);
+        rden = 1.f / (den + a.eps);
+        gsc = a.gate[head];
+    }
+    uint16_t* out = (uint16_t*)a.out + (bh * L + (qval ? qrow : 0)) * D;
+    uint16_t* osp = a.o_sp ? (uint16_t*)a.o_sp + (bh * L + (qval ? qrow : 0)) * D : nullptr;
+    uint16_t* olr = a.o_lr ? (uint16_t*)a.o_lr + (bh * L + (qval ? qrow : 0)) * D : nullptr;
+    // one 32-dim block at a time: num^T = S^T rho(w)^T (m = d, k = r, n = query), combine, store
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        f32x16_t nacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) nacc[i] = 0.f;
+        if (LR != 0) {
+            const long so = (bh * D + 32 * db + l32) * RP + 8 * hf;
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const u32x4_t sh = ldg16(a.st_hi + so + 32 * rb + 16 * h2);
+                    const u32x4_t sl = ldg16(a.st_lo + so + 32 * rb + 16 * h2);
+                    nacc = mfma32(sh, whi[rb][h2], nacc);
+                    nacc = mfma32(sh, wlo[rb][h2], nacc);
+                    nacc = mfma32(sl, whi[rb][h2], nacc);
+                }
+        }
+        if (qval) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = 32 * db + 8 * g4 + 4 * hf;
+                float vs[4], vl[4], vo[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    vs[i] = oacc[db][4 * g4 + i] * inv;
+                    vl[i] = LR != 0 ? nacc[4 * g4 + i] * rden : 0.f;
+                    vo[i] = vs[i] + gsc * vl[i];
+                }
+                *reinterpret_cast<u32x2_t*>(out + d0) = u32x2_t{pack_bf2(vo[0], vo[1]), pack_bf2(vo[2], vo[3])};
+                if (osp)
+                    *reinterpret_cast<u32x2_t*>(osp + d0) = u32x2_t{pack_bf2(vs[0], vs[1]), pack_bf2(vs[2], vs[3])};
+                if (olr)
+                    *reinterpret_cast<u32x2_t*>(olr + d0) = u32x2_t{pack_bf2(vl[0], vl[1]), pack_bf2(vl[2], vl[3])};
+            }
+        }
+    }
+}
 
 template <int D, int BS, int RP, int LR, bool DENSE>
 __global__ __launch_bounds__(BS * 2) void k_flash_bf16(FlashArgs a) {
@@ -188,6 +317,194 @@ __global__ __launch_bounds__(BS * 2) void k_flash_bf16(FlashArgs a) {
 }
 
 
+// ---------------------------------------------------------------------------
+// Streaming variant for bf16, D = 128, 64-token blocks (every workload shape).
+//
+// Each kept key block is one contiguous 32 KB tile in operand order (see the
+// rotate kernel): a 16 KB K part and a 16 KB V^T part whose 1 KB chunks are
+// each one wave's MFMA operand, so the LDS image equals the memory image and
+// is filled by direct global-to-LDS copies with no repacking. Workgroup = 4
+// waves = one 64-row query block; wave (rh, kh) owns query rows 32rh.. and
+// keys 32kh.. of every tile, with S^T = K Q^T computed so that each lane holds
+// one query row. The K and V^T parts stream through separate LDS rings (K
+// three deep, V^T two deep; one barrier per tile). The key halves of each row
+// are merged once at the end through LDS. The running max is only raised when
+// it grows by more than 2^8 (the probabilities then stay <= 256, exact after
+// the final normalisation), so the accumulator rescale is rare.
+
+// online softmax of one 32-row block's scores -> bf16 probabilities
+__device__ __forceinline__ void softmax_block(f32x16_t& sacc, f32x16_t* oacc, float& m_run, float& l_run, float sl2,
+                                              u32x4_t* pop) {
+    float mx = sacc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+    mx = max_xor32(mx) * sl2;
+    if (__ballot(mx > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p0 = fast_exp2(fmaf(sacc[8 * h2 + 2 * i], sl2, -m_run));
+            const float p1 = fast_exp2(fmaf(sacc[8 * h2 + 2 * i + 1], sl2, -m_run));
+            l_run += p0 + p1;
+            pop[h2][i] = pack_bf2(p0, p1);
+        }
+}
+
+// Eight 16-byte LDS reads (1 KB apart) into registers; the block waits for
+// them itself, so no read is left in flight when it ends.
+__device__ __forceinline__ void lds_read8(u32x4_t* r, const uint16_t* lds_base) {
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds_base;
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %4, %8 offset:4096\n\t"
+        "ds_read_b128 %5, %8 offset:5120\n\t"
+        "ds_read_b128 %6, %8 offset:6144\n\t"
+        "ds_read_b128 %7, %8 offset:7168\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7])
+        : "v"(a)
+        : "memory");
+}
+
+template <int RP, int LR, bool DENSE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_flash_tiled(
+    FlashArgs a, const int32_t* __restrict__ idx_all, const uint16_t* __restrict__ kvt_all) {
+    constexpr int D = 128, BS = 64;
+    constexpr int PART = kTileElems / 2;                 // K or V^T part of a tile (elements)
+    constexpr int PLOADS = PART * 2 / (256 * 16);        // 16-byte copies per thread per part (4)
+    // K ring (3 parts) | V^T ring (2 parts), 80 KB; the start is reused as the
+    // key-half exchange area at the end
+    __shared__ __attribute__((aligned(16))) uint16_t lds[5 * PART];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rh = wave & 1, kh = wave >> 1;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const long wid = xcd_remap(blockIdx.x, a.nwg);
+    const long bh = wid / a.nblk;
+    const int qb = (int)(wid % a.nblk);
+    const int head = (int)(bh % a.H);
+    const long L = a.L;
+    const int nblk = a.nblk;
+    const uint16_t* tiles = kvt_all + bh * (long)nblk * kTileElems + (long)tid * 8;
+    const int32_t* ix = DENSE ? nullptr : idx_all + (bh * nblk + qb) * (long)a.keep;
+    const int ntile = DENSE ? nblk : a.keep;
+    auto tile_of = [&](int n) -> int { return DENSE ? n : ix[n]; };
+
+    // B operand of S^T = K Q^T: query row 32rh + l32 of the block
+    u32x4_t qop[8];
+    const uint16_t* qr = (const uint16_t*)a.qr + (bh * (long)nblk * BS + (long)qb * BS + 32 * rh + l32) * D + 8 * hf;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qop[s] = ldg16(qr + 16 * s);
+    wait_vmcnt<0>();
+
+    // part (0 = K, 1 = V^T) of tile j -> LDS: the LDS image equals the memory
+    // image (operand order)
+    auto issue = [&](int j, int part, uint16_t* dst) {
+        const uint16_t* src = tiles + (long)j * kTileElems + part * PART;
+#pragma unroll
+        for (int m = 0; m < PLOADS; ++m)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(src + m * 256 * 8),
+                (__attribute__((address_space(3))) void*)(dst + (m * 256 + wave * 64) * 8), 16, 0, 0);
+    };
+    const int rd = ((kh * 8) * 64 + lane) * 8;   // this lane's operand chunks (kh, 0..7) within a part
+
+    f32x16_t oacc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    float m_run = -1e30f, l_run = 0.f;   // log2-domain (scaled) running max, partial row sum
+    const float sl2 = a.scale * kLog2e;
+    const bool ragged = (L % BS) != 0;
+
+    // K of tile t lives in K slot t % 3, V^T in V slot t % 2. The barrier that
+    // opens tile t also certifies that every wave is done with tile t - 1, so
+    // V^T of t + 1 and K of t + 2 are requested into those slots right away:
+    // K parts land two tiles ahead (they are needed first), V^T parts one.
+    issue(tile_of(0), 0, lds);
+    issue(tile_of(0), 1, lds + 3 * PART);
+    if (ntile > 1) issue(tile_of(1), 0, lds + PART);
+    int ks = 0;   // K slot of tile t
+    for (int t = 0; t < ntile; ++t) {
+        const int jcur = tile_of(t);
+        // outstanding in issue order: ..., V^T(t), K(t + 1) -> keep K(t + 1) in flight
+        if (t + 1 < ntile) wait_vmcnt<PLOADS>(); else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (t + 1 < ntile) issue(tile_of(t + 1), 1, lds + (3 + ((t + 1) & 1)) * PART);
+        if (t + 2 < ntile) issue(tile_of(t + 2), 0, lds + (ks == 0 ? 2 : ks - 1) * PART);
+        const uint16_t* kcur = lds + ks * PART;
+        const uint16_t* vcur = lds + (3 + (t & 1)) * PART;
+        ks = ks == 2 ? 0 : ks + 1;
+        u32x4_t op[8], vop[8];
+        lds_read8(op, kcur + rd);                 // K chunks (kh, s)
+        f32x16_t sacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+        __builtin_amdgcn_s_setprio(1);   // matrix phase first when two waves share a SIMD
+#pragma unroll
+        for (int s = 0; s < 8; ++s) sacc = mfma32(op[s], qop[s], sacc);
+        __builtin_amdgcn_s_setprio(0);
+        // V^T chunks (kh, db, h2): read while the score MFMAs run, into
+        // registers other than the K operands those MFMAs still read
+        lds_read8(vop, vcur + rd);
+        asm volatile("" ::"v"(op[0]), "v"(op[1]), "v"(op[2]), "v"(op[3]), "v"(op[4]), "v"(op[5]), "v"(op[6]),
+                     "v"(op[7]));
+        if (ragged && jcur == nblk - 1) {
+            const long key0 = (long)jcur * BS + 32 * kh;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (key0 + 8 * (i >> 2) + 4 * hf + (i & 3) >= L) sacc[i] = -INFINITY;
+        }
+        u32x4_t pop[2];
+        softmax_block(sacc, oacc, m_run, l_run, sl2, pop);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) oacc[db] = mfma32(vop[db * 2 + h2], pop[h2], oacc[db]);
+        __builtin_amdgcn_s_setprio(0);
+    }
+    __syncthreads();
+    float (*mrg)[66 * 64] = reinterpret_cast<float (*)[66 * 64]>(&lds[0]);
+
+    // ---- merge the two key halves of each row half through LDS
+    float* m_lds = mrg[rh];
+    if (kh == 1) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m_lds[(16 * db + i) * 64 + lane] = oacc[db][i];
+        m_lds[64 * 64 + lane] = m_run;
+        m_lds[65 * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = m_lds[64 * 64 + lane], l1 = m_lds[65 * 64 + lane];
+    const float m = fmaxf(m_run, m1);
+    const float f0 = fast_exp2(m_run - m), f1 = fast_exp2(m1 - m);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = oacc[db][i] * f0 + m_lds[(16 * db + i) * 64 + lane] * f1;
+    const float lsum = l_run * f0 + l1 * f1;
+    flash_epilogue<D, RP, LR>(a, bh, head, (long)qb * BS + 32 * rh, sum_xor32(lsum), oacc);
+}
+
 // fp32 layers: one thread per query row, K / V tiles staged in LDS, fp32
 // VALU throughout (the precision the tiny fp32 check layer asks for).
 template <int D, int RP, int LR, bool DENSE>
@@ -327,9 +644,21 @@ static hipError_t flash_f32_t(int lr_mode, bool dense, const FlashArgs& a, int B
     return hipGetLastError();
 }
 
+template <int RP>
+static hipError_t flash_tiled_t(int lr_mode, bool dense, const FlashArgs& a, hipStream_t st) {
+    dim3 grid((unsigned)a.nwg), blk(256);
+    if (dense) hipLaunchKernelGGL((k_flash_tiled<RP, 0, true>), grid, blk, 0, st, a, a.idx, a.kvt);
+    else if (lr_mode == 1) hipLaunchKernelGGL((k_flash_tiled<RP, 1, false>), grid, blk, 0, st, a, a.idx, a.kvt);
+    else if (lr_mode == 2) hipLaunchKernelGGL((k_flash_tiled<RP, 2, false>), grid, blk, 0, st, a, a.idx, a.kvt);
+    else hipLaunchKernelGGL((k_flash_tiled<RP, 0, false>), grid, blk, 0, st, a, a.idx, a.kvt);
+    return hipGetLastError();
+}
+
 hipError_t launch_flash(int dtype_bf16, int D, int BS, int RP, int lr_mode, bool dense, const FlashArgs& a, long BH,
                         hipStream_t st) {
     (void)BH;
+    if (dtype_bf16 && D == 128 && BS == 64 && a.kvt)
+        return RP == 64 ? flash_tiled_t<64>(lr_mode, dense, a, st) : flash_tiled_t<32>(lr_mode, dense, a, st);
     if (!dtype_bf16) {
         if (D == 64) return RP == 64 ? flash_f32_t<64, 64>(lr_mode, dense, a, BS, st)
                                      : flash_f32_t<64, 32>(lr_mode, dense, a, BS, st);

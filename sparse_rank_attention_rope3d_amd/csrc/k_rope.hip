@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void k_rope_pool(const TIO* __restrict__ q, co
                                                    float* __restrict__ qbar, float* __restrict__ kbar,
                                                    const float2* __restrict__ tab, RopeGeom g, long L,
                                                    long out_rows, int nblk, const TIO* __restrict__ v,
-                                                   uint16_t* __restrict__ kv_tiles, float qscale) {
+                                                   uint16_t* __restrict__ kv_tiles) {
     constexpr int CH = D / 8;          // threads per row
     constexpr int RPP = 256 / CH;      // rows per pass
     constexpr int bs = BS;
@@ -185,12 +185,7 @@ __global__ __launch_bounds__(256) void k_rope_pool(const TIO* __restrict__ q, co
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) { sq[i] += xq[p][i]; sk[i] += xk[p][i]; }
-            if (qo) {
-                float xs[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) xs[i] = xq[p][i] * qscale;
-                Io8<TIO>::store(qo + l * D + 8 * c, xs);
-            }
+            if (qo) Io8<TIO>::store(qo + l * D + 8 * c, xq[p]);
             if (TILED) {
                 const int r = p * RPP + rsub;   // key within the block; dims 8c .. 8c+7 = step c/2, lane half c%2
                 const int kh = r >> 5, ln = (r & 31) + 32 * (c & 1);
@@ -254,7 +249,7 @@ static hipError_t rope_pool_t(const void* q, const void* k, void* qo, void* ko, 
     dim3 grid((unsigned)nblk, (unsigned)BH);
     hipLaunchKernelGGL((k_rope_pool<TIO, D, BS, TWO, false>), grid, dim3(256), 0, st, (const TIO*)q, (const TIO*)k,
                        (TIO*)qo, (TIO*)ko, qbar, kbar, tab, g, L, out_rows, nblk, (const TIO*)nullptr,
-                       (uint16_t*)nullptr, 1.f);
+                       (uint16_t*)nullptr);
     return hipGetLastError();
 }
 
@@ -271,11 +266,11 @@ static hipError_t rope_pool_d(const void* q, const void* k, void* qo, void* ko, 
 
 hipError_t launch_rope_pool_tiled(const void* q, const void* k, const void* v, void* qo, uint16_t* kv_tiles,
                                   float* qbar, float* kbar, const float2* tab, const RopeGeom& g, long BH, long L,
-                                  int nblk, float qscale, hipStream_t st) {
+                                  int nblk, hipStream_t st) {
     dim3 grid((unsigned)nblk, (unsigned)BH);
     hipLaunchKernelGGL((k_rope_pool<uint16_t, 128, 64, true, true>), grid, dim3(256), 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (uint16_t*)qo, (uint16_t*)nullptr, qbar, kbar, tab, g, L,
-                       (long)nblk * 64, nblk, (const uint16_t*)v, kv_tiles, qscale);
+                       (long)nblk * 64, nblk, (const uint16_t*)v, kv_tiles);
     return hipGetLastError();
 }
 

@@ -2,12 +2,9 @@
 //
 // Every check runs on the host before the first HIP call, so a rejected call
 // has no side effect. Launch order of the layer forward (one stream):
-//   rope tables -> rotate + pool q, k (+ the [K | V^T] tiles) -> block
-//   top-k -> key-range segments -> low-rank split-L summary -> fixed-order
-//   reduce -> projection prep -> persistent block-sparse flash (partials)
-//   -> partial merge + low-rank readout + gated combine.
-// Shapes outside the tiled kernel set (fp32, D = 64, 32-token blocks) run
-// one flash kernel with the readout and combine fused into its epilogue.
+//   rope tables -> (bf16) projection prep -> rotate + pool q, k -> block
+//   top-k -> low-rank split-L summary -> fixed-order reduce -> fused
+//   sparse flash + low-rank readout + gated combine.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -134,9 +131,8 @@ void summary_split(const Dims& d, int slots, int* chunk, int* nsplit) {
 
 // Workspace layout (byte offsets, each 256-byte aligned).
 struct Layout {
-    size_t tab, qr, kr, kvt, qbar, kbar, scores, idx, wqt, wkt, part, S, z, sthi, stlo, zp, seg, po, pml, total;
+    size_t tab, qr, kr, kvt, qbar, kbar, scores, idx, wqt, wkt, part, S, z, sthi, stlo, zp, total;
     bool tiled;
-    int ksplit;
 };
 
 // bf16, D = 128, 64-token blocks: K and V^T go to contiguous per-block tiles
@@ -162,14 +158,6 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         if (use_tiles(d, bs)) {
             w.tiled = true;
             w.kvt = take(2ul * d.BH * nblk * kTileElems);
-            if (op == SLR_OP_ATTENTION) {
-                // key-range segments and the normalised partials of every (query block, range) task
-                w.ksplit = sparse_flash_ksplit(d.BH, nblk, keep, false);
-                const size_t tasks = (size_t)d.BH * nblk * w.ksplit;
-                if (w.ksplit > 1) w.seg = take(4ul * d.BH * nblk * (w.ksplit + 1));
-                w.po = take(tasks * 2 * 16 * 64 * 4 * 2);
-                w.pml = take(tasks * 2 * 64 * 4);
-            }
         } else {
             w.kr = take((size_t)d.es * d.BH * rows * d.D);
         }
@@ -387,20 +375,16 @@ int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sp
     float* S = at<float>(ws, w.S);
     float* z = at<float>(ws, w.z);
 
-    const double scale = 1.0 / std::sqrt((double)d.D);
     auto mark = [&](int i) { return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess; };
     SLR_TRY(mark(0));
     SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
     if (w.tiled)
-        SLR_TRY(launch_rope_pool_tiled(q, k, v, qr, kvt, qbar, kbar, tab, g, d.BH, d.L, nblk,
-                                       (float)(scale * 1.4426950408889634), s));
+        SLR_TRY(launch_rope_pool_tiled(q, k, v, qr, kvt, qbar, kbar, tab, g, d.BH, d.L, nblk, s));
     else
         SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, qr, kr, qbar, kbar, tab, g, d.BH, d.L, (long)nblk * bs, bs,
                                  nblk, s));
     SLR_TRY(mark(1));
     SLR_TRY(launch_select((int)d.D, qbar, kbar, at<float>(ws, w.scores), idx, d.BH, nblk, sparse->keep, s));
-    int32_t* seg = w.seg ? at<int32_t>(ws, w.seg) : nullptr;
-    if (seg) SLR_TRY(launch_segments(idx, seg, d.BH * nblk, sparse->keep, nblk, w.ksplit, s));
     SLR_TRY(mark(2));
     if ((st = run_summary(d, g, lg, RP, lowrank, k, v, kvt, nblk, ws, w, S, z, d.bf16 != 0, s))) return st;
     uint16_t* wqt = nullptr;
@@ -424,23 +408,12 @@ int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sp
     a.g = lg;
     a.out = out; a.o_sp = o_sparse_out; a.o_lr = o_lowrank_out;
     a.L = d.L; a.H = (int)d.H; a.nblk = nblk; a.keep = sparse->keep;
-    a.scale = (float)scale;
+    a.scale = (float)(1.0 / std::sqrt((double)d.D));
     a.eps = lowrank->eps;
     a.nwg = d.BH * nblk;
     const int lr_mode = lowrank->mode == SLR_LR_ABS_PE ? 2 : 1;
-    if (w.tiled) {
-        a.ksplit = w.ksplit;
-        a.seg = seg;
-        a.part_o = at<uint16_t>(ws, w.po);
-        a.part_ml = at<float>(ws, w.pml);
-        SLR_TRY(launch_sparse_flash(a, false, false, s));
-        SLR_TRY(mark(4));
-        SLR_TRY(launch_lr_apply(RP, lr_mode, a, d.BH, s));
-    } else {
-        SLR_TRY(launch_flash(d.bf16, (int)d.D, bs, RP, lr_mode, false, a, d.BH, s));
-        SLR_TRY(mark(4));
-    }
-    SLR_TRY(mark(5));
+    SLR_TRY(launch_flash(d.bf16, (int)d.D, bs, RP, lr_mode, false, a, d.BH, s));
+    SLR_TRY(mark(4));
     return SLR_OK;
 }
 
@@ -457,9 +430,9 @@ int slr_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
 int slr_attention_fwd_staged(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
                              const slr_lowrank_cfg* lowrank, const void* q, const void* k, const void* v, void* out,
                              int32_t* idx_out, void* o_sparse_out, void* o_lowrank_out, void* ws, size_t ws_bytes,
-                             void* const events[6], void* stream) {
+                             void* const events[5], void* stream) {
     if (!events) return SLR_EINVAL;
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < 5; ++i)
         if (!events[i]) return SLR_EINVAL;
     return attention_fwd(shape, rope, sparse, lowrank, q, k, v, out, idx_out, o_sparse_out, o_lowrank_out, ws,
                          ws_bytes, events, stream);
@@ -484,11 +457,9 @@ int slr_dense_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, co
     void* qr = at<void>(ws, w.qr);
     void* kr = w.tiled ? nullptr : at<void>(ws, w.kr);
     uint16_t* kvt = w.tiled ? at<uint16_t>(ws, w.kvt) : nullptr;
-    const double scale = 1.0 / std::sqrt((double)d.D);
     SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
     if (w.tiled)
-        SLR_TRY(launch_rope_pool_tiled(q, k, v, qr, kvt, nullptr, nullptr, tab, g, d.BH, d.L, nblk,
-                                       (float)(scale * 1.4426950408889634), s));
+        SLR_TRY(launch_rope_pool_tiled(q, k, v, qr, kvt, nullptr, nullptr, tab, g, d.BH, d.L, nblk, s));
     else
         SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, qr, kr, nullptr, nullptr, tab, g, d.BH, d.L, (long)nblk * bs,
                                  bs, nblk, s));
@@ -496,13 +467,9 @@ int slr_dense_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, co
     std::memset(&a, 0, sizeof(a));
     a.qr = qr; a.kr = kr; a.kvt = kvt; a.v = v; a.out = out;
     a.L = d.L; a.H = (int)d.H; a.nblk = nblk; a.keep = nblk;
-    a.scale = (float)scale;
+    a.scale = (float)(1.0 / std::sqrt((double)d.D));
     a.nwg = d.BH * nblk;
-    a.ksplit = 1;
-    if (w.tiled)
-        SLR_TRY(launch_sparse_flash(a, true, true, s));
-    else
-        SLR_TRY(launch_flash(d.bf16, (int)d.D, bs, 32, 0, true, a, d.BH, s));
+    SLR_TRY(launch_flash(d.bf16, (int)d.D, bs, 32, 0, true, a, d.BH, s));
     return SLR_OK;
 }
 

@@ -41,11 +41,6 @@ struct FlashArgs {
     float scale;             // 1/sqrt(D)
     float eps;
     long nwg;                // workgroups in the grid
-    // persistent block-sparse path (bf16, D = 128, 64-token blocks)
-    int ksplit;              // key ranges per query block (1, 2, 4, 8 or a multiple of 8)
-    const int32_t* seg;      // [BH][nblk][ksplit + 1] offsets of each range in the kept list (ksplit > 1)
-    uint16_t* part_o;        // [BH*nblk][ksplit][2][4][4][64] x 4 bf16: normalised partial O, lane order
-    float* part_ml;          // [BH*nblk][ksplit][2][2][32]: row max (log2 units) and row sum of each partial
 };
 
 hipError_t launch_rope_tables(float2* tab, const RopeGeom& g, double base, hipStream_t st);
@@ -54,10 +49,9 @@ hipError_t launch_rope_pool(int dtype_bf16, int D, const void* q, const void* k,
                             int bs, int nblk, hipStream_t st);
 // Tiled K / V^T layout of the block-sparse flash kernel (bf16, D = 128, 64-token blocks).
 constexpr int kTileElems = 2 * 64 * 128;
-// qscale multiplies the rotated q copy (not the block means)
 hipError_t launch_rope_pool_tiled(const void* q, const void* k, const void* v, void* qo, uint16_t* kv_tiles,
                                   float* qbar, float* kbar, const float2* tab, const RopeGeom& g, long BH, long L,
-                                  int nblk, float qscale, hipStream_t st);
+                                  int nblk, hipStream_t st);
 size_t select_scores_bytes(long BH, int nblk);
 hipError_t launch_select(int D, const float* qbar, const float* kbar, float* scores, int32_t* idx, long BH, int nblk,
                          int keep, hipStream_t st);
@@ -73,17 +67,6 @@ hipError_t launch_lr_summary(int dtype_bf16, int D, int RP, bool abspe, const vo
                              int H, int chunk, int nsplit, float* part, hipStream_t st);
 hipError_t launch_lr_reduce(const float* part, long BH, int nsplit, int D, int R, int RP, float* S, float* z,
                             uint16_t* st_hi, uint16_t* st_lo, float* zp, hipStream_t st);
-// Persistent block-sparse / dense flash for bf16, D = 128, 64-token blocks
-// (rotated q pre-scaled by scale * log2 e, [K | V^T] tiles). Writes the
-// normalised partials of every (query block, key range) task; with
-// direct_out (dense, ksplit = 1) it writes the final rows to a.out instead.
-int sparse_flash_ksplit(long BH, int nblk, int keep, bool dense);
-hipError_t launch_segments(const int32_t* idx, int32_t* seg, long rows, int keep, int nblk, int ksplit,
-                           hipStream_t st);
-hipError_t launch_sparse_flash(const FlashArgs& a, bool dense, bool direct_out, hipStream_t st);
-// Merges the partials, adds the gated low-rank readout and writes out (and
-// the optional debug outputs). lr_mode as below.
-hipError_t launch_lr_apply(int RP, int lr_mode, const FlashArgs& a, long BH, hipStream_t st);
 // lr_mode: 0 = no low-rank term (plain attention), 1 = rotary after phi, 2 = absolute PE
 hipError_t launch_flash(int dtype_bf16, int D, int BS, int RP, int lr_mode, bool dense, const FlashArgs& a,
                         long BH, hipStream_t st);

@@ -56,13 +56,9 @@ def test_workspace_bytes_matches_layout_size():
     shape, rope, sparse, lr = _cfgs()
     n = B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lr)
     layer = synth.wan13b()
-    # bf16, D = 128, 64-token blocks: rotated q plus per-block [K | V^T] tiles,
-    # and per (query block, key range) task a bf16 partial output (16 KB) with
-    # its row maxima and sums (512 B); at most 32 key ranges per query block
+    # bf16, D = 128, 64-token blocks: rotated q plus per-block [K | V^T] tiles
     rot = 3 * (layer.B * layer.H * layer.nblk * layer.block * layer.D * 2)
-    task = layer.B * layer.H * layer.nblk * (16384 + 512)
-    assert rot + task <= n < rot + 32 * task + 128 * 2 ** 20
-    assert (n - rot) % task < 128 * 2 ** 20
+    assert rot < n < rot + 128 * 2 ** 20
     assert B.slr_workspace_bytes(B.SLR_OP_ROPE3D, shape, rope) < 2 ** 20
     assert B.slr_workspace_bytes(B.SLR_OP_DENSE, shape, rope) >= rot
     # other shapes keep plain rotated q and k copies
