@@ -328,36 +328,59 @@ __global__ __launch_bounds__(BS * 2) void k_flash_bf16(FlashArgs a) {
 // keys 32kh.. of every tile, with S^T = K Q^T computed so that each lane holds
 // one query row. The K and V^T parts stream through separate LDS rings (K
 // three deep, V^T two deep; one barrier per tile). The key halves of each row
-// are merged once at the end through LDS. The running max is only raised when
-// it grows by more than 2^8 (the probabilities then stay <= 256, exact after
-// the final normalisation), so the accumulator rescale is rare.
+// are merged once at the end through LDS. q comes pre-scaled into log2 units
+// and the score accumulator starts at minus the row's reference, so the
+// common tile needs only exp2 of the MFMA results; the reference moves only
+// when a tile's probabilities could overflow, so the accumulator rescale is
+// rare.
 
-// online softmax of one 32-row block's scores -> bf16 probabilities
-__device__ __forceinline__ void softmax_block(f32x16_t& sacc, f32x16_t* oacc, float& m_run, float& l_run, float sl2,
-                                              u32x4_t* pop) {
-    float mx = sacc[0];
+// Online softmax of one 32-row block's scores -> bf16 probabilities, exp2
+// domain. q arrives multiplied by 1/sqrt(D) * log2(e) and the score
+// accumulator of a tile starts at -m_run (0 while the row has no reference
+// yet: m_run = -inf), so s already holds score - reference in log2 units and
+// p = exp2(s) needs no max or FMA. The reference is raised only when some
+// probability of the tile could exceed ~2^36 (its sum passes 2^40, or is not
+// finite), and set from the tile when the row has none; O and l are scaled
+// by the same factor, so the result after normalisation is unchanged.
+__device__ __forceinline__ void softmax_tile(f32x16_t& s, f32x16_t* o, float& m_run, float& l_run, u32x4_t* pop) {
+    float p[16];
+    float l = 0.f;
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-    mx = max_xor32(mx) * sl2;
-    if (__ballot(mx > m_run + 8.f)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
+    for (int i = 0; i < 16; ++i) {
+        p[i] = fast_exp2(s[i]);
+        l += p[i];
+    }
+    const bool noref = m_run == -INFINITY;
+    if (__ballot(!(l <= 1.0995116e12f) || noref)) {
+        float mx = s[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+        mx = max_xor32(mx);
+        // shift of the reference: to the tile max for a row without one (it
+        // stays -inf while every key seen is masked), else up to the tile max
+        // when that is higher
+        const float shift = noref ? mx : fmaxf(mx, 0.f);
+        const bool none = shift == -INFINITY;
+        const float ref = noref ? 0.f : m_run;
+        const float alpha = noref ? 0.f : fast_exp2(-shift);
+        m_run = none ? -INFINITY : ref + shift;
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        l = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            p[i] = none ? 0.f : fast_exp2(s[i] - shift);
+            l += p[i];
+        }
     }
+    l_run += l;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float p0 = fast_exp2(fmaf(sacc[8 * h2 + 2 * i], sl2, -m_run));
-            const float p1 = fast_exp2(fmaf(sacc[8 * h2 + 2 * i + 1], sl2, -m_run));
-            l_run += p0 + p1;
-            pop[h2][i] = pack_bf2(p0, p1);
-        }
+        for (int i = 0; i < 4; ++i) pop[h2][i] = pack_bf2(p[8 * h2 + 2 * i], p[8 * h2 + 2 * i + 1]);
 }
 
 // Eight 16-byte LDS reads (1 KB apart) into registers; the block waits for
@@ -428,8 +451,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    float m_run = -1e30f, l_run = 0.f;   // log2-domain (scaled) running max, partial row sum
-    const float sl2 = a.scale * kLog2e;
+    float m_run = -INFINITY, l_run = 0.f;   // reference (log2 units), partial row sum
     const bool ragged = (L % BS) != 0;
 
     // K of tile t lives in K slot t % 3, V^T in V slot t % 2. The barrier that
@@ -453,8 +475,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         u32x4_t op[8], vop[8];
         lds_read8(op, kcur + rd);                 // K chunks (kh, s)
         f32x16_t sacc;
+        {
+            const float init = m_run == -INFINITY ? 0.f : -m_run;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+            for (int i = 0; i < 16; ++i) sacc[i] = init;
+        }
         __builtin_amdgcn_s_setprio(1);   // matrix phase first when two waves share a SIMD
 #pragma unroll
         for (int s = 0; s < 8; ++s) sacc = mfma32(op[s], qop[s], sacc);
@@ -471,7 +496,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 if (key0 + 8 * (i >> 2) + 4 * hf + (i & 3) >= L) sacc[i] = -INFINITY;
         }
         u32x4_t pop[2];
-        softmax_block(sacc, oacc, m_run, l_run, sl2, pop);
+        softmax_tile(sacc, oacc, m_run, l_run, pop);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < 4; ++db)

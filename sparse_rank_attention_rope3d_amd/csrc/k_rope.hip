@@ -65,8 +65,9 @@ template <> struct Io8<float> {
 // row per thread, D/8 threads per row, 256/(D/8) rows per pass.
 // Writes the rotated rows when q_out / k_out are non-null (rows in
 // [L, out_rows) of the block are written as zeros, which pads the workspace
-// copy to whole blocks) and, when qbar is non-null, the block means of the
-// fp32 rotated values over valid tokens.
+// copy to whole blocks; the q copy is multiplied by qscale before rounding)
+// and, when qbar is non-null, the block means of the fp32 rotated values
+// over valid tokens (not scaled).
 //
 // Tiled mode (bf16, D = 128, 64-token blocks; the layout the block-sparse
 // flash kernel streams): instead of a plain copy, rotated k and the
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256) void k_rope_pool(const TIO* __restrict__ q, co
                                                    float* __restrict__ qbar, float* __restrict__ kbar,
                                                    const float2* __restrict__ tab, RopeGeom g, long L,
                                                    long out_rows, int nblk, const TIO* __restrict__ v,
-                                                   uint16_t* __restrict__ kv_tiles) {
+                                                   uint16_t* __restrict__ kv_tiles, float qscale) {
     constexpr int CH = D / 8;          // threads per row
     constexpr int RPP = 256 / CH;      // rows per pass
     constexpr int bs = BS;
@@ -185,7 +186,12 @@ __global__ __launch_bounds__(256) void k_rope_pool(const TIO* __restrict__ q, co
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) { sq[i] += xq[p][i]; sk[i] += xk[p][i]; }
-            if (qo) Io8<TIO>::store(qo + l * D + 8 * c, xq[p]);
+            if (qo) {
+                float xs[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xs[i] = xq[p][i] * qscale;
+                Io8<TIO>::store(qo + l * D + 8 * c, xs);
+            }
             if (TILED) {
                 const int r = p * RPP + rsub;   // key within the block; dims 8c .. 8c+7 = step c/2, lane half c%2
                 const int kh = r >> 5, ln = (r & 31) + 32 * (c & 1);
@@ -249,7 +255,7 @@ static hipError_t rope_pool_t(const void* q, const void* k, void* qo, void* ko, 
     dim3 grid((unsigned)nblk, (unsigned)BH);
     hipLaunchKernelGGL((k_rope_pool<TIO, D, BS, TWO, false>), grid, dim3(256), 0, st, (const TIO*)q, (const TIO*)k,
                        (TIO*)qo, (TIO*)ko, qbar, kbar, tab, g, L, out_rows, nblk, (const TIO*)nullptr,
-                       (uint16_t*)nullptr);
+                       (uint16_t*)nullptr, 1.f);
     return hipGetLastError();
 }
 
@@ -266,11 +272,11 @@ static hipError_t rope_pool_d(const void* q, const void* k, void* qo, void* ko, 
 
 hipError_t launch_rope_pool_tiled(const void* q, const void* k, const void* v, void* qo, uint16_t* kv_tiles,
                                   float* qbar, float* kbar, const float2* tab, const RopeGeom& g, long BH, long L,
-                                  int nblk, hipStream_t st) {
+                                  int nblk, float qscale, hipStream_t st) {
     dim3 grid((unsigned)nblk, (unsigned)BH);
     hipLaunchKernelGGL((k_rope_pool<uint16_t, 128, 64, true, true>), grid, dim3(256), 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (uint16_t*)qo, (uint16_t*)nullptr, qbar, kbar, tab, g, L,
-                       (long)nblk * 64, nblk, (const uint16_t*)v, kv_tiles);
+                       (long)nblk * 64, nblk, (const uint16_t*)v, kv_tiles, qscale);
     return hipGetLastError();
 }
 

@@ -21,6 +21,9 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+// The tiled path stores q already multiplied by 1/sqrt(D) * log2(e): the
+// flash kernel's scores then come out of the MFMAs in log2 units.
+float tiled_qscale(long D) { return (float)(1.4426950408889634 / std::sqrt((double)D)); }
 
 struct Dims {
     long B, H, BH, D, L;
@@ -379,7 +382,7 @@ int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sp
     SLR_TRY(mark(0));
     SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
     if (w.tiled)
-        SLR_TRY(launch_rope_pool_tiled(q, k, v, qr, kvt, qbar, kbar, tab, g, d.BH, d.L, nblk, s));
+        SLR_TRY(launch_rope_pool_tiled(q, k, v, qr, kvt, qbar, kbar, tab, g, d.BH, d.L, nblk, tiled_qscale(d.D), s));
     else
         SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, qr, kr, qbar, kbar, tab, g, d.BH, d.L, (long)nblk * bs, bs,
                                  nblk, s));
@@ -459,7 +462,8 @@ int slr_dense_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, co
     uint16_t* kvt = w.tiled ? at<uint16_t>(ws, w.kvt) : nullptr;
     SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
     if (w.tiled)
-        SLR_TRY(launch_rope_pool_tiled(q, k, v, qr, kvt, nullptr, nullptr, tab, g, d.BH, d.L, nblk, s));
+        SLR_TRY(launch_rope_pool_tiled(q, k, v, qr, kvt, nullptr, nullptr, tab, g, d.BH, d.L, nblk, tiled_qscale(d.D),
+                                       s));
     else
         SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, qr, kr, nullptr, nullptr, tab, g, d.BH, d.L, (long)nblk * bs,
                                  bs, nblk, s));

@@ -49,9 +49,11 @@ hipError_t launch_rope_pool(int dtype_bf16, int D, const void* q, const void* k,
                             int bs, int nblk, hipStream_t st);
 // Tiled K / V^T layout of the block-sparse flash kernel (bf16, D = 128, 64-token blocks).
 constexpr int kTileElems = 2 * 64 * 128;
+// qscale multiplies the rotated q copy (the flash kernel's scores then come
+// out in log2 units), not the block means.
 hipError_t launch_rope_pool_tiled(const void* q, const void* k, const void* v, void* qo, uint16_t* kv_tiles,
                                   float* qbar, float* kbar, const float2* tab, const RopeGeom& g, long BH, long L,
-                                  int nblk, hipStream_t st);
+                                  int nblk, float qscale, hipStream_t st);
 size_t select_scores_bytes(long BH, int nblk);
 hipError_t launch_select(int D, const float* qbar, const float* kbar, float* scores, int32_t* idx, long BH, int nblk,
                          int keep, hipStream_t st);
