@@ -11,6 +11,7 @@ it with ctypes and chains its steps in the order the method states
   phi(k W_k) -> rotate after phi -> summary S, z
   phi(q W_q) -> rotate after phi -> readout S / (w.z + eps)   (low-rank)
   O = O_sparse + g_h * O_lowrank                              (combine)
+  or, token-wise (RoLA §4.4): O = O_sparse + g(q) * RMS-aligned O_lowrank
 
 Every function takes and returns float64 numpy arrays for one (b, h) slice.
 The absolute-PE variant (RoPeSLR, arXiv 2605.20659, abstract) adds per-axis
@@ -62,6 +63,8 @@ def _load():
         lib.orc_lowrank_summary.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp, _dp]
         lib.orc_lowrank_readout.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _lp, _dp, _dp, _dp, _dp,
                                             ctypes.c_double, _dp]
+        lib.orc_token_gate.argtypes = [ctypes.c_long, ctypes.c_int, _dp, _dp, ctypes.c_double, _dp, _dp,
+                                       ctypes.c_double, _dp, _dp]
         for f in ("orc_rope3d", "orc_block_mean", "orc_block_scores", "orc_topk_blocks",
                   "orc_block_sparse_attention", "orc_lowrank_features", "orc_lowrank_rotate",
                   "orc_lowrank_summary", "orc_lowrank_readout"):
@@ -183,11 +186,20 @@ def lowrank_readout(fq, w, S, z, eps, rows=None) -> np.ndarray:
     return out
 
 
+def token_gate(q, wg, bg, o_sp, o_lr, eps):
+    """Token-wise gated fusion of [n, D] rows (RoLA §4.4): returns (out, g)."""
+    q, wg, o_sp, o_lr = _d(q), _d(wg), _d(o_sp), _d(o_lr)
+    n, D = o_sp.shape
+    out, g = np.empty((n, D)), np.empty(n)
+    _load().orc_token_gate(n, D, _p(q), _p(wg), float(bg), _p(o_sp), _p(o_lr), float(eps), _p(out), _p(g))
+    return out, g
+
+
 # ---------------------------------------------------------------------------
 # one (b, h) slice of the whole layer
 
 def layer_slice(cfg, q, k, v, wq, wk, gate_h, E=None, qblocks=None, idx=None,
-                origin=(0, 0, 0)) -> Dict[str, np.ndarray]:
+                origin=(0, 0, 0), token_gate_wb=None) -> Dict[str, np.ndarray]:
     """Forward of one (b, h) slice.
 
     ``cfg`` supplies T, Hg, Wg, base, pairs, block, keep, lr_mode, lr_pairs
@@ -195,7 +207,9 @@ def layer_slice(cfg, q, k, v, wq, wk, gate_h, E=None, qblocks=None, idx=None,
     query blocks (all when None). ``idx`` replaces the selection for the
     sparse branch (used where a near-tie allows another valid selection).
     Returns the intermediates: q_rot, k_rot, qbar, kbar, scores, idx_ref,
-    thr, next, S, z, o_sp, o_lr, out (the last three as [nq, bs, D])."""
+    thr, next, S, z, o_sp, o_lr, out (the last three as [nq, bs, D]).
+    ``token_gate_wb = (wg [D], bg)`` replaces the per-head gate by the
+    token-wise gate of RoLA §4.4 (then also returns ``g`` per row)."""
     grid = (cfg.T, cfg.Hg, cfg.Wg)
     L, bs = cfg.T * cfg.Hg * cfg.Wg, cfg.block
     nblk = (L + bs - 1) // bs
@@ -227,5 +241,14 @@ def layer_slice(cfg, q, k, v, wq, wk, gate_h, E=None, qblocks=None, idx=None,
     o_lr[valid] = lowrank_readout(fq, w, S, z, cfg.eps, rows[valid])
     o_lr = o_lr.reshape(len(qblocks), bs, -1)
     res["o_sp"], res["o_lr"] = o_sp, o_lr
-    res["out"] = o_sp + float(gate_h) * o_lr
+    if token_gate_wb is None:
+        res["out"] = o_sp + float(gate_h) * o_lr
+    else:
+        D = q.shape[1]
+        qrows = np.zeros((len(rows), D))
+        qrows[valid] = _d(q)[rows[valid]]
+        out, g = token_gate(qrows, token_gate_wb[0], token_gate_wb[1], o_sp.reshape(-1, D), o_lr.reshape(-1, D),
+                            cfg.eps)
+        res["out"] = out.reshape(o_sp.shape)
+        res["g"] = g.reshape(len(qblocks), bs)
     return res

@@ -27,7 +27,11 @@
  *    go to the lower block index; indices are stored ascending;
  *  - softmax scale is 1/sqrt(D);
  *  - phi(x) = elu(x) + 1; the normaliser uses the un-rotated features plus
- *    eps after the dot; the combine is additive with a per-head gate.
+ *    eps after the dot; the combine is additive with a per-head gate;
+ *  - the token-wise gate (optional) reads the token's raw query row, is a
+ *    logistic of one linear form plus a bias, and the low-rank output is
+ *    rescaled to the RMS (over the head dims) of the sparse output before
+ *    it is added (see orc_token_gate).
  */
 #include <math.h>
 #include <stdint.h>
@@ -292,5 +296,33 @@ void orc_lowrank_readout(int D, int r, int nrows, const int64_t *rows, const dou
             for (int c = 0; c < r; ++c) num += fq[l * r + c] * S[(long)c * D + d];
             out[(long)n * D + d] = num / den;
         }
+    }
+}
+
+/*
+ * Token-wise gated fusion ([RoLA] §4.4 "Feature Alignment and Gated
+ * Fusion"): a scalar gate per token combines the sparse and the low-rank
+ * outputs, and the sparse output's RMS is the scale reference of the fusion.
+ * For each of the n rows:
+ *   g     = 1 / (1 + exp(-(q . wg + bg)))        (q = the raw query row)
+ *   rms_s = sqrt(sum_d o_sp[d]^2 / D),  rms_l = sqrt(sum_d o_lr[d]^2 / D)
+ *   out   = o_sp + g * rms_s / (rms_l + eps) * o_lr
+ * The gate value of every row goes to gate[] when it is not NULL.
+ */
+void orc_token_gate(long n, int D, const double *q, const double *wg, double bg, const double *o_sp,
+                    const double *o_lr, double eps, double *out, double *gate)
+{
+    for (long i = 0; i < n; ++i) {
+        double t = bg;
+        for (int d = 0; d < D; ++d) t += q[i * D + d] * wg[d];
+        double g = 1.0 / (1.0 + exp(-t));
+        double ss = 0.0, sl = 0.0;
+        for (int d = 0; d < D; ++d) {
+            ss += o_sp[i * D + d] * o_sp[i * D + d];
+            sl += o_lr[i * D + d] * o_lr[i * D + d];
+        }
+        double scale = sqrt(ss / D) / (sqrt(sl / D) + eps);
+        for (int d = 0; d < D; ++d) out[i * D + d] = o_sp[i * D + d] + g * scale * o_lr[i * D + d];
+        if (gate) gate[i] = g;
     }
 }
