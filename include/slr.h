@@ -11,7 +11,11 @@
  *     after phi (RoLA §4.2-4.3) or learnable per-axis absolute embeddings
  *     added before phi (RoPeSLR abstract), read out through one reusable
  *     per-head summary S = sum rho(phi(k)) v^T, z = sum phi(k);
- *   - an additive per-head gated combine  O = O_sparse + g_h * O_lowrank.
+ *   - an additive gated combine: per head,  O = O_sparse + g_h * O_lowrank,
+ *     or per token (RoLA §4.4 "Feature Alignment and Gated Fusion"),
+ *     O = O_sparse + sigmoid(q . W_g + b_g) * RMS(O_sparse) / (RMS(O_lowrank)
+ *     + eps) * O_lowrank, with q the token's raw query row and the RMS taken
+ *     over the head dims.
  *
  * Conventions shared by every entry point
  *   Tensors q, k, v, out are [B, H, L, D] contiguous, L = T*Hg*Wg tokens
@@ -62,6 +66,10 @@ extern "C" {
 #define SLR_LR_ROPE_OUTSIDE 0  /* RoLA: truncated rotary schedule after phi      */
 #define SLR_LR_ABS_PE 1        /* RoPeSLR: E_t[t]+E_h[h]+E_w[w] added before phi */
 
+/* Gate of the combine (slr_lowrank_cfg.gate_mode) */
+#define SLR_GATE_HEAD 0        /* one scalar g_h per head: gate[H]                 */
+#define SLR_GATE_TOKEN 1       /* RoLA §4.4: per token, from Wg[H, D] and bg[H]    */
+
 /* operations, for slr_workspace_bytes */
 #define SLR_OP_ROPE3D 0
 #define SLR_OP_SELECT 1
@@ -92,8 +100,11 @@ typedef struct {
                                     <= the backbone pairs of its axis; ignored for ABS_PE */
     float eps;                   /* normaliser epsilon (> 0), e.g. 1e-6             */
     const float *Wq, *Wk;        /* [H, D, r] fp32; bf16 layers use them rounded to bf16 */
-    const float *gate;           /* [H] fp32, the per-head gate g_h                 */
+    const float *gate;           /* [H] fp32, the per-head gate g_h (SLR_GATE_HEAD)   */
     const float *Et, *Eh, *Ew;   /* ABS_PE only: [T, r], [Hg, r], [Wg, r] fp32; else NULL */
+    int32_t gate_mode;           /* SLR_GATE_HEAD or SLR_GATE_TOKEN                 */
+    const float *Wg;             /* SLR_GATE_TOKEN: [H, D] fp32 gate weights, else NULL */
+    const float *bg;             /* SLR_GATE_TOKEN: [H] fp32 gate biases, else NULL */
 } slr_lowrank_cfg;
 
 /*

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libslr.so")
 SLR_OK, SLR_EINVAL, SLR_EUNSUPPORTED, SLR_EWORKSPACE, SLR_EHIP = 0, -1, -2, -3, -4
 SLR_F32, SLR_BF16 = 0, 1
 SLR_LR_ROPE_OUTSIDE, SLR_LR_ABS_PE = 0, 1
+SLR_GATE_HEAD, SLR_GATE_TOKEN = 0, 1
 SLR_OP_ROPE3D, SLR_OP_SELECT, SLR_OP_LOWRANK_SUMMARY, SLR_OP_ATTENTION, SLR_OP_DENSE = 0, 1, 2, 3, 4
 
 EXPORTS = ("slr_workspace_bytes", "slr_rope3d", "slr_select_blocks", "slr_lowrank_summary",
@@ -44,7 +45,8 @@ class SlrLowrankCfg(ctypes.Structure):
     _fields_ = [("rank", ctypes.c_int32), ("mode", ctypes.c_int32), ("lr_pairs_t", ctypes.c_int32),
                 ("lr_pairs_h", ctypes.c_int32), ("lr_pairs_w", ctypes.c_int32), ("eps", ctypes.c_float),
                 ("Wq", ctypes.c_void_p), ("Wk", ctypes.c_void_p), ("gate", ctypes.c_void_p),
-                ("Et", ctypes.c_void_p), ("Eh", ctypes.c_void_p), ("Ew", ctypes.c_void_p)]
+                ("Et", ctypes.c_void_p), ("Eh", ctypes.c_void_p), ("Ew", ctypes.c_void_p),
+                ("gate_mode", ctypes.c_int32), ("Wg", ctypes.c_void_p), ("bg", ctypes.c_void_p)]
 
 
 class SlrError(RuntimeError):
@@ -121,12 +123,16 @@ def sparse_of(layer) -> SlrSparseCfg:
 def lowrank_of(layer, params: Dict[str, torch.Tensor]) -> SlrLowrankCfg:
     abspe = layer.lr_mode == "abspe"
     lp = (0, 0, 0) if abspe else tuple(layer.lr_pairs)
+    token = getattr(layer, "gate", "head") == "token"
     return SlrLowrankCfg(layer.rank, SLR_LR_ABS_PE if abspe else SLR_LR_ROPE_OUTSIDE, lp[0], lp[1], lp[2],
                          float(layer.eps), params["wq"].data_ptr(), params["wk"].data_ptr(),
                          params["gate"].data_ptr(),
                          params["et"].data_ptr() if abspe else None,
                          params["eh"].data_ptr() if abspe else None,
-                         params["ew"].data_ptr() if abspe else None)
+                         params["ew"].data_ptr() if abspe else None,
+                         SLR_GATE_TOKEN if token else SLR_GATE_HEAD,
+                         params["wg"].data_ptr() if token else None,
+                         params["bg"].data_ptr() if token else None)
 
 
 def slr_workspace_bytes(op: int, shape: SlrShape, rope: SlrRopeCfg, sparse: Optional[SlrSparseCfg] = None,

@@ -39,7 +39,10 @@ __device__ __forceinline__ float2 lr_cossin_q(const float2* __restrict__ tab, co
 // O^T accumulator dims 32db + 8(i/4) + 4hf + i%4. Normalises the sparse
 // branch, evaluates the low-rank readout rho(w)^T S / (w . z + eps) with
 // w = phi(q W_q [+ E]) on MFMA (hi/lo bf16 splits of w and S for ~fp32
-// accuracy), combines with the per-head gate and stores bf16 rows.
+// accuracy), combines with the gate and stores bf16 rows. The gate is the
+// head's scalar, or (token gate, RoLA §4.4) sigmoid(q . W_g + b_g) of the
+// token's raw query row times RMS(O_sparse) / (RMS(O_lowrank) + eps), both
+// RMS over the head dims of the row.
 template <int D, int RP, int LR>
 __device__ __forceinline__ void flash_epilogue(const FlashArgs& a, long bh, int head, long q0, float lsum,
                                                const f32x16_t* oacc) {
@@ -109,15 +112,33 @@ __device__ __forceinline__ void flash_epilogue(const FlashArgs& a, long bh, int 
         }
         den = sum_xor32(den);
         rden = 1.f / (den + a.eps);
-        gsc = a.gate[head];
+        if (a.gate_mode == 0) {
+            gsc = a.gate[head];
+        } else {
+            // token gate logit: this lane's dims 16s + 8hf .. +7, then the pair lane's
+            float t = 0.f;
+            if (qval) {
+                const float* wgh = a.wg + (long)head * D;
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const u32x4_t qv = ldg16(qraw + 16 * s + 8 * hf);
+                    const float4 w0 = *reinterpret_cast<const float4*>(wgh + 16 * s + 8 * hf);
+                    const float4 w1 = *reinterpret_cast<const float4*>(wgh + 16 * s + 8 * hf + 4);
+                    t += bf_lo(qv[0]) * w0.x + bf_hi(qv[0]) * w0.y + bf_lo(qv[1]) * w0.z + bf_hi(qv[1]) * w0.w;
+                    t += bf_lo(qv[2]) * w1.x + bf_hi(qv[2]) * w1.y + bf_lo(qv[3]) * w1.z + bf_hi(qv[3]) * w1.w;
+                }
+            }
+            gsc = 1.f / (1.f + __expf(-(sum_xor32(t) + a.bg[head])));
+        }
     }
     uint16_t* out = (uint16_t*)a.out + (bh * L + (qval ? qrow : 0)) * D;
     uint16_t* osp = a.o_sp ? (uint16_t*)a.o_sp + (bh * L + (qval ? qrow : 0)) * D : nullptr;
     uint16_t* olr = a.o_lr ? (uint16_t*)a.o_lr + (bh * L + (qval ? qrow : 0)) * D : nullptr;
-    // one 32-dim block at a time: num^T = S^T rho(w)^T (m = d, k = r, n = query), combine, store
+    // num^T = S^T rho(w)^T, one 32-dim block per accumulator (m = d, k = r, n = query)
+    f32x16_t nall[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-        f32x16_t nacc;
+        f32x16_t& nacc = nall[db];
 #pragma unroll
         for (int i = 0; i < 16; ++i) nacc[i] = 0.f;
         if (LR != 0) {
@@ -133,6 +154,26 @@ __device__ __forceinline__ void flash_epilogue(const FlashArgs& a, long bh, int 
                     nacc = mfma32(sl, whi[rb][h2], nacc);
                 }
         }
+    }
+    if (LR != 0 && a.gate_mode != 0) {
+        // token gate: scale the low-rank rows to the sparse rows' RMS
+        float ss = 0.f, sl = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float xs = oacc[db][i] * inv, xl = nall[db][i] * rden;
+                ss += xs * xs;
+                sl += xl * xl;
+            }
+        ss = sum_xor32(ss);
+        sl = sum_xor32(sl);
+        gsc *= sqrtf(ss * (1.f / D)) / (sqrtf(sl * (1.f / D)) + a.eps);
+    }
+    // combine, store
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const f32x16_t& nacc = nall[db];
         if (qval) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
@@ -628,8 +669,24 @@ __global__ __launch_bounds__(64) void k_flash_f32(FlashArgs a, int BS) {
         }
     }
     const float rd = 1.f / (den + a.eps);
-    const float gs = a.gate[head];
     const float* S = a.S + bh * (long)R * D;
+    float gs;
+    if (a.gate_mode == 0) {
+        gs = a.gate[head];
+    } else {
+        // token gate (RoLA §4.4): sigmoid(q . W_g + b_g) * RMS(O_sparse) / (RMS(O_lowrank) + eps)
+        const float* wgh = a.wg + (long)head * D;
+        float t = a.bg[head], ss = 0.f, sl = 0.f;
+        for (int d = 0; d < D; ++d) t += qraw[d] * wgh[d];
+        for (int d = 0; d < D; ++d) {
+            float num = 0.f;
+            for (int r = 0; r < R; ++r) num += f[r] * S[(long)r * D + d];
+            const float sp = o[d] * inv, lr = num * rd;
+            ss += sp * sp;
+            sl += lr * lr;
+        }
+        gs = 1.f / (1.f + expf(-t)) * sqrtf(ss / D) / (sqrtf(sl / D) + a.eps);
+    }
     for (int d = 0; d < D; ++d) {
         float num = 0.f;
         for (int r = 0; r < R; ++r) num += f[r] * S[(long)r * D + d];

@@ -79,7 +79,16 @@ int check_lowrank(const slr_lowrank_cfg* lr, const slr_rope_cfg* rope, const Dim
     if (lr->mode != SLR_LR_ROPE_OUTSIDE && lr->mode != SLR_LR_ABS_PE) return SLR_EINVAL;
     if (!std::isfinite(lr->eps) || !(lr->eps > 0.f)) return SLR_EINVAL;
     if (!lr->Wk || !aligned(lr->Wk, 4)) return SLR_EINVAL;
-    if (need_q && (!lr->Wq || !aligned(lr->Wq, 4) || !lr->gate || !aligned(lr->gate, 4))) return SLR_EINVAL;
+    if (need_q) {
+        if (!lr->Wq || !aligned(lr->Wq, 4)) return SLR_EINVAL;
+        if (lr->gate_mode == SLR_GATE_HEAD) {
+            if (!lr->gate || !aligned(lr->gate, 4)) return SLR_EINVAL;
+        } else if (lr->gate_mode == SLR_GATE_TOKEN) {
+            if (!lr->Wg || !aligned(lr->Wg, 16) || !lr->bg || !aligned(lr->bg, 4)) return SLR_EINVAL;
+        } else {
+            return SLR_EINVAL;
+        }
+    }
     lg->lp[0] = lg->lp[1] = lg->lp[2] = 0;
     if (lr->mode == SLR_LR_ROPE_OUTSIDE) {
         if (lr->lr_pairs_t < 0 || lr->lr_pairs_h < 0 || lr->lr_pairs_w < 0) return SLR_EINVAL;
@@ -246,6 +255,7 @@ int slr_workspace_bytes(int op, const slr_shape* shape, const slr_rope_cfg* rope
         float dummy[4] __attribute__((aligned(16)));
         probe.Wq = probe.Wk = probe.gate = dummy;
         probe.Et = probe.Eh = probe.Ew = dummy;
+        probe.Wg = probe.bg = dummy;
         if ((st = check_lowrank(&probe, rope, d, op == SLR_OP_ATTENTION, &lg, &RP))) return st;
         R = lowrank->rank;
     }
@@ -406,6 +416,9 @@ int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sp
     a.S = S;
     a.zp = d.bf16 ? at<float>(ws, w.zp) : z;
     a.gate = lowrank->gate;
+    a.gate_mode = lowrank->gate_mode;
+    a.wg = lowrank->Wg;
+    a.bg = lowrank->bg;
     a.Et = lowrank->Et; a.Eh = lowrank->Eh; a.Ew = lowrank->Ew;
     a.tab = tab;
     a.g = lg;

@@ -29,7 +29,10 @@ struct FlashArgs {
     const uint16_t* st_lo;
     const float* S;          // fp32 layers: S [BH][R][D]
     const float* zp;         // [BH][RP] (bf16 layers) or [BH][R] (fp32 layers)
-    const float* gate;       // [H]
+    const float* gate;       // [H] per-head gate (gate_mode 0)
+    int gate_mode;           // 0: per-head gate; 1: per-token gate from wg, bg
+    const float* wg;         // [H, D] token-gate weights
+    const float* bg;         // [H] token-gate biases
     const float *Et, *Eh, *Ew;
     const float2* tab;
     LrGeom g;

@@ -34,6 +34,7 @@ import numpy as np
 # tensor ids of the per-slice random streams
 TID_Q, TID_K, TID_V, TID_WQ, TID_WK, TID_GATE, TID_CENT, TID_CLUSTER = 0, 1, 2, 3, 4, 5, 6, 7
 TID_ET, TID_EH, TID_EW = 8, 9, 10
+TID_WG, TID_BG = 11, 12
 TID_SAMPLE = 99  # query-block sample for the oracle's partial coverage
 
 N_CENTROIDS = 64
@@ -64,6 +65,7 @@ class Layer:
     seed: int
     gen: str                       # "normal", "clustered" or "zero_qk" (q = k = 0: every block score ties)
     eps: float = 1e-6
+    gate: str = "head"             # combine gate: "head" (g_h) or "token" (RoLA §4.4)
 
     @property
     def L(self) -> int:
@@ -199,8 +201,10 @@ def qkv_slice(cfg: Layer, b: int, h: int, L: Optional[int] = None) -> Tuple[np.n
 
 def lowrank_params(cfg: Layer) -> Dict[str, np.ndarray]:
     """Per-head projections W_q, W_k [H, D, r] ~ N(0, 1/D) (variance), the
-    per-head gate g [H] ~ U(0, 1), and for the absolute-PE variant the axis
-    tables E_t [T, r], E_h [Hg, r], E_w [Wg, r] ~ N(0, 0.02) (variance)."""
+    per-head gate g [H] ~ U(0, 1), for the token gate W_g [H, D] ~ N(0, 1/D)
+    and b_g [H] ~ U(-2, 0.5) (a mostly negative bias, as the pages start
+    the gate), and for the absolute-PE variant the axis tables E_t [T, r],
+    E_h [Hg, r], E_w [Wg, r] ~ N(0, 0.02) (variance)."""
     H, D, r = cfg.H, cfg.D, cfg.rank
     std = np.float32(1.0 / math.sqrt(D))
     wq = np.stack([_rng(cfg.seed, TID_WQ, 0, h).standard_normal((D, r), dtype=np.float32) * std
@@ -209,6 +213,9 @@ def lowrank_params(cfg: Layer) -> Dict[str, np.ndarray]:
                    for h in range(H)])
     g = _rng(cfg.seed, TID_GATE).uniform(0.0, 1.0, size=H).astype(np.float32)
     out = {"wq": wq, "wk": wk, "gate": g}
+    if cfg.gate == "token":
+        out["wg"] = _rng(cfg.seed, TID_WG).standard_normal((H, D), dtype=np.float32) * std
+        out["bg"] = _rng(cfg.seed, TID_BG).uniform(-2.0, 0.5, size=H).astype(np.float32)
     if cfg.lr_mode == "abspe":
         es = np.float32(math.sqrt(EMBED_VAR))
         out["et"] = _rng(cfg.seed, TID_ET).standard_normal((cfg.T, r), dtype=np.float32) * es

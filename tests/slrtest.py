@@ -124,8 +124,11 @@ def check_layer(inp: Inputs, out, idx, o_sp, o_lr, slices: Optional[Iterable] = 
         qs, ks, vs = synth.qkv_slice(cfg, b, h)
         ig = idx[b, h].cpu().numpy()
         qblocks = None if qblocks_per_slice is None else synth.sample_query_blocks(cfg, b, h, qblocks_per_slice)
+        tg = None
+        if cfg.gate == "token":
+            tg = (inp.params_np["wg"][h], float(inp.params_np["bg"][h]))
         res = oracle.layer_slice(cfg, qs, ks, vs, inp.params_np["wq"][h], inp.params_np["wk"][h],
-                                 inp.params_np["gate"][h], E, qblocks=qblocks, idx=ig)
+                                 inp.params_np["gate"][h], E, qblocks=qblocks, idx=ig, token_gate_wb=tg)
         check_selection(ig, res["scores"], res["thr"], cfg.keep)
         differ += rows_differing(ig, res["idx_ref"])
         qb = res["qblocks"]

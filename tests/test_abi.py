@@ -100,7 +100,9 @@ def test_bad_sparse(block, keep):
     assert _attn(shape, rope, sparse, lr) == B.SLR_EINVAL
 
 
-@pytest.mark.parametrize("change", ["rank", "pairs_sum", "pairs_axis", "mode", "eps", "wq", "abspe_tables"])
+@pytest.mark.parametrize("change", ["rank", "pairs_sum", "pairs_axis", "mode", "eps", "wq", "abspe_tables",
+                                    "gate_mode", "head_gate_null", "token_wg_null", "token_bg_null",
+                                    "token_wg_misaligned"])
 def test_bad_lowrank(change):
     shape, rope, sparse, lr = _cfgs()
     if change == "rank":
@@ -117,7 +119,28 @@ def test_bad_lowrank(change):
         lr.Wq = None
     elif change == "abspe_tables":
         lr.mode = B.SLR_LR_ABS_PE
+    elif change == "gate_mode":
+        lr.gate_mode = 2
+    elif change == "head_gate_null":
+        lr.gate = None
+    elif change.startswith("token"):
+        lr.gate_mode, lr.gate, lr.Wg, lr.bg = B.SLR_GATE_TOKEN, None, FAKE, FAKE
+        if change == "token_wg_null":
+            lr.Wg = None
+        elif change == "token_bg_null":
+            lr.bg = None
+        else:
+            lr.Wg = MISALIGNED + 4     # 4-byte aligned, not 16
     assert _attn(shape, rope, sparse, lr) == B.SLR_EINVAL
+
+
+def test_token_gate_config_is_accepted_by_sizing():
+    """With the gate pointers in place the token gate needs no extra
+    workspace and passes the host checks (sizing does not read pointers)."""
+    shape, rope, sparse, lr = _cfgs()
+    n_head = B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lr)
+    lr.gate_mode, lr.gate, lr.Wg, lr.bg = B.SLR_GATE_TOKEN, None, FAKE, FAKE
+    assert B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lr) == n_head
 
 
 def test_null_and_misaligned_tensors():

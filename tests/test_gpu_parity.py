@@ -117,6 +117,40 @@ def test_gate_zero_gives_sparse_branch():
     assert torch.equal(out, o_sp)
 
 
+TOKEN_GATE = [
+    # D, block, rank, mode, grid, keep, dtype: the three flash kernels (tiled bf16, other bf16, fp32)
+    (128, 64, 32, "rola", (5, 9, 13), 3, "bf16"),
+    (128, 64, 32, "abspe", (3, 5, 17), 4, "bf16"),
+    (64, 32, 8, "rola", (4, 8, 8), 2, "bf16"),
+    (128, 32, 16, "rola", (3, 7, 11), 3, "bf16"),
+    (128, 64, 32, "rola", (5, 9, 13), 3, "f32"),
+    (64, 64, 16, "abspe", (3, 6, 7), 2, "f32"),
+]
+
+
+@pytest.mark.parametrize("D,bs,r,mode,grid,keep,dtype", TOKEN_GATE)
+def test_token_gate_layers(D, bs, r, mode, grid, keep, dtype):
+    """Token-wise gated fusion (RoLA §4.4) against the oracle."""
+    p = r // 2
+    lp = (p // 2, p // 4, p - p // 2 - p // 4) if mode == "rola" else (0, 0, 0)
+    pairs = (12, 10, 10) if D == 64 else (22, 21, 21)
+    cfg = T.custom(synth.wan13b(), name=f"token gate D{D} bs{bs} r{r} {mode} {grid} k{keep} {dtype}", B=2, H=3,
+                   D=D, T=grid[0], Hg=grid[1], Wg=grid[2], block=bs, keep=keep, rank=r, lr_mode=mode, lr_pairs=lp,
+                   pairs=pairs, dtype=dtype, seed=9, gate="token")
+    _full_check(cfg)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_token_gate_very_negative_bias_gives_sparse_branch(dtype):
+    cfg = T.custom(synth.wan13b(), name=f"token gate off {dtype}", B=1, H=2, T=3, Hg=5, Wg=9, keep=2, dtype=dtype,
+                   gate="token")
+    inp = T.make_inputs(cfg)
+    inp.params["bg"].fill_(-1e4)
+    out, _, o_sp, _ = T.run_layer(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o_sp)
+
+
 def test_runs_are_bitwise_reproducible():
     cfg = T.custom(synth.wan13b(), name="repro", B=1, H=4, T=4, Hg=9, Wg=13, keep=5)
     inp = T.make_inputs(cfg)
