@@ -34,8 +34,8 @@ PEAK_HBM_GBS = 8000.0
 # on, identified by the sha256 of its files; any other source reports null.
 FLASH_TRAFFIC_SOURCES = ["k_flash.hip", "slr_common.h", "slr_launch.h"]
 FLASH_TRAFFIC = {
-    "sha256": "522e4504c949f0dfcbabb9f5022abdfe68c51429c65bab5c8c65a64b091882e6",
-    "bytes_per_launch": {"wan13b": 8276.3e6 + 202.0e6, "wan14b": 219812.6e6 + 1577.1e6},
+    "sha256": "08070d84c0477d8fab12e17ec0e054e84b2ce1833ec8d768389607cc8c392a62",
+    "bytes_per_launch": {"wan13b": 8389.6e6 + 201.3e6, "wan14b": 217956.6e6 + 1548.4e6},
 }
 
 
@@ -160,7 +160,10 @@ def cpu_baseline(cfg, blocks: int):
     rows = (qblocks[:, None].astype(np.int64) * cfg.block + np.arange(cfg.block)[None, :]).reshape(-1)
     rows = rows[rows < cfg.L]
     oracle.block_sparse_attention(qr, kr, v, cfg.block, idx, qblocks)
-    oracle.lowrank_readout(fq, w, S, z, cfg.eps, rows)
+    o_lr = oracle.lowrank_readout(fq, w, S, z, cfg.eps, rows)
+    if cfg.gate == "token":
+        o_sp = np.zeros_like(o_lr)   # the gate's cost does not depend on the values
+        oracle.token_gate(q[rows], p["wg"][0], float(p["bg"][0]), o_sp, o_lr, cfg.eps)
     t2 = time.perf_counter()
     per_slice = (t1 - t0) + (t2 - t1) * cfg.nblk / len(qblocks)
     layer_s = per_slice * cfg.B * cfg.H
@@ -216,6 +219,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan13b", choices=["wan13b", "wan14b", "hunyuan13b"])
+    ap.add_argument("--gate", default="head", choices=["head", "token"],
+                    help="combine gate: one scalar per head (the workloads' default) or the token-wise gate")
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--cpu-blocks", type=int, default=512, help="query blocks the CPU oracle samples")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -251,6 +256,9 @@ def main() -> int:
         return run_sweep(args, torch, B, synth)
 
     cfg = synth.by_name(args.workload)
+    if args.gate != "head":
+        import dataclasses
+        cfg = dataclasses.replace(cfg, gate=args.gate)
     print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     q, k, v, params = make_device_inputs(cfg, torch)
     shape, rope, sparse = B.shape_of(cfg), B.rope_of(cfg), B.sparse_of(cfg)
@@ -352,7 +360,7 @@ def main() -> int:
         "data": "synthetic (seeded clustered Q/K, Gaussian V; random-init projections)",
         "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "D": cfg.D, "L": cfg.L,
                    "grid": [cfg.T, cfg.Hg, cfg.Wg], "block": cfg.block, "keep": cfg.keep, "nblk": cfg.nblk,
-                   "rank": cfg.rank, "lowrank": cfg.lr_mode, "parallelism": "single GPU"},
+                   "rank": cfg.rank, "lowrank": cfg.lr_mode, "gate": cfg.gate, "parallelism": "single GPU"},
         "roofline": {"kernel": "k_flash_tiled (block-sparse flash + low-rank readout + combine)",
                      "bound": "mfma", "achieved": round(flash_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flash_tf / PEAK_BF16_TFLOPS, 4), "traffic": flash_traffic(args.workload),
