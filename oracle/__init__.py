@@ -9,7 +9,8 @@ it with ctypes and chains its steps in the order the method states
   rotate q, k (3D RoPE) -> block means -> block scores -> top-k blocks
   -> block-sparse softmax attention                        (sparse branch)
   phi(k W_k) -> rotate after phi -> summary S, z
-  phi(q W_q) -> rotate after phi -> readout S / (w.z + eps)   (low-rank)
+  phi(q W_q) -> rotate after phi -> readout S / (w.z + eps)   (low-rank;
+                                    phi = elu + 1, or SiLU with readout S / L)
   O = O_sparse + g_h * O_lowrank                              (combine)
   or, token-wise (RoLA §4.4): O = O_sparse + g(q) * RMS-aligned O_lowrank
 
@@ -58,11 +59,11 @@ def _load():
         lib.orc_topk_blocks.argtypes = [ctypes.c_long, ctypes.c_int, _dp, _ip, _dp, _dp]
         lib.orc_block_sparse_attention.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                    _dp, _dp, _dp, _ip, ctypes.c_int, _ip, _dp]
-        lib.orc_lowrank_features.argtypes = [ctypes.c_int] * 5 + [_dp] * 6
+        lib.orc_lowrank_features.argtypes = [ctypes.c_int] * 5 + [_dp] * 5 + [ctypes.c_int, _dp]
         lib.orc_lowrank_rotate.argtypes = [ctypes.c_int] * 3 + [i3, ctypes.c_int, ctypes.c_double, i3, i3, _dp, _dp]
         lib.orc_lowrank_summary.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp, _dp]
         lib.orc_lowrank_readout.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _lp, _dp, _dp, _dp, _dp,
-                                            ctypes.c_double, _dp]
+                                            ctypes.c_double, ctypes.c_double, _dp]
         lib.orc_token_gate.argtypes = [ctypes.c_long, ctypes.c_int, _dp, _dp, ctypes.c_double, _dp, _dp,
                                        ctypes.c_double, _dp, _dp]
         for f in ("orc_rope3d", "orc_block_mean", "orc_block_scores", "orc_topk_blocks",
@@ -147,13 +148,17 @@ def dense_attention(qr, kr, v, bs) -> np.ndarray:
     return block_sparse_attention(qr, kr, v, bs, idx).reshape(-1, qr.shape[1])[:L]
 
 
-def lowrank_features(x, W, grid, E=None) -> np.ndarray:
+FMAPS = {"elu1": 0, "silu": 1}
+
+
+def lowrank_features(x, W, grid, E=None, fmap="elu1") -> np.ndarray:
+    """phi(x W [+ E]) per token; fmap "elu1" (elu + 1) or "silu"."""
     x, W = _d(x), _d(W)
     T, Hg, Wg = grid
     D, r = W.shape
     u = np.empty((x.shape[0], r))
     et, eh, ew = (None, None, None) if E is None else tuple(_d(e) for e in E)
-    _load().orc_lowrank_features(T, Hg, Wg, D, r, _p(x), _p(W), _p(et), _p(eh), _p(ew), _p(u))
+    _load().orc_lowrank_features(T, Hg, Wg, D, r, _p(x), _p(W), _p(et), _p(eh), _p(ew), FMAPS[fmap], _p(u))
     return u
 
 
@@ -176,13 +181,14 @@ def lowrank_summary(fk, u, v):
     return S, z
 
 
-def lowrank_readout(fq, w, S, z, eps, rows=None) -> np.ndarray:
+def lowrank_readout(fq, w, S, z, eps, rows=None, count=0.0) -> np.ndarray:
+    """count > 0 replaces the denominator w.z + eps by count (mean readout)."""
     fq, w, S, z = _d(fq), _d(w), _d(S), _d(z)
     r, D = S.shape
     rows = np.arange(fq.shape[0], dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     out = np.empty((len(rows), D))
     _load().orc_lowrank_readout(D, r, len(rows), rows.ctypes.data_as(_lp), _p(fq), _p(w), _p(S), _p(z),
-                                float(eps), _p(out))
+                                float(eps), float(count), _p(out))
     return out
 
 
@@ -225,20 +231,21 @@ def layer_slice(cfg, q, k, v, wq, wk, gate_h, E=None, qblocks=None, idx=None,
     res["qblocks"] = qblocks
     o_sp = block_sparse_attention(qr, kr, v, bs, use_idx, qblocks)
 
+    fmap = getattr(cfg, "fmap", "elu1")
     if cfg.lr_mode == "rola":
-        u = lowrank_features(k, wk, grid)
-        w = lowrank_features(q, wq, grid)
+        u = lowrank_features(k, wk, grid, fmap=fmap)
+        w = lowrank_features(q, wq, grid, fmap=fmap)
         fk = lowrank_rotate(u, grid, cfg.base, cfg.pairs, cfg.lr_pairs, origin)
         fq = lowrank_rotate(w, grid, cfg.base, cfg.pairs, cfg.lr_pairs, origin)
     else:
-        u = lowrank_features(k, wk, grid, E)
-        w = lowrank_features(q, wq, grid, E)
+        u = lowrank_features(k, wk, grid, E, fmap=fmap)
+        w = lowrank_features(q, wq, grid, E, fmap=fmap)
         fk, fq = u, w
     res["S"], res["z"] = S, z = lowrank_summary(fk, u, v)
     rows = (qblocks[:, None].astype(np.int64) * bs + np.arange(bs)[None, :]).reshape(-1)
     valid = rows < L
     o_lr = np.zeros((len(rows), q.shape[1]))
-    o_lr[valid] = lowrank_readout(fq, w, S, z, cfg.eps, rows[valid])
+    o_lr[valid] = lowrank_readout(fq, w, S, z, cfg.eps, rows[valid], count=float(L) if fmap == "silu" else 0.0)
     o_lr = o_lr.reshape(len(qblocks), bs, -1)
     res["o_sp"], res["o_lr"] = o_sp, o_lr
     if token_gate_wb is None:

@@ -28,6 +28,8 @@
  *  - softmax scale is 1/sqrt(D);
  *  - phi(x) = elu(x) + 1; the normaliser uses the un-rotated features plus
  *    eps after the dot; the combine is additive with a per-head gate;
+ *  - with the SiLU feature map (optional; sign-indefinite) the normaliser
+ *    is the number of valid tokens instead;
  *  - the token-wise gate (optional) reads the token's raw query row, is a
  *    logistic of one linear form plus a bias, and the low-rank output is
  *    rescaled to the RMS (over the head dims) of the sparse output before
@@ -211,6 +213,10 @@ void orc_block_sparse_attention(long L, int D, int bs, int k, const double *qr, 
 /* phi(x) = elu(x) + 1: x + 1 for x > 0, exp(x) otherwise. */
 static double phi(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
 
+/* SiLU(x) = x * sigmoid(x) = x / (1 + exp(-x)): the activation RoLA's
+ * ablation finds best ([RoLA] §5.3, Table 6). */
+static double silu(double x) { return x / (1.0 + exp(-x)); }
+
 /*
  * Low-rank features u_l = phi(x_l W [+ E_t[t] + E_h[h] + E_w[w]]) of a
  * [L, D] slice with W [D, r]. The rotary variant ([RoLA] §4.3) feeds the
@@ -219,7 +225,7 @@ static double phi(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
  * injection) adds the per-axis tables before phi.
  */
 void orc_lowrank_features(int T, int Hg, int Wg, int D, int r, const double *x, const double *W,
-                          const double *Et, const double *Eh, const double *Ew, double *u)
+                          const double *Et, const double *Eh, const double *Ew, int fmap, double *u)
 {
     long L = (long)T * Hg * Wg;
     for (long l = 0; l < L; ++l) {
@@ -229,7 +235,7 @@ void orc_lowrank_features(int T, int Hg, int Wg, int D, int r, const double *x, 
             double acc = 0.0;
             for (int d = 0; d < D; ++d) acc += x[l * D + d] * W[(long)d * r + c];
             if (Et) acc += Et[(long)t * r + c] + Eh[(long)h * r + c] + Ew[(long)w * r + c];
-            u[l * r + c] = phi(acc);
+            u[l * r + c] = fmap ? silu(acc) : phi(acc);
         }
     }
 }
@@ -280,17 +286,21 @@ void orc_lowrank_summary(long L, int D, int r, const double *fk, const double *u
  * Per-query readout of the summary ([RoLA] App. A, Algorithm 1; §4.3):
  *   O_lr,l = (fq_l^T S) / (w_l . z + eps)
  * for the listed token rows; fq = rotated query features (plain ones for
- * the absolute-PE variant), w = un-rotated query features.
+ * the absolute-PE variant), w = un-rotated query features. With count > 0
+ * (sign-indefinite features such as SiLU, where w . z can vanish) the
+ * denominator is count, the number of valid tokens: the readout is then the
+ * mean over the tokens.
  */
 void orc_lowrank_readout(int D, int r, int nrows, const int64_t *rows, const double *fq,
                          const double *w, const double *S, const double *z, double eps,
-                         double *out)
+                         double count, double *out)
 {
     for (int n = 0; n < nrows; ++n) {
         long l = rows[n];
         double den = 0.0;
         for (int c = 0; c < r; ++c) den += w[l * r + c] * z[c];
         den += eps;
+        if (count > 0.0) den = count;   /* sign-indefinite features: mean over the tokens */
         for (int d = 0; d < D; ++d) {
             double num = 0.0;
             for (int c = 0; c < r; ++c) num += fq[l * r + c] * S[(long)c * D + d];

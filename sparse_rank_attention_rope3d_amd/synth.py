@@ -66,6 +66,7 @@ class Layer:
     gen: str                       # "normal", "clustered" or "zero_qk" (q = k = 0: every block score ties)
     eps: float = 1e-6
     gate: str = "head"             # combine gate: "head" (g_h) or "token" (RoLA §4.4)
+    fmap: str = "elu1"             # low-rank feature map: "elu1" (elu + 1) or "silu" (RoLA §5.3)
 
     @property
     def L(self) -> int:

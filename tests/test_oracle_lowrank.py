@@ -202,3 +202,76 @@ def test_abspe_table_follows_its_axis(axis):
     assert np.ptp(u, axis=axis).min() > 0.0
     want = np.exp(np.minimum(E[axis], 0)) + np.maximum(E[axis], 0)  # elu(x) + 1
     np.testing.assert_allclose(np.moveaxis(u, axis, 0)[:, 0, 0], want, rtol=1e-15)
+
+
+# ---- SiLU feature map (RoLA §5.3, Table 6: the best of the tested activations) ----
+
+def test_silu_is_x_times_sigmoid():
+    x = np.linspace(-30, 30, 241).reshape(1, -1)
+    u = oracle.lowrank_features(x, np.eye(241), (1, 1, 1), fmap="silu")
+    want = torch.nn.functional.silu(torch.tensor(x, dtype=torch.float64)).numpy()
+    np.testing.assert_allclose(u, want, rtol=1e-13, atol=1e-300)
+    assert u.min() < -0.27   # sign-indefinite (minimum -0.2785 near x = -1.28)
+
+
+@pytest.mark.parametrize("mode", ["rola", "abspe"])
+def test_silu_mean_readout_equals_quadratic_form(mode):
+    """With SiLU features the readout is the mean over the L tokens:
+    O_lr,l = (1/L) sum_m <fq_l, fk_m> v_m, from the explicit L x L form."""
+    rng = np.random.default_rng(36)
+    grid, pairs, lr = (2, 3, 4), (4, 2, 2), (2, 1, 1)
+    L, D, r = 24, 16, 8
+    q, k, v = (rng.standard_normal((L, D)) for _ in range(3))
+    wq, wk = rng.standard_normal((D, r)) / 4, rng.standard_normal((D, r)) / 4
+    E = tuple(rng.standard_normal((n, r)) * 0.14 for n in grid)
+    Ex = E if mode == "abspe" else None
+    u = oracle.lowrank_features(k, wk, grid, Ex, fmap="silu")
+    w = oracle.lowrank_features(q, wq, grid, Ex, fmap="silu")
+    if mode == "rola":
+        fk = oracle.lowrank_rotate(u, grid, 10000.0, pairs, lr)
+        fq = oracle.lowrank_rotate(w, grid, 10000.0, pairs, lr)
+    else:
+        fk, fq = u, w
+    S, z = oracle.lowrank_summary(fk, u, v)
+    got = oracle.lowrank_readout(fq, w, S, z, 1e-6, count=float(L))
+    A = np.array([[fq[a] @ fk[b] for b in range(L)] for a in range(L)])
+    np.testing.assert_allclose(got, (A @ v) / L, rtol=1e-12, atol=1e-13)
+
+
+def test_silu_outside_rotation_keeps_zero_shift_residual():
+    """Position-free SiLU features rotated after the activation give offset-
+    only numerator weights, as elu + 1 does (RoLA §4.3, App. B.1)."""
+    rng = np.random.default_rng(37)
+    grid, pairs, lr = (3, 3, 4), (4, 2, 2), (2, 1, 1)
+    L, D, r = 36, 16, 8
+    q = np.tile(rng.standard_normal(D), (L, 1))
+    k = np.tile(rng.standard_normal(D), (L, 1))
+    wq, wk = rng.standard_normal((D, r)) / 4, rng.standard_normal((D, r)) / 4
+    coords = np.array(list(itertools.product(*(range(n) for n in grid))))
+    fq = oracle.lowrank_rotate(oracle.lowrank_features(q, wq, grid, fmap="silu"), grid, 10000.0, pairs, lr)
+    fk = oracle.lowrank_rotate(oracle.lowrank_features(k, wk, grid, fmap="silu"), grid, 10000.0, pairs, lr)
+    assert _shift_residual(fq @ fk.T, coords) < 1e-12
+    iq = oracle.lowrank_features(oracle.rope3d(q, grid, 10000.0, pairs), wq, grid, fmap="silu")
+    ik = oracle.lowrank_features(oracle.rope3d(k, grid, 10000.0, pairs), wk, grid, fmap="silu")
+    assert _shift_residual(iq @ ik.T, coords) > 1e-3
+
+
+def test_silu_layer_uses_mean_readout_and_token_gate_ignores_the_scale():
+    """The layer with fmap = silu reads out S / L; under the token gate any
+    positive per-row scale of O_lr cancels (RMS alignment), so the gated
+    output equals the one computed from the unnormalised numerator."""
+    base = synth.tiny()
+    cfg = synth.Layer(**{**base.__dict__, "fmap": "silu", "eps": 1e-12})
+    q, k, v = synth.qkv_slice(cfg, 0, 1)
+    p = synth.lowrank_params(cfg)
+    wg, bg = np.random.default_rng(38).standard_normal(cfg.D) * 0.1, -0.3
+    res = oracle.layer_slice(cfg, q, k, v, p["wq"][1], p["wk"][1], 0.0, token_gate_wb=(wg, bg))
+    D = cfg.D
+    o_lr = res["o_lr"].reshape(-1, D)
+    rows = np.arange(o_lr.shape[0])
+    valid = rows < cfg.L
+    unnorm = o_lr[valid] * cfg.L
+    qrows = np.asarray(q, np.float64)[rows[valid]]
+    out2, _ = oracle.token_gate(qrows, wg, bg, res["o_sp"].reshape(-1, D)[valid], unnorm, cfg.eps)
+    # (rows whose low-rank RMS is tiny still feel eps = 1e-12 at ~1e-11)
+    np.testing.assert_allclose(res["out"].reshape(-1, D)[valid], out2, rtol=1e-9, atol=1e-10)
