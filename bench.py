@@ -149,18 +149,20 @@ def cpu_baseline(cfg, blocks: int):
     s = oracle.block_scores(oracle.block_mean(qr, cfg.block), oracle.block_mean(kr, cfg.block))
     idx, _, _ = oracle.topk_blocks(s, cfg.keep)
     if cfg.lr_mode == "rola":
-        u, w = oracle.lowrank_features(k, p["wk"][0], grid), oracle.lowrank_features(q, p["wq"][0], grid)
+        u = oracle.lowrank_features(k, p["wk"][0], grid, fmap=cfg.fmap)
+        w = oracle.lowrank_features(q, p["wq"][0], grid, fmap=cfg.fmap)
         fk = oracle.lowrank_rotate(u, grid, cfg.base, cfg.pairs, cfg.lr_pairs)
         fq = oracle.lowrank_rotate(w, grid, cfg.base, cfg.pairs, cfg.lr_pairs)
     else:
-        u, w = oracle.lowrank_features(k, p["wk"][0], grid, E), oracle.lowrank_features(q, p["wq"][0], grid, E)
+        u = oracle.lowrank_features(k, p["wk"][0], grid, E, fmap=cfg.fmap)
+        w = oracle.lowrank_features(q, p["wq"][0], grid, E, fmap=cfg.fmap)
         fk, fq = u, w
     S, z = oracle.lowrank_summary(fk, u, v)
     t1 = time.perf_counter()
     rows = (qblocks[:, None].astype(np.int64) * cfg.block + np.arange(cfg.block)[None, :]).reshape(-1)
     rows = rows[rows < cfg.L]
     oracle.block_sparse_attention(qr, kr, v, cfg.block, idx, qblocks)
-    o_lr = oracle.lowrank_readout(fq, w, S, z, cfg.eps, rows)
+    o_lr = oracle.lowrank_readout(fq, w, S, z, cfg.eps, rows, count=float(cfg.L) if cfg.fmap == "silu" else 0.0)
     if cfg.gate == "token":
         o_sp = np.zeros_like(o_lr)   # the gate's cost does not depend on the values
         oracle.token_gate(q[rows], p["wg"][0], float(p["bg"][0]), o_sp, o_lr, cfg.eps)
@@ -221,6 +223,8 @@ def main() -> int:
     ap.add_argument("--workload", default="wan13b", choices=["wan13b", "wan14b", "hunyuan13b"])
     ap.add_argument("--gate", default="head", choices=["head", "token"],
                     help="combine gate: one scalar per head (the workloads' default) or the token-wise gate")
+    ap.add_argument("--fmap", default="elu1", choices=["elu1", "silu"],
+                    help="low-rank feature map: elu + 1 (the workloads' default) or SiLU")
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--cpu-blocks", type=int, default=512, help="query blocks the CPU oracle samples")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -256,9 +260,9 @@ def main() -> int:
         return run_sweep(args, torch, B, synth)
 
     cfg = synth.by_name(args.workload)
-    if args.gate != "head":
+    if args.gate != "head" or args.fmap != "elu1":
         import dataclasses
-        cfg = dataclasses.replace(cfg, gate=args.gate)
+        cfg = dataclasses.replace(cfg, gate=args.gate, fmap=args.fmap)
     print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     q, k, v, params = make_device_inputs(cfg, torch)
     shape, rope, sparse = B.shape_of(cfg), B.rope_of(cfg), B.sparse_of(cfg)
@@ -360,7 +364,8 @@ def main() -> int:
         "data": "synthetic (seeded clustered Q/K, Gaussian V; random-init projections)",
         "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "D": cfg.D, "L": cfg.L,
                    "grid": [cfg.T, cfg.Hg, cfg.Wg], "block": cfg.block, "keep": cfg.keep, "nblk": cfg.nblk,
-                   "rank": cfg.rank, "lowrank": cfg.lr_mode, "gate": cfg.gate, "parallelism": "single GPU"},
+                   "rank": cfg.rank, "lowrank": cfg.lr_mode, "gate": cfg.gate, "fmap": cfg.fmap,
+                   "parallelism": "single GPU"},
         "roofline": {"kernel": "k_flash_tiled (block-sparse flash + low-rank readout + combine)",
                      "bound": "mfma", "achieved": round(flash_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flash_tf / PEAK_BF16_TFLOPS, 4), "traffic": flash_traffic(args.workload),

@@ -6,7 +6,8 @@
  * RoPeSLR, arXiv 2605.20659, abstract) combines
  *   - a block-sparse softmax branch: 3D RoPE of q and k, block mean-pool,
  *     per-query-block top-k key blocks, exact softmax over the kept blocks;
- *   - a head-wise rank-r linear-attention branch: phi(x W) with phi = elu+1,
+ *   - a head-wise rank-r linear-attention branch: phi(x W) with phi = elu+1
+ *     (or SiLU, RoLA §5.3, read out as a mean over the tokens),
  *     and either the backbone's rotary schedule truncated to r dims applied
  *     after phi (RoLA §4.2-4.3) or learnable per-axis absolute embeddings
  *     added before phi (RoPeSLR abstract), read out through one reusable
@@ -66,6 +67,11 @@ extern "C" {
 #define SLR_LR_ROPE_OUTSIDE 0  /* RoLA: truncated rotary schedule after phi      */
 #define SLR_LR_ABS_PE 1        /* RoPeSLR: E_t[t]+E_h[h]+E_w[w] added before phi */
 
+/* Feature map of the low-rank branch (slr_lowrank_cfg.feature_map) */
+#define SLR_FMAP_ELU1 0        /* phi = elu + 1; readout / (w . z + eps)            */
+#define SLR_FMAP_SILU 1        /* RoLA §5.3 / Table 6: phi = SiLU (sign-indefinite);
+                                  readout / L, the mean over the valid tokens        */
+
 /* Gate of the combine (slr_lowrank_cfg.gate_mode) */
 #define SLR_GATE_HEAD 0        /* one scalar g_h per head: gate[H]                 */
 #define SLR_GATE_TOKEN 1       /* RoLA §4.4: per token, from Wg[H, D] and bg[H]    */
@@ -105,6 +111,7 @@ typedef struct {
     int32_t gate_mode;           /* SLR_GATE_HEAD or SLR_GATE_TOKEN                 */
     const float *Wg;             /* SLR_GATE_TOKEN: [H, D] fp32 gate weights, else NULL */
     const float *bg;             /* SLR_GATE_TOKEN: [H] fp32 gate biases, else NULL */
+    int32_t feature_map;         /* SLR_FMAP_ELU1 or SLR_FMAP_SILU                  */
 } slr_lowrank_cfg;
 
 /*

@@ -21,6 +21,7 @@ SLR_OK, SLR_EINVAL, SLR_EUNSUPPORTED, SLR_EWORKSPACE, SLR_EHIP = 0, -1, -2, -3, 
 SLR_F32, SLR_BF16 = 0, 1
 SLR_LR_ROPE_OUTSIDE, SLR_LR_ABS_PE = 0, 1
 SLR_GATE_HEAD, SLR_GATE_TOKEN = 0, 1
+SLR_FMAP_ELU1, SLR_FMAP_SILU = 0, 1
 SLR_OP_ROPE3D, SLR_OP_SELECT, SLR_OP_LOWRANK_SUMMARY, SLR_OP_ATTENTION, SLR_OP_DENSE = 0, 1, 2, 3, 4
 
 EXPORTS = ("slr_workspace_bytes", "slr_rope3d", "slr_select_blocks", "slr_lowrank_summary",
@@ -46,7 +47,8 @@ class SlrLowrankCfg(ctypes.Structure):
                 ("lr_pairs_h", ctypes.c_int32), ("lr_pairs_w", ctypes.c_int32), ("eps", ctypes.c_float),
                 ("Wq", ctypes.c_void_p), ("Wk", ctypes.c_void_p), ("gate", ctypes.c_void_p),
                 ("Et", ctypes.c_void_p), ("Eh", ctypes.c_void_p), ("Ew", ctypes.c_void_p),
-                ("gate_mode", ctypes.c_int32), ("Wg", ctypes.c_void_p), ("bg", ctypes.c_void_p)]
+                ("gate_mode", ctypes.c_int32), ("Wg", ctypes.c_void_p), ("bg", ctypes.c_void_p),
+                ("feature_map", ctypes.c_int32)]
 
 
 class SlrError(RuntimeError):
@@ -132,7 +134,8 @@ def lowrank_of(layer, params: Dict[str, torch.Tensor]) -> SlrLowrankCfg:
                          params["ew"].data_ptr() if abspe else None,
                          SLR_GATE_TOKEN if token else SLR_GATE_HEAD,
                          params["wg"].data_ptr() if token else None,
-                         params["bg"].data_ptr() if token else None)
+                         params["bg"].data_ptr() if token else None,
+                         SLR_FMAP_SILU if getattr(layer, "fmap", "elu1") == "silu" else SLR_FMAP_ELU1)
 
 
 def slr_workspace_bytes(op: int, shape: SlrShape, rope: SlrRopeCfg, sparse: Optional[SlrSparseCfg] = None,

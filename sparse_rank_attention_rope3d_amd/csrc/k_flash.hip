@@ -85,7 +85,7 @@ __device__ __forceinline__ void flash_epilogue(const FlashArgs& a, long bh, int 
                 const bool ok = qval && r < a.g.R;
                 float x = wacc[rb][i];
                 if (LR == 2 && ok) x += a.Et[crd[0] * a.g.R + r] + a.Eh[crd[1] * a.g.R + r] + a.Ew[crd[2] * a.g.R + r];
-                w[i] = ok ? phi_elu1(x) : 0.f;
+                w[i] = ok ? phi_feat(a.g.fmap, x) : 0.f;
                 den += w[i] * zp[r];
             }
             if (LR == 1) {
@@ -111,7 +111,8 @@ __device__ __forceinline__ void flash_epilogue(const FlashArgs& a, long bh, int 
                 }
         }
         den = sum_xor32(den);
-        rden = 1.f / (den + a.eps);
+        // sign-indefinite SiLU features: the readout is the mean over the L tokens
+        rden = a.g.fmap ? 1.f / (float)L : 1.f / (den + a.eps);
         if (a.gate_mode == 0) {
             gsc = a.gate[head];
         } else {
@@ -655,7 +656,7 @@ __global__ __launch_bounds__(64) void k_flash_f32(FlashArgs a, int BS) {
             for (int d = 0; d < D; ++d) x += qraw[d] * W[d * R + r];
             if (LR == 2) x += a.Et[crd[0] * R + r] + a.Eh[crd[1] * R + r] + a.Ew[crd[2] * R + r];
         }
-        w[r] = r < R ? phi_elu1(x) : 0.f;
+        w[r] = r < R ? phi_feat(a.g.fmap, x) : 0.f;
         den += r < R ? w[r] * a.zp[bh * R + r] : 0.f;
     }
     for (int r = 0; r < RP; r += 2) {
@@ -668,7 +669,7 @@ __global__ __launch_bounds__(64) void k_flash_f32(FlashArgs a, int BS) {
             f[r + 1] = w[r + 1];
         }
     }
-    const float rd = 1.f / (den + a.eps);
+    const float rd = a.g.fmap ? 1.f / (float)L : 1.f / (den + a.eps);
     const float* S = a.S + bh * (long)R * D;
     float gs;
     if (a.gate_mode == 0) {

@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
                 const bool ok = t0 + 4 * hf + 8 * (vv >> 2) + (vv & 3) < tok_hi && r < g.R;
                 float x = uacc[rb][vv];
                 if (ABSPE) x += ev[vv];
-                float u = ok ? phi_elu1_fast(x) : 0.f;
+                float u = ok ? phi_feat_fast(g.fmap, x) : 0.f;
                 zacc[rb] += u;
                 if (!ABSPE) {
                     const float p = lane_swap1(u);  // partner dim r ^ 1
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(256) void k_lr_summary_f32(const float* __restrict_
                 float acc = 0.f;
                 for (int d = 0; d < D; ++d) acc += ksh[tl][d] * Wh[d * R + r];
                 if (absPE) acc += Et[crd[0] * R + r] + Eh[crd[1] * R + r] + Ew[crd[2] * R + r];
-                u[q] = phi_elu1(acc);
+                u[q] = phi_feat(g.fmap, acc);
             }
             ush[tl][2 * pr] = u[0];
             ush[tl][2 * pr + 1] = u[1];

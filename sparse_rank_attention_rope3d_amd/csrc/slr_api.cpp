@@ -89,6 +89,8 @@ int check_lowrank(const slr_lowrank_cfg* lr, const slr_rope_cfg* rope, const Dim
             return SLR_EINVAL;
         }
     }
+    if (lr->feature_map != SLR_FMAP_ELU1 && lr->feature_map != SLR_FMAP_SILU) return SLR_EINVAL;
+    lg->fmap = lr->feature_map;
     lg->lp[0] = lg->lp[1] = lg->lp[2] = 0;
     if (lr->mode == SLR_LR_ROPE_OUTSIDE) {
         if (lr->lr_pairs_t < 0 || lr->lr_pairs_h < 0 || lr->lr_pairs_w < 0) return SLR_EINVAL;

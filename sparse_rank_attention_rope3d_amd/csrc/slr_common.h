@@ -86,6 +86,16 @@ __device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : 
 __device__ __forceinline__ float phi_elu1_fast(float x) {
     return x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
+// SiLU(x) = x / (1 + exp(-x)) (exp(-x) = inf for very negative x gives -0)
+__device__ __forceinline__ float phi_silu(float x) { return x / (1.f + expf(-x)); }
+__device__ __forceinline__ float phi_silu_fast(float x) {
+    return x / (1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+// feature map of the low-rank branch: 0 = elu + 1, 1 = SiLU
+__device__ __forceinline__ float phi_feat(int fmap, float x) { return fmap ? phi_silu(x) : phi_elu1(x); }
+__device__ __forceinline__ float phi_feat_fast(int fmap, float x) {
+    return fmap ? phi_silu_fast(x) : phi_elu1_fast(x);
+}
 
 // Grid coordinates of token l + delta given those of token l (t-major, then
 // h, then w), without divisions.

@@ -13,6 +13,7 @@ struct LrGeom {
     RopeGeom rope;
     int lp[3];
     int R;
+    int fmap;   // feature map: 0 = elu + 1 (readout / (w . z + eps)), 1 = SiLU (readout / L)
 };
 
 // Everything the fused sparse/dense flash kernel reads.

@@ -102,7 +102,7 @@ def test_bad_sparse(block, keep):
 
 @pytest.mark.parametrize("change", ["rank", "pairs_sum", "pairs_axis", "mode", "eps", "wq", "abspe_tables",
                                     "gate_mode", "head_gate_null", "token_wg_null", "token_bg_null",
-                                    "token_wg_misaligned"])
+                                    "token_wg_misaligned", "feature_map"])
 def test_bad_lowrank(change):
     shape, rope, sparse, lr = _cfgs()
     if change == "rank":
@@ -121,6 +121,8 @@ def test_bad_lowrank(change):
         lr.mode = B.SLR_LR_ABS_PE
     elif change == "gate_mode":
         lr.gate_mode = 2
+    elif change == "feature_map":
+        lr.feature_map = 2
     elif change == "head_gate_null":
         lr.gate = None
     elif change.startswith("token"):

@@ -140,6 +140,29 @@ def test_token_gate_layers(D, bs, r, mode, grid, keep, dtype):
     _full_check(cfg)
 
 
+SILU = [
+    # D, block, rank, mode, grid, keep, dtype, gate: the three flash kernels, both gates
+    (128, 64, 32, "rola", (5, 9, 13), 3, "bf16", "head"),
+    (128, 64, 32, "abspe", (3, 5, 17), 4, "bf16", "token"),
+    (64, 32, 8, "rola", (4, 8, 8), 2, "bf16", "head"),
+    (128, 32, 16, "rola", (3, 7, 11), 3, "bf16", "token"),
+    (128, 64, 32, "rola", (5, 9, 13), 3, "f32", "head"),
+    (64, 64, 16, "abspe", (3, 6, 7), 2, "f32", "token"),
+]
+
+
+@pytest.mark.parametrize("D,bs,r,mode,grid,keep,dtype,gate", SILU)
+def test_silu_feature_map_layers(D, bs, r, mode, grid, keep, dtype, gate):
+    """SiLU low-rank features (RoLA §5.3) with the mean readout, against the oracle (summary included)."""
+    p = r // 2
+    lp = (p // 2, p // 4, p - p // 2 - p // 4) if mode == "rola" else (0, 0, 0)
+    pairs = (12, 10, 10) if D == 64 else (22, 21, 21)
+    cfg = T.custom(synth.wan13b(), name=f"silu D{D} bs{bs} r{r} {mode} {grid} k{keep} {dtype} {gate}", B=2, H=3,
+                   D=D, T=grid[0], Hg=grid[1], Wg=grid[2], block=bs, keep=keep, rank=r, lr_mode=mode, lr_pairs=lp,
+                   pairs=pairs, dtype=dtype, seed=13, gate=gate, fmap="silu")
+    _full_check(cfg)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_token_gate_very_negative_bias_gives_sparse_branch(dtype):
     cfg = T.custom(synth.wan13b(), name=f"token gate off {dtype}", B=1, H=2, T=3, Hg=5, Wg=9, keep=2, dtype=dtype,
