@@ -34,8 +34,8 @@ PEAK_HBM_GBS = 8000.0
 # on, identified by the sha256 of its files; any other source reports null.
 FLASH_TRAFFIC_SOURCES = ["k_flash.hip", "slr_common.h", "slr_launch.h"]
 FLASH_TRAFFIC = {
-    "sha256": "08070d84c0477d8fab12e17ec0e054e84b2ce1833ec8d768389607cc8c392a62",
-    "bytes_per_launch": {"wan13b": 8389.6e6 + 201.3e6, "wan14b": 217956.6e6 + 1548.4e6},
+    "sha256": "0eb2fa3def1286864c8a95c709eb58825b42d287ddfc4b7b5a819550c3f77a89",
+    "bytes_per_launch": {"wan13b": 8213.9e6 + 201.3e6, "wan14b": 216920.2e6 + 1548.4e6},
 }
 
 
