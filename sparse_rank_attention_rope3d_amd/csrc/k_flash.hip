@@ -383,8 +383,11 @@ __global__ __launch_bounds__(BS * 2) void k_flash_bf16(FlashArgs a) {
 // p = exp2(s) needs no max or FMA. The reference is raised only when some
 // probability of the tile could exceed ~2^36 (its sum passes 2^40, or is not
 // finite), and set from the tile when the row has none; O and l are scaled
-// by the same factor, so the result after normalisation is unchanged.
-__device__ __forceinline__ void softmax_tile(f32x16_t& s, f32x16_t* o, float& m_run, float& l_run, u32x4_t* pop) {
+// by the same factor, so the result after normalisation is unchanged. negm
+// holds -m_run (0 without a reference) in all 16 accumulator slots: it is
+// the C operand of a tile's first score MFMA and changes only with m_run.
+__device__ __forceinline__ void softmax_tile(f32x16_t& s, f32x16_t* o, float& m_run, float& l_run, u32x4_t* pop,
+                                             f32x16_t& negm) {
     float p[16];
     float l = 0.f;
 #pragma unroll
@@ -406,6 +409,11 @@ __device__ __forceinline__ void softmax_tile(f32x16_t& s, f32x16_t* o, float& m_
         const float ref = noref ? 0.f : m_run;
         const float alpha = noref ? 0.f : fast_exp2(-shift);
         m_run = none ? -INFINITY : ref + shift;
+        {
+            const float init = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) negm[i] = init;
+        }
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -494,6 +502,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;   // reference (log2 units), partial row sum
+    f32x16_t negm;                           // -m_run (0 without a reference): C of the first score MFMA
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negm[i] = 0.f;
     const bool ragged = (L % BS) != 0;
 
     // K of tile t lives in K slot t % 3, V^T in V slot t % 2. The barrier that
@@ -516,15 +527,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         ks = ks == 2 ? 0 : ks + 1;
         u32x4_t op[8], vop[8];
         lds_read8(op, kcur + rd);                 // K chunks (kh, s)
-        f32x16_t sacc;
-        {
-            const float init = m_run == -INFINITY ? 0.f : -m_run;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[i] = init;
-        }
         __builtin_amdgcn_s_setprio(1);   // matrix phase first when two waves share a SIMD
+        f32x16_t sacc = mfma32(op[0], qop[0], negm);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) sacc = mfma32(op[s], qop[s], sacc);
+        for (int s = 1; s < 8; ++s) sacc = mfma32(op[s], qop[s], sacc);
         __builtin_amdgcn_s_setprio(0);
         // V^T chunks (kh, db, h2): read while the score MFMAs run, into
         // registers other than the K operands those MFMAs still read
@@ -538,7 +544,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 if (key0 + 8 * (i >> 2) + 4 * hf + (i & 3) >= L) sacc[i] = -INFINITY;
         }
         u32x4_t pop[2];
-        softmax_tile(sacc, oacc, m_run, l_run, pop);
+        softmax_tile(sacc, oacc, m_run, l_run, pop, negm);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
