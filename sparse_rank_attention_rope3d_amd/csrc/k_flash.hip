@@ -528,7 +528,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         u32x4_t op[8], vop[8];
         lds_read8(op, kcur + rd);                 // K chunks (kh, s)
         __builtin_amdgcn_s_setprio(1);   // matrix phase first when two waves share a SIMD
-        f32x16_t sacc = mfma32(op[0], qop[0], negm);
+        // First score MFMA with C = -m into a distinct accumulator (the builtin
+        // form makes the compiler copy negm into the accumulator first). Its
+        // inputs are old: op from an asm read that waited for itself, qop from
+        // loads waited before the loop, negm written a tile earlier at most;
+        // the next MFMA reads the result as C with exact overlap, which the
+        // hardware chains back to back.
+        f32x16_t sacc;
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(sacc) : "v"(op[0]), "v"(qop[0]), "v"(negm));
 #pragma unroll
         for (int s = 1; s < 8; ++s) sacc = mfma32(op[s], qop[s], sacc);
         __builtin_amdgcn_s_setprio(0);
