@@ -280,10 +280,16 @@ def main() -> int:
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        B.slr_attention_fwd_staged(q, k, v, shape, rope, sparse, lowrank, out, ws, events[i])
+        B.slr_attention_fwd(q, k, v, shape, rope, sparse, lowrank, out=out, ws=ws)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+    # stage times from the same number of steps of the staged call (its event
+    # records add a few microseconds between stages, so it is not the headline)
+    print(f"[bench] {args.steps} staged steps for the stage times", file=sys.stderr, flush=True)
+    for i in range(args.steps):
+        B.slr_attention_fwd_staged(q, k, v, shape, rope, sparse, lowrank, out, ws, events[i])
+    torch.cuda.synchronize()
     stage_names = ["rope_pool", "select", "lowrank_summary", "sparse_flash"]
     stages = {n: [] for n in stage_names}
     for ev in events:
