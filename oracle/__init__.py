@@ -15,6 +15,7 @@ it with ctypes and chains its steps in the order the method states
   or, token-wise (RoLA §4.4): O = O_sparse + g(q) * RMS-aligned O_lowrank
 
 Every function takes and returns float64 numpy arrays for one (b, h) slice.
+The gradients of this forward (the backward pass) are in ``oracle.backward``.
 The absolute-PE variant (RoPeSLR, arXiv 2605.20659, abstract) adds per-axis
 tables before phi and skips the rotation after it.
 """

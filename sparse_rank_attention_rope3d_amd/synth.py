@@ -35,6 +35,7 @@ import numpy as np
 TID_Q, TID_K, TID_V, TID_WQ, TID_WK, TID_GATE, TID_CENT, TID_CLUSTER = 0, 1, 2, 3, 4, 5, 6, 7
 TID_ET, TID_EH, TID_EW = 8, 9, 10
 TID_WG, TID_BG = 11, 12
+TID_DOUT = 13      # upstream gradient of the layer output (backward)
 TID_SAMPLE = 99  # query-block sample for the oracle's partial coverage
 
 N_CENTROIDS = 64
@@ -198,6 +199,13 @@ def qkv_slice(cfg: Layer, b: int, h: int, L: Optional[int] = None) -> Tuple[np.n
     if cfg.dtype == "bf16":
         q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
     return q, k, v
+
+
+def dout_slice(cfg: Layer, b: int, h: int) -> np.ndarray:
+    """Upstream gradient dL/dout of one (b, h) slice, fp32 [L, D] ~ N(0, 1)
+    (bf16-representable for bf16 layers): the input of the backward pass."""
+    g = _rng(cfg.seed, TID_DOUT, b, h).standard_normal((cfg.L, cfg.D), dtype=np.float32)
+    return round_bf16(g) if cfg.dtype == "bf16" else g
 
 
 def lowrank_params(cfg: Layer) -> Dict[str, np.ndarray]:
