@@ -82,6 +82,7 @@ extern "C" {
 #define SLR_OP_LOWRANK_SUMMARY 2
 #define SLR_OP_ATTENTION 3
 #define SLR_OP_DENSE 4
+#define SLR_OP_ATTENTION_BWD 5
 
 typedef struct {
     int32_t B, H, D;       /* batch, heads, head dim (64 or 128)      */
@@ -188,6 +189,33 @@ int slr_attention_fwd_staged(const slr_shape *shape, const slr_rope_cfg *rope, c
 int slr_dense_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, const void *q,
                             const void *k, const void *v, void *out,
                             void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward pass of the layer (gradients of slr_attention_fwd's output; the
+ * pages fine-tune this layer, RoLA §4.4 and App. E.2). Given dout = dL/dout:
+ *   sparse branch (RoLA §4.1): per query row, P = softmax over the kept keys
+ *     of (R q).(R k) / sqrt(D), dP = dout V^T, dS = P (dP - dout . O_sparse);
+ *     dq += R^T (dS K_rot) / sqrt(D), dk += R^T (dS^T Q_rot) / sqrt(D),
+ *     dv += P^T dout, with R^T the transpose of the 3D RoPE;
+ *   low-rank branch (RoLA §4.1-4.3, App. A): the chain rule through
+ *     phi(x W), the rotation after phi, S, z and the normaliser, with
+ *     dO_lowrank = g_h dout;
+ *   dgate[h] = sum over b and rows of dout . O_lowrank.
+ * The selection is held fixed: idx [B,H,nblk,keep] int32 is the forward's
+ * (idx_out of slr_attention_fwd); each row must list distinct blocks in
+ * [0, nblk) (entries outside that range are skipped). o_sparse [B,H,L,D] is
+ * the forward's O_sparse (o_sparse_out). dout, dq, dk, dv: [B,H,L,D] bf16;
+ * dq, dk, dv must not overlap each other or any input. dWq, dWk: [H,D,r]
+ * fp32, dgate: [H] fp32, all overwritten (sums over the batch).
+ * Built for bf16 layers with SLR_GATE_HEAD and SLR_LR_ROPE_OUTSIDE (either
+ * feature map); other settings return SLR_EUNSUPPORTED. Workspace:
+ * slr_workspace_bytes(SLR_OP_ATTENTION_BWD, ...). Results are bitwise
+ * reproducible (fixed reduction orders, no floating-point atomics).
+ */
+int slr_attention_bwd(const slr_shape *shape, const slr_rope_cfg *rope, const slr_sparse_cfg *sparse,
+                      const slr_lowrank_cfg *lowrank, const void *q, const void *k, const void *v,
+                      const int32_t *idx, const void *o_sparse, const void *dout, void *dq, void *dk, void *dv,
+                      float *dWq, float *dWk, float *dgate, void *ws, size_t ws_bytes, void *stream);
 
 /* Static text for a status code. */
 const char *slr_status_string(int status);

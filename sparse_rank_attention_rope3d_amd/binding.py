@@ -23,9 +23,11 @@ SLR_LR_ROPE_OUTSIDE, SLR_LR_ABS_PE = 0, 1
 SLR_GATE_HEAD, SLR_GATE_TOKEN = 0, 1
 SLR_FMAP_ELU1, SLR_FMAP_SILU = 0, 1
 SLR_OP_ROPE3D, SLR_OP_SELECT, SLR_OP_LOWRANK_SUMMARY, SLR_OP_ATTENTION, SLR_OP_DENSE = 0, 1, 2, 3, 4
+SLR_OP_ATTENTION_BWD = 5
 
 EXPORTS = ("slr_workspace_bytes", "slr_rope3d", "slr_select_blocks", "slr_lowrank_summary",
-           "slr_attention_fwd", "slr_attention_fwd_staged", "slr_dense_attention_fwd", "slr_status_string")
+           "slr_attention_fwd", "slr_attention_fwd_staged", "slr_dense_attention_fwd", "slr_attention_bwd",
+           "slr_status_string")
 
 
 class SlrShape(ctypes.Structure):
@@ -80,6 +82,7 @@ def lib() -> ctypes.CDLL:
         L.slr_attention_fwd_staged.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg), vp,
                                                vp, vp, vp, vp, vp, vp, vp, sz, P(vp), vp]
         L.slr_dense_attention_fwd.argtypes = [P(SlrShape), P(SlrRopeCfg), vp, vp, vp, vp, vp, sz, vp]
+        L.slr_attention_bwd.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg)] + [vp] * 13 + [sz, vp]
         for f in EXPORTS[:-1]:
             getattr(L, f).restype = ctypes.c_int
         L.slr_status_string.argtypes = [ctypes.c_int]
@@ -207,6 +210,27 @@ def slr_attention_fwd(q, k, v, shape: SlrShape, rope: SlrRopeCfg, sparse: SlrSpa
                                    ctypes.byref(lowrank), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(idx),
                                    _ptr(o_sp), _ptr(o_lr), _ptr(ws), ws.numel(), _stream()), "slr_attention_fwd")
     return (out, idx, o_sp, o_lr) if debug else out
+
+
+def slr_attention_bwd(q, k, v, idx, o_sparse, dout, shape: SlrShape, rope: SlrRopeCfg, sparse: SlrSparseCfg,
+                      lowrank: SlrLowrankCfg, ws: Optional[torch.Tensor] = None, grads=None):
+    """Backward of slr_attention_fwd given dout (idx and o_sparse saved from
+    the forward). Returns (dq, dk, dv, dWq [H, D, r] fp32, dWk, dgate [H] fp32);
+    ``grads`` may supply those six output tensors."""
+    if grads is None:
+        dev = q.device
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dWq = torch.empty((shape.H, shape.D, lowrank.rank), dtype=torch.float32, device=dev)
+        dWk = torch.empty_like(dWq)
+        dg = torch.empty((shape.H,), dtype=torch.float32, device=dev)
+    else:
+        dq, dk, dv, dWq, dWk, dg = grads
+    ws = _ws(SLR_OP_ATTENTION_BWD, shape, rope, sparse, lowrank, ws, q.device)
+    _check(lib().slr_attention_bwd(ctypes.byref(shape), ctypes.byref(rope), ctypes.byref(sparse),
+                                   ctypes.byref(lowrank), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(o_sparse),
+                                   _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dWq), _ptr(dWk), _ptr(dg),
+                                   _ptr(ws), ws.numel(), _stream()), "slr_attention_bwd")
+    return dq, dk, dv, dWq, dWk, dg
 
 
 def slr_attention_fwd_staged(q, k, v, shape: SlrShape, rope: SlrRopeCfg, sparse: SlrSparseCfg,

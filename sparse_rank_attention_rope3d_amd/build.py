@@ -16,7 +16,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libslr.so")
-SOURCES = ["k_rope.hip", "k_select.hip", "k_lowrank.hip", "k_flash.hip", "slr_api.cpp"]
+SOURCES = ["k_rope.hip", "k_select.hip", "k_lowrank.hip", "k_flash.hip", "k_backward.hip", "slr_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

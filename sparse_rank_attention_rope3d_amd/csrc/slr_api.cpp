@@ -143,15 +143,36 @@ void summary_split(const Dims& d, int slots, int* chunk, int* nsplit) {
     *nsplit = (int)best_n;
 }
 
+// The backward is built for bf16 layers with the per-head gate and the
+// rotary low-rank variant.
+int check_bwd_supported(const Dims& d, const slr_lowrank_cfg* lr) {
+    if (!d.bf16 || lr->gate_mode != SLR_GATE_HEAD || lr->mode != SLR_LR_ROPE_OUTSIDE) return SLR_EUNSUPPORTED;
+    return SLR_OK;
+}
+
 // Workspace layout (byte offsets, each 256-byte aligned).
 struct Layout {
     size_t tab, qr, kr, kvt, qbar, kbar, scores, idx, wqt, wkt, part, S, z, sthi, stlo, zp, total;
+    // backward
+    size_t lse, delta, dqlr, dklr, dvlr, lrpart, dsz, bits, cnt, off, list;
     bool tiled;
 };
 
 // bf16, D = 128, 64-token blocks: K and V^T go to contiguous per-block tiles
 // that the streaming flash kernel copies straight into LDS.
 bool use_tiles(const Dims& d, int bs) { return d.bf16 && d.D == 128 && bs == 64; }
+
+// Split-L partition of the low-rank backward: about 1024 workgroups over the
+// BH slices, chunks of a multiple of 32 tokens.
+void lr_bwd_split(const Dims& d, int* chunk, int* nsplit) {
+    const long tiles = (d.L + 31) / 32;
+    long n = 1024 / d.BH;
+    if (n < 1) n = 1;
+    if (n > tiles) n = tiles;
+    const long c = ((d.L + n - 1) / n + 31) / 32 * 32;
+    *chunk = (int)c;
+    *nsplit = (int)((d.L + c - 1) / c);
+}
 
 Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int keep, int R, int RP) {
     Layout w;
@@ -166,6 +187,33 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         w.idx = take(4ul * d.BH * nblk * keep);
     }
     w.tiled = false;
+    if (op == SLR_OP_ATTENTION_BWD) {
+        // rotated q, k (rows padded to whole blocks), the recomputed summary,
+        // per-row softmax statistics, the low-rank gradient parts and the
+        // inverse of the kept lists
+        const size_t rows = (size_t)nblk * bs;
+        w.qr = take(2ul * d.BH * rows * d.D);
+        w.kr = take(2ul * d.BH * rows * d.D);
+        w.wkt = take(2ul * d.H * RP * d.D);
+        w.part = take(4ul * d.BH * summary_split_cap(d) * (RP * d.D + RP));
+        w.S = take(4ul * d.BH * R * d.D);
+        w.z = take(4ul * d.BH * R);
+        w.lse = take(4ul * d.BH * rows);
+        w.delta = take(4ul * d.BH * rows);
+        w.dqlr = take(4ul * d.BH * d.L * d.D);
+        w.dklr = take(4ul * d.BH * d.L * d.D);
+        w.dvlr = take(4ul * d.BH * d.L * d.D);
+        int chunk, nsplit;
+        lr_bwd_split(d, &chunk, &nsplit);
+        w.lrpart = take(4ul * d.BH * nsplit * (2ul * d.D * R + R + 1));
+        w.dsz = take(4ul * d.BH * ((size_t)R * d.D + R));
+        w.bits = take(4ul * d.BH * nblk * ((nblk + 31) / 32));
+        w.cnt = take(4ul * d.BH * nblk);
+        w.off = take(4ul * d.BH * (nblk + 1));
+        w.list = take(4ul * d.BH * nblk * keep);
+        w.total = off;
+        return w;
+    }
     if (op == SLR_OP_ATTENTION || op == SLR_OP_DENSE) {
         const size_t rows = (size_t)nblk * bs;
         w.qr = take((size_t)d.es * d.BH * rows * d.D);
@@ -240,6 +288,7 @@ int slr_workspace_bytes(int op, const slr_shape* shape, const slr_rope_cfg* rope
             break;
         case SLR_OP_SELECT:
         case SLR_OP_ATTENTION:
+        case SLR_OP_ATTENTION_BWD:
             if ((st = check_sparse(sparse, d, &nblk))) return st;
             bs = sparse->block;
             keep = sparse->keep;
@@ -249,7 +298,7 @@ int slr_workspace_bytes(int op, const slr_shape* shape, const slr_rope_cfg* rope
         default:
             return SLR_EINVAL;
     }
-    if (op == SLR_OP_ATTENTION || op == SLR_OP_LOWRANK_SUMMARY) {
+    if (op == SLR_OP_ATTENTION || op == SLR_OP_LOWRANK_SUMMARY || op == SLR_OP_ATTENTION_BWD) {
         if (!lowrank) return SLR_EINVAL;
         LrGeom lg;
         // pointer fields are not needed for sizing
@@ -258,9 +307,10 @@ int slr_workspace_bytes(int op, const slr_shape* shape, const slr_rope_cfg* rope
         probe.Wq = probe.Wk = probe.gate = dummy;
         probe.Et = probe.Eh = probe.Ew = dummy;
         probe.Wg = probe.bg = dummy;
-        if ((st = check_lowrank(&probe, rope, d, op == SLR_OP_ATTENTION, &lg, &RP))) return st;
+        if ((st = check_lowrank(&probe, rope, d, op != SLR_OP_LOWRANK_SUMMARY, &lg, &RP))) return st;
         R = lowrank->rank;
     }
+    if (op == SLR_OP_ATTENTION_BWD && (st = check_bwd_supported(d, lowrank))) return st;
     *bytes = layout(op, d, g, bs, nblk, keep, R, RP).total;
     return SLR_OK;
 }
@@ -489,6 +539,90 @@ int slr_dense_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, co
     a.scale = (float)(1.0 / std::sqrt((double)d.D));
     a.nwg = d.BH * nblk;
     SLR_TRY(launch_flash(d.bf16, (int)d.D, bs, 32, 0, true, a, d.BH, s));
+    return SLR_OK;
+}
+
+int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
+                      const slr_lowrank_cfg* lowrank, const void* q, const void* k, const void* v, const int32_t* idx,
+                      const void* o_sparse, const void* dout, void* dq, void* dk, void* dv, float* dWq, float* dWk,
+                      float* dgate, void* ws, size_t ws_bytes, void* stream) {
+    Dims d;
+    RopeGeom g;
+    LrGeom lg;
+    int nblk, RP;
+    int st = check_shape(shape, &d);
+    if (st) return st;
+    if ((st = check_rope(rope, d, &g))) return st;
+    if ((st = check_sparse(sparse, d, &nblk))) return st;
+    if ((st = check_lowrank(lowrank, rope, d, true, &lg, &RP))) return st;
+    if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o_sparse) || !tensor_ok(dout)) return SLR_EINVAL;
+    if (!tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv) || !idx || !aligned(idx, 4)) return SLR_EINVAL;
+    if (!dWq || !dWk || !dgate || !aligned(dWq, 4) || !aligned(dWk, 4) || !aligned(dgate, 4)) return SLR_EINVAL;
+    {
+        const void* outs[3] = {dq, dk, dv};
+        const void* ins[5] = {q, k, v, o_sparse, dout};
+        for (int i = 0; i < 3; ++i) {
+            for (int j = 0; j < 5; ++j)
+                if (outs[i] == ins[j]) return SLR_EINVAL;
+            for (int j = i + 1; j < 3; ++j)
+                if (outs[i] == outs[j]) return SLR_EINVAL;
+        }
+    }
+    if ((st = check_bwd_supported(d, lowrank))) return st;
+    lg.rope = g;
+    const int bs = sparse->block, keep = sparse->keep, R = lowrank->rank;
+    Layout w = layout(SLR_OP_ATTENTION_BWD, d, g, bs, nblk, keep, R, RP);
+    if ((st = check_ws(ws, ws_bytes, w.total))) return st;
+    hipStream_t s = (hipStream_t)stream;
+    float2* tab = at<float2>(ws, w.tab);
+    uint16_t* qr = at<uint16_t>(ws, w.qr);
+    uint16_t* kr = at<uint16_t>(ws, w.kr);
+    float* S = at<float>(ws, w.S);
+    float* z = at<float>(ws, w.z);
+
+    SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
+    SLR_TRY(launch_rope_pool(1, (int)d.D, q, k, qr, kr, nullptr, nullptr, tab, g, d.BH, d.L, (long)nblk * bs, bs, nblk,
+                             s));
+    if ((st = run_summary(d, g, lg, RP, lowrank, k, v, nullptr, 0, ws, w, S, z, false, s))) return st;
+
+    // low-rank branch: query side, reductions, key side
+    LrBwdArgs la;
+    std::memset(&la, 0, sizeof(la));
+    la.q = (const uint16_t*)q; la.k = (const uint16_t*)k; la.v = (const uint16_t*)v; la.dout = (const uint16_t*)dout;
+    la.Wq = lowrank->Wq; la.Wk = lowrank->Wk; la.S = S; la.z = z; la.gate = lowrank->gate;
+    float* dsz = at<float>(ws, w.dsz);
+    la.dSz = dsz;
+    la.tab = tab; la.g = lg; la.eps = lowrank->eps; la.L = d.L; la.H = (int)d.H;
+    lr_bwd_split(d, &la.chunk, &la.nsplit);
+    la.dq_lr = at<float>(ws, w.dqlr); la.dk_lr = at<float>(ws, w.dklr); la.dv_lr = at<float>(ws, w.dvlr);
+    la.part = at<float>(ws, w.lrpart);
+    const long qstride = 2l * d.D * R + R + 1;
+    SLR_TRY(launch_bwd_lr((int)d.D, R, false, la, d.BH, s));
+    // [dW_q | dS | dz | dg] partials -> dS, dz per slice; dW_q, dg per head
+    SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, qstride, d.D * R, (long)R * d.D + R, false,
+                                 dsz, s));
+    SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, qstride, 0, d.D * R, true, dWq, s));
+    SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, qstride, 2l * d.D * R + R, 1, true, dgate,
+                                 s));
+    SLR_TRY(launch_bwd_lr((int)d.D, R, true, la, d.BH, s));
+    SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, d.D * R, 0, d.D * R, true, dWk, s));
+
+    // sparse branch: dQ (and the row statistics), the inverse lists, dK and dV
+    BwdArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.qr = qr; a.kr = kr; a.v = (const uint16_t*)v; a.o_sp = (const uint16_t*)o_sparse;
+    a.dout = (const uint16_t*)dout; a.idx = idx;
+    a.inv_off = at<int32_t>(ws, w.off); a.inv_list = at<int32_t>(ws, w.list);
+    a.lse2 = at<float>(ws, w.lse); a.delta = at<float>(ws, w.delta);
+    a.dq_lr = la.dq_lr; a.dk_lr = la.dk_lr; a.dv_lr = la.dv_lr;
+    a.dq = (uint16_t*)dq; a.dk = (uint16_t*)dk; a.dv = (uint16_t*)dv;
+    a.tab = tab; a.g = g; a.L = d.L; a.nblk = nblk; a.keep = keep;
+    a.scale = (float)(1.0 / std::sqrt((double)d.D));
+    a.nwg = d.BH * nblk;
+    SLR_TRY(launch_bwd_dq((int)d.D, bs, a, s));
+    SLR_TRY(launch_bwd_inverse(idx, d.BH, nblk, keep, at<uint32_t>(ws, w.bits), at<int32_t>(ws, w.cnt),
+                               at<int32_t>(ws, w.off), at<int32_t>(ws, w.list), s));
+    SLR_TRY(launch_bwd_dkdv((int)d.D, bs, a, s));
     return SLR_OK;
 }
 

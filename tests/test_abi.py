@@ -175,3 +175,45 @@ def test_other_entry_points_validate():
     n = ctypes.c_size_t()
     assert L.slr_workspace_bytes(9, r(shape), r(rope), None, None, r(n)) == B.SLR_EINVAL
     assert L.slr_workspace_bytes(B.SLR_OP_ATTENTION, r(shape), r(rope), None, r(lr), r(n)) == B.SLR_EINVAL
+
+
+def _bwd(shape, rope, sparse, lr, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, idx=FAKE + 0x3000, osp=FAKE + 0x4000,
+         dout=FAKE + 0x5000, dq=FAKE + 0x6000, dk=FAKE + 0x7000, dv=FAKE + 0x8000, dwq=FAKE + 0x9000,
+         dwk=FAKE + 0xa000, dg=FAKE + 0xb000, ws=None, ws_bytes=0):
+    r = ctypes.byref
+    return B.lib().slr_attention_bwd(r(shape), r(rope), r(sparse), r(lr), q, k, v, idx, osp, dout, dq, dk, dv, dwq,
+                                     dwk, dg, ws, ws_bytes, None)
+
+
+def test_backward_validates_before_launching():
+    shape, rope, sparse, lr = _cfgs()
+    need = B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lr)
+    layer = synth.wan13b()
+    # rotated q, k plus three fp32 low-rank gradient parts
+    assert need > (2 * 2 + 3 * 4) * layer.B * layer.H * layer.L * layer.D
+    assert _bwd(shape, rope, sparse, lr) == B.SLR_EWORKSPACE
+    assert _bwd(shape, rope, sparse, lr, ws=FAKE, ws_bytes=need - 1) == B.SLR_EWORKSPACE
+    for bad in ("q", "osp", "dout", "dq", "dv", "dwq", "dg"):
+        assert _bwd(shape, rope, sparse, lr, **{bad: None}) == B.SLR_EINVAL, bad
+    assert _bwd(shape, rope, sparse, lr, idx=FAKE + 2) == B.SLR_EINVAL
+    assert _bwd(shape, rope, sparse, lr, dk=MISALIGNED) == B.SLR_EINVAL
+    # outputs may not alias an input or each other
+    assert _bwd(shape, rope, sparse, lr, dq=FAKE) == B.SLR_EINVAL
+    assert _bwd(shape, rope, sparse, lr, dv=FAKE + 0x2000) == B.SLR_EINVAL
+    assert _bwd(shape, rope, sparse, lr, dk=FAKE + 0x6000) == B.SLR_EINVAL
+
+
+@pytest.mark.parametrize("change", ["f32", "token_gate", "abspe"])
+def test_backward_unsupported_settings(change):
+    shape, rope, sparse, lr = _cfgs()
+    if change == "f32":
+        shape.dtype = B.SLR_F32
+    elif change == "token_gate":
+        lr.gate_mode, lr.gate, lr.Wg, lr.bg = B.SLR_GATE_TOKEN, None, FAKE, FAKE
+    else:
+        lr.mode, lr.Et, lr.Eh, lr.Ew = B.SLR_LR_ABS_PE, FAKE, FAKE, FAKE
+    n = ctypes.c_size_t()
+    r = ctypes.byref
+    assert B.lib().slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, r(shape), r(rope), r(sparse), r(lr),
+                                       r(n)) == B.SLR_EUNSUPPORTED
+    assert _bwd(shape, rope, sparse, lr, ws=FAKE, ws_bytes=1 << 40) == B.SLR_EUNSUPPORTED

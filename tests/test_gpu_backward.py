@@ -1,0 +1,150 @@
+"""GPU parity of the layer backward (slr_attention_bwd) with the oracle's.
+
+The GPU forward supplies the selection (checked to be a valid top-k) and
+its O_sparse, as a training step would; the oracle recomputes its own O in
+float64 on the same selection. Bar (bf16 layers): relative Frobenius error
+<= 1e-2 and max-abs error <= 3e-2 x max |reference| for dq, dk, dv, dW_q,
+dW_k and the gate gradient. (The gradients are ~0.05 RMS, so the forward's
+absolute 3e-2 is stated relative to the gradient's own scale.)
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import backward as OB
+from sparse_rank_attention_rope3d_amd import binding as B
+from sparse_rank_attention_rope3d_amd import synth
+
+import slrtest as T
+
+pytestmark = pytest.mark.gpu
+
+REL, MAXREL = 1e-2, 3e-2
+
+
+def _close(name, got, ref):
+    rf = T.rel_fro(got, ref)
+    scale = float(np.abs(ref).max()) if ref.size else 1.0
+    ma = T.max_abs(got, ref) / (scale if scale > 0 else 1.0)
+    T.log(f"    {name}: rel_fro={rf:.3e} max_abs/max|ref|={ma:.3e}")
+    assert rf <= REL, f"{name}: relative Frobenius error {rf:.3e} > {REL}"
+    assert ma <= MAXREL, f"{name}: max abs error {ma:.3e} x max|ref| > {MAXREL}"
+
+
+def _dout(cfg):
+    g = torch.empty((cfg.B, cfg.H, cfg.L, cfg.D), dtype=torch.bfloat16, device="cuda")
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            g[b, h] = T.to_device(synth.dout_slice(cfg, b, h), cfg.dtype)
+    return g
+
+
+def _run_gpu(cfg):
+    inp = T.make_inputs(cfg)
+    dout = _dout(cfg)
+    shape, rope, sparse = B.shape_of(cfg), B.rope_of(cfg), B.sparse_of(cfg)
+    lowrank = B.lowrank_of(cfg, inp.params)
+    _, idx, o_sp, _ = B.slr_attention_fwd(inp.q, inp.k, inp.v, shape, rope, sparse, lowrank, debug=True)
+    grads = B.slr_attention_bwd(inp.q, inp.k, inp.v, idx, o_sp, dout, shape, rope, sparse, lowrank)
+    torch.cuda.synchronize()
+    return inp, idx, grads
+
+
+def _oracle_slice(cfg, inp, b, h, ig, qblocks=None, kblocks=None):
+    """dq rows of qblocks and dk, dv rows of kblocks (all rows when None)."""
+    qs, ks, vs = synth.qkv_slice(cfg, b, h)
+    ds = np.asarray(synth.dout_slice(cfg, b, h), np.float64)
+    p = inp.params_np
+    grid = (cfg.T, cfg.Hg, cfg.Wg)
+    res = oracle.layer_slice(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], p["gate"][h], qblocks=[0], idx=ig)
+    T.check_selection(ig, res["scores"], res["thr"], cfg.keep)
+    qr, kr = res["q_rot"], res["k_rot"]
+    lr = OB.lowrank_bwd(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], float(p["gate"][h]) * ds)
+    spq = OB.sparse_attention_bwd(qr, kr, vs, cfg.block, ig, ds, qblocks=qblocks)
+    if kblocks is None:
+        spk = spq
+    else:
+        spk = OB.sparse_attention_bwd(qr, kr, vs, cfg.block, ig, ds, qblocks=OB.query_blocks_keeping(ig, kblocks))
+    ref = {
+        "dq": OB.rope3d_transpose(spq["dq"], grid, cfg.base, cfg.pairs) + lr["dq"],
+        "dk": OB.rope3d_transpose(spk["dk"], grid, cfg.base, cfg.pairs) + lr["dk"],
+        "dv": spk["dv"] + lr["dv"],
+        "dWq": lr["dWq"], "dWk": lr["dWk"], "dg": float((ds * lr["o_lr"]).sum()),
+    }
+    return ref
+
+
+def _rows(cfg, blocks):
+    if blocks is None:
+        return np.arange(cfg.L)
+    r = (np.asarray(blocks, np.int64)[:, None] * cfg.block + np.arange(cfg.block)[None, :]).reshape(-1)
+    return r[r < cfg.L]
+
+
+def _check(cfg, slices=None, qsample=None, ksample=None, heads=None):
+    T.log(f"  case {cfg.name}: L={cfg.L} nblk={cfg.nblk} keep={cfg.keep} D={cfg.D} r={cfg.rank} fmap={cfg.fmap}")
+    inp, idx, (dq, dk, dv, dWq, dWk, dg) = _run_gpu(cfg)
+    slices = slices or [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    heads = sorted({h for _, h in slices}) if heads is None else heads
+    got = {"dq": [], "dk": [], "dv": []}
+    want = {"dq": [], "dk": [], "dv": []}
+    dW = {}
+    for (b, h) in [(b, h) for h in heads for b in range(cfg.B)] + slices:
+        if (b, h) in dW:
+            continue
+        ig = idx[b, h].cpu().numpy()
+        qb = None if qsample is None else synth.sample_query_blocks(cfg, b, h, qsample)
+        kb = None if ksample is None else synth.sample_query_blocks(cfg, b, h + 1000, ksample)
+        ref = _oracle_slice(cfg, inp, b, h, ig, qb, kb)
+        dW[b, h] = ref
+        if (b, h) in slices:
+            rq, rk = _rows(cfg, qb), _rows(cfg, kb)
+            for name, t, rows in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rk)):
+                got[name].append(T.to_host(t[b, h])[rows])
+                want[name].append(ref[name][rows])
+    for name in ("dq", "dk", "dv"):
+        _close(name, np.concatenate(got[name]), np.concatenate(want[name]))
+    for h in heads:
+        _close(f"dWq[{h}]", T.to_host(dWq[h]), sum(dW[b, h]["dWq"] for b in range(cfg.B)))
+        _close(f"dWk[{h}]", T.to_host(dWk[h]), sum(dW[b, h]["dWk"] for b in range(cfg.B)))
+        _close(f"dgate[{h}]", T.to_host(dg[h:h + 1]), np.array([sum(dW[b, h]["dg"] for b in range(cfg.B))]))
+
+
+SMALL = [
+    # (name, changes to the Wan2.1-1.3B layer)
+    ("ragged 4x9x13 keep3", dict(B=1, H=2, T=4, Hg=9, Wg=13, keep=3)),
+    ("two batches keep1", dict(B=2, H=1, T=3, Hg=8, Wg=16, keep=1)),
+    ("every block kept", dict(B=1, H=2, T=4, Hg=9, Wg=13, keep=8)),
+    ("silu", dict(B=1, H=2, T=4, Hg=9, Wg=13, keep=3, fmap="silu")),
+    ("rank 64", dict(B=1, H=1, T=4, Hg=9, Wg=13, keep=2, rank=64, lr_pairs=(16, 8, 8))),
+    ("rank 8", dict(B=1, H=1, T=4, Hg=9, Wg=13, keep=2, rank=8, lr_pairs=(2, 1, 1))),
+    ("D64 block32", dict(B=1, H=2, D=64, pairs=(12, 10, 10), T=3, Hg=10, Wg=11, block=32, keep=4, rank=16,
+                         lr_pairs=(4, 2, 2))),
+    ("D128 block32 one block", dict(B=1, H=1, T=1, Hg=3, Wg=7, block=32, keep=1)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_backward_small_layers(name, kw):
+    cfg = dataclasses.replace(synth.wan13b(), name=f"bwd {name}", **kw)
+    _check(cfg)
+
+
+def test_backward_wan13b_sampled():
+    """Full Wan2.1-1.3B shape: dq on sampled query blocks, dk, dv on sampled
+    key blocks of two slices; dW_q, dW_k and the gate gradient of their heads
+    over both batches (the low-rank branch is cheap enough for the oracle in
+    full)."""
+    cfg = synth.wan13b()
+    _check(cfg, slices=[(0, 0), (1, 7)], qsample=4, ksample=4)
+
+
+def test_backward_is_deterministic():
+    cfg = dataclasses.replace(synth.wan13b(), name="bwd determinism", B=1, H=2, T=4, Hg=9, Wg=13, keep=3)
+    _, _, g1 = _run_gpu(cfg)
+    _, _, g2 = _run_gpu(cfg)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
