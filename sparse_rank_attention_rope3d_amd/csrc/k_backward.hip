@@ -56,51 +56,84 @@ __device__ __forceinline__ void rot_t(float& y0, float& y1, float2 cs) {
 }
 
 // ---------------------------------------------------------------------------
-// Staging of one BS x D bf16 block of rows into LDS. Thread tid < (BS/8)(D/8)
-// takes 8 rows x 8 dims: rows 16G + 4h + (e & 3) + 8(e >> 2) (e = 0..7) of
-// 16-row group G with lane half h, dims 8c .. 8c+7. `rm` (optional) receives
-// the rows row-major with stride D + 8; `tr` (optional) receives the
-// transpose [D][BS + 8] with the rows of each 16-group at positions
-// 16G + 8h + e, the slot order in which a 32x32 MFMA accumulator holds its
-// rows, so an accumulator packs straight into the B operand that meets it.
-// Rows at or past `limit` read as zeros.
+// Staging of one BS x D bf16 block of rows into LDS, in two steps so the
+// global loads of the next block can be in flight while the current one is
+// consumed. Thread tid < (BS/8)(D/8) takes 8 rows x 8 dims: rows
+// 16G + 4h + (e & 3) + 8(e >> 2) (e = 0..7) of 16-row group G with lane half
+// h, dims 8c .. 8c+7. `rm` (optional) receives the rows row-major with
+// stride D + 8; `tr` (optional) receives the transpose [D][BS + 8] with the
+// rows of each 16-group at positions 16G + 8h + e, the slot order in which a
+// 32x32 MFMA accumulator holds its rows, so an accumulator packs straight
+// into the B operand that meets it. Rows at or past `limit` read as zeros.
 template <int D, int BS>
-__device__ __forceinline__ void stage_block(const uint16_t* __restrict__ src, long row0, long limit, uint16_t* rm,
-                                            uint16_t* tr, int tid) {
-    constexpr int KLD = D + 8, VLD = BS + 8, NB = (BS / 8) * (D / 8);
-    if (tid >= NB) return;
-    const int c = tid % (D / 8), gp = tid / (D / 8), G = gp >> 1, h = gp & 1;
-    u32x4_t x[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int r = 16 * G + 4 * h + (e & 3) + 8 * (e >> 2);
-        x[e] = row0 + r < limit ? ldg16(src + (row0 + r) * D + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
+struct Stager {
+    static constexpr int KLD = D + 8, VLD = BS + 8, NB = (BS / 8) * (D / 8);
+    int c, G, h;
+    bool on;
+    __device__ explicit Stager(int tid) {
+        on = tid < NB;
+        c = tid % (D / 8);
+        const int gp = tid / (D / 8);
+        G = gp >> 1;
+        h = gp & 1;
     }
-    if (rm) {
+    __device__ __forceinline__ int row(int e) const { return 16 * G + 4 * h + (e & 3) + 8 * (e >> 2); }
+    __device__ __forceinline__ void fetch(u32x4_t* x, const uint16_t* __restrict__ src, long row0, long limit) const {
+        if (!on) return;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int r = 16 * G + 4 * h + (e & 3) + 8 * (e >> 2);
-            *reinterpret_cast<u32x4_t*>(rm + r * KLD + 8 * c) = x[e];
+            const long r = row0 + row(e);
+            x[e] = r < limit ? ldg16(src + r * D + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
         }
     }
-    if (tr) {
+    __device__ __forceinline__ void stash(const u32x4_t* x, uint16_t* rm, uint16_t* tr) const {
+        if (!on) return;
+        if (rm) {
 #pragma unroll
-        for (int f = 0; f < 8; ++f) {
-            u32x4_t o;
+            for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4_t*>(rm + row(e) * KLD + 8 * c) = x[e];
+        }
+        if (tr) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t a0 = x[2 * i][f >> 1], a1 = x[2 * i + 1][f >> 1];
-                o[i] = (f & 1) ? __builtin_amdgcn_perm(a1, a0, 0x07060302u) : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+            for (int f = 0; f < 8; ++f) {
+                u32x4_t o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t a0 = x[2 * i][f >> 1], a1 = x[2 * i + 1][f >> 1];
+                    o[i] = (f & 1) ? __builtin_amdgcn_perm(a1, a0, 0x07060302u)
+                                   : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+                }
+                *reinterpret_cast<u32x4_t*>(tr + (8 * c + f) * VLD + 16 * G + 8 * h) = o;
             }
-            *reinterpret_cast<u32x4_t*>(tr + (8 * c + f) * VLD + 16 * G + 8 * h) = o;
         }
     }
+};
+
+// Eight 16-byte LDS reads into distinct registers, read i at byte offset
+// (i & 1) * SI + (i >> 1) * SO from base; the block waits for them itself
+// (early-clobber outputs: no destination can alias the address register).
+template <int SI, int SO>
+__device__ __forceinline__ void lds_read8x(u32x4_t* r, const uint16_t* base) {
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)base;
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%9\n\t"
+        "ds_read_b128 %1, %8 offset:%10\n\t"
+        "ds_read_b128 %2, %8 offset:%11\n\t"
+        "ds_read_b128 %3, %8 offset:%12\n\t"
+        "ds_read_b128 %4, %8 offset:%13\n\t"
+        "ds_read_b128 %5, %8 offset:%14\n\t"
+        "ds_read_b128 %6, %8 offset:%15\n\t"
+        "ds_read_b128 %7, %8 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a), "n"(0), "n"(SI), "n"(SO), "n"(SI + SO), "n"(2 * SO), "n"(SI + 2 * SO), "n"(3 * SO),
+          "n"(SI + 3 * SO)
+        : "memory");
 }
 
 // ---------------------------------------------------------------------------
 // dQ. Workgroup = one query block, BS/32 waves of 32 rows.
 template <int D, int BS>
-__global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a) {
+__global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a, const int32_t* __restrict__ idx_all) {
     constexpr int KLD = D + 8, VLD = BS + 8, NKB = BS / 32, NS = D / 16, NDB = D / 32;
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[BS * KLD];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[BS * KLD];
@@ -117,7 +150,7 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a) {
     const bool qval = qrow < L;
     const uint16_t* kr = a.kr + bh * rows * D;
     const uint16_t* vg = a.v + bh * L * D;
-    const int32_t* ix = a.idx + (bh * a.nblk + qb) * (long)a.keep;
+    const int32_t* ix = idx_all + (bh * a.nblk + qb) * (long)a.keep;
 
     // B operands: rotated q row and dO row (dims 16s + 8hf + e); delta = dO . O
     u32x4_t qop[NS], doop[NS];
@@ -144,14 +177,33 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a) {
     const float sl2 = a.scale * kLog2e;
     const bool ragged = (L % BS) != 0;
 
+    // kept tiles in list order, entries outside [0, nblk) skipped; the list
+    // is read with scalar loads (uniform per workgroup)
+    auto next_tile = [&](int n) {
+        while (n < a.keep) {
+            const int j = __builtin_amdgcn_readfirstlane(ix[n]);
+            if (j >= 0 && j < a.nblk) break;
+            ++n;
+        }
+        return n;
+    };
+    auto tile_at = [&](int n) { return __builtin_amdgcn_readfirstlane(ix[n]); };
+    const Stager<D, BS> stg(tid);
+    u32x4_t xk[8], xv[8];   // next tile's rows, in flight while the current one is consumed
+
     // ---- pass 1: log-sum-exp of each row over its kept keys (log2 units)
     float m_run = -INFINITY, l_run = 0.f;
-    for (int n = 0; n < a.keep; ++n) {
-        const int j = ix[n];
-        if (j < 0 || j >= a.nblk) continue;
+    int n = next_tile(0);
+    if (n < a.keep) stg.fetch(xk, kr, (long)tile_at(n) * BS, rows);
+    // nothing from the prologue stays in flight into the loop
+    wait_vmcnt<0>();
+    while (n < a.keep) {
+        const int j = tile_at(n);
         __syncthreads();
-        stage_block<D, BS>(kr, (long)j * BS, rows, k_lds, nullptr, tid);
+        stg.stash(xk, k_lds, nullptr);
         __syncthreads();
+        n = next_tile(n + 1);
+        if (n < a.keep) stg.fetch(xk, kr, (long)tile_at(n) * BS, rows);
         float x[NKB][16];
         float mx = -INFINITY;
 #pragma unroll
@@ -159,10 +211,17 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a) {
             f32x16_t sacc;
 #pragma unroll
             for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+            if constexpr (NS == 8) {
+                u32x4_t ak[8];
+                lds_read8x<32, 64>(ak, k_lds + (32 * kb + l32) * KLD + 8 * hf);
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
-                sacc = mfma32(*reinterpret_cast<const u32x4_t*>(k_lds + (32 * kb + l32) * KLD + 16 * s + 8 * hf),
-                              qop[s], sacc);
+                for (int s = 0; s < 8; ++s) sacc = mfma32(ak[s], qop[s], sacc);
+            } else {
+#pragma unroll
+                for (int s = 0; s < NS; ++s)
+                    sacc = mfma32(*reinterpret_cast<const u32x4_t*>(k_lds + (32 * kb + l32) * KLD + 16 * s + 8 * hf),
+                                  qop[s], sacc);
+            }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const long key = (long)j * BS + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
@@ -200,23 +259,44 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
-    for (int n = 0; n < a.keep; ++n) {
-        const int j = ix[n];
-        if (j < 0 || j >= a.nblk) continue;
+    n = next_tile(0);
+    if (n < a.keep) {
+        stg.fetch(xk, kr, (long)tile_at(n) * BS, rows);
+        stg.fetch(xv, vg, (long)tile_at(n) * BS, L);
+    }
+    wait_vmcnt<0>();
+    while (n < a.keep) {
+        const int j = tile_at(n);
         __syncthreads();
-        stage_block<D, BS>(kr, (long)j * BS, rows, k_lds, kt_lds, tid);
-        stage_block<D, BS>(vg, (long)j * BS, L, v_lds, nullptr, tid);
+        stg.stash(xk, k_lds, kt_lds);
+        stg.stash(xv, v_lds, nullptr);
         __syncthreads();
+        n = next_tile(n + 1);
+        if (n < a.keep) {
+            stg.fetch(xk, kr, (long)tile_at(n) * BS, rows);
+            stg.fetch(xv, vg, (long)tile_at(n) * BS, L);
+        }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             f32x16_t sacc, dpacc;
 #pragma unroll
             for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; dpacc[i] = 0.f; }
+            if constexpr (NS == 8) {
+                u32x4_t ak[8], av[8];
+                lds_read8x<32, 64>(ak, k_lds + (32 * kb + l32) * KLD + 8 * hf);
+                lds_read8x<32, 64>(av, v_lds + (32 * kb + l32) * KLD + 8 * hf);
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const int o = (32 * kb + l32) * KLD + 16 * s + 8 * hf;
-                sacc = mfma32(*reinterpret_cast<const u32x4_t*>(k_lds + o), qop[s], sacc);
-                dpacc = mfma32(*reinterpret_cast<const u32x4_t*>(v_lds + o), doop[s], dpacc);
+                for (int s = 0; s < 8; ++s) {
+                    sacc = mfma32(ak[s], qop[s], sacc);
+                    dpacc = mfma32(av[s], doop[s], dpacc);
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const int o = (32 * kb + l32) * KLD + 16 * s + 8 * hf;
+                    sacc = mfma32(*reinterpret_cast<const u32x4_t*>(k_lds + o), qop[s], sacc);
+                    dpacc = mfma32(*reinterpret_cast<const u32x4_t*>(v_lds + o), doop[s], dpacc);
+                }
             }
             float ds[16];
 #pragma unroll
@@ -230,13 +310,20 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a) {
             for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dsop[h2][i] = pack_bf2(ds[8 * h2 + 2 * i], ds[8 * h2 + 2 * i + 1]);
+            if constexpr (NDB == 4) {
+                u32x4_t at[8];   // (db, h2) = (i / 2, i % 2)
+                lds_read8x<32, 64 * VLD>(at, kt_lds + l32 * VLD + 32 * kb + 8 * hf);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+                for (int i = 0; i < 8; ++i) dqacc[i >> 1] = mfma32(at[i], dsop[i & 1], dqacc[i >> 1]);
+            } else {
 #pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-                    dqacc[db] = mfma32(
-                        *reinterpret_cast<const u32x4_t*>(kt_lds + (32 * db + l32) * VLD + 32 * kb + 16 * h2 + 8 * hf),
-                        dsop[h2], dqacc[db]);
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+                        dqacc[db] = mfma32(*reinterpret_cast<const u32x4_t*>(kt_lds + (32 * db + l32) * VLD + 32 * kb +
+                                                                             16 * h2 + 8 * hf),
+                                           dsop[h2], dqacc[db]);
+            }
         }
     }
 
@@ -266,7 +353,8 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK, dV. Workgroup = one key block, BS/32 waves of 32 keys.
 template <int D, int BS>
-__global__ __launch_bounds__(BS * 2) void k_bwd_dkdv(BwdArgs a) {
+__global__ __launch_bounds__(BS * 2) void k_bwd_dkdv(BwdArgs a, const int32_t* __restrict__ inv_off,
+                                                   const int32_t* __restrict__ inv_list) {
     constexpr int KLD = D + 8, VLD = BS + 8, NQB = BS / 32, NS = D / 16, NDB = D / 32;
     __shared__ __attribute__((aligned(16))) uint16_t q_lds[BS * KLD];
     __shared__ __attribute__((aligned(16))) uint16_t do_lds[BS * KLD];
@@ -304,29 +392,55 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dkdv(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) { dkacc[db][i] = 0.f; dvacc[db][i] = 0.f; }
 
-    const int32_t* off = a.inv_off + bh * (long)(a.nblk + 1);
-    const int32_t* list = a.inv_list + bh * (long)a.nblk * a.keep;
-    const int n0 = off[jb], n1 = off[jb + 1];
-    for (int n = n0; n < n1; ++n) {
-        const int i = list[n];
-        __syncthreads();
-        stage_block<D, BS>(qr, (long)i * BS, rows, q_lds, qt_lds, tid);
-        stage_block<D, BS>(dg, (long)i * BS, L, do_lds, dot_lds, tid);
+    const int32_t* off = inv_off + bh * (long)(a.nblk + 1);
+    const int32_t* list = inv_list + bh * (long)a.nblk * a.keep;
+    const int n0 = __builtin_amdgcn_readfirstlane(off[jb]), n1 = __builtin_amdgcn_readfirstlane(off[jb + 1]);
+    auto qblock_at = [&](int n) { return __builtin_amdgcn_readfirstlane(list[n]); };
+    const Stager<D, BS> stg(tid);
+    u32x4_t xq[8], xd[8];   // next query block's rows, in flight while the current one is consumed
+    float xl = 0.f, xdl = 0.f;
+    auto fetch = [&](int i) {
+        stg.fetch(xq, qr, (long)i * BS, rows);
+        stg.fetch(xd, dg, (long)i * BS, L);
         if (tid < BS) {
-            lse_lds[tid] = a.lse2[bh * rows + (long)i * BS + tid];
-            dl_lds[tid] = a.delta[bh * rows + (long)i * BS + tid];
+            xl = a.lse2[bh * rows + (long)i * BS + tid];
+            xdl = a.delta[bh * rows + (long)i * BS + tid];
+        }
+    };
+    if (n0 < n1) fetch(qblock_at(n0));
+    // nothing from the prologue stays in flight into the loop
+    wait_vmcnt<0>();
+    for (int n = n0; n < n1; ++n) {
+        __syncthreads();
+        stg.stash(xq, q_lds, qt_lds);
+        stg.stash(xd, do_lds, dot_lds);
+        if (tid < BS) {
+            lse_lds[tid] = xl;
+            dl_lds[tid] = xdl;
         }
         __syncthreads();
+        if (n + 1 < n1) fetch(qblock_at(n + 1));
 #pragma unroll
         for (int qs = 0; qs < NQB; ++qs) {
             f32x16_t sacc, dpacc;
 #pragma unroll
             for (int e = 0; e < 16; ++e) { sacc[e] = 0.f; dpacc[e] = 0.f; }
+            if constexpr (NS == 8) {
+                u32x4_t aq[8], ad[8];
+                lds_read8x<32, 64>(aq, q_lds + (32 * qs + l32) * KLD + 8 * hf);
+                lds_read8x<32, 64>(ad, do_lds + (32 * qs + l32) * KLD + 8 * hf);
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const int o = (32 * qs + l32) * KLD + 16 * s + 8 * hf;
-                sacc = mfma32(*reinterpret_cast<const u32x4_t*>(q_lds + o), kop[s], sacc);
-                dpacc = mfma32(*reinterpret_cast<const u32x4_t*>(do_lds + o), vop[s], dpacc);
+                for (int s = 0; s < 8; ++s) {
+                    sacc = mfma32(aq[s], kop[s], sacc);
+                    dpacc = mfma32(ad[s], vop[s], dpacc);
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const int o = (32 * qs + l32) * KLD + 16 * s + 8 * hf;
+                    sacc = mfma32(*reinterpret_cast<const u32x4_t*>(q_lds + o), kop[s], sacc);
+                    dpacc = mfma32(*reinterpret_cast<const u32x4_t*>(do_lds + o), vop[s], dpacc);
+                }
             }
             // lane = key, register e = query row 32qs + 8(e/4) + 4hf + e%4
             float p[16], ds[16];
@@ -344,14 +458,25 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dkdv(BwdArgs a) {
                     pb[h2][e] = pack_bf2(p[8 * h2 + 2 * e], p[8 * h2 + 2 * e + 1]);
                     dsb[h2][e] = pack_bf2(ds[8 * h2 + 2 * e], ds[8 * h2 + 2 * e + 1]);
                 }
+            if constexpr (NDB == 4) {
+                u32x4_t at[8], aq[8];   // (db, h2) = (i / 2, i % 2)
+                lds_read8x<32, 64 * VLD>(at, dot_lds + l32 * VLD + 32 * qs + 8 * hf);
+                lds_read8x<32, 64 * VLD>(aq, qt_lds + l32 * VLD + 32 * qs + 8 * hf);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const int o = (32 * db + l32) * VLD + 32 * qs + 16 * h2 + 8 * hf;
-                    dvacc[db] = mfma32(*reinterpret_cast<const u32x4_t*>(dot_lds + o), pb[h2], dvacc[db]);
-                    dkacc[db] = mfma32(*reinterpret_cast<const u32x4_t*>(qt_lds + o), dsb[h2], dkacc[db]);
+                for (int i = 0; i < 8; ++i) {
+                    dvacc[i >> 1] = mfma32(at[i], pb[i & 1], dvacc[i >> 1]);
+                    dkacc[i >> 1] = mfma32(aq[i], dsb[i & 1], dkacc[i >> 1]);
                 }
+            } else {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int o = (32 * db + l32) * VLD + 32 * qs + 16 * h2 + 8 * hf;
+                        dvacc[db] = mfma32(*reinterpret_cast<const u32x4_t*>(dot_lds + o), pb[h2], dvacc[db]);
+                        dkacc[db] = mfma32(*reinterpret_cast<const u32x4_t*>(qt_lds + o), dsb[h2], dkacc[db]);
+                    }
+            }
         }
     }
 
@@ -475,25 +600,167 @@ __device__ __forceinline__ void phi_grad(int fmap, float x, float& f, float& df)
 
 __device__ __forceinline__ float round_bf(float x) { return bf2f(f2bf(x)); }
 
+// Shared tile machinery of the two low-rank kernels: fp32 LDS copies of the
+// weights W [D][R + 4] and of S (or dS) [R][D], a tile of TT token rows of
+// two inputs [TT][D + 4], and per-token rank vectors [TT][R + 4]. Every
+// product is register-blocked over float4 LDS reads: work items take the
+// token index fastest (lanes then read rows 16 bytes apart mod 256: no bank
+// conflicts) and 4 outputs each; the partial sums over tokens take 4x4
+// blocks per thread.
+template <int D, int R>
+struct LrTile {
+    static constexpr int TT = 32, XLD = D + 4, RW = R + 4, RLD = R + 4;
+    static constexpr int NBLK = D * R / 16;                  // 4x4 blocks of a [D][R] or [R][D] sum
+    static constexpr int NB16 = (NBLK + 255) / 256;          // blocks per thread
+};
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void fma4(float4& acc, float s, const float4& v) {
+    acc.x += s * v.x; acc.y += s * v.y; acc.z += s * v.z; acc.w += s * v.w;
+}
+
+// y[t][4g .. 4g+3] = sum_r v[t][r] M[4g + i][r] (M rows of length R, stride ld)
+template <int R>
+__device__ __forceinline__ float4 rowdot4(const float* vrow, const float* M, int ld, int g) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 2
+    for (int r = 0; r < R; r += 4) {
+        const float4 v = ld4(vrow + r);
+        const float4 m0 = ld4(M + (4 * g) * ld + r), m1 = ld4(M + (4 * g + 1) * ld + r);
+        const float4 m2 = ld4(M + (4 * g + 2) * ld + r), m3 = ld4(M + (4 * g + 3) * ld + r);
+        acc.x += v.x * m0.x + v.y * m0.y + v.z * m0.z + v.w * m0.w;
+        acc.y += v.x * m1.x + v.y * m1.y + v.z * m1.z + v.w * m1.w;
+        acc.z += v.x * m2.x + v.y * m2.y + v.z * m2.z + v.w * m2.w;
+        acc.w += v.x * m3.x + v.y * m3.y + v.z * m3.z + v.w * m3.w;
+    }
+    return acc;
+}
+
+// y[t][4g .. 4g+3] = sum_k v[t][k] M[k][4g .. 4g+3] (M rows of length >= 4g + 4, stride ld), K terms
+template <int K>
+__device__ __forceinline__ float4 vecmat4(const float* vrow, const float* M, int ld, int g) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 2
+    for (int k = 0; k < K; k += 4) {
+        const float4 v = ld4(vrow + k);
+        fma4(acc, v.x, ld4(M + k * ld + 4 * g));
+        fma4(acc, v.y, ld4(M + (k + 1) * ld + 4 * g));
+        fma4(acc, v.z, ld4(M + (k + 2) * ld + 4 * g));
+        fma4(acc, v.w, ld4(M + (k + 3) * ld + 4 * g));
+    }
+    return acc;
+}
+
+// Load TT token rows of two bf16 [L][D] inputs into fp32 LDS tiles (zeros past t_hi).
+template <int D, int R>
+__device__ __forceinline__ void lr_load_rows(const uint16_t* a_src, const uint16_t* b_src, long t0, long t_hi,
+                                             float* xa, float* xb, int tid) {
+    using Tl = LrTile<D, R>;
+    for (int e = tid; e < Tl::TT * D / 8; e += 256) {
+        const int t = e / (D / 8), c = e % (D / 8);
+        const long l = t0 + t;
+        u32x4_t ua{0u, 0u, 0u, 0u}, ub{0u, 0u, 0u, 0u};
+        if (l < t_hi) {
+            ua = ldg16(a_src + l * D + 8 * c);
+            ub = ldg16(b_src + l * D + 8 * c);
+        }
+        float* pa = xa + t * Tl::XLD + 8 * c;
+        float* pb = xb + t * Tl::XLD + 8 * c;
+        *reinterpret_cast<float4*>(pa) = make_float4(bf_lo(ua[0]), bf_hi(ua[0]), bf_lo(ua[1]), bf_hi(ua[1]));
+        *reinterpret_cast<float4*>(pa + 4) = make_float4(bf_lo(ua[2]), bf_hi(ua[2]), bf_lo(ua[3]), bf_hi(ua[3]));
+        *reinterpret_cast<float4*>(pb) = make_float4(bf_lo(ub[0]), bf_hi(ub[0]), bf_lo(ub[1]), bf_hi(ub[1]));
+        *reinterpret_cast<float4*>(pb + 4) = make_float4(bf_lo(ub[2]), bf_hi(ub[2]), bf_lo(ub[3]), bf_hi(ub[3]));
+    }
+}
+
+// Projection and feature map of a token tile: p = x W, f_raw = phi(p) -> wt,
+// phi'(p) -> dt; then the rotation after phi -> ft (pairs of one token).
+template <int D, int R>
+__device__ __forceinline__ void lr_features(const LrBwdArgs& a, const float* x, const float* w_s, float* wt,
+                                            float* ft, float* dt, long t0, long t_hi, int tid) {
+    using Tl = LrTile<D, R>;
+    for (int e = tid; e < Tl::TT * (R / 4); e += 256) {
+        const int t = e % Tl::TT, g = e / Tl::TT;
+        const float4 p = vecmat4<D>(x + t * Tl::XLD, w_s, Tl::RW, g);
+        float f[4], df[4];
+        phi_grad(a.g.fmap, p.x, f[0], df[0]);
+        phi_grad(a.g.fmap, p.y, f[1], df[1]);
+        phi_grad(a.g.fmap, p.z, f[2], df[2]);
+        phi_grad(a.g.fmap, p.w, f[3], df[3]);
+        *reinterpret_cast<float4*>(wt + t * Tl::RLD + 4 * g) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(dt + t * Tl::RLD + 4 * g) = make_float4(df[0], df[1], df[2], df[3]);
+        // rotation after phi of the two pairs (4g, 4g+1), (4g+2, 4g+3)
+        const long l = t0 + t;
+        if (l < t_hi) {
+            int crd[3];
+            token_coords(l, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const float2 cs = lowrank_cs(a.tab, a.g, 2 * g + q2, crd);
+                const float f0 = f[2 * q2], f1 = f[2 * q2 + 1];
+                f[2 * q2] = f0 * cs.x - f1 * cs.y;
+                f[2 * q2 + 1] = f0 * cs.y + f1 * cs.x;
+            }
+        }
+        *reinterpret_cast<float4*>(ft + t * Tl::RLD + 4 * g) = make_float4(f[0], f[1], f[2], f[3]);
+    }
+}
+
+// d_pre[t][r] = (rho_t^T (sum_d M[r][d] v[t][d] * scale_t) + add_t z[r]) * phi'[t][r]
+// (dt holds phi' on entry and the result on exit), pairs of one token per item.
+template <int D, int R>
+__device__ __forceinline__ void lr_back_features(const LrBwdArgs& a, const float* vtile, const float* m_s,
+                                                 const float* z_s, const float* scale_t, const float* add_t,
+                                                 float* dt, long t0, long t_hi, int tid) {
+    using Tl = LrTile<D, R>;
+    for (int e = tid; e < Tl::TT * (R / 2); e += 256) {
+        const int t = e % Tl::TT, pr = e / Tl::TT;
+        const float* vr = vtile + t * Tl::XLD;
+        const float* m0 = m_s + (2 * pr) * D;
+        const float* m1 = m0 + D;
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll 4
+        for (int d = 0; d < D; d += 4) {
+            const float4 v = ld4(vr + d), x0 = ld4(m0 + d), x1 = ld4(m1 + d);
+            a0 += v.x * x0.x + v.y * x0.y + v.z * x0.z + v.w * x0.w;
+            a1 += v.x * x1.x + v.y * x1.y + v.z * x1.z + v.w * x1.w;
+        }
+        const float sc = scale_t ? scale_t[t] : 1.f;
+        a0 *= sc;
+        a1 *= sc;
+        const long l = t0 + t;
+        if (l < t_hi) {
+            int crd[3];
+            token_coords(l, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
+            rot_t(a0, a1, lowrank_cs(a.tab, a.g, pr, crd));
+        }
+        const float ad = add_t ? add_t[t] : 1.f;
+        dt[t * Tl::RLD + 2 * pr] *= a0 + ad * z_s[2 * pr];
+        dt[t * Tl::RLD + 2 * pr + 1] *= a1 + ad * z_s[2 * pr + 1];
+    }
+}
+
 // Query side, per token l (O_l = rho_l(w_l)^T S / n_l, w_l = phi(q_l W_q),
 // n_l = w_l . z + eps, or L for SiLU), given dO_lr = g_h dout:
 //   dfq = S dO / n, dn = -(dO . O) / n, dw = rho^T dfq + dn z, dpq = dw phi',
 //   dq_lr = W_q dpq; partial sums of dW_q = q^T dpq, dS = fq dO^T / n,
 //   dz = dn w and dg = dout . O over the workgroup's tokens.
-// Partial layout per (slice, split): [dW_q D*R | dS R*D | dz R | dg 1].
+// Partial layout per (slice, split): [dW_q D*R | dS R*D | dz R | dg 1 | pad 3]
+// (a stride of 2DR + R + 4 floats keeps every block 16-byte aligned).
 template <int D, int R>
 __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
-    constexpr int TT = 32, XLD = D + 1, RLD = R + 1, NW = D * R / 256;
-    static_assert(NW >= 1 && D * R % 256 == 0, "partials per thread");
-    __shared__ float w_s[D * R];
-    __shared__ float s_s[R * D];
+    using Tl = LrTile<D, R>;
+    constexpr int TT = Tl::TT, XLD = Tl::XLD, RW = Tl::RW, RLD = Tl::RLD, NB16 = Tl::NB16;
+    __shared__ __attribute__((aligned(16))) float w_s[D * RW];
+    __shared__ __attribute__((aligned(16))) float s_s[R * D];
     __shared__ float z_s[R];
-    __shared__ float x_s[TT * XLD];
-    __shared__ float g_s[TT * XLD];
-    __shared__ float w_t[TT * RLD];
-    __shared__ float f_t[TT * RLD];
-    __shared__ float d_t[TT * RLD];
-    __shared__ float n_s[TT], dn_s[TT];
+    __shared__ __attribute__((aligned(16))) float x_s[TT * XLD];
+    __shared__ __attribute__((aligned(16))) float g_s[TT * XLD];
+    __shared__ __attribute__((aligned(16))) float w_t[TT * RLD];
+    __shared__ __attribute__((aligned(16))) float f_t[TT * RLD];
+    __shared__ __attribute__((aligned(16))) float d_t[TT * RLD];
+    __shared__ float part_s[(D / 4) * TT];
+    __shared__ float n_s[TT], dn_s[TT], sc_s[TT];
     __shared__ float red[256];
     const int tid = threadIdx.x;
     const int split = blockIdx.x;
@@ -504,127 +771,81 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
     const long t_hi = t_lo + a.chunk < L ? t_lo + a.chunk : L;
     const float gh = a.gate[head];
     const bool silu = a.g.fmap != 0;
-    for (int e = tid; e < D * R; e += 256) w_s[e] = round_bf(a.Wq[(long)head * D * R + e]);
+    for (int e = tid; e < D * R; e += 256) w_s[(e / R) * RW + e % R] = round_bf(a.Wq[(long)head * D * R + e]);
     for (int e = tid; e < R * D; e += 256) s_s[e] = a.S[bh * R * D + e];
     for (int e = tid; e < R; e += 256) z_s[e] = a.z[bh * R + e];
-    float accW[NW], accS[NW], accz = 0.f, accg = 0.f;
+    float4 accW[NB16][4], accS[NB16][4];
 #pragma unroll
-    for (int c = 0; c < NW; ++c) { accW[c] = 0.f; accS[c] = 0.f; }
+    for (int c = 0; c < NB16; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            accW[c][i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            accS[c][i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    float accz = 0.f, accg = 0.f;
     const uint16_t* qs = a.q + bh * L * D;
     const uint16_t* gs = a.dout + bh * L * D;
-    __syncthreads();
 
     for (long t0 = t_lo; t0 < t_hi; t0 += TT) {
-        for (int e = tid; e < TT * D / 8; e += 256) {
-            const int t = e / (D / 8), c = e % (D / 8);
-            const long l = t0 + t;
-            u32x4_t xq{0u, 0u, 0u, 0u}, xg{0u, 0u, 0u, 0u};
-            if (l < t_hi) {
-                xq = ldg16(qs + l * D + 8 * c);
-                xg = ldg16(gs + l * D + 8 * c);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x_s[t * XLD + 8 * c + 2 * i] = bf_lo(xq[i]);
-                x_s[t * XLD + 8 * c + 2 * i + 1] = bf_hi(xq[i]);
-                g_s[t * XLD + 8 * c + 2 * i] = bf_lo(xg[i]);
-                g_s[t * XLD + 8 * c + 2 * i + 1] = bf_hi(xg[i]);
-            }
-        }
         __syncthreads();
-        for (int e = tid; e < TT * R; e += 256) {
-            const int t = e / R, r = e % R;
-            float acc = 0.f;
-#pragma unroll 8
-            for (int d = 0; d < D; ++d) acc += x_s[t * XLD + d] * w_s[d * R + r];
-            float f, df;
-            phi_grad(a.g.fmap, acc, f, df);
-            w_t[t * RLD + r] = f;
-            d_t[t * RLD + r] = df;
-        }
+        lr_load_rows<D, R>(qs, gs, t0, t_hi, x_s, g_s, tid);
         __syncthreads();
-        for (int e = tid; e < TT * R / 2; e += 256) {
-            const int t = e / (R / 2), pr = e % (R / 2);
-            const long l = t0 + t;
-            float f0 = w_t[t * RLD + 2 * pr], f1 = w_t[t * RLD + 2 * pr + 1];
-            if (l < t_hi) {
-                int crd[3];
-                token_coords(l, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
-                const float2 cs = lowrank_cs(a.tab, a.g, pr, crd);
-                const float y0 = f0 * cs.x - f1 * cs.y, y1 = f0 * cs.y + f1 * cs.x;
-                f0 = y0;
-                f1 = y1;
-            }
-            f_t[t * RLD + 2 * pr] = f0;
-            f_t[t * RLD + 2 * pr + 1] = f1;
-        }
+        lr_features<D, R>(a, x_s, w_s, w_t, f_t, d_t, t0, t_hi, tid);
+        __syncthreads();
         if (tid < TT) {
             float n = 0.f;
             for (int r = 0; r < R; ++r) n += w_t[tid * RLD + r] * z_s[r];
             n_s[tid] = silu ? (float)L : n + a.eps;
         }
+        // readout O = fq S / n (unnormalised here) and its dot with dout, per (token, 4 dims)
+        for (int e = tid; e < TT * (D / 4); e += 256) {
+            const int t = e % TT, g = e / TT;
+            const float4 o = vecmat4<R>(f_t + t * RLD, s_s, D, g);
+            const float4 go = ld4(g_s + t * XLD + 4 * g);
+            part_s[g * TT + t] = go.x * o.x + go.y * o.y + go.z * o.z + go.w * o.w;
+        }
         __syncthreads();
-        {
-            // 8 threads per row: readout O and dout . O
-            const int t = tid >> 3, c = tid & 7;
-            const float invn = 1.f / n_s[t];
+        if (tid < TT) {
             float dot = 0.f;
-            for (int dd = 0; dd < D / 8; ++dd) {
-                const int d = c + 8 * dd;
-                float o = 0.f;
-                for (int r = 0; r < R; ++r) o += f_t[t * RLD + r] * s_s[r * D + d];
-                dot += g_s[t * XLD + d] * (o * invn);
-            }
-            dot += __shfl_xor(dot, 1, 64);
-            dot += __shfl_xor(dot, 2, 64);
-            dot += __shfl_xor(dot, 4, 64);
-            if (c == 0) {
-                dn_s[t] = silu ? 0.f : -gh * dot * invn;
-                accg += dot;
-            }
+            for (int g = 0; g < D / 4; ++g) dot += part_s[g * TT + tid];
+            const float invn = 1.f / n_s[tid];
+            dot *= invn;
+            dn_s[tid] = silu ? 0.f : -gh * dot * invn;
+            sc_s[tid] = gh * invn;
+            accg += dot;
         }
         __syncthreads();
-        for (int e = tid; e < TT * R / 2; e += 256) {
-            const int t = e / (R / 2), pr = e % (R / 2);
-            const long l = t0 + t;
-            const float sc = gh / n_s[t];
-            float a0 = 0.f, a1 = 0.f;
-#pragma unroll 8
-            for (int d = 0; d < D; ++d) {
-                const float go = g_s[t * XLD + d];
-                a0 += s_s[(2 * pr) * D + d] * go;
-                a1 += s_s[(2 * pr + 1) * D + d] * go;
-            }
-            a0 *= sc;
-            a1 *= sc;
-            if (l < t_hi) {
-                int crd[3];
-                token_coords(l, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
-                rot_t(a0, a1, lowrank_cs(a.tab, a.g, pr, crd));
-            }
-            const float dn = dn_s[t];
-            d_t[t * RLD + 2 * pr] *= a0 + dn * z_s[2 * pr];
-            d_t[t * RLD + 2 * pr + 1] *= a1 + dn * z_s[2 * pr + 1];
-        }
+        // dfq = S (g dout) / n -> rho^T, + dn z, * phi'  (d_t becomes dpq)
+        lr_back_features<D, R>(a, g_s, s_s, z_s, sc_s, dn_s, d_t, t0, t_hi, tid);
         __syncthreads();
-        for (int e = tid; e < TT * D; e += 256) {
-            const int t = e / D, d = e % D;
+        // dq_lr = W_q dpq per (token, 4 dims)
+        for (int e = tid; e < TT * (D / 4); e += 256) {
+            const int t = e % TT, g = e / TT;
             const long l = t0 + t;
-            if (l < t_hi) {
-                float acc = 0.f;
-                for (int r = 0; r < R; ++r) acc += w_s[d * R + r] * d_t[t * RLD + r];
-                a.dq_lr[(bh * L + l) * D + d] = acc;
-            }
+            const float4 y = rowdot4<R>(d_t + t * RLD, w_s, RW, g);
+            if (l < t_hi) *reinterpret_cast<float4*>(a.dq_lr + (bh * L + l) * D + 4 * g) = y;
         }
-        // partial sums: element tid + 256c of dW_q [D][R] and of dS [R][D]
-#pragma unroll 1
-        for (int t = 0; t < TT; ++t) {
-            const float sc = gh / n_s[t];
+        // partial sums over the tile's tokens, 4x4 blocks
 #pragma unroll
-            for (int c = 0; c < NW; ++c) {
-                const int e = tid + 256 * c;
-                accW[c] += x_s[t * XLD + e / R] * d_t[t * RLD + e % R];
-                accS[c] += f_t[t * RLD + e / D] * (g_s[t * XLD + e % D] * sc);
+        for (int c = 0; c < NB16; ++c) {
+            const int blk = tid + 256 * c;
+            if (blk < Tl::NBLK) {
+                const int bd = blk / (R / 4), br = blk % (R / 4);     // dW_q block (4 d) x (4 r)
+                const int sr = blk / (D / 4), sd = blk % (D / 4);     // dS block (4 r) x (4 d)
+#pragma unroll 4
+                for (int t = 0; t < TT; ++t) {
+                    const float4 xv = ld4(x_s + t * XLD + 4 * bd), dv = ld4(d_t + t * RLD + 4 * br);
+                    fma4(accW[c][0], xv.x, dv);
+                    fma4(accW[c][1], xv.y, dv);
+                    fma4(accW[c][2], xv.z, dv);
+                    fma4(accW[c][3], xv.w, dv);
+                    const float sc = sc_s[t];
+                    const float4 fv = ld4(f_t + t * RLD + 4 * sr), gv = ld4(g_s + t * XLD + 4 * sd);
+                    fma4(accS[c][0], fv.x * sc, gv);
+                    fma4(accS[c][1], fv.y * sc, gv);
+                    fma4(accS[c][2], fv.z * sc, gv);
+                    fma4(accS[c][3], fv.w * sc, gv);
+                }
             }
         }
         if (tid < R) {
@@ -632,13 +853,20 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
             for (int t = 0; t < TT; ++t) acc += dn_s[t] * w_t[t * RLD + tid];
             accz += acc;
         }
-        __syncthreads();
     }
-    float* part = a.part + (bh * a.nsplit + split) * (long)(2 * D * R + R + 1);
+    float* part = a.part + (bh * a.nsplit + split) * (long)(2 * D * R + R + 4);
 #pragma unroll
-    for (int c = 0; c < NW; ++c) {
-        part[tid + 256 * c] = accW[c];
-        part[D * R + tid + 256 * c] = accS[c];
+    for (int c = 0; c < NB16; ++c) {
+        const int blk = tid + 256 * c;
+        if (blk < Tl::NBLK) {
+            const int bd = blk / (R / 4), br = blk % (R / 4);
+            const int sr = blk / (D / 4), sd = blk % (D / 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                *reinterpret_cast<float4*>(part + (4 * bd + i) * R + 4 * br) = accW[c][i];
+                *reinterpret_cast<float4*>(part + D * R + (4 * sr + i) * D + 4 * sd) = accS[c][i];
+            }
+        }
     }
     if (tid < R) part[2 * D * R + tid] = accz;
     red[tid] = accg;
@@ -655,14 +883,16 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
 // dpk = du phi', dk_lr = W_k dpk; partial sums of dW_k = k^T dpk [D*R].
 template <int D, int R>
 __global__ __launch_bounds__(256) void k_bwd_lr_k(LrBwdArgs a) {
-    constexpr int TT = 32, XLD = D + 1, RLD = R + 1, NW = D * R / 256;
-    __shared__ float w_s[D * R];
-    __shared__ float s_s[R * D];
+    using Tl = LrTile<D, R>;
+    constexpr int TT = Tl::TT, XLD = Tl::XLD, RW = Tl::RW, RLD = Tl::RLD, NB16 = Tl::NB16;
+    __shared__ __attribute__((aligned(16))) float w_s[D * RW];
+    __shared__ __attribute__((aligned(16))) float s_s[R * D];
     __shared__ float z_s[R];
-    __shared__ float x_s[TT * XLD];
-    __shared__ float v_s[TT * XLD];
-    __shared__ float f_t[TT * RLD];
-    __shared__ float d_t[TT * RLD];
+    __shared__ __attribute__((aligned(16))) float x_s[TT * XLD];
+    __shared__ __attribute__((aligned(16))) float v_s[TT * XLD];
+    __shared__ __attribute__((aligned(16))) float u_t[TT * RLD];
+    __shared__ __attribute__((aligned(16))) float f_t[TT * RLD];
+    __shared__ __attribute__((aligned(16))) float d_t[TT * RLD];
     const int tid = threadIdx.x;
     const int split = blockIdx.x;
     const long bh = blockIdx.y;
@@ -671,114 +901,65 @@ __global__ __launch_bounds__(256) void k_bwd_lr_k(LrBwdArgs a) {
     const long t_lo = (long)split * a.chunk;
     const long t_hi = t_lo + a.chunk < L ? t_lo + a.chunk : L;
     const float* dsz = a.dSz + bh * (long)(R * D + R);
-    for (int e = tid; e < D * R; e += 256) w_s[e] = round_bf(a.Wk[(long)head * D * R + e]);
+    for (int e = tid; e < D * R; e += 256) w_s[(e / R) * RW + e % R] = round_bf(a.Wk[(long)head * D * R + e]);
     for (int e = tid; e < R * D; e += 256) s_s[e] = dsz[e];
     for (int e = tid; e < R; e += 256) z_s[e] = dsz[R * D + e];
-    float accW[NW];
+    float4 accW[NB16][4];
 #pragma unroll
-    for (int c = 0; c < NW; ++c) accW[c] = 0.f;
+    for (int c = 0; c < NB16; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accW[c][i] = make_float4(0.f, 0.f, 0.f, 0.f);
     const uint16_t* ks = a.k + bh * L * D;
     const uint16_t* vs = a.v + bh * L * D;
-    __syncthreads();
 
     for (long t0 = t_lo; t0 < t_hi; t0 += TT) {
-        for (int e = tid; e < TT * D / 8; e += 256) {
-            const int t = e / (D / 8), c = e % (D / 8);
+        __syncthreads();
+        lr_load_rows<D, R>(ks, vs, t0, t_hi, x_s, v_s, tid);
+        __syncthreads();
+        lr_features<D, R>(a, x_s, w_s, u_t, f_t, d_t, t0, t_hi, tid);
+        __syncthreads();
+        // dv_lr = dS^T fk per (token, 4 dims)
+        for (int e = tid; e < TT * (D / 4); e += 256) {
+            const int t = e % TT, g = e / TT;
             const long l = t0 + t;
-            u32x4_t xk{0u, 0u, 0u, 0u}, xv{0u, 0u, 0u, 0u};
-            if (l < t_hi) {
-                xk = ldg16(ks + l * D + 8 * c);
-                xv = ldg16(vs + l * D + 8 * c);
-            }
+            const float4 y = vecmat4<R>(f_t + t * RLD, s_s, D, g);
+            if (l < t_hi) *reinterpret_cast<float4*>(a.dv_lr + (bh * L + l) * D + 4 * g) = y;
+        }
+        // dfk = dS v -> rho^T, + dz, * phi'  (d_t becomes dpk)
+        lr_back_features<D, R>(a, v_s, s_s, z_s, nullptr, nullptr, d_t, t0, t_hi, tid);
+        __syncthreads();
+        for (int e = tid; e < TT * (D / 4); e += 256) {
+            const int t = e % TT, g = e / TT;
+            const long l = t0 + t;
+            const float4 y = rowdot4<R>(d_t + t * RLD, w_s, RW, g);
+            if (l < t_hi) *reinterpret_cast<float4*>(a.dk_lr + (bh * L + l) * D + 4 * g) = y;
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x_s[t * XLD + 8 * c + 2 * i] = bf_lo(xk[i]);
-                x_s[t * XLD + 8 * c + 2 * i + 1] = bf_hi(xk[i]);
-                v_s[t * XLD + 8 * c + 2 * i] = bf_lo(xv[i]);
-                v_s[t * XLD + 8 * c + 2 * i + 1] = bf_hi(xv[i]);
+        for (int c = 0; c < NB16; ++c) {
+            const int blk = tid + 256 * c;
+            if (blk < Tl::NBLK) {
+                const int bd = blk / (R / 4), br = blk % (R / 4);
+#pragma unroll 4
+                for (int t = 0; t < TT; ++t) {
+                    const float4 xv = ld4(x_s + t * XLD + 4 * bd), dv = ld4(d_t + t * RLD + 4 * br);
+                    fma4(accW[c][0], xv.x, dv);
+                    fma4(accW[c][1], xv.y, dv);
+                    fma4(accW[c][2], xv.z, dv);
+                    fma4(accW[c][3], xv.w, dv);
+                }
             }
         }
-        __syncthreads();
-        // features, rotated features and phi' (pairs in one thread)
-        for (int e = tid; e < TT * R / 2; e += 256) {
-            const int t = e / (R / 2), pr = e % (R / 2);
-            const long l = t0 + t;
-            float p0 = 0.f, p1 = 0.f;
-#pragma unroll 8
-            for (int d = 0; d < D; ++d) {
-                const float x = x_s[t * XLD + d];
-                p0 += x * w_s[d * R + 2 * pr];
-                p1 += x * w_s[d * R + 2 * pr + 1];
-            }
-            float u0, u1, g0, g1;
-            phi_grad(a.g.fmap, p0, u0, g0);
-            phi_grad(a.g.fmap, p1, u1, g1);
-            float f0 = u0, f1 = u1;
-            if (l < t_hi) {
-                int crd[3];
-                token_coords(l, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
-                const float2 cs = lowrank_cs(a.tab, a.g, pr, crd);
-                f0 = u0 * cs.x - u1 * cs.y;
-                f1 = u0 * cs.y + u1 * cs.x;
-            }
-            f_t[t * RLD + 2 * pr] = f0;
-            f_t[t * RLD + 2 * pr + 1] = f1;
-            d_t[t * RLD + 2 * pr] = g0;
-            d_t[t * RLD + 2 * pr + 1] = g1;
-        }
-        __syncthreads();
-        // dv_lr = dS^T fk
-        for (int e = tid; e < TT * D; e += 256) {
-            const int t = e / D, d = e % D;
-            const long l = t0 + t;
-            if (l < t_hi) {
-                float acc = 0.f;
-                for (int r = 0; r < R; ++r) acc += s_s[r * D + d] * f_t[t * RLD + r];
-                a.dv_lr[(bh * L + l) * D + d] = acc;
-            }
-        }
-        // dfk = dS v, back through the rotation, + dz, times phi'
-        for (int e = tid; e < TT * R / 2; e += 256) {
-            const int t = e / (R / 2), pr = e % (R / 2);
-            const long l = t0 + t;
-            float a0 = 0.f, a1 = 0.f;
-#pragma unroll 8
-            for (int d = 0; d < D; ++d) {
-                const float vv = v_s[t * XLD + d];
-                a0 += s_s[(2 * pr) * D + d] * vv;
-                a1 += s_s[(2 * pr + 1) * D + d] * vv;
-            }
-            if (l < t_hi) {
-                int crd[3];
-                token_coords(l, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
-                rot_t(a0, a1, lowrank_cs(a.tab, a.g, pr, crd));
-            }
-            d_t[t * RLD + 2 * pr] *= a0 + z_s[2 * pr];
-            d_t[t * RLD + 2 * pr + 1] *= a1 + z_s[2 * pr + 1];
-        }
-        __syncthreads();
-        for (int e = tid; e < TT * D; e += 256) {
-            const int t = e / D, d = e % D;
-            const long l = t0 + t;
-            if (l < t_hi) {
-                float acc = 0.f;
-                for (int r = 0; r < R; ++r) acc += w_s[d * R + r] * d_t[t * RLD + r];
-                a.dk_lr[(bh * L + l) * D + d] = acc;
-            }
-        }
-#pragma unroll 1
-        for (int t = 0; t < TT; ++t) {
-#pragma unroll
-            for (int c = 0; c < NW; ++c) {
-                const int e = tid + 256 * c;
-                accW[c] += x_s[t * XLD + e / R] * d_t[t * RLD + e % R];
-            }
-        }
-        __syncthreads();
     }
     float* part = a.part + (bh * a.nsplit + split) * (long)(D * R);
 #pragma unroll
-    for (int c = 0; c < NW; ++c) part[tid + 256 * c] = accW[c];
+    for (int c = 0; c < NB16; ++c) {
+        const int blk = tid + 256 * c;
+        if (blk < Tl::NBLK) {
+            const int bd = blk / (R / 4), br = blk % (R / 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(part + (4 * bd + i) * R + 4 * br) = accW[c][i];
+        }
+    }
 }
 
 __global__ void k_bwd_sum_parts(const float* __restrict__ part, int B, int H, int nsplit, long stride, long off,
@@ -852,9 +1033,9 @@ hipError_t launch_bwd_inverse(const int32_t* idx, long BH, int nblk, int keep, u
 template <int D, int BS>
 static hipError_t bwd_sparse_t(bool dkdv, const BwdArgs& a, hipStream_t st) {
     if (dkdv)
-        hipLaunchKernelGGL((k_bwd_dkdv<D, BS>), dim3((unsigned)a.nwg), dim3(BS * 2), 0, st, a);
+        hipLaunchKernelGGL((k_bwd_dkdv<D, BS>), dim3((unsigned)a.nwg), dim3(BS * 2), 0, st, a, a.inv_off, a.inv_list);
     else
-        hipLaunchKernelGGL((k_bwd_dq<D, BS>), dim3((unsigned)a.nwg), dim3(BS * 2), 0, st, a);
+        hipLaunchKernelGGL((k_bwd_dq<D, BS>), dim3((unsigned)a.nwg), dim3(BS * 2), 0, st, a, a.idx);
     return hipGetLastError();
 }
 

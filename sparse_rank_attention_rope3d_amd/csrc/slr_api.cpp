@@ -205,7 +205,7 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         w.dvlr = take(4ul * d.BH * d.L * d.D);
         int chunk, nsplit;
         lr_bwd_split(d, &chunk, &nsplit);
-        w.lrpart = take(4ul * d.BH * nsplit * (2ul * d.D * R + R + 1));
+        w.lrpart = take(4ul * d.BH * nsplit * (2ul * d.D * R + R + 4));
         w.dsz = take(4ul * d.BH * ((size_t)R * d.D + R));
         w.bits = take(4ul * d.BH * nblk * ((nblk + 31) / 32));
         w.cnt = take(4ul * d.BH * nblk);
@@ -596,7 +596,7 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     lr_bwd_split(d, &la.chunk, &la.nsplit);
     la.dq_lr = at<float>(ws, w.dqlr); la.dk_lr = at<float>(ws, w.dklr); la.dv_lr = at<float>(ws, w.dvlr);
     la.part = at<float>(ws, w.lrpart);
-    const long qstride = 2l * d.D * R + R + 1;
+    const long qstride = 2l * d.D * R + R + 4;   // [dW_q | dS | dz | dg | pad]
     SLR_TRY(launch_bwd_lr((int)d.D, R, false, la, d.BH, s));
     // [dW_q | dS | dz | dg] partials -> dS, dz per slice; dW_q, dg per head
     SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, qstride, d.D * R, (long)R * d.D + R, false,
