@@ -182,6 +182,18 @@ int slr_attention_fwd_staged(const slr_shape *shape, const slr_rope_cfg *rope, c
                              void *ws, size_t ws_bytes, void *const events[5], void *stream);
 
 /*
+ * slr_attention_fwd for a training step: also saves what slr_attention_bwd
+ * needs. idx_out, o_sparse_out (as in slr_attention_fwd) and lse_out are
+ * required: lse_out [B,H,L] fp32 receives, per query row, log2 of the
+ * softmax normaliser over its kept keys, sum_j 2^(s_j) with s_j the row's
+ * scores in log2 units (q.k / sqrt(D) * log2(e)). Same results otherwise.
+ */
+int slr_attention_fwd_train(const slr_shape *shape, const slr_rope_cfg *rope, const slr_sparse_cfg *sparse,
+                            const slr_lowrank_cfg *lowrank, const void *q, const void *k, const void *v, void *out,
+                            int32_t *idx_out, void *o_sparse_out, float *lse_out, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/*
  * Dense softmax attention with 3D RoPE applied inside (RoLA §3 "Full
  * attention"; the baseline the sparse branch is measured against):
  *   out = softmax(R q (R k)^T / sqrt(D)) v  over all L keys.
@@ -202,9 +214,11 @@ int slr_dense_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, co
  *     dO_lowrank = g_h dout;
  *   dgate[h] = sum over b and rows of dout . O_lowrank.
  * The selection is held fixed: idx [B,H,nblk,keep] int32 is the forward's
- * (idx_out of slr_attention_fwd); each row must list distinct blocks in
- * [0, nblk) (entries outside that range are skipped). o_sparse [B,H,L,D] is
- * the forward's O_sparse (o_sparse_out). dout, dq, dk, dv: [B,H,L,D] bf16;
+ * (idx_out of slr_attention_fwd_train); each row must list distinct blocks
+ * in [0, nblk) (entries outside that range are skipped). o_sparse
+ * [B,H,L,D] and lse [B,H,L] fp32 are that call's o_sparse_out and lse_out
+ * (the softmax normalisers are reused, not recomputed), for the same q, k,
+ * v and configuration. dout, dq, dk, dv: [B,H,L,D] bf16;
  * dq, dk, dv must not overlap each other or any input. dWq, dWk: [H,D,r]
  * fp32, dgate: [H] fp32, all overwritten (sums over the batch).
  * Built for bf16 layers with SLR_GATE_HEAD and SLR_LR_ROPE_OUTSIDE (either
@@ -214,8 +228,9 @@ int slr_dense_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, co
  */
 int slr_attention_bwd(const slr_shape *shape, const slr_rope_cfg *rope, const slr_sparse_cfg *sparse,
                       const slr_lowrank_cfg *lowrank, const void *q, const void *k, const void *v,
-                      const int32_t *idx, const void *o_sparse, const void *dout, void *dq, void *dk, void *dv,
-                      float *dWq, float *dWk, float *dgate, void *ws, size_t ws_bytes, void *stream);
+                      const int32_t *idx, const void *o_sparse, const float *lse, const void *dout, void *dq,
+                      void *dk, void *dv, float *dWq, float *dWk, float *dgate, void *ws, size_t ws_bytes,
+                      void *stream);
 
 /* Static text for a status code. */
 const char *slr_status_string(int status);

@@ -121,6 +121,22 @@ def sparse_attention_bwd(qr, kr, v, bs, idx, dO, qblocks: Optional[Sequence[int]
     return {"dq": dq, "dk": dk, "dv": dv}
 
 
+def row_log2_normaliser(qr, kr, bs, idx, qblocks: Optional[Sequence[int]] = None) -> np.ndarray:
+    """log2 of each valid query row's softmax normaliser over its kept key
+    tokens, sum_j exp(q . k_j / sqrt(D)) (the statistic a training forward
+    saves so the backward need not recompute it). Rows of the listed query
+    blocks (all when None), [n_rows]."""
+    qr, kr = _d(qr), _d(kr)
+    L, D = qr.shape
+    out = []
+    for i in (range(idx.shape[0]) if qblocks is None else qblocks):
+        rows = np.arange(i * bs, min((i + 1) * bs, L))
+        s = qr[rows] @ kr[_kept_tokens(idx[i], bs, L)].T / np.sqrt(D)
+        m = s.max(axis=1)
+        out.append((m + np.log(np.exp(s - m[:, None]).sum(axis=1))) / np.log(2.0))
+    return np.concatenate(out) if out else np.zeros(0)
+
+
 def query_blocks_keeping(idx, kblocks) -> np.ndarray:
     """Query blocks whose kept list holds any of ``kblocks`` (ascending)."""
     want = np.zeros(int(idx.max()) + 1 if idx.size else 1, dtype=bool)

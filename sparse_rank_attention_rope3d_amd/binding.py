@@ -26,8 +26,8 @@ SLR_OP_ROPE3D, SLR_OP_SELECT, SLR_OP_LOWRANK_SUMMARY, SLR_OP_ATTENTION, SLR_OP_D
 SLR_OP_ATTENTION_BWD = 5
 
 EXPORTS = ("slr_workspace_bytes", "slr_rope3d", "slr_select_blocks", "slr_lowrank_summary",
-           "slr_attention_fwd", "slr_attention_fwd_staged", "slr_dense_attention_fwd", "slr_attention_bwd",
-           "slr_status_string")
+           "slr_attention_fwd", "slr_attention_fwd_staged", "slr_attention_fwd_train", "slr_dense_attention_fwd",
+           "slr_attention_bwd", "slr_status_string")
 
 
 class SlrShape(ctypes.Structure):
@@ -82,7 +82,8 @@ def lib() -> ctypes.CDLL:
         L.slr_attention_fwd_staged.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg), vp,
                                                vp, vp, vp, vp, vp, vp, vp, sz, P(vp), vp]
         L.slr_dense_attention_fwd.argtypes = [P(SlrShape), P(SlrRopeCfg), vp, vp, vp, vp, vp, sz, vp]
-        L.slr_attention_bwd.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg)] + [vp] * 13 + [sz, vp]
+        L.slr_attention_bwd.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg)] + [vp] * 14 + [sz, vp]
+        L.slr_attention_fwd_train.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg)] + [vp] * 8 + [sz, vp]
         for f in EXPORTS[:-1]:
             getattr(L, f).restype = ctypes.c_int
         L.slr_status_string.argtypes = [ctypes.c_int]
@@ -212,11 +213,31 @@ def slr_attention_fwd(q, k, v, shape: SlrShape, rope: SlrRopeCfg, sparse: SlrSpa
     return (out, idx, o_sp, o_lr) if debug else out
 
 
-def slr_attention_bwd(q, k, v, idx, o_sparse, dout, shape: SlrShape, rope: SlrRopeCfg, sparse: SlrSparseCfg,
+def slr_attention_fwd_train(q, k, v, shape: SlrShape, rope: SlrRopeCfg, sparse: SlrSparseCfg,
+                            lowrank: SlrLowrankCfg, ws: Optional[torch.Tensor] = None, outs=None):
+    """Training forward: returns (out, idx, o_sparse, lse [B, H, L] fp32);
+    ``outs`` may supply those four tensors."""
+    if outs is None:
+        L = shape.T * shape.Hg * shape.Wg
+        nblk = -(-L // sparse.block)
+        out, o_sp = torch.empty_like(q), torch.empty_like(q)
+        idx = torch.empty((shape.B, shape.H, nblk, sparse.keep), dtype=torch.int32, device=q.device)
+        lse = torch.empty((shape.B, shape.H, L), dtype=torch.float32, device=q.device)
+    else:
+        out, idx, o_sp, lse = outs
+    ws = _ws(SLR_OP_ATTENTION, shape, rope, sparse, lowrank, ws, q.device)
+    _check(lib().slr_attention_fwd_train(ctypes.byref(shape), ctypes.byref(rope), ctypes.byref(sparse),
+                                         ctypes.byref(lowrank), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(idx),
+                                         _ptr(o_sp), _ptr(lse), _ptr(ws), ws.numel(), _stream()),
+           "slr_attention_fwd_train")
+    return out, idx, o_sp, lse
+
+
+def slr_attention_bwd(q, k, v, idx, o_sparse, lse, dout, shape: SlrShape, rope: SlrRopeCfg, sparse: SlrSparseCfg,
                       lowrank: SlrLowrankCfg, ws: Optional[torch.Tensor] = None, grads=None):
-    """Backward of slr_attention_fwd given dout (idx and o_sparse saved from
-    the forward). Returns (dq, dk, dv, dWq [H, D, r] fp32, dWk, dgate [H] fp32);
-    ``grads`` may supply those six output tensors."""
+    """Backward of the layer given dout (idx, o_sparse and lse saved by
+    slr_attention_fwd_train). Returns (dq, dk, dv, dWq [H, D, r] fp32, dWk,
+    dgate [H] fp32); ``grads`` may supply those six output tensors."""
     if grads is None:
         dev = q.device
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -228,7 +249,7 @@ def slr_attention_bwd(q, k, v, idx, o_sparse, dout, shape: SlrShape, rope: SlrRo
     ws = _ws(SLR_OP_ATTENTION_BWD, shape, rope, sparse, lowrank, ws, q.device)
     _check(lib().slr_attention_bwd(ctypes.byref(shape), ctypes.byref(rope), ctypes.byref(sparse),
                                    ctypes.byref(lowrank), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(o_sparse),
-                                   _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dWq), _ptr(dWk), _ptr(dg),
+                                   _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dWq), _ptr(dWk), _ptr(dg),
                                    _ptr(ws), ws.numel(), _stream()), "slr_attention_bwd")
     return dq, dk, dv, dWq, dWk, dg
 

@@ -9,10 +9,10 @@
 // query row, P = softmax(q K^T / sqrt(D)) over the kept keys, dP = dO V^T,
 // dS = P (dP - dO . O), dq = dS K / sqrt(D); every kept key receives
 // dk += dS q / sqrt(D) and dv += P dO. Two kernels, no atomics:
-//   k_bwd_dq    one workgroup per query block: a first pass over its kept
-//               tiles gives each row's log-sum-exp, a second forms dS tile by
-//               tile on MFMA (S^T = K Q^T and dP^T = V dO^T, so each lane owns
-//               one query row) and accumulates dQ^T = K^T dS^T;
+//   k_bwd_dq    one workgroup per query block: with each row's log-sum-exp
+//               saved by the forward, it forms dS tile by tile on MFMA
+//               (S^T = K Q^T and dP^T = V dO^T, so each lane owns one query
+//               row) and accumulates dQ^T = K^T dS^T;
 //   k_bwd_dkdv  one workgroup per key block, over the query blocks that keep
 //               it (an inverse of the kept lists, built deterministically from
 //               a bitmap): S = Q K^T and dP = dO V^T with each lane owning one
@@ -78,16 +78,27 @@ struct Stager {
         h = gp & 1;
     }
     __device__ __forceinline__ int row(int e) const { return 16 * G + 4 * h + (e & 3) + 8 * (e >> 2); }
-    __device__ __forceinline__ void fetch(u32x4_t* x, const uint16_t* __restrict__ src, long row0, long limit) const {
-        if (!on) return;
+    // Branch free: a row past `limit` loads row limit - 1 (always in bounds);
+    // bit e of the returned mask marks row e valid, and stash() zeroes the
+    // others (after the loads have landed, so no wait is forced here).
+    __device__ __forceinline__ uint32_t fetch(u32x4_t* x, const uint16_t* __restrict__ src, long row0,
+                                              long limit) const {
+        uint32_t ok = 0;
+        if (!on) return ok;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const long r = row0 + row(e);
-            x[e] = r < limit ? ldg16(src + r * D + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
+            ok |= (r < limit ? 1u : 0u) << e;
+            x[e] = ldg16(src + (r < limit ? r : limit - 1) * D + 8 * c);
         }
+        return ok;
     }
-    __device__ __forceinline__ void stash(const u32x4_t* x, uint16_t* rm, uint16_t* tr) const {
+    __device__ __forceinline__ void stash(u32x4_t* x, uint32_t ok, uint16_t* rm, uint16_t* tr) const {
         if (!on) return;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[e][i] = ((ok >> e) & 1u) ? x[e][i] : 0u;
         if (rm) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4_t*>(rm + row(e) * KLD + 8 * c) = x[e];
@@ -174,7 +185,6 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a, const int32_t* __r
     }
     dl = sum_xor32(dl);
 
-    const float sl2 = a.scale * kLog2e;
     const bool ragged = (L % BS) != 0;
 
     // kept tiles in list order, entries outside [0, nblk) skipped; the list
@@ -190,70 +200,18 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a, const int32_t* __r
     auto tile_at = [&](int n) { return __builtin_amdgcn_readfirstlane(ix[n]); };
     const Stager<D, BS> stg(tid);
     u32x4_t xk[8], xv[8];   // next tile's rows, in flight while the current one is consumed
+    uint32_t okk = 0, okv = 0;
 
-    // ---- pass 1: log-sum-exp of each row over its kept keys (log2 units)
-    float m_run = -INFINITY, l_run = 0.f;
-    int n = next_tile(0);
-    if (n < a.keep) stg.fetch(xk, kr, (long)tile_at(n) * BS, rows);
-    // nothing from the prologue stays in flight into the loop
-    wait_vmcnt<0>();
-    while (n < a.keep) {
-        const int j = tile_at(n);
-        __syncthreads();
-        stg.stash(xk, k_lds, nullptr);
-        __syncthreads();
-        n = next_tile(n + 1);
-        if (n < a.keep) stg.fetch(xk, kr, (long)tile_at(n) * BS, rows);
-        float x[NKB][16];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            f32x16_t sacc;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-            if constexpr (NS == 8) {
-                u32x4_t ak[8];
-                lds_read8x<32, 64>(ak, k_lds + (32 * kb + l32) * KLD + 8 * hf);
-#pragma unroll
-                for (int s = 0; s < 8; ++s) sacc = mfma32(ak[s], qop[s], sacc);
-            } else {
-#pragma unroll
-                for (int s = 0; s < NS; ++s)
-                    sacc = mfma32(*reinterpret_cast<const u32x4_t*>(k_lds + (32 * kb + l32) * KLD + 16 * s + 8 * hf),
-                                  qop[s], sacc);
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const long key = (long)j * BS + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-                x[kb][i] = (ragged && key >= L) ? -INFINITY : sacc[i] * sl2;
-                mx = fmaxf(mx, x[kb][i]);
-            }
-        }
-        const float mn = fmaxf(m_run, mx);
-        if (mn != -INFINITY) {
-            float l = l_run * exp2f(m_run - mn);
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) l += exp2f(x[kb][i] - mn);
-            l_run = l;
-            m_run = mn;
-        }
-    }
-    float lse2;
-    {
-        const float mo = wave_xor32(m_run), lo = wave_xor32(l_run);
-        const float m = fmaxf(m_run, mo);
-        const float l = (m_run == -INFINITY ? 0.f : l_run * exp2f(m_run - m)) +
-                        (mo == -INFINITY ? 0.f : lo * exp2f(mo - m));
-        lse2 = m + log2f(l);
-    }
+    // the forward's log2 normaliser of the row (zero on padded rows, whose
+    // dO and delta are zero); kept for the key-side kernel
+    const float lse2 = qval ? a.lse_in[bh * L + qrow] : 0.f;
     if (hf == 0) {
         a.lse2[bh * rows + qrow] = lse2;
         a.delta[bh * rows + qrow] = qval ? dl : 0.f;
     }
+    int n;
 
-    // ---- pass 2: dS and dQ^T = K^T dS^T
+    // ---- dS and dQ^T = K^T dS^T, tile by tile
     f32x16_t dqacc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -261,20 +219,20 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a, const int32_t* __r
         for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
     n = next_tile(0);
     if (n < a.keep) {
-        stg.fetch(xk, kr, (long)tile_at(n) * BS, rows);
-        stg.fetch(xv, vg, (long)tile_at(n) * BS, L);
+        okk = stg.fetch(xk, kr, (long)tile_at(n) * BS, rows);
+        okv = stg.fetch(xv, vg, (long)tile_at(n) * BS, L);
     }
     wait_vmcnt<0>();
     while (n < a.keep) {
         const int j = tile_at(n);
         __syncthreads();
-        stg.stash(xk, k_lds, kt_lds);
-        stg.stash(xv, v_lds, nullptr);
+        stg.stash(xk, okk, k_lds, kt_lds);
+        stg.stash(xv, okv, v_lds, nullptr);
         __syncthreads();
         n = next_tile(n + 1);
         if (n < a.keep) {
-            stg.fetch(xk, kr, (long)tile_at(n) * BS, rows);
-            stg.fetch(xv, vg, (long)tile_at(n) * BS, L);
+            okk = stg.fetch(xk, kr, (long)tile_at(n) * BS, rows);
+            okv = stg.fetch(xv, vg, (long)tile_at(n) * BS, L);
         }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -302,7 +260,7 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a, const int32_t* __r
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const long key = (long)j * BS + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-                const float p = (ragged && key >= L) ? 0.f : exp2f(sacc[i] * sl2 - lse2);
+                const float p = (ragged && key >= L) ? 0.f : exp2f(sacc[i] * a.qmul - lse2);
                 ds[i] = p * (dpacc[i] - dl);
             }
             u32x4_t dsop[2];
@@ -385,7 +343,6 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dkdv(BwdArgs a, const int32_t* _
             vop[s] = kval ? ldg16(vp + 16 * s) : u32x4_t{0u, 0u, 0u, 0u};
         }
     }
-    const float sl2 = a.scale * kLog2e;
     f32x16_t dkacc[NDB], dvacc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -399,9 +356,10 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dkdv(BwdArgs a, const int32_t* _
     const Stager<D, BS> stg(tid);
     u32x4_t xq[8], xd[8];   // next query block's rows, in flight while the current one is consumed
     float xl = 0.f, xdl = 0.f;
+    uint32_t okq = 0, okd = 0;
     auto fetch = [&](int i) {
-        stg.fetch(xq, qr, (long)i * BS, rows);
-        stg.fetch(xd, dg, (long)i * BS, L);
+        okq = stg.fetch(xq, qr, (long)i * BS, rows);
+        okd = stg.fetch(xd, dg, (long)i * BS, L);
         if (tid < BS) {
             xl = a.lse2[bh * rows + (long)i * BS + tid];
             xdl = a.delta[bh * rows + (long)i * BS + tid];
@@ -412,8 +370,8 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dkdv(BwdArgs a, const int32_t* _
     wait_vmcnt<0>();
     for (int n = n0; n < n1; ++n) {
         __syncthreads();
-        stg.stash(xq, q_lds, qt_lds);
-        stg.stash(xd, do_lds, dot_lds);
+        stg.stash(xq, okq, q_lds, qt_lds);
+        stg.stash(xd, okd, do_lds, dot_lds);
         if (tid < BS) {
             lse_lds[tid] = xl;
             dl_lds[tid] = xdl;
@@ -447,7 +405,7 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dkdv(BwdArgs a, const int32_t* _
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int r = 32 * qs + 8 * (e >> 2) + 4 * hf + (e & 3);
-                p[e] = exp2f(sacc[e] * sl2 - lse_lds[r]);
+                p[e] = exp2f(sacc[e] * a.qmul - lse_lds[r]);
                 ds[e] = p[e] * (dpacc[e] - dl_lds[r]);
             }
             u32x4_t pb[2], dsb[2];
@@ -492,7 +450,7 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dkdv(BwdArgs a, const int32_t* _
             const int d0 = 32 * db + 8 * g4 + 4 * hf;
             float y[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = dkacc[db][4 * g4 + i] * a.scale;
+            for (int i = 0; i < 4; ++i) y[i] = dkacc[db][4 * g4 + i] * a.kscale;
             rot_t(y[0], y[1], rope_cs(a.tab, a.g, d0 >> 1, crd));
             rot_t(y[2], y[3], rope_cs(a.tab, a.g, (d0 >> 1) + 1, crd));
             const float4 kl = *reinterpret_cast<const float4*>(a.dk_lr + ro + d0);

@@ -355,7 +355,11 @@ __global__ __launch_bounds__(BS * 2) void k_flash_bf16(FlashArgs a) {
         __syncthreads();
     }
 
-    flash_epilogue<D, RP, LR>(a, bh, head, (long)qb * BS + 32 * wave, l_run + wave_xor32(l_run), oacc);
+    const float lrow = l_run + wave_xor32(l_run);
+    // training forward: log2 of the row's softmax normaliser over its scaled scores
+    if (a.lse && hf == 0 && (long)qb * BS + 32 * wave + l32 < L)
+        a.lse[bh * L + (long)qb * BS + 32 * wave + l32] = m_run + __log2f(lrow);
+    flash_epilogue<D, RP, LR>(a, bh, head, (long)qb * BS + 32 * wave, lrow, oacc);
 }
 
 
@@ -581,8 +585,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] = oacc[db][i] * f0 + m_lds[(16 * db + i) * 64 + lane] * f1;
-    const float lsum = l_run * f0 + l1 * f1;
-    flash_epilogue<D, RP, LR>(a, bh, head, (long)qb * BS + 32 * rh, sum_xor32(lsum), oacc);
+    const float lsum = sum_xor32(l_run * f0 + l1 * f1);
+    // training forward: log2 of the row's softmax normaliser (q arrives in log2 units)
+    if (a.lse && hf == 0 && (long)qb * BS + 32 * rh + l32 < L)
+        a.lse[bh * L + (long)qb * BS + 32 * rh + l32] = m + __log2f(lsum);
+    flash_epilogue<D, RP, LR>(a, bh, head, (long)qb * BS + 32 * rh, lsum, oacc);
 }
 
 // fp32 layers: one thread per query row, K / V tiles staged in LDS, fp32
@@ -645,6 +652,7 @@ __global__ __launch_bounds__(64) void k_flash_f32(FlashArgs a, int BS) {
     }
     const long qrow = (long)qb * BS + tid;
     if (!act || qrow >= L) return;
+    if (a.lse) a.lse[bh * L + qrow] = (m_run + logf(l_run)) * kLog2e;   // log2 of the normaliser
     const float inv = 1.f / l_run;
     float* out = (float*)a.out + (bh * L + qrow) * D;
     float* osp = a.o_sp ? (float*)a.o_sp + (bh * L + qrow) * D : nullptr;

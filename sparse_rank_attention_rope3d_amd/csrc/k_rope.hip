@@ -251,23 +251,23 @@ hipError_t launch_rope_tables(float2* tab, const RopeGeom& g, double base, hipSt
 template <typename TIO, int D, int BS, bool TWO>
 static hipError_t rope_pool_t(const void* q, const void* k, void* qo, void* ko, float* qbar, float* kbar,
                               const float2* tab, const RopeGeom& g, long BH, long L, long out_rows, int nblk,
-                              hipStream_t st) {
+                              hipStream_t st, float qscale) {
     dim3 grid((unsigned)nblk, (unsigned)BH);
     hipLaunchKernelGGL((k_rope_pool<TIO, D, BS, TWO, false>), grid, dim3(256), 0, st, (const TIO*)q, (const TIO*)k,
                        (TIO*)qo, (TIO*)ko, qbar, kbar, tab, g, L, out_rows, nblk, (const TIO*)nullptr,
-                       (uint16_t*)nullptr, 1.f);
+                       (uint16_t*)nullptr, qscale);
     return hipGetLastError();
 }
 
 template <typename TIO, int D>
 static hipError_t rope_pool_d(const void* q, const void* k, void* qo, void* ko, float* qbar, float* kbar,
                               const float2* tab, const RopeGeom& g, long BH, long L, long out_rows, int bs,
-                              int nblk, hipStream_t st) {
+                              int nblk, hipStream_t st, float qs) {
     if (bs == 32)
-        return k ? rope_pool_t<TIO, D, 32, true>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, nblk, st)
-                 : rope_pool_t<TIO, D, 32, false>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, nblk, st);
-    return k ? rope_pool_t<TIO, D, 64, true>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, nblk, st)
-             : rope_pool_t<TIO, D, 64, false>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, nblk, st);
+        return k ? rope_pool_t<TIO, D, 32, true>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, nblk, st, qs)
+                 : rope_pool_t<TIO, D, 32, false>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, nblk, st, qs);
+    return k ? rope_pool_t<TIO, D, 64, true>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, nblk, st, qs)
+             : rope_pool_t<TIO, D, 64, false>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, nblk, st, qs);
 }
 
 hipError_t launch_rope_pool_tiled(const void* q, const void* k, const void* v, void* qo, uint16_t* kv_tiles,
@@ -282,13 +282,14 @@ hipError_t launch_rope_pool_tiled(const void* q, const void* k, const void* v, v
 
 hipError_t launch_rope_pool(int dtype_bf16, int D, const void* q, const void* k, void* qo, void* ko, float* qbar,
                             float* kbar, const float2* tab, const RopeGeom& g, long BH, long L, long out_rows,
-                            int bs, int nblk, hipStream_t st) {
+                            int bs, int nblk, hipStream_t st, float qs) {
     if (dtype_bf16) {
-        if (D == 64) return rope_pool_d<uint16_t, 64>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
-        return rope_pool_d<uint16_t, 128>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
+        if (D == 64)
+            return rope_pool_d<uint16_t, 64>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st, qs);
+        return rope_pool_d<uint16_t, 128>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st, qs);
     }
-    if (D == 64) return rope_pool_d<float, 64>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
-    return rope_pool_d<float, 128>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st);
+    if (D == 64) return rope_pool_d<float, 64>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st, qs);
+    return rope_pool_d<float, 128>(q, k, qo, ko, qbar, kbar, tab, g, BH, L, out_rows, bs, nblk, st, qs);
 }
 
 }  // namespace slr

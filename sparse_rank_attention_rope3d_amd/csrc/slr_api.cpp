@@ -409,8 +409,8 @@ namespace {
 
 int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
                   const slr_lowrank_cfg* lowrank, const void* q, const void* k, const void* v, void* out,
-                  int32_t* idx_out, void* o_sparse_out, void* o_lowrank_out, void* ws, size_t ws_bytes,
-                  void* const* events, void* stream) {
+                  int32_t* idx_out, void* o_sparse_out, void* o_lowrank_out, float* lse_out, void* ws,
+                  size_t ws_bytes, void* const* events, void* stream) {
     Dims d;
     RopeGeom g;
     LrGeom lg;
@@ -424,6 +424,7 @@ int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sp
     if (idx_out && !aligned(idx_out, 4)) return SLR_EINVAL;
     if ((o_sparse_out && !tensor_ok(o_sparse_out)) || (o_lowrank_out && !tensor_ok(o_lowrank_out)))
         return SLR_EINVAL;
+    if (lse_out && !aligned(lse_out, 4)) return SLR_EINVAL;
     lg.rope = g;
     const int bs = sparse->block;
     Layout w = layout(SLR_OP_ATTENTION, d, g, bs, nblk, sparse->keep, lowrank->rank, RP);
@@ -474,7 +475,7 @@ int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sp
     a.Et = lowrank->Et; a.Eh = lowrank->Eh; a.Ew = lowrank->Ew;
     a.tab = tab;
     a.g = lg;
-    a.out = out; a.o_sp = o_sparse_out; a.o_lr = o_lowrank_out;
+    a.out = out; a.o_sp = o_sparse_out; a.o_lr = o_lowrank_out; a.lse = lse_out;
     a.L = d.L; a.H = (int)d.H; a.nblk = nblk; a.keep = sparse->keep;
     a.scale = (float)(1.0 / std::sqrt((double)d.D));
     a.eps = lowrank->eps;
@@ -491,7 +492,16 @@ int slr_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
                       const slr_lowrank_cfg* lowrank, const void* q, const void* k, const void* v, void* out,
                       int32_t* idx_out, void* o_sparse_out, void* o_lowrank_out, void* ws, size_t ws_bytes,
                       void* stream) {
-    return attention_fwd(shape, rope, sparse, lowrank, q, k, v, out, idx_out, o_sparse_out, o_lowrank_out, ws,
+    return attention_fwd(shape, rope, sparse, lowrank, q, k, v, out, idx_out, o_sparse_out, o_lowrank_out, nullptr,
+                         ws, ws_bytes, nullptr, stream);
+}
+
+int slr_attention_fwd_train(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
+                            const slr_lowrank_cfg* lowrank, const void* q, const void* k, const void* v, void* out,
+                            int32_t* idx_out, void* o_sparse_out, float* lse_out, void* ws, size_t ws_bytes,
+                            void* stream) {
+    if (!idx_out || !o_sparse_out || !lse_out) return SLR_EINVAL;
+    return attention_fwd(shape, rope, sparse, lowrank, q, k, v, out, idx_out, o_sparse_out, nullptr, lse_out, ws,
                          ws_bytes, nullptr, stream);
 }
 
@@ -502,8 +512,8 @@ int slr_attention_fwd_staged(const slr_shape* shape, const slr_rope_cfg* rope, c
     if (!events) return SLR_EINVAL;
     for (int i = 0; i < 5; ++i)
         if (!events[i]) return SLR_EINVAL;
-    return attention_fwd(shape, rope, sparse, lowrank, q, k, v, out, idx_out, o_sparse_out, o_lowrank_out, ws,
-                         ws_bytes, events, stream);
+    return attention_fwd(shape, rope, sparse, lowrank, q, k, v, out, idx_out, o_sparse_out, o_lowrank_out, nullptr,
+                         ws, ws_bytes, events, stream);
 }
 
 int slr_dense_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const void* q, const void* k,
@@ -544,8 +554,8 @@ int slr_dense_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, co
 
 int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
                       const slr_lowrank_cfg* lowrank, const void* q, const void* k, const void* v, const int32_t* idx,
-                      const void* o_sparse, const void* dout, void* dq, void* dk, void* dv, float* dWq, float* dWk,
-                      float* dgate, void* ws, size_t ws_bytes, void* stream) {
+                      const void* o_sparse, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      float* dWq, float* dWk, float* dgate, void* ws, size_t ws_bytes, void* stream) {
     Dims d;
     RopeGeom g;
     LrGeom lg;
@@ -557,6 +567,7 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     if ((st = check_lowrank(lowrank, rope, d, true, &lg, &RP))) return st;
     if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o_sparse) || !tensor_ok(dout)) return SLR_EINVAL;
     if (!tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv) || !idx || !aligned(idx, 4)) return SLR_EINVAL;
+    if (!lse || !aligned(lse, 4)) return SLR_EINVAL;
     if (!dWq || !dWk || !dgate || !aligned(dWq, 4) || !aligned(dWk, 4) || !aligned(dgate, 4)) return SLR_EINVAL;
     {
         const void* outs[3] = {dq, dk, dv};
@@ -580,9 +591,13 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     float* S = at<float>(ws, w.S);
     float* z = at<float>(ws, w.z);
 
+    // q scaled exactly as the forward scored it (pre-scaled into log2 units on
+    // the tiled path), so the saved normalisers match the recomputed scores
+    const bool tiled_fwd = use_tiles(d, bs);
+    const float log2e = 1.4426950408889634f, inv_sqrt_d = (float)(1.0 / std::sqrt((double)d.D));
     SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
     SLR_TRY(launch_rope_pool(1, (int)d.D, q, k, qr, kr, nullptr, nullptr, tab, g, d.BH, d.L, (long)nblk * bs, bs, nblk,
-                             s));
+                             s, tiled_fwd ? tiled_qscale(d.D) : 1.f));
     if ((st = run_summary(d, g, lg, RP, lowrank, k, v, nullptr, 0, ws, w, S, z, false, s))) return st;
 
     // low-rank branch: query side, reductions, key side
@@ -613,7 +628,9 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     a.qr = qr; a.kr = kr; a.v = (const uint16_t*)v; a.o_sp = (const uint16_t*)o_sparse;
     a.dout = (const uint16_t*)dout; a.idx = idx;
     a.inv_off = at<int32_t>(ws, w.off); a.inv_list = at<int32_t>(ws, w.list);
-    a.lse2 = at<float>(ws, w.lse); a.delta = at<float>(ws, w.delta);
+    a.lse_in = lse; a.lse2 = at<float>(ws, w.lse); a.delta = at<float>(ws, w.delta);
+    a.qmul = tiled_fwd ? 1.f : log2e * inv_sqrt_d;
+    a.kscale = tiled_fwd ? 0.6931471805599453f : inv_sqrt_d;
     a.dq_lr = la.dq_lr; a.dk_lr = la.dk_lr; a.dv_lr = la.dv_lr;
     a.dq = (uint16_t*)dq; a.dk = (uint16_t*)dk; a.dv = (uint16_t*)dv;
     a.tab = tab; a.g = g; a.L = d.L; a.nblk = nblk; a.keep = keep;

@@ -40,6 +40,8 @@ struct FlashArgs {
     void* out;               // [BH][L][D]
     void* o_sp;              // optional debug outputs, same layout
     void* o_lr;
+    float* lse;              // optional [BH][L]: log2 of each row's softmax normaliser over its
+                             // scores in log2 units (training forward)
     long L;
     int H, nblk, keep;
     float scale;             // 1/sqrt(D)
@@ -50,7 +52,7 @@ struct FlashArgs {
 hipError_t launch_rope_tables(float2* tab, const RopeGeom& g, double base, hipStream_t st);
 hipError_t launch_rope_pool(int dtype_bf16, int D, const void* q, const void* k, void* qo, void* ko, float* qbar,
                             float* kbar, const float2* tab, const RopeGeom& g, long BH, long L, long out_rows,
-                            int bs, int nblk, hipStream_t st);
+                            int bs, int nblk, hipStream_t st, float qscale = 1.f);
 // Tiled K / V^T layout of the block-sparse flash kernel (bf16, D = 128, 64-token blocks).
 constexpr int kTileElems = 2 * 64 * 128;
 // qscale multiplies the rotated q copy (the flash kernel's scores then come
@@ -89,7 +91,11 @@ struct BwdArgs {
     const int32_t* idx;        // [BH][nblk][keep] kept key blocks per query block
     const int32_t* inv_off;    // [BH][nblk + 1] query-block list offsets per key block
     const int32_t* inv_list;   // [BH][nblk * keep] query blocks keeping each key block, ascending
-    float* lse2;               // [BH][nblk*BS] log2 of each row's softmax normaliser (log2 units)
+    const float* lse_in;       // [BH][L] the forward's log2 normalisers
+    float* lse2;               // [BH][nblk*BS] the same, zero on padded rows
+    float qmul;                // score (log2 units) = qmul * (q_rot . k_rot): log2(e)/sqrt(D), or 1
+                               // when q_rot already carries that factor
+    float kscale;              // dk_rot = kscale * sum dS q_rot: 1/sqrt(D), or ln 2 for scaled q
     float* delta;              // [BH][nblk*BS] dO . O_sparse per row
     const float* dq_lr;        // [BH][L][D] low-rank parts of the gradients (fp32)
     const float* dk_lr;

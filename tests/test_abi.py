@@ -178,11 +178,11 @@ def test_other_entry_points_validate():
 
 
 def _bwd(shape, rope, sparse, lr, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, idx=FAKE + 0x3000, osp=FAKE + 0x4000,
-         dout=FAKE + 0x5000, dq=FAKE + 0x6000, dk=FAKE + 0x7000, dv=FAKE + 0x8000, dwq=FAKE + 0x9000,
-         dwk=FAKE + 0xa000, dg=FAKE + 0xb000, ws=None, ws_bytes=0):
+         lse=FAKE + 0xc000, dout=FAKE + 0x5000, dq=FAKE + 0x6000, dk=FAKE + 0x7000, dv=FAKE + 0x8000,
+         dwq=FAKE + 0x9000, dwk=FAKE + 0xa000, dg=FAKE + 0xb000, ws=None, ws_bytes=0):
     r = ctypes.byref
-    return B.lib().slr_attention_bwd(r(shape), r(rope), r(sparse), r(lr), q, k, v, idx, osp, dout, dq, dk, dv, dwq,
-                                     dwk, dg, ws, ws_bytes, None)
+    return B.lib().slr_attention_bwd(r(shape), r(rope), r(sparse), r(lr), q, k, v, idx, osp, lse, dout, dq, dk, dv,
+                                     dwq, dwk, dg, ws, ws_bytes, None)
 
 
 def test_backward_validates_before_launching():
@@ -193,7 +193,7 @@ def test_backward_validates_before_launching():
     assert need > (2 * 2 + 3 * 4) * layer.B * layer.H * layer.L * layer.D
     assert _bwd(shape, rope, sparse, lr) == B.SLR_EWORKSPACE
     assert _bwd(shape, rope, sparse, lr, ws=FAKE, ws_bytes=need - 1) == B.SLR_EWORKSPACE
-    for bad in ("q", "osp", "dout", "dq", "dv", "dwq", "dg"):
+    for bad in ("q", "osp", "lse", "dout", "dq", "dv", "dwq", "dg"):
         assert _bwd(shape, rope, sparse, lr, **{bad: None}) == B.SLR_EINVAL, bad
     assert _bwd(shape, rope, sparse, lr, idx=FAKE + 2) == B.SLR_EINVAL
     assert _bwd(shape, rope, sparse, lr, dk=MISALIGNED) == B.SLR_EINVAL
@@ -217,3 +217,18 @@ def test_backward_unsupported_settings(change):
     assert B.lib().slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, r(shape), r(rope), r(sparse), r(lr),
                                        r(n)) == B.SLR_EUNSUPPORTED
     assert _bwd(shape, rope, sparse, lr, ws=FAKE, ws_bytes=1 << 40) == B.SLR_EUNSUPPORTED
+
+
+def test_training_forward_requires_its_outputs():
+    shape, rope, sparse, lr = _cfgs()
+    r = ctypes.byref
+    L = B.lib()
+
+    def call(idx=FAKE + 0x1000, osp=FAKE + 0x2000, lse=FAKE + 0x3000):
+        return L.slr_attention_fwd_train(r(shape), r(rope), r(sparse), r(lr), FAKE, FAKE, FAKE, FAKE + 0x4000, idx,
+                                         osp, lse, None, 0, None)
+    assert call() == B.SLR_EWORKSPACE
+    assert call(idx=None) == B.SLR_EINVAL
+    assert call(osp=None) == B.SLR_EINVAL
+    assert call(lse=None) == B.SLR_EINVAL
+    assert call(lse=FAKE + 2) == B.SLR_EINVAL

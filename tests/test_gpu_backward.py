@@ -1,8 +1,10 @@
 """GPU parity of the layer backward (slr_attention_bwd) with the oracle's.
 
-The GPU forward supplies the selection (checked to be a valid top-k) and
-its O_sparse, as a training step would; the oracle recomputes its own O in
-float64 on the same selection. Bar (bf16 layers): relative Frobenius error
+The GPU training forward (slr_attention_fwd_train) supplies the selection
+(checked to be a valid top-k), its O_sparse and the rows' log2 softmax
+normalisers, as a training step would; the oracle recomputes its own in
+float64 on the same selection (the saved normalisers are checked against
+it to 3e-2 absolute, in log2 units). Bar (bf16 layers): relative Frobenius error
 <= 1e-2 and max-abs error <= 3e-2 x max |reference| for dq, dk, dv, dW_q,
 dW_k and the gate gradient. (The gradients are ~0.05 RMS, so the forward's
 absolute 3e-2 is stated relative to the gradient's own scale.)
@@ -47,10 +49,10 @@ def _run_gpu(cfg):
     dout = _dout(cfg)
     shape, rope, sparse = B.shape_of(cfg), B.rope_of(cfg), B.sparse_of(cfg)
     lowrank = B.lowrank_of(cfg, inp.params)
-    _, idx, o_sp, _ = B.slr_attention_fwd(inp.q, inp.k, inp.v, shape, rope, sparse, lowrank, debug=True)
-    grads = B.slr_attention_bwd(inp.q, inp.k, inp.v, idx, o_sp, dout, shape, rope, sparse, lowrank)
+    _, idx, o_sp, lse = B.slr_attention_fwd_train(inp.q, inp.k, inp.v, shape, rope, sparse, lowrank)
+    grads = B.slr_attention_bwd(inp.q, inp.k, inp.v, idx, o_sp, lse, dout, shape, rope, sparse, lowrank)
     torch.cuda.synchronize()
-    return inp, idx, grads
+    return inp, idx, grads, lse
 
 
 def _oracle_slice(cfg, inp, b, h, ig, qblocks=None, kblocks=None):
@@ -73,6 +75,7 @@ def _oracle_slice(cfg, inp, b, h, ig, qblocks=None, kblocks=None):
         "dk": OB.rope3d_transpose(spk["dk"], grid, cfg.base, cfg.pairs) + lr["dk"],
         "dv": spk["dv"] + lr["dv"],
         "dWq": lr["dWq"], "dWk": lr["dWk"], "dg": float((ds * lr["o_lr"]).sum()),
+        "q_rot": qr, "k_rot": kr,
     }
     return ref
 
@@ -86,7 +89,7 @@ def _rows(cfg, blocks):
 
 def _check(cfg, slices=None, qsample=None, ksample=None, heads=None):
     T.log(f"  case {cfg.name}: L={cfg.L} nblk={cfg.nblk} keep={cfg.keep} D={cfg.D} r={cfg.rank} fmap={cfg.fmap}")
-    inp, idx, (dq, dk, dv, dWq, dWk, dg) = _run_gpu(cfg)
+    inp, idx, (dq, dk, dv, dWq, dWk, dg), lse = _run_gpu(cfg)
     slices = slices or [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
     heads = sorted({h for _, h in slices}) if heads is None else heads
     got = {"dq": [], "dk": [], "dv": []}
@@ -101,6 +104,12 @@ def _check(cfg, slices=None, qsample=None, ksample=None, heads=None):
         ref = _oracle_slice(cfg, inp, b, h, ig, qb, kb)
         dW[b, h] = ref
         if (b, h) in slices:
+            # the normaliser the training forward saved: log2 units, abs error
+            got_l = T.to_host(lse[b, h])[_rows(cfg, qb)]
+            want_l = OB.row_log2_normaliser(ref["q_rot"], ref["k_rot"], cfg.block, ig, qb)
+            err = float(np.abs(got_l - want_l).max())
+            T.log(f"    lse[{b},{h}]: max_abs={err:.3e}")
+            assert err <= 3e-2, f"saved log2 normaliser off by {err:.3e}"
             rq, rk = _rows(cfg, qb), _rows(cfg, kb)
             for name, t, rows in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rk)):
                 got[name].append(T.to_host(t[b, h])[rows])
@@ -144,7 +153,7 @@ def test_backward_wan13b_sampled():
 
 def test_backward_is_deterministic():
     cfg = dataclasses.replace(synth.wan13b(), name="bwd determinism", B=1, H=2, T=4, Hg=9, Wg=13, keep=3)
-    _, _, g1 = _run_gpu(cfg)
-    _, _, g2 = _run_gpu(cfg)
+    _, _, g1, _ = _run_gpu(cfg)
+    _, _, g2, _ = _run_gpu(cfg)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)

@@ -171,3 +171,19 @@ def test_key_sampled_gradient_equals_full():
         rows = slice(j * cfg.block, (j + 1) * cfg.block)
         np.testing.assert_allclose(part["dk"][rows], full["dk"][rows], rtol=1e-12, atol=1e-14)
         np.testing.assert_allclose(part["dv"][rows], full["dv"][rows], rtol=1e-12, atol=1e-14)
+
+
+def test_row_normaliser_matches_torch_logsumexp():
+    """Every block kept: the saved normaliser is torch's logsumexp of the
+    scaled scores, in base 2; with one block kept it covers that block only."""
+    cfg = _cfg(T=3, Hg=5, Wg=7, keep=4)
+    q, k, v, _, _, _, _, _ = _inputs(cfg)
+    grid = (cfg.T, cfg.Hg, cfg.Wg)
+    qr = oracle.rope3d(q, grid, cfg.base, cfg.pairs)
+    kr = oracle.rope3d(k, grid, cfg.base, cfg.pairs)
+    idx = np.tile(np.arange(cfg.nblk, dtype=np.int32), (cfg.nblk, 1))
+    want = torch.logsumexp(torch.tensor(qr @ kr.T / np.sqrt(cfg.D)), dim=1).numpy() / np.log(2.0)
+    np.testing.assert_allclose(OB.row_log2_normaliser(qr, kr, cfg.block, idx), want, rtol=1e-12, atol=1e-12)
+    one = np.array([[2]] * cfg.nblk, dtype=np.int32)
+    want1 = torch.logsumexp(torch.tensor(qr @ kr[64:96].T / np.sqrt(cfg.D)), dim=1).numpy() / np.log(2.0)
+    np.testing.assert_allclose(OB.row_log2_normaliser(qr, kr, cfg.block, one), want1, rtol=1e-12, atol=1e-12)
