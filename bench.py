@@ -226,6 +226,8 @@ def main() -> int:
     ap.add_argument("--fmap", default="elu1", choices=["elu1", "silu"],
                     help="low-rank feature map: elu + 1 (the workloads' default) or SiLU")
     ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--bwd-reps", type=int, default=3,
+                    help="timed calls of the layer backward (training forward saves idx, O_sparse, lse); 0 skips")
     ap.add_argument("--cpu-blocks", type=int, default=512, help="query blocks the CPU oracle samples")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", metavar="JSONL", default=None,
@@ -340,6 +342,46 @@ def main() -> int:
                  "speedup_of_slr_layer": round(dms / ms_step, 2)}
         del wsd
 
+    # layer backward (bf16, per-head gate, rotary low-rank): the training
+    # forward saves the selection, O_sparse and the row normalisers once, then
+    # the backward is timed on a seeded N(0, 1) output gradient
+    backward = None
+    if args.bwd_reps > 0 and cfg.dtype == "bf16" and cfg.gate == "head" and cfg.lr_mode == "rola":
+        print("[bench] layer backward", file=sys.stderr, flush=True)
+        gen = torch.Generator(device="cuda").manual_seed(1234)
+        dout = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        saved = B.slr_attention_fwd_train(q, k, v, shape, rope, sparse, lowrank, ws=ws)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.bwd_reps):
+            B.slr_attention_fwd_train(q, k, v, shape, rope, sparse, lowrank, ws=ws, outs=saved)
+        e1.record()
+        torch.cuda.synchronize()
+        fwd_train_ms = e0.elapsed_time(e1) / args.bwd_reps
+        _, idx_s, osp_s, lse_s = saved
+        wsb = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lowrank), "cuda")
+        grads = B.slr_attention_bwd(q, k, v, idx_s, osp_s, lse_s, dout, shape, rope, sparse, lowrank, ws=wsb)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.bwd_reps):
+            B.slr_attention_bwd(q, k, v, idx_s, osp_s, lse_s, dout, shape, rope, sparse, lowrank, ws=wsb,
+                                grads=grads)
+        e1.record()
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / args.bwd_reps
+        # algorithmic: S recomputed once, dP, dV, dK, dQ = 5 products of the
+        # forward's 2 over the kept tiles; low-rank: 11 (D x r) products per token
+        f_bsp = 2.5 * F["sparse"]
+        f_blr = 22.0 * cfg.B * cfg.H * cfg.L * cfg.D * cfg.rank
+        btf = (f_bsp + f_blr) / (bms * 1e-3) / 1e12
+        backward = {"ms": round(bms, 3), "TFLOP/s (algorithmic)": round(btf, 1),
+                    "frac_bf16_peak": round(btf / PEAK_BF16_TFLOPS, 4),
+                    "algorithmic_flops": {"sparse": f_bsp, "lowrank": f_blr},
+                    "training_forward_ms": round(fwd_train_ms, 3),
+                    "training_step_ms": round(fwd_train_ms + bms, 3)}
+        del wsb, grads, saved, dout
+
     print("[bench] achievable GEMM and copy rates", file=sys.stderr, flush=True)
     ach = achievable_peaks(torch)
     for d in hbm.values():
@@ -382,6 +424,7 @@ def main() -> int:
         "hbm_stages": hbm,
         "select": {"TFLOP/s": round(sel_tf, 2), "frac_fp32_peak": round(sel_tf / PEAK_FP32_TFLOPS, 4)},
         "dense_flash": dense,
+        "backward": backward,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
