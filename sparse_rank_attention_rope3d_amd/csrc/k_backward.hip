@@ -25,6 +25,7 @@
 // tiles, split along L with fixed-order reductions of the partial sums.
 #include "slr_common.h"
 #include "slr_launch.h"
+#include "slr_backward.h"
 
 namespace slr {
 

@@ -13,6 +13,7 @@
 
 #include "../../include/slr.h"
 #include "slr_launch.h"
+#include "slr_backward.h"
 
 using namespace slr;
 

@@ -79,63 +79,4 @@ hipError_t launch_lr_reduce(const float* part, long BH, int nsplit, int D, int R
 hipError_t launch_flash(int dtype_bf16, int D, int BS, int RP, int lr_mode, bool dense, const FlashArgs& a,
                         long BH, hipStream_t st);
 
-// ---- backward pass (bf16 layers) -----------------------------------------
-
-// Sparse branch: softmax attention over the kept blocks, differentiated.
-struct BwdArgs {
-    const uint16_t* qr;        // [BH][nblk*BS][D] rotated q, zero rows past L (unscaled)
-    const uint16_t* kr;        // same layout, rotated k
-    const uint16_t* v;         // [BH][L][D]
-    const uint16_t* o_sp;      // [BH][L][D] the forward's sparse-branch output
-    const uint16_t* dout;      // [BH][L][D] gradient of the layer output
-    const int32_t* idx;        // [BH][nblk][keep] kept key blocks per query block
-    const int32_t* inv_off;    // [BH][nblk + 1] query-block list offsets per key block
-    const int32_t* inv_list;   // [BH][nblk * keep] query blocks keeping each key block, ascending
-    const float* lse_in;       // [BH][L] the forward's log2 normalisers
-    float* lse2;               // [BH][nblk*BS] the same, zero on padded rows
-    float qmul;                // score (log2 units) = qmul * (q_rot . k_rot): log2(e)/sqrt(D), or 1
-                               // when q_rot already carries that factor
-    float kscale;              // dk_rot = kscale * sum dS q_rot: 1/sqrt(D), or ln 2 for scaled q
-    float* delta;              // [BH][nblk*BS] dO . O_sparse per row
-    const float* dq_lr;        // [BH][L][D] low-rank parts of the gradients (fp32)
-    const float* dk_lr;
-    const float* dv_lr;
-    uint16_t* dq;              // [BH][L][D] outputs
-    uint16_t* dk;
-    uint16_t* dv;
-    const float2* tab;         // rotary (cos, sin) tables
-    RopeGeom g;
-    long L;
-    int nblk, keep;
-    float scale;               // 1/sqrt(D)
-    long nwg;
-};
-
-// Low-rank branch (per-head gate): gradients of O_lr given g_h dout.
-struct LrBwdArgs {
-    const uint16_t *q, *k, *v, *dout;   // [BH][L][D]
-    const float *Wq, *Wk;               // [H][D][R] (used rounded to bf16)
-    const float *S, *z;                 // [BH][R][D], [BH][R] the forward summary
-    const float* gate;                  // [H]
-    const float* dSz;                   // [BH][R*D + R] reduced dS, dz (key side input)
-    const float2* tab;
-    LrGeom g;
-    float eps;
-    long L;
-    int H, chunk, nsplit;
-    float *dq_lr, *dk_lr, *dv_lr;       // [BH][L][D]
-    float* part;                        // split partials
-};
-
-hipError_t launch_bwd_lr(int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st);
-// out[o][e] = sum over (b < nb, split < nsplit) of part[((b*H + h)*nsplit + split)*stride + off + e]:
-// per_head sums the batches into [H][n], else [BH][n] (nb = 1, h = slice).
-hipError_t launch_bwd_sum_parts(const float* part, int B, int H, int nsplit, long stride, long off, long n,
-                                bool per_head, float* out, hipStream_t st);
-// Inverse of the kept-block lists, deterministic: bits [BH][nblk][ceil(nblk/32)] scratch.
-hipError_t launch_bwd_inverse(const int32_t* idx, long BH, int nblk, int keep, uint32_t* bits, int32_t* cnt,
-                              int32_t* off, int32_t* list, hipStream_t st);
-hipError_t launch_bwd_dq(int D, int BS, const BwdArgs& a, hipStream_t st);
-hipError_t launch_bwd_dkdv(int D, int BS, const BwdArgs& a, hipStream_t st);
-
 }  // namespace slr
