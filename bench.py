@@ -34,8 +34,8 @@ PEAK_HBM_GBS = 8000.0
 # on, identified by the sha256 of its files; any other source reports null.
 FLASH_TRAFFIC_SOURCES = ["k_flash.hip", "slr_common.h", "slr_launch.h"]
 FLASH_TRAFFIC = {
-    "sha256": "c2d64d2f22adf32bfa111ac87bf2a18c59c0fc5dd9097bd54552eb734236de18",
-    "bytes_per_launch": {"wan13b": 8257.7e6 + 201.3e6, "wan14b": 224431.4e6 + 1548.9e6},
+    "sha256": "521af05705e58f31b89a6e02bff7a4fba5cd17a8ec1ece9018d1572b5306cab9",
+    "bytes_per_launch": {"wan13b": 8188.6e6 + 201.3e6, "wan14b": 218470.1e6 + 1548.4e6},
 }
 
 
