@@ -209,9 +209,9 @@ int slr_dense_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, co
  *     of (R q).(R k) / sqrt(D), dP = dout V^T, dS = P (dP - dout . O_sparse);
  *     dq += R^T (dS K_rot) / sqrt(D), dk += R^T (dS^T Q_rot) / sqrt(D),
  *     dv += P^T dout, with R^T the transpose of the 3D RoPE;
- *   low-rank branch (RoLA §4.1-4.3, App. A): the chain rule through
- *     phi(x W), the rotation after phi, S, z and the normaliser, with
- *     dO_lowrank = g_h dout;
+ *   low-rank branch (RoLA §4.1-4.3, App. A; RoPeSLR abstract): the chain
+ *     rule through phi(x W [+ E]), the rotation after phi (rotary variant),
+ *     S, z and the normaliser, with dO_lowrank = g_h dout;
  *   dgate[h] = sum over b and rows of dout . O_lowrank.
  * The selection is held fixed: idx [B,H,nblk,keep] int32 is the forward's
  * (idx_out of slr_attention_fwd_train); each row must list distinct blocks
@@ -221,7 +221,10 @@ int slr_dense_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, co
  * v and configuration. dout, dq, dk, dv: [B,H,L,D] bf16;
  * dq, dk, dv must not overlap each other or any input. dWq, dWk: [H,D,r]
  * fp32, dgate: [H] fp32, all overwritten (sums over the batch).
- * Built for bf16 layers with SLR_GATE_HEAD and SLR_LR_ROPE_OUTSIDE (either
+ * SLR_LR_ABS_PE layers also get the tables' gradients dEt [T,r], dEh [Hg,r],
+ * dEw [Wg,r] fp32 (overwritten; sums over batch, heads and tokens; required,
+ * 4-byte aligned); for SLR_LR_ROPE_OUTSIDE they are ignored (may be NULL).
+ * Built for bf16 layers with SLR_GATE_HEAD (either low-rank variant, either
  * feature map); other settings return SLR_EUNSUPPORTED. Workspace:
  * slr_workspace_bytes(SLR_OP_ATTENTION_BWD, ...). Results are bitwise
  * reproducible (fixed reduction orders, no floating-point atomics).
@@ -229,8 +232,8 @@ int slr_dense_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, co
 int slr_attention_bwd(const slr_shape *shape, const slr_rope_cfg *rope, const slr_sparse_cfg *sparse,
                       const slr_lowrank_cfg *lowrank, const void *q, const void *k, const void *v,
                       const int32_t *idx, const void *o_sparse, const float *lse, const void *dout, void *dq,
-                      void *dk, void *dv, float *dWq, float *dWk, float *dgate, void *ws, size_t ws_bytes,
-                      void *stream);
+                      void *dk, void *dv, float *dWq, float *dWk, float *dgate, float *dEt, float *dEh,
+                      float *dEw, void *ws, size_t ws_bytes, void *stream);
 
 /* Static text for a status code. */
 const char *slr_status_string(int status);

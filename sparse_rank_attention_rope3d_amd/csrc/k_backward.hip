@@ -640,7 +640,20 @@ __device__ __forceinline__ void lr_features(const LrBwdArgs& a, const float* x, 
     using Tl = LrTile<D, R>;
     for (int e = tid; e < Tl::TT * (R / 4); e += 256) {
         const int t = e % Tl::TT, g = e / Tl::TT;
-        const float4 p = vecmat4<D>(x + t * Tl::XLD, w_s, Tl::RW, g);
+        float4 p = vecmat4<D>(x + t * Tl::XLD, w_s, Tl::RW, g);
+        const long l = t0 + t;
+        int crd[3] = {0, 0, 0};
+        if (l < t_hi) token_coords(l, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
+        if (a.abspe && l < t_hi) {
+            // absolute PE: E_t[t] + E_h[h] + E_w[w] added before phi (tables only 4-byte aligned)
+            const float* et = a.Et + crd[0] * R + 4 * g;
+            const float* eh = a.Eh + crd[1] * R + 4 * g;
+            const float* ew = a.Ew + crd[2] * R + 4 * g;
+            p.x += et[0] + eh[0] + ew[0];
+            p.y += et[1] + eh[1] + ew[1];
+            p.z += et[2] + eh[2] + ew[2];
+            p.w += et[3] + eh[3] + ew[3];
+        }
         float f[4], df[4];
         phi_grad(a.g.fmap, p.x, f[0], df[0]);
         phi_grad(a.g.fmap, p.y, f[1], df[1]);
@@ -648,11 +661,8 @@ __device__ __forceinline__ void lr_features(const LrBwdArgs& a, const float* x, 
         phi_grad(a.g.fmap, p.w, f[3], df[3]);
         *reinterpret_cast<float4*>(wt + t * Tl::RLD + 4 * g) = make_float4(f[0], f[1], f[2], f[3]);
         *reinterpret_cast<float4*>(dt + t * Tl::RLD + 4 * g) = make_float4(df[0], df[1], df[2], df[3]);
-        // rotation after phi of the two pairs (4g, 4g+1), (4g+2, 4g+3)
-        const long l = t0 + t;
-        if (l < t_hi) {
-            int crd[3];
-            token_coords(l, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
+        // rotation after phi of the two pairs (4g, 4g+1), (4g+2, 4g+3) (rotary variant)
+        if (!a.abspe && l < t_hi) {
 #pragma unroll
             for (int q2 = 0; q2 < 2; ++q2) {
                 const float2 cs = lowrank_cs(a.tab, a.g, 2 * g + q2, crd);
@@ -688,7 +698,7 @@ __device__ __forceinline__ void lr_back_features(const LrBwdArgs& a, const float
         a0 *= sc;
         a1 *= sc;
         const long l = t0 + t;
-        if (l < t_hi) {
+        if (!a.abspe && l < t_hi) {
             int crd[3];
             token_coords(l, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
             rot_t(a0, a1, lowrank_cs(a.tab, a.g, pr, crd));
@@ -777,6 +787,13 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
         // dfq = S (g dout) / n -> rho^T, + dn z, * phi'  (d_t becomes dpq)
         lr_back_features<D, R>(a, g_s, s_s, z_s, sc_s, dn_s, d_t, t0, t_hi, tid);
         __syncthreads();
+        if (a.abspe) {
+            // gradient w.r.t. q W_q + E of each valid token (the E tables' share)
+            for (int e = tid; e < TT * R; e += 256) {
+                const int t = e / R, r = e % R;
+                if (t0 + t < t_hi) a.dpre[(bh * L + t0 + t) * R + r] = d_t[t * RLD + r];
+            }
+        }
         // dq_lr = W_q dpq per (token, 4 dims)
         for (int e = tid; e < TT * (D / 4); e += 256) {
             const int t = e % TT, g = e / TT;
@@ -887,6 +904,13 @@ __global__ __launch_bounds__(256) void k_bwd_lr_k(LrBwdArgs a) {
         // dfk = dS v -> rho^T, + dz, * phi'  (d_t becomes dpk)
         lr_back_features<D, R>(a, v_s, s_s, z_s, nullptr, nullptr, d_t, t0, t_hi, tid);
         __syncthreads();
+        if (a.abspe) {
+            // adds the key side's share (the query side wrote its own first)
+            for (int e = tid; e < TT * R; e += 256) {
+                const int t = e / R, r = e % R;
+                if (t0 + t < t_hi) a.dpre[(bh * L + t0 + t) * R + r] += d_t[t * RLD + r];
+            }
+        }
         for (int e = tid; e < TT * (D / 4); e += 256) {
             const int t = e % TT, g = e / TT;
             const long l = t0 + t;
@@ -918,6 +942,37 @@ __global__ __launch_bounds__(256) void k_bwd_lr_k(LrBwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(part + (4 * bd + i) * R + 4 * br) = accW[c][i];
         }
+    }
+}
+
+// Per-axis sums for the absolute-PE tables: workgroup (c, bh) adds dpre over
+// the tokens of slice bh whose coordinate on `axis` is c, in a fixed order
+// (thread (j, r) takes every (256/R)-th such token from j, then the j's are
+// added in order).
+__global__ __launch_bounds__(256) void k_bwd_e_sum(const float* __restrict__ dpre, long L, int Hg, int Wg, int axis,
+                                                   int R, float* __restrict__ part) {
+    __shared__ float red[256];
+    const int c = blockIdx.x;
+    const long bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int step = 256 / R, r = tid % R, j0 = tid / R;
+    const long HW = (long)Hg * Wg;
+    const long n = axis == 0 ? HW : (axis == 1 ? L / HW * Wg : L / HW * Hg);
+    const float* src = dpre + bh * L * R;
+    float acc = 0.f;
+    for (long k = j0; k < n; k += step) {
+        long l;
+        if (axis == 0) l = (long)c * HW + k;
+        else if (axis == 1) l = (k / Wg) * HW + (long)c * Wg + k % Wg;
+        else l = k * Wg + c;
+        acc += src[l * R + r];
+    }
+    red[tid] = acc;
+    __syncthreads();
+    if (tid < R) {
+        float s = 0.f;
+        for (int j = 0; j < step; ++j) s += red[j * R + tid];
+        part[(bh * gridDim.x + c) * R + tid] = s;
     }
 }
 
@@ -973,6 +1028,13 @@ hipError_t launch_bwd_sum_parts(const float* part, int B, int H, int nsplit, lon
     const long nout = (per_head ? (long)H : (long)B * H) * n;
     hipLaunchKernelGGL(k_bwd_sum_parts, dim3(grid_for(nout)), dim3(256), 0, st, part, B, H, nsplit, stride, off, n,
                        per_head ? 1 : 0, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_e_sum(const float* dpre, long BH, long L, int T, int Hg, int Wg, int axis, int R, float* part,
+                            hipStream_t st) {
+    const int n = axis == 0 ? T : (axis == 1 ? Hg : Wg);
+    hipLaunchKernelGGL(k_bwd_e_sum, dim3((unsigned)n, (unsigned)BH), dim3(256), 0, st, dpre, L, Hg, Wg, axis, R, part);
     return hipGetLastError();
 }
 

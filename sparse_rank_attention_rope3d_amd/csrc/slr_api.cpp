@@ -144,10 +144,10 @@ void summary_split(const Dims& d, int slots, int* chunk, int* nsplit) {
     *nsplit = (int)best_n;
 }
 
-// The backward is built for bf16 layers with the per-head gate and the
-// rotary low-rank variant.
+// The backward is built for bf16 layers with the per-head gate (either
+// low-rank variant, either feature map).
 int check_bwd_supported(const Dims& d, const slr_lowrank_cfg* lr) {
-    if (!d.bf16 || lr->gate_mode != SLR_GATE_HEAD || lr->mode != SLR_LR_ROPE_OUTSIDE) return SLR_EUNSUPPORTED;
+    if (!d.bf16 || lr->gate_mode != SLR_GATE_HEAD) return SLR_EUNSUPPORTED;
     return SLR_OK;
 }
 
@@ -155,7 +155,7 @@ int check_bwd_supported(const Dims& d, const slr_lowrank_cfg* lr) {
 struct Layout {
     size_t tab, qr, kr, kvt, qbar, kbar, scores, idx, wqt, wkt, part, S, z, sthi, stlo, zp, total;
     // backward
-    size_t lse, delta, dqlr, dklr, dvlr, lrpart, dsz, bits, cnt, off, list;
+    size_t lse, delta, dqlr, dklr, dvlr, lrpart, dsz, bits, cnt, off, list, dpre, epart;
     bool tiled;
 };
 
@@ -175,7 +175,8 @@ void lr_bwd_split(const Dims& d, int* chunk, int* nsplit) {
     *nsplit = (int)((d.L + c - 1) / c);
 }
 
-Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int keep, int R, int RP) {
+Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int keep, int R, int RP,
+              bool abspe = false) {
     Layout w;
     std::memset(&w, 0, sizeof(w));
     size_t off = 0;
@@ -208,6 +209,12 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         lr_bwd_split(d, &chunk, &nsplit);
         w.lrpart = take(4ul * d.BH * nsplit * (2ul * d.D * R + R + 4));
         w.dsz = take(4ul * d.BH * ((size_t)R * d.D + R));
+        if (abspe) {
+            // per-token gradient of x W + E and the per-slice axis sums of it
+            w.dpre = take(4ul * d.BH * d.L * R);
+            const int na = d.T > d.Hg ? (d.T > d.Wg ? d.T : d.Wg) : (d.Hg > d.Wg ? d.Hg : d.Wg);
+            w.epart = take(4ul * d.BH * na * R);
+        }
         w.bits = take(4ul * d.BH * nblk * ((nblk + 31) / 32));
         w.cnt = take(4ul * d.BH * nblk);
         w.off = take(4ul * d.BH * (nblk + 1));
@@ -312,7 +319,7 @@ int slr_workspace_bytes(int op, const slr_shape* shape, const slr_rope_cfg* rope
         R = lowrank->rank;
     }
     if (op == SLR_OP_ATTENTION_BWD && (st = check_bwd_supported(d, lowrank))) return st;
-    *bytes = layout(op, d, g, bs, nblk, keep, R, RP).total;
+    *bytes = layout(op, d, g, bs, nblk, keep, R, RP, lowrank && lowrank->mode == SLR_LR_ABS_PE).total;
     return SLR_OK;
 }
 
@@ -556,7 +563,8 @@ int slr_dense_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, co
 int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
                       const slr_lowrank_cfg* lowrank, const void* q, const void* k, const void* v, const int32_t* idx,
                       const void* o_sparse, const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                      float* dWq, float* dWk, float* dgate, void* ws, size_t ws_bytes, void* stream) {
+                      float* dWq, float* dWk, float* dgate, float* dEt, float* dEh, float* dEw, void* ws,
+                      size_t ws_bytes, void* stream) {
     Dims d;
     RopeGeom g;
     LrGeom lg;
@@ -570,6 +578,9 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     if (!tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv) || !idx || !aligned(idx, 4)) return SLR_EINVAL;
     if (!lse || !aligned(lse, 4)) return SLR_EINVAL;
     if (!dWq || !dWk || !dgate || !aligned(dWq, 4) || !aligned(dWk, 4) || !aligned(dgate, 4)) return SLR_EINVAL;
+    const bool abspe = lowrank->mode == SLR_LR_ABS_PE;
+    if (abspe && (!dEt || !dEh || !dEw || !aligned(dEt, 4) || !aligned(dEh, 4) || !aligned(dEw, 4)))
+        return SLR_EINVAL;
     {
         const void* outs[3] = {dq, dk, dv};
         const void* ins[5] = {q, k, v, o_sparse, dout};
@@ -583,7 +594,7 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     if ((st = check_bwd_supported(d, lowrank))) return st;
     lg.rope = g;
     const int bs = sparse->block, keep = sparse->keep, R = lowrank->rank;
-    Layout w = layout(SLR_OP_ATTENTION_BWD, d, g, bs, nblk, keep, R, RP);
+    Layout w = layout(SLR_OP_ATTENTION_BWD, d, g, bs, nblk, keep, R, RP, abspe);
     if ((st = check_ws(ws, ws_bytes, w.total))) return st;
     hipStream_t s = (hipStream_t)stream;
     float2* tab = at<float2>(ws, w.tab);
@@ -612,6 +623,9 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     lr_bwd_split(d, &la.chunk, &la.nsplit);
     la.dq_lr = at<float>(ws, w.dqlr); la.dk_lr = at<float>(ws, w.dklr); la.dv_lr = at<float>(ws, w.dvlr);
     la.part = at<float>(ws, w.lrpart);
+    la.abspe = abspe ? 1 : 0;
+    la.Et = lowrank->Et; la.Eh = lowrank->Eh; la.Ew = lowrank->Ew;
+    la.dpre = abspe ? at<float>(ws, w.dpre) : nullptr;
     const long qstride = 2l * d.D * R + R + 4;   // [dW_q | dS | dz | dg | pad]
     SLR_TRY(launch_bwd_lr((int)d.D, R, false, la, d.BH, s));
     // [dW_q | dS | dz | dg] partials -> dS, dz per slice; dW_q, dg per head
@@ -622,6 +636,16 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
                                  s));
     SLR_TRY(launch_bwd_lr((int)d.D, R, true, la, d.BH, s));
     SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, d.D * R, 0, d.D * R, true, dWk, s));
+    if (abspe) {
+        // E tables: per-axis sums of the per-token gradient, per slice, then over the slices
+        float* ep = at<float>(ws, w.epart);
+        const int na[3] = {d.T, d.Hg, d.Wg};
+        float* outs[3] = {dEt, dEh, dEw};
+        for (int ax = 0; ax < 3; ++ax) {
+            SLR_TRY(launch_bwd_e_sum(la.dpre, d.BH, d.L, d.T, d.Hg, d.Wg, ax, R, ep, s));
+            SLR_TRY(launch_bwd_sum_parts(ep, (int)d.BH, 1, 1, (long)na[ax] * R, 0, (long)na[ax] * R, true, outs[ax], s));
+        }
+    }
 
     // sparse branch: dQ (and the row statistics), the inverse lists, dK and dV
     BwdArgs a;

@@ -51,6 +51,9 @@ struct LrBwdArgs {
     int H, chunk, nsplit;
     float *dq_lr, *dk_lr, *dv_lr;       // [BH][L][D]
     float* part;                        // split partials
+    int abspe;                          // absolute-PE variant: E added before phi, no rotation
+    const float *Et, *Eh, *Ew;          // [T|Hg|Wg][R] (absolute PE)
+    float* dpre;                        // absolute PE: [BH][L][R] gradient w.r.t. x W + E (q side + k side)
 };
 
 hipError_t launch_bwd_lr(int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st);
@@ -58,6 +61,10 @@ hipError_t launch_bwd_lr(int D, int R, bool key_side, const LrBwdArgs& a, long B
 // per_head sums the batches into [H][n], else [BH][n] (nb = 1, h = slice).
 hipError_t launch_bwd_sum_parts(const float* part, int B, int H, int nsplit, long stride, long off, long n,
                                 bool per_head, float* out, hipStream_t st);
+// Absolute PE: part[bh][c][r] = sum over the tokens l of slice bh with coordinate c on `axis`
+// (0 = t, 1 = h, 2 = w) of dpre[bh][l][r]; grid (axis length, BH).
+hipError_t launch_bwd_e_sum(const float* dpre, long BH, long L, int T, int Hg, int Wg, int axis, int R, float* part,
+                            hipStream_t st);
 // Inverse of the kept-block lists, deterministic: bits [BH][nblk][ceil(nblk/32)] scratch.
 hipError_t launch_bwd_inverse(const int32_t* idx, long BH, int nblk, int keep, uint32_t* bits, int32_t* cnt,
                               int32_t* off, int32_t* list, hipStream_t st);

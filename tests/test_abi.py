@@ -179,10 +179,11 @@ def test_other_entry_points_validate():
 
 def _bwd(shape, rope, sparse, lr, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, idx=FAKE + 0x3000, osp=FAKE + 0x4000,
          lse=FAKE + 0xc000, dout=FAKE + 0x5000, dq=FAKE + 0x6000, dk=FAKE + 0x7000, dv=FAKE + 0x8000,
-         dwq=FAKE + 0x9000, dwk=FAKE + 0xa000, dg=FAKE + 0xb000, ws=None, ws_bytes=0):
+         dwq=FAKE + 0x9000, dwk=FAKE + 0xa000, dg=FAKE + 0xb000, det=FAKE + 0xd000, deh=FAKE + 0xe000,
+         dew=FAKE + 0xf000, ws=None, ws_bytes=0):
     r = ctypes.byref
     return B.lib().slr_attention_bwd(r(shape), r(rope), r(sparse), r(lr), q, k, v, idx, osp, lse, dout, dq, dk, dv,
-                                     dwq, dwk, dg, ws, ws_bytes, None)
+                                     dwq, dwk, dg, det, deh, dew, ws, ws_bytes, None)
 
 
 def test_backward_validates_before_launching():
@@ -203,15 +204,29 @@ def test_backward_validates_before_launching():
     assert _bwd(shape, rope, sparse, lr, dk=FAKE + 0x6000) == B.SLR_EINVAL
 
 
-@pytest.mark.parametrize("change", ["f32", "token_gate", "abspe"])
+def test_backward_absolute_pe_needs_the_table_gradients():
+    shape, rope, sparse, lr = _cfgs()
+    lr.mode, lr.Et, lr.Eh, lr.Ew = B.SLR_LR_ABS_PE, FAKE, FAKE, FAKE
+    n_abs = B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lr)
+    layer = synth.wan13b()
+    # the per-token gradient of x W + E [BH, L, r] fp32 comes on top
+    assert n_abs >= 4 * layer.B * layer.H * layer.L * layer.rank
+    assert _bwd(shape, rope, sparse, lr) == B.SLR_EWORKSPACE
+    for bad in ("det", "deh", "dew"):
+        assert _bwd(shape, rope, sparse, lr, **{bad: None}) == B.SLR_EINVAL, bad
+    assert _bwd(shape, rope, sparse, lr, dew=FAKE + 2) == B.SLR_EINVAL
+    # the rotary variant ignores them
+    shape, rope, sparse, lr = _cfgs()
+    assert _bwd(shape, rope, sparse, lr, det=None, deh=None, dew=None) == B.SLR_EWORKSPACE
+
+
+@pytest.mark.parametrize("change", ["f32", "token_gate"])
 def test_backward_unsupported_settings(change):
     shape, rope, sparse, lr = _cfgs()
     if change == "f32":
         shape.dtype = B.SLR_F32
-    elif change == "token_gate":
-        lr.gate_mode, lr.gate, lr.Wg, lr.bg = B.SLR_GATE_TOKEN, None, FAKE, FAKE
     else:
-        lr.mode, lr.Et, lr.Eh, lr.Ew = B.SLR_LR_ABS_PE, FAKE, FAKE, FAKE
+        lr.gate_mode, lr.gate, lr.Wg, lr.bg = B.SLR_GATE_TOKEN, None, FAKE, FAKE
     n = ctypes.c_size_t()
     r = ctypes.byref
     assert B.lib().slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, r(shape), r(rope), r(sparse), r(lr),

@@ -55,16 +55,28 @@ def _run_gpu(cfg):
     return inp, idx, grads, lse
 
 
+def _tables(cfg, p):
+    return (p["et"], p["eh"], p["ew"]) if cfg.lr_mode == "abspe" else None
+
+
+def _oracle_lowrank(cfg, inp, b, h):
+    qs, ks, vs = synth.qkv_slice(cfg, b, h)
+    ds = np.asarray(synth.dout_slice(cfg, b, h), np.float64)
+    p = inp.params_np
+    return OB.lowrank_bwd(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], float(p["gate"][h]) * ds, E=_tables(cfg, p))
+
+
 def _oracle_slice(cfg, inp, b, h, ig, qblocks=None, kblocks=None):
     """dq rows of qblocks and dk, dv rows of kblocks (all rows when None)."""
     qs, ks, vs = synth.qkv_slice(cfg, b, h)
     ds = np.asarray(synth.dout_slice(cfg, b, h), np.float64)
     p = inp.params_np
     grid = (cfg.T, cfg.Hg, cfg.Wg)
-    res = oracle.layer_slice(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], p["gate"][h], qblocks=[0], idx=ig)
+    res = oracle.layer_slice(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], p["gate"][h], E=_tables(cfg, p), qblocks=[0],
+                             idx=ig)
     T.check_selection(ig, res["scores"], res["thr"], cfg.keep)
     qr, kr = res["q_rot"], res["k_rot"]
-    lr = OB.lowrank_bwd(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], float(p["gate"][h]) * ds)
+    lr = _oracle_lowrank(cfg, inp, b, h)
     spq = OB.sparse_attention_bwd(qr, kr, vs, cfg.block, ig, ds, qblocks=qblocks)
     if kblocks is None:
         spk = spq
@@ -75,7 +87,7 @@ def _oracle_slice(cfg, inp, b, h, ig, qblocks=None, kblocks=None):
         "dk": OB.rope3d_transpose(spk["dk"], grid, cfg.base, cfg.pairs) + lr["dk"],
         "dv": spk["dv"] + lr["dv"],
         "dWq": lr["dWq"], "dWk": lr["dWk"], "dg": float((ds * lr["o_lr"]).sum()),
-        "q_rot": qr, "k_rot": kr,
+        "q_rot": qr, "k_rot": kr, "dE": lr.get("dE"),
     }
     return ref
 
@@ -89,7 +101,7 @@ def _rows(cfg, blocks):
 
 def _check(cfg, slices=None, qsample=None, ksample=None, heads=None):
     T.log(f"  case {cfg.name}: L={cfg.L} nblk={cfg.nblk} keep={cfg.keep} D={cfg.D} r={cfg.rank} fmap={cfg.fmap}")
-    inp, idx, (dq, dk, dv, dWq, dWk, dg), lse = _run_gpu(cfg)
+    inp, idx, (dq, dk, dv, dWq, dWk, dg, dE), lse = _run_gpu(cfg)
     slices = slices or [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
     heads = sorted({h for _, h in slices}) if heads is None else heads
     got = {"dq": [], "dk": [], "dv": []}
@@ -116,6 +128,16 @@ def _check(cfg, slices=None, qsample=None, ksample=None, heads=None):
                 want[name].append(ref[name][rows])
     for name in ("dq", "dk", "dv"):
         _close(name, np.concatenate(got[name]), np.concatenate(want[name]))
+    if cfg.lr_mode == "abspe":
+        # the tables are shared by every slice: their gradient sums over all of them
+        want_e = [np.zeros((n, cfg.rank)) for n in (cfg.T, cfg.Hg, cfg.Wg)]
+        for b in range(cfg.B):
+            for h in range(cfg.H):
+                de = dW[b, h]["dE"] if (b, h) in dW else _oracle_lowrank(cfg, inp, b, h)["dE"]
+                for i in range(3):
+                    want_e[i] += de[i]
+        for i, name in enumerate(("dEt", "dEh", "dEw")):
+            _close(name, T.to_host(dE[i]), want_e[i])
     for h in heads:
         _close(f"dWq[{h}]", T.to_host(dWq[h]), sum(dW[b, h]["dWq"] for b in range(cfg.B)))
         _close(f"dWk[{h}]", T.to_host(dWk[h]), sum(dW[b, h]["dWk"] for b in range(cfg.B)))
@@ -133,6 +155,9 @@ SMALL = [
     ("D64 block32", dict(B=1, H=2, D=64, pairs=(12, 10, 10), T=3, Hg=10, Wg=11, block=32, keep=4, rank=16,
                          lr_pairs=(4, 2, 2))),
     ("D128 block32 one block", dict(B=1, H=1, T=1, Hg=3, Wg=7, block=32, keep=1)),
+    ("absolute PE", dict(B=2, H=2, T=4, Hg=9, Wg=13, keep=3, lr_mode="abspe", lr_pairs=(0, 0, 0))),
+    ("absolute PE silu D64 block32", dict(B=1, H=2, D=64, pairs=(12, 10, 10), T=3, Hg=10, Wg=11, block=32, keep=4,
+                                          rank=16, lr_mode="abspe", lr_pairs=(0, 0, 0), fmap="silu")),
 ]
 
 
@@ -151,9 +176,16 @@ def test_backward_wan13b_sampled():
     _check(cfg, slices=[(0, 0), (1, 7)], qsample=4, ksample=4)
 
 
+def test_backward_hunyuan13b_sampled():
+    """Full HunyuanVideo-13B shape (absolute-PE low-rank variant): sampled
+    rows of two slices as above; the E tables' gradients over all slices."""
+    cfg = synth.hunyuan13b()
+    _check(cfg, slices=[(0, 0), (0, 11)], qsample=3, ksample=2)
+
+
 def test_backward_is_deterministic():
     cfg = dataclasses.replace(synth.wan13b(), name="bwd determinism", B=1, H=2, T=4, Hg=9, Wg=13, keep=3)
     _, _, g1, _ = _run_gpu(cfg)
     _, _, g2, _ = _run_gpu(cfg)
-    for a, b in zip(g1, g2):
+    for a, b in zip(g1[:6], g2[:6]):
         assert torch.equal(a, b)
