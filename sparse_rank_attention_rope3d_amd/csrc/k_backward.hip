@@ -1,4 +1,4 @@
-// Backward pass of the hybrid layer (bf16 layers, per-head gate).
+// Backward pass of the hybrid layer (per-head gate; bf16 on MFMA, fp32 on VALU).
 //
 // The pages fine-tune this layer (RoLA, arXiv 2609.06712v3, §4.4 and
 // App. E.2: the low-rank projections and the gate are trained), so its
@@ -466,6 +466,182 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dkdv(BwdArgs a, const int32_t* _
 }
 
 // ---------------------------------------------------------------------------
+// fp32 layers: the same two kernels in fp32 VALU (the precision the tiny fp32
+// check layer asks for). Thread (row, c) owns the 32 dims 32c .. 32c+31 of one
+// row (NC = D/32 threads per row); a row's dot products add the NC partial
+// sums with lane swaps. Key (dq) or query (dk, dv) rows of a block are staged
+// in LDS as fp32.
+template <int NC>
+__device__ __forceinline__ float sum_lanes(float x) {
+    x += __shfl_xor(x, 1, 64);
+    if (NC == 4) x += __shfl_xor(x, 2, 64);
+    return x;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_dq_f32(BwdArgs a, const int32_t* __restrict__ idx_all, int BS) {
+    constexpr int NC = D / 32;
+    __shared__ float k_s[64 * (D + 1)];
+    __shared__ float v_s[64 * (D + 1)];
+    const int tid = threadIdx.x, row = tid / NC, c = tid % NC;
+    const long wid = xcd_remap(blockIdx.x, a.nwg);
+    const long bh = wid / a.nblk;
+    const int qb = (int)(wid % a.nblk);
+    const long rows = (long)a.nblk * BS;
+    const long L = a.L;
+    const bool act = row < BS;
+    const long qrow = (long)qb * BS + (act ? row : 0);
+    const bool qval = act && qrow < L;
+    const float* qr = (const float*)(const void*)a.qr + bh * rows * D;
+    const float* kr = (const float*)(const void*)a.kr + bh * rows * D;
+    const float* vg = (const float*)(const void*)a.v + bh * L * D;
+    const float* dg = (const float*)(const void*)a.dout + bh * L * D;
+    const float* og = (const float*)(const void*)a.o_sp + bh * L * D;
+    const int32_t* ix = idx_all + (bh * a.nblk + qb) * (long)a.keep;
+    float q[32], g[32], acc[32];
+    float dl = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const int d = 32 * c + i;
+        q[i] = qr[qrow * D + d];
+        g[i] = qval ? dg[qrow * D + d] : 0.f;
+        dl += qval ? g[i] * og[qrow * D + d] : 0.f;
+        acc[i] = 0.f;
+    }
+    dl = sum_lanes<NC>(dl);
+    const float lse2 = qval ? a.lse_in[bh * L + qrow] : 0.f;
+    if (act && c == 0) {
+        a.lse2[bh * rows + qrow] = lse2;
+        a.delta[bh * rows + qrow] = qval ? dl : 0.f;
+    }
+    for (int n = 0; n < a.keep; ++n) {
+        const int j = ix[n];
+        if (j < 0 || j >= a.nblk) continue;
+        __syncthreads();
+        for (int e = tid; e < BS * D; e += 256) {
+            const int r = e / D, d = e % D;
+            const long key = (long)j * BS + r;
+            k_s[r * (D + 1) + d] = kr[key * D + d];
+            v_s[r * (D + 1) + d] = key < L ? vg[key * D + d] : 0.f;
+        }
+        __syncthreads();
+        for (int r = 0; r < BS; ++r) {
+            if ((long)j * BS + r >= L) break;
+            const float* kk = k_s + r * (D + 1) + 32 * c;
+            const float* vv = v_s + r * (D + 1) + 32 * c;
+            float s = 0.f, dp = 0.f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                s += q[i] * kk[i];
+                dp += g[i] * vv[i];
+            }
+            s = sum_lanes<NC>(s);
+            dp = sum_lanes<NC>(dp);
+            const float ds = exp2f(s * a.qmul - lse2) * (dp - dl);
+#pragma unroll
+            for (int i = 0; i < 32; ++i) acc[i] += ds * kk[i];
+        }
+    }
+    if (!qval) return;
+    int crd[3];
+    token_coords(qrow, a.g.Hg, a.g.Wg, crd[0], crd[1], crd[2]);
+    float* out = (float*)(void*)a.dq + (bh * L + qrow) * D;
+    const float* lr = a.dq_lr + (bh * L + qrow) * D;
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) {
+        const int d = 32 * c + i;
+        float y0 = acc[i] * a.scale, y1 = acc[i + 1] * a.scale;
+        rot_t(y0, y1, rope_cs(a.tab, a.g, d >> 1, crd));
+        out[d] = y0 + lr[d];
+        out[d + 1] = y1 + lr[d + 1];
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_dkdv_f32(BwdArgs a, const int32_t* __restrict__ inv_off,
+                                                      const int32_t* __restrict__ inv_list, int BS) {
+    constexpr int NC = D / 32;
+    __shared__ float q_s[64 * (D + 1)];
+    __shared__ float g_s[64 * (D + 1)];
+    __shared__ float lse_s[64], dl_s[64];
+    const int tid = threadIdx.x, row = tid / NC, c = tid % NC;
+    const long wid = xcd_remap(blockIdx.x, a.nwg);
+    const long bh = wid / a.nblk;
+    const int jb = (int)(wid % a.nblk);
+    const long rows = (long)a.nblk * BS;
+    const long L = a.L;
+    const bool act = row < BS;
+    const long key = (long)jb * BS + (act ? row : 0);
+    const bool kval = act && key < L;
+    const float* qr = (const float*)(const void*)a.qr + bh * rows * D;
+    const float* kr = (const float*)(const void*)a.kr + bh * rows * D;
+    const float* vg = (const float*)(const void*)a.v + bh * L * D;
+    const float* dg = (const float*)(const void*)a.dout + bh * L * D;
+    float k[32], v[32], dk[32], dv[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const int d = 32 * c + i;
+        k[i] = kr[key * D + d];
+        v[i] = kval ? vg[key * D + d] : 0.f;
+        dk[i] = 0.f;
+        dv[i] = 0.f;
+    }
+    const int32_t* off = inv_off + bh * (long)(a.nblk + 1);
+    const int32_t* list = inv_list + bh * (long)a.nblk * a.keep;
+    for (int n = off[jb]; n < off[jb + 1]; ++n) {
+        const int ib = list[n];
+        __syncthreads();
+        for (int e = tid; e < BS * D; e += 256) {
+            const int r = e / D, d = e % D;
+            const long qrow = (long)ib * BS + r;
+            q_s[r * (D + 1) + d] = qr[qrow * D + d];
+            g_s[r * (D + 1) + d] = qrow < L ? dg[qrow * D + d] : 0.f;
+        }
+        if (tid < BS) {
+            lse_s[tid] = a.lse2[bh * rows + (long)ib * BS + tid];
+            dl_s[tid] = a.delta[bh * rows + (long)ib * BS + tid];
+        }
+        __syncthreads();
+        for (int r = 0; r < BS; ++r) {
+            if ((long)ib * BS + r >= L) break;
+            const float* qq = q_s + r * (D + 1) + 32 * c;
+            const float* gg = g_s + r * (D + 1) + 32 * c;
+            float s = 0.f, dp = 0.f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                s += qq[i] * k[i];
+                dp += gg[i] * v[i];
+            }
+            s = sum_lanes<NC>(s);
+            dp = sum_lanes<NC>(dp);
+            const float p = exp2f(s * a.qmul - lse_s[r]);
+            const float ds = p * (dp - dl_s[r]);
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                dv[i] += p * gg[i];
+                dk[i] += ds * qq[i];
+            }
+        }
+    }
+    if (!kval) return;
+    int crd[3];
+    token_coords(key, a.g.Hg, a.g.Wg, crd[0], crd[1], crd[2]);
+    const long ro = (bh * L + key) * D;
+    float* dko = (float*)(void*)a.dk + ro;
+    float* dvo = (float*)(void*)a.dv + ro;
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) {
+        const int d = 32 * c + i;
+        float y0 = dk[i] * a.kscale, y1 = dk[i + 1] * a.kscale;
+        rot_t(y0, y1, rope_cs(a.tab, a.g, d >> 1, crd));
+        dko[d] = y0 + a.dk_lr[ro + d];
+        dko[d + 1] = y1 + a.dk_lr[ro + d + 1];
+        dvo[d] = dv[i] + a.dv_lr[ro + d];
+        dvo[d + 1] = dv[i + 1] + a.dv_lr[ro + d + 1];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Inverse of the kept lists: for each key block, the query blocks that keep
 // it, ascending. A bitmap [BH][key block][query-block bits] is set with
 // atomic ORs (the result does not depend on their order), counted, scanned
@@ -610,25 +786,39 @@ __device__ __forceinline__ float4 vecmat4(const float* vrow, const float* M, int
     return acc;
 }
 
-// Load TT token rows of two bf16 [L][D] inputs into fp32 LDS tiles (zeros past t_hi).
-template <int D, int R>
-__device__ __forceinline__ void lr_load_rows(const uint16_t* a_src, const uint16_t* b_src, long t0, long t_hi,
-                                             float* xa, float* xb, int tid) {
+// Load TT token rows of two [L][D] inputs (bf16 when BF, else fp32) into fp32
+// LDS tiles (zeros past t_hi).
+template <int D, int R, bool BF>
+__device__ __forceinline__ void lr_load_rows(const void* a_src, const void* b_src, long t0, long t_hi, float* xa,
+                                             float* xb, int tid) {
     using Tl = LrTile<D, R>;
     for (int e = tid; e < Tl::TT * D / 8; e += 256) {
         const int t = e / (D / 8), c = e % (D / 8);
         const long l = t0 + t;
-        u32x4_t ua{0u, 0u, 0u, 0u}, ub{0u, 0u, 0u, 0u};
-        if (l < t_hi) {
-            ua = ldg16(a_src + l * D + 8 * c);
-            ub = ldg16(b_src + l * D + 8 * c);
-        }
         float* pa = xa + t * Tl::XLD + 8 * c;
         float* pb = xb + t * Tl::XLD + 8 * c;
-        *reinterpret_cast<float4*>(pa) = make_float4(bf_lo(ua[0]), bf_hi(ua[0]), bf_lo(ua[1]), bf_hi(ua[1]));
-        *reinterpret_cast<float4*>(pa + 4) = make_float4(bf_lo(ua[2]), bf_hi(ua[2]), bf_lo(ua[3]), bf_hi(ua[3]));
-        *reinterpret_cast<float4*>(pb) = make_float4(bf_lo(ub[0]), bf_hi(ub[0]), bf_lo(ub[1]), bf_hi(ub[1]));
-        *reinterpret_cast<float4*>(pb + 4) = make_float4(bf_lo(ub[2]), bf_hi(ub[2]), bf_lo(ub[3]), bf_hi(ub[3]));
+        if constexpr (BF) {
+            u32x4_t ua{0u, 0u, 0u, 0u}, ub{0u, 0u, 0u, 0u};
+            if (l < t_hi) {
+                ua = ldg16((const uint16_t*)a_src + l * D + 8 * c);
+                ub = ldg16((const uint16_t*)b_src + l * D + 8 * c);
+            }
+            *reinterpret_cast<float4*>(pa) = make_float4(bf_lo(ua[0]), bf_hi(ua[0]), bf_lo(ua[1]), bf_hi(ua[1]));
+            *reinterpret_cast<float4*>(pa + 4) = make_float4(bf_lo(ua[2]), bf_hi(ua[2]), bf_lo(ua[3]), bf_hi(ua[3]));
+            *reinterpret_cast<float4*>(pb) = make_float4(bf_lo(ub[0]), bf_hi(ub[0]), bf_lo(ub[1]), bf_hi(ub[1]));
+            *reinterpret_cast<float4*>(pb + 4) = make_float4(bf_lo(ub[2]), bf_hi(ub[2]), bf_lo(ub[3]), bf_hi(ub[3]));
+        } else {
+            float4 z = make_float4(0.f, 0.f, 0.f, 0.f), a0 = z, a1 = z, b0 = z, b1 = z;
+            if (l < t_hi) {
+                const float* fa = (const float*)a_src + l * D + 8 * c;
+                const float* fb = (const float*)b_src + l * D + 8 * c;
+                a0 = ld4(fa); a1 = ld4(fa + 4); b0 = ld4(fb); b1 = ld4(fb + 4);
+            }
+            *reinterpret_cast<float4*>(pa) = a0;
+            *reinterpret_cast<float4*>(pa + 4) = a1;
+            *reinterpret_cast<float4*>(pb) = b0;
+            *reinterpret_cast<float4*>(pb + 4) = b1;
+        }
     }
 }
 
@@ -716,7 +906,7 @@ __device__ __forceinline__ void lr_back_features(const LrBwdArgs& a, const float
 //   dz = dn w and dg = dout . O over the workgroup's tokens.
 // Partial layout per (slice, split): [dW_q D*R | dS R*D | dz R | dg 1 | pad 3]
 // (a stride of 2DR + R + 4 floats keeps every block 16-byte aligned).
-template <int D, int R>
+template <int D, int R, bool BF>
 __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
     using Tl = LrTile<D, R>;
     constexpr int TT = Tl::TT, XLD = Tl::XLD, RW = Tl::RW, RLD = Tl::RLD, NB16 = Tl::NB16;
@@ -740,7 +930,10 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
     const long t_hi = t_lo + a.chunk < L ? t_lo + a.chunk : L;
     const float gh = a.gate[head];
     const bool silu = a.g.fmap != 0;
-    for (int e = tid; e < D * R; e += 256) w_s[(e / R) * RW + e % R] = round_bf(a.Wq[(long)head * D * R + e]);
+    for (int e = tid; e < D * R; e += 256) {
+        const float x = a.Wq[(long)head * D * R + e];
+        w_s[(e / R) * RW + e % R] = BF ? round_bf(x) : x;
+    }
     for (int e = tid; e < R * D; e += 256) s_s[e] = a.S[bh * R * D + e];
     for (int e = tid; e < R; e += 256) z_s[e] = a.z[bh * R + e];
     float4 accW[NB16][4], accS[NB16][4];
@@ -752,12 +945,13 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
             accS[c][i] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
     float accz = 0.f, accg = 0.f;
-    const uint16_t* qs = a.q + bh * L * D;
-    const uint16_t* gs = a.dout + bh * L * D;
+    const size_t es = BF ? 2 : 4;
+    const void* qs = (const char*)(const void*)a.q + bh * L * D * es;
+    const void* gs = (const char*)(const void*)a.dout + bh * L * D * es;
 
     for (long t0 = t_lo; t0 < t_hi; t0 += TT) {
         __syncthreads();
-        lr_load_rows<D, R>(qs, gs, t0, t_hi, x_s, g_s, tid);
+        lr_load_rows<D, R, BF>(qs, gs, t0, t_hi, x_s, g_s, tid);
         __syncthreads();
         lr_features<D, R>(a, x_s, w_s, w_t, f_t, d_t, t0, t_hi, tid);
         __syncthreads();
@@ -857,7 +1051,7 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
 // Key side, per token m (S = sum rho_m(u_m) v_m^T, z = sum u_m, u = phi(k W_k)),
 // given the reduced dS, dz: dv_lr = dS^T fk, dfk = dS v, du = rho^T dfk + dz,
 // dpk = du phi', dk_lr = W_k dpk; partial sums of dW_k = k^T dpk [D*R].
-template <int D, int R>
+template <int D, int R, bool BF>
 __global__ __launch_bounds__(256) void k_bwd_lr_k(LrBwdArgs a) {
     using Tl = LrTile<D, R>;
     constexpr int TT = Tl::TT, XLD = Tl::XLD, RW = Tl::RW, RLD = Tl::RLD, NB16 = Tl::NB16;
@@ -877,7 +1071,10 @@ __global__ __launch_bounds__(256) void k_bwd_lr_k(LrBwdArgs a) {
     const long t_lo = (long)split * a.chunk;
     const long t_hi = t_lo + a.chunk < L ? t_lo + a.chunk : L;
     const float* dsz = a.dSz + bh * (long)(R * D + R);
-    for (int e = tid; e < D * R; e += 256) w_s[(e / R) * RW + e % R] = round_bf(a.Wk[(long)head * D * R + e]);
+    for (int e = tid; e < D * R; e += 256) {
+        const float x = a.Wk[(long)head * D * R + e];
+        w_s[(e / R) * RW + e % R] = BF ? round_bf(x) : x;
+    }
     for (int e = tid; e < R * D; e += 256) s_s[e] = dsz[e];
     for (int e = tid; e < R; e += 256) z_s[e] = dsz[R * D + e];
     float4 accW[NB16][4];
@@ -885,12 +1082,13 @@ __global__ __launch_bounds__(256) void k_bwd_lr_k(LrBwdArgs a) {
     for (int c = 0; c < NB16; ++c)
 #pragma unroll
         for (int i = 0; i < 4; ++i) accW[c][i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    const uint16_t* ks = a.k + bh * L * D;
-    const uint16_t* vs = a.v + bh * L * D;
+    const size_t es = BF ? 2 : 4;
+    const void* ks = (const char*)(const void*)a.k + bh * L * D * es;
+    const void* vs = (const char*)(const void*)a.v + bh * L * D * es;
 
     for (long t0 = t_lo; t0 < t_hi; t0 += TT) {
         __syncthreads();
-        lr_load_rows<D, R>(ks, vs, t0, t_hi, x_s, v_s, tid);
+        lr_load_rows<D, R, BF>(ks, vs, t0, t_hi, x_s, v_s, tid);
         __syncthreads();
         lr_features<D, R>(a, x_s, w_s, u_t, f_t, d_t, t0, t_hi, tid);
         __syncthreads();
@@ -999,28 +1197,30 @@ static unsigned grid_for(long n) {
     return (unsigned)(g < 1 ? 1 : g);
 }
 
-template <int D, int R>
+template <int D, int R, bool BF>
 static hipError_t bwd_lr_t(bool key_side, const LrBwdArgs& a, long BH, hipStream_t st) {
     dim3 grid((unsigned)a.nsplit, (unsigned)BH);
     if (key_side)
-        hipLaunchKernelGGL((k_bwd_lr_k<D, R>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_bwd_lr_k<D, R, BF>), grid, dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((k_bwd_lr_q<D, R>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_bwd_lr_q<D, R, BF>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool BF>
 static hipError_t bwd_lr_d(int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st) {
     switch (R) {
-        case 8: return bwd_lr_t<D, 8>(key_side, a, BH, st);
-        case 16: return bwd_lr_t<D, 16>(key_side, a, BH, st);
-        case 32: return bwd_lr_t<D, 32>(key_side, a, BH, st);
-        default: return bwd_lr_t<D, 64>(key_side, a, BH, st);
+        case 8: return bwd_lr_t<D, 8, BF>(key_side, a, BH, st);
+        case 16: return bwd_lr_t<D, 16, BF>(key_side, a, BH, st);
+        case 32: return bwd_lr_t<D, 32, BF>(key_side, a, BH, st);
+        default: return bwd_lr_t<D, 64, BF>(key_side, a, BH, st);
     }
 }
 
-hipError_t launch_bwd_lr(int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st) {
-    return D == 64 ? bwd_lr_d<64>(R, key_side, a, BH, st) : bwd_lr_d<128>(R, key_side, a, BH, st);
+hipError_t launch_bwd_lr(int dtype_bf16, int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st) {
+    if (dtype_bf16)
+        return D == 64 ? bwd_lr_d<64, true>(R, key_side, a, BH, st) : bwd_lr_d<128, true>(R, key_side, a, BH, st);
+    return D == 64 ? bwd_lr_d<64, false>(R, key_side, a, BH, st) : bwd_lr_d<128, false>(R, key_side, a, BH, st);
 }
 
 hipError_t launch_bwd_sum_parts(const float* part, int B, int H, int nsplit, long stride, long off, long n,
@@ -1065,7 +1265,23 @@ static hipError_t bwd_sparse(int D, int BS, bool dkdv, const BwdArgs& a, hipStre
     return BS == 64 ? bwd_sparse_t<64, 64>(dkdv, a, st) : bwd_sparse_t<64, 32>(dkdv, a, st);
 }
 
-hipError_t launch_bwd_dq(int D, int BS, const BwdArgs& a, hipStream_t st) { return bwd_sparse(D, BS, false, a, st); }
-hipError_t launch_bwd_dkdv(int D, int BS, const BwdArgs& a, hipStream_t st) { return bwd_sparse(D, BS, true, a, st); }
+hipError_t launch_bwd_dq(int dtype_bf16, int D, int BS, const BwdArgs& a, hipStream_t st) {
+    if (dtype_bf16) return bwd_sparse(D, BS, false, a, st);
+    if (D == 64)
+        hipLaunchKernelGGL((k_bwd_dq_f32<64>), dim3((unsigned)a.nwg), dim3(256), 0, st, a, a.idx, BS);
+    else
+        hipLaunchKernelGGL((k_bwd_dq_f32<128>), dim3((unsigned)a.nwg), dim3(256), 0, st, a, a.idx, BS);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(int dtype_bf16, int D, int BS, const BwdArgs& a, hipStream_t st) {
+    if (dtype_bf16) return bwd_sparse(D, BS, true, a, st);
+    if (D == 64)
+        hipLaunchKernelGGL((k_bwd_dkdv_f32<64>), dim3((unsigned)a.nwg), dim3(256), 0, st, a, a.inv_off, a.inv_list, BS);
+    else
+        hipLaunchKernelGGL((k_bwd_dkdv_f32<128>), dim3((unsigned)a.nwg), dim3(256), 0, st, a, a.inv_off, a.inv_list,
+                           BS);
+    return hipGetLastError();
+}
 
 }  // namespace slr

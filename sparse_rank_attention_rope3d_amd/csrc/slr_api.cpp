@@ -144,10 +144,11 @@ void summary_split(const Dims& d, int slots, int* chunk, int* nsplit) {
     *nsplit = (int)best_n;
 }
 
-// The backward is built for bf16 layers with the per-head gate (either
-// low-rank variant, either feature map).
+// The backward is built for the per-head gate (either low-rank variant,
+// either feature map, bf16 or fp32 layers).
 int check_bwd_supported(const Dims& d, const slr_lowrank_cfg* lr) {
-    if (!d.bf16 || lr->gate_mode != SLR_GATE_HEAD) return SLR_EUNSUPPORTED;
+    (void)d;
+    if (lr->gate_mode != SLR_GATE_HEAD) return SLR_EUNSUPPORTED;
     return SLR_OK;
 }
 
@@ -194,8 +195,8 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         // per-row softmax statistics, the low-rank gradient parts and the
         // inverse of the kept lists
         const size_t rows = (size_t)nblk * bs;
-        w.qr = take(2ul * d.BH * rows * d.D);
-        w.kr = take(2ul * d.BH * rows * d.D);
+        w.qr = take((size_t)d.es * d.BH * rows * d.D);
+        w.kr = take((size_t)d.es * d.BH * rows * d.D);
         w.wkt = take(2ul * d.H * RP * d.D);
         w.part = take(4ul * d.BH * summary_split_cap(d) * (RP * d.D + RP));
         w.S = take(4ul * d.BH * R * d.D);
@@ -608,8 +609,8 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     const bool tiled_fwd = use_tiles(d, bs);
     const float log2e = 1.4426950408889634f, inv_sqrt_d = (float)(1.0 / std::sqrt((double)d.D));
     SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
-    SLR_TRY(launch_rope_pool(1, (int)d.D, q, k, qr, kr, nullptr, nullptr, tab, g, d.BH, d.L, (long)nblk * bs, bs, nblk,
-                             s, tiled_fwd ? tiled_qscale(d.D) : 1.f));
+    SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, qr, kr, nullptr, nullptr, tab, g, d.BH, d.L, (long)nblk * bs, bs,
+                             nblk, s, tiled_fwd ? tiled_qscale(d.D) : 1.f));
     if ((st = run_summary(d, g, lg, RP, lowrank, k, v, nullptr, 0, ws, w, S, z, false, s))) return st;
 
     // low-rank branch: query side, reductions, key side
@@ -627,14 +628,14 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     la.Et = lowrank->Et; la.Eh = lowrank->Eh; la.Ew = lowrank->Ew;
     la.dpre = abspe ? at<float>(ws, w.dpre) : nullptr;
     const long qstride = 2l * d.D * R + R + 4;   // [dW_q | dS | dz | dg | pad]
-    SLR_TRY(launch_bwd_lr((int)d.D, R, false, la, d.BH, s));
+    SLR_TRY(launch_bwd_lr(d.bf16, (int)d.D, R, false, la, d.BH, s));
     // [dW_q | dS | dz | dg] partials -> dS, dz per slice; dW_q, dg per head
     SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, qstride, d.D * R, (long)R * d.D + R, false,
                                  dsz, s));
     SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, qstride, 0, d.D * R, true, dWq, s));
     SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, qstride, 2l * d.D * R + R, 1, true, dgate,
                                  s));
-    SLR_TRY(launch_bwd_lr((int)d.D, R, true, la, d.BH, s));
+    SLR_TRY(launch_bwd_lr(d.bf16, (int)d.D, R, true, la, d.BH, s));
     SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, d.D * R, 0, d.D * R, true, dWk, s));
     if (abspe) {
         // E tables: per-axis sums of the per-token gradient, per slice, then over the slices
@@ -661,10 +662,10 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     a.tab = tab; a.g = g; a.L = d.L; a.nblk = nblk; a.keep = keep;
     a.scale = (float)(1.0 / std::sqrt((double)d.D));
     a.nwg = d.BH * nblk;
-    SLR_TRY(launch_bwd_dq((int)d.D, bs, a, s));
+    SLR_TRY(launch_bwd_dq(d.bf16, (int)d.D, bs, a, s));
     SLR_TRY(launch_bwd_inverse(idx, d.BH, nblk, keep, at<uint32_t>(ws, w.bits), at<int32_t>(ws, w.cnt),
                                at<int32_t>(ws, w.off), at<int32_t>(ws, w.list), s));
-    SLR_TRY(launch_bwd_dkdv((int)d.D, bs, a, s));
+    SLR_TRY(launch_bwd_dkdv(d.bf16, (int)d.D, bs, a, s));
     return SLR_OK;
 }
 

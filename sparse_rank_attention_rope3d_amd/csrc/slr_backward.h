@@ -5,7 +5,7 @@
 
 namespace slr {
 
-// ---- backward pass (bf16 layers) -----------------------------------------
+// ---- backward pass ---------------------------------------------------------
 
 // Sparse branch: softmax attention over the kept blocks, differentiated.
 struct BwdArgs {
@@ -56,7 +56,7 @@ struct LrBwdArgs {
     float* dpre;                        // absolute PE: [BH][L][R] gradient w.r.t. x W + E (q side + k side)
 };
 
-hipError_t launch_bwd_lr(int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st);
+hipError_t launch_bwd_lr(int dtype_bf16, int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st);
 // out[o][e] = sum over (b < nb, split < nsplit) of part[((b*H + h)*nsplit + split)*stride + off + e]:
 // per_head sums the batches into [H][n], else [BH][n] (nb = 1, h = slice).
 hipError_t launch_bwd_sum_parts(const float* part, int B, int H, int nsplit, long stride, long off, long n,
@@ -68,7 +68,7 @@ hipError_t launch_bwd_e_sum(const float* dpre, long BH, long L, int T, int Hg, i
 // Inverse of the kept-block lists, deterministic: bits [BH][nblk][ceil(nblk/32)] scratch.
 hipError_t launch_bwd_inverse(const int32_t* idx, long BH, int nblk, int keep, uint32_t* bits, int32_t* cnt,
                               int32_t* off, int32_t* list, hipStream_t st);
-hipError_t launch_bwd_dq(int D, int BS, const BwdArgs& a, hipStream_t st);
-hipError_t launch_bwd_dkdv(int D, int BS, const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_dq(int dtype_bf16, int D, int BS, const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_dkdv(int dtype_bf16, int D, int BS, const BwdArgs& a, hipStream_t st);
 
 }  // namespace slr

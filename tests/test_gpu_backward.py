@@ -4,10 +4,12 @@ The GPU training forward (slr_attention_fwd_train) supplies the selection
 (checked to be a valid top-k), its O_sparse and the rows' log2 softmax
 normalisers, as a training step would; the oracle recomputes its own in
 float64 on the same selection (the saved normalisers are checked against
-it to 3e-2 absolute, in log2 units). Bar (bf16 layers): relative Frobenius error
-<= 1e-2 and max-abs error <= 3e-2 x max |reference| for dq, dk, dv, dW_q,
-dW_k and the gate gradient. (The gradients are ~0.05 RMS, so the forward's
-absolute 3e-2 is stated relative to the gradient's own scale.)
+it to 3e-2 absolute, in log2 units). Bar: for bf16 layers relative Frobenius
+error <= 1e-2 and max-abs error <= 3e-2 x max |reference| for dq, dk, dv,
+dW_q, dW_k, the gate gradient and the E tables' gradients (the gradients are
+~0.05 RMS, so the forward's absolute 3e-2 is stated relative to the
+gradient's own scale); for fp32 layers 1e-5 relative Frobenius and 1e-5 x
+max |reference|.
 """
 import dataclasses
 
@@ -24,20 +26,23 @@ import slrtest as T
 
 pytestmark = pytest.mark.gpu
 
-REL, MAXREL = 1e-2, 3e-2
+BAR = {"bf16": (1e-2, 3e-2), "f32": (1e-5, 1e-5)}
+_dtype = ["bf16"]
 
 
 def _close(name, got, ref):
+    rel, maxrel = BAR[_dtype[0]]
     rf = T.rel_fro(got, ref)
     scale = float(np.abs(ref).max()) if ref.size else 1.0
     ma = T.max_abs(got, ref) / (scale if scale > 0 else 1.0)
     T.log(f"    {name}: rel_fro={rf:.3e} max_abs/max|ref|={ma:.3e}")
-    assert rf <= REL, f"{name}: relative Frobenius error {rf:.3e} > {REL}"
-    assert ma <= MAXREL, f"{name}: max abs error {ma:.3e} x max|ref| > {MAXREL}"
+    assert rf <= rel, f"{name}: relative Frobenius error {rf:.3e} > {rel}"
+    assert ma <= maxrel, f"{name}: max abs error {ma:.3e} x max|ref| > {maxrel}"
 
 
 def _dout(cfg):
-    g = torch.empty((cfg.B, cfg.H, cfg.L, cfg.D), dtype=torch.bfloat16, device="cuda")
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    g = torch.empty((cfg.B, cfg.H, cfg.L, cfg.D), dtype=tdt, device="cuda")
     for b in range(cfg.B):
         for h in range(cfg.H):
             g[b, h] = T.to_device(synth.dout_slice(cfg, b, h), cfg.dtype)
@@ -100,7 +105,9 @@ def _rows(cfg, blocks):
 
 
 def _check(cfg, slices=None, qsample=None, ksample=None, heads=None):
-    T.log(f"  case {cfg.name}: L={cfg.L} nblk={cfg.nblk} keep={cfg.keep} D={cfg.D} r={cfg.rank} fmap={cfg.fmap}")
+    T.log(f"  case {cfg.name}: L={cfg.L} nblk={cfg.nblk} keep={cfg.keep} D={cfg.D} r={cfg.rank} fmap={cfg.fmap} "
+          f"{cfg.dtype}")
+    _dtype[0] = cfg.dtype
     inp, idx, (dq, dk, dv, dWq, dWk, dg, dE), lse = _run_gpu(cfg)
     slices = slices or [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
     heads = sorted({h for _, h in slices}) if heads is None else heads
@@ -164,6 +171,20 @@ SMALL = [
 @pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
 def test_backward_small_layers(name, kw):
     cfg = dataclasses.replace(synth.wan13b(), name=f"bwd {name}", **kw)
+    _check(cfg)
+
+
+F32 = [
+    ("tiny fp32 check layer", synth.tiny()),
+    ("fp32 ragged D128 block64", dataclasses.replace(synth.wan13b(), name="fp32 ragged", dtype="f32", B=1, H=2, T=4,
+                                                     Hg=9, Wg=13, keep=3)),
+    ("fp32 absolute PE silu", dataclasses.replace(synth.tiny(), name="fp32 abspe silu", lr_mode="abspe",
+                                                  lr_pairs=(0, 0, 0), fmap="silu", T=3, Hg=5, Wg=7)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", F32, ids=[s[0] for s in F32])
+def test_backward_fp32_layers(name, cfg):
     _check(cfg)
 
 
