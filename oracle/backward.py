@@ -18,7 +18,10 @@ states them. Readings:
   (each 2x2 pair turned by the opposite angle);
 - the low-rank branch's gradient follows phi, the rotation after phi, the
   summary S, z and the normaliser w . z + eps (or the token count for SiLU);
-- the per-head gate's gradient is sum over rows of dout . O_lowrank.
+- the per-head gate's gradient is sum over rows of dout . O_lowrank;
+- with RoLA's token-wise gate (§4.4; the forward's reading is that of
+  ``oracle.token_gate``) the gradient flows through the gate's logistic of
+  q . W_g + b_g and through both RMS terms of its scale.
 
 Each function names the forward step it differentiates.
 """
@@ -243,14 +246,46 @@ def lowrank_bwd(cfg, q, k, v, wq, wk, dolr, E=None, origin=(0, 0, 0)) -> Dict[st
 # ---------------------------------------------------------------------------
 # one (b, h) slice of the whole layer
 
+def token_gate_bwd(q, wg, bg, o_sp, o_lr, eps, dout) -> Dict[str, np.ndarray]:
+    """Gradient of the token-wise gated fusion (RoLA §4.4; the forward is
+    ``oracle.token_gate``), row by row:
+        out = o_sp + G o_lr,  G = g c,  g = sigmoid(q . wg + bg),
+        c = rs / (rl + eps),  rs = RMS(o_sp), rl = RMS(o_lr) over the D dims.
+    Given dout: dG = dout . o_lr, dg = dG c, dc = dG g, drs = dc / (rl + eps),
+    drl = -dc rs / (rl + eps)^2, and d RMS(x) / dx = x / (D RMS(x)):
+        d o_sp = dout + drs o_sp / (D rs),   d o_lr = G dout + drl o_lr / (D rl),
+        dt = dg g (1 - g):  dq = dt wg,  dwg = sum_rows dt q,  dbg = sum_rows dt.
+    Rows are [n, D]; returns d_osp, d_olr, dq [n, D], dwg [D], dbg."""
+    q, o_sp, o_lr, dout = _d(q), _d(o_sp), _d(o_lr), _d(dout)
+    D = o_sp.shape[1]
+    g = 1.0 / (1.0 + np.exp(-(q @ _d(wg) + float(bg))))
+    rs = np.sqrt((o_sp * o_sp).mean(axis=1))
+    rl = np.sqrt((o_lr * o_lr).mean(axis=1))
+    c = rs / (rl + eps)
+    G = g * c
+    dG = (dout * o_lr).sum(axis=1)
+    dgl, dc = dG * c, dG * g
+    drs = dc / (rl + eps)
+    drl = -dc * rs / (rl + eps) ** 2
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ks = np.where(rs > 0, drs / (D * rs), 0.0)
+        kl = np.where(rl > 0, drl / (D * rl), 0.0)
+    dt = dgl * g * (1.0 - g)
+    return {"d_osp": dout + ks[:, None] * o_sp, "d_olr": G[:, None] * dout + kl[:, None] * o_lr,
+            "dq": dt[:, None] * _d(wg)[None, :], "dwg": (dt[:, None] * q).sum(axis=0), "dbg": float(dt.sum()),
+            "g": g}
+
+
 def layer_slice_bwd(cfg, q, k, v, wq, wk, gate_h, dout, E=None, idx=None,
-                    o_sp: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                    o_sp: Optional[np.ndarray] = None, token_gate_wb=None) -> Dict[str, np.ndarray]:
     """Gradients of one (b, h) slice of the layer (per-head gate):
     out = O_sparse + g_h O_lowrank, so dO_sparse = dout, dO_lowrank = g_h dout
     and dg_h = sum over rows of dout . O_lowrank. ``idx`` fixes the kept blocks
     (the forward's selection when None); ``o_sp`` [L, D] replaces the sparse
     output used for dO . o (the saved forward output). Returns dq, dk, dv
-    [L, D], dWq, dWk [D, r], dg (scalar), dE (absolute PE), idx and the parts."""
+    [L, D], dWq, dWk [D, r], dg (scalar), dE (absolute PE), idx and the parts.
+    ``token_gate_wb = (wg [D], bg)`` uses RoLA's token-wise gate instead of
+    g_h (then dWg [D] and dbg replace dg)."""
     grid = (cfg.T, cfg.Hg, cfg.Wg)
     dout = _d(dout)
     L = dout.shape[0]
@@ -258,8 +293,18 @@ def layer_slice_bwd(cfg, q, k, v, wq, wk, gate_h, dout, E=None, idx=None,
         idx = oracle.layer_slice(cfg, q, k, v, wq, wk, gate_h, E=E)["idx_ref"]
     qr = oracle.rope3d(q, grid, cfg.base, cfg.pairs)
     kr = oracle.rope3d(k, grid, cfg.base, cfg.pairs)
-    sp = sparse_attention_bwd(qr, kr, v, cfg.block, idx, dout, o=o_sp)
-    lr = lowrank_bwd(cfg, q, k, v, wq, wk, float(gate_h) * dout, E=E)
+    tg = None
+    if token_gate_wb is None:
+        d_sp, d_lr = dout, float(gate_h) * dout
+    else:
+        # the gate reads both branch outputs: the forward's O_sparse and O_lowrank
+        L, D = dout.shape
+        osp = oracle.block_sparse_attention(qr, kr, v, cfg.block, idx).reshape(-1, D)[:L] if o_sp is None else _d(o_sp)
+        olr = lowrank_bwd(cfg, q, k, v, wq, wk, np.zeros_like(dout), E=E)["o_lr"]
+        tg = token_gate_bwd(q, token_gate_wb[0], token_gate_wb[1], osp, olr, cfg.eps, dout)
+        d_sp, d_lr, o_sp = tg["d_osp"], tg["d_olr"], osp
+    sp = sparse_attention_bwd(qr, kr, v, cfg.block, idx, d_sp, o=o_sp)
+    lr = lowrank_bwd(cfg, q, k, v, wq, wk, d_lr, E=E)
     res = {
         "dq": rope3d_transpose(sp["dq"], grid, cfg.base, cfg.pairs) + lr["dq"],
         "dk": rope3d_transpose(sp["dk"], grid, cfg.base, cfg.pairs) + lr["dk"],
@@ -268,6 +313,10 @@ def layer_slice_bwd(cfg, q, k, v, wq, wk, gate_h, dout, E=None, idx=None,
         "dg": float((dout * lr["o_lr"]).sum()),
         "idx": idx, "sparse": sp, "lowrank": lr,
     }
+    if tg is not None:
+        res["dq"] = res["dq"] + tg["dq"]
+        res["dWg"], res["dbg"], res["gate"] = tg["dwg"], tg["dbg"], tg
+        del res["dg"]
     if E is not None:
         res["dE"] = lr["dE"]
     assert res["dq"].shape == (L, q.shape[1])

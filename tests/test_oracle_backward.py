@@ -5,7 +5,8 @@ is pinned on its own (RoPE, selection, attention and low-rank pins). Here:
 
 - central finite differences of that forward (the kept blocks held fixed,
   as the top-k carries no gradient) along seeded random directions in q, k,
-  v, W_q, W_k, the gate and the absolute-PE tables match <grad, direction>;
+  v, W_q, W_k, the gate (per head, or the token gate's W_g and b_g) and the
+  absolute-PE tables match <grad, direction>;
   this pins every step of the chain rule, since any dropped term, wrong
   sign or transposed operand changes some directional derivative;
 - with every block kept the sparse gradient equals torch's autograd of
@@ -50,14 +51,22 @@ def _loss(cfg, q, k, v, wq, wk, g, E, dout, idx):
     return float((dout * out).sum())
 
 
-def _fd_check(cfg, seed):
+def _fd_check(cfg, seed, token=False):
     q, k, v, wq, wk, g, E, dout = _inputs(cfg)
-    grads = OB.layer_slice_bwd(cfg, q, k, v, wq, wk, g, dout, E=E)
+    tg = None
+    if token:
+        rng0 = np.random.default_rng(seed + 100)
+        tg = (rng0.standard_normal(cfg.D) * 0.2, -0.3)
+    grads = OB.layer_slice_bwd(cfg, q, k, v, wq, wk, g, dout, E=E, token_gate_wb=tg)
     idx = grads["idx"]
     rng = np.random.default_rng(seed)
-    args = {"q": q, "k": k, "v": v, "wq": wq, "wk": wk, "g": np.array(g)}
-    gmap = {"q": grads["dq"], "k": grads["dk"], "v": grads["dv"], "wq": grads["dWq"], "wk": grads["dWk"],
-            "g": np.array(grads["dg"])}
+    args = {"q": q, "k": k, "v": v, "wq": wq, "wk": wk}
+    gmap = {"q": grads["dq"], "k": grads["dk"], "v": grads["dv"], "wq": grads["dWq"], "wk": grads["dWk"]}
+    if token:
+        args["wg"], args["bg"] = np.asarray(tg[0]), np.array(tg[1])
+        gmap["wg"], gmap["bg"] = grads["dWg"], np.array(grads["dbg"])
+    else:
+        args["g"], gmap["g"] = np.array(g), np.array(grads["dg"])
     if E is not None:
         for i, name in enumerate(("et", "eh", "ew")):
             args[name] = np.asarray(E[i], np.float64)
@@ -65,6 +74,10 @@ def _fd_check(cfg, seed):
 
     def call(a):
         EE = (a["et"], a["eh"], a["ew"]) if E is not None else None
+        if token:
+            res = oracle.layer_slice(cfg, a["q"], a["k"], a["v"], a["wq"], a["wk"], 0.0, E=EE, idx=idx,
+                                     token_gate_wb=(a["wg"], float(a["bg"])))
+            return float((dout * res["out"].reshape(-1, cfg.D)[: cfg.L]).sum())
         return _loss(cfg, a["q"], a["k"], a["v"], a["wq"], a["wk"], float(a["g"]), EE, dout, idx)
 
     h = 1e-5
@@ -88,6 +101,14 @@ def test_finite_differences_rotary_silu():
 
 def test_finite_differences_absolute_pe():
     _fd_check(_abspe_cfg(), 3)
+
+
+def test_finite_differences_token_gate():
+    _fd_check(_cfg(), 5, token=True)
+
+
+def test_finite_differences_token_gate_silu_absolute_pe():
+    _fd_check(_abspe_cfg(fmap="silu"), 6, token=True)
 
 
 def test_finite_differences_ragged_tail_and_one_kept_block():
