@@ -342,11 +342,11 @@ def main() -> int:
                  "speedup_of_slr_layer": round(dms / ms_step, 2)}
         del wsd
 
-    # layer backward (bf16, per-head gate, either low-rank variant): the training
+    # layer backward (bf16 layers): the training
     # forward saves the selection, O_sparse and the row normalisers once, then
     # the backward is timed on a seeded N(0, 1) output gradient
     backward = None
-    if args.bwd_reps > 0 and cfg.dtype == "bf16" and cfg.gate == "head":
+    if args.bwd_reps > 0 and cfg.dtype == "bf16":
         print("[bench] layer backward", file=sys.stderr, flush=True)
         gen = torch.Generator(device="cuda").manual_seed(1234)
         dout = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)

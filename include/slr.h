@@ -212,7 +212,11 @@ int slr_dense_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, co
  *   low-rank branch (RoLA §4.1-4.3, App. A; RoPeSLR abstract): the chain
  *     rule through phi(x W [+ E]), the rotation after phi (rotary variant),
  *     S, z and the normaliser, with dO_lowrank = g_h dout;
- *   dgate[h] = sum over b and rows of dout . O_lowrank.
+ *   dgate[h] = sum over b and rows of dout . O_lowrank (per-head gate);
+ *   with the token gate (RoLA §4.4; out = O_sparse + G O_lowrank, G =
+ *     sigmoid(q . W_g + b_g) RMS(O_sparse) / (RMS(O_lowrank) + eps)) the
+ *     gradient also flows through both RMS terms and the gate's logit:
+ *     dWg [H,D] and dbg [H] fp32 (sums over batch and rows) replace dgate.
  * The selection is held fixed: idx [B,H,nblk,keep] int32 is the forward's
  * (idx_out of slr_attention_fwd_train); each row must list distinct blocks
  * in [0, nblk) (entries outside that range are skipped). o_sparse
@@ -220,20 +224,22 @@ int slr_dense_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, co
  * (the softmax normalisers are reused, not recomputed), for the same q, k,
  * v and configuration. dout, dq, dk, dv: [B,H,L,D] bf16;
  * dq, dk, dv must not overlap each other or any input. dWq, dWk: [H,D,r]
- * fp32, dgate: [H] fp32, all overwritten (sums over the batch).
+ * fp32, all overwritten (sums over the batch); dgate [H] fp32 for
+ * SLR_GATE_HEAD (dWg, dbg ignored, may be NULL), dWg [H,D] and dbg [H]
+ * fp32 for SLR_GATE_TOKEN (dgate ignored, may be NULL).
  * SLR_LR_ABS_PE layers also get the tables' gradients dEt [T,r], dEh [Hg,r],
  * dEw [Wg,r] fp32 (overwritten; sums over batch, heads and tokens; required,
  * 4-byte aligned); for SLR_LR_ROPE_OUTSIDE they are ignored (may be NULL).
- * Built for bf16 layers with SLR_GATE_HEAD (either low-rank variant, either
- * feature map); other settings return SLR_EUNSUPPORTED. Workspace:
+ * Every setting of the forward is covered (either gate, either low-rank
+ * variant, either feature map, bf16 or fp32). Workspace:
  * slr_workspace_bytes(SLR_OP_ATTENTION_BWD, ...). Results are bitwise
  * reproducible (fixed reduction orders, no floating-point atomics).
  */
 int slr_attention_bwd(const slr_shape *shape, const slr_rope_cfg *rope, const slr_sparse_cfg *sparse,
                       const slr_lowrank_cfg *lowrank, const void *q, const void *k, const void *v,
                       const int32_t *idx, const void *o_sparse, const float *lse, const void *dout, void *dq,
-                      void *dk, void *dv, float *dWq, float *dWk, float *dgate, float *dEt, float *dEh,
-                      float *dEw, void *ws, size_t ws_bytes, void *stream);
+                      void *dk, void *dv, float *dWq, float *dWk, float *dgate, float *dWg, float *dbg,
+                      float *dEt, float *dEh, float *dEw, void *ws, size_t ws_bytes, void *stream);
 
 /* Static text for a status code. */
 const char *slr_status_string(int status);

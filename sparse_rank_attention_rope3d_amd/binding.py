@@ -82,7 +82,7 @@ def lib() -> ctypes.CDLL:
         L.slr_attention_fwd_staged.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg), vp,
                                                vp, vp, vp, vp, vp, vp, vp, sz, P(vp), vp]
         L.slr_dense_attention_fwd.argtypes = [P(SlrShape), P(SlrRopeCfg), vp, vp, vp, vp, vp, sz, vp]
-        L.slr_attention_bwd.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg)] + [vp] * 17 + [sz, vp]
+        L.slr_attention_bwd.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg)] + [vp] * 19 + [sz, vp]
         L.slr_attention_fwd_train.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg)] + [vp] * 8 + [sz, vp]
         for f in EXPORTS[:-1]:
             getattr(L, f).restype = ctypes.c_int
@@ -237,7 +237,8 @@ def slr_attention_bwd(q, k, v, idx, o_sparse, lse, dout, shape: SlrShape, rope: 
                       lowrank: SlrLowrankCfg, ws: Optional[torch.Tensor] = None, grads=None):
     """Backward of the layer given dout (idx, o_sparse and lse saved by
     slr_attention_fwd_train). Returns (dq, dk, dv, dWq [H, D, r] fp32, dWk,
-    dgate [H] fp32, dE) with dE = (dEt [T, r], dEh [Hg, r], dEw [Wg, r]) fp32
+    dgate, dE): dgate is [H] fp32 for the per-head gate, (dWg [H, D], dbg [H])
+    fp32 for the token gate; dE = (dEt [T, r], dEh [Hg, r], dEw [Wg, r]) fp32
     for the absolute-PE variant, else None; ``grads`` may supply those
     outputs."""
     if grads is None:
@@ -246,6 +247,8 @@ def slr_attention_bwd(q, k, v, idx, o_sparse, lse, dout, shape: SlrShape, rope: 
         dWq = torch.empty((shape.H, shape.D, lowrank.rank), dtype=torch.float32, device=dev)
         dWk = torch.empty_like(dWq)
         dg = torch.empty((shape.H,), dtype=torch.float32, device=dev)
+        if lowrank.gate_mode == SLR_GATE_TOKEN:
+            dg = (torch.empty((shape.H, shape.D), dtype=torch.float32, device=dev), dg)
         dE = None
         if lowrank.mode == SLR_LR_ABS_PE:
             dE = tuple(torch.empty((n, lowrank.rank), dtype=torch.float32, device=dev)
@@ -255,7 +258,8 @@ def slr_attention_bwd(q, k, v, idx, o_sparse, lse, dout, shape: SlrShape, rope: 
     ws = _ws(SLR_OP_ATTENTION_BWD, shape, rope, sparse, lowrank, ws, q.device)
     _check(lib().slr_attention_bwd(ctypes.byref(shape), ctypes.byref(rope), ctypes.byref(sparse),
                                    ctypes.byref(lowrank), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(o_sparse),
-                                   _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dWq), _ptr(dWk), _ptr(dg),
+                                   _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dWq), _ptr(dWk),
+                                   *((None, _ptr(dg[0]), _ptr(dg[1])) if isinstance(dg, tuple) else (_ptr(dg), None, None)),
                                    *(_ptr(t) for t in (dE or (None, None, None))),
                                    _ptr(ws), ws.numel(), _stream()), "slr_attention_bwd")
     return dq, dk, dv, dWq, dWk, dg, dE

@@ -921,6 +921,9 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
     __shared__ float part_s[(D / 4) * TT];
     __shared__ float n_s[TT], dn_s[TT], sc_s[TT];
     __shared__ float red[256];
+    // token gate: per-row sums of O.O and O_sp.O_sp, and the gate's row coefficients
+    __shared__ float part2_s[(D / 4) * TT], part3_s[(D / 4) * TT];
+    __shared__ float G_s[TT], kl_s[TT], ks_s[TT], dtt_s[TT];
     const int tid = threadIdx.x;
     const int split = blockIdx.x;
     const long bh = blockIdx.y;
@@ -944,10 +947,23 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
             accW[c][i] = make_float4(0.f, 0.f, 0.f, 0.f);
             accS[c][i] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
-    float accz = 0.f, accg = 0.f;
+    float accz = 0.f, accg = 0.f, accwg = 0.f;
     const size_t es = BF ? 2 : 4;
     const void* qs = (const char*)(const void*)a.q + bh * L * D * es;
     const void* gs = (const char*)(const void*)a.dout + bh * L * D * es;
+    const bool token = a.token != 0;
+    const float* wgh = token ? a.wg + (long)head * D : nullptr;
+    const float bgh = token ? a.bg[head] : 0.f;
+    // 4 dims of the forward's O_sparse (zero past t_hi)
+    auto osp4 = [&](long l, int g) -> float4 {
+        if (l >= t_hi) return make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (BF) {
+            const u32x2_t u = *reinterpret_cast<const u32x2_t*>((const uint16_t*)a.o_sp + (bh * L + l) * D + 4 * g);
+            return make_float4(bf_lo(u[0]), bf_hi(u[0]), bf_lo(u[1]), bf_hi(u[1]));
+        } else {
+            return ld4((const float*)a.o_sp + (bh * L + l) * D + 4 * g);
+        }
+    };
 
     for (long t0 = t_lo; t0 < t_hi; t0 += TT) {
         __syncthreads();
@@ -966,6 +982,11 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
             const float4 o = vecmat4<R>(f_t + t * RLD, s_s, D, g);
             const float4 go = ld4(g_s + t * XLD + 4 * g);
             part_s[g * TT + t] = go.x * o.x + go.y * o.y + go.z * o.z + go.w * o.w;
+            if (token) {
+                const float4 sp = osp4(t0 + t, g);
+                part2_s[g * TT + t] = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+                part3_s[g * TT + t] = sp.x * sp.x + sp.y * sp.y + sp.z * sp.z + sp.w * sp.w;
+            }
         }
         __syncthreads();
         if (tid < TT) {
@@ -973,11 +994,69 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
             for (int g = 0; g < D / 4; ++g) dot += part_s[g * TT + tid];
             const float invn = 1.f / n_s[tid];
             dot *= invn;
-            dn_s[tid] = silu ? 0.f : -gh * dot * invn;
-            sc_s[tid] = gh * invn;
-            accg += dot;
+            if (!token) {
+                dn_s[tid] = silu ? 0.f : -gh * dot * invn;
+                sc_s[tid] = gh * invn;
+                accg += dot;
+            } else {
+                // out = O_sp + G O_lr, G = sigmoid(q . W_g + b_g) RMS(O_sp) / (RMS(O_lr) + eps):
+                // dO_lr = G dout + kl O_lr, dO_sp = dout + ks O_sp, d(logit) = dtt
+                float oo = 0.f, ss = 0.f, lg = bgh;
+                for (int g = 0; g < D / 4; ++g) {
+                    oo += part2_s[g * TT + tid];
+                    ss += part3_s[g * TT + tid];
+                }
+                oo *= invn * invn;
+                for (int d = 0; d < D; ++d) lg += x_s[tid * XLD + d] * wgh[d];
+                const float gg = 1.f / (1.f + expf(-lg));
+                const float rl = sqrtf(oo / D), rs = sqrtf(ss / D);
+                const float c = rs / (rl + a.eps), G = gg * c;
+                const float dc = dot * gg;
+                const float drs = dc / (rl + a.eps), drl = -dc * rs / ((rl + a.eps) * (rl + a.eps));
+                const float kl = rl > 0.f ? drl / (D * rl) : 0.f;
+                G_s[tid] = G;
+                kl_s[tid] = kl;
+                ks_s[tid] = rs > 0.f ? drs / (D * rs) : 0.f;
+                const float dtt = dot * c * gg * (1.f - gg);
+                dtt_s[tid] = dtt;
+                // dO_lr . O = G (dout . O) + kl (O . O)
+                dn_s[tid] = silu ? 0.f : -(G * dot + kl * oo) * invn;
+                sc_s[tid] = invn;
+                accg += dtt;
+            }
         }
         __syncthreads();
+        if (token) {
+            // dO_lr replaces dout in the tile; dO_sp goes out for the sparse branch
+            for (int e = tid; e < TT * (D / 4); e += 256) {
+                const int t = e % TT, g = e / TT;
+                const long l = t0 + t;
+                const float invn = 1.f / n_s[t];
+                float4 o = vecmat4<R>(f_t + t * RLD, s_s, D, g);
+                o.x *= invn; o.y *= invn; o.z *= invn; o.w *= invn;
+                float* gp = g_s + t * XLD + 4 * g;
+                const float4 go = ld4(gp);
+                const float G = G_s[t], kl = kl_s[t], ks = ks_s[t];
+                *reinterpret_cast<float4*>(gp) = make_float4(G * go.x + kl * o.x, G * go.y + kl * o.y,
+                                                             G * go.z + kl * o.z, G * go.w + kl * o.w);
+                if (l < t_hi) {
+                    const float4 sp = osp4(l, g);
+                    const float4 y = make_float4(go.x + ks * sp.x, go.y + ks * sp.y, go.z + ks * sp.z, go.w + ks * sp.w);
+                    if constexpr (BF) {
+                        *reinterpret_cast<u32x2_t*>((uint16_t*)a.dosp + (bh * L + l) * D + 4 * g) =
+                            u32x2_t{pack_bf2(y.x, y.y), pack_bf2(y.z, y.w)};
+                    } else {
+                        *reinterpret_cast<float4*>((float*)a.dosp + (bh * L + l) * D + 4 * g) = y;
+                    }
+                }
+            }
+            for (int d = tid; d < D; d += 256) {
+                float acc = 0.f;
+                for (int t = 0; t < TT; ++t) acc += dtt_s[t] * x_s[t * XLD + d];
+                accwg += acc;
+            }
+            __syncthreads();
+        }
         // dfq = S (g dout) / n -> rho^T, + dn z, * phi'  (d_t becomes dpq)
         lr_back_features<D, R>(a, g_s, s_s, z_s, sc_s, dn_s, d_t, t0, t_hi, tid);
         __syncthreads();
@@ -992,7 +1071,12 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
         for (int e = tid; e < TT * (D / 4); e += 256) {
             const int t = e % TT, g = e / TT;
             const long l = t0 + t;
-            const float4 y = rowdot4<R>(d_t + t * RLD, w_s, RW, g);
+            float4 y = rowdot4<R>(d_t + t * RLD, w_s, RW, g);
+            if (token) {
+                // the gate's logit reads the raw query row: + dtt W_g
+                const float dt = dtt_s[t];
+                y.x += dt * wgh[4 * g]; y.y += dt * wgh[4 * g + 1]; y.z += dt * wgh[4 * g + 2]; y.w += dt * wgh[4 * g + 3];
+            }
             if (l < t_hi) *reinterpret_cast<float4*>(a.dq_lr + (bh * L + l) * D + 4 * g) = y;
         }
         // partial sums over the tile's tokens, 4x4 blocks
@@ -1044,8 +1128,10 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
     if (tid == 0) {
         float s = 0.f;
         for (int t = 0; t < 256; ++t) s += red[t];
-        part[2 * D * R + R] = s;
+        if (token) a.gpart[(bh * a.nsplit + split) * (long)(D + 4) + D] = s;   // db_g
+        else part[2 * D * R + R] = s;                                           // dg_h
     }
+    if (token && tid < D) a.gpart[(bh * a.nsplit + split) * (long)(D + 4) + tid] = accwg;
 }
 
 // Key side, per token m (S = sum rho_m(u_m) v_m^T, z = sum u_m, u = phi(k W_k)),

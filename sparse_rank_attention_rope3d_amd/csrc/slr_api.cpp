@@ -144,11 +144,11 @@ void summary_split(const Dims& d, int slots, int* chunk, int* nsplit) {
     *nsplit = (int)best_n;
 }
 
-// The backward is built for the per-head gate (either low-rank variant,
-// either feature map, bf16 or fp32 layers).
+// The backward covers every forward setting (either gate, either low-rank
+// variant, either feature map, bf16 or fp32 layers).
 int check_bwd_supported(const Dims& d, const slr_lowrank_cfg* lr) {
     (void)d;
-    if (lr->gate_mode != SLR_GATE_HEAD) return SLR_EUNSUPPORTED;
+    (void)lr;
     return SLR_OK;
 }
 
@@ -156,7 +156,7 @@ int check_bwd_supported(const Dims& d, const slr_lowrank_cfg* lr) {
 struct Layout {
     size_t tab, qr, kr, kvt, qbar, kbar, scores, idx, wqt, wkt, part, S, z, sthi, stlo, zp, total;
     // backward
-    size_t lse, delta, dqlr, dklr, dvlr, lrpart, dsz, bits, cnt, off, list, dpre, epart;
+    size_t lse, delta, dqlr, dklr, dvlr, lrpart, dsz, bits, cnt, off, list, dpre, epart, dosp, gpart;
     bool tiled;
 };
 
@@ -177,7 +177,7 @@ void lr_bwd_split(const Dims& d, int* chunk, int* nsplit) {
 }
 
 Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int keep, int R, int RP,
-              bool abspe = false) {
+              bool abspe = false, bool token = false) {
     Layout w;
     std::memset(&w, 0, sizeof(w));
     size_t off = 0;
@@ -215,6 +215,11 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
             w.dpre = take(4ul * d.BH * d.L * R);
             const int na = d.T > d.Hg ? (d.T > d.Wg ? d.T : d.Wg) : (d.Hg > d.Wg ? d.Hg : d.Wg);
             w.epart = take(4ul * d.BH * na * R);
+        }
+        if (token) {
+            // the sparse branch's upstream gradient and the gate parameters' partials
+            w.dosp = take((size_t)d.es * d.BH * d.L * d.D);
+            w.gpart = take(4ul * d.BH * nsplit * (d.D + 4));
         }
         w.bits = take(4ul * d.BH * nblk * ((nblk + 31) / 32));
         w.cnt = take(4ul * d.BH * nblk);
@@ -320,7 +325,8 @@ int slr_workspace_bytes(int op, const slr_shape* shape, const slr_rope_cfg* rope
         R = lowrank->rank;
     }
     if (op == SLR_OP_ATTENTION_BWD && (st = check_bwd_supported(d, lowrank))) return st;
-    *bytes = layout(op, d, g, bs, nblk, keep, R, RP, lowrank && lowrank->mode == SLR_LR_ABS_PE).total;
+    *bytes = layout(op, d, g, bs, nblk, keep, R, RP, lowrank && lowrank->mode == SLR_LR_ABS_PE,
+                    lowrank && lowrank->gate_mode == SLR_GATE_TOKEN).total;
     return SLR_OK;
 }
 
@@ -564,8 +570,8 @@ int slr_dense_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, co
 int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
                       const slr_lowrank_cfg* lowrank, const void* q, const void* k, const void* v, const int32_t* idx,
                       const void* o_sparse, const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                      float* dWq, float* dWk, float* dgate, float* dEt, float* dEh, float* dEw, void* ws,
-                      size_t ws_bytes, void* stream) {
+                      float* dWq, float* dWk, float* dgate, float* dWg, float* dbg, float* dEt, float* dEh,
+                      float* dEw, void* ws, size_t ws_bytes, void* stream) {
     Dims d;
     RopeGeom g;
     LrGeom lg;
@@ -578,7 +584,10 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o_sparse) || !tensor_ok(dout)) return SLR_EINVAL;
     if (!tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv) || !idx || !aligned(idx, 4)) return SLR_EINVAL;
     if (!lse || !aligned(lse, 4)) return SLR_EINVAL;
-    if (!dWq || !dWk || !dgate || !aligned(dWq, 4) || !aligned(dWk, 4) || !aligned(dgate, 4)) return SLR_EINVAL;
+    const bool token = lowrank->gate_mode == SLR_GATE_TOKEN;
+    if (!dWq || !dWk || !aligned(dWq, 4) || !aligned(dWk, 4)) return SLR_EINVAL;
+    if (!token && (!dgate || !aligned(dgate, 4))) return SLR_EINVAL;
+    if (token && (!dWg || !dbg || !aligned(dWg, 4) || !aligned(dbg, 4))) return SLR_EINVAL;
     const bool abspe = lowrank->mode == SLR_LR_ABS_PE;
     if (abspe && (!dEt || !dEh || !dEw || !aligned(dEt, 4) || !aligned(dEh, 4) || !aligned(dEw, 4)))
         return SLR_EINVAL;
@@ -595,7 +604,7 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     if ((st = check_bwd_supported(d, lowrank))) return st;
     lg.rope = g;
     const int bs = sparse->block, keep = sparse->keep, R = lowrank->rank;
-    Layout w = layout(SLR_OP_ATTENTION_BWD, d, g, bs, nblk, keep, R, RP, abspe);
+    Layout w = layout(SLR_OP_ATTENTION_BWD, d, g, bs, nblk, keep, R, RP, abspe, token);
     if ((st = check_ws(ws, ws_bytes, w.total))) return st;
     hipStream_t s = (hipStream_t)stream;
     float2* tab = at<float2>(ws, w.tab);
@@ -627,14 +636,24 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     la.abspe = abspe ? 1 : 0;
     la.Et = lowrank->Et; la.Eh = lowrank->Eh; la.Ew = lowrank->Ew;
     la.dpre = abspe ? at<float>(ws, w.dpre) : nullptr;
+    la.token = token ? 1 : 0;
+    la.wg = lowrank->Wg; la.bg = lowrank->bg; la.o_sp = o_sparse;
+    la.dosp = token ? at<void>(ws, w.dosp) : nullptr;
+    la.gpart = token ? at<float>(ws, w.gpart) : nullptr;
     const long qstride = 2l * d.D * R + R + 4;   // [dW_q | dS | dz | dg | pad]
     SLR_TRY(launch_bwd_lr(d.bf16, (int)d.D, R, false, la, d.BH, s));
     // [dW_q | dS | dz | dg] partials -> dS, dz per slice; dW_q, dg per head
     SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, qstride, d.D * R, (long)R * d.D + R, false,
                                  dsz, s));
     SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, qstride, 0, d.D * R, true, dWq, s));
-    SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, qstride, 2l * d.D * R + R, 1, true, dgate,
-                                 s));
+    if (!token) {
+        SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, qstride, 2l * d.D * R + R, 1, true, dgate,
+                                     s));
+    } else {
+        // token gate: dW_g [H][D] and db_g [H] from the [dW_g | db_g | pad] partials
+        SLR_TRY(launch_bwd_sum_parts(la.gpart, (int)d.B, (int)d.H, la.nsplit, d.D + 4, 0, d.D, true, dWg, s));
+        SLR_TRY(launch_bwd_sum_parts(la.gpart, (int)d.B, (int)d.H, la.nsplit, d.D + 4, d.D, 1, true, dbg, s));
+    }
     SLR_TRY(launch_bwd_lr(d.bf16, (int)d.D, R, true, la, d.BH, s));
     SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, d.D * R, 0, d.D * R, true, dWk, s));
     if (abspe) {
@@ -652,7 +671,8 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     BwdArgs a;
     std::memset(&a, 0, sizeof(a));
     a.qr = qr; a.kr = kr; a.v = (const uint16_t*)v; a.o_sp = (const uint16_t*)o_sparse;
-    a.dout = (const uint16_t*)dout; a.idx = idx;
+    // with the token gate the sparse branch's upstream gradient is dout plus the RMS term
+    a.dout = (const uint16_t*)(token ? la.dosp : dout); a.idx = idx;
     a.inv_off = at<int32_t>(ws, w.off); a.inv_list = at<int32_t>(ws, w.list);
     a.lse_in = lse; a.lse2 = at<float>(ws, w.lse); a.delta = at<float>(ws, w.delta);
     a.qmul = tiled_fwd ? 1.f : log2e * inv_sqrt_d;

@@ -54,6 +54,11 @@ struct LrBwdArgs {
     int abspe;                          // absolute-PE variant: E added before phi, no rotation
     const float *Et, *Eh, *Ew;          // [T|Hg|Wg][R] (absolute PE)
     float* dpre;                        // absolute PE: [BH][L][R] gradient w.r.t. x W + E (q side + k side)
+    int token;                          // token-wise gate (RoLA §4.4) instead of g_h
+    const float *wg, *bg;               // [H][D], [H]
+    const void* o_sp;                   // [BH][L][D] the forward's O_sparse (layer dtype)
+    void* dosp;                         // [BH][L][D] (layer dtype): the sparse branch's upstream gradient
+    float* gpart;                       // [BH][nsplit][D + 4]: dW_g, db_g partials
 };
 
 hipError_t launch_bwd_lr(int dtype_bf16, int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st);

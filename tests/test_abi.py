@@ -179,11 +179,11 @@ def test_other_entry_points_validate():
 
 def _bwd(shape, rope, sparse, lr, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, idx=FAKE + 0x3000, osp=FAKE + 0x4000,
          lse=FAKE + 0xc000, dout=FAKE + 0x5000, dq=FAKE + 0x6000, dk=FAKE + 0x7000, dv=FAKE + 0x8000,
-         dwq=FAKE + 0x9000, dwk=FAKE + 0xa000, dg=FAKE + 0xb000, det=FAKE + 0xd000, deh=FAKE + 0xe000,
-         dew=FAKE + 0xf000, ws=None, ws_bytes=0):
+         dwq=FAKE + 0x9000, dwk=FAKE + 0xa000, dg=FAKE + 0xb000, dwg=FAKE + 0x10000, dbg=FAKE + 0x11000,
+         det=FAKE + 0xd000, deh=FAKE + 0xe000, dew=FAKE + 0xf000, ws=None, ws_bytes=0):
     r = ctypes.byref
     return B.lib().slr_attention_bwd(r(shape), r(rope), r(sparse), r(lr), q, k, v, idx, osp, lse, dout, dq, dk, dv,
-                                     dwq, dwk, dg, det, deh, dew, ws, ws_bytes, None)
+                                     dwq, dwk, dg, dwg, dbg, det, deh, dew, ws, ws_bytes, None)
 
 
 def test_backward_validates_before_launching():
@@ -220,15 +220,24 @@ def test_backward_absolute_pe_needs_the_table_gradients():
     assert _bwd(shape, rope, sparse, lr, det=None, deh=None, dew=None) == B.SLR_EWORKSPACE
 
 
-@pytest.mark.parametrize("change", ["token_gate"])
-def test_backward_unsupported_settings(change):
+def test_backward_token_gate_outputs():
+    """The token gate's backward returns dW_g, db_g (required) instead of
+    dgate (ignored), and needs room for the sparse branch's upstream
+    gradient."""
     shape, rope, sparse, lr = _cfgs()
+    n_head = B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lr)
     lr.gate_mode, lr.gate, lr.Wg, lr.bg = B.SLR_GATE_TOKEN, None, FAKE, FAKE
-    n = ctypes.c_size_t()
-    r = ctypes.byref
-    assert B.lib().slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, r(shape), r(rope), r(sparse), r(lr),
-                                       r(n)) == B.SLR_EUNSUPPORTED
-    assert _bwd(shape, rope, sparse, lr, ws=FAKE, ws_bytes=1 << 40) == B.SLR_EUNSUPPORTED
+    n_tok = B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lr)
+    layer = synth.wan13b()
+    assert n_tok - n_head >= 2 * layer.B * layer.H * layer.L * layer.D
+    assert _bwd(shape, rope, sparse, lr, dg=None) == B.SLR_EWORKSPACE
+    assert _bwd(shape, rope, sparse, lr, dwg=None) == B.SLR_EINVAL
+    assert _bwd(shape, rope, sparse, lr, dbg=None) == B.SLR_EINVAL
+    assert _bwd(shape, rope, sparse, lr, dbg=FAKE + 2) == B.SLR_EINVAL
+    # the per-head gate needs dgate and ignores dW_g, db_g
+    shape, rope, sparse, lr = _cfgs()
+    assert _bwd(shape, rope, sparse, lr, dg=None) == B.SLR_EINVAL
+    assert _bwd(shape, rope, sparse, lr, dwg=None, dbg=None) == B.SLR_EWORKSPACE
 
 
 def test_training_forward_requires_its_outputs():

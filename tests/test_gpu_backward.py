@@ -188,6 +188,58 @@ def test_backward_fp32_layers(name, cfg):
     _check(cfg)
 
 
+TOKEN = [
+    ("token gate bf16", dataclasses.replace(synth.wan13b(), name="token bf16", B=2, H=2, T=4, Hg=9, Wg=13, keep=3,
+                                            gate="token")),
+    ("token gate bf16 absolute PE silu", dataclasses.replace(synth.wan13b(), name="token abspe silu", B=1, H=2, T=3,
+                                                             Hg=10, Wg=11, keep=4, gate="token", lr_mode="abspe",
+                                                             lr_pairs=(0, 0, 0), fmap="silu")),
+    ("token gate fp32", dataclasses.replace(synth.tiny(), name="token fp32", gate="token")),
+]
+
+
+@pytest.mark.parametrize("name,cfg", TOKEN, ids=[s[0] for s in TOKEN])
+def test_backward_token_gate(name, cfg):
+    """RoLA's token-wise gate: every gradient of every slice against the
+    oracle's layer backward (which recomputes O_sparse and O_lowrank in fp64);
+    dW_g, db_g summed over the batch."""
+    T.log(f"  case {cfg.name}: L={cfg.L} D={cfg.D} r={cfg.rank} fmap={cfg.fmap} {cfg.lr_mode} {cfg.dtype}")
+    _dtype[0] = cfg.dtype
+    inp, idx, (dq, dk, dv, dWq, dWk, (dWg, dbg), dE), lse = _run_gpu(cfg)
+    p = inp.params_np
+    E = _tables(cfg, p)
+    got = {n: [] for n in ("dq", "dk", "dv")}
+    want = {n: [] for n in ("dq", "dk", "dv")}
+    sums = {}
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            qs, ks, vs = synth.qkv_slice(cfg, b, h)
+            ig = idx[b, h].cpu().numpy()
+            ref_f = oracle.layer_slice(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], 0.0, E=E, qblocks=[0], idx=ig)
+            T.check_selection(ig, ref_f["scores"], ref_f["thr"], cfg.keep)
+            ds = np.asarray(synth.dout_slice(cfg, b, h), np.float64)
+            ref = OB.layer_slice_bwd(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], 0.0, ds, E=E, idx=ig,
+                                     token_gate_wb=(p["wg"][h], float(p["bg"][h])))
+            for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+                got[n].append(T.to_host(t[b, h]))
+                want[n].append(ref[n])
+            for n in ("dWq", "dWk", "dWg", "dbg"):
+                sums[n, h] = sums.get((n, h), 0.0) + np.asarray(ref[n])
+            if E is not None:
+                for i in range(3):
+                    sums["dE", i] = sums.get(("dE", i), 0.0) + ref["dE"][i]
+    for n in ("dq", "dk", "dv"):
+        _close(n, np.concatenate(got[n]), np.concatenate(want[n]))
+    for h in range(cfg.H):
+        _close(f"dWq[{h}]", T.to_host(dWq[h]), sums["dWq", h])
+        _close(f"dWk[{h}]", T.to_host(dWk[h]), sums["dWk", h])
+        _close(f"dWg[{h}]", T.to_host(dWg[h]), sums["dWg", h])
+        _close(f"dbg[{h}]", T.to_host(dbg[h:h + 1]), np.array([sums["dbg", h]]))
+    if E is not None:
+        for i, n in enumerate(("dEt", "dEh", "dEw")):
+            _close(n, T.to_host(dE[i]), sums["dE", i])
+
+
 def test_backward_wan13b_sampled():
     """Full Wan2.1-1.3B shape: dq on sampled query blocks, dk, dv on sampled
     key blocks of two slices; dW_q, dW_k and the gate gradient of their heads
