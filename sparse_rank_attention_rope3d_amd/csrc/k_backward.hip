@@ -313,7 +313,8 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a, const int32_t* __r
 // dK, dV. Workgroup = one key block, BS/32 waves of 32 keys.
 template <int D, int BS>
 __global__ __launch_bounds__(BS * 2) void k_bwd_dkdv(BwdArgs a, const int32_t* __restrict__ inv_off,
-                                                   const int32_t* __restrict__ inv_list) {
+                                                   const int32_t* __restrict__ inv_list,
+                                                   const int32_t* __restrict__ order) {
     constexpr int KLD = D + 8, VLD = BS + 8, NQB = BS / 32, NS = D / 16, NDB = D / 32;
     __shared__ __attribute__((aligned(16))) uint16_t q_lds[BS * KLD];
     __shared__ __attribute__((aligned(16))) uint16_t do_lds[BS * KLD];
@@ -325,7 +326,8 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dkdv(BwdArgs a, const int32_t* _
     const int l32 = lane & 31, hf = lane >> 5;
     const long wid = xcd_remap(blockIdx.x, a.nwg);
     const long bh = wid / a.nblk;
-    const int jb = (int)(wid % a.nblk);
+    // key blocks of a slice run longest list first
+    const int jb = order ? __builtin_amdgcn_readfirstlane(order[bh * a.nblk + wid % a.nblk]) : (int)(wid % a.nblk);
     const long rows = (long)a.nblk * BS;
     const long L = a.L;
     const long key = (long)jb * BS + 32 * wave + l32;
@@ -697,6 +699,25 @@ __global__ __launch_bounds__(256) void k_inv_scan(const int32_t* __restrict__ cn
         run += cnt[bh * nblk + j];
     }
     if (tid == 255) o[nblk] = run;
+}
+
+// Order of the key blocks of a slice for the dK/dV kernel: longest query-block
+// list first (lists are skewed; the longest runs ~4x the mean), ties by index:
+// rank(j) = #{i : cnt_i > cnt_j} + #{i < j : cnt_i = cnt_j}, so order is a
+// deterministic permutation and each workgroup still computes one key block.
+__global__ __launch_bounds__(256) void k_inv_order(const int32_t* __restrict__ cnt, int nblk,
+                                                   int32_t* __restrict__ order) {
+    const long bh = blockIdx.y;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= nblk) return;
+    const int32_t* c = cnt + bh * nblk;
+    const int cj = c[j];
+    int rank = 0;
+    for (int i = 0; i < nblk; ++i) {
+        const int ci = c[i];
+        rank += (ci > cj || (ci == cj && i < j)) ? 1 : 0;
+    }
+    order[bh * nblk + rank] = j;
 }
 
 __global__ void k_inv_fill(const uint32_t* __restrict__ bits, const int32_t* __restrict__ off, long BH, int nblk,
@@ -1325,7 +1346,7 @@ hipError_t launch_bwd_e_sum(const float* dpre, long BH, long L, int T, int Hg, i
 }
 
 hipError_t launch_bwd_inverse(const int32_t* idx, long BH, int nblk, int keep, uint32_t* bits, int32_t* cnt,
-                              int32_t* off, int32_t* list, hipStream_t st) {
+                              int32_t* off, int32_t* list, int32_t* order, hipStream_t st) {
     const int W = (nblk + 31) / 32;
     const long nbits = BH * nblk * (long)W;
     hipLaunchKernelGGL(k_inv_zero, dim3(grid_for(nbits)), dim3(256), 0, st, bits, nbits);
@@ -1334,13 +1355,17 @@ hipError_t launch_bwd_inverse(const int32_t* idx, long BH, int nblk, int keep, u
     hipLaunchKernelGGL(k_inv_count, dim3(grid_for(BH * nblk)), dim3(256), 0, st, bits, BH * nblk, W, cnt);
     hipLaunchKernelGGL(k_inv_scan, dim3((unsigned)BH), dim3(256), 0, st, cnt, nblk, off);
     hipLaunchKernelGGL(k_inv_fill, dim3(grid_for(BH * nblk)), dim3(256), 0, st, bits, off, BH, nblk, keep, W, list);
+    if (order)
+        hipLaunchKernelGGL(k_inv_order, dim3((unsigned)((nblk + 255) / 256), (unsigned)BH), dim3(256), 0, st, cnt, nblk,
+                           order);
     return hipGetLastError();
 }
 
 template <int D, int BS>
 static hipError_t bwd_sparse_t(bool dkdv, const BwdArgs& a, hipStream_t st) {
     if (dkdv)
-        hipLaunchKernelGGL((k_bwd_dkdv<D, BS>), dim3((unsigned)a.nwg), dim3(BS * 2), 0, st, a, a.inv_off, a.inv_list);
+        hipLaunchKernelGGL((k_bwd_dkdv<D, BS>), dim3((unsigned)a.nwg), dim3(BS * 2), 0, st, a, a.inv_off, a.inv_list,
+                           a.order);
     else
         hipLaunchKernelGGL((k_bwd_dq<D, BS>), dim3((unsigned)a.nwg), dim3(BS * 2), 0, st, a, a.idx);
     return hipGetLastError();

@@ -156,7 +156,7 @@ int check_bwd_supported(const Dims& d, const slr_lowrank_cfg* lr) {
 struct Layout {
     size_t tab, qr, kr, kvt, qbar, kbar, scores, idx, wqt, wkt, part, S, z, sthi, stlo, zp, total;
     // backward
-    size_t lse, delta, dqlr, dklr, dvlr, lrpart, dsz, bits, cnt, off, list, dpre, epart, dosp, gpart;
+    size_t lse, delta, dqlr, dklr, dvlr, lrpart, dsz, bits, cnt, off, list, order, dpre, epart, dosp, gpart;
     bool tiled;
 };
 
@@ -225,6 +225,7 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         w.cnt = take(4ul * d.BH * nblk);
         w.off = take(4ul * d.BH * (nblk + 1));
         w.list = take(4ul * d.BH * nblk * keep);
+        w.order = take(4ul * d.BH * nblk);
         w.total = off;
         return w;
     }
@@ -683,8 +684,9 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     a.scale = (float)(1.0 / std::sqrt((double)d.D));
     a.nwg = d.BH * nblk;
     SLR_TRY(launch_bwd_dq(d.bf16, (int)d.D, bs, a, s));
+    a.order = at<int32_t>(ws, w.order);
     SLR_TRY(launch_bwd_inverse(idx, d.BH, nblk, keep, at<uint32_t>(ws, w.bits), at<int32_t>(ws, w.cnt),
-                               at<int32_t>(ws, w.off), at<int32_t>(ws, w.list), s));
+                               at<int32_t>(ws, w.off), at<int32_t>(ws, w.list), at<int32_t>(ws, w.order), s));
     SLR_TRY(launch_bwd_dkdv(d.bf16, (int)d.D, bs, a, s));
     return SLR_OK;
 }

@@ -17,6 +17,7 @@ struct BwdArgs {
     const int32_t* idx;        // [BH][nblk][keep] kept key blocks per query block
     const int32_t* inv_off;    // [BH][nblk + 1] query-block list offsets per key block
     const int32_t* inv_list;   // [BH][nblk * keep] query blocks keeping each key block, ascending
+    const int32_t* order;      // [BH][nblk] key blocks by list length, longest first (dK/dV launch order)
     const float* lse_in;       // [BH][L] the forward's log2 normalisers
     float* lse2;               // [BH][nblk*BS] the same, zero on padded rows
     float qmul;                // score (log2 units) = qmul * (q_rot . k_rot): log2(e)/sqrt(D), or 1
@@ -72,7 +73,7 @@ hipError_t launch_bwd_e_sum(const float* dpre, long BH, long L, int T, int Hg, i
                             hipStream_t st);
 // Inverse of the kept-block lists, deterministic: bits [BH][nblk][ceil(nblk/32)] scratch.
 hipError_t launch_bwd_inverse(const int32_t* idx, long BH, int nblk, int keep, uint32_t* bits, int32_t* cnt,
-                              int32_t* off, int32_t* list, hipStream_t st);
+                              int32_t* off, int32_t* list, int32_t* order, hipStream_t st);
 hipError_t launch_bwd_dq(int dtype_bf16, int D, int BS, const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_dkdv(int dtype_bf16, int D, int BS, const BwdArgs& a, hipStream_t st);
 
