@@ -765,7 +765,7 @@ __device__ __forceinline__ float round_bf(float x) { return bf2f(f2bf(x)); }
 // blocks per thread.
 template <int D, int R>
 struct LrTile {
-    static constexpr int TT = 32, XLD = D + 4, RW = R + 4, RLD = R + 4;
+    static constexpr int TT = 16, XLD = D + 4, RW = R + 4, RLD = R + 4;
     static constexpr int NBLK = D * R / 16;                  // 4x4 blocks of a [D][R] or [R][D] sum
     static constexpr int NB16 = (NBLK + 255) / 256;          // blocks per thread
 };
