@@ -172,6 +172,36 @@ def cpu_baseline(cfg, blocks: int):
     return layer_s, {"measured_s": round(t2 - t0, 2), "sampled_blocks": int(len(qblocks))}
 
 
+def cpu_backward_baseline(cfg, blocks: int):
+    """The oracle's backward (numpy fp64, BLAS held to one thread) on one
+    (b, h) slice: the whole low-rank backward plus the sparse backward of
+    `blocks` sampled query blocks (their dq and their keys' dk, dv), the
+    selection held as the oracle's, extrapolated linearly to the layer."""
+    import oracle
+    from oracle import backward as OB
+    from sparse_rank_attention_rope3d_amd import synth
+    from threadpoolctl import threadpool_limits
+    q, k, v = synth.qkv_slice(cfg, 0, 0)
+    p = synth.lowrank_params(cfg)
+    E = (p["et"], p["eh"], p["ew"]) if cfg.lr_mode == "abspe" else None
+    dout = np.asarray(synth.dout_slice(cfg, 0, 0), np.float64)
+    grid = (cfg.T, cfg.Hg, cfg.Wg)
+    qr = oracle.rope3d(q, grid, cfg.base, cfg.pairs)
+    kr = oracle.rope3d(k, grid, cfg.base, cfg.pairs)
+    idx, _, _ = oracle.topk_blocks(oracle.block_scores(oracle.block_mean(qr, cfg.block),
+                                                       oracle.block_mean(kr, cfg.block)), cfg.keep)
+    rng = np.random.default_rng([cfg.seed, synth.TID_SAMPLE, 0, 1])
+    qblocks = np.sort(rng.choice(cfg.nblk, size=min(blocks, cfg.nblk), replace=False))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        OB.lowrank_bwd(cfg, q, k, v, p["wq"][0], p["wk"][0], float(p["gate"][0]) * dout, E=E)
+        t1 = time.perf_counter()
+        OB.sparse_attention_bwd(qr, kr, v, cfg.block, idx, dout, qblocks=qblocks)
+        t2 = time.perf_counter()
+    per_slice = (t1 - t0) + (t2 - t1) * cfg.nblk / len(qblocks)
+    return per_slice * cfg.B * cfg.H, {"measured_s": round(t2 - t0, 2), "sampled_blocks": int(len(qblocks))}
+
+
 def _time_ms(torch, fn, reps):
     fn()
     torch.cuda.synchronize()
@@ -380,6 +410,15 @@ def main() -> int:
                     "algorithmic_flops": {"sparse": f_bsp, "lowrank": f_blr},
                     "training_forward_ms": round(fwd_train_ms, 3),
                     "training_step_ms": round(fwd_train_ms + bms, 3)}
+        if not args.no_cpu_baseline:
+            print("[bench] CPU oracle baseline of the backward", file=sys.stderr, flush=True)
+            bs_s, binfo = cpu_backward_baseline(cfg, max(1, args.cpu_blocks // 16))
+            backward["cpu_baseline"] = {
+                "value": (f_bsp + f_blr) / bs_s / 1e12, "unit": "TFLOP/s (algorithmic)", "cores": 1,
+                "kind": "oracle", "ms_per_layer": round(bs_s * 1e3, 1),
+                "sample": f"one (b,h) slice of {cfg.B * cfg.H}: the whole low-rank backward and the sparse backward "
+                          f"of {binfo['sampled_blocks']} of {cfg.nblk} query blocks, numpy fp64 with BLAS on one "
+                          f"thread, {binfo['measured_s']} s measured, extrapolated linearly to the layer"}
         del wsb, grads, saved, dout
 
     print("[bench] achievable GEMM and copy rates", file=sys.stderr, flush=True)
