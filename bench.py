@@ -236,6 +236,20 @@ def run_sweep(args, torch, B, synth):
         row = {"keep": cfg.keep, "keep_pct": round(100.0 * cfg.keep / cfg.nblk, 1), "rank": cfg.rank,
                "layer_ms": round(ms, 4), "dense_ms": round(dense_ms, 3), "speedup_vs_dense": round(dense_ms / ms, 2),
                "effective_tflops": round((F["sparse"] + F["lowrank"] + F["select"]) / (ms * 1e-3) / 1e12, 1)}
+        if args.bwd_reps > 0:
+            # the layer backward at this point (the training forward saves what it needs)
+            saved = B.slr_attention_fwd_train(q, k, v, shape, rope, sparse, lowrank, ws=ws)
+            wsb = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lowrank), "cuda")
+            dout = torch.ones_like(q)
+            grads = B.slr_attention_bwd(q, k, v, saved[1], saved[2], saved[3], dout, shape, rope, sparse, lowrank,
+                                        ws=wsb)
+            bms = _time_ms(torch, lambda: B.slr_attention_bwd(q, k, v, saved[1], saved[2], saved[3], dout, shape,
+                                                              rope, sparse, lowrank, ws=wsb, grads=grads),
+                           args.bwd_reps)
+            row["backward_ms"] = round(bms, 3)
+            row["backward_tflops"] = round((2.5 * F["sparse"] + 22.0 * cfg.B * cfg.H * cfg.L * cfg.D * cfg.rank)
+                                           / (bms * 1e-3) / 1e12, 1)
+            del saved, wsb, grads, dout
         rows.append(row)
         print(f"[sweep] {row}", file=sys.stderr, flush=True)
         del ws

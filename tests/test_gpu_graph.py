@@ -46,3 +46,52 @@ def test_layer_forward_replays_in_a_graph(gate):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, want), f"replay {rep} differs from the eager result"
+
+
+def test_training_step_replays_in_a_graph():
+    """The training forward and the backward capture together: the backward
+    allocates nothing either and clears its scratch with a kernel (no memset
+    nodes); every replay equals the eager gradients bit for bit."""
+    cfg = T.custom(synth.wan13b(), name="graph training step", B=1, H=2, T=4, Hg=9, Wg=13, keep=3)
+    inp = T.make_inputs(cfg)
+    dout = torch.empty_like(inp.q)
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            dout[b, h] = T.to_device(synth.dout_slice(cfg, b, h), cfg.dtype)
+    shape, rope, sparse = B.shape_of(cfg), B.rope_of(cfg), B.sparse_of(cfg)
+    lowrank = B.lowrank_of(cfg, inp.params)
+    wsf = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lowrank), "cuda")
+    wsb = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lowrank), "cuda")
+    saved = B.slr_attention_fwd_train(inp.q, inp.k, inp.v, shape, rope, sparse, lowrank, ws=wsf)
+    want = B.slr_attention_bwd(inp.q, inp.k, inp.v, saved[1], saved[2], saved[3], dout, shape, rope, sparse, lowrank,
+                               ws=wsb)
+    want = [t.clone() for t in want[:6]]
+    torch.cuda.synchronize()
+
+    outs = tuple(torch.empty_like(t) for t in saved)
+    grads = tuple(torch.empty_like(t) for t in want) + (None,)
+
+    def step():
+        B.slr_attention_fwd_train(inp.q, inp.k, inp.v, shape, rope, sparse, lowrank, ws=wsf, outs=outs)
+        B.slr_attention_bwd(inp.q, inp.k, inp.v, outs[1], outs[2], outs[3], dout, shape, rope, sparse, lowrank,
+                            ws=wsb, grads=grads)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in grads[:6]:
+            t.zero_()
+        wsb.fill_(0x5A)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, g, w in zip(("dq", "dk", "dv", "dWq", "dWk", "dgate"), grads[:6], want):
+            assert torch.equal(g, w), f"replay {rep}: {name} differs from the eager result"
