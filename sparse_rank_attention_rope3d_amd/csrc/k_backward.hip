@@ -310,6 +310,260 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a, const int32_t* __r
 }
 
 // ---------------------------------------------------------------------------
+// Streaming dQ for bf16, D = 128, 64-token blocks (every workload shape).
+//
+// Each key block has one contiguous 48 KB tile [K | V | K^T] in operand
+// order, written once per backward call (k_bwd_dq_tiles): every 1 KB chunk
+// is one wave's MFMA operand, lane l's 16 bytes at l * 16, so the LDS image
+// equals the memory image and direct global-to-LDS copies fill it.
+//   K chunk (kh, s):        lane l holds K[key 32kh + l%32][dims 16s + 8(l/32) .. +7]
+//   V chunk (kh, s):        lane l holds V[key 32kh + l%32][dims 16s + 8(l/32) .. +7]
+//   K^T chunk (kh, db, h2): lane l holds K[keys (slot16 order) 32kh + 16h2 + 8(l/32) .. +7][dim 32db + l%32]
+// Keys past L are zero (K from the zero-padded rotated copy).
+constexpr int kDqPart = 64 * 128;           // elements of one part
+constexpr int kDqTileElems = 3 * kDqPart;   // [K | V | K^T]
+
+__global__ __launch_bounds__(256) void k_bwd_dq_tiles(const uint16_t* __restrict__ kr, const uint16_t* __restrict__ v,
+                                                      long L, int nblk, uint16_t* __restrict__ tiles) {
+    constexpr int D = 128;
+    const int tid = threadIdx.x, blk = blockIdx.x;
+    const long bh = blockIdx.y;
+    const uint16_t* ks = kr + (bh * nblk + blk) * 64l * D;   // zero rows past L
+    const uint16_t* vs = v + bh * L * D;
+    uint16_t* t = tiles + (bh * nblk + blk) * (long)kDqTileElems;
+    // K and V parts: thread takes dims 8c .. 8c+7 of rows 16p + tid/16
+    {
+        const int c = tid & 15, rs = tid >> 4;
+        u32x4_t xk[4], xv[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int r = 16 * p + rs;
+            const long l = (long)blk * 64 + r;
+            xk[p] = ldg16(ks + (long)r * D + 8 * c);
+            const u32x4_t w = ldg16(vs + (l < L ? l : L - 1) * D + 8 * c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xv[p][i] = l < L ? w[i] : 0u;
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int r = 16 * p + rs;
+            const int o = (((r >> 5) * 8 + (c >> 1)) * 64 + (r & 31) + 32 * (c & 1)) * 8;
+            stg16(t + o, xk[p]);
+            stg16(t + kDqPart + o, xv[p]);
+        }
+    }
+    // K^T part: thread tid < 128 takes 8 keys (slots 8vh .. 8vh+7 of 16-key
+    // group vG) x 8 dims and transposes them in registers (threads 128..255
+    // repeat the loads of tid - 128, served by the caches, and store nothing)
+    const int vc = tid & 15, vg = (tid >> 4) & 7, vG = vg >> 1, vh = vg & 1;
+    uint32_t rows[8][4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const u32x4_t w = ldg16(ks + (long)(16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2)) * D + 8 * vc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rows[e][i] = w[i];
+    }
+    if (tid >= 128) return;
+    uint16_t* kt = t + 2 * kDqPart;
+    const int kh = vG >> 1, h2 = vG & 1;
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        u32x4_t o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t a0 = rows[2 * i][f >> 1], a1 = rows[2 * i + 1][f >> 1];
+            o[i] = (f & 1) ? __builtin_amdgcn_perm(a1, a0, 0x07060302u) : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+        }
+        const int d = 8 * vc + f;
+        stg16(kt + ((kh * 8 + (d >> 5) * 2 + h2) * 64 + (d & 31) + 32 * vh) * 8, o);
+    }
+}
+
+// Eight 16-byte LDS reads 1 KB apart (one operand chunk each); the block
+// waits for its own reads (early-clobber outputs: no destination can alias
+// the address register).
+__device__ __forceinline__ void lds_read8k(u32x4_t* r, const uint16_t* base) { lds_read8x<1024, 2048>(r, base); }
+
+// Workgroup = 4 waves = one 64-row query block; wave (rh, kh) owns query rows
+// 32rh .. and keys 32kh .. of every kept tile: S^T = K Q^T and dP^T = V dO^T
+// (a lane owns one query row), dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.
+// The parts stream through LDS (80 KB: two workgroups per CU): K and V in
+// two-slot rings requested one tile ahead, K^T in one slot refilled as soon
+// as every wave has read it, and waited for only just before its reads (three
+// barriers per tile). The two key halves' dQ^T are added through LDS at the
+// end. The tiled path scores with q pre-multiplied by log2(e)/sqrt(D), so
+// p = exp2(score - lse2).
+__global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* __restrict__ idx_all,
+                                                      const uint16_t* __restrict__ tiles_all) {
+    constexpr int D = 128, BS = 64, PART = kDqPart, PLOADS = PART * 2 / (256 * 16);
+    __shared__ __attribute__((aligned(16))) uint16_t lds[5 * PART];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rh = wave & 1, kh = wave >> 1;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const long wid = xcd_remap(blockIdx.x, a.nwg);
+    const int nblk = a.nblk;
+    const long bh = wid / nblk;
+    const int qb = (int)(wid % nblk);
+    const long rows = (long)nblk * BS;
+    const long L = a.L;
+    const long qrow = (long)qb * BS + 32 * rh + l32;
+    const bool qval = qrow < L;
+    const uint16_t* tiles = tiles_all + bh * (long)nblk * kDqTileElems + (long)tid * 8;
+    const int32_t* ix = idx_all + (bh * nblk + qb) * (long)a.keep;
+    const int ntile = a.keep;
+
+    // B operands: rotated (scaled) q row and dO row (dims 16s + 8hf + e); delta = dO . O
+    u32x4_t qop[8], doop[8];
+    float dl = 0.f;
+    {
+        const uint16_t* qp = a.qr + (bh * rows + qrow) * D + 8 * hf;
+        const long orow = bh * L + (qval ? qrow : 0);
+        const uint16_t* dp = a.dout + orow * D + 8 * hf;
+        const uint16_t* op = a.o_sp + orow * D + 8 * hf;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            qop[s] = ldg16(qp + 16 * s);
+            const u32x4_t dd = ldg16(dp + 16 * s);
+            const u32x4_t o = ldg16(op + 16 * s);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                doop[s][i] = qval ? dd[i] : 0u;
+                dl += bf_lo(doop[s][i]) * bf_lo(o[i]) + bf_hi(doop[s][i]) * bf_hi(o[i]);
+            }
+        }
+    }
+    dl = sum_xor32(dl);
+    const float lse2 = qval ? a.lse_in[bh * L + (qval ? qrow : 0)] : 0.f;
+    wait_vmcnt<0>();
+    // the row statistics, zero on padded rows, for the key-side kernel
+    if (kh == 0 && hf == 0) {
+        a.lse2[bh * rows + qrow] = lse2;
+        a.delta[bh * rows + qrow] = qval ? dl : 0.f;
+    }
+
+    // entries outside [0, nblk) contribute nothing (their slot streams tile 0)
+    auto tile_of = [&](int n) -> int {
+        const int j = ix[n];
+        return (unsigned)j < (unsigned)nblk ? j : 0;
+    };
+    auto issue = [&](int j, int part, uint16_t* dst) {
+        const uint16_t* src = tiles + (long)j * kDqTileElems + part * PART;
+#pragma unroll
+        for (int m = 0; m < PLOADS; ++m)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(src + m * 256 * 8),
+                (__attribute__((address_space(3))) void*)(dst + (m * 256 + wave * 64) * 8), 16, 0, 0);
+    };
+    const int rd = ((kh * 8) * 64 + lane) * 8;   // this lane's chunks (kh, 0..7) within a part
+    const bool ragged = (L % BS) != 0;
+    uint16_t* kt_slot = lds + 4 * PART;
+
+    f32x16_t dqacc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
+
+    // K and V of tile t in slots t % 2 (K: parts 0, 1; V: parts 2, 3), K^T in
+    // part 4. Issue order: KT0 K0 V0, then per tile t: K(t+1) V(t+1) after the
+    // opening barrier (into the slots of tile t - 1, which it certifies as
+    // consumed), KT(t+1) after the barrier that follows every wave's K^T reads;
+    // so from tile 1 on the sequence is ..., K(t) V(t) KT(t) K(t+1) V(t+1) ...
+    if (ntile > 0) {
+        const int j0 = tile_of(0);
+        issue(j0, 2, kt_slot);
+        issue(j0, 0, lds);
+        issue(j0, 1, lds + 2 * PART);
+    }
+    for (int t = 0; t < ntile; ++t) {
+        const int jraw = ix[t];
+        const bool jok = (unsigned)jraw < (unsigned)nblk;
+        const int sl = t & 1;
+        // K(t), V(t) landed; from tile 1 on, KT(t) (issued after them) may still be in flight
+        if (t > 0) wait_vmcnt<PLOADS>(); else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (t + 1 < ntile) {
+            const int j1 = tile_of(t + 1);
+            issue(j1, 0, lds + (sl ^ 1) * PART);
+            issue(j1, 1, lds + (2 + (sl ^ 1)) * PART);
+        }
+        f32x16_t sacc, dpacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; dpacc[i] = 0.f; }
+        u32x4_t op[8];
+        lds_read8k(op, lds + sl * PART + rd);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) sacc = mfma32(op[s], qop[s], sacc);
+        u32x4_t vop[8];
+        lds_read8k(vop, lds + (2 + sl) * PART + rd);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) dpacc = mfma32(vop[s], doop[s], dpacc);
+        const long key0 = (long)jraw * BS + 32 * kh + 4 * hf;
+        float ds[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const bool off = !jok || (ragged && key0 + 8 * (i >> 2) + (i & 3) >= L);
+            ds[i] = off ? 0.f : exp2f(sacc[i] - lse2) * (dpacc[i] - dl);
+        }
+        u32x4_t dsop[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dsop[h2][i] = pack_bf2(ds[8 * h2 + 2 * i], ds[8 * h2 + 2 * i + 1]);
+        u32x4_t at[8];   // K^T chunks (kh, db, h2) = (kh, i / 2, i % 2)
+        if (t > 0) {
+            // outstanding in issue order: ..., KT(t), K(t+1), V(t+1) (the last two only if t + 1 < ntile)
+            if (t + 1 < ntile) wait_vmcnt<2 * PLOADS>(); else wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+        }
+        lds_read8k(at, kt_slot + rd);
+        __builtin_amdgcn_s_barrier();   // every wave has its K^T operands: refill the slot
+        if (t + 1 < ntile) issue(tile_of(t + 1), 2, kt_slot);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dqacc[i >> 1] = mfma32(at[i], dsop[i & 1], dqacc[i >> 1]);
+    }
+
+    // ---- add the key halves through LDS (no copy is in flight: the last tile waited for all)
+    __syncthreads();
+    float* mrg = reinterpret_cast<float*>(lds) + rh * (64 * 64);
+    if (kh == 1) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mrg[(16 * db + i) * 64 + lane] = dqacc[db][i];
+    }
+    __syncthreads();
+    if (kh == 1 || !qval) return;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dqacc[db][i] += mrg[(16 * db + i) * 64 + lane];
+
+    // ---- epilogue: dq = R^T (dQ_rot / sqrt(D)) + dq_lowrank; lane owns row qrow,
+    // dims 32db + 8g4 + 4hf + 0..3
+    int crd[3];
+    token_coords(qrow, a.g.Hg, a.g.Wg, crd[0], crd[1], crd[2]);
+    const float* lr = a.dq_lr + (bh * L + qrow) * D;
+    uint16_t* out = a.dq + (bh * L + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int d0 = 32 * db + 8 * g4 + 4 * hf;
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = dqacc[db][4 * g4 + i] * a.scale;
+            rot_t(y[0], y[1], rope_cs(a.tab, a.g, d0 >> 1, crd));
+            rot_t(y[2], y[3], rope_cs(a.tab, a.g, (d0 >> 1) + 1, crd));
+            const float4 l4 = *reinterpret_cast<const float4*>(lr + d0);
+            *reinterpret_cast<u32x2_t*>(out + d0) =
+                u32x2_t{pack_bf2(y[0] + l4.x, y[1] + l4.y), pack_bf2(y[2] + l4.z, y[3] + l4.w)};
+        }
+}
+
+// ---------------------------------------------------------------------------
 // dK, dV. Workgroup = one key block, BS/32 waves of 32 keys.
 template <int D, int BS>
 __global__ __launch_bounds__(BS * 2) void k_bwd_dkdv(BwdArgs a, const int32_t* __restrict__ inv_off,
@@ -1376,7 +1630,17 @@ static hipError_t bwd_sparse(int D, int BS, bool dkdv, const BwdArgs& a, hipStre
     return BS == 64 ? bwd_sparse_t<64, 64>(dkdv, a, st) : bwd_sparse_t<64, 32>(dkdv, a, st);
 }
 
+hipError_t launch_bwd_dq_tiles(const uint16_t* kr, const uint16_t* v, long BH, long L, int nblk, uint16_t* tiles,
+                               hipStream_t st) {
+    hipLaunchKernelGGL(k_bwd_dq_tiles, dim3((unsigned)nblk, (unsigned)BH), dim3(256), 0, st, kr, v, L, nblk, tiles);
+    return hipGetLastError();
+}
+
 hipError_t launch_bwd_dq(int dtype_bf16, int D, int BS, const BwdArgs& a, hipStream_t st) {
+    if (dtype_bf16 && D == 128 && BS == 64 && a.dqt) {
+        hipLaunchKernelGGL(k_bwd_dq_tiled, dim3((unsigned)a.nwg), dim3(256), 0, st, a, a.idx, a.dqt);
+        return hipGetLastError();
+    }
     if (dtype_bf16) return bwd_sparse(D, BS, false, a, st);
     if (D == 64)
         hipLaunchKernelGGL((k_bwd_dq_f32<64>), dim3((unsigned)a.nwg), dim3(256), 0, st, a, a.idx, BS);

@@ -156,7 +156,7 @@ int check_bwd_supported(const Dims& d, const slr_lowrank_cfg* lr) {
 struct Layout {
     size_t tab, qr, kr, kvt, qbar, kbar, scores, idx, wqt, wkt, part, S, z, sthi, stlo, zp, total;
     // backward
-    size_t lse, delta, dqlr, dklr, dvlr, lrpart, dsz, bits, cnt, off, list, order, dpre, epart, dosp, gpart;
+    size_t lse, delta, dqlr, dklr, dvlr, lrpart, dsz, bits, cnt, off, list, order, dpre, epart, dosp, gpart, dqt;
     bool tiled;
 };
 
@@ -226,6 +226,7 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         w.off = take(4ul * d.BH * (nblk + 1));
         w.list = take(4ul * d.BH * nblk * keep);
         w.order = take(4ul * d.BH * nblk);
+        if (use_tiles(d, bs)) w.dqt = take(2ul * d.BH * nblk * 3 * 64 * 128);
         w.total = off;
         return w;
     }
@@ -683,6 +684,11 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     a.tab = tab; a.g = g; a.L = d.L; a.nblk = nblk; a.keep = keep;
     a.scale = (float)(1.0 / std::sqrt((double)d.D));
     a.nwg = d.BH * nblk;
+    if (tiled_fwd) {
+        uint16_t* dqt = at<uint16_t>(ws, w.dqt);
+        SLR_TRY(launch_bwd_dq_tiles(kr, (const uint16_t*)v, d.BH, d.L, nblk, dqt, s));
+        a.dqt = dqt;
+    }
     SLR_TRY(launch_bwd_dq(d.bf16, (int)d.D, bs, a, s));
     a.order = at<int32_t>(ws, w.order);
     SLR_TRY(launch_bwd_inverse(idx, d.BH, nblk, keep, at<uint32_t>(ws, w.bits), at<int32_t>(ws, w.cnt),

@@ -18,6 +18,8 @@ struct BwdArgs {
     const int32_t* inv_off;    // [BH][nblk + 1] query-block list offsets per key block
     const int32_t* inv_list;   // [BH][nblk * keep] query blocks keeping each key block, ascending
     const int32_t* order;      // [BH][nblk] key blocks by list length, longest first (dK/dV launch order)
+    const uint16_t* dqt;       // bf16, D = 128, 64-token blocks: [BH][nblk][K | V | K^T] 48 KB operand-order
+                               // tiles of the streaming dQ kernel (null: the staging kernel)
     const float* lse_in;       // [BH][L] the forward's log2 normalisers
     float* lse2;               // [BH][nblk*BS] the same, zero on padded rows
     float qmul;                // score (log2 units) = qmul * (q_rot . k_rot): log2(e)/sqrt(D), or 1
@@ -74,6 +76,10 @@ hipError_t launch_bwd_e_sum(const float* dpre, long BH, long L, int T, int Hg, i
 // Inverse of the kept-block lists, deterministic: bits [BH][nblk][ceil(nblk/32)] scratch.
 hipError_t launch_bwd_inverse(const int32_t* idx, long BH, int nblk, int keep, uint32_t* bits, int32_t* cnt,
                               int32_t* off, int32_t* list, int32_t* order, hipStream_t st);
+// [K | V | K^T] operand-order tiles of every key block for the streaming dQ kernel, from the
+// zero-padded rotated k copy kr [BH][nblk*64][128] and v [BH][L][128] (bf16); grid (nblk, BH).
+hipError_t launch_bwd_dq_tiles(const uint16_t* kr, const uint16_t* v, long BH, long L, int nblk, uint16_t* tiles,
+                               hipStream_t st);
 hipError_t launch_bwd_dq(int dtype_bf16, int D, int BS, const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_dkdv(int dtype_bf16, int D, int BS, const BwdArgs& a, hipStream_t st);
 

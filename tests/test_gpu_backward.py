@@ -262,3 +262,43 @@ def test_backward_is_deterministic():
     _, _, g2, _ = _run_gpu(cfg)
     for a, b in zip(g1[:6], g2[:6]):
         assert torch.equal(a, b)
+
+
+def test_backward_skips_entries_outside_range():
+    """Kept-list entries outside [0, nblk) are skipped: with -1, nblk and -7
+    written over entries of three rows, and the normalisers and O_sparse of
+    the reduced lists (from the oracle) passed in, every gradient equals the
+    oracle's layer backward on the reduced lists."""
+    cfg = dataclasses.replace(synth.wan13b(), name="bwd skipped entries", B=1, H=1, T=4, Hg=9, Wg=13, keep=3)
+    _dtype[0] = cfg.dtype
+    inp = T.make_inputs(cfg)
+    dout = _dout(cfg)
+    shape, rope, sparse = B.shape_of(cfg), B.rope_of(cfg), B.sparse_of(cfg)
+    lowrank = B.lowrank_of(cfg, inp.params)
+    _, idx, _, _ = B.slr_attention_fwd_train(inp.q, inp.k, inp.v, shape, rope, sparse, lowrank)
+    ig = idx[0, 0].cpu().numpy().copy()
+    nblk = cfg.nblk
+    ig[1, 0], ig[4, 2], ig[nblk - 1, 1] = -1, nblk, -7
+    red = np.empty(nblk, dtype=object)
+    for i in range(nblk):
+        red[i] = ig[i][(ig[i] >= 0) & (ig[i] < nblk)]
+    qs, ks, vs = synth.qkv_slice(cfg, 0, 0)
+    grid = (cfg.T, cfg.Hg, cfg.Wg)
+    qr = oracle.rope3d(np.asarray(qs, np.float64), grid, cfg.base, cfg.pairs)
+    kr = oracle.rope3d(np.asarray(ks, np.float64), grid, cfg.base, cfg.pairs)
+    o = np.concatenate([oracle.block_sparse_attention(qr, kr, vs, cfg.block, np.tile(red[i], (nblk, 1)), qblocks=[i])[0]
+                        for i in range(nblk)])[: cfg.L]
+    o_dev = T.to_device(o, cfg.dtype).reshape(1, 1, cfg.L, cfg.D)
+    lse = torch.tensor(OB.row_log2_normaliser(qr, kr, cfg.block, red), dtype=torch.float32, device="cuda")
+    idx_dev = torch.tensor(ig, dtype=torch.int32, device="cuda").reshape(1, 1, nblk, cfg.keep)
+    dq, dk, dv, dWq, dWk, dg, _ = B.slr_attention_bwd(inp.q, inp.k, inp.v, idx_dev, o_dev, lse.reshape(1, 1, cfg.L),
+                                                      dout, shape, rope, sparse, lowrank)
+    torch.cuda.synchronize()
+    p = inp.params_np
+    ds = np.asarray(synth.dout_slice(cfg, 0, 0), np.float64)
+    ref = OB.layer_slice_bwd(cfg, qs, ks, vs, p["wq"][0], p["wk"][0], float(p["gate"][0]), ds, idx=red,
+                             o_sp=T.to_host(o_dev[0, 0]))
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _close(n, T.to_host(t[0, 0]), ref[n])
+    _close("dWq", T.to_host(dWq[0]), ref["dWq"])
+    _close("dgate", T.to_host(dg[0:1]), np.array([ref["dg"]]))
