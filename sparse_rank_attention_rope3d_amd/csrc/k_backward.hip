@@ -313,7 +313,7 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a, const int32_t* __r
 // Streaming dQ for bf16, D = 128, 64-token blocks (every workload shape).
 //
 // Each key block has one contiguous 48 KB tile [K | V | K^T] in operand
-// order, written once per backward call (k_bwd_dq_tiles): every 1 KB chunk
+// order, written once per backward call (k_bwd_tiles): every 1 KB chunk
 // is one wave's MFMA operand, lane l's 16 bytes at l * 16, so the LDS image
 // equals the memory image and direct global-to-LDS copies fill it.
 //   K chunk (kh, s):        lane l holds K[key 32kh + l%32][dims 16s + 8(l/32) .. +7]
@@ -322,49 +322,72 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a, const int32_t* __r
 // Keys past L are zero (K from the zero-padded rotated copy).
 constexpr int kDqPart = 64 * 128;           // elements of one part
 constexpr int kDqTileElems = 3 * kDqPart;   // [K | V | K^T]
+// Query-side tiles of the streaming dK/dV kernel: [Q | dO | Q^T | dO^T | stats]
+// per query block, the same chunk layouts with query rows in place of keys;
+// stats = 2 KB of floats: the rows' log2 normalisers [64], delta = dO . O
+// [64], zeros [384] (one 4-byte copy per lane of each of eight waves).
+constexpr int kQtStatsElems = 1024;
+constexpr int kQtTileElems = 4 * kDqPart + kQtStatsElems;
 
-__global__ __launch_bounds__(256) void k_bwd_dq_tiles(const uint16_t* __restrict__ kr, const uint16_t* __restrict__ v,
-                                                      long L, int nblk, uint16_t* __restrict__ tiles) {
+// One tile [A | B | A^T (| B^T) (| stats)] per 64-row block, from A rows that
+// are zero-padded to whole blocks (rotated k or q) and B rows [L] (v or dO,
+// rows past L read as zero). Grid (nblk, BH).
+template <bool BT>
+__global__ __launch_bounds__(256) void k_bwd_tiles(const uint16_t* __restrict__ a_rows, const uint16_t* __restrict__ b_rows,
+                                                   long L, int nblk, const float* __restrict__ lse2,
+                                                   const float* __restrict__ delta, uint16_t* __restrict__ tiles,
+                                                   long tile_elems) {
     constexpr int D = 128;
     const int tid = threadIdx.x, blk = blockIdx.x;
     const long bh = blockIdx.y;
-    const uint16_t* ks = kr + (bh * nblk + blk) * 64l * D;   // zero rows past L
-    const uint16_t* vs = v + bh * L * D;
-    uint16_t* t = tiles + (bh * nblk + blk) * (long)kDqTileElems;
-    // K and V parts: thread takes dims 8c .. 8c+7 of rows 16p + tid/16
+    const uint16_t* as = a_rows + (bh * nblk + blk) * 64l * D;   // zero rows past L
+    const uint16_t* bs = b_rows + bh * L * D;
+    uint16_t* t = tiles + (bh * nblk + blk) * tile_elems;
+    // A and B parts: thread takes dims 8c .. 8c+7 of rows 16p + tid/16
     {
         const int c = tid & 15, rs = tid >> 4;
-        u32x4_t xk[4], xv[4];
+        u32x4_t xa[4], xb[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int r = 16 * p + rs;
             const long l = (long)blk * 64 + r;
-            xk[p] = ldg16(ks + (long)r * D + 8 * c);
-            const u32x4_t w = ldg16(vs + (l < L ? l : L - 1) * D + 8 * c);
+            xa[p] = ldg16(as + (long)r * D + 8 * c);
+            const u32x4_t w = ldg16(bs + (l < L ? l : L - 1) * D + 8 * c);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xv[p][i] = l < L ? w[i] : 0u;
+            for (int i = 0; i < 4; ++i) xb[p][i] = l < L ? w[i] : 0u;
         }
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int r = 16 * p + rs;
             const int o = (((r >> 5) * 8 + (c >> 1)) * 64 + (r & 31) + 32 * (c & 1)) * 8;
-            stg16(t + o, xk[p]);
-            stg16(t + kDqPart + o, xv[p]);
+            stg16(t + o, xa[p]);
+            stg16(t + kDqPart + o, xb[p]);
         }
     }
-    // K^T part: thread tid < 128 takes 8 keys (slots 8vh .. 8vh+7 of 16-key
-    // group vG) x 8 dims and transposes them in registers (threads 128..255
-    // repeat the loads of tid - 128, served by the caches, and store nothing)
-    const int vc = tid & 15, vg = (tid >> 4) & 7, vG = vg >> 1, vh = vg & 1;
+    // A^T part (threads 0..127) and B^T part (threads 128..255, when BT): a
+    // thread takes 8 rows (slots 8vh .. 8vh+7 of 16-row group vG) x 8 dims
+    // and transposes them in registers
+    const int u = tid & 127;
+    const int vc = u & 15, vg = (u >> 4) & 7, vG = vg >> 1, vh = vg & 1;
+    const bool second = tid >= 128;
+    if (second && !BT) return;
     uint32_t rows[8][4];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const u32x4_t w = ldg16(ks + (long)(16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2)) * D + 8 * vc);
+        const int r = 16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2);
+        const long l = (long)blk * 64 + r;
+        u32x4_t w;
+        if (second) {
+            w = ldg16(bs + (l < L ? l : L - 1) * D + 8 * vc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = l < L ? w[i] : 0u;
+        } else {
+            w = ldg16(as + (long)r * D + 8 * vc);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) rows[e][i] = w[i];
     }
-    if (tid >= 128) return;
-    uint16_t* kt = t + 2 * kDqPart;
+    uint16_t* tt = t + (second ? 3 : 2) * kDqPart;
     const int kh = vG >> 1, h2 = vG & 1;
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
@@ -375,7 +398,14 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiles(const uint16_t* __restrict
             o[i] = (f & 1) ? __builtin_amdgcn_perm(a1, a0, 0x07060302u) : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
         }
         const int d = 8 * vc + f;
-        stg16(kt + ((kh * 8 + (d >> 5) * 2 + h2) * 64 + (d & 31) + 32 * vh) * 8, o);
+        stg16(tt + ((kh * 8 + (d >> 5) * 2 + h2) * 64 + (d & 31) + 32 * vh) * 8, o);
+    }
+    if (BT && tid < 128) {
+        // stats: [lse2 | delta | zeros] of the block's 64 rows (padded rows hold zeros)
+        float* st = reinterpret_cast<float*>(t + 4 * kDqPart);
+        const long r0 = (bh * nblk + blk) * 64l;
+        for (int e = tid; e < 512; e += 128)
+            st[e] = e < 64 ? lse2[r0 + e] : (e < 128 ? delta[r0 + e - 64] : 0.f);
     }
 }
 
@@ -560,6 +590,241 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* 
             const float4 l4 = *reinterpret_cast<const float4*>(lr + d0);
             *reinterpret_cast<u32x2_t*>(out + d0) =
                 u32x2_t{pack_bf2(y[0] + l4.x, y[1] + l4.y), pack_bf2(y[2] + l4.z, y[3] + l4.w)};
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming dK, dV for bf16, D = 128, 64-token blocks. Workgroup = 8 waves =
+// one 64-key block; waves 0..3 accumulate dV^T, waves 4..7 dK^T, and wave
+// w & 3 = (kw, qh) takes keys 32kw .. and query rows 32qh .. of every query
+// block that keeps the key block. A lane owns one key, register e of an
+// accumulator the row 32qh + 8(e/4) + 4hf + e%4. The dV wave computes
+// S = Q K^T and P, passes P (fp32) to the dK wave of the same (kw, qh)
+// through LDS and adds dO^T P; the dK wave meanwhile computes dP = dO V^T,
+// then dS = P (dP - delta), and adds Q^T dS: 16 MFMAs per wave per tile.
+// Waves w and w + 4 share a SIMD, one of each role (two waves per SIMD). The query-side tiles [Q | dO | Q^T | dO^T | stats] stream through
+// LDS (134 KB): Q, dO and the row statistics in a three-slot ring requested
+// two tiles ahead, Q^T and dO^T in one slot refilled as soon as every wave
+// has read it and waited for only just before those reads (three barriers
+// per tile); the query halves' partial sums are added through LDS at the end.
+template <int ROLE>
+__device__ __forceinline__ void dkdv_tiled_loop(const BwdArgs& a, uint16_t* lds, const uint16_t* qt,
+                                                const int32_t* list, int n0, int n1, int tid, int wave, int lane,
+                                                int qh, int hf, const u32x4_t* op, float* pex,
+                                                f32x16_t* acc) {
+    constexpr int PART = kDqPart, TILE = kQtTileElems, PL = PART * 2 / (512 * 16);
+    constexpr int FSZ = 2 * PART + kQtStatsElems;   // first-use group in LDS: [Q | dO | stats]
+    constexpr int NF = 2 * PL + 1, NT = 2 * PL;     // copies per lane of the two groups
+    // First-use group of tile i -> F slot: Q, dO (two 16-byte copies per lane
+    // each) and the 2 KB of row statistics (one 4-byte copy per lane)
+    auto issue_f = [&](int i, uint16_t* slot) {
+        const uint16_t* src = qt + (long)i * TILE;
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int m = 0; m < PL; ++m)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(src + p * PART + (m * 512 + tid) * 8),
+                    (__attribute__((address_space(3))) void*)(slot + p * PART + (m * 512 + wave * 64) * 8), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 4 * PART + tid * 2),
+                                         (__attribute__((address_space(3))) void*)(slot + 2 * PART + wave * 128), 4,
+                                         0, 0);
+    };
+    // Transposed group [Q^T | dO^T] of tile i -> the T slot
+    uint16_t* tslot = lds + 3 * FSZ;
+    auto issue_t = [&](int i) {
+        const uint16_t* src = qt + (long)i * TILE + 2 * PART;
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int m = 0; m < PL; ++m)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(src + p * PART + (m * 512 + tid) * 8),
+                    (__attribute__((address_space(3))) void*)(tslot + p * PART + (m * 512 + wave * 64) * 8), 16, 0,
+                    0);
+    };
+    auto qblock = [&](int n) { return __builtin_amdgcn_readfirstlane(list[n]); };
+    const int rd = ((qh * 8) * 64 + lane) * 8;   // this lane's chunks (qh, 0..7) within a part
+    const int ntile = n1 - n0;
+    // F of tile t in F slot t % 3, T in the T slot. Issue order: T0 F0 F1,
+    // then per tile t: F(t+2) after the opening barrier (into the slot of
+    // tile t - 1, which it certifies as consumed), T(t+1) after the barrier
+    // that follows every wave's reads of T(t); so from tile 1 on the sequence
+    // is ..., F(t+1) T(t) F(t+2) T(t+1) ...
+    if (ntile > 0) {
+        issue_t(qblock(n0));
+        issue_f(qblock(n0), lds);
+    }
+    if (ntile > 1) issue_f(qblock(n0 + 1), lds + FSZ);
+    int fs = 0;   // F slot of tile t
+    for (int t = 0; t < ntile; ++t) {
+        // F(t) landed (tile 0: everything issued so far)
+        if (t == 0) wait_vmcnt<0>();
+        else if (t + 1 < ntile) wait_vmcnt<NF + NT>();
+        else wait_vmcnt<NT>();
+        __builtin_amdgcn_s_barrier();
+        if (t + 2 < ntile) issue_f(qblock(n0 + t + 2), lds + (fs == 0 ? 2 : fs - 1) * FSZ);
+        const uint16_t* cur = lds + fs * FSZ;
+        fs = fs == 2 ? 0 : fs + 1;
+        const float* st = reinterpret_cast<const float*>(cur + 2 * PART) + 32 * qh + 4 * hf;
+        // dV waves: S = Q K^T and P, handed to the dK wave of the same (kw, qh)
+        // through LDS; dK waves meanwhile: dP = dO V^T
+        f32x16_t sacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+        u32x4_t aq[8];
+        lds_read8k(aq, cur + (ROLE == 0 ? 0 : PART) + rd);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) sacc = mfma32(aq[s], op[s], sacc);
+        u32x4_t bop[2];   // P (dV waves) or dS (dK waves): the keys' B operand of the second product
+        if constexpr (ROLE == 0) {
+            float p[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 l4 = *reinterpret_cast<const float4*>(st + 8 * g);
+                p[4 * g + 0] = exp2f(sacc[4 * g + 0] * a.qmul - l4.x);
+                p[4 * g + 1] = exp2f(sacc[4 * g + 1] * a.qmul - l4.y);
+                p[4 * g + 2] = exp2f(sacc[4 * g + 2] * a.qmul - l4.z);
+                p[4 * g + 3] = exp2f(sacc[4 * g + 3] * a.qmul - l4.w);
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) pex[e * 64 + lane] = p[e];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bop[h2][e] = pack_bf2(p[8 * h2 + 2 * e], p[8 * h2 + 2 * e + 1]);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // P stored before the barrier below
+        }
+        // T(t) landed (outstanding in issue order ..., T(t), F(t+2), the last only if
+        // t + 2 < ntile; tile 0 waited for everything) and P is in LDS
+        if (t > 0) {
+            if (t + 2 < ntile) wait_vmcnt<NF>(); else wait_vmcnt<0>();
+        }
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if constexpr (ROLE == 1) {
+            float ds[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 d4 = *reinterpret_cast<const float4*>(st + 64 + 8 * g);
+                ds[4 * g + 0] = pex[(4 * g + 0) * 64 + lane] * (sacc[4 * g + 0] - d4.x);
+                ds[4 * g + 1] = pex[(4 * g + 1) * 64 + lane] * (sacc[4 * g + 1] - d4.y);
+                ds[4 * g + 2] = pex[(4 * g + 2) * 64 + lane] * (sacc[4 * g + 2] - d4.z);
+                ds[4 * g + 3] = pex[(4 * g + 3) * 64 + lane] * (sacc[4 * g + 3] - d4.w);
+            }
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bop[h2][e] = pack_bf2(ds[8 * h2 + 2 * e], ds[8 * h2 + 2 * e + 1]);
+        }
+        u32x4_t at[8];   // dO^T (dV waves) or Q^T (dK waves) chunks (qh, db, h2) = (qh, i / 2, i % 2)
+        lds_read8k(at, tslot + (ROLE == 0 ? PART : 0) + rd);
+        // every wave has its transposed operands (and the dK waves their P): refill the slot
+        __builtin_amdgcn_s_barrier();
+        if (t + 1 < ntile) issue_t(qblock(n0 + t + 1));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i >> 1] = mfma32(at[i], bop[i & 1], acc[i >> 1]);
+    }
+}
+
+__global__ __launch_bounds__(512) void k_bwd_dkdv_tiled(BwdArgs a, const int32_t* __restrict__ inv_off,
+                                                        const int32_t* __restrict__ inv_list,
+                                                        const int32_t* __restrict__ order,
+                                                        const uint16_t* __restrict__ qt_all) {
+    constexpr int D = 128, BS = 64, TILE = kQtTileElems;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[3 * (2 * kDqPart + kQtStatsElems) + 2 * kDqPart];
+    __shared__ float pex_all[4][16 * 64];   // P of each (kw, qh), from the dV wave to the dK wave
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int role = wave >> 2, kw = wave & 1, qh = (wave >> 1) & 1;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const long wid = xcd_remap(blockIdx.x, a.nwg);
+    const int nblk = a.nblk;
+    const long bh = wid / nblk;
+    // key blocks of a slice run longest list first
+    const int jb = __builtin_amdgcn_readfirstlane(order[bh * nblk + wid % nblk]);
+    const long rows = (long)nblk * BS;
+    const long L = a.L;
+    const long key = (long)jb * BS + 32 * kw + l32;
+    const bool kval = key < L;
+    const uint16_t* qt = qt_all + bh * (long)nblk * TILE;
+    const int32_t* off = inv_off + bh * (long)(nblk + 1);
+    const int32_t* list = inv_list + bh * (long)nblk * a.keep;
+    const int n0 = __builtin_amdgcn_readfirstlane(off[jb]), n1 = __builtin_amdgcn_readfirstlane(off[jb + 1]);
+
+    f32x16_t acc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+    // B operand of the first product: rotated k row of this lane's key (dV
+    // waves: S = Q K^T) or its v row (dK waves: dP = dO V^T); dims 16s + 8hf + e
+    u32x4_t op[8];
+    {
+        const uint16_t* src = role == 0 ? a.kr + (bh * rows + key) * D : a.v + (bh * L + (kval ? key : 0)) * D;
+        const bool zero = role == 1 && !kval;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const u32x4_t w = ldg16(src + 8 * hf + 16 * s);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) op[s][i] = zero ? 0u : w[i];
+        }
+    }
+    wait_vmcnt<0>();
+    float* pex = pex_all[kw * 2 + qh];
+    if (role == 0)
+        dkdv_tiled_loop<0>(a, lds, qt, list, n0, n1, tid, wave, lane, qh, hf, op, pex, acc);
+    else
+        dkdv_tiled_loop<1>(a, lds, qt, list, n0, n1, tid, wave, lane, qh, hf, op, pex, acc);
+
+    // ---- add the query halves through LDS (no copy is in flight: the last tile waited for all)
+    __syncthreads();
+    float* mrg = reinterpret_cast<float*>(lds) + (role * 2 + kw) * (64 * 64);
+    if (qh == 1) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mrg[(16 * db + i) * 64 + lane] = acc[db][i];
+    }
+    __syncthreads();
+    if (qh == 1 || !kval) return;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] += mrg[(16 * db + i) * 64 + lane];
+
+    // ---- epilogue: dv = dV + dv_lowrank (dV waves); dk = R^T (kscale dK_rot) + dk_lowrank (dK
+    // waves); lane owns key `key`, dims 32db + 8g4 + 4hf + 0..3
+    const long ro = (bh * L + key) * D;
+    if (role == 0) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = 32 * db + 8 * g4 + 4 * hf;
+                const float4 vl = *reinterpret_cast<const float4*>(a.dv_lr + ro + d0);
+                *reinterpret_cast<u32x2_t*>(a.dv + ro + d0) =
+                    u32x2_t{pack_bf2(acc[db][4 * g4] + vl.x, acc[db][4 * g4 + 1] + vl.y),
+                            pack_bf2(acc[db][4 * g4 + 2] + vl.z, acc[db][4 * g4 + 3] + vl.w)};
+            }
+        return;
+    }
+    int crd[3];
+    token_coords(key, a.g.Hg, a.g.Wg, crd[0], crd[1], crd[2]);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int d0 = 32 * db + 8 * g4 + 4 * hf;
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = acc[db][4 * g4 + i] * a.kscale;
+            rot_t(y[0], y[1], rope_cs(a.tab, a.g, d0 >> 1, crd));
+            rot_t(y[2], y[3], rope_cs(a.tab, a.g, (d0 >> 1) + 1, crd));
+            const float4 kl = *reinterpret_cast<const float4*>(a.dk_lr + ro + d0);
+            *reinterpret_cast<u32x2_t*>(a.dk + ro + d0) =
+                u32x2_t{pack_bf2(y[0] + kl.x, y[1] + kl.y), pack_bf2(y[2] + kl.z, y[3] + kl.w)};
         }
 }
 
@@ -1632,7 +1897,15 @@ static hipError_t bwd_sparse(int D, int BS, bool dkdv, const BwdArgs& a, hipStre
 
 hipError_t launch_bwd_dq_tiles(const uint16_t* kr, const uint16_t* v, long BH, long L, int nblk, uint16_t* tiles,
                                hipStream_t st) {
-    hipLaunchKernelGGL(k_bwd_dq_tiles, dim3((unsigned)nblk, (unsigned)BH), dim3(256), 0, st, kr, v, L, nblk, tiles);
+    hipLaunchKernelGGL(k_bwd_tiles<false>, dim3((unsigned)nblk, (unsigned)BH), dim3(256), 0, st, kr, v, L, nblk,
+                       (const float*)nullptr, (const float*)nullptr, tiles, (long)kDqTileElems);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_q_tiles(const uint16_t* qr, const uint16_t* dout, const float* lse2, const float* delta, long BH,
+                              long L, int nblk, uint16_t* tiles, hipStream_t st) {
+    hipLaunchKernelGGL(k_bwd_tiles<true>, dim3((unsigned)nblk, (unsigned)BH), dim3(256), 0, st, qr, dout, L, nblk, lse2,
+                       delta, tiles, (long)kQtTileElems);
     return hipGetLastError();
 }
 
@@ -1650,6 +1923,11 @@ hipError_t launch_bwd_dq(int dtype_bf16, int D, int BS, const BwdArgs& a, hipStr
 }
 
 hipError_t launch_bwd_dkdv(int dtype_bf16, int D, int BS, const BwdArgs& a, hipStream_t st) {
+    if (dtype_bf16 && D == 128 && BS == 64 && a.qtt) {
+        hipLaunchKernelGGL(k_bwd_dkdv_tiled, dim3((unsigned)a.nwg), dim3(512), 0, st, a, a.inv_off, a.inv_list, a.order,
+                           a.qtt);
+        return hipGetLastError();
+    }
     if (dtype_bf16) return bwd_sparse(D, BS, true, a, st);
     if (D == 64)
         hipLaunchKernelGGL((k_bwd_dkdv_f32<64>), dim3((unsigned)a.nwg), dim3(256), 0, st, a, a.inv_off, a.inv_list, BS);

@@ -156,7 +156,7 @@ int check_bwd_supported(const Dims& d, const slr_lowrank_cfg* lr) {
 struct Layout {
     size_t tab, qr, kr, kvt, qbar, kbar, scores, idx, wqt, wkt, part, S, z, sthi, stlo, zp, total;
     // backward
-    size_t lse, delta, dqlr, dklr, dvlr, lrpart, dsz, bits, cnt, off, list, order, dpre, epart, dosp, gpart, dqt;
+    size_t lse, delta, dqlr, dklr, dvlr, lrpart, dsz, bits, cnt, off, list, order, dpre, epart, dosp, gpart, dqt, qtt;
     bool tiled;
 };
 
@@ -226,7 +226,10 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         w.off = take(4ul * d.BH * (nblk + 1));
         w.list = take(4ul * d.BH * nblk * keep);
         w.order = take(4ul * d.BH * nblk);
-        if (use_tiles(d, bs)) w.dqt = take(2ul * d.BH * nblk * 3 * 64 * 128);
+        if (use_tiles(d, bs)) {
+            w.dqt = take(2ul * d.BH * nblk * 3 * 64 * 128);
+            w.qtt = take(2ul * d.BH * nblk * (4 * 64 * 128 + 1024));
+        }
         w.total = off;
         return w;
     }
@@ -691,6 +694,11 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     }
     SLR_TRY(launch_bwd_dq(d.bf16, (int)d.D, bs, a, s));
     a.order = at<int32_t>(ws, w.order);
+    if (tiled_fwd) {
+        uint16_t* qtt = at<uint16_t>(ws, w.qtt);
+        SLR_TRY(launch_bwd_q_tiles(qr, a.dout, a.lse2, a.delta, d.BH, d.L, nblk, qtt, s));
+        a.qtt = qtt;
+    }
     SLR_TRY(launch_bwd_inverse(idx, d.BH, nblk, keep, at<uint32_t>(ws, w.bits), at<int32_t>(ws, w.cnt),
                                at<int32_t>(ws, w.off), at<int32_t>(ws, w.list), at<int32_t>(ws, w.order), s));
     SLR_TRY(launch_bwd_dkdv(d.bf16, (int)d.D, bs, a, s));
