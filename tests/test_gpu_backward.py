@@ -162,6 +162,7 @@ SMALL = [
     ("D64 block32", dict(B=1, H=2, D=64, pairs=(12, 10, 10), T=3, Hg=10, Wg=11, block=32, keep=4, rank=16,
                          lr_pairs=(4, 2, 2))),
     ("D128 block32 one block", dict(B=1, H=1, T=1, Hg=3, Wg=7, block=32, keep=1)),
+    ("D128 block64 one ragged block", dict(B=1, H=2, T=1, Hg=3, Wg=7, keep=1)),
     ("absolute PE", dict(B=2, H=2, T=4, Hg=9, Wg=13, keep=3, lr_mode="abspe", lr_pairs=(0, 0, 0))),
     ("absolute PE silu D64 block32", dict(B=1, H=2, D=64, pairs=(12, 10, 10), T=3, Hg=10, Wg=11, block=32, keep=4,
                                           rank=16, lr_mode="abspe", lr_pairs=(0, 0, 0), fmap="silu")),
