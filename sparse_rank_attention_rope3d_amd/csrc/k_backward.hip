@@ -313,7 +313,7 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a, const int32_t* __r
 // Streaming dQ for bf16, D = 128, 64-token blocks (every workload shape).
 //
 // Each key block has one contiguous 48 KB tile [K | V | K^T] in operand
-// order, written once per backward call (k_bwd_tiles): every 1 KB chunk
+// order, written once per backward call (k_bwd_dq_tiles): every 1 KB chunk
 // is one wave's MFMA operand, lane l's 16 bytes at l * 16, so the LDS image
 // equals the memory image and direct global-to-LDS copies fill it.
 //   K chunk (kh, s):        lane l holds K[key 32kh + l%32][dims 16s + 8(l/32) .. +7]
@@ -323,71 +323,57 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a, const int32_t* __r
 constexpr int kDqPart = 64 * 128;           // elements of one part
 constexpr int kDqTileElems = 3 * kDqPart;   // [K | V | K^T]
 // Query-side tiles of the streaming dK/dV kernel: [Q | dO | Q^T | dO^T | stats]
-// per query block, the same chunk layouts with query rows in place of keys;
-// stats = 2 KB of floats: the rows' log2 normalisers [64], delta = dO . O
-// [64], zeros [384] (one 4-byte copy per lane of each of eight waves).
+// per query block, the same chunk layouts with query rows in place of keys,
+// written by the dQ kernel (which holds those rows); stats = 2 KB of floats:
+// the rows' log2 normalisers [64], delta = dO . O [64], and 384 unused (one
+// 4-byte copy per lane of each of eight waves).
 constexpr int kQtStatsElems = 1024;
 constexpr int kQtTileElems = 4 * kDqPart + kQtStatsElems;
 
-// One tile [A | B | A^T (| B^T) (| stats)] per 64-row block, from A rows that
-// are zero-padded to whole blocks (rotated k or q) and B rows [L] (v or dO,
-// rows past L read as zero). Grid (nblk, BH).
-template <bool BT>
-__global__ __launch_bounds__(256) void k_bwd_tiles(const uint16_t* __restrict__ a_rows, const uint16_t* __restrict__ b_rows,
-                                                   long L, int nblk, const float* __restrict__ lse2,
-                                                   const float* __restrict__ delta, uint16_t* __restrict__ tiles,
-                                                   long tile_elems) {
+// The dQ kernel's tile [K | V | K^T] of every key block, from the rotated k
+// rows (zero-padded to whole blocks) and v [L] (rows past L read as zero).
+// Grid (nblk, BH).
+__global__ __launch_bounds__(256) void k_bwd_dq_tiles(const uint16_t* __restrict__ kr, const uint16_t* __restrict__ v,
+                                                      long L, int nblk, uint16_t* __restrict__ tiles) {
     constexpr int D = 128;
     const int tid = threadIdx.x, blk = blockIdx.x;
     const long bh = blockIdx.y;
-    const uint16_t* as = a_rows + (bh * nblk + blk) * 64l * D;   // zero rows past L
-    const uint16_t* bs = b_rows + bh * L * D;
-    uint16_t* t = tiles + (bh * nblk + blk) * tile_elems;
-    // A and B parts: thread takes dims 8c .. 8c+7 of rows 16p + tid/16
+    const uint16_t* ks = kr + (bh * nblk + blk) * 64l * D;   // zero rows past L
+    const uint16_t* vs = v + bh * L * D;
+    uint16_t* t = tiles + (bh * nblk + blk) * (long)kDqTileElems;
+    // K and V parts: thread takes dims 8c .. 8c+7 of rows 16p + tid/16
     {
         const int c = tid & 15, rs = tid >> 4;
-        u32x4_t xa[4], xb[4];
+        u32x4_t xk[4], xv[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int r = 16 * p + rs;
             const long l = (long)blk * 64 + r;
-            xa[p] = ldg16(as + (long)r * D + 8 * c);
-            const u32x4_t w = ldg16(bs + (l < L ? l : L - 1) * D + 8 * c);
+            xk[p] = ldg16(ks + (long)r * D + 8 * c);
+            const u32x4_t w = ldg16(vs + (l < L ? l : L - 1) * D + 8 * c);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xb[p][i] = l < L ? w[i] : 0u;
+            for (int i = 0; i < 4; ++i) xv[p][i] = l < L ? w[i] : 0u;
         }
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int r = 16 * p + rs;
             const int o = (((r >> 5) * 8 + (c >> 1)) * 64 + (r & 31) + 32 * (c & 1)) * 8;
-            stg16(t + o, xa[p]);
-            stg16(t + kDqPart + o, xb[p]);
+            stg16(t + o, xk[p]);
+            stg16(t + kDqPart + o, xv[p]);
         }
     }
-    // A^T part (threads 0..127) and B^T part (threads 128..255, when BT): a
-    // thread takes 8 rows (slots 8vh .. 8vh+7 of 16-row group vG) x 8 dims
-    // and transposes them in registers
-    const int u = tid & 127;
-    const int vc = u & 15, vg = (u >> 4) & 7, vG = vg >> 1, vh = vg & 1;
-    const bool second = tid >= 128;
-    if (second && !BT) return;
+    // K^T part: thread tid < 128 takes 8 keys (slots 8vh .. 8vh+7 of 16-key
+    // group vG) x 8 dims and transposes them in registers
+    if (tid >= 128) return;
+    const int vc = tid & 15, vg = (tid >> 4) & 7, vG = vg >> 1, vh = vg & 1;
     uint32_t rows[8][4];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int r = 16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2);
-        const long l = (long)blk * 64 + r;
-        u32x4_t w;
-        if (second) {
-            w = ldg16(bs + (l < L ? l : L - 1) * D + 8 * vc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = l < L ? w[i] : 0u;
-        } else {
-            w = ldg16(as + (long)r * D + 8 * vc);
-        }
+        const u32x4_t w = ldg16(ks + (long)(16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2)) * D + 8 * vc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) rows[e][i] = w[i];
     }
-    uint16_t* tt = t + (second ? 3 : 2) * kDqPart;
+    uint16_t* kt = t + 2 * kDqPart;
     const int kh = vG >> 1, h2 = vG & 1;
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
@@ -398,14 +384,7 @@ __global__ __launch_bounds__(256) void k_bwd_tiles(const uint16_t* __restrict__ 
             o[i] = (f & 1) ? __builtin_amdgcn_perm(a1, a0, 0x07060302u) : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
         }
         const int d = 8 * vc + f;
-        stg16(tt + ((kh * 8 + (d >> 5) * 2 + h2) * 64 + (d & 31) + 32 * vh) * 8, o);
-    }
-    if (BT && tid < 128) {
-        // stats: [lse2 | delta | zeros] of the block's 64 rows (padded rows hold zeros)
-        float* st = reinterpret_cast<float*>(t + 4 * kDqPart);
-        const long r0 = (bh * nblk + blk) * 64l;
-        for (int e = tid; e < 512; e += 128)
-            st[e] = e < 64 ? lse2[r0 + e] : (e < 128 ? delta[r0 + e - 64] : 0.f);
+        stg16(kt + ((kh * 8 + (d >> 5) * 2 + h2) * 64 + (d & 31) + 32 * vh) * 8, o);
     }
 }
 
@@ -471,6 +450,53 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* 
     if (kh == 0 && hf == 0) {
         a.lse2[bh * rows + qrow] = lse2;
         a.delta[bh * rows + qrow] = qval ? dl : 0.f;
+    }
+    if (a.qtt) {
+        // this query block's tile [Q | dO | Q^T | dO^T | stats] for the streaming
+        // dK/dV kernel: qop / doop already are the Q / dO chunks (rh, s) of this
+        // lane (waves kh = 0 store Q, kh = 1 dO); the transposed parts go through
+        // LDS (the ring is not in use yet): rows row-major, then each thread
+        // transposes 8 rows x 8 dims in registers
+        uint16_t* qt = const_cast<uint16_t*>(a.qtt) + (bh * nblk + qb) * (long)kQtTileElems;
+        constexpr int RLD = D + 8;
+        uint16_t* rm = lds + kh * (BS * RLD);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const u32x4_t x = kh == 0 ? qop[s] : doop[s];
+            stg16(qt + kh * PART + ((rh * 8 + s) * 64 + lane) * 8, x);
+            *reinterpret_cast<u32x4_t*>(rm + (32 * rh + l32) * RLD + 16 * s + 8 * hf) = x;
+        }
+        if (hf == 0) {
+            float* st = reinterpret_cast<float*>(qt + 4 * PART);
+            st[(kh == 0 ? 0 : 64) + 32 * rh + l32] = kh == 0 ? lse2 : (qval ? dl : 0.f);
+        }
+        __syncthreads();
+        const int u = tid & 127, which = tid >> 7;   // 0: Q^T, 1: dO^T
+        const int vc = u & 15, vg = (u >> 4) & 7, vG = vg >> 1, vh = vg & 1;
+        const uint16_t* src = lds + which * (BS * RLD);
+        uint32_t rws[8][4];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const u32x4_t w =
+                *reinterpret_cast<const u32x4_t*>(src + (16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2)) * RLD + 8 * vc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rws[e][i] = w[i];
+        }
+        uint16_t* tt = qt + (2 + which) * PART;
+        const int th = vG >> 1, h2 = vG & 1;
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            u32x4_t o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t a0 = rws[2 * i][f >> 1], a1 = rws[2 * i + 1][f >> 1];
+                o[i] = (f & 1) ? __builtin_amdgcn_perm(a1, a0, 0x07060302u)
+                               : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+            }
+            const int d = 8 * vc + f;
+            stg16(tt + ((th * 8 + (d >> 5) * 2 + h2) * 64 + (d & 31) + 32 * vh) * 8, o);
+        }
+        __syncthreads();   // the rows' LDS area becomes the ring
     }
 
     // entries outside [0, nblk) contribute nothing (their slot streams tile 0)
@@ -1897,15 +1923,7 @@ static hipError_t bwd_sparse(int D, int BS, bool dkdv, const BwdArgs& a, hipStre
 
 hipError_t launch_bwd_dq_tiles(const uint16_t* kr, const uint16_t* v, long BH, long L, int nblk, uint16_t* tiles,
                                hipStream_t st) {
-    hipLaunchKernelGGL(k_bwd_tiles<false>, dim3((unsigned)nblk, (unsigned)BH), dim3(256), 0, st, kr, v, L, nblk,
-                       (const float*)nullptr, (const float*)nullptr, tiles, (long)kDqTileElems);
-    return hipGetLastError();
-}
-
-hipError_t launch_bwd_q_tiles(const uint16_t* qr, const uint16_t* dout, const float* lse2, const float* delta, long BH,
-                              long L, int nblk, uint16_t* tiles, hipStream_t st) {
-    hipLaunchKernelGGL(k_bwd_tiles<true>, dim3((unsigned)nblk, (unsigned)BH), dim3(256), 0, st, qr, dout, L, nblk, lse2,
-                       delta, tiles, (long)kQtTileElems);
+    hipLaunchKernelGGL(k_bwd_dq_tiles, dim3((unsigned)nblk, (unsigned)BH), dim3(256), 0, st, kr, v, L, nblk, tiles);
     return hipGetLastError();
 }
 

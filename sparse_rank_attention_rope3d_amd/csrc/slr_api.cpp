@@ -691,14 +691,10 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
         uint16_t* dqt = at<uint16_t>(ws, w.dqt);
         SLR_TRY(launch_bwd_dq_tiles(kr, (const uint16_t*)v, d.BH, d.L, nblk, dqt, s));
         a.dqt = dqt;
+        a.qtt = at<uint16_t>(ws, w.qtt);   // written by the dQ kernel for the dK/dV kernel
     }
     SLR_TRY(launch_bwd_dq(d.bf16, (int)d.D, bs, a, s));
     a.order = at<int32_t>(ws, w.order);
-    if (tiled_fwd) {
-        uint16_t* qtt = at<uint16_t>(ws, w.qtt);
-        SLR_TRY(launch_bwd_q_tiles(qr, a.dout, a.lse2, a.delta, d.BH, d.L, nblk, qtt, s));
-        a.qtt = qtt;
-    }
     SLR_TRY(launch_bwd_inverse(idx, d.BH, nblk, keep, at<uint32_t>(ws, w.bits), at<int32_t>(ws, w.cnt),
                                at<int32_t>(ws, w.off), at<int32_t>(ws, w.list), at<int32_t>(ws, w.order), s));
     SLR_TRY(launch_bwd_dkdv(d.bf16, (int)d.D, bs, a, s));

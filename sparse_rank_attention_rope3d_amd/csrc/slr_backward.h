@@ -21,7 +21,7 @@ struct BwdArgs {
     const uint16_t* dqt;       // bf16, D = 128, 64-token blocks: [BH][nblk][K | V | K^T] 48 KB operand-order
                                // tiles of the streaming dQ kernel (null: the staging kernel)
     const uint16_t* qtt;       // same shapes: [BH][nblk][Q | dO | Q^T | dO^T | stats] 66 KB tiles of the
-                               // streaming dK/dV kernel (null: the staging kernel)
+                               // streaming dK/dV kernel, written by the dQ kernel (null: staging kernels)
     const float* lse_in;       // [BH][L] the forward's log2 normalisers
     float* lse2;               // [BH][nblk*BS] the same, zero on padded rows
     float qmul;                // score (log2 units) = qmul * (q_rot . k_rot): log2(e)/sqrt(D), or 1
@@ -82,11 +82,6 @@ hipError_t launch_bwd_inverse(const int32_t* idx, long BH, int nblk, int keep, u
 // zero-padded rotated k copy kr [BH][nblk*64][128] and v [BH][L][128] (bf16); grid (nblk, BH).
 hipError_t launch_bwd_dq_tiles(const uint16_t* kr, const uint16_t* v, long BH, long L, int nblk, uint16_t* tiles,
                                hipStream_t st);
-// [Q | dO | Q^T | dO^T | stats] tiles of every query block for the streaming dK/dV kernel, from
-// the zero-padded (scaled) rotated q copy qr [BH][nblk*64][128], dout [BH][L][128] (bf16) and the
-// row statistics lse2, delta [BH][nblk*64] that the dQ kernel wrote; grid (nblk, BH).
-hipError_t launch_bwd_q_tiles(const uint16_t* qr, const uint16_t* dout, const float* lse2, const float* delta, long BH,
-                              long L, int nblk, uint16_t* tiles, hipStream_t st);
 hipError_t launch_bwd_dq(int dtype_bf16, int D, int BS, const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_dkdv(int dtype_bf16, int D, int BS, const BwdArgs& a, hipStream_t st);
 
