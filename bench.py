@@ -34,8 +34,8 @@ PEAK_HBM_GBS = 8000.0
 # on, identified by the sha256 of its files; any other source reports null.
 FLASH_TRAFFIC_SOURCES = ["k_flash.hip", "slr_common.h", "slr_launch.h"]
 FLASH_TRAFFIC = {
-    "sha256": "521af05705e58f31b89a6e02bff7a4fba5cd17a8ec1ece9018d1572b5306cab9",
-    "bytes_per_launch": {"wan13b": 8188.6e6 + 201.3e6, "wan14b": 218470.1e6 + 1548.4e6},
+    "sha256": "7d776f0545ef627a151a7e498bce077389493b0a1417e52510607e12c8671b19",
+    "bytes_per_launch": {"wan13b": 8202.8e6 + 201.3e6, "wan14b": 220518.4e6 + 1548.4e6},
 }
 
 

@@ -438,7 +438,8 @@ __device__ __forceinline__ void softmax_tile(f32x16_t& s, f32x16_t* o, float& m_
 }
 
 // Eight 16-byte LDS reads (1 KB apart) into registers; the block waits for
-// them itself, so no read is left in flight when it ends.
+// them itself, so no read is left in flight when it ends (early-clobber
+// outputs: no destination can alias the address register the later reads use).
 __device__ __forceinline__ void lds_read8(u32x4_t* r, const uint16_t* lds_base) {
     const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds_base;
     asm volatile(
@@ -451,7 +452,7 @@ __device__ __forceinline__ void lds_read8(u32x4_t* r, const uint16_t* lds_base) 
         "ds_read_b128 %6, %8 offset:6144\n\t"
         "ds_read_b128 %7, %8 offset:7168\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7])
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
         : "v"(a)
         : "memory");
 }
