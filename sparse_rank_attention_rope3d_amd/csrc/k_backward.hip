@@ -628,11 +628,11 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* 
 // S = Q K^T and P, passes P (fp32) to the dK wave of the same (kw, qh)
 // through LDS and adds dO^T P; the dK wave meanwhile computes dP = dO V^T,
 // then dS = P (dP - delta), and adds Q^T dS: 16 MFMAs per wave per tile.
-// Waves w and w + 4 share a SIMD, one of each role (two waves per SIMD). The query-side tiles [Q | dO | Q^T | dO^T | stats] stream through
-// LDS (134 KB): Q, dO and the row statistics in a three-slot ring requested
-// two tiles ahead, Q^T and dO^T in one slot refilled as soon as every wave
-// has read it and waited for only just before those reads (three barriers
-// per tile); the query halves' partial sums are added through LDS at the end.
+// Waves w and w + 4 share a SIMD, one of each role (two waves per SIMD). The
+// query-side tiles [Q | dO | Q^T | dO^T | stats] stream through two-slot LDS
+// rings (132 KB, and 16 KB for P), requested one tile ahead; two barriers
+// per tile (tile landed, P handed over). The query halves' partial sums are
+// added through LDS at the end.
 template <int ROLE>
 __device__ __forceinline__ void dkdv_tiled_loop(const BwdArgs& a, uint16_t* lds, const uint16_t* qt,
                                                 const int32_t* list, int n0, int n1, int tid, int wave, int lane,
@@ -640,7 +640,6 @@ __device__ __forceinline__ void dkdv_tiled_loop(const BwdArgs& a, uint16_t* lds,
                                                 f32x16_t* acc) {
     constexpr int PART = kDqPart, TILE = kQtTileElems, PL = PART * 2 / (512 * 16);
     constexpr int FSZ = 2 * PART + kQtStatsElems;   // first-use group in LDS: [Q | dO | stats]
-    constexpr int NF = 2 * PL + 1, NT = 2 * PL;     // copies per lane of the two groups
     // First-use group of tile i -> F slot: Q, dO (two 16-byte copies per lane
     // each) and the 2 KB of row statistics (one 4-byte copy per lane)
     auto issue_f = [&](int i, uint16_t* slot) {
@@ -656,9 +655,8 @@ __device__ __forceinline__ void dkdv_tiled_loop(const BwdArgs& a, uint16_t* lds,
                                          (__attribute__((address_space(3))) void*)(slot + 2 * PART + wave * 128), 4,
                                          0, 0);
     };
-    // Transposed group [Q^T | dO^T] of tile i -> the T slot
-    uint16_t* tslot = lds + 3 * FSZ;
-    auto issue_t = [&](int i) {
+    // Transposed group [Q^T | dO^T] of tile i -> a T slot
+    auto issue_t = [&](int i, uint16_t* tslot) {
         const uint16_t* src = qt + (long)i * TILE + 2 * PART;
 #pragma unroll
         for (int p = 0; p < 2; ++p)
@@ -672,26 +670,24 @@ __device__ __forceinline__ void dkdv_tiled_loop(const BwdArgs& a, uint16_t* lds,
     auto qblock = [&](int n) { return __builtin_amdgcn_readfirstlane(list[n]); };
     const int rd = ((qh * 8) * 64 + lane) * 8;   // this lane's chunks (qh, 0..7) within a part
     const int ntile = n1 - n0;
-    // F of tile t in F slot t % 3, T in the T slot. Issue order: T0 F0 F1,
-    // then per tile t: F(t+2) after the opening barrier (into the slot of
-    // tile t - 1, which it certifies as consumed), T(t+1) after the barrier
-    // that follows every wave's reads of T(t); so from tile 1 on the sequence
-    // is ..., F(t+1) T(t) F(t+2) T(t+1) ...
+    uint16_t* tbase = lds + 2 * FSZ;
+    // Tile t in F slot t % 2 and T slot t % 2; both groups of tile t + 1 are
+    // requested right after the barrier that opens tile t (which certifies
+    // that every wave is done with tile t - 1, whose slots they take).
     if (ntile > 0) {
-        issue_t(qblock(n0));
         issue_f(qblock(n0), lds);
+        issue_t(qblock(n0), tbase);
     }
-    if (ntile > 1) issue_f(qblock(n0 + 1), lds + FSZ);
-    int fs = 0;   // F slot of tile t
     for (int t = 0; t < ntile; ++t) {
-        // F(t) landed (tile 0: everything issued so far)
-        if (t == 0) wait_vmcnt<0>();
-        else if (t + 1 < ntile) wait_vmcnt<NF + NT>();
-        else wait_vmcnt<NT>();
+        wait_vmcnt<0>();   // tile t landed (the only copies in flight)
         __builtin_amdgcn_s_barrier();
-        if (t + 2 < ntile) issue_f(qblock(n0 + t + 2), lds + (fs == 0 ? 2 : fs - 1) * FSZ);
-        const uint16_t* cur = lds + fs * FSZ;
-        fs = fs == 2 ? 0 : fs + 1;
+        if (t + 1 < ntile) {
+            const int i1 = qblock(n0 + t + 1);
+            issue_f(i1, lds + ((t + 1) & 1) * FSZ);
+            issue_t(i1, tbase + ((t + 1) & 1) * (2 * PART));
+        }
+        const uint16_t* cur = lds + (t & 1) * FSZ;
+        const uint16_t* tcur = tbase + (t & 1) * (2 * PART);
         const float* st = reinterpret_cast<const float*>(cur + 2 * PART) + 32 * qh + 4 * hf;
         // dV waves: S = Q K^T and P, handed to the dK wave of the same (kw, qh)
         // through LDS; dK waves meanwhile: dP = dO V^T
@@ -721,12 +717,7 @@ __device__ __forceinline__ void dkdv_tiled_loop(const BwdArgs& a, uint16_t* lds,
                 for (int e = 0; e < 4; ++e) bop[h2][e] = pack_bf2(p[8 * h2 + 2 * e], p[8 * h2 + 2 * e + 1]);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // P stored before the barrier below
         }
-        // T(t) landed (outstanding in issue order ..., T(t), F(t+2), the last only if
-        // t + 2 < ntile; tile 0 waited for everything) and P is in LDS
-        if (t > 0) {
-            if (t + 2 < ntile) wait_vmcnt<NF>(); else wait_vmcnt<0>();
-        }
-        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_s_barrier();   // P is in LDS
         asm volatile("" ::: "memory");
         if constexpr (ROLE == 1) {
             float ds[16];
@@ -744,10 +735,7 @@ __device__ __forceinline__ void dkdv_tiled_loop(const BwdArgs& a, uint16_t* lds,
                 for (int e = 0; e < 4; ++e) bop[h2][e] = pack_bf2(ds[8 * h2 + 2 * e], ds[8 * h2 + 2 * e + 1]);
         }
         u32x4_t at[8];   // dO^T (dV waves) or Q^T (dK waves) chunks (qh, db, h2) = (qh, i / 2, i % 2)
-        lds_read8k(at, tslot + (ROLE == 0 ? PART : 0) + rd);
-        // every wave has its transposed operands (and the dK waves their P): refill the slot
-        __builtin_amdgcn_s_barrier();
-        if (t + 1 < ntile) issue_t(qblock(n0 + t + 1));
+        lds_read8k(at, tcur + (ROLE == 0 ? PART : 0) + rd);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i >> 1] = mfma32(at[i], bop[i & 1], acc[i >> 1]);
     }
@@ -758,7 +746,7 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_tiled(BwdArgs a, const int32_t
                                                         const int32_t* __restrict__ order,
                                                         const uint16_t* __restrict__ qt_all) {
     constexpr int D = 128, BS = 64, TILE = kQtTileElems;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[3 * (2 * kDqPart + kQtStatsElems) + 2 * kDqPart];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (2 * kDqPart + kQtStatsElems) + 4 * kDqPart];
     __shared__ float pex_all[4][16 * 64];   // P of each (kw, qh), from the dV wave to the dK wave
 
     const int tid = threadIdx.x, lane = tid & 63;
