@@ -561,7 +561,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* 
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const bool off = !jok || (ragged && key0 + 8 * (i >> 2) + (i & 3) >= L);
-            ds[i] = off ? 0.f : exp2f(sacc[i] - lse2) * (dpacc[i] - dl);
+            ds[i] = off ? 0.f : __builtin_amdgcn_exp2f(sacc[i] - lse2) * (dpacc[i] - dl);
         }
         u32x4_t dsop[2];
 #pragma unroll
@@ -704,10 +704,10 @@ __device__ __forceinline__ void dkdv_tiled_loop(const BwdArgs& a, uint16_t* lds,
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const float4 l4 = *reinterpret_cast<const float4*>(st + 8 * g);
-                p[4 * g + 0] = exp2f(sacc[4 * g + 0] * a.qmul - l4.x);
-                p[4 * g + 1] = exp2f(sacc[4 * g + 1] * a.qmul - l4.y);
-                p[4 * g + 2] = exp2f(sacc[4 * g + 2] * a.qmul - l4.z);
-                p[4 * g + 3] = exp2f(sacc[4 * g + 3] * a.qmul - l4.w);
+                p[4 * g + 0] = __builtin_amdgcn_exp2f(sacc[4 * g + 0] * a.qmul - l4.x);
+                p[4 * g + 1] = __builtin_amdgcn_exp2f(sacc[4 * g + 1] * a.qmul - l4.y);
+                p[4 * g + 2] = __builtin_amdgcn_exp2f(sacc[4 * g + 2] * a.qmul - l4.z);
+                p[4 * g + 3] = __builtin_amdgcn_exp2f(sacc[4 * g + 3] * a.qmul - l4.w);
             }
 #pragma unroll
             for (int e = 0; e < 16; ++e) pex[e * 64 + lane] = p[e];
