@@ -1,21 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the 3D-RoPE sparse + low-rank attention layer forward on one
 MI355X: ms/layer and effective TFLOP/s, with the dominant kernel's roofline,
-per-stage times, the in-library dense flash kernel and the CPU oracle.
+per-stage times and their HBM rooflines, the in-library dense flash kernel,
+the layer backward and the CPU oracle.
 
-    python bench.py [--steps K] [--warmup W] [--workload wan13b|wan14b|hunyuan13b]
+    python bench.py [--steps K] [--warmup W] [--workload wan14b|wan13b|hunyuan13b]
+                    [--sub wan13b,hunyuan13b] [--sweep JSONL]
 
 One step = one slr_attention_fwd over the whole layer (rotate + pool, block
 top-k, low-rank summary, block-sparse flash + low-rank readout + gated
-combine). Inputs are seeded synthetic layers already resident in HBM.
-Prints one JSON line.
+combine). Inputs are seeded synthetic layers already resident in HBM. The
+headline is the Wan2.1-14B layer at 720p, 81 frames (L = 75600); the
+Wan2.1-1.3B (L = 32760) and HunyuanVideo-13B (L = 118800) layers are timed
+the same way as sub-records. Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import concurrent.futures as cf
 import ctypes
+import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -27,6 +34,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+METRIC = "SLR attn fwd ms/layer + effective TFLOP/s at L=32760/75600/118800, 1 GPU"
 
 # HBM bytes per launch of the sparse flash kernel, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (KiB per dispatch, scaled x2 and x1 by what the same counters read
@@ -37,11 +45,13 @@ FLASH_TRAFFIC = {
     "sha256": "7d776f0545ef627a151a7e498bce077389493b0a1417e52510607e12c8671b19",
     "bytes_per_launch": {"wan13b": 8202.8e6 + 201.3e6, "wan14b": 220518.4e6 + 1548.4e6},
 }
+GEN_THREADS = 8   # input generation: numpy fills each slice's arrays without the GIL
 
 
 def flash_traffic(workload: str):
-    import hashlib
-    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_rank_attention_rope3d_amd", "csrc")
+    if workload is None:
+        return None
+    csrc = os.path.join(ROOT, "sparse_rank_attention_rope3d_amd", "csrc")
     h = hashlib.sha256()
     try:
         for f in FLASH_TRAFFIC_SOURCES:
@@ -52,6 +62,23 @@ def flash_traffic(workload: str):
     if h.hexdigest() != FLASH_TRAFFIC["sha256"]:
         return None
     return FLASH_TRAFFIC["bytes_per_launch"].get(workload)
+
+
+def host_cpu() -> dict:
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"model": model, "nproc": usable, "logical_cpus": os.cpu_count()}
 
 
 def achievable_peaks(torch) -> dict:
@@ -94,6 +121,46 @@ def achievable_peaks(torch) -> dict:
             "what": "8192^3 bf16 torch.matmul on random operands; 1 GiB device copy, read + write bytes"}
 
 
+def memory_read_probe(torch) -> dict:
+    """Read-only streaming rate of a buffer at sizes that sit in the XCDs'
+    L2 (16 MB), in the 256 MB memory-side cache (64 and 160 MB) and in HBM
+    (1 and 4 GiB), with ordinary vector loads and with the direct
+    global -> LDS copies the flash kernel uses (libslr_probe.so)."""
+    path = os.path.join(ROOT, "sparse_rank_attention_rope3d_amd", "libslr_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.slrprobe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.slrprobe_stream_read.restype = ctypes.c_int
+    nwg = 2048
+    sink = torch.empty(nwg * 256, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    big = torch.ones(4 * 2 ** 30, dtype=torch.uint8, device="cuda")
+    out = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for mb in (16, 64, 160, 1024, 4096):
+        nbytes = mb * 2 ** 20
+        passes = max(1, (8 * 2 ** 30) // nbytes)
+        for to_lds in (0, 1):
+            call = lambda: lib.slrprobe_stream_read(ctypes.c_void_p(big.data_ptr()), nbytes, passes, to_lds, nwg,
+                                                    ctypes.c_void_p(sink.data_ptr()), stream)
+            assert call() == 0
+            torch.cuda.synchronize()
+            reps = 3
+            e0.record()
+            for _ in range(reps):
+                assert call() == 0
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = nbytes * passes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            out[f"{mb}MB_{'to_lds' if to_lds else 'vgpr'}_GB/s"] = round(gbs, 1)
+    del big, sink
+    out["what"] = ("read-only stream, 2048 workgroups x 256 threads, 16-byte loads; 16 MB fits the XCDs' L2, "
+                   "64/160 MB the memory-side cache, 1/4 GiB only HBM")
+    return out
+
+
 def _hip():
     h = ctypes.CDLL("libamdhip64.so")
     h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
@@ -114,19 +181,30 @@ def _elapsed(h, a, b) -> float:
     return ms.value
 
 
-def make_device_inputs(cfg, torch):
+def _slice_arrays(cfg, b, h):
+    from sparse_rank_attention_rope3d_amd import synth
+    arrs = synth.qkv_slice(cfg, b, h)
+    if cfg.dtype == "bf16":
+        return [synth.f32_to_bf16_bits(a).view(np.int16) for a in arrs]
+    return list(arrs)
+
+
+def make_device_inputs(cfg, torch, threads: int = GEN_THREADS):
+    """q, k, v [B, H, L, D] on the device from the seeded per-slice
+    generators (slices drawn on `threads` host threads), and the low-rank
+    parameters."""
     from sparse_rank_attention_rope3d_amd import synth
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     shp = (cfg.B, cfg.H, cfg.L, cfg.D)
     q, k, v = (torch.empty(shp, dtype=tdt, device="cuda") for _ in range(3))
-    for b in range(cfg.B):
-        for h in range(cfg.H):
-            for dst, arr in zip((q, k, v), synth.qkv_slice(cfg, b, h)):
-                if cfg.dtype == "bf16":
-                    bits = synth.f32_to_bf16_bits(arr)
-                    dst[b, h] = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
-                else:
-                    dst[b, h] = torch.from_numpy(arr).cuda()
+    slices = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    with cf.ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        for n, ((b, h), arrs) in enumerate(zip(slices, ex.map(lambda bh: _slice_arrays(cfg, *bh), slices))):
+            for dst, arr in zip((q, k, v), arrs):
+                t = torch.from_numpy(arr)
+                dst[b, h] = (t.view(torch.bfloat16) if cfg.dtype == "bf16" else t).cuda()
+            if (n + 1) % 20 == 0:
+                print(f"[bench]   {n + 1}/{len(slices)} slices on the device", file=sys.stderr, flush=True)
     params = {kk: torch.from_numpy(vv).cuda() for kk, vv in synth.lowrank_params(cfg).items()}
     return q, k, v, params
 
@@ -216,8 +294,27 @@ def _time_ms(torch, fn, reps):
 
 def run_sweep(args, torch, B, synth):
     """Keep fraction x rank sweep at the Wan2.1-1.3B shape: layer time of
-    every point and the dense kernel's time on the same inputs."""
+    every point and the dense kernel's time on the same inputs. One JSON
+    line per point is appended to the file as soon as the point is done; a
+    rerun keeps the points the file already holds and starts at the first
+    missing one."""
     points = synth.sweep()
+    done = set()
+    if os.path.exists(args.sweep):
+        with open(args.sweep) as f:
+            for ln in f:
+                ln = ln.strip()
+                if not ln:
+                    continue
+                try:
+                    row = json.loads(ln)
+                except json.JSONDecodeError:
+                    continue   # a line cut short by an interrupted run: that point runs again
+                done.add((row["keep"], row["rank"]))
+    todo = [p for p in points if (p.keep, p.rank) not in done]
+    print(f"[sweep] {len(done)} of {len(points)} points already in {args.sweep}", file=sys.stderr, flush=True)
+    if not todo:
+        return 0
     base = points[0]
     q, k, v, _ = make_device_inputs(base, torch)
     shape, rope = B.shape_of(base), B.rope_of(base)
@@ -225,8 +322,7 @@ def run_sweep(args, torch, B, synth):
     out = torch.empty_like(q)
     dense_ms = _time_ms(torch, lambda: B.slr_dense_attention_fwd(q, k, v, shape, rope, out=out, ws=wsd), 3)
     del wsd
-    rows = []
-    for cfg in points:
+    for cfg in todo:
         params = {kk: torch.from_numpy(vv).cuda() for kk, vv in synth.lowrank_params(cfg).items()}
         sparse, lowrank = B.sparse_of(cfg), B.lowrank_of(cfg, params)
         ws = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lowrank), "cuda")
@@ -250,13 +346,171 @@ def run_sweep(args, torch, B, synth):
             row["backward_tflops"] = round((2.5 * F["sparse"] + 22.0 * cfg.B * cfg.H * cfg.L * cfg.D * cfg.rank)
                                            / (bms * 1e-3) / 1e12, 1)
             del saved, wsb, grads, dout
-        rows.append(row)
+        with open(args.sweep, "a") as f:
+            f.write(json.dumps(row) + "\n")
         print(f"[sweep] {row}", file=sys.stderr, flush=True)
         del ws
-    with open(args.sweep, "w") as f:
-        for row in rows:
-            f.write(json.dumps(row) + "\n")
     return 0
+
+
+def measure_forward(cfg, args, torch, B, hip, ach=None, dense_reps=0):
+    """Time the layer forward of one workload: per-step times (hipEvents on
+    the stream the library launches on) over `args.steps` plain forward
+    calls, then the same number of staged calls for the stage times; the
+    flash kernel's MFMA roofline and the HBM rooflines of the rotate + pool +
+    select and summary stages. Returns (record, device inputs)."""
+    print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    q, k, v, params = make_device_inputs(cfg, torch)
+    shape, rope, sparse = B.shape_of(cfg), B.rope_of(cfg), B.sparse_of(cfg)
+    lowrank = B.lowrank_of(cfg, params)
+    ws = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lowrank), "cuda")
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    fwd = lambda: B.slr_attention_fwd(q, k, v, shape, rope, sparse, lowrank, out=out, ws=ws)
+    print(f"[bench] {cfg.name}: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    print(f"[bench] {cfg.name}: timing {args.steps} steps", file=sys.stderr, flush=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(args.steps):
+        fwd()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    # stage times from the same number of staged calls (their event records
+    # add a few microseconds between stages, so they are not the headline)
+    events = [[_event(hip) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        B.slr_attention_fwd_staged(q, k, v, shape, rope, sparse, lowrank, out, ws, events[i])
+    torch.cuda.synchronize()
+    stage_names = ["rope_pool", "select", "lowrank_summary", "sparse_flash"]
+    stages = {n: [] for n in stage_names}
+    for evs in events:
+        for j, n in enumerate(stage_names):
+            stages[n].append(_elapsed(hip, evs[j], evs[j + 1]))
+    for evs in events:
+        for e in evs:
+            hip.hipEventDestroy(ctypes.c_void_p(e))
+    stage_ms = {n: float(np.mean(vs)) for n, vs in stages.items()}
+
+    F = cfg.flops()
+    f_total = F["sparse"] + F["lowrank"] + F["select"]
+    ms_mean = float(step_ms.mean())
+    flash_ms = stage_ms["sparse_flash"]
+    flash_tf = F["sparse"] / (flash_ms * 1e-3) / 1e12
+    es = 2 if cfg.dtype == "bf16" else 4
+    BHLD = cfg.B * cfg.H * cfg.L * cfg.D
+    rows_pad = cfg.B * cfg.H * cfg.nblk * cfg.block * cfg.D
+    idx_bytes = 4 * cfg.B * cfg.H * cfg.nblk * cfg.keep
+    # algorithmic bytes (the survey's roofline table): rotate + pool + select
+    # read q, k and write the rotated q, k (+ the kept indices); the summary
+    # reads k, v; the low-rank apply + combine is fused into the flash kernel
+    k1_bytes = 4 * BHLD * es + idx_bytes
+    k2_bytes = 2 * BHLD * es
+    k1_ms = stage_ms["rope_pool"] + stage_ms["select"]
+    # what the rotate + pool kernel itself moves on the tiled path: it also
+    # reads v and writes the [K | V^T] tiles and the block means
+    tiled = cfg.dtype == "bf16" and cfg.D == 128 and cfg.block == 64
+    n_io = 3 if tiled else 2
+    own_bytes = n_io * BHLD * es + n_io * rows_pad * es + 2 * cfg.B * cfg.H * cfg.nblk * cfg.D * 4
+
+    def hbm(nbytes, ms):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        d = {"GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes,
+             "ms": round(ms, 4)}
+        if ach:
+            d["frac_of_copy"] = round(gbs / ach["copy_GB/s"], 4)
+        return d
+
+    rec = {
+        "workload": cfg.name,
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "D": cfg.D, "L": cfg.L,
+                   "grid": [cfg.T, cfg.Hg, cfg.Wg], "block": cfg.block, "keep": cfg.keep, "nblk": cfg.nblk,
+                   "rank": cfg.rank, "lowrank": cfg.lr_mode, "gate": cfg.gate, "fmap": cfg.fmap,
+                   "parallelism": "single GPU"},
+        "ms_per_layer": {"mean": round(ms_mean, 4), "median": round(float(np.median(step_ms)), 4),
+                         "min": round(float(step_ms.min()), 4), "max": round(float(step_ms.max()), 4),
+                         "wall_clock_mean": round(wall_ms, 4), "steps": args.steps},
+        "effective_TFLOP/s": round(f_total / (ms_mean * 1e-3) / 1e12, 2),
+        "effective_TFLOP/s_at_median": round(f_total / (float(np.median(step_ms)) * 1e-3) / 1e12, 2),
+        "dense_equivalent_TFLOP/s": round(F["dense"] / (ms_mean * 1e-3) / 1e12, 1),
+        "flops": {k_: float(v_) for k_, v_ in F.items()},
+        "roofline": {"kernel": "k_flash_tiled (block-sparse flash + low-rank readout + combine)",
+                     "bound": "mfma", "achieved": round(flash_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flash_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": flash_traffic(args_key(cfg)),
+                     "algorithmic_flops_per_launch": F["sparse"], "avg_launch_ms": round(flash_ms, 4)},
+        "stages_ms": {n: round(vv, 4) for n, vv in stage_ms.items()},
+        "hbm_stages": {
+            "rotate_pool_select": hbm(k1_bytes, k1_ms),
+            "lowrank_summary": hbm(k2_bytes, stage_ms["lowrank_summary"]),
+            "lowrank_apply_combine": "fused into the flash kernel's epilogue (no pass of its own)",
+            "rotate_pool_kernel_own_traffic": hbm(own_bytes, stage_ms["rope_pool"]),
+        },
+        "select": {"TFLOP/s": round(F["select"] / (stage_ms["select"] * 1e-3) / 1e12, 2)},
+    }
+    if ach:
+        rec["roofline"]["frac_of_achievable_gemm"] = round(flash_tf / ach["gemm_bf16_TFLOP/s"], 4)
+    if dense_reps > 0:
+        print(f"[bench] {cfg.name}: dense flash baseline", file=sys.stderr, flush=True)
+        wsd = B.workspace(B.slr_workspace_bytes(B.SLR_OP_DENSE, shape, rope), "cuda")
+        dms = _time_ms(torch, lambda: B.slr_dense_attention_fwd(q, k, v, shape, rope, out=out, ws=wsd), dense_reps)
+        dtf = F["dense"] / (dms * 1e-3) / 1e12
+        rec["dense_flash"] = {"ms": round(dms, 3), "TFLOP/s": round(dtf, 1),
+                              "frac_bf16_peak": round(dtf / PEAK_BF16_TFLOPS, 4),
+                              "speedup_of_slr_layer": round(dms / ms_mean, 2)}
+        del wsd
+    del ws, out
+    return rec, (q, k, v, params, shape, rope, sparse, lowrank)
+
+
+def args_key(cfg) -> str:
+    """The short name of a stock workload (None for a modified one)."""
+    from sparse_rank_attention_rope3d_amd import synth
+    if cfg.gate != "head" or cfg.fmap != "elu1":
+        return None
+    for key in ("wan13b", "wan14b", "hunyuan13b"):
+        if synth.by_name(key).name == cfg.name:
+            return key
+    return None
+
+
+def measure_backward(cfg, args, torch, B, dev):
+    """The layer backward (bf16): the training forward saves the selection,
+    O_sparse and the row normalisers once, then the backward is timed on a
+    seeded N(0, 1) output gradient."""
+    q, k, v, params, shape, rope, sparse, lowrank = dev
+    print(f"[bench] {cfg.name}: layer backward", file=sys.stderr, flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    dout = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    ws = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lowrank), "cuda")
+    saved = B.slr_attention_fwd_train(q, k, v, shape, rope, sparse, lowrank, ws=ws)
+    fwd_train_ms = _time_ms(torch, lambda: B.slr_attention_fwd_train(q, k, v, shape, rope, sparse, lowrank, ws=ws,
+                                                                     outs=saved), args.bwd_reps)
+    del ws
+    _, idx_s, osp_s, lse_s = saved
+    wsb = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lowrank), "cuda")
+    grads = B.slr_attention_bwd(q, k, v, idx_s, osp_s, lse_s, dout, shape, rope, sparse, lowrank, ws=wsb)
+    bms = _time_ms(torch, lambda: B.slr_attention_bwd(q, k, v, idx_s, osp_s, lse_s, dout, shape, rope, sparse,
+                                                      lowrank, ws=wsb, grads=grads), args.bwd_reps)
+    F = cfg.flops()
+    # algorithmic: S recomputed once, dP, dV, dK, dQ = 5 products of the
+    # forward's 2 over the kept tiles; low-rank: 11 (D x r) products per token
+    f_bsp = 2.5 * F["sparse"]
+    f_blr = 22.0 * cfg.B * cfg.H * cfg.L * cfg.D * cfg.rank
+    btf = (f_bsp + f_blr) / (bms * 1e-3) / 1e12
+    rec = {"ms": round(bms, 3), "TFLOP/s (algorithmic)": round(btf, 1),
+           "frac_bf16_peak": round(btf / PEAK_BF16_TFLOPS, 4),
+           "algorithmic_flops": {"sparse": f_bsp, "lowrank": f_blr},
+           "training_forward_ms": round(fwd_train_ms, 3),
+           "training_step_ms": round(fwd_train_ms + bms, 3)}
+    del wsb, grads, saved, dout
+    return rec
 
 
 def main() -> int:
@@ -264,7 +518,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="wan13b", choices=["wan13b", "wan14b", "hunyuan13b"])
+    ap.add_argument("--workload", default="wan14b", choices=["wan13b", "wan14b", "hunyuan13b"],
+                    help="headline workload (default: the Wan2.1-14B layer, L = 75600)")
+    ap.add_argument("--sub", default="wan13b,hunyuan13b",
+                    help="comma-separated workloads timed as sub-records ('' for none)")
     ap.add_argument("--gate", default="head", choices=["head", "token"],
                     help="combine gate: one scalar per head (the workloads' default) or the token-wise gate")
     ap.add_argument("--fmap", default="elu1", choices=["elu1", "silu"],
@@ -272,11 +529,14 @@ def main() -> int:
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--bwd-reps", type=int, default=3,
                     help="timed calls of the layer backward (training forward saves idx, O_sparse, lse); 0 skips")
-    ap.add_argument("--cpu-blocks", type=int, default=512, help="query blocks the CPU oracle samples")
+    ap.add_argument("--cpu-blocks", type=int, default=0,
+                    help="query blocks the CPU oracle samples (default: 64, 512 for the Wan2.1-1.3B layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the GEMM / copy / memory read probes")
     ap.add_argument("--sweep", metavar="JSONL", default=None,
                     help="time every keep-fraction x rank point of the Wan2.1-1.3B sweep against the dense "
-                         "kernel, write one JSON object per point to JSONL and exit")
+                         "kernel, append one JSON object per point to JSONL (resuming after the points it "
+                         "holds) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; used to scale "
                          "the FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -305,185 +565,99 @@ def main() -> int:
     if args.sweep:
         return run_sweep(args, torch, B, synth)
 
-    cfg = synth.by_name(args.workload)
-    if args.gate != "head" or args.fmap != "elu1":
-        import dataclasses
-        cfg = dataclasses.replace(cfg, gate=args.gate, fmap=args.fmap)
-    print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
-    q, k, v, params = make_device_inputs(cfg, torch)
-    shape, rope, sparse = B.shape_of(cfg), B.rope_of(cfg), B.sparse_of(cfg)
-    lowrank = B.lowrank_of(cfg, params)
-    ws = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lowrank), "cuda")
-    out = torch.empty_like(q)
-    torch.cuda.synchronize()
+    def workload(name):
+        cfg = synth.by_name(name)
+        if args.gate != "head" or args.fmap != "elu1":
+            import dataclasses
+            cfg = dataclasses.replace(cfg, gate=args.gate, fmap=args.fmap)
+        return cfg
 
     hip = _hip()
-    events = [[_event(hip) for _ in range(5)] for _ in range(args.steps)]
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        B.slr_attention_fwd(q, k, v, shape, rope, sparse, lowrank, out=out, ws=ws)
-    torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        B.slr_attention_fwd(q, k, v, shape, rope, sparse, lowrank, out=out, ws=ws)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    # stage times from the same number of steps of the staged call (its event
-    # records add a few microseconds between stages, so it is not the headline)
-    print(f"[bench] {args.steps} staged steps for the stage times", file=sys.stderr, flush=True)
-    for i in range(args.steps):
-        B.slr_attention_fwd_staged(q, k, v, shape, rope, sparse, lowrank, out, ws, events[i])
-    torch.cuda.synchronize()
-    stage_names = ["rope_pool", "select", "lowrank_summary", "sparse_flash"]
-    stages = {n: [] for n in stage_names}
-    for ev in events:
-        for j, n in enumerate(stage_names):
-            stages[n].append(_elapsed(hip, ev[j], ev[j + 1]))
-    stage_ms = {n: float(np.mean(vs)) for n, vs in stages.items()}
-
-    F = cfg.flops()
-    f_total = F["sparse"] + F["lowrank"] + F["select"]
-    tflops = f_total / (ms_step * 1e-3) / 1e12
-    flash_ms = stage_ms["sparse_flash"]
-    flash_tf = F["sparse"] / (flash_ms * 1e-3) / 1e12
-    es = 2 if cfg.dtype == "bf16" else 4
-    BHLD = cfg.B * cfg.H * cfg.L * cfg.D
-    rows_pad = cfg.B * cfg.H * cfg.nblk * cfg.block * cfg.D
-    # rotate + pool: read q, k (and v, for the [K | V^T] tiles of the bf16 D=128 path), write the
-    # rotated q, the k and V^T tiles (or rotated k) and the block means
-    tiled = cfg.dtype == "bf16" and cfg.D == 128 and cfg.block == 64
-    n_io = 3 if tiled else 2
-    rope_bytes = n_io * BHLD * es + n_io * rows_pad * es + 2 * cfg.B * cfg.H * cfg.nblk * cfg.D * 4
-    summ_bytes = 2 * BHLD * es
-    hbm = {
-        "rope_pool": {"GB/s": rope_bytes / (stage_ms["rope_pool"] * 1e-3) / 1e9},
-        "lowrank_summary": {"GB/s": summ_bytes / (stage_ms["lowrank_summary"] * 1e-3) / 1e9},
-    }
-    for d in hbm.values():
-        d["frac"] = d["GB/s"] / PEAK_HBM_GBS
-        d["GB/s"] = round(d["GB/s"], 1)
-        d["frac"] = round(d["frac"], 4)
-    sel_tf = F["select"] / (stage_ms["select"] * 1e-3) / 1e12
-
-    # in-library dense flash attention (RoPE inside) at the same shape
-    dense = None
-    if args.dense_reps > 0:
-        print("[bench] dense flash baseline", file=sys.stderr, flush=True)
-        wsd = B.workspace(B.slr_workspace_bytes(B.SLR_OP_DENSE, shape, rope), "cuda")
-        B.slr_dense_attention_fwd(q, k, v, shape, rope, out=out, ws=wsd)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.dense_reps):
-            B.slr_dense_attention_fwd(q, k, v, shape, rope, out=out, ws=wsd)
-        e1.record()
-        torch.cuda.synchronize()
-        dms = e0.elapsed_time(e1) / args.dense_reps
-        dtf = F["dense"] / (dms * 1e-3) / 1e12
-        dense = {"ms": round(dms, 3), "TFLOP/s": round(dtf, 1), "frac_bf16_peak": round(dtf / PEAK_BF16_TFLOPS, 4),
-                 "speedup_of_slr_layer": round(dms / ms_step, 2)}
-        del wsd
-
-    # layer backward (bf16 layers): the training
-    # forward saves the selection, O_sparse and the row normalisers once, then
-    # the backward is timed on a seeded N(0, 1) output gradient
+    cfg = workload(args.workload)
+    head, dev = measure_forward(cfg, args, torch, B, hip, dense_reps=args.dense_reps)
     backward = None
     if args.bwd_reps > 0 and cfg.dtype == "bf16":
-        print("[bench] layer backward", file=sys.stderr, flush=True)
-        gen = torch.Generator(device="cuda").manual_seed(1234)
-        dout = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        saved = B.slr_attention_fwd_train(q, k, v, shape, rope, sparse, lowrank, ws=ws)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.bwd_reps):
-            B.slr_attention_fwd_train(q, k, v, shape, rope, sparse, lowrank, ws=ws, outs=saved)
-        e1.record()
-        torch.cuda.synchronize()
-        fwd_train_ms = e0.elapsed_time(e1) / args.bwd_reps
-        _, idx_s, osp_s, lse_s = saved
-        wsb = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lowrank), "cuda")
-        grads = B.slr_attention_bwd(q, k, v, idx_s, osp_s, lse_s, dout, shape, rope, sparse, lowrank, ws=wsb)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.bwd_reps):
-            B.slr_attention_bwd(q, k, v, idx_s, osp_s, lse_s, dout, shape, rope, sparse, lowrank, ws=wsb,
-                                grads=grads)
-        e1.record()
-        torch.cuda.synchronize()
-        bms = e0.elapsed_time(e1) / args.bwd_reps
-        # algorithmic: S recomputed once, dP, dV, dK, dQ = 5 products of the
-        # forward's 2 over the kept tiles; low-rank: 11 (D x r) products per token
-        f_bsp = 2.5 * F["sparse"]
-        f_blr = 22.0 * cfg.B * cfg.H * cfg.L * cfg.D * cfg.rank
-        btf = (f_bsp + f_blr) / (bms * 1e-3) / 1e12
-        backward = {"ms": round(bms, 3), "TFLOP/s (algorithmic)": round(btf, 1),
-                    "frac_bf16_peak": round(btf / PEAK_BF16_TFLOPS, 4),
-                    "algorithmic_flops": {"sparse": f_bsp, "lowrank": f_blr},
-                    "training_forward_ms": round(fwd_train_ms, 3),
-                    "training_step_ms": round(fwd_train_ms + bms, 3)}
-        if not args.no_cpu_baseline:
+        backward = measure_backward(cfg, args, torch, B, dev)
+    del dev
+    torch.cuda.empty_cache()
+
+    subs = []
+    for name in [s for s in args.sub.split(",") if s and s != args.workload]:
+        rec, dev = measure_forward(workload(name), args, torch, B, hip, dense_reps=args.dense_reps)
+        subs.append(rec)
+        del dev
+        torch.cuda.empty_cache()
+
+    ach = probe = None
+    if not args.no_probe:
+        print("[bench] achievable GEMM and copy rates, memory read probe", file=sys.stderr, flush=True)
+        ach = achievable_peaks(torch)
+        probe = memory_read_probe(torch)
+        for rec in [head] + subs:
+            rec["roofline"]["frac_of_achievable_gemm"] = round(rec["roofline"]["achieved"] / ach["gemm_bf16_TFLOP/s"],
+                                                               4)
+            for st in rec["hbm_stages"].values():
+                if isinstance(st, dict):
+                    st["frac_of_copy"] = round(st["GB/s"] / ach["copy_GB/s"], 4)
+
+    cpu = None
+    f_total = head["flops"]["sparse"] + head["flops"]["lowrank"] + head["flops"]["select"]
+    cpuinfo = host_cpu()
+    if not args.no_cpu_baseline:
+        blocks = args.cpu_blocks or (512 if cfg.nblk <= 512 else 64)
+        print(f"[bench] CPU oracle baseline ({blocks} sampled query blocks of one slice)", file=sys.stderr,
+              flush=True)
+        layer_s, info = cpu_baseline(cfg, blocks)
+        value = f_total / layer_s / 1e12
+        n = cpuinfo["nproc"]
+        cpu = {"value": value, "unit": "TFLOP/s (effective)", "cores": 1, "kind": "oracle",
+               "ms_per_layer": round(layer_s * 1e3, 1),
+               "sample": f"one (b,h) slice of {cfg.B * cfg.H} of {cfg.name}: full selection and summary, "
+                         f"{info['sampled_blocks']} of {cfg.nblk} query blocks of the sparse branch and readout, "
+                         f"fp64 single thread, {info['measured_s']} s measured, extrapolated linearly to the layer",
+               "host_cpu": cpuinfo["model"], "nproc": n,
+               "ideal_n_core": {"cores": n, "value": value * n, "ms_per_layer": round(layer_s * 1e3 / n, 1),
+                                "what": "the single-thread figure times the usable cores (slices are independent)"}}
+        if backward is not None:
             print("[bench] CPU oracle baseline of the backward", file=sys.stderr, flush=True)
-            bs_s, binfo = cpu_backward_baseline(cfg, max(1, args.cpu_blocks // 16))
+            bs_s, binfo = cpu_backward_baseline(cfg, 4 if cfg.nblk > 512 else 32)
+            fb = backward["algorithmic_flops"]["sparse"] + backward["algorithmic_flops"]["lowrank"]
             backward["cpu_baseline"] = {
-                "value": (f_bsp + f_blr) / bs_s / 1e12, "unit": "TFLOP/s (algorithmic)", "cores": 1,
-                "kind": "oracle", "ms_per_layer": round(bs_s * 1e3, 1),
+                "value": fb / bs_s / 1e12, "unit": "TFLOP/s (algorithmic)", "cores": 1, "kind": "oracle",
+                "ms_per_layer": round(bs_s * 1e3, 1), "host_cpu": cpuinfo["model"], "nproc": cpuinfo["nproc"],
                 "sample": f"one (b,h) slice of {cfg.B * cfg.H}: the whole low-rank backward and the sparse backward "
                           f"of {binfo['sampled_blocks']} of {cfg.nblk} query blocks, numpy fp64 with BLAS on one "
                           f"thread, {binfo['measured_s']} s measured, extrapolated linearly to the layer"}
-        del wsb, grads, saved, dout
 
-    print("[bench] achievable GEMM and copy rates", file=sys.stderr, flush=True)
-    ach = achievable_peaks(torch)
-    for d in hbm.values():
-        d["frac_of_copy"] = round(d["GB/s"] / ach["copy_GB/s"], 4)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        layer_s, info = cpu_baseline(cfg, args.cpu_blocks)
-        cpu = {"value": f_total / layer_s / 1e12, "unit": "TFLOP/s (effective)", "cores": 1, "kind": "oracle",
-               "ms_per_layer": round(layer_s * 1e3, 1),
-               "sample": f"one (b,h) slice of {cfg.B * cfg.H}: full selection and summary, "
-                         f"{info['sampled_blocks']} of {cfg.nblk} query blocks of the sparse branch and readout, "
-                         f"fp64 single thread, {info['measured_s']} s measured, extrapolated linearly to the layer"}
-
+    ms = head["ms_per_layer"]["mean"]
     line = {
-        "metric": "SLR attn fwd ms/layer + effective TFLOP/s at L=32760/75600/118800, 1 GPU",
-        "value": round(tflops, 2),
+        "metric": METRIC,
+        "value": head["effective_TFLOP/s"],
         "unit": "TFLOP/s (effective)",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded clustered Q/K, Gaussian V; random-init projections)",
-        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "D": cfg.D, "L": cfg.L,
-                   "grid": [cfg.T, cfg.Hg, cfg.Wg], "block": cfg.block, "keep": cfg.keep, "nblk": cfg.nblk,
-                   "rank": cfg.rank, "lowrank": cfg.lr_mode, "gate": cfg.gate, "fmap": cfg.fmap,
-                   "parallelism": "single GPU"},
-        "roofline": {"kernel": "k_flash_tiled (block-sparse flash + low-rank readout + combine)",
-                     "bound": "mfma", "achieved": round(flash_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(flash_tf / PEAK_BF16_TFLOPS, 4), "traffic": flash_traffic(args.workload),
-                     "algorithmic_flops_per_launch": F["sparse"], "avg_launch_ms": round(flash_ms, 4),
-                     "frac_of_achievable_gemm": round(flash_tf / ach["gemm_bf16_TFLOP/s"], 4)},
-        "achievable": ach,
-        "stages_ms": {n: round(vv, 4) for n, vv in stage_ms.items()},
-        "hbm_stages": hbm,
-        "select": {"TFLOP/s": round(sel_tf, 2), "frac_fp32_peak": round(sel_tf / PEAK_FP32_TFLOPS, 4)},
-        "dense_flash": dense,
+        "config": head["config"],
+        "ms_per_layer": head["ms_per_layer"],
+        "roofline": head["roofline"],
+        "stages_ms": head["stages_ms"],
+        "hbm_stages": head["hbm_stages"],
+        "select": head["select"],
+        "dense_flash": head.get("dense_flash"),
+        "dense_equivalent_TFLOP/s": head["dense_equivalent_TFLOP/s"],
         "backward": backward,
         "cpu_baseline": cpu,
+        "achievable": ach,
+        "memory_read_probe": probe,
+        "workloads": {r["config"]["workload"]: r for r in subs},
     }
     print(json.dumps(line))
-    for ev in events:
-        for e in ev:
-            hip.hipEventDestroy(ctypes.c_void_p(e))
     return 0
 
 

@@ -219,11 +219,14 @@ int slr_dense_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, co
  *     dWg [H,D] and dbg [H] fp32 (sums over batch and rows) replace dgate.
  * The selection is held fixed: idx [B,H,nblk,keep] int32 is the forward's
  * (idx_out of slr_attention_fwd_train); each row must list distinct blocks
- * in [0, nblk) (entries outside that range are skipped). o_sparse
- * [B,H,L,D] and lse [B,H,L] fp32 are that call's o_sparse_out and lse_out
- * (the softmax normalisers are reused, not recomputed), for the same q, k,
- * v and configuration. dout, dq, dk, dv: [B,H,L,D] bf16;
- * dq, dk, dv must not overlap each other or any input. dWq, dWk: [H,D,r]
+ * in [0, nblk): entries outside that range are skipped, and a row that
+ * lists a block twice gives undefined gradients (the forward's selection
+ * never does). o_sparse [B,H,L,D] and lse [B,H,L] fp32 are that call's
+ * o_sparse_out and lse_out (the softmax normalisers are reused, not
+ * recomputed), for the same q, k, v and configuration. dout, dq, dk, dv:
+ * [B,H,L,D] of shape->dtype (bf16 or fp32, like q, k, v); the byte ranges
+ * of dq, dk and dv may not overlap each other or those of q, k, v,
+ * o_sparse, dout (SLR_EINVAL). dWq, dWk: [H,D,r]
  * fp32, all overwritten (sums over the batch); dgate [H] fp32 for
  * SLR_GATE_HEAD (dWg, dbg ignored, may be NULL), dWg [H,D] and dbg [H]
  * fp32 for SLR_GATE_TOKEN (dgate ignored, may be NULL).

@@ -132,7 +132,7 @@ def lowrank_of(layer, params: Dict[str, torch.Tensor]) -> SlrLowrankCfg:
     token = getattr(layer, "gate", "head") == "token"
     return SlrLowrankCfg(layer.rank, SLR_LR_ABS_PE if abspe else SLR_LR_ROPE_OUTSIDE, lp[0], lp[1], lp[2],
                          float(layer.eps), params["wq"].data_ptr(), params["wk"].data_ptr(),
-                         params["gate"].data_ptr(),
+                         None if token else params["gate"].data_ptr(),
                          params["et"].data_ptr() if abspe else None,
                          params["eh"].data_ptr() if abspe else None,
                          params["ew"].data_ptr() if abspe else None,

@@ -17,6 +17,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libslr.so")
 SOURCES = ["k_rope.hip", "k_select.hip", "k_lowrank.hip", "k_flash.hip", "k_backward.hip", "slr_api.cpp"]
+# the bench's memory-hierarchy read probe, a library of its own (not part of the layer's ABI)
+PROBE_OUT = os.path.join(PKG, "libslr_probe.so")
+PROBE_SOURCES = ["probe_stream.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -35,18 +38,24 @@ def _compile(src: str, obj: str, extra) -> None:
         sys.stderr.write("\n".join(noise) + "\n")
 
 
-def build(extra=(), jobs: int = 8) -> str:
-    bdir = os.path.join(CSRC, "_build")
-    os.makedirs(bdir, exist_ok=True)
-    objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
-        list(ex.map(lambda so: _compile(so[0], so[1], list(extra)), zip(SOURCES, objs)))
-    tmp = OUT + ".tmp%d" % os.getpid()
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(extra=(), jobs: int = 8) -> str:
+    bdir = os.path.join(CSRC, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in srcs]
+    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
+        list(ex.map(lambda so: _compile(so[0], so[1], list(extra)), zip(srcs, objs)))
+    _link(objs[:len(SOURCES)], OUT)
+    _link(objs[len(SOURCES):], PROBE_OUT)
     return OUT
 
 

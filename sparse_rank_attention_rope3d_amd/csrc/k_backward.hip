@@ -1485,7 +1485,9 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
     const long L = a.L;
     const long t_lo = (long)split * a.chunk;
     const long t_hi = t_lo + a.chunk < L ? t_lo + a.chunk : L;
-    const float gh = a.gate[head];
+    const bool token = a.token != 0;
+    // the per-head gate exists only in head mode (the token gate passes no gate array)
+    const float gh = token ? 0.f : a.gate[head];
     const bool silu = a.g.fmap != 0;
     for (int e = tid; e < D * R; e += 256) {
         const float x = a.Wq[(long)head * D * R + e];
@@ -1505,7 +1507,6 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
     const size_t es = BF ? 2 : 4;
     const void* qs = (const char*)(const void*)a.q + bh * L * D * es;
     const void* gs = (const char*)(const void*)a.dout + bh * L * D * es;
-    const bool token = a.token != 0;
     const float* wgh = token ? a.wg + (long)head * D : nullptr;
     const float bgh = token ? a.bg[head] : 0.f;
     // 4 dims of the forward's O_sparse (zero past t_hi)

@@ -144,12 +144,10 @@ void summary_split(const Dims& d, int slots, int* chunk, int* nsplit) {
     *nsplit = (int)best_n;
 }
 
-// The backward covers every forward setting (either gate, either low-rank
-// variant, either feature map, bf16 or fp32 layers).
-int check_bwd_supported(const Dims& d, const slr_lowrank_cfg* lr) {
-    (void)d;
-    (void)lr;
-    return SLR_OK;
+// Whether the byte ranges [a, a + n) and [b, b + n) share a byte.
+bool overlaps(const void* a, const void* b, size_t n) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + n && y < x + n;
 }
 
 // Workspace layout (byte offsets, each 256-byte aligned).
@@ -329,7 +327,6 @@ int slr_workspace_bytes(int op, const slr_shape* shape, const slr_rope_cfg* rope
         if ((st = check_lowrank(&probe, rope, d, op != SLR_OP_LOWRANK_SUMMARY, &lg, &RP))) return st;
         R = lowrank->rank;
     }
-    if (op == SLR_OP_ATTENTION_BWD && (st = check_bwd_supported(d, lowrank))) return st;
     *bytes = layout(op, d, g, bs, nblk, keep, R, RP, lowrank && lowrank->mode == SLR_LR_ABS_PE,
                     lowrank && lowrank->gate_mode == SLR_GATE_TOKEN).total;
     return SLR_OK;
@@ -597,16 +594,18 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     if (abspe && (!dEt || !dEh || !dEw || !aligned(dEt, 4) || !aligned(dEh, 4) || !aligned(dEw, 4)))
         return SLR_EINVAL;
     {
+        // dq, dk, dv ([B,H,L,D] each) may share no byte with each other or
+        // with the [B,H,L,D] inputs
+        const size_t nb = (size_t)d.es * d.BH * d.L * d.D;
         const void* outs[3] = {dq, dk, dv};
         const void* ins[5] = {q, k, v, o_sparse, dout};
         for (int i = 0; i < 3; ++i) {
             for (int j = 0; j < 5; ++j)
-                if (outs[i] == ins[j]) return SLR_EINVAL;
+                if (overlaps(outs[i], ins[j], nb)) return SLR_EINVAL;
             for (int j = i + 1; j < 3; ++j)
-                if (outs[i] == outs[j]) return SLR_EINVAL;
+                if (overlaps(outs[i], outs[j], nb)) return SLR_EINVAL;
         }
     }
-    if ((st = check_bwd_supported(d, lowrank))) return st;
     lg.rope = g;
     const int bs = sparse->block, keep = sparse->keep, R = lowrank->rank;
     Layout w = layout(SLR_OP_ATTENTION_BWD, d, g, bs, nblk, keep, R, RP, abspe, token);

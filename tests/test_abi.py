@@ -177,10 +177,14 @@ def test_other_entry_points_validate():
     assert L.slr_workspace_bytes(B.SLR_OP_ATTENTION, r(shape), r(rope), None, r(lr), r(n)) == B.SLR_EINVAL
 
 
-def _bwd(shape, rope, sparse, lr, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, idx=FAKE + 0x3000, osp=FAKE + 0x4000,
-         lse=FAKE + 0xc000, dout=FAKE + 0x5000, dq=FAKE + 0x6000, dk=FAKE + 0x7000, dv=FAKE + 0x8000,
-         dwq=FAKE + 0x9000, dwk=FAKE + 0xa000, dg=FAKE + 0xb000, dwg=FAKE + 0x10000, dbg=FAKE + 0x11000,
-         det=FAKE + 0xd000, deh=FAKE + 0xe000, dew=FAKE + 0xf000, ws=None, ws_bytes=0):
+GIB = 2 ** 30   # the [B,H,L,D] fakes below sit 1 GiB apart: their byte ranges do not overlap
+
+
+def _bwd(shape, rope, sparse, lr, q=FAKE, k=FAKE + GIB, v=FAKE + 2 * GIB, idx=FAKE + 8 * GIB + 0x3000,
+         osp=FAKE + 3 * GIB, lse=FAKE + 8 * GIB + 0xc000, dout=FAKE + 4 * GIB, dq=FAKE + 5 * GIB, dk=FAKE + 6 * GIB,
+         dv=FAKE + 7 * GIB, dwq=FAKE + 8 * GIB + 0x9000, dwk=FAKE + 8 * GIB + 0xa000, dg=FAKE + 8 * GIB + 0xb000,
+         dwg=FAKE + 8 * GIB + 0x10000, dbg=FAKE + 8 * GIB + 0x11000, det=FAKE + 8 * GIB + 0xd000,
+         deh=FAKE + 8 * GIB + 0xe000, dew=FAKE + 8 * GIB + 0xf000, ws=None, ws_bytes=0):
     r = ctypes.byref
     return B.lib().slr_attention_bwd(r(shape), r(rope), r(sparse), r(lr), q, k, v, idx, osp, lse, dout, dq, dk, dv,
                                      dwq, dwk, dg, dwg, dbg, det, deh, dew, ws, ws_bytes, None)
@@ -198,10 +202,17 @@ def test_backward_validates_before_launching():
         assert _bwd(shape, rope, sparse, lr, **{bad: None}) == B.SLR_EINVAL, bad
     assert _bwd(shape, rope, sparse, lr, idx=FAKE + 2) == B.SLR_EINVAL
     assert _bwd(shape, rope, sparse, lr, dk=MISALIGNED) == B.SLR_EINVAL
-    # outputs may not alias an input or each other
+    # outputs may not share a byte with an input or with each other
+    nbytes = 2 * layer.B * layer.H * layer.L * layer.D
     assert _bwd(shape, rope, sparse, lr, dq=FAKE) == B.SLR_EINVAL
-    assert _bwd(shape, rope, sparse, lr, dv=FAKE + 0x2000) == B.SLR_EINVAL
-    assert _bwd(shape, rope, sparse, lr, dk=FAKE + 0x6000) == B.SLR_EINVAL
+    assert _bwd(shape, rope, sparse, lr, dv=FAKE + 2 * GIB + 0x2000) == B.SLR_EINVAL
+    assert _bwd(shape, rope, sparse, lr, dk=FAKE + 5 * GIB + 0x6000) == B.SLR_EINVAL
+    # partial overlaps: the last bytes of an input, the first bytes of another output
+    assert _bwd(shape, rope, sparse, lr, dq=FAKE + 4 * GIB + nbytes - 16) == B.SLR_EINVAL
+    assert _bwd(shape, rope, sparse, lr, dk=FAKE + 7 * GIB - nbytes + 16) == B.SLR_EINVAL
+    # adjacent ranges are fine (the call then stops at the missing workspace)
+    assert _bwd(shape, rope, sparse, lr, dq=FAKE + 4 * GIB + nbytes) == B.SLR_EWORKSPACE
+    assert _bwd(shape, rope, sparse, lr, dk=FAKE + 7 * GIB - nbytes) == B.SLR_EWORKSPACE
 
 
 def test_backward_absolute_pe_needs_the_table_gradients():

@@ -250,6 +250,14 @@ def test_backward_wan13b_sampled():
     _check(cfg, slices=[(0, 0), (1, 7)], qsample=4, ksample=4)
 
 
+def test_backward_wan14b_sampled():
+    """Full Wan2.1-14B shape (1182 blocks, 119 kept: long kept and inverse
+    lists through the two-slot rings of the streaming kernels): sampled rows
+    of two slices as above."""
+    cfg = synth.wan14b()
+    _check(cfg, slices=[(0, 0), (1, 39)], qsample=2, ksample=2)
+
+
 def test_backward_hunyuan13b_sampled():
     """Full HunyuanVideo-13B shape (absolute-PE low-rank variant): sampled
     rows of two slices as above; the E tables' gradients over all slices."""
@@ -257,8 +265,12 @@ def test_backward_hunyuan13b_sampled():
     _check(cfg, slices=[(0, 0), (0, 11)], qsample=3, ksample=2)
 
 
-def test_backward_is_deterministic():
-    cfg = dataclasses.replace(synth.wan13b(), name="bwd determinism", B=1, H=2, T=4, Hg=9, Wg=13, keep=3)
+@pytest.mark.parametrize("grid,keep", [((4, 9, 13), 3), ((21, 30, 52), 52)], ids=["small", "wan13b-grid"])
+def test_backward_is_deterministic(grid, keep):
+    """Bitwise reproducible gradients; the Wan2.1-1.3B grid gives kept and
+    inverse lists of dozens of tiles (many turns of the two-slot rings)."""
+    cfg = dataclasses.replace(synth.wan13b(), name="bwd determinism", B=1, H=2, T=grid[0], Hg=grid[1], Wg=grid[2],
+                              keep=keep)
     _, _, g1, _ = _run_gpu(cfg)
     _, _, g2, _ = _run_gpu(cfg)
     for a, b in zip(g1[:6], g2[:6]):

@@ -174,8 +174,10 @@ def test_token_gate_very_negative_bias_gives_sparse_branch(dtype):
     assert torch.equal(out, o_sp)
 
 
-def test_runs_are_bitwise_reproducible():
-    cfg = T.custom(synth.wan13b(), name="repro", B=1, H=4, T=4, Hg=9, Wg=13, keep=5)
+@pytest.mark.parametrize("grid,keep", [((4, 9, 13), 5), ((21, 30, 52), 52)], ids=["small", "wan13b-grid"])
+def test_runs_are_bitwise_reproducible(grid, keep):
+    cfg = T.custom(synth.wan13b(), name="repro", B=1, H=4 if grid[0] == 4 else 2, T=grid[0], Hg=grid[1], Wg=grid[2],
+                   keep=keep)
     inp = T.make_inputs(cfg)
     a = T.run_layer(inp)
     b = T.run_layer(inp)
@@ -254,9 +256,24 @@ def test_keep_all_equals_dense_plus_lowrank():
 
 # ---- full-size layers (sampled query blocks) -----------------------------
 
-def _big(cfg, slices, nq=6):
+# oracle block scores per (seed, shape, b, h): they do not depend on keep or
+# rank, so the sweep points reuse them
+_SCORES = {}
+
+
+def _oracle_scores(cfg, b, h):
+    key = (cfg.seed, cfg.gen, cfg.B, cfg.H, cfg.D, cfg.T, cfg.Hg, cfg.Wg, cfg.block, cfg.base, cfg.pairs, b, h)
+    if key not in _SCORES:
+        qs, ks, _ = synth.qkv_slice(cfg, b, h)
+        grid = (cfg.T, cfg.Hg, cfg.Wg)
+        rq, rk = oracle.rope3d(qs, grid, cfg.base, cfg.pairs), oracle.rope3d(ks, grid, cfg.base, cfg.pairs)
+        _SCORES[key] = oracle.block_scores(oracle.block_mean(rq, cfg.block), oracle.block_mean(rk, cfg.block))
+    return _SCORES[key]
+
+
+def _big(cfg, slices, nq=6, inp=None):
     T.log(f"  case {cfg.name} (full size), slices {slices}")
-    inp = T.make_inputs(cfg)
+    inp = T.make_inputs(cfg) if inp is None else inp
     out, idx, o_sp, o_lr = T.run_layer(inp)
     S, z = _summary(inp)
     torch.cuda.synchronize()
@@ -266,10 +283,7 @@ def _big(cfg, slices, nq=6):
         for h in range(cfg.H):
             if (b, h) in slices:
                 continue
-            qs, ks, _ = synth.qkv_slice(cfg, b, h)
-            grid = (cfg.T, cfg.Hg, cfg.Wg)
-            rq, rk = oracle.rope3d(qs, grid, cfg.base, cfg.pairs), oracle.rope3d(ks, grid, cfg.base, cfg.pairs)
-            s = oracle.block_scores(oracle.block_mean(rq, cfg.block), oracle.block_mean(rk, cfg.block))
+            s = _oracle_scores(cfg, b, h)
             _, thr, _ = oracle.topk_blocks(s, cfg.keep)
             T.check_selection(idx[b, h].cpu().numpy(), s, thr, cfg.keep)
     del inp, out, idx, o_sp, o_lr
@@ -291,8 +305,30 @@ def test_hunyuan13b_full_size():
     _big(synth.hunyuan13b(), [(0, 0), (0, 23)], nq=4)
 
 
+_SWEEP_QKV = {}
+
+
+def _sweep_inputs(cfg):
+    """Inputs of a sweep point: q, k, v are the same for every point (same
+    seed and shape) and stay on the device; the projections follow the rank."""
+    if "qkv" not in _SWEEP_QKV:
+        _SWEEP_QKV.clear()
+        base = T.make_inputs(cfg)
+        _SWEEP_QKV["qkv"] = (base.q, base.k, base.v)
+    q, k, v = _SWEEP_QKV["qkv"]
+    pn = synth.lowrank_params(cfg)
+    pd = {key: torch.from_numpy(val).to("cuda") for key, val in pn.items()}
+    return T.Inputs(cfg, q, k, v, pn, pd)
+
+
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("point", [0, 5, 9, 14])
+@pytest.mark.parametrize("point", range(15), ids=[f"keep{p.keep}-r{p.rank}" for p in synth.sweep()])
 def test_sweep_points(point):
+    """Every keep x rank point of the Wan2.1-1.3B sweep (keep 26/52/103/256/512
+    of 512, ranks 16/32/64): the selection of all 24 slices, outputs and S, z
+    of two slices on sampled query blocks."""
     cfg = synth.sweep()[point]
-    _big(cfg, [(0, 3), (1, 8)], nq=3)
+    _big(cfg, [(0, 3), (1, 8)], nq=2, inp=_sweep_inputs(cfg))
+    if point == len(synth.sweep()) - 1:
+        _SWEEP_QKV.clear()
+        torch.cuda.empty_cache()
