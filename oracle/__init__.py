@@ -60,7 +60,7 @@ def _load():
         lib.orc_topk_blocks.argtypes = [ctypes.c_long, ctypes.c_int, _dp, _ip, _dp, _dp]
         lib.orc_block_sparse_attention.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                    _dp, _dp, _dp, _ip, ctypes.c_int, _ip, _dp]
-        lib.orc_lowrank_features.argtypes = [ctypes.c_int] * 5 + [_dp] * 5 + [ctypes.c_int, _dp]
+        lib.orc_lowrank_features.argtypes = [ctypes.c_int] * 5 + [_dp] * 5 + [ctypes.c_int, _dp, _dp]
         lib.orc_lowrank_rotate.argtypes = [ctypes.c_int] * 3 + [i3, ctypes.c_int, ctypes.c_double, i3, i3, _dp, _dp]
         lib.orc_lowrank_summary.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp, _dp]
         lib.orc_lowrank_readout.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _lp, _dp, _dp, _dp, _dp,
@@ -149,17 +149,24 @@ def dense_attention(qr, kr, v, bs) -> np.ndarray:
     return block_sparse_attention(qr, kr, v, bs, idx).reshape(-1, qr.shape[1])[:L]
 
 
-FMAPS = {"elu1": 0, "silu": 1}
+FMAPS = {"elu1": 0, "silu": 1, "favor": 2}
 
 
-def lowrank_features(x, W, grid, E=None, fmap="elu1") -> np.ndarray:
-    """phi(x W [+ E]) per token; fmap "elu1" (elu + 1) or "silu"."""
+def lowrank_features(x, W, grid, E=None, fmap="elu1", omega=None) -> np.ndarray:
+    """phi(x W [+ E]) per token; fmap "elu1" (elu + 1), "silu", or "favor"
+    (positive random features exp(omega p - |p|^2/2) / sqrt(r) of p = x W
+    [+ E], omega [r, r] the random directions)."""
     x, W = _d(x), _d(W)
     T, Hg, Wg = grid
     D, r = W.shape
     u = np.empty((x.shape[0], r))
     et, eh, ew = (None, None, None) if E is None else tuple(_d(e) for e in E)
-    _load().orc_lowrank_features(T, Hg, Wg, D, r, _p(x), _p(W), _p(et), _p(eh), _p(ew), FMAPS[fmap], _p(u))
+    om = None
+    if fmap == "favor":
+        om = _d(omega)
+        assert om.shape == (r, r)
+    _load().orc_lowrank_features(T, Hg, Wg, D, r, _p(x), _p(W), _p(et), _p(eh), _p(ew), FMAPS[fmap], _p(om),
+                                 _p(u))
     return u
 
 
@@ -171,6 +178,45 @@ def lowrank_rotate(u, grid, base, pairs, lr_pairs, origin=(0, 0, 0)) -> np.ndarr
     ur = np.empty_like(u)
     _load().orc_lowrank_rotate(T, Hg, Wg, _i3(origin), r, float(base), _i3(pairs), _i3(lr_pairs), _p(u), _p(ur))
     return ur
+
+
+LR_ORDERS = ("outside", "inside", "none")
+
+
+def lowrank_branch(q, k, v, wq, wk, grid, base, pairs, lr_pairs, order="outside", eps=1e-6, fmap="elu1",
+                   omega=None, rows=None):
+    """The rank-r branch with the rotation placed as ``order`` says (RoLA
+    §4.3 and §5.1 / Table 2, the design and its two controls):
+      "outside": rho(phi(x W)), the rotation after the activation (RoLA);
+      "inside":  phi(rho(x W)), the rotation before the activation;
+      "none":    phi(x W), no positional rotation.
+    Numerator features fq, fk as above; the normaliser uses phi(x W) for
+    "outside" (the un-rotated features, as the layer does) and the numerator
+    features themselves otherwise. Returns (O_lr [rows, D], fq, fk, w, u)
+    with w, u the normaliser features."""
+    if order == "outside":
+        w = lowrank_features(q, wq, grid, fmap=fmap, omega=omega)
+        u = lowrank_features(k, wk, grid, fmap=fmap, omega=omega)
+        fq = lowrank_rotate(w, grid, base, pairs, lr_pairs)
+        fk = lowrank_rotate(u, grid, base, pairs, lr_pairs)
+    elif order == "inside":
+        # the projection x W as features of the identity map, rotated, then phi
+        r = _d(wq).shape[1]
+        pq = _d(q) @ _d(wq)
+        pk = _d(k) @ _d(wk)
+        eye = np.eye(r)
+        fq = w = lowrank_features(lowrank_rotate(pq, grid, base, pairs, lr_pairs), eye, (pq.shape[0], 1, 1),
+                                  fmap=fmap, omega=omega)
+        fk = u = lowrank_features(lowrank_rotate(pk, grid, base, pairs, lr_pairs), eye, (pk.shape[0], 1, 1),
+                                  fmap=fmap, omega=omega)
+    elif order == "none":
+        fq = w = lowrank_features(q, wq, grid, fmap=fmap, omega=omega)
+        fk = u = lowrank_features(k, wk, grid, fmap=fmap, omega=omega)
+    else:
+        raise ValueError(order)
+    S, z = lowrank_summary(fk, u, v)
+    o = lowrank_readout(fq, w, S, z, eps, rows, count=float(_d(q).shape[0]) if fmap == "silu" else 0.0)
+    return o, fq, fk, w, u
 
 
 def lowrank_summary(fk, u, v):
@@ -206,7 +252,7 @@ def token_gate(q, wg, bg, o_sp, o_lr, eps):
 # one (b, h) slice of the whole layer
 
 def layer_slice(cfg, q, k, v, wq, wk, gate_h, E=None, qblocks=None, idx=None,
-                origin=(0, 0, 0), token_gate_wb=None) -> Dict[str, np.ndarray]:
+                origin=(0, 0, 0), token_gate_wb=None, omega=None) -> Dict[str, np.ndarray]:
     """Forward of one (b, h) slice.
 
     ``cfg`` supplies T, Hg, Wg, base, pairs, block, keep, lr_mode, lr_pairs
@@ -216,7 +262,9 @@ def layer_slice(cfg, q, k, v, wq, wk, gate_h, E=None, qblocks=None, idx=None,
     Returns the intermediates: q_rot, k_rot, qbar, kbar, scores, idx_ref,
     thr, next, S, z, o_sp, o_lr, out (the last three as [nq, bs, D]).
     ``token_gate_wb = (wg [D], bg)`` replaces the per-head gate by the
-    token-wise gate of RoLA §4.4 (then also returns ``g`` per row)."""
+    token-wise gate of RoLA §4.4 (then also returns ``g`` per row).
+    ``omega`` [r, r] are the head's random directions when cfg.fmap is
+    "favor" (positive random features)."""
     grid = (cfg.T, cfg.Hg, cfg.Wg)
     L, bs = cfg.T * cfg.Hg * cfg.Wg, cfg.block
     nblk = (L + bs - 1) // bs
@@ -234,13 +282,13 @@ def layer_slice(cfg, q, k, v, wq, wk, gate_h, E=None, qblocks=None, idx=None,
 
     fmap = getattr(cfg, "fmap", "elu1")
     if cfg.lr_mode == "rola":
-        u = lowrank_features(k, wk, grid, fmap=fmap)
-        w = lowrank_features(q, wq, grid, fmap=fmap)
+        u = lowrank_features(k, wk, grid, fmap=fmap, omega=omega)
+        w = lowrank_features(q, wq, grid, fmap=fmap, omega=omega)
         fk = lowrank_rotate(u, grid, cfg.base, cfg.pairs, cfg.lr_pairs, origin)
         fq = lowrank_rotate(w, grid, cfg.base, cfg.pairs, cfg.lr_pairs, origin)
     else:
-        u = lowrank_features(k, wk, grid, E, fmap=fmap)
-        w = lowrank_features(q, wq, grid, E, fmap=fmap)
+        u = lowrank_features(k, wk, grid, E, fmap=fmap, omega=omega)
+        w = lowrank_features(q, wq, grid, E, fmap=fmap, omega=omega)
         fk, fq = u, w
     res["S"], res["z"] = S, z = lowrank_summary(fk, u, v)
     rows = (qblocks[:, None].astype(np.int64) * bs + np.arange(bs)[None, :]).reshape(-1)

@@ -223,11 +223,23 @@ static double silu(double x) { return x / (1.0 + exp(-x)); }
  * raw, position-free content features (E tables NULL); the absolute-PE
  * variant ([RoPeSLR] abstract: learnable 3D absolute positional embedding
  * injection) adds the per-axis tables before phi.
+ *
+ * fmap 0: phi = elu + 1; 1: SiLU (per component).
+ * fmap 2: positive random features of the exponential kernel (FAVOR+ of
+ * Performers, which the [RoPeSLR] appendix uses to linearise the softmax
+ * exponential while keeping the branch low-rank): with p = x_l W [+ E] in
+ * R^r and r random directions omega_c (rows of omega [r, r], drawn by the
+ * caller from N(0, I_r)),
+ *     u_c = exp(omega_c . p - |p|^2 / 2) / sqrt(r),
+ * so that E_omega[u(p) . u(p')] = exp(p . p'). omega is ignored (may be
+ * NULL) for fmap 0 and 1.
  */
 void orc_lowrank_features(int T, int Hg, int Wg, int D, int r, const double *x, const double *W,
-                          const double *Et, const double *Eh, const double *Ew, int fmap, double *u)
+                          const double *Et, const double *Eh, const double *Ew, int fmap,
+                          const double *omega, double *u)
 {
     long L = (long)T * Hg * Wg;
+    double *p = (double *)malloc(sizeof(double) * (size_t)r);
     for (long l = 0; l < L; ++l) {
         int t, h, w;
         token_coords(l, Hg, Wg, &t, &h, &w);
@@ -235,9 +247,21 @@ void orc_lowrank_features(int T, int Hg, int Wg, int D, int r, const double *x, 
             double acc = 0.0;
             for (int d = 0; d < D; ++d) acc += x[l * D + d] * W[(long)d * r + c];
             if (Et) acc += Et[(long)t * r + c] + Eh[(long)h * r + c] + Ew[(long)w * r + c];
-            u[l * r + c] = fmap ? silu(acc) : phi(acc);
+            p[c] = acc;
+        }
+        if (fmap == 2) {
+            double sq = 0.0;
+            for (int c = 0; c < r; ++c) sq += p[c] * p[c];
+            for (int c = 0; c < r; ++c) {
+                double dot = 0.0;
+                for (int j = 0; j < r; ++j) dot += omega[(long)c * r + j] * p[j];
+                u[l * r + c] = exp(dot - 0.5 * sq) / sqrt((double)r);
+            }
+        } else {
+            for (int c = 0; c < r; ++c) u[l * r + c] = fmap ? silu(p[c]) : phi(p[c]);
         }
     }
+    free(p);
 }
 
 /*

@@ -11,6 +11,7 @@ a full-width linear branch costs 4 B H L D^2) and RoLA App. F (equal
 leading matmul FLOPs at r = D/2).
 """
 import itertools
+import math
 
 import numpy as np
 import pytest
@@ -275,3 +276,150 @@ def test_silu_layer_uses_mean_readout_and_token_gate_ignores_the_scale():
     out2, _ = oracle.token_gate(qrows, wg, bg, res["o_sp"].reshape(-1, D)[valid], unnorm, cfg.eps)
     # (rows whose low-rank RMS is tiny still feel eps = 1e-12 at ~1e-11)
     np.testing.assert_allclose(res["out"].reshape(-1, D)[valid], out2, rtol=1e-9, atol=1e-10)
+
+
+# ---- rotation order: RoLA §5.1 / Table 2 (outside vs inside vs no RoPE) ----
+
+def _offset_range(weights, coords):
+    """Spread over the offsets of the numerator weight (one representative
+    per offset), relative to the largest weight: zero for a position-blind
+    map."""
+    groups = {}
+    for a, b in itertools.product(range(len(coords)), repeat=2):
+        groups.setdefault(tuple(coords[b] - coords[a]), []).append(weights[a, b])
+    reps = np.array([g[0] for g in groups.values()])
+    return float(np.ptp(reps) / np.abs(weights).max())
+
+
+@pytest.mark.parametrize("fmap", ["elu1", "silu", "favor"])
+def test_rotation_order_controls_match_table2_contrast(fmap):
+    """Content-controlled input (the same q and k row at every token), as in
+    RoLA §5.1: only the rotation outside the activation has a zero shift
+    residual and a non-zero offset range; inside the activation the residual
+    is clearly non-zero; without RoPE the residual is zero but so is the
+    offset range (position-blind)."""
+    rng = np.random.default_rng(40)
+    grid, pairs, lr = (3, 3, 4), (4, 2, 2), (2, 1, 1)
+    L, D, r = 36, 16, 8
+    q = np.tile(rng.standard_normal(D), (L, 1))
+    k = np.tile(rng.standard_normal(D), (L, 1))
+    v = rng.standard_normal((L, D))
+    wq, wk = rng.standard_normal((D, r)) / 4, rng.standard_normal((D, r)) / 4
+    omega = rng.standard_normal((r, r)) if fmap == "favor" else None
+    coords = np.array(list(itertools.product(*(range(n) for n in grid))))
+    res = {}
+    for order in oracle.LR_ORDERS:
+        _, fq, fk, _, _ = oracle.lowrank_branch(q, k, v, wq, wk, grid, 10000.0, pairs, lr, order=order, fmap=fmap,
+                                                omega=omega)
+        A = fq @ fk.T
+        res[order] = (_shift_residual(A, coords), _offset_range(A, coords))
+    assert res["outside"][0] < 1e-12 and res["outside"][1] > 1e-3
+    assert res["inside"][0] > 1e-3
+    assert res["none"][0] == 0.0 and res["none"][1] == 0.0
+
+
+def test_rotation_order_outside_is_the_layer_branch():
+    """The "outside" order is exactly the layer's rotary low-rank branch."""
+    cfg, q, k, v, p = _tiny_slice()
+    res = oracle.layer_slice(cfg, q, k, v, p["wq"][1], p["wk"][1], 0.5)
+    got, *_ = oracle.lowrank_branch(q, k, v, p["wq"][1], p["wk"][1], (cfg.T, cfg.Hg, cfg.Wg), cfg.base, cfg.pairs,
+                                    cfg.lr_pairs, order="outside", eps=cfg.eps)
+    np.testing.assert_array_equal(got, res["o_lr"].reshape(-1, cfg.D)[:cfg.L])
+
+
+# ---- FAVOR+ positive random features (RoPeSLR appendix: the softmax
+# exponential kernel linearised by positive random features, Performers) ----
+
+def _favor_features(x, omega):
+    """FAVOR+ features of the rows of x [n, d] with m = omega.shape[0] random
+    directions, through the oracle: x is embedded as the first d of m
+    components (the projection W = [I_d | 0]), so omega's first d columns are
+    the directions that act."""
+    n, d = x.shape
+    m = omega.shape[0]
+    W = np.zeros((d, m))
+    W[:, :d] = np.eye(d)
+    return oracle.lowrank_features(x, W, (n, 1, 1), fmap="favor", omega=omega)
+
+
+def test_favor_features_are_positive():
+    rng = np.random.default_rng(41)
+    r = 16
+    x = rng.standard_normal((200, r)) * 2.0
+    u = oracle.lowrank_features(x, np.eye(r), (200, 1, 1), fmap="favor", omega=rng.standard_normal((r, r)))
+    assert np.isfinite(u).all() and (u > 0).all()
+
+
+def test_favor_dot_product_is_an_unbiased_estimate_of_exp_kernel():
+    """Monte-Carlo check with a fixed seed: u(x) . u(y) over m = 2048 random
+    features estimates exp(x . y) within 5 standard errors, the per-feature
+    variance being exp(|x|^2 + |y|^2 + 4 x.y) - exp(2 x.y) for Gaussian
+    directions. A wrong sign or factor of the |x|^2/2 term, or a 1/r
+    instead of 1/sqrt(r) normalisation, misses by far more."""
+    rng = np.random.default_rng(42)
+    m, d = 2048, 3
+    omega = rng.standard_normal((m, m))
+    for trial in range(6):
+        x, y = rng.standard_normal((2, d)) * 0.4
+        ux, uy = _favor_features(np.stack([x, y]), omega)
+        est = float(ux @ uy)
+        exact = math.exp(float(x @ y))
+        var = math.exp(float(x @ x + y @ y + 4 * x @ y)) - math.exp(2 * float(x @ y))
+        assert abs(est - exact) <= 5 * math.sqrt(var / m), (trial, est, exact)
+
+
+def test_favor_branch_approximates_softmax_attention():
+    """With many random features and no positional rotation, the linear
+    branch's readout sum_m u(x_l).u(y_m) v_m / sum_m u(x_l).u(y_m)
+    approaches softmax attention with logits x_l . y_m (the kernel FAVOR+
+    linearises): its distance to softmax attention is a small fraction
+    (here < 0.35, at m = 2048 features) of the distance between softmax
+    attention and the plain mean of v (what a feature map that ignores the
+    logits would give)."""
+    rng = np.random.default_rng(43)
+    m, d, L, D = 2048, 3, 12, 5
+    omega = rng.standard_normal((m, m))
+    x = rng.standard_normal((L, d)) * 0.4
+    y = rng.standard_normal((L, d)) * 0.4
+    v = rng.standard_normal((L, D))
+    fq, fk = _favor_features(x, omega), _favor_features(y, omega)
+    S, z = oracle.lowrank_summary(fk, fk, v)
+    got = oracle.lowrank_readout(fq, fq, S, z, 1e-12)
+    s = x @ y.T
+    p = np.exp(s - s.max(1, keepdims=True))
+    want = (p / p.sum(1, keepdims=True)) @ v
+    flat = np.broadcast_to(v.mean(0), want.shape)
+    assert np.linalg.norm(got - want) < 0.35 * np.linalg.norm(flat - want)
+
+
+def test_favor_uses_rows_of_omega():
+    """Interface convention: feature c uses row c of omega (omega[c, j]
+    multiplies component j of x W)."""
+    omega = np.array([[1.0, 2.0], [3.0, 4.0]])
+    x = np.array([[0.5, -1.0]])
+    u = oracle.lowrank_features(x, np.eye(2), (1, 1, 1), fmap="favor", omega=omega)
+    sq = 0.25 + 1.0
+    np.testing.assert_allclose(u[0], [math.exp(0.5 - 2.0 - sq / 2) / math.sqrt(2),
+                                      math.exp(1.5 - 4.0 - sq / 2) / math.sqrt(2)], rtol=1e-15)
+
+
+@pytest.mark.parametrize("mode", ["rola", "abspe"])
+def test_favor_linear_summary_equals_quadratic_form(mode):
+    """The reusable summary with FAVOR+ features equals the explicit L x L
+    form (normaliser w . z + eps, as for elu + 1: the features are positive)."""
+    rng = np.random.default_rng(44)
+    grid, pairs, lr = (2, 3, 4), (4, 2, 2), (2, 1, 1)
+    L, D, r = 24, 16, 8
+    q, k, v = (rng.standard_normal((L, D)) for _ in range(3))
+    wq, wk = rng.standard_normal((D, r)) / 4, rng.standard_normal((D, r)) / 4
+    omega = rng.standard_normal((r, r))
+    E = tuple(rng.standard_normal((n, r)) * 0.14 for n in grid) if mode == "abspe" else None
+    u = oracle.lowrank_features(k, wk, grid, E, fmap="favor", omega=omega)
+    w = oracle.lowrank_features(q, wq, grid, E, fmap="favor", omega=omega)
+    fk, fq = (oracle.lowrank_rotate(u, grid, 10000.0, pairs, lr), oracle.lowrank_rotate(w, grid, 10000.0, pairs, lr)) \
+        if mode == "rola" else (u, w)
+    S, z = oracle.lowrank_summary(fk, u, v)
+    got = oracle.lowrank_readout(fq, w, S, z, 1e-6)
+    A = np.array([[fq[a] @ fk[b] for b in range(L)] for a in range(L)])
+    Z = np.array([[w[a] @ u[b] for b in range(L)] for a in range(L)])
+    np.testing.assert_allclose(got, (A @ v) / (Z.sum(1, keepdims=True) + 1e-6), rtol=1e-12, atol=1e-13)
