@@ -226,14 +226,15 @@ def cpu_baseline(cfg, blocks: int):
     kr = oracle.rope3d(k, grid, cfg.base, cfg.pairs)
     s = oracle.block_scores(oracle.block_mean(qr, cfg.block), oracle.block_mean(kr, cfg.block))
     idx, _, _ = oracle.topk_blocks(s, cfg.keep)
+    om = p["omega"][0] if cfg.fmap == "favor" else None
     if cfg.lr_mode == "rola":
-        u = oracle.lowrank_features(k, p["wk"][0], grid, fmap=cfg.fmap)
-        w = oracle.lowrank_features(q, p["wq"][0], grid, fmap=cfg.fmap)
+        u = oracle.lowrank_features(k, p["wk"][0], grid, fmap=cfg.fmap, omega=om)
+        w = oracle.lowrank_features(q, p["wq"][0], grid, fmap=cfg.fmap, omega=om)
         fk = oracle.lowrank_rotate(u, grid, cfg.base, cfg.pairs, cfg.lr_pairs)
         fq = oracle.lowrank_rotate(w, grid, cfg.base, cfg.pairs, cfg.lr_pairs)
     else:
-        u = oracle.lowrank_features(k, p["wk"][0], grid, E, fmap=cfg.fmap)
-        w = oracle.lowrank_features(q, p["wq"][0], grid, E, fmap=cfg.fmap)
+        u = oracle.lowrank_features(k, p["wk"][0], grid, E, fmap=cfg.fmap, omega=om)
+        w = oracle.lowrank_features(q, p["wq"][0], grid, E, fmap=cfg.fmap, omega=om)
         fk, fq = u, w
     S, z = oracle.lowrank_summary(fk, u, v)
     t1 = time.perf_counter()
@@ -524,8 +525,8 @@ def main() -> int:
                     help="comma-separated workloads timed as sub-records ('' for none)")
     ap.add_argument("--gate", default="head", choices=["head", "token"],
                     help="combine gate: one scalar per head (the workloads' default) or the token-wise gate")
-    ap.add_argument("--fmap", default="elu1", choices=["elu1", "silu"],
-                    help="low-rank feature map: elu + 1 (the workloads' default) or SiLU")
+    ap.add_argument("--fmap", default="elu1", choices=["elu1", "silu", "favor"],
+                    help="low-rank feature map: elu + 1 (the workloads' default), SiLU or FAVOR+ random features")
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--bwd-reps", type=int, default=3,
                     help="timed calls of the layer backward (training forward saves idx, O_sparse, lse); 0 skips")
@@ -576,7 +577,7 @@ def main() -> int:
     cfg = workload(args.workload)
     head, dev = measure_forward(cfg, args, torch, B, hip, dense_reps=args.dense_reps)
     backward = None
-    if args.bwd_reps > 0 and cfg.dtype == "bf16":
+    if args.bwd_reps > 0 and cfg.dtype == "bf16" and cfg.fmap != "favor":   # FAVOR+ has no backward
         backward = measure_backward(cfg, args, torch, B, dev)
     del dev
     torch.cuda.empty_cache()

@@ -71,6 +71,11 @@ extern "C" {
 #define SLR_FMAP_ELU1 0        /* phi = elu + 1; readout / (w . z + eps)            */
 #define SLR_FMAP_SILU 1        /* RoLA §5.3 / Table 6: phi = SiLU (sign-indefinite);
                                   readout / L, the mean over the valid tokens        */
+#define SLR_FMAP_FAVOR 2       /* RoPeSLR appendix: positive random features (FAVOR+)
+                                  of the exponential kernel, feature c of p = x W [+ E]:
+                                  exp(omega_c . p - |p|^2 / 2) / sqrt(r), omega from
+                                  slr_lowrank_cfg.omega; readout / (w . z + eps).
+                                  Forward only (slr_attention_bwd: SLR_EUNSUPPORTED) */
 
 /* Gate of the combine (slr_lowrank_cfg.gate_mode) */
 #define SLR_GATE_HEAD 0        /* one scalar g_h per head: gate[H]                 */
@@ -112,7 +117,10 @@ typedef struct {
     int32_t gate_mode;           /* SLR_GATE_HEAD or SLR_GATE_TOKEN                 */
     const float *Wg;             /* SLR_GATE_TOKEN: [H, D] fp32 gate weights, else NULL */
     const float *bg;             /* SLR_GATE_TOKEN: [H] fp32 gate biases, else NULL */
-    int32_t feature_map;         /* SLR_FMAP_ELU1 or SLR_FMAP_SILU                  */
+    int32_t feature_map;         /* SLR_FMAP_ELU1, SLR_FMAP_SILU or SLR_FMAP_FAVOR   */
+    const float *omega;          /* SLR_FMAP_FAVOR: [H, r, r] fp32 random directions, row c
+                                    = omega_c of the head (the caller draws them, e.g. from
+                                    N(0, I_r)); else NULL                              */
 } slr_lowrank_cfg;
 
 /*

@@ -21,7 +21,7 @@ SLR_OK, SLR_EINVAL, SLR_EUNSUPPORTED, SLR_EWORKSPACE, SLR_EHIP = 0, -1, -2, -3, 
 SLR_F32, SLR_BF16 = 0, 1
 SLR_LR_ROPE_OUTSIDE, SLR_LR_ABS_PE = 0, 1
 SLR_GATE_HEAD, SLR_GATE_TOKEN = 0, 1
-SLR_FMAP_ELU1, SLR_FMAP_SILU = 0, 1
+SLR_FMAP_ELU1, SLR_FMAP_SILU, SLR_FMAP_FAVOR = 0, 1, 2
 SLR_OP_ROPE3D, SLR_OP_SELECT, SLR_OP_LOWRANK_SUMMARY, SLR_OP_ATTENTION, SLR_OP_DENSE = 0, 1, 2, 3, 4
 SLR_OP_ATTENTION_BWD = 5
 
@@ -50,7 +50,7 @@ class SlrLowrankCfg(ctypes.Structure):
                 ("Wq", ctypes.c_void_p), ("Wk", ctypes.c_void_p), ("gate", ctypes.c_void_p),
                 ("Et", ctypes.c_void_p), ("Eh", ctypes.c_void_p), ("Ew", ctypes.c_void_p),
                 ("gate_mode", ctypes.c_int32), ("Wg", ctypes.c_void_p), ("bg", ctypes.c_void_p),
-                ("feature_map", ctypes.c_int32)]
+                ("feature_map", ctypes.c_int32), ("omega", ctypes.c_void_p)]
 
 
 class SlrError(RuntimeError):
@@ -139,7 +139,9 @@ def lowrank_of(layer, params: Dict[str, torch.Tensor]) -> SlrLowrankCfg:
                          SLR_GATE_TOKEN if token else SLR_GATE_HEAD,
                          params["wg"].data_ptr() if token else None,
                          params["bg"].data_ptr() if token else None,
-                         SLR_FMAP_SILU if getattr(layer, "fmap", "elu1") == "silu" else SLR_FMAP_ELU1)
+                         {"silu": SLR_FMAP_SILU, "favor": SLR_FMAP_FAVOR}.get(getattr(layer, "fmap", "elu1"),
+                                                                              SLR_FMAP_ELU1),
+                         params["omega"].data_ptr() if getattr(layer, "fmap", "elu1") == "favor" else None)
 
 
 def slr_workspace_bytes(op: int, shape: SlrShape, rope: SlrRopeCfg, sparse: Optional[SlrSparseCfg] = None,

@@ -43,7 +43,8 @@ __device__ __forceinline__ float2 lr_cossin_q(const float2* __restrict__ tab, co
 // head's scalar, or (token gate, RoLA §4.4) sigmoid(q . W_g + b_g) of the
 // token's raw query row times RMS(O_sparse) / (RMS(O_lowrank) + eps), both
 // RMS over the head dims of the row.
-template <int D, int RP, int LR>
+// FAV: 0 = elu + 1 / SiLU features only, 1 = FAVOR+ features only, 2 = either (picked from a.g.fmap).
+template <int D, int RP, int LR, int FAV = 2>
 __device__ __forceinline__ void flash_epilogue(const FlashArgs& a, long bh, int head, long q0, float lsum,
                                                const f32x16_t* oacc) {
     constexpr int NS = D / 16;
@@ -58,6 +59,7 @@ __device__ __forceinline__ void flash_epilogue(const FlashArgs& a, long bh, int 
     u32x4_t whi[NRB][2], wlo[NRB][2];
     if (LR != 0) {
         const uint16_t* qraw = (const uint16_t*)a.q + (bh * L + (qval ? qrow : 0)) * D;
+        const bool fav = FAV == 2 ? a.g.fmap == 2 : FAV == 1;
         f32x16_t wacc[NRB];
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
@@ -76,16 +78,59 @@ __device__ __forceinline__ void flash_epilogue(const FlashArgs& a, long bh, int 
         if (qval) token_coords(qrow, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
         const float* zp = a.zp + bh * RP;
         float den = 0.f;
+        // FAVOR+: |p|^2 of the row's projection p = q W_q [+ E] (this lane's
+        // 16 ranks of each block, then the pair lane's)
+        float sq = 0.f;
+        if (fav) {
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = 32 * rb + 8 * (i >> 2) + 4 * hf + (i & 3);
+                    const bool ok = qval && r < a.g.R;
+                    float x = wacc[rb][i];
+                    if (LR == 2 && ok) x += a.Et[crd[0] * a.g.R + r] + a.Eh[crd[1] * a.g.R + r] + a.Ew[crd[2] * a.g.R + r];
+                    x = ok ? x : 0.f;
+                    sq += x * x;
+                }
+            sq = sum_xor32(sq);
+        }
+        const float rsr = 1.f / sqrtf((float)a.g.R);
+        const int na = a.g.rope.T + a.g.rope.Hg + a.g.rope.Wg;
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
             float w[16];
+            // FAVOR+ exponent omega_c . (q W_q) = q . (W_q omega^T)_c for this
+            // rank block, hi and lo weight parts (q re-read: L2-resident)
+            f32x16_t yacc;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) yacc[i] = 0.f;
+            if (fav) {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const u32x4_t qo2 = qval ? ldg16(qraw + 16 * s + 8 * hf) : u32x4_t{0u, 0u, 0u, 0u};
+                    const long wo = ((long)head * RP + 32 * rb + l32) * D + 16 * s + 8 * hf;
+                    yacc = mfma32(ldg16(a.wqot_hi + wo), qo2, yacc);
+                    yacc = mfma32(ldg16(a.wqot_lo + wo), qo2, yacc);
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int r = 32 * rb + 8 * (i >> 2) + 4 * hf + (i & 3);
                 const bool ok = qval && r < a.g.R;
-                float x = wacc[rb][i];
-                if (LR == 2 && ok) x += a.Et[crd[0] * a.g.R + r] + a.Eh[crd[1] * a.g.R + r] + a.Ew[crd[2] * a.g.R + r];
-                w[i] = ok ? phi_feat(a.g.fmap, x) : 0.f;
+                if (fav) {
+                    float y = yacc[i];
+                    if (LR == 2 && ok) {
+                        const float* eoh = a.g.eo + (long)head * na * a.g.R + r;
+                        y += eoh[crd[0] * a.g.R] + eoh[(a.g.rope.T + crd[1]) * a.g.R] +
+                             eoh[(a.g.rope.T + a.g.rope.Hg + crd[2]) * a.g.R];
+                    }
+                    w[i] = ok ? __builtin_amdgcn_exp2f((y - 0.5f * sq) * kLog2e) * rsr : 0.f;
+                } else {
+                    float x = wacc[rb][i];
+                    if (LR == 2 && ok) x += a.Et[crd[0] * a.g.R + r] + a.Eh[crd[1] * a.g.R + r] + a.Ew[crd[2] * a.g.R + r];
+                    w[i] = ok ? phi_feat(a.g.fmap, x) : 0.f;
+                }
                 den += w[i] * zp[r];
             }
             if (LR == 1) {
@@ -111,8 +156,8 @@ __device__ __forceinline__ void flash_epilogue(const FlashArgs& a, long bh, int 
                 }
         }
         den = sum_xor32(den);
-        // sign-indefinite SiLU features: the readout is the mean over the L tokens
-        rden = a.g.fmap ? 1.f / (float)L : 1.f / (den + a.eps);
+        // sign-indefinite SiLU features (fmap 1): the readout is the mean over the L tokens
+        rden = a.g.fmap == 1 ? 1.f / (float)L : 1.f / (den + a.eps);
         if (a.gate_mode == 0) {
             gsc = a.gate[head];
         } else {
@@ -457,7 +502,7 @@ __device__ __forceinline__ void lds_read8(u32x4_t* r, const uint16_t* lds_base) 
         : "memory");
 }
 
-template <int RP, int LR, bool DENSE>
+template <int RP, int LR, bool DENSE, bool FAV = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_flash_tiled(
     FlashArgs a, const int32_t* __restrict__ idx_all, const uint16_t* __restrict__ kvt_all) {
     constexpr int D = 128, BS = 64;
@@ -590,7 +635,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // training forward: log2 of the row's softmax normaliser (q arrives in log2 units)
     if (a.lse && hf == 0 && (long)qb * BS + 32 * rh + l32 < L)
         a.lse[bh * L + (long)qb * BS + 32 * rh + l32] = m + __log2f(lsum);
-    flash_epilogue<D, RP, LR>(a, bh, head, (long)qb * BS + 32 * rh, lsum, oacc);
+    flash_epilogue<D, RP, LR, FAV ? 1 : 0>(a, bh, head, (long)qb * BS + 32 * rh, lsum, oacc);
 }
 
 // fp32 layers: one thread per query row, K / V tiles staged in LDS, fp32
@@ -678,9 +723,21 @@ __global__ __launch_bounds__(64) void k_flash_f32(FlashArgs a, int BS) {
             for (int d = 0; d < D; ++d) x += qraw[d] * W[d * R + r];
             if (LR == 2) x += a.Et[crd[0] * R + r] + a.Eh[crd[1] * R + r] + a.Ew[crd[2] * R + r];
         }
-        w[r] = r < R ? phi_feat(a.g.fmap, x) : 0.f;
-        den += r < R ? w[r] * a.zp[bh * R + r] : 0.f;
+        w[r] = r < R ? (a.g.fmap == 2 ? x : phi_feat(a.g.fmap, x)) : 0.f;
     }
+    if (a.g.fmap == 2) {
+        // FAVOR+: w_c = exp(omega_c . p - |p|^2 / 2) / sqrt(R) of the projection p (held in w)
+        float sq = 0.f;
+        for (int r = 0; r < R; ++r) sq += w[r] * w[r];
+        const float* om = a.g.omega + (long)head * R * R;
+        for (int c = 0; c < R; ++c) {
+            float y = 0.f;
+            for (int j = 0; j < R; ++j) y += om[c * R + j] * w[j];
+            f[c] = expf(y - 0.5f * sq) / sqrtf((float)R);
+        }
+        for (int c = 0; c < R; ++c) w[c] = f[c];
+    }
+    for (int r = 0; r < R; ++r) den += w[r] * a.zp[bh * R + r];
     for (int r = 0; r < RP; r += 2) {
         if (LR == 1 && r < R) {
             const float2 cs = lr_cossin_q(a.tab, a.g, r >> 1, crd);
@@ -691,7 +748,7 @@ __global__ __launch_bounds__(64) void k_flash_f32(FlashArgs a, int BS) {
             f[r + 1] = w[r + 1];
         }
     }
-    const float rd = a.g.fmap ? 1.f / (float)L : 1.f / (den + a.eps);
+    const float rd = a.g.fmap == 1 ? 1.f / (float)L : 1.f / (den + a.eps);
     const float* S = a.S + bh * (long)R * D;
     float gs;
     if (a.gate_mode == 0) {
@@ -753,6 +810,10 @@ template <int RP>
 static hipError_t flash_tiled_t(int lr_mode, bool dense, const FlashArgs& a, hipStream_t st) {
     dim3 grid((unsigned)a.nwg), blk(256);
     if (dense) hipLaunchKernelGGL((k_flash_tiled<RP, 0, true>), grid, blk, 0, st, a, a.idx, a.kvt);
+    else if (lr_mode == 1 && a.g.fmap == 2)
+        hipLaunchKernelGGL((k_flash_tiled<RP, 1, false, true>), grid, blk, 0, st, a, a.idx, a.kvt);
+    else if (lr_mode == 2 && a.g.fmap == 2)
+        hipLaunchKernelGGL((k_flash_tiled<RP, 2, false, true>), grid, blk, 0, st, a, a.idx, a.kvt);
     else if (lr_mode == 1) hipLaunchKernelGGL((k_flash_tiled<RP, 1, false>), grid, blk, 0, st, a, a.idx, a.kvt);
     else if (lr_mode == 2) hipLaunchKernelGGL((k_flash_tiled<RP, 2, false>), grid, blk, 0, st, a, a.idx, a.kvt);
     else hipLaunchKernelGGL((k_flash_tiled<RP, 0, false>), grid, blk, 0, st, a, a.idx, a.kvt);

@@ -31,6 +31,54 @@ __global__ void k_lr_prep(const float* __restrict__ W, uint16_t* __restrict__ Wt
     }
 }
 
+// FAVOR+ projections (positive random features of the exponential kernel,
+// RoPeSLR appendix): the feature exponent omega_c . (x W) is x . (W omega^T)_c,
+// so one more projection matrix per side serves it on MFMA. Writes
+// (W omega^T)^T [H][RP][D] as bf16 hi + lo parts (about 16 mantissa bits;
+// rows c >= R zero), W rounded to bf16 first for bf16 layers (the layer uses
+// the rounded W), sums over j in fp32.
+__global__ void k_lr_prep_favor(const float* __restrict__ W, const float* __restrict__ omega, int round_bf16, int H,
+                                int D, int R, int RP, uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
+    const long n = (long)H * RP * D;
+    for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < n; e += (long)gridDim.x * blockDim.x) {
+        const int d = (int)(e % D);
+        const int c = (int)((e / D) % RP);
+        const long h = e / ((long)D * RP);
+        float s = 0.f;
+        if (c < R) {
+            const float* wr = W + (h * D + d) * R;
+            const float* om = omega + (h * R + c) * R;
+            for (int j = 0; j < R; ++j) {
+                const float w = round_bf16 ? bf2f(f2bf(wr[j])) : wr[j];
+                s = fmaf(w, om[j], s);
+            }
+        }
+        const uint16_t h16 = f2bf(s);
+        hi[e] = h16;
+        lo[e] = f2bf(s - bf2f(h16));
+    }
+}
+
+// FAVOR+ with absolute PE: eo[h][n][c] = sum_j omega[h][c][j] E[n][j] over the
+// concatenated axis tables n in [0, T + Hg + Wg) (E_t rows, then E_h, E_w).
+__global__ void k_lr_prep_favor_e(const float* __restrict__ Et, const float* __restrict__ Eh,
+                                  const float* __restrict__ Ew, const float* __restrict__ omega, int H, int T,
+                                  int Hg, int Wg, int R, float* __restrict__ eo) {
+    const int na = T + Hg + Wg;
+    const long n = (long)H * na * R;
+    for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < n; e += (long)gridDim.x * blockDim.x) {
+        const int c = (int)(e % R);
+        const int row = (int)((e / R) % na);
+        const long h = e / ((long)R * na);
+        const float* er = row < T ? Et + (long)row * R : row < T + Hg ? Eh + (long)(row - T) * R
+                                                                        : Ew + (long)(row - T - Hg) * R;
+        const float* om = omega + (h * R + c) * R;
+        float s = 0.f;
+        for (int j = 0; j < R; ++j) s = fmaf(om[j], er[j], s);
+        eo[e] = s;
+    }
+}
+
 // Rotation of low-rank feature pair index pr (0 .. R/2-1) at token coords.
 __device__ __forceinline__ float2 lr_cossin(const float2* __restrict__ tab, const LrGeom& g, int pr, const int* crd) {
     int a, j;
@@ -52,7 +100,12 @@ __device__ __forceinline__ float2 lr_cossin(const float2* __restrict__ tab, cons
 // from the rotate kernel's [K | V^T] tiles, whose V^T chunks already hold a
 // wave's B operand in this kernel's token-slot order, so no LDS transpose is
 // needed (the tail block's padded keys are zero there).
-template <int D, int RP, bool ABSPE, bool TILEDV>
+//
+// FAV (FAVOR+ features): besides U = K W_k (the exponent's |p|^2 term, per
+// token a sum over the r lanes of a 32-lane half), Y = K (W_k omega^T) on
+// MFMA with bf16 hi + lo weights gives omega_c . p; u_c = exp(y_c -
+// |p|^2 / 2) / sqrt(R).
+template <int D, int RP, bool ABSPE, bool TILEDV, bool FAV = false>
 __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
                                                          const uint16_t* __restrict__ kv_tiles, int nblk,
@@ -61,7 +114,9 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
                                                          const float* __restrict__ Eh,
                                                          const float* __restrict__ Ew,
                                                          const float2* __restrict__ tab, LrGeom g, long L,
-                                                         int H, int chunk, int nsplit, float* __restrict__ part) {
+                                                         int H, int chunk, int nsplit, float* __restrict__ part,
+                                                         const uint16_t* __restrict__ wkot_hi,
+                                                         const uint16_t* __restrict__ wkot_lo) {
     constexpr int NRB = RP / 32;   // r blocks
     constexpr int NDB = D / 32;    // d blocks
     constexpr int NKS = D / 16;    // k steps over d
@@ -140,6 +195,22 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) uacc[rb] = mfma32(kop[s], wop[rb][s], uacc[rb]);
         }
+        // FAVOR+: Y = K_sub (W_k omega^T), hi and lo weight parts
+        f32x16_t yacc[FAV ? NRB : 1];
+        if constexpr (FAV) {
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) yacc[rb][i] = 0.f;
+#pragma unroll
+            for (int s = 0; s < NKS; ++s)
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb) {
+                    const long wo = ((long)head * RP + 32 * rb + l32) * D + 16 * s + 8 * hf;
+                    yacc[rb] = mfma32(kop[s], ldg16(wkot_hi + wo), yacc[rb]);
+                    yacc[rb] = mfma32(kop[s], ldg16(wkot_lo + wo), yacc[rb]);
+                }
+        }
         // ---- V sub-tile -> this wave's LDS area, transposed to [d][slot16(tok)]
         u32x4_t vop[TILEDV ? 8 : 1];
         if (TILEDV) {
@@ -194,6 +265,71 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
                     cA[rb][vv] = rax[rb] == 2 ? cW[vv] : (rax[rb] == 1 ? cH[vv] : cT[vv]);
         }
         float fv[NRB][16];
+        if constexpr (FAV) {
+            // |p|^2 per token: this lane's r, then the other 31 lanes of its half
+            float sqv[16];
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv) sqv[vv] = 0.f;
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                const int r = 32 * rb + l32;
+                float ev[16];
+                if (ABSPE) {
+#pragma unroll
+                    for (int vv = 0; vv < 16; ++vv) {
+                        const bool ok = t0 + 4 * hf + 8 * (vv >> 2) + (vv & 3) < tok_hi && r < g.R;
+                        const int rr = r < g.R ? r : 0;
+                        const int it = ok ? cT[vv] : 0, ih = ok ? cH[vv] : 0, iw = ok ? cW[vv] : 0;
+                        ev[vv] = Et[it * g.R + rr] + Eh[ih * g.R + rr] + Ew[iw * g.R + rr];
+                    }
+                }
+#pragma unroll
+                for (int vv = 0; vv < 16; ++vv) {
+                    const bool ok = t0 + 4 * hf + 8 * (vv >> 2) + (vv & 3) < tok_hi && r < g.R;
+                    float x = uacc[rb][vv];
+                    if (ABSPE) x += ev[vv];
+                    x = ok ? x : 0.f;
+                    sqv[vv] += x * x;
+                }
+            }
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv)
+#pragma unroll
+                for (int o = 1; o < 32; o <<= 1) sqv[vv] += __shfl_xor(sqv[vv], o, 64);
+            const float rs = 1.f / sqrtf((float)g.R);
+            const int na = g.rope.T + g.rope.Hg + g.rope.Wg;
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                const int r = 32 * rb + l32;
+                float2 cs[16];
+                float eo[16];
+#pragma unroll
+                for (int vv = 0; vv < 16; ++vv) {
+                    const bool ok = t0 + 4 * hf + 8 * (vv >> 2) + (vv & 3) < tok_hi && r < g.R;
+                    if (ABSPE) {
+                        const int rr = r < g.R ? r : 0;
+                        const int it = ok ? cT[vv] : 0, ih = ok ? cH[vv] : 0, iw = ok ? cW[vv] : 0;
+                        const float* eoh = g.eo + (long)head * na * g.R + rr;
+                        eo[vv] = eoh[it * g.R] + eoh[(g.rope.T + ih) * g.R] + eoh[(g.rope.T + g.rope.Hg + iw) * g.R];
+                    } else {
+                        cs[vv] = tab[rbase[rb] + (ok ? cA[rb][vv] : 0) * rstride[rb]];
+                    }
+                }
+#pragma unroll
+                for (int vv = 0; vv < 16; ++vv) {
+                    const bool ok = t0 + 4 * hf + 8 * (vv >> 2) + (vv & 3) < tok_hi && r < g.R;
+                    float y = yacc[rb][vv];
+                    if (ABSPE) y += eo[vv];
+                    float u = ok ? __builtin_amdgcn_exp2f((y - 0.5f * sqv[vv]) * kLog2e) * rs : 0.f;
+                    zacc[rb] += u;
+                    if (!ABSPE) {
+                        const float p = lane_swap1(u);  // partner dim r ^ 1
+                        u = (r & 1) ? (p * cs[vv].y + u * cs[vv].x) : (u * cs[vv].x - p * cs[vv].y);
+                    }
+                    fv[rb][vv] = u;
+                }
+            }
+        } else {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
             const int r = 32 * rb + l32;
@@ -224,6 +360,7 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
                 }
                 fv[rb][vv] = u;
             }
+        }
         }
         u32x4_t fhi[NRB][2], flo[NRB][2];
 #pragma unroll
@@ -303,7 +440,7 @@ __global__ __launch_bounds__(256) void k_lr_summary_f32(const float* __restrict_
                                                         const float2* __restrict__ tab, LrGeom g, long L, int H,
                                                         int absPE, int chunk, int nsplit, float* __restrict__ part) {
     constexpr int TS = 16;  // tokens per step
-    __shared__ float ksh[TS][D], vsh[TS][D], fsh[TS][RP], ush[TS][RP];
+    __shared__ float ksh[TS][D], vsh[TS][D], fsh[TS][RP], ush[TS][RP], xsh[TS][RP];
     const int tid = threadIdx.x;
     const long bh = blockIdx.y;
     const int head = (int)(bh % H);
@@ -326,6 +463,25 @@ __global__ __launch_bounds__(256) void k_lr_summary_f32(const float* __restrict_
             vsh[tl][d] = t < tok_hi ? v[(bh * L + t) * D + d] : 0.f;
         }
         __syncthreads();
+        const bool fav = g.fmap == 2;
+        if (fav) {
+            // FAVOR+: the projections p = k W [+ E] of the step's tokens first
+            for (int e = tid; e < TS * RP; e += 256) {
+                const int tl = e / RP, r = e % RP;
+                const long t = t0 + tl;
+                float acc = 0.f;
+                if (t < tok_hi && r < R) {
+                    for (int d = 0; d < D; ++d) acc += ksh[tl][d] * Wh[d * R + r];
+                    if (absPE) {
+                        int crd[3];
+                        token_coords(t, g.rope.Hg, g.rope.Wg, crd[0], crd[1], crd[2]);
+                        acc += Et[crd[0] * R + r] + Eh[crd[1] * R + r] + Ew[crd[2] * R + r];
+                    }
+                }
+                xsh[tl][r] = acc;
+            }
+            __syncthreads();
+        }
         // features, one (token, pair) per thread
         for (int e = tid; e < TS * (RP / 2); e += 256) {
             const int tl = e / (RP / 2), pr = e % (RP / 2);
@@ -337,6 +493,17 @@ __global__ __launch_bounds__(256) void k_lr_summary_f32(const float* __restrict_
             for (int q = 0; q < 2; ++q) {
                 const int r = 2 * pr + q;
                 if (!tv || r >= R) continue;
+                if (fav) {
+                    // u_r = exp(omega_r . p - |p|^2 / 2) / sqrt(R)
+                    const float* om = g.omega + ((long)head * R + r) * R;
+                    float y = 0.f, sq = 0.f;
+                    for (int j = 0; j < R; ++j) {
+                        y += om[j] * xsh[tl][j];
+                        sq += xsh[tl][j] * xsh[tl][j];
+                    }
+                    u[q] = expf(y - 0.5f * sq) / sqrtf((float)R);
+                    continue;
+                }
                 float acc = 0.f;
                 for (int d = 0; d < D; ++d) acc += ksh[tl][d] * Wh[d * R + r];
                 if (absPE) acc += Et[crd[0] * R + r] + Eh[crd[1] * R + r] + Ew[crd[2] * R + r];
@@ -415,24 +582,57 @@ hipError_t launch_lr_prep(const float* W, uint16_t* Wt, int H, int D, int R, int
     return hipGetLastError();
 }
 
+hipError_t launch_lr_prep_favor(const float* W, const float* omega, int round_bf16, int H, int D, int R, int RP,
+                                uint16_t* wot_hi, uint16_t* wot_lo, const float* Et, const float* Eh, const float* Ew,
+                                int T, int Hg, int Wg, float* eo, hipStream_t st) {
+    if (wot_hi) {
+        const long n = (long)H * RP * D;
+        hipLaunchKernelGGL(k_lr_prep_favor, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, W, omega, round_bf16,
+                           H, D, R, RP, wot_hi, wot_lo);
+    }
+    if (Et && eo) {
+        const long n = (long)H * (T + Hg + Wg) * R;
+        hipLaunchKernelGGL(k_lr_prep_favor_e, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, Et, Eh, Ew, omega,
+                           H, T, Hg, Wg, R, eo);
+    }
+    return hipGetLastError();
+}
+
 template <int D, int RP, bool TILEDV>
 static hipError_t summary_bf16_t(bool abspe, const void* k, const void* v, const uint16_t* kvt, int nblk,
                                  const uint16_t* wkt, const float* Et, const float* Eh, const float* Ew,
                                  const float2* tab, const LrGeom& g, long BH, long L, int H, int chunk, int nsplit,
-                                 float* part, hipStream_t st) {
+                                 float* part, hipStream_t st, const uint16_t* woh, const uint16_t* wol) {
     dim3 grid((unsigned)nsplit, (unsigned)BH);
-    if (abspe)
-        hipLaunchKernelGGL((k_lr_summary_bf16<D, RP, true, TILEDV>), grid, dim3(256), 0, st, (const uint16_t*)k,
-                           (const uint16_t*)v, kvt, nblk, wkt, Et, Eh, Ew, tab, g, L, H, chunk, nsplit, part);
-    else
-        hipLaunchKernelGGL((k_lr_summary_bf16<D, RP, false, TILEDV>), grid, dim3(256), 0, st, (const uint16_t*)k,
-                           (const uint16_t*)v, kvt, nblk, wkt, Et, Eh, Ew, tab, g, L, H, chunk, nsplit, part);
+    const bool fav = g.fmap == 2;
+#define SLR_SUMB(AB, FV)                                                                                            \
+    hipLaunchKernelGGL((k_lr_summary_bf16<D, RP, AB, TILEDV, FV>), grid, dim3(256), 0, st, (const uint16_t*)k,      \
+                       (const uint16_t*)v, kvt, nblk, wkt, Et, Eh, Ew, tab, g, L, H, chunk, nsplit, part, woh, wol)
+    if (abspe) {
+        if (fav) SLR_SUMB(true, true); else SLR_SUMB(true, false);
+    } else {
+        if (fav) SLR_SUMB(false, true); else SLR_SUMB(false, false);
+    }
+#undef SLR_SUMB
     return hipGetLastError();
 }
 
 // The kernel instance launch_lr_summary picks for these arguments.
-static const void* summary_kernel(int dtype_bf16, int D, int RP, bool abspe, bool tiled) {
+static const void* summary_kernel(int dtype_bf16, int D, int RP, bool abspe, bool tiled, bool favor) {
 #define SLR_PICK(...) return reinterpret_cast<const void*>(&__VA_ARGS__)
+    if (dtype_bf16 && favor) {
+        // FAVOR+ instances (their occupancy is what sizes the split)
+        if (tiled && D == 128) {
+            if (RP == 32) { if (abspe) SLR_PICK(k_lr_summary_bf16<128, 32, true, true, true>); SLR_PICK(k_lr_summary_bf16<128, 32, false, true, true>); }
+            if (abspe) SLR_PICK(k_lr_summary_bf16<128, 64, true, true, true>);
+            SLR_PICK(k_lr_summary_bf16<128, 64, false, true, true>);
+        }
+        if (D == 64 && RP == 32) { if (abspe) SLR_PICK(k_lr_summary_bf16<64, 32, true, false, true>); SLR_PICK(k_lr_summary_bf16<64, 32, false, false, true>); }
+        if (D == 64) { if (abspe) SLR_PICK(k_lr_summary_bf16<64, 64, true, false, true>); SLR_PICK(k_lr_summary_bf16<64, 64, false, false, true>); }
+        if (RP == 32) { if (abspe) SLR_PICK(k_lr_summary_bf16<128, 32, true, false, true>); SLR_PICK(k_lr_summary_bf16<128, 32, false, false, true>); }
+        if (abspe) SLR_PICK(k_lr_summary_bf16<128, 64, true, false, true>);
+        SLR_PICK(k_lr_summary_bf16<128, 64, false, false, true>);
+    }
     if (dtype_bf16) {
         if (tiled && D == 128) {
             if (RP == 32) { if (abspe) SLR_PICK(k_lr_summary_bf16<128, 32, true, true>); SLR_PICK(k_lr_summary_bf16<128, 32, false, true>); }
@@ -452,20 +652,21 @@ static const void* summary_kernel(int dtype_bf16, int D, int RP, bool abspe, boo
 #undef SLR_PICK
 }
 
-hipError_t lr_summary_slots(int dtype_bf16, int D, int RP, bool abspe, bool tiled, int* slots) {
+hipError_t lr_summary_slots(int dtype_bf16, int D, int RP, bool abspe, bool tiled, int* slots, bool favor) {
     constexpr int kMaxDev = 64;
-    static std::atomic<int> cache[kMaxDev][32];
+    static std::atomic<int> cache[kMaxDev][64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    const int key = (dtype_bf16 ? 16 : 0) | (D == 128 ? 8 : 0) | (RP == 64 ? 4 : 0) | (abspe ? 2 : 0) | (tiled ? 1 : 0);
+    const int key = (favor && dtype_bf16 ? 32 : 0) | (dtype_bf16 ? 16 : 0) | (D == 128 ? 8 : 0) | (RP == 64 ? 4 : 0) |
+                    (abspe ? 2 : 0) | (tiled ? 1 : 0);
     if (dev >= 0 && dev < kMaxDev) {
         const int c = cache[dev][key].load(std::memory_order_relaxed);
         if (c > 0) { *slots = c; return hipSuccess; }
     }
     int cus = 0, per = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, summary_kernel(dtype_bf16, D, RP, abspe, tiled), 256,
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, summary_kernel(dtype_bf16, D, RP, abspe, tiled, favor), 256,
                                                           0)) != hipSuccess)
         return e;
     const int n = (cus > 0 ? cus : 1) * (per > 0 ? per : 1);
@@ -477,26 +678,27 @@ hipError_t lr_summary_slots(int dtype_bf16, int D, int RP, bool abspe, bool tile
 hipError_t launch_lr_summary(int dtype_bf16, int D, int RP, bool abspe, const void* k, const void* v,
                              const uint16_t* kvt, int nblk, const float* W, const uint16_t* wkt, const float* Et,
                              const float* Eh, const float* Ew, const float2* tab, const LrGeom& g, long BH, long L,
-                             int H, int chunk, int nsplit, float* part, hipStream_t st) {
+                             int H, int chunk, int nsplit, float* part, hipStream_t st, const uint16_t* wkot_hi,
+                             const uint16_t* wkot_lo) {
     if (dtype_bf16) {
         if (kvt && D == 128) {
             if (RP == 32)
                 return summary_bf16_t<128, 32, true>(abspe, k, v, kvt, nblk, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk,
-                                                     nsplit, part, st);
+                                                     nsplit, part, st, wkot_hi, wkot_lo);
             return summary_bf16_t<128, 64, true>(abspe, k, v, kvt, nblk, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk,
-                                                 nsplit, part, st);
+                                                 nsplit, part, st, wkot_hi, wkot_lo);
         }
         if (D == 64 && RP == 32)
             return summary_bf16_t<64, 32, false>(abspe, k, v, nullptr, 0, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk,
-                                                 nsplit, part, st);
+                                                 nsplit, part, st, wkot_hi, wkot_lo);
         if (D == 64)
             return summary_bf16_t<64, 64, false>(abspe, k, v, nullptr, 0, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk,
-                                                 nsplit, part, st);
+                                                 nsplit, part, st, wkot_hi, wkot_lo);
         if (RP == 32)
             return summary_bf16_t<128, 32, false>(abspe, k, v, nullptr, 0, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk,
-                                                  nsplit, part, st);
+                                                  nsplit, part, st, wkot_hi, wkot_lo);
         return summary_bf16_t<128, 64, false>(abspe, k, v, nullptr, 0, wkt, Et, Eh, Ew, tab, g, BH, L, H, chunk,
-                                              nsplit, part, st);
+                                              nsplit, part, st, wkot_hi, wkot_lo);
     }
     dim3 grid((unsigned)nsplit, (unsigned)BH);
 #define SLR_SUMF32(DD, RR)                                                                                     \

@@ -90,8 +90,12 @@ int check_lowrank(const slr_lowrank_cfg* lr, const slr_rope_cfg* rope, const Dim
             return SLR_EINVAL;
         }
     }
-    if (lr->feature_map != SLR_FMAP_ELU1 && lr->feature_map != SLR_FMAP_SILU) return SLR_EINVAL;
+    if (lr->feature_map != SLR_FMAP_ELU1 && lr->feature_map != SLR_FMAP_SILU && lr->feature_map != SLR_FMAP_FAVOR)
+        return SLR_EINVAL;
+    if (lr->feature_map == SLR_FMAP_FAVOR && (!lr->omega || !aligned(lr->omega, 4))) return SLR_EINVAL;
     lg->fmap = lr->feature_map;
+    lg->omega = lr->feature_map == SLR_FMAP_FAVOR ? lr->omega : nullptr;
+    lg->eo = nullptr;
     lg->lp[0] = lg->lp[1] = lg->lp[2] = 0;
     if (lr->mode == SLR_LR_ROPE_OUTSIDE) {
         if (lr->lr_pairs_t < 0 || lr->lr_pairs_h < 0 || lr->lr_pairs_w < 0) return SLR_EINVAL;
@@ -153,6 +157,8 @@ bool overlaps(const void* a, const void* b, size_t n) {
 // Workspace layout (byte offsets, each 256-byte aligned).
 struct Layout {
     size_t tab, qr, kr, kvt, qbar, kbar, scores, idx, wqt, wkt, part, S, z, sthi, stlo, zp, total;
+    // FAVOR+ (bf16 layers): (W omega^T)^T hi/lo parts of both sides, the projected axis tables
+    size_t wqo_hi, wqo_lo, wko_hi, wko_lo, eo;
     // backward
     size_t lse, delta, dqlr, dklr, dvlr, lrpart, dsz, bits, cnt, off, list, order, dpre, epart, dosp, gpart, dqt, qtt;
     bool tiled;
@@ -175,7 +181,7 @@ void lr_bwd_split(const Dims& d, int* chunk, int* nsplit) {
 }
 
 Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int keep, int R, int RP,
-              bool abspe = false, bool token = false) {
+              bool abspe = false, bool token = false, bool favor = false) {
     Layout w;
     std::memset(&w, 0, sizeof(w));
     size_t off = 0;
@@ -246,6 +252,13 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         if (d.bf16) {
             w.wqt = take(2ul * d.H * RP * d.D);
             w.wkt = take(2ul * d.H * RP * d.D);
+            if (favor) {
+                w.wqo_hi = take(2ul * d.H * RP * d.D);
+                w.wqo_lo = take(2ul * d.H * RP * d.D);
+                w.wko_hi = take(2ul * d.H * RP * d.D);
+                w.wko_lo = take(2ul * d.H * RP * d.D);
+                if (abspe) w.eo = take(4ul * d.H * ((long)d.T + d.Hg + d.Wg) * R);
+            }
         }
         w.part = take(4ul * d.BH * nsplit * (RP * d.D + RP));
         w.S = take(4ul * d.BH * R * d.D);
@@ -317,6 +330,8 @@ int slr_workspace_bytes(int op, const slr_shape* shape, const slr_rope_cfg* rope
     }
     if (op == SLR_OP_ATTENTION || op == SLR_OP_LOWRANK_SUMMARY || op == SLR_OP_ATTENTION_BWD) {
         if (!lowrank) return SLR_EINVAL;
+        // the backward covers elu + 1 and SiLU features, not FAVOR+
+        if (op == SLR_OP_ATTENTION_BWD && lowrank->feature_map == SLR_FMAP_FAVOR) return SLR_EUNSUPPORTED;
         LrGeom lg;
         // pointer fields are not needed for sizing
         slr_lowrank_cfg probe = *lowrank;
@@ -324,11 +339,13 @@ int slr_workspace_bytes(int op, const slr_shape* shape, const slr_rope_cfg* rope
         probe.Wq = probe.Wk = probe.gate = dummy;
         probe.Et = probe.Eh = probe.Ew = dummy;
         probe.Wg = probe.bg = dummy;
+        probe.omega = dummy;
         if ((st = check_lowrank(&probe, rope, d, op != SLR_OP_LOWRANK_SUMMARY, &lg, &RP))) return st;
         R = lowrank->rank;
     }
     *bytes = layout(op, d, g, bs, nblk, keep, R, RP, lowrank && lowrank->mode == SLR_LR_ABS_PE,
-                    lowrank && lowrank->gate_mode == SLR_GATE_TOKEN).total;
+                    lowrank && lowrank->gate_mode == SLR_GATE_TOKEN,
+                    lowrank && lowrank->feature_map == SLR_FMAP_FAVOR).total;
     return SLR_OK;
 }
 
@@ -380,19 +397,38 @@ int slr_select_blocks(const slr_shape* shape, const slr_rope_cfg* rope, const sl
 namespace {
 
 // Shared by the summary entry point and the layer forward.
+// FAVOR+ on bf16 layers: the projected axis tables of the absolute-PE
+// variant (shared by both sides), placed in the geometry the kernels get.
+int favor_tables(const Dims& d, LrGeom* lg, const slr_lowrank_cfg* lr, void* ws, const Layout& w, hipStream_t s) {
+    if (lr->feature_map != SLR_FMAP_FAVOR || !d.bf16 || lr->mode != SLR_LR_ABS_PE) return SLR_OK;
+    float* eo = at<float>(ws, w.eo);
+    SLR_TRY(launch_lr_prep_favor(nullptr, lr->omega, 1, (int)d.H, (int)d.D, lg->R, 0, nullptr, nullptr, lr->Et,
+                                 lr->Eh, lr->Ew, d.T, d.Hg, d.Wg, eo, s));
+    lg->eo = eo;
+    return SLR_OK;
+}
+
 int run_summary(const Dims& d, const RopeGeom& g, const LrGeom& lg, int RP, const slr_lowrank_cfg* lr, const void* k,
                 const void* v, const uint16_t* kvt, int nblk, void* ws, const Layout& w, float* S, float* z,
                 bool want_st, hipStream_t s) {
     const bool abspe = lr->mode == SLR_LR_ABS_PE;
+    const bool favor = lr->feature_map == SLR_FMAP_FAVOR;
     int slots = 0, chunk, nsplit;
-    SLR_TRY(lr_summary_slots(d.bf16, (int)d.D, RP, abspe, kvt != nullptr, &slots));
+    SLR_TRY(lr_summary_slots(d.bf16, (int)d.D, RP, abspe, kvt != nullptr, &slots, favor));
     summary_split(d, slots, &chunk, &nsplit);
     const float2* tab = at<float2>(ws, w.tab);
     uint16_t* wkt = d.bf16 ? at<uint16_t>(ws, w.wkt) : nullptr;
     if (d.bf16) SLR_TRY(launch_lr_prep(lr->Wk, wkt, (int)d.H, (int)d.D, lg.R, RP, s));
+    uint16_t *woh = nullptr, *wol = nullptr;
+    if (favor && d.bf16) {
+        woh = at<uint16_t>(ws, w.wko_hi);
+        wol = at<uint16_t>(ws, w.wko_lo);
+        SLR_TRY(launch_lr_prep_favor(lr->Wk, lr->omega, 1, (int)d.H, (int)d.D, lg.R, RP, woh, wol, nullptr, nullptr,
+                                     nullptr, d.T, d.Hg, d.Wg, nullptr, s));
+    }
     float* part = at<float>(ws, w.part);
     SLR_TRY(launch_lr_summary(d.bf16, (int)d.D, RP, abspe, k, v, kvt, nblk, lr->Wk, wkt, lr->Et, lr->Eh, lr->Ew, tab,
-                              lg, d.BH, d.L, (int)d.H, chunk, nsplit, part, s));
+                              lg, d.BH, d.L, (int)d.H, chunk, nsplit, part, s, woh, wol));
     uint16_t* sthi = want_st ? at<uint16_t>(ws, w.sthi) : nullptr;
     uint16_t* stlo = want_st ? at<uint16_t>(ws, w.stlo) : nullptr;
     float* zp = want_st ? at<float>(ws, w.zp) : nullptr;
@@ -415,10 +451,12 @@ int slr_lowrank_summary(const slr_shape* shape, const slr_rope_cfg* rope, const 
     if ((st = check_lowrank(lowrank, rope, d, false, &lg, &RP))) return st;
     if (!tensor_ok(k) || !tensor_ok(v) || !S || !z || !aligned(S, 4) || !aligned(z, 4)) return SLR_EINVAL;
     lg.rope = g;
-    Layout w = layout(SLR_OP_LOWRANK_SUMMARY, d, g, 64, 0, 0, lowrank->rank, RP);
+    Layout w = layout(SLR_OP_LOWRANK_SUMMARY, d, g, 64, 0, 0, lowrank->rank, RP, lowrank->mode == SLR_LR_ABS_PE,
+                      false, lowrank->feature_map == SLR_FMAP_FAVOR);
     if ((st = check_ws(ws, ws_bytes, w.total))) return st;
     hipStream_t s = (hipStream_t)stream;
     SLR_TRY(launch_rope_tables(at<float2>(ws, w.tab), g, rope->base, s));
+    if ((st = favor_tables(d, &lg, lowrank, ws, w, s))) return st;
     return run_summary(d, g, lg, RP, lowrank, k, v, nullptr, 0, ws, w, S, z, false, s);
 }
 
@@ -444,7 +482,9 @@ int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sp
     if (lse_out && !aligned(lse_out, 4)) return SLR_EINVAL;
     lg.rope = g;
     const int bs = sparse->block;
-    Layout w = layout(SLR_OP_ATTENTION, d, g, bs, nblk, sparse->keep, lowrank->rank, RP);
+    const bool favor = lowrank->feature_map == SLR_FMAP_FAVOR;
+    Layout w = layout(SLR_OP_ATTENTION, d, g, bs, nblk, sparse->keep, lowrank->rank, RP,
+                      lowrank->mode == SLR_LR_ABS_PE, false, favor);
     if ((st = check_ws(ws, ws_bytes, w.total))) return st;
     hipStream_t s = (hipStream_t)stream;
 
@@ -469,11 +509,19 @@ int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sp
     SLR_TRY(mark(1));
     SLR_TRY(launch_select((int)d.D, qbar, kbar, at<float>(ws, w.scores), idx, d.BH, nblk, sparse->keep, s));
     SLR_TRY(mark(2));
+    if ((st = favor_tables(d, &lg, lowrank, ws, w, s))) return st;
     if ((st = run_summary(d, g, lg, RP, lowrank, k, v, kvt, nblk, ws, w, S, z, d.bf16 != 0, s))) return st;
     uint16_t* wqt = nullptr;
+    uint16_t *wqoh = nullptr, *wqol = nullptr;
     if (d.bf16) {
         wqt = at<uint16_t>(ws, w.wqt);
         SLR_TRY(launch_lr_prep(lowrank->Wq, wqt, (int)d.H, (int)d.D, lg.R, RP, s));
+        if (favor) {
+            wqoh = at<uint16_t>(ws, w.wqo_hi);
+            wqol = at<uint16_t>(ws, w.wqo_lo);
+            SLR_TRY(launch_lr_prep_favor(lowrank->Wq, lowrank->omega, 1, (int)d.H, (int)d.D, lg.R, RP, wqoh, wqol,
+                                         nullptr, nullptr, nullptr, d.T, d.Hg, d.Wg, nullptr, s));
+        }
     }
     SLR_TRY(mark(3));
 
@@ -490,6 +538,7 @@ int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sp
     a.wg = lowrank->Wg;
     a.bg = lowrank->bg;
     a.Et = lowrank->Et; a.Eh = lowrank->Eh; a.Ew = lowrank->Ew;
+    a.wqot_hi = wqoh; a.wqot_lo = wqol;
     a.tab = tab;
     a.g = lg;
     a.out = out; a.o_sp = o_sparse_out; a.o_lr = o_lowrank_out; a.lse = lse_out;
@@ -583,6 +632,7 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     if ((st = check_rope(rope, d, &g))) return st;
     if ((st = check_sparse(sparse, d, &nblk))) return st;
     if ((st = check_lowrank(lowrank, rope, d, true, &lg, &RP))) return st;
+    if (lowrank->feature_map == SLR_FMAP_FAVOR) return SLR_EUNSUPPORTED;   // forward only
     if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o_sparse) || !tensor_ok(dout)) return SLR_EINVAL;
     if (!tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv) || !idx || !aligned(idx, 4)) return SLR_EINVAL;
     if (!lse || !aligned(lse, 4)) return SLR_EINVAL;

@@ -13,7 +13,11 @@ struct LrGeom {
     RopeGeom rope;
     int lp[3];
     int R;
-    int fmap;   // feature map: 0 = elu + 1 (readout / (w . z + eps)), 1 = SiLU (readout / L)
+    int fmap;   // feature map: 0 = elu + 1 (readout / (w . z + eps)), 1 = SiLU (readout / L),
+                // 2 = FAVOR+ positive random features exp(omega p - |p|^2 / 2) / sqrt(R), p = x W [+ E]
+                // (readout / (w . z + eps))
+    const float* omega;   // FAVOR+: [H][R][R] random directions (row c = omega_c)
+    const float* eo;      // FAVOR+ with absolute PE: [H][T + Hg + Wg][R], the axis tables times omega^T
 };
 
 // Everything the fused sparse/dense flash kernel reads.
@@ -35,6 +39,8 @@ struct FlashArgs {
     const float* wg;         // [H, D] token-gate weights
     const float* bg;         // [H] token-gate biases
     const float *Et, *Eh, *Ew;
+    const uint16_t* wqot_hi;   // FAVOR+, bf16 layers: (W_q omega^T)^T [H][RP][D] as bf16 hi + lo parts
+    const uint16_t* wqot_lo;
     const float2* tab;
     LrGeom g;
     void* out;               // [BH][L][D]
@@ -64,15 +70,22 @@ size_t select_scores_bytes(long BH, int nblk);
 hipError_t launch_select(int D, const float* qbar, const float* kbar, float* scores, int32_t* idx, long BH, int nblk,
                          int keep, hipStream_t st);
 hipError_t launch_lr_prep(const float* W, uint16_t* Wt, int H, int D, int R, int RP, hipStream_t st);
+// FAVOR+: (W omega^T)^T [H][RP][D] as bf16 hi + lo parts (W rounded to bf16 first when round_bf16), and, when
+// Et is non-null, eo [H][T + Hg + Wg][R] = the concatenated axis tables times omega^T
+hipError_t launch_lr_prep_favor(const float* W, const float* omega, int round_bf16, int H, int D, int R, int RP,
+                                uint16_t* wot_hi, uint16_t* wot_lo, const float* Et, const float* Eh, const float* Ew,
+                                int T, int Hg, int Wg, float* eo, hipStream_t st);
 // Workgroups of the summary kernel chosen for these arguments that the
 // current device holds at once (CUs x resident workgroups per CU; cached).
-hipError_t lr_summary_slots(int dtype_bf16, int D, int RP, bool abspe, bool tiled, int* slots);
+hipError_t lr_summary_slots(int dtype_bf16, int D, int RP, bool abspe, bool tiled, int* slots, bool favor = false);
 
 // kvt: when non-null (bf16, D = 128, 64-token blocks), V operands come from the [K | V^T] tiles
+// wkot_hi / wkot_lo: FAVOR+ on bf16 layers, (W_k omega^T)^T from launch_lr_prep_favor (else null)
 hipError_t launch_lr_summary(int dtype_bf16, int D, int RP, bool abspe, const void* k, const void* v,
                              const uint16_t* kvt, int nblk, const float* W, const uint16_t* wkt, const float* Et,
                              const float* Eh, const float* Ew, const float2* tab, const LrGeom& g, long BH, long L,
-                             int H, int chunk, int nsplit, float* part, hipStream_t st);
+                             int H, int chunk, int nsplit, float* part, hipStream_t st,
+                             const uint16_t* wkot_hi = nullptr, const uint16_t* wkot_lo = nullptr);
 hipError_t launch_lr_reduce(const float* part, long BH, int nsplit, int D, int R, int RP, float* S, float* z,
                             uint16_t* st_hi, uint16_t* st_lo, float* zp, hipStream_t st);
 // lr_mode: 0 = no low-rank term (plain attention), 1 = rotary after phi, 2 = absolute PE

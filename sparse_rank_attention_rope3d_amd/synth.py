@@ -36,6 +36,7 @@ TID_Q, TID_K, TID_V, TID_WQ, TID_WK, TID_GATE, TID_CENT, TID_CLUSTER = 0, 1, 2, 
 TID_ET, TID_EH, TID_EW = 8, 9, 10
 TID_WG, TID_BG = 11, 12
 TID_DOUT = 13      # upstream gradient of the layer output (backward)
+TID_OMEGA = 14     # FAVOR+ random directions
 TID_SAMPLE = 99  # query-block sample for the oracle's partial coverage
 
 N_CENTROIDS = 64
@@ -67,7 +68,8 @@ class Layer:
     gen: str                       # "normal", "clustered" or "zero_qk" (q = k = 0: every block score ties)
     eps: float = 1e-6
     gate: str = "head"             # combine gate: "head" (g_h) or "token" (RoLA §4.4)
-    fmap: str = "elu1"             # low-rank feature map: "elu1" (elu + 1) or "silu" (RoLA §5.3)
+    fmap: str = "elu1"             # low-rank feature map: "elu1" (elu + 1), "silu" (RoLA §5.3) or
+                                   # "favor" (positive random features, RoPeSLR appendix)
 
     @property
     def L(self) -> int:
@@ -212,8 +214,9 @@ def lowrank_params(cfg: Layer) -> Dict[str, np.ndarray]:
     """Per-head projections W_q, W_k [H, D, r] ~ N(0, 1/D) (variance), the
     per-head gate g [H] ~ U(0, 1), for the token gate W_g [H, D] ~ N(0, 1/D)
     and b_g [H] ~ U(-2, 0.5) (a mostly negative bias, as the pages start
-    the gate), and for the absolute-PE variant the axis tables E_t [T, r],
-    E_h [Hg, r], E_w [Wg, r] ~ N(0, 0.02) (variance)."""
+    the gate), for FAVOR+ features the random directions omega [H, r, r] ~
+    N(0, 1) (fp32, not rounded), and for the absolute-PE variant the axis
+    tables E_t [T, r], E_h [Hg, r], E_w [Wg, r] ~ N(0, 0.02) (variance)."""
     H, D, r = cfg.H, cfg.D, cfg.rank
     std = np.float32(1.0 / math.sqrt(D))
     wq = np.stack([_rng(cfg.seed, TID_WQ, 0, h).standard_normal((D, r), dtype=np.float32) * std
@@ -225,6 +228,11 @@ def lowrank_params(cfg: Layer) -> Dict[str, np.ndarray]:
     if cfg.gate == "token":
         out["wg"] = _rng(cfg.seed, TID_WG).standard_normal((H, D), dtype=np.float32) * std
         out["bg"] = _rng(cfg.seed, TID_BG).uniform(-2.0, 0.5, size=H).astype(np.float32)
+    if cfg.fmap == "favor":
+        # FAVOR+ random directions omega [H, r, r] ~ N(0, I_r) per row (the
+        # random numbers of the method, drawn here and passed in)
+        out["omega"] = np.stack([_rng(cfg.seed, TID_OMEGA, 0, h).standard_normal((r, r), dtype=np.float32)
+                                 for h in range(H)])
     if cfg.lr_mode == "abspe":
         es = np.float32(math.sqrt(EMBED_VAR))
         out["et"] = _rng(cfg.seed, TID_ET).standard_normal((cfg.T, r), dtype=np.float32) * es

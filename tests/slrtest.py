@@ -79,13 +79,23 @@ def max_abs(a: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(a - ref))) if a.size else 0.0
 
 
-def assert_close(name: str, got: np.ndarray, ref: np.ndarray, dtype: str) -> None:
+def assert_close(name: str, got: np.ndarray, ref: np.ndarray, dtype: str, branch: bool = False) -> None:
+    """Relative Frobenius and max-abs bars. ``branch``: a debug copy of one
+    branch (O_sparse, O_lowrank; or the summary S, z) rather than the layer
+    output; its values
+    can be far larger than the output's (a rotated low-rank numerator over an
+    un-rotated normaliser reaches ~10 with FAVOR+ features, where one bf16
+    half-ulp is 0.031), so its max-abs bar is max(3e-2, 2^-6 max|ref|), about
+    four bf16 half-ulps at its largest value."""
     t = TOL[dtype]
     rf, ma = rel_fro(got, ref), max_abs(got, ref)
     log(f"    {name}: rel_fro={rf:.3e} max_abs={ma:.3e}")
     assert rf <= t["rel"], f"{name}: relative Frobenius error {rf:.3e} > {t['rel']}"
     if t["maxabs"] is not None:
-        assert ma <= t["maxabs"], f"{name}: max abs error {ma:.3e} > {t['maxabs']}"
+        bar = t["maxabs"]
+        if branch and ref.size:
+            bar = max(bar, 2.0 ** -6 * float(np.abs(ref).max()))
+        assert ma <= bar, f"{name}: max abs error {ma:.3e} > {bar:.3e}"
 
 
 def check_selection(idx_gpu: np.ndarray, scores: np.ndarray, thr: np.ndarray, keep: int) -> None:
@@ -127,8 +137,9 @@ def check_layer(inp: Inputs, out, idx, o_sp, o_lr, slices: Optional[Iterable] = 
         tg = None
         if cfg.gate == "token":
             tg = (inp.params_np["wg"][h], float(inp.params_np["bg"][h]))
+        omega = inp.params_np["omega"][h] if cfg.fmap == "favor" else None
         res = oracle.layer_slice(cfg, qs, ks, vs, inp.params_np["wq"][h], inp.params_np["wk"][h],
-                                 inp.params_np["gate"][h], E, qblocks=qblocks, idx=ig, token_gate_wb=tg)
+                                 inp.params_np["gate"][h], E, qblocks=qblocks, idx=ig, token_gate_wb=tg, omega=omega)
         check_selection(ig, res["scores"], res["thr"], cfg.keep)
         differ += rows_differing(ig, res["idx_ref"])
         qb = res["qblocks"]
@@ -139,9 +150,10 @@ def check_layer(inp: Inputs, out, idx, o_sp, o_lr, slices: Optional[Iterable] = 
             gots[name].append(g[rows[valid]])
             refs[name].append(res[name].reshape(-1, cfg.D)[valid])
         if S_gpu is not None:
-            assert_close(f"S[{b},{h}]", to_host(S_gpu[b, h]), res["S"], cfg.dtype)
-            assert_close(f"z[{b},{h}]", to_host(z_gpu[b, h]), res["z"], cfg.dtype)
+            # sums over the L tokens: their max-abs bar scales with their magnitude like a branch's
+            assert_close(f"S[{b},{h}]", to_host(S_gpu[b, h]), res["S"], cfg.dtype, branch=True)
+            assert_close(f"z[{b},{h}]", to_host(z_gpu[b, h]), res["z"], cfg.dtype, branch=True)
     log(f"    selection rows differing from the oracle inside the window: {differ}")
     for name in ("out", "o_sp", "o_lr"):
-        assert_close(name, np.concatenate(gots[name]), np.concatenate(refs[name]), cfg.dtype)
+        assert_close(name, np.concatenate(gots[name]), np.concatenate(refs[name]), cfg.dtype, branch=name != "out")
     return {"differ": differ}

@@ -264,3 +264,29 @@ def test_training_forward_requires_its_outputs():
     assert call(osp=None) == B.SLR_EINVAL
     assert call(lse=None) == B.SLR_EINVAL
     assert call(lse=FAKE + 2) == B.SLR_EINVAL
+
+
+def test_favor_feature_map_needs_omega_and_has_no_backward():
+    """FAVOR+ features (SLR_FMAP_FAVOR) need the random directions; the
+    backward does not cover them (SLR_EUNSUPPORTED, before any other check
+    of its outputs)."""
+    shape, rope, sparse, lr = _cfgs()
+    lr.feature_map = B.SLR_FMAP_FAVOR
+    assert _attn(shape, rope, sparse, lr) == B.SLR_EINVAL          # omega missing
+    lr.omega = FAKE + 2
+    assert _attn(shape, rope, sparse, lr) == B.SLR_EINVAL          # misaligned
+    lr.omega = FAKE
+    assert _attn(shape, rope, sparse, lr) == B.SLR_EWORKSPACE
+    n_fav = B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lr)
+    lr.feature_map = B.SLR_FMAP_ELU1
+    n_elu = B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lr)
+    layer = synth.wan13b()
+    # four (W omega^T)^T bf16 parts [H, 32, D] on top
+    assert n_fav - n_elu >= 4 * 2 * layer.H * 32 * layer.D
+    lr.feature_map = B.SLR_FMAP_FAVOR
+    with pytest.raises(B.SlrError) as e:
+        B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lr)
+    assert e.value.code == B.SLR_EUNSUPPORTED
+    assert _bwd(shape, rope, sparse, lr) == B.SLR_EUNSUPPORTED
+    lr.feature_map = 3
+    assert _attn(shape, rope, sparse, lr) == B.SLR_EINVAL
