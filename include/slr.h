@@ -58,6 +58,8 @@ extern "C" {
 #define SLR_EUNSUPPORTED (-2)  /* valid but not built (e.g. D not 64/128) */
 #define SLR_EWORKSPACE (-3)    /* workspace missing or too small          */
 #define SLR_EHIP (-4)          /* a HIP call or kernel launch failed      */
+#define SLR_ESCRATCH (-5)      /* needs more than the fixed scratch of a
+                                  *_noalloc entry point                   */
 
 /* element types */
 #define SLR_F32 0
@@ -163,6 +165,26 @@ int slr_select_blocks(const slr_shape *shape, const slr_rope_cfg *rope, const sl
 int slr_lowrank_summary(const slr_shape *shape, const slr_rope_cfg *rope, const slr_lowrank_cfg *lowrank,
                         const void *k, const void *v, float *S, float *z,
                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * slr_lowrank_summary for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same sums with no workspace argument. Its scratch (rotary
+ * tables, projection copies, split-L partial sums) is a fixed per-GPU buffer
+ * of SLR_NOALLOC_SCRATCH_BYTES inside the library, held by every GPU the
+ * library runs on until the process ends; the call allocates nothing (no
+ * hipMalloc, no library allocation). When the partial sums would not fit,
+ * fewer splits are used (S and z then differ from slr_lowrank_summary's only
+ * by rounding order); a shape whose scratch exceeds the buffer even with one
+ * split per slice returns SLR_ESCRATCH before anything is launched. Every call
+ * on one GPU shares that buffer: calls that overlap on one GPU (different
+ * streams, or host threads without ordering) race and give undefined
+ * results; calls ordered on one stream are safe. The first call on a device
+ * looks up the buffer's device address (hipGetSymbolAddress).
+ */
+#define SLR_NOALLOC_SCRATCH_BYTES (32u << 20)
+int slr_lowrank_summary_noalloc(const slr_shape *shape, const slr_rope_cfg *rope, const slr_lowrank_cfg *lowrank,
+                                const void *k, const void *v, float *S, float *z, void *stream);
 
 /*
  * The whole hybrid layer forward (RoLA App. A, Algorithm 1):

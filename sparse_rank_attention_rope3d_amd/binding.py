@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libslr.so")
 
-SLR_OK, SLR_EINVAL, SLR_EUNSUPPORTED, SLR_EWORKSPACE, SLR_EHIP = 0, -1, -2, -3, -4
+SLR_OK, SLR_EINVAL, SLR_EUNSUPPORTED, SLR_EWORKSPACE, SLR_EHIP, SLR_ESCRATCH = 0, -1, -2, -3, -4, -5
 SLR_F32, SLR_BF16 = 0, 1
 SLR_LR_ROPE_OUTSIDE, SLR_LR_ABS_PE = 0, 1
 SLR_GATE_HEAD, SLR_GATE_TOKEN = 0, 1
@@ -26,7 +26,7 @@ SLR_OP_ROPE3D, SLR_OP_SELECT, SLR_OP_LOWRANK_SUMMARY, SLR_OP_ATTENTION, SLR_OP_D
 SLR_OP_ATTENTION_BWD = 5
 
 EXPORTS = ("slr_workspace_bytes", "slr_rope3d", "slr_select_blocks", "slr_lowrank_summary",
-           "slr_attention_fwd", "slr_attention_fwd_staged", "slr_attention_fwd_train", "slr_dense_attention_fwd",
+           "slr_lowrank_summary_noalloc", "slr_attention_fwd", "slr_attention_fwd_staged", "slr_attention_fwd_train", "slr_dense_attention_fwd",
            "slr_attention_bwd", "slr_status_string")
 
 
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
         L.slr_rope3d.argtypes = [P(SlrShape), P(SlrRopeCfg), vp, vp, vp, sz, vp]
         L.slr_select_blocks.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), vp, vp, vp, vp, vp, vp, sz, vp]
         L.slr_lowrank_summary.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrLowrankCfg), vp, vp, vp, vp, vp, sz, vp]
+        L.slr_lowrank_summary_noalloc.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrLowrankCfg), vp, vp, vp, vp, vp]
         L.slr_attention_fwd.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg), vp, vp, vp,
                                         vp, vp, vp, vp, vp, sz, vp]
         L.slr_attention_fwd_staged.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg), vp,
@@ -195,6 +196,19 @@ def slr_lowrank_summary(k: torch.Tensor, v: torch.Tensor, shape: SlrShape, rope:
     _check(lib().slr_lowrank_summary(ctypes.byref(shape), ctypes.byref(rope), ctypes.byref(lowrank), _ptr(k),
                                      _ptr(v), _ptr(S), _ptr(z), _ptr(ws), ws.numel(), _stream()),
            "slr_lowrank_summary")
+    return S, z
+
+
+def slr_lowrank_summary_noalloc(k: torch.Tensor, v: torch.Tensor, shape: SlrShape, rope: SlrRopeCfg,
+                                lowrank: SlrLowrankCfg, S: Optional[torch.Tensor] = None,
+                                z: Optional[torch.Tensor] = None):
+    """slr_lowrank_summary with the library's fixed scratch instead of a
+    workspace (S and z are still caller tensors)."""
+    S = torch.empty((shape.B, shape.H, lowrank.rank, shape.D), dtype=torch.float32, device=k.device) if S is None else S
+    z = torch.empty((shape.B, shape.H, lowrank.rank), dtype=torch.float32, device=k.device) if z is None else z
+    _check(lib().slr_lowrank_summary_noalloc(ctypes.byref(shape), ctypes.byref(rope), ctypes.byref(lowrank),
+                                             _ptr(k), _ptr(v), _ptr(S), _ptr(z), _stream()),
+           "slr_lowrank_summary_noalloc")
     return S, z
 
 

@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/slr.h"
 #include "slr_launch.h"
@@ -128,9 +129,10 @@ int summary_split_cap(const Dims& d) {
 // The split that minimises the modelled time when `slots` workgroups run at
 // once: rounds of workgroups x (128-token steps per workgroup + a fixed
 // per-workgroup cost of about three steps); ties go to fewer splits.
-// slots = 0 gives the cap.
-void summary_split(const Dims& d, int slots, int* chunk, int* nsplit) {
-    const int cap = summary_split_cap(d);
+// slots = 0 gives the cap. max_split (> 0) lowers the cap.
+void summary_split(const Dims& d, int slots, int* chunk, int* nsplit, int max_split = 0) {
+    int cap = summary_split_cap(d);
+    if (max_split > 0 && max_split < cap) cap = max_split;
     long best_cost = -1, best_c = 0, best_n = 0;
     for (int n = 1; n <= cap; ++n) {
         const long c = ((d.L + n - 1) / n + 127) / 128 * 128;
@@ -181,7 +183,7 @@ void lr_bwd_split(const Dims& d, int* chunk, int* nsplit) {
 }
 
 Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int keep, int R, int RP,
-              bool abspe = false, bool token = false, bool favor = false) {
+              bool abspe = false, bool token = false, bool favor = false, int max_split = 0) {
     Layout w;
     std::memset(&w, 0, sizeof(w));
     size_t off = 0;
@@ -248,7 +250,8 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         }
     }
     if (op == SLR_OP_ATTENTION || op == SLR_OP_LOWRANK_SUMMARY) {
-        const int nsplit = summary_split_cap(d);
+        int nsplit = summary_split_cap(d);
+        if (max_split > 0 && max_split < nsplit) nsplit = max_split;
         if (d.bf16) {
             w.wqt = take(2ul * d.H * RP * d.D);
             w.wkt = take(2ul * d.H * RP * d.D);
@@ -287,6 +290,33 @@ T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws)
         if ((expr) != hipSuccess) return SLR_EHIP;     \
     } while (0)
 
+// The fixed scratch of slr_lowrank_summary_noalloc: one copy per GPU, held
+// until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory: kernels get the address hipGetSymbolAddress returns for
+// the current device (kept per device below), never the name.
+constexpr size_t kScratchBytes = (size_t)SLR_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+// Device address of this GPU's scratch, looked up once per device (with that
+// device current) on the first call there.
+int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SLR_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return SLR_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SLR_EHIP;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return SLR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -298,6 +328,7 @@ const char* slr_status_string(int status) {
         case SLR_EUNSUPPORTED: return "SLR_EUNSUPPORTED: valid arguments outside the built kernel set";
         case SLR_EWORKSPACE: return "SLR_EWORKSPACE: workspace missing, misaligned or too small";
         case SLR_EHIP: return "SLR_EHIP: a HIP runtime call or kernel launch failed";
+        case SLR_ESCRATCH: return "SLR_ESCRATCH: the call needs more than the library's fixed scratch buffer";
         default: return "unknown slr status";
     }
 }
@@ -399,7 +430,7 @@ namespace {
 // Shared by the summary entry point and the layer forward.
 // FAVOR+ on bf16 layers: the projected axis tables of the absolute-PE
 // variant (shared by both sides), placed in the geometry the kernels get.
-int favor_tables(const Dims& d, LrGeom* lg, const slr_lowrank_cfg* lr, void* ws, const Layout& w, hipStream_t s) {
+static int favor_tables(const Dims& d, LrGeom* lg, const slr_lowrank_cfg* lr, void* ws, const Layout& w, hipStream_t s) {
     if (lr->feature_map != SLR_FMAP_FAVOR || !d.bf16 || lr->mode != SLR_LR_ABS_PE) return SLR_OK;
     float* eo = at<float>(ws, w.eo);
     SLR_TRY(launch_lr_prep_favor(nullptr, lr->omega, 1, (int)d.H, (int)d.D, lg->R, 0, nullptr, nullptr, lr->Et,
@@ -408,14 +439,14 @@ int favor_tables(const Dims& d, LrGeom* lg, const slr_lowrank_cfg* lr, void* ws,
     return SLR_OK;
 }
 
-int run_summary(const Dims& d, const RopeGeom& g, const LrGeom& lg, int RP, const slr_lowrank_cfg* lr, const void* k,
+static int run_summary(const Dims& d, const RopeGeom& g, const LrGeom& lg, int RP, const slr_lowrank_cfg* lr, const void* k,
                 const void* v, const uint16_t* kvt, int nblk, void* ws, const Layout& w, float* S, float* z,
-                bool want_st, hipStream_t s) {
+                bool want_st, hipStream_t s, int max_split = 0) {
     const bool abspe = lr->mode == SLR_LR_ABS_PE;
     const bool favor = lr->feature_map == SLR_FMAP_FAVOR;
     int slots = 0, chunk, nsplit;
     SLR_TRY(lr_summary_slots(d.bf16, (int)d.D, RP, abspe, kvt != nullptr, &slots, favor));
-    summary_split(d, slots, &chunk, &nsplit);
+    summary_split(d, slots, &chunk, &nsplit, max_split);
     const float2* tab = at<float2>(ws, w.tab);
     uint16_t* wkt = d.bf16 ? at<uint16_t>(ws, w.wkt) : nullptr;
     if (d.bf16) SLR_TRY(launch_lr_prep(lr->Wk, wkt, (int)d.H, (int)d.D, lg.R, RP, s));
@@ -460,9 +491,39 @@ int slr_lowrank_summary(const slr_shape* shape, const slr_rope_cfg* rope, const 
     return run_summary(d, g, lg, RP, lowrank, k, v, nullptr, 0, ws, w, S, z, false, s);
 }
 
+int slr_lowrank_summary_noalloc(const slr_shape* shape, const slr_rope_cfg* rope, const slr_lowrank_cfg* lowrank,
+                                const void* k, const void* v, float* S, float* z, void* stream) {
+    Dims d;
+    RopeGeom g;
+    LrGeom lg;
+    int RP;
+    int st = check_shape(shape, &d);
+    if (st) return st;
+    if ((st = check_rope(rope, d, &g))) return st;
+    if ((st = check_lowrank(lowrank, rope, d, false, &lg, &RP))) return st;
+    if (!tensor_ok(k) || !tensor_ok(v) || !S || !z || !aligned(S, 4) || !aligned(z, 4)) return SLR_EINVAL;
+    lg.rope = g;
+    // the most splits whose partial sums fit the fixed scratch (fewer splits:
+    // the same sums in a coarser fixed order)
+    const bool abspe = lowrank->mode == SLR_LR_ABS_PE, favor = lowrank->feature_map == SLR_FMAP_FAVOR;
+    int max_split = summary_split_cap(d);
+    Layout w = layout(SLR_OP_LOWRANK_SUMMARY, d, g, 64, 0, 0, lowrank->rank, RP, abspe, false, favor, max_split);
+    while (w.total > kScratchBytes && max_split > 1) {
+        --max_split;
+        w = layout(SLR_OP_LOWRANK_SUMMARY, d, g, 64, 0, 0, lowrank->rank, RP, abspe, false, favor, max_split);
+    }
+    if (w.total > kScratchBytes) return SLR_ESCRATCH;
+    void* ws = nullptr;
+    if ((st = scratch_address(&ws))) return st;
+    hipStream_t s = (hipStream_t)stream;
+    SLR_TRY(launch_rope_tables(at<float2>(ws, w.tab), g, rope->base, s));
+    if ((st = favor_tables(d, &lg, lowrank, ws, w, s))) return st;
+    return run_summary(d, g, lg, RP, lowrank, k, v, nullptr, 0, ws, w, S, z, false, s, max_split);
+}
+
 namespace {
 
-int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
+static int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
                   const slr_lowrank_cfg* lowrank, const void* q, const void* k, const void* v, void* out,
                   int32_t* idx_out, void* o_sparse_out, void* o_lowrank_out, float* lse_out, void* ws,
                   size_t ws_bytes, void* const* events, void* stream) {

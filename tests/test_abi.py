@@ -290,3 +290,19 @@ def test_favor_feature_map_needs_omega_and_has_no_backward():
     assert _bwd(shape, rope, sparse, lr) == B.SLR_EUNSUPPORTED
     lr.feature_map = 3
     assert _attn(shape, rope, sparse, lr) == B.SLR_EINVAL
+
+
+def test_noalloc_summary_validates_on_the_host():
+    """slr_lowrank_summary_noalloc checks its arguments and the size of its
+    fixed scratch before any HIP call."""
+    shape, rope, sparse, lr = _cfgs()
+    r = ctypes.byref
+    L = B.lib()
+    assert L.slr_lowrank_summary_noalloc(r(shape), r(rope), r(lr), FAKE, FAKE, None, FAKE, None) == B.SLR_EINVAL
+    assert L.slr_lowrank_summary_noalloc(r(shape), r(rope), r(lr), MISALIGNED, FAKE, FAKE, FAKE, None) == B.SLR_EINVAL
+    # 1024 slices at rank 64: more partial-sum bytes than the buffer holds, even at one split per slice
+    big = synth.Layer(**{**synth.wan13b().__dict__, "B": 16, "H": 64, "rank": 64, "lr_pairs": (16, 8, 8)})
+    s2, r2 = B.shape_of(big), B.rope_of(big)
+    lr2 = B.SlrLowrankCfg(64, B.SLR_LR_ROPE_OUTSIDE, 16, 8, 8, 1e-6, FAKE, FAKE, FAKE, None, None, None)
+    assert L.slr_lowrank_summary_noalloc(r(s2), r(r2), r(lr2), FAKE, FAKE, FAKE, FAKE, None) == B.SLR_ESCRATCH
+    assert "scratch" in B.status_string(B.SLR_ESCRATCH)
