@@ -15,7 +15,8 @@ from typing import Dict, Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libslr.so")
+# SLR_LIB selects another build of the same library (the host-sanitized one in the CPU ABI tests)
+LIB_PATH = os.environ.get("SLR_LIB") or os.path.join(_HERE, "libslr.so")
 
 SLR_OK, SLR_EINVAL, SLR_EUNSUPPORTED, SLR_EWORKSPACE, SLR_EHIP, SLR_ESCRATCH = 0, -1, -2, -3, -4, -5
 SLR_F32, SLR_BF16 = 0, 1
