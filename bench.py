@@ -42,8 +42,9 @@ METRIC = "SLR attn fwd ms/layer + effective TFLOP/s at L=32760/75600/118800, 1 G
 # on, identified by the sha256 of its files; any other source reports null.
 FLASH_TRAFFIC_SOURCES = ["k_flash.hip", "slr_common.h", "slr_launch.h"]
 FLASH_TRAFFIC = {
-    "sha256": "7d776f0545ef627a151a7e498bce077389493b0a1417e52510607e12c8671b19",
-    "bytes_per_launch": {"wan13b": 8202.8e6 + 201.3e6, "wan14b": 220518.4e6 + 1548.4e6},
+    "sha256": "cf0508e80607d6cccdb3a8e7f8f8e1b9358c2c484292572488efd6e75dc2c32f",
+    "bytes_per_launch": {"wan13b": 8203.9e6 + 201.3e6, "wan14b": 229030.0e6 + 1549.1e6,
+                         "hunyuan13b": 195059.5e6 + 730.2e6},
 }
 GEN_THREADS = 8   # input generation: numpy fills each slice's arrays without the GIL
 
@@ -122,10 +123,10 @@ def achievable_peaks(torch) -> dict:
 
 
 def memory_read_probe(torch) -> dict:
-    """Read-only streaming rate of a buffer at sizes that sit in the XCDs'
-    L2 (16 MB), in the 256 MB memory-side cache (64 and 160 MB) and in HBM
-    (1 and 4 GiB), with ordinary vector loads and with the direct
-    global -> LDS copies the flash kernel uses (libslr_probe.so)."""
+    """Read-only streaming rate of a buffer from 8 MB to 4 GiB (the XCDs'
+    L2s hold 32 MB, the memory-side cache 256 MB), with ordinary vector
+    loads and with the direct global -> LDS copies the flash kernel uses
+    (libslr_probe.so)."""
     path = os.path.join(ROOT, "sparse_rank_attention_rope3d_amd", "libslr_probe.so")
     if not os.path.exists(path):
         return None
@@ -139,7 +140,7 @@ def memory_read_probe(torch) -> dict:
     big = torch.ones(4 * 2 ** 30, dtype=torch.uint8, device="cuda")
     out = {}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for mb in (16, 64, 160, 1024, 4096):
+    for mb in (8, 16, 32, 48, 64, 80, 96, 128, 160, 256, 512, 1024, 4096):
         nbytes = mb * 2 ** 20
         passes = max(1, (8 * 2 ** 30) // nbytes)
         for to_lds in (0, 1):
@@ -156,8 +157,9 @@ def memory_read_probe(torch) -> dict:
             gbs = nbytes * passes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
             out[f"{mb}MB_{'to_lds' if to_lds else 'vgpr'}_GB/s"] = round(gbs, 1)
     del big, sink
-    out["what"] = ("read-only stream, 2048 workgroups x 256 threads, 16-byte loads; 16 MB fits the XCDs' L2, "
-                   "64/160 MB the memory-side cache, 1/4 GiB only HBM")
+    out["what"] = ("read-only stream, 2048 workgroups x 256 threads, 16-byte loads, each XCD touching one eighth "
+                   "of the buffer; up to 32 MB it fits the XCDs' L2s, up to 256 MB the memory-side cache, beyond "
+                   "that only HBM")
     return out
 
 
