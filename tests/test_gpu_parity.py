@@ -261,6 +261,22 @@ def test_select_blocks_and_rotated_outputs():
     T.log(f"    rows differing inside the window: {differ}")
 
 
+def test_select_blocks_with_long_rows():
+    """2063 blocks of 32 tokens per slice (keep 100): rows of more than 2048
+    scores, the widest row top-k instance (up to 64 keys per lane)."""
+    cfg = T.custom(synth.wan13b(), name="select 2063 blocks", B=1, H=1, T=6, Hg=100, Wg=110, block=32, keep=100,
+                   seed=17)
+    assert cfg.nblk > 2048
+    inp = T.make_inputs(cfg)
+    idx = B.slr_select_blocks(inp.q, inp.k, B.shape_of(cfg), B.rope_of(cfg), B.sparse_of(cfg))
+    torch.cuda.synchronize()
+    s = _oracle_scores(cfg, 0, 0)
+    ref, thr, _ = oracle.topk_blocks(s, cfg.keep)
+    ig = idx[0, 0].cpu().numpy()
+    T.check_selection(ig, s, thr, cfg.keep)
+    T.log(f"    rows differing inside the window: {T.rows_differing(ig, ref)}")
+
+
 def test_dense_attention_matches_oracle():
     for dtype in ("bf16", "f32"):
         cfg = T.custom(synth.wan13b(), name=f"dense {dtype}", B=1, H=2, T=3, Hg=7, Wg=11, dtype=dtype)  # L=231
