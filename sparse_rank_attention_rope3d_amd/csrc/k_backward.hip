@@ -312,26 +312,97 @@ __global__ __launch_bounds__(BS * 2) void k_bwd_dq(BwdArgs a, const int32_t* __r
 // ---------------------------------------------------------------------------
 // Streaming dQ for bf16, D = 128, 64-token blocks (every workload shape).
 //
-// Each key block has one contiguous 48 KB tile [K | V | K^T] in operand
-// order, written once per backward call (k_bwd_dq_tiles): every 1 KB chunk
-// is one wave's MFMA operand, lane l's 16 bytes at l * 16, so the LDS image
-// equals the memory image and direct global-to-LDS copies fill it.
-//   K chunk (kh, s):        lane l holds K[key 32kh + l%32][dims 16s + 8(l/32) .. +7]
-//   V chunk (kh, s):        lane l holds V[key 32kh + l%32][dims 16s + 8(l/32) .. +7]
-//   K^T chunk (kh, db, h2): lane l holds K[keys (slot16 order) 32kh + 16h2 + 8(l/32) .. +7][dim 32db + l%32]
-// Keys past L are zero (K from the zero-padded rotated copy).
+// Each key block has one contiguous 32 KB tile [K | V] in operand order,
+// written once per backward call (k_bwd_dq_tiles): every 1 KB chunk is one
+// wave's MFMA operand, lane l's 16 bytes in slot opslot(l, s) of the chunk, so
+// the LDS image equals the memory image and direct global-to-LDS copies fill
+// it.
+//   K chunk (kh, s): lane l holds K[key 32kh + l%32][dims 16s + 8(l/32) .. +7]
+//   V chunk (kh, s): lane l holds V[key 32kh + l%32][dims 16s + 8(l/32) .. +7]
+// The transposed operand K^T is read out of the K part with gfx950's
+// transposing LDS reads (lds_read_t8). Keys past L are zero (K from the
+// zero-padded rotated copy).
 constexpr int kDqPart = 64 * 128;           // elements of one part
-constexpr int kDqTileElems = 3 * kDqPart;   // [K | V | K^T]
-// Query-side tiles of the streaming dK/dV kernel: [Q | dO | Q^T | dO^T | stats]
-// per query block, the same chunk layouts with query rows in place of keys,
-// written by the dQ kernel (which holds those rows); stats = 2 KB of floats:
-// the rows' log2 normalisers [64], delta = dO . O [64], and 384 unused (one
-// 4-byte copy per lane of each of eight waves).
+constexpr int kDqTileElems = 2 * kDqPart;   // [K | V]
+// Query-side tiles of the streaming dK/dV kernel: [Q | dO | stats] per query
+// block, the same chunk layout with query rows in place of keys, written by
+// the dQ kernel (which holds those rows); stats = 2 KB of floats: the rows'
+// log2 normalisers [64], delta = dO . O [64], and 384 unused (one 4-byte copy
+// per lane of each of eight waves).
 constexpr int kQtStatsElems = 1024;
-constexpr int kQtTileElems = 4 * kDqPart + kQtStatsElems;
+constexpr int kQtTileElems = 2 * kDqPart + kQtStatsElems;
+static_assert(kDqTileElems * 2 == kBwdDqTileBytes && kQtTileElems * 2 == kBwdQtTileBytes, "tile sizes");
 
-// The dQ kernel's tile [K | V | K^T] of every key block, from the rotated k
-// rows (zero-padded to whole blocks) and v [L] (rows past L read as zero).
+// Slot of lane l's 16 bytes within operand chunk s of a part: l with bit 2
+// flipped in the upper half-wave and bit 3 flipped in odd chunks. Each aligned
+// group of 16 lanes keeps its 256 bytes, so a wave's 16-byte operand reads of
+// a chunk stay conflict-free, and the transposed 8-byte reads of lds_read_t8
+// (four rows x 16 dims of two neighbouring chunks per 32 lanes) fall on
+// distinct banks.
+__device__ __forceinline__ int opslot(int l, int s) { return l ^ ((l >> 3) & 4) ^ ((s & 1) << 3); }
+
+// Eight 16-byte LDS reads into distinct registers, read i at byte offset
+// (i >> 1) * SO from base0 (i even) or base1 (i odd); the block waits for
+// them itself.
+template <int SO>
+__device__ __forceinline__ void lds_read8x2(u32x4_t* r, const uint16_t* base0, const uint16_t* base1) {
+    const uint32_t a0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)base0;
+    const uint32_t a1 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)base1;
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:0\n\t"
+        "ds_read_b128 %1, %9 offset:0\n\t"
+        "ds_read_b128 %2, %8 offset:%10\n\t"
+        "ds_read_b128 %3, %9 offset:%10\n\t"
+        "ds_read_b128 %4, %8 offset:%11\n\t"
+        "ds_read_b128 %5, %9 offset:%11\n\t"
+        "ds_read_b128 %6, %8 offset:%12\n\t"
+        "ds_read_b128 %7, %9 offset:%12\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a0), "v"(a1), "n"(SO), "n"(2 * SO), "n"(3 * SO)
+        : "memory");
+}
+
+// Operand chunks (h, 0 .. 7) of a part into r[0 .. 7] (this lane's slots)
+__device__ __forceinline__ void lds_read_chunks(u32x4_t* r, const uint16_t* part, int h, int lane) {
+    lds_read8x2<2048>(r, part + ((h * 8) * 64 + opslot(lane, 0)) * 8, part + ((h * 8 + 1) * 64 + opslot(lane, 1)) * 8);
+}
+
+// Element offset, within the 32-row half h = 0 of a part, that this lane
+// addresses in the transposed read x (rows 8x ..) of chunk (db, h2) = (0, 0).
+// ds_read_tr16_b64 gives lane i of each 16-lane group the 16-bit element i % 4
+// of the 8 bytes addressed by lanes 4j + i / 4, j = 0 .. 3; lane c of group g
+// therefore addresses row 16h2 + 8x + 4(g / 2) + c / 4 at dims
+// 32db + 16(g % 2) + 4(c % 4) .. +3, and lane i receives those four rows at
+// dim 32db + 16(g % 2) + i.
+__device__ __forceinline__ int tr_lane_off(int lane, int x) {
+    const int c = lane & 15, gd = (lane >> 4) & 1, hf = lane >> 5, hh = (c & 3) >> 1;
+    // chunk s = 2db + gd; slot opslot(row + 32hh, s) = 32hh + 16h2 + 8(x ^ gd) + 4(hf ^ hh) + c / 4
+    return gd * 512 + (32 * hh + 8 * (x ^ gd) + 4 * (hf ^ hh) + (c >> 2)) * 8 + 4 * (c & 1);
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2_t lds_tr8(const uint16_t* p) {
+    const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+    return __builtin_bit_cast(u32x2_t, r);
+}
+
+// The eight A operand chunks (h, db, h2), i = 2db + h2, of X^T from a part
+// holding X: lane l gets X[rows 32h + 16h2 + 8(e / 4) + 4(l / 32) + e % 4,
+// e = 0 .. 7][dim 32db + l % 32], the row order in which a 32x32 score
+// accumulator holds its rows; t0 / t1 = part + 4096h + tr_lane_off(lane, 0 / 1).
+__device__ __forceinline__ void lds_read_t8(u32x4_t* at, const uint16_t* t0, const uint16_t* t1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int o = (i >> 1) * 1024 + (i & 1) * 128;
+        const u32x2_t lo = lds_tr8(t0 + o), hi = lds_tr8(t1 + o);
+        at[i] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    }
+}
+
+// The dQ kernel's tile [K | V] of every key block, from the rotated k rows
+// (zero-padded to whole blocks) and v [L] (rows past L read as zero).
 // Grid (nblk, BH).
 __global__ __launch_bounds__(256) void k_bwd_dq_tiles(const uint16_t* __restrict__ kr, const uint16_t* __restrict__ v,
                                                       long L, int nblk, uint16_t* __restrict__ tiles) {
@@ -341,71 +412,39 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiles(const uint16_t* __restrict
     const uint16_t* ks = kr + (bh * nblk + blk) * 64l * D;   // zero rows past L
     const uint16_t* vs = v + bh * L * D;
     uint16_t* t = tiles + (bh * nblk + blk) * (long)kDqTileElems;
-    // K and V parts: thread takes dims 8c .. 8c+7 of rows 16p + tid/16
-    {
-        const int c = tid & 15, rs = tid >> 4;
-        u32x4_t xk[4], xv[4];
+    // thread takes dims 8c .. 8c+7 of rows 16p + tid/16
+    const int c = tid & 15, rs = tid >> 4;
+    u32x4_t xk[4], xv[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int r = 16 * p + rs;
-            const long l = (long)blk * 64 + r;
-            xk[p] = ldg16(ks + (long)r * D + 8 * c);
-            const u32x4_t w = ldg16(vs + (l < L ? l : L - 1) * D + 8 * c);
+    for (int p = 0; p < 4; ++p) {
+        const int r = 16 * p + rs;
+        const long l = (long)blk * 64 + r;
+        xk[p] = ldg16(ks + (long)r * D + 8 * c);
+        const u32x4_t w = ldg16(vs + (l < L ? l : L - 1) * D + 8 * c);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xv[p][i] = l < L ? w[i] : 0u;
-        }
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int r = 16 * p + rs;
-            const int o = (((r >> 5) * 8 + (c >> 1)) * 64 + (r & 31) + 32 * (c & 1)) * 8;
-            stg16(t + o, xk[p]);
-            stg16(t + kDqPart + o, xv[p]);
-        }
+        for (int i = 0; i < 4; ++i) xv[p][i] = l < L ? w[i] : 0u;
     }
-    // K^T part: thread tid < 128 takes 8 keys (slots 8vh .. 8vh+7 of 16-key
-    // group vG) x 8 dims and transposes them in registers
-    if (tid >= 128) return;
-    const int vc = tid & 15, vg = (tid >> 4) & 7, vG = vg >> 1, vh = vg & 1;
-    uint32_t rows[8][4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const u32x4_t w = ldg16(ks + (long)(16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2)) * D + 8 * vc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rows[e][i] = w[i];
-    }
-    uint16_t* kt = t + 2 * kDqPart;
-    const int kh = vG >> 1, h2 = vG & 1;
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-        u32x4_t o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t a0 = rows[2 * i][f >> 1], a1 = rows[2 * i + 1][f >> 1];
-            o[i] = (f & 1) ? __builtin_amdgcn_perm(a1, a0, 0x07060302u) : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-        }
-        const int d = 8 * vc + f;
-        stg16(kt + ((kh * 8 + (d >> 5) * 2 + h2) * 64 + (d & 31) + 32 * vh) * 8, o);
+    for (int p = 0; p < 4; ++p) {
+        const int r = 16 * p + rs;
+        const int o = (((r >> 5) * 8 + (c >> 1)) * 64 + opslot((r & 31) + 32 * (c & 1), c >> 1)) * 8;
+        stg16(t + o, xk[p]);
+        stg16(t + kDqPart + o, xv[p]);
     }
 }
-
-// Eight 16-byte LDS reads 1 KB apart (one operand chunk each); the block
-// waits for its own reads (early-clobber outputs: no destination can alias
-// the address register).
-__device__ __forceinline__ void lds_read8k(u32x4_t* r, const uint16_t* base) { lds_read8x<1024, 2048>(r, base); }
 
 // Workgroup = 4 waves = one 64-row query block; wave (rh, kh) owns query rows
 // 32rh .. and keys 32kh .. of every kept tile: S^T = K Q^T and dP^T = V dO^T
 // (a lane owns one query row), dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.
-// The parts stream through LDS (80 KB: two workgroups per CU): K and V in
-// two-slot rings requested one tile ahead, K^T in one slot refilled as soon
-// as every wave has read it, and waited for only just before its reads (three
-// barriers per tile). The two key halves' dQ^T are added through LDS at the
-// end. The tiled path scores with q pre-multiplied by log2(e)/sqrt(D), so
-// p = exp2(score - lse2).
+// The tiles stream through a two-slot LDS ring (64 KB: two workgroups per
+// CU), each requested one tile ahead, one barrier per tile; K^T comes from
+// the K part by transposing reads. The two key halves' dQ^T are added through
+// LDS at the end. The tiled path scores with q pre-multiplied by
+// log2(e)/sqrt(D), so p = exp2(score - lse2).
 __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* __restrict__ idx_all,
                                                       const uint16_t* __restrict__ tiles_all) {
     constexpr int D = 128, BS = 64, PART = kDqPart, PLOADS = PART * 2 / (256 * 16);
-    __shared__ __attribute__((aligned(16))) uint16_t lds[5 * PART];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[4 * PART];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -452,51 +491,17 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* 
         a.delta[bh * rows + qrow] = qval ? dl : 0.f;
     }
     if (a.qtt) {
-        // this query block's tile [Q | dO | Q^T | dO^T | stats] for the streaming
-        // dK/dV kernel: qop / doop already are the Q / dO chunks (rh, s) of this
-        // lane (waves kh = 0 store Q, kh = 1 dO); the transposed parts go through
-        // LDS (the ring is not in use yet): rows row-major, then each thread
-        // transposes 8 rows x 8 dims in registers
+        // this query block's tile [Q | dO | stats] for the streaming dK/dV
+        // kernel: qop / doop already are the Q / dO chunks (rh, s) of this lane
+        // (waves kh = 0 store Q, kh = 1 dO)
         uint16_t* qt = const_cast<uint16_t*>(a.qtt) + (bh * nblk + qb) * (long)kQtTileElems;
-        constexpr int RLD = D + 8;
-        uint16_t* rm = lds + kh * (BS * RLD);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const u32x4_t x = kh == 0 ? qop[s] : doop[s];
-            stg16(qt + kh * PART + ((rh * 8 + s) * 64 + lane) * 8, x);
-            *reinterpret_cast<u32x4_t*>(rm + (32 * rh + l32) * RLD + 16 * s + 8 * hf) = x;
-        }
+        for (int s = 0; s < 8; ++s)
+            stg16(qt + kh * PART + ((rh * 8 + s) * 64 + opslot(lane, s)) * 8, kh == 0 ? qop[s] : doop[s]);
         if (hf == 0) {
-            float* st = reinterpret_cast<float*>(qt + 4 * PART);
+            float* st = reinterpret_cast<float*>(qt + 2 * PART);
             st[(kh == 0 ? 0 : 64) + 32 * rh + l32] = kh == 0 ? lse2 : (qval ? dl : 0.f);
         }
-        __syncthreads();
-        const int u = tid & 127, which = tid >> 7;   // 0: Q^T, 1: dO^T
-        const int vc = u & 15, vg = (u >> 4) & 7, vG = vg >> 1, vh = vg & 1;
-        const uint16_t* src = lds + which * (BS * RLD);
-        uint32_t rws[8][4];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const u32x4_t w =
-                *reinterpret_cast<const u32x4_t*>(src + (16 * vG + 4 * vh + (e & 3) + 8 * (e >> 2)) * RLD + 8 * vc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rws[e][i] = w[i];
-        }
-        uint16_t* tt = qt + (2 + which) * PART;
-        const int th = vG >> 1, h2 = vG & 1;
-#pragma unroll
-        for (int f = 0; f < 8; ++f) {
-            u32x4_t o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t a0 = rws[2 * i][f >> 1], a1 = rws[2 * i + 1][f >> 1];
-                o[i] = (f & 1) ? __builtin_amdgcn_perm(a1, a0, 0x07060302u)
-                               : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-            }
-            const int d = 8 * vc + f;
-            stg16(tt + ((th * 8 + (d >> 5) * 2 + h2) * 64 + (d & 31) + 32 * vh) * 8, o);
-        }
-        __syncthreads();   // the rows' LDS area becomes the ring
     }
 
     // entries outside [0, nblk) contribute nothing (their slot streams tile 0)
@@ -504,17 +509,20 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* 
         const int j = ix[n];
         return (unsigned)j < (unsigned)nblk ? j : 0;
     };
-    auto issue = [&](int j, int part, uint16_t* dst) {
-        const uint16_t* src = tiles + (long)j * kDqTileElems + part * PART;
+    // tile j -> ring slot sl: K to part sl, V to part 2 + sl
+    auto issue = [&](int j, int sl) {
+        const uint16_t* src = tiles + (long)j * kDqTileElems;
 #pragma unroll
-        for (int m = 0; m < PLOADS; ++m)
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(src + m * 256 * 8),
-                (__attribute__((address_space(3))) void*)(dst + (m * 256 + wave * 64) * 8), 16, 0, 0);
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int m = 0; m < PLOADS; ++m)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(src + p * PART + m * 256 * 8),
+                    (__attribute__((address_space(3))) void*)(lds + (2 * p + sl) * PART + (m * 256 + wave * 64) * 8),
+                    16, 0, 0);
     };
-    const int rd = ((kh * 8) * 64 + lane) * 8;   // this lane's chunks (kh, 0..7) within a part
     const bool ragged = (L % BS) != 0;
-    uint16_t* kt_slot = lds + 4 * PART;
+    const int tr0 = kh * 4096 + tr_lane_off(lane, 0), tr1 = kh * 4096 + tr_lane_off(lane, 1);
 
     f32x16_t dqacc[4];
 #pragma unroll
@@ -522,40 +530,32 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* 
 #pragma unroll
         for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
 
-    // K and V of tile t in slots t % 2 (K: parts 0, 1; V: parts 2, 3), K^T in
-    // part 4. Issue order: KT0 K0 V0, then per tile t: K(t+1) V(t+1) after the
-    // opening barrier (into the slots of tile t - 1, which it certifies as
-    // consumed), KT(t+1) after the barrier that follows every wave's K^T reads;
-    // so from tile 1 on the sequence is ..., K(t) V(t) KT(t) K(t+1) V(t+1) ...
-    if (ntile > 0) {
-        const int j0 = tile_of(0);
-        issue(j0, 2, kt_slot);
-        issue(j0, 0, lds);
-        issue(j0, 1, lds + 2 * PART);
-    }
+    // tile t in slot t % 2; tile t + 1 is requested right after the barrier
+    // that opens tile t (which certifies that every wave is done with tile
+    // t - 1, whose slot it takes)
+    if (ntile > 0) issue(tile_of(0), 0);
     for (int t = 0; t < ntile; ++t) {
         const int jraw = ix[t];
         const bool jok = (unsigned)jraw < (unsigned)nblk;
         const int sl = t & 1;
-        // K(t), V(t) landed; from tile 1 on, KT(t) (issued after them) may still be in flight
-        if (t > 0) wait_vmcnt<PLOADS>(); else wait_vmcnt<0>();
+        wait_vmcnt<0>();   // tile t landed (the only copies in flight)
         __builtin_amdgcn_s_barrier();
-        if (t + 1 < ntile) {
-            const int j1 = tile_of(t + 1);
-            issue(j1, 0, lds + (sl ^ 1) * PART);
-            issue(j1, 1, lds + (2 + (sl ^ 1)) * PART);
-        }
+        asm volatile("" ::: "memory");
+        if (t + 1 < ntile) issue(tile_of(t + 1), sl ^ 1);
+        const uint16_t* kp = lds + sl * PART;
         f32x16_t sacc, dpacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; dpacc[i] = 0.f; }
         u32x4_t op[8];
-        lds_read8k(op, lds + sl * PART + rd);
+        lds_read_chunks(op, kp, kh, lane);
 #pragma unroll
         for (int s = 0; s < 8; ++s) sacc = mfma32(op[s], qop[s], sacc);
         u32x4_t vop[8];
-        lds_read8k(vop, lds + (2 + sl) * PART + rd);
+        lds_read_chunks(vop, lds + (2 + sl) * PART, kh, lane);
 #pragma unroll
         for (int s = 0; s < 8; ++s) dpacc = mfma32(vop[s], doop[s], dpacc);
+        u32x4_t at[8];   // K^T chunks (kh, db, h2) = (kh, i / 2, i % 2)
+        lds_read_t8(at, kp + tr0, kp + tr1);
         const long key0 = (long)jraw * BS + 32 * kh + 4 * hf;
         float ds[16];
 #pragma unroll
@@ -568,15 +568,6 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* 
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
             for (int i = 0; i < 4; ++i) dsop[h2][i] = pack_bf2(ds[8 * h2 + 2 * i], ds[8 * h2 + 2 * i + 1]);
-        u32x4_t at[8];   // K^T chunks (kh, db, h2) = (kh, i / 2, i % 2)
-        if (t > 0) {
-            // outstanding in issue order: ..., KT(t), K(t+1), V(t+1) (the last two only if t + 1 < ntile)
-            if (t + 1 < ntile) wait_vmcnt<2 * PLOADS>(); else wait_vmcnt<0>();
-            __builtin_amdgcn_s_barrier();
-        }
-        lds_read8k(at, kt_slot + rd);
-        __builtin_amdgcn_s_barrier();   // every wave has its K^T operands: refill the slot
-        if (t + 1 < ntile) issue(tile_of(t + 1), 2, kt_slot);
 #pragma unroll
         for (int i = 0; i < 8; ++i) dqacc[i >> 1] = mfma32(at[i], dsop[i & 1], dqacc[i >> 1]);
     }
@@ -629,19 +620,20 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* 
 // through LDS and adds dO^T P; the dK wave meanwhile computes dP = dO V^T,
 // then dS = P (dP - delta), and adds Q^T dS: 16 MFMAs per wave per tile.
 // Waves w and w + 4 share a SIMD, one of each role (two waves per SIMD). The
-// query-side tiles [Q | dO | Q^T | dO^T | stats] stream through two-slot LDS
-// rings (132 KB, and 16 KB for P), requested one tile ahead; two barriers
-// per tile (tile landed, P handed over). The query halves' partial sums are
-// added through LDS at the end.
+// query-side tiles [Q | dO | stats] stream through a two-slot LDS ring
+// (68 KB, and 16 KB for P), requested one tile ahead; Q^T and dO^T come from
+// the Q and dO parts by transposing reads. Two barriers per tile (tile
+// landed, P handed over). The query halves' partial sums are added through
+// LDS at the end.
 template <int ROLE>
 __device__ __forceinline__ void dkdv_tiled_loop(const BwdArgs& a, uint16_t* lds, const uint16_t* qt,
                                                 const int32_t* list, int n0, int n1, int tid, int wave, int lane,
                                                 int qh, int hf, const u32x4_t* op, float* pex,
                                                 f32x16_t* acc) {
     constexpr int PART = kDqPart, TILE = kQtTileElems, PL = PART * 2 / (512 * 16);
-    constexpr int FSZ = 2 * PART + kQtStatsElems;   // first-use group in LDS: [Q | dO | stats]
-    // First-use group of tile i -> F slot: Q, dO (two 16-byte copies per lane
-    // each) and the 2 KB of row statistics (one 4-byte copy per lane)
+    constexpr int FSZ = 2 * PART + kQtStatsElems;   // one slot: [Q | dO | stats]
+    // Tile i -> a slot: Q, dO (two 16-byte copies per lane each) and the 2 KB
+    // of row statistics (one 4-byte copy per lane)
     auto issue_f = [&](int i, uint16_t* slot) {
         const uint16_t* src = qt + (long)i * TILE;
 #pragma unroll
@@ -651,43 +643,25 @@ __device__ __forceinline__ void dkdv_tiled_loop(const BwdArgs& a, uint16_t* lds,
                 __builtin_amdgcn_global_load_lds(
                     (const __attribute__((address_space(1))) void*)(src + p * PART + (m * 512 + tid) * 8),
                     (__attribute__((address_space(3))) void*)(slot + p * PART + (m * 512 + wave * 64) * 8), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 4 * PART + tid * 2),
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 2 * PART + tid * 2),
                                          (__attribute__((address_space(3))) void*)(slot + 2 * PART + wave * 128), 4,
                                          0, 0);
     };
-    // Transposed group [Q^T | dO^T] of tile i -> a T slot
-    auto issue_t = [&](int i, uint16_t* tslot) {
-        const uint16_t* src = qt + (long)i * TILE + 2 * PART;
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-            for (int m = 0; m < PL; ++m)
-                __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void*)(src + p * PART + (m * 512 + tid) * 8),
-                    (__attribute__((address_space(3))) void*)(tslot + p * PART + (m * 512 + wave * 64) * 8), 16, 0,
-                    0);
-    };
     auto qblock = [&](int n) { return __builtin_amdgcn_readfirstlane(list[n]); };
-    const int rd = ((qh * 8) * 64 + lane) * 8;   // this lane's chunks (qh, 0..7) within a part
     const int ntile = n1 - n0;
-    uint16_t* tbase = lds + 2 * FSZ;
-    // Tile t in F slot t % 2 and T slot t % 2; both groups of tile t + 1 are
-    // requested right after the barrier that opens tile t (which certifies
-    // that every wave is done with tile t - 1, whose slots they take).
-    if (ntile > 0) {
-        issue_f(qblock(n0), lds);
-        issue_t(qblock(n0), tbase);
-    }
+    // transposed reads of Q (dK waves) or dO (dV waves): this lane's addresses in part 0
+    const int tpart = ROLE == 0 ? PART : 0;
+    const int tr0 = tpart + qh * 4096 + tr_lane_off(lane, 0), tr1 = tpart + qh * 4096 + tr_lane_off(lane, 1);
+    // Tile t in slot t % 2; tile t + 1 is requested right after the barrier
+    // that opens tile t (which certifies that every wave is done with tile
+    // t - 1, whose slot it takes).
+    if (ntile > 0) issue_f(qblock(n0), lds);
     for (int t = 0; t < ntile; ++t) {
         wait_vmcnt<0>();   // tile t landed (the only copies in flight)
         __builtin_amdgcn_s_barrier();
-        if (t + 1 < ntile) {
-            const int i1 = qblock(n0 + t + 1);
-            issue_f(i1, lds + ((t + 1) & 1) * FSZ);
-            issue_t(i1, tbase + ((t + 1) & 1) * (2 * PART));
-        }
+        asm volatile("" ::: "memory");
+        if (t + 1 < ntile) issue_f(qblock(n0 + t + 1), lds + ((t + 1) & 1) * FSZ);
         const uint16_t* cur = lds + (t & 1) * FSZ;
-        const uint16_t* tcur = tbase + (t & 1) * (2 * PART);
         const float* st = reinterpret_cast<const float*>(cur + 2 * PART) + 32 * qh + 4 * hf;
         // dV waves: S = Q K^T and P, handed to the dK wave of the same (kw, qh)
         // through LDS; dK waves meanwhile: dP = dO V^T
@@ -695,7 +669,7 @@ __device__ __forceinline__ void dkdv_tiled_loop(const BwdArgs& a, uint16_t* lds,
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
         u32x4_t aq[8];
-        lds_read8k(aq, cur + (ROLE == 0 ? 0 : PART) + rd);
+        lds_read_chunks(aq, cur + (ROLE == 0 ? 0 : PART), qh, lane);
 #pragma unroll
         for (int s = 0; s < 8; ++s) sacc = mfma32(aq[s], op[s], sacc);
         u32x4_t bop[2];   // P (dV waves) or dS (dK waves): the keys' B operand of the second product
@@ -735,7 +709,7 @@ __device__ __forceinline__ void dkdv_tiled_loop(const BwdArgs& a, uint16_t* lds,
                 for (int e = 0; e < 4; ++e) bop[h2][e] = pack_bf2(ds[8 * h2 + 2 * e], ds[8 * h2 + 2 * e + 1]);
         }
         u32x4_t at[8];   // dO^T (dV waves) or Q^T (dK waves) chunks (qh, db, h2) = (qh, i / 2, i % 2)
-        lds_read8k(at, tcur + (ROLE == 0 ? PART : 0) + rd);
+        lds_read_t8(at, cur + tr0, cur + tr1);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i >> 1] = mfma32(at[i], bop[i & 1], acc[i >> 1]);
     }
@@ -746,7 +720,7 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_tiled(BwdArgs a, const int32_t
                                                         const int32_t* __restrict__ order,
                                                         const uint16_t* __restrict__ qt_all) {
     constexpr int D = 128, BS = 64, TILE = kQtTileElems;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (2 * kDqPart + kQtStatsElems) + 4 * kDqPart];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (2 * kDqPart + kQtStatsElems)];
     __shared__ float pex_all[4][16 * 64];   // P of each (kw, qh), from the dV wave to the dK wave
 
     const int tid = threadIdx.x, lane = tid & 63;

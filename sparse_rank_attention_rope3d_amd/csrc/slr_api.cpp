@@ -233,8 +233,8 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         w.list = take(4ul * d.BH * nblk * keep);
         w.order = take(4ul * d.BH * nblk);
         if (use_tiles(d, bs)) {
-            w.dqt = take(2ul * d.BH * nblk * 3 * 64 * 128);
-            w.qtt = take(2ul * d.BH * nblk * (4 * 64 * 128 + 1024));
+            w.dqt = take(d.BH * nblk * kBwdDqTileBytes);
+            w.qtt = take(d.BH * nblk * kBwdQtTileBytes);
         }
         w.total = off;
         return w;

@@ -7,6 +7,11 @@ namespace slr {
 
 // ---- backward pass ---------------------------------------------------------
 
+// Bytes per block of the streaming kernels' tiles (bf16, D = 128, 64-token
+// blocks): [K | V] for dQ, [Q | dO | 2 KB of row statistics] for dK/dV.
+constexpr size_t kBwdDqTileBytes = 2ul * 64 * 128 * 2;
+constexpr size_t kBwdQtTileBytes = (2ul * 64 * 128 + 1024) * 2;
+
 // Sparse branch: softmax attention over the kept blocks, differentiated.
 struct BwdArgs {
     const uint16_t* qr;        // [BH][nblk*BS][D] rotated q, zero rows past L (unscaled)
@@ -18,10 +23,10 @@ struct BwdArgs {
     const int32_t* inv_off;    // [BH][nblk + 1] query-block list offsets per key block
     const int32_t* inv_list;   // [BH][nblk * keep] query blocks keeping each key block, ascending
     const int32_t* order;      // [BH][nblk] key blocks by list length, longest first (dK/dV launch order)
-    const uint16_t* dqt;       // bf16, D = 128, 64-token blocks: [BH][nblk][K | V | K^T] 48 KB operand-order
+    const uint16_t* dqt;       // bf16, D = 128, 64-token blocks: [BH][nblk][K | V] 32 KB operand-order
                                // tiles of the streaming dQ kernel (null: the staging kernel)
-    const uint16_t* qtt;       // same shapes: [BH][nblk][Q | dO | Q^T | dO^T | stats] 66 KB tiles of the
-                               // streaming dK/dV kernel, written by the dQ kernel (null: staging kernels)
+    const uint16_t* qtt;       // same shapes: [BH][nblk][Q | dO | stats] 34 KB tiles of the streaming
+                               // dK/dV kernel, written by the dQ kernel (null: staging kernels)
     const float* lse_in;       // [BH][L] the forward's log2 normalisers
     float* lse2;               // [BH][nblk*BS] the same, zero on padded rows
     float qmul;                // score (log2 units) = qmul * (q_rot . k_rot): log2(e)/sqrt(D), or 1
