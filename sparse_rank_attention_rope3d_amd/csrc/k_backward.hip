@@ -1758,6 +1758,500 @@ __global__ __launch_bounds__(256) void k_bwd_lr_k(LrBwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Low-rank branch on MFMA (lr_bwd_on_mfma: bf16, D = 128, R = 32 or 64,
+// rotary features, per-head gate). Tokens sit on the MFMA column axis: lane
+// l owns token l % 32 of its wave's 32, and a product over d leaves rank
+// r = 32rb + 8(v/4) + 4(l/32) + v%4 in register v of block rb (the slot16
+// order), which is the B operand layout of a product over r, and keeps each
+// rank pair (2j, 2j+1) of a token in one lane for the rotations. q, k, v,
+// dout and the bf16-rounded W are exact in bf16; fp32 operands (S, dS and
+// the per-token rank vectors) enter as hi + lo bf16 pairs (hi = bf16(x),
+// lo = bf16(x - hi)), and the products take hi*hi + lo*hi (+ hi*lo), about
+// 16 significant bits. Workgroup = 4 waves, 32 tokens per wave per step.
+//
+//   k_bwd_lrm_q    p^T = W_q^T q^T, f = phi(p), fq = rho(f), n = f . z + eps
+//                  (L for SiLU), sg = S dout (dout . O_un = fq . sg),
+//                  dot = fq . sg / n, dpq = (rho^T(g sg / n) - (g dot / n) z) phi',
+//                  dq_lr = W_q dpq; stores dpq and fq g / n (hi, lo) per token,
+//                  and the workgroup's sums of dn f (dz) and dot (dg).
+//   k_bwd_lrm_k    u = phi(k W_k), fk = rho(u), dv_lr = dS^T fk,
+//                  dpk = (rho^T(dS v) + dz) phi', dk_lr = W_k dpk; stores dpk.
+//   k_bwd_lrm_red  per (slice, split): sum over the split's tokens of
+//                  x^T y (x [t][128] bf16, y [t][R] hi + lo): dW_q = q^T dpq,
+//                  dS^T = dout^T (fq g / n), dW_k = k^T dpk.
+
+// Operand-order LDS copies of an R x 128 matrix m(r, d) (1 KB blocks, lane
+// l's 16 bytes at l * 16):
+//   rd: A[row r][k = d], block (rb, s) = 8rb + s, lane l: m(32rb + l%32, 16s + 8(l/32) + e)
+//   dr: A[row d][k = r], block (db, ks) = db (R/16) + ks, lane l:
+//       m(16ks + 8(e/4) + 4(l/32) + e%4, 32db + l%32)
+// SPLIT: hi to `hi`, lo to `lo`; else the bf16 rounding to `hi`.
+template <int R, bool DR, bool SPLIT, typename M>
+__device__ __forceinline__ void lrm_build(u32x4_t* hi, u32x4_t* lo, M m, int tid) {
+    constexpr int NBLK = R / 4;   // (R / 32) * 8 = 4 * (R / 16)
+    for (int it = tid; it < NBLK * 64; it += 256) {
+        const int blk = it >> 6, l = it & 63, h = l >> 5;
+        float x[8];
+        if constexpr (!DR) {
+            const int rb = blk >> 3, s = blk & 7;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = m(32 * rb + (l & 31), 16 * s + 8 * h + e);
+        } else {
+            const int db = blk / (R / 16), ks = blk % (R / 16);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = m(16 * ks + 8 * (e >> 2) + 4 * h + (e & 3), 32 * db + (l & 31));
+        }
+        u32x4_t a, b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[i] = pack_bf2(x[2 * i], x[2 * i + 1]);
+            if constexpr (SPLIT)
+                b[i] = pack_bf2(x[2 * i] - bf_lo(a[i]), x[2 * i + 1] - bf_hi(a[i]));
+        }
+        hi[it] = a;
+        if constexpr (SPLIT) lo[it] = b;
+    }
+}
+
+// B operands (hi, lo) of k-step ks = (rb, h2) of a product over r from a
+// rank vector in accumulator layout: registers 8h2 .. 8h2 + 7 of block rb
+__device__ __forceinline__ void lrm_bop(const f32x16_t& y, int h2, u32x4_t& hi, u32x4_t& lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float x0 = y[8 * h2 + 2 * i], x1 = y[8 * h2 + 2 * i + 1];
+        hi[i] = pack_bf2(x0, x1);
+        lo[i] = pack_bf2(x0 - bf_lo(hi[i]), x1 - bf_hi(hi[i]));
+    }
+}
+
+// The 8 B operands of a product over d (lane: token row t, dims 16s + 8(l/32) .. +7); zero past t_hi
+__device__ __forceinline__ void lrm_rowops(u32x4_t* b, const uint16_t* row, bool valid, int hf) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const u32x4_t w = ldg16(row + 16 * s + 8 * hf);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[s][i] = valid ? w[i] : 0u;
+    }
+}
+
+// Stores of a rank vector in accumulator layout to y [t][R] as bf16 hi + lo
+template <int NR>
+__device__ __forceinline__ void lrm_store_rank(const f32x16_t* y, uint16_t* dh, uint16_t* dl, int hf) {
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int r0 = 32 * rb + 8 * g4 + 4 * hf;
+            uint32_t h[2], l[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const float x0 = y[rb][4 * g4 + 2 * i], x1 = y[rb][4 * g4 + 2 * i + 1];
+                h[i] = pack_bf2(x0, x1);
+                l[i] = pack_bf2(x0 - bf_lo(h[i]), x1 - bf_hi(h[i]));
+            }
+            *reinterpret_cast<u32x2_t*>(dh + r0) = u32x2_t{h[0], h[1]};
+            *reinterpret_cast<u32x2_t*>(dl + r0) = u32x2_t{l[0], l[1]};
+        }
+}
+
+// phi and phi' without branches: elu + 1 or SiLU
+template <bool SILU>
+__device__ __forceinline__ void lrm_phi(float x, float& f, float& df) {
+    if constexpr (SILU) {
+        const float sg = 1.f / (1.f + expf(-x));
+        f = x * sg;
+        df = sg * (1.f + x * (1.f - sg));
+    } else {
+        const float e = expf(fminf(x, 0.f));
+        f = x > 0.f ? x + 1.f : e;
+        df = x > 0.f ? 1.f : e;
+    }
+}
+
+// z (or dz) at the ranks register v of block rb holds: 4 consecutive floats per group v / 4
+__device__ __forceinline__ float4 lrm_z4(const float* z_s, int rb, int g4, int hf) {
+    return *reinterpret_cast<const float4*>(z_s + 32 * rb + 8 * g4 + 4 * hf);
+}
+
+// (cos, sin) of the rank pairs (v, v + 1), v even, of block rb at token coordinates crd
+template <int NR>
+__device__ __forceinline__ void lrm_pairs_cs(const LrBwdArgs& a, const int* crd, int hf, float2 (*cs)[8]) {
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            cs[rb][j] = lowrank_cs(a.tab, a.g, 16 * rb + 4 * (j >> 1) + 2 * hf + (j & 1), crd);
+}
+
+// y = W dpq (or dS^T fk ...): the 4 column blocks of a [128] x [R] product over r, one at a
+// time, each stored (for valid tokens) as it completes; bh / bl: hi / lo B operands of the
+// k-steps. Called by the whole wave: lane l supplies the A operand's row l % 32 for every
+// token, so the products must not sit under a branch on the lane's own token.
+template <int KS, bool THREE>
+__device__ __forceinline__ void lrm_apply_store(const u32x4_t* ahi, const u32x4_t* alo, const u32x4_t* bh,
+                                                const u32x4_t* bl, int lane, float* dst, int hf, bool valid) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        f32x16_t y;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4_t w = ahi[(db * KS + ks) * 64 + lane];
+            y = mfma32(w, bh[ks], y);
+            y = mfma32(w, bl[ks], y);
+            if constexpr (THREE) y = mfma32(alo[(db * KS + ks) * 64 + lane], bh[ks], y);
+        }
+        if (valid) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+                *reinterpret_cast<float4*>(dst + 32 * db + 8 * g4 + 4 * hf) =
+                    make_float4(y[4 * g4], y[4 * g4 + 1], y[4 * g4 + 2], y[4 * g4 + 3]);
+        }
+    }
+}
+
+template <int R, bool SILU>
+__global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
+    constexpr int D = 128, NR = R / 32, NB = R / 4, KS = R / 16;
+    __shared__ u32x4_t w_rd[NB * 64], w_dr[NB * 64], s_hi[NB * 64], s_lo[NB * 64];
+    __shared__ __attribute__((aligned(16))) float z_s[R];
+    __shared__ float red[4][R + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
+    const int split = blockIdx.x;
+    const long bh = blockIdx.y;
+    const int head = (int)(bh % a.H);
+    const long L = a.L;
+    const long t_lo = (long)split * a.chunk;
+    const long t_hi = t_lo + a.chunk < L ? t_lo + a.chunk : L;
+    const float gh = a.gate[head];
+    const float* W = a.Wq + (long)head * D * R;
+    const float* S = a.S + bh * R * D;
+    lrm_build<R, false, false>(w_rd, nullptr, [&](int r, int d) { return W[d * R + r]; }, tid);
+    lrm_build<R, true, false>(w_dr, nullptr, [&](int r, int d) { return W[d * R + r]; }, tid);
+    lrm_build<R, false, true>(s_hi, s_lo, [&](int r, int d) { return S[r * D + d]; }, tid);
+    for (int e = tid; e < R; e += 256) z_s[e] = a.z[bh * R + e];
+    __syncthreads();
+    float accz[NR][16];
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) accz[rb][v] = 0.f;
+    float accg = 0.f;
+
+    for (long t0 = t_lo + 32 * wave; t0 < t_hi; t0 += 128) {
+        const long t = t0 + (lane & 31);
+        const bool valid = t < t_hi;
+        const long row = bh * L + (valid ? t : t_lo);
+        int crd[3];
+        token_coords(valid ? t : 0, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
+        // f = phi(q W_q), phi', n
+        f32x16_t f[NR], df[NR];
+        float nz = 0.f;
+        {
+            u32x4_t xb[8];
+            lrm_rowops(xb, a.q + row * D, valid, hf);
+#pragma unroll
+            for (int rb = 0; rb < NR; ++rb) {
+                f32x16_t p;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) p[i] = 0.f;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) p = mfma32(w_rd[(8 * rb + s) * 64 + lane], xb[s], p);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    float fv, dv;
+                    lrm_phi<SILU>(p[v], fv, dv);
+                    f[rb][v] = fv;
+                    df[rb][v] = dv;
+                }
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const float4 z4 = lrm_z4(z_s, rb, g4, hf);
+                    nz += f[rb][4 * g4] * z4.x + f[rb][4 * g4 + 1] * z4.y + f[rb][4 * g4 + 2] * z4.z +
+                          f[rb][4 * g4 + 3] * z4.w;
+                }
+            }
+        }
+        // sg = S dout
+        f32x16_t sg[NR];
+        {
+            u32x4_t gb[8];
+            lrm_rowops(gb, a.dout + row * D, valid, hf);
+#pragma unroll
+            for (int rb = 0; rb < NR; ++rb) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sg[rb][i] = 0.f;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const int bi = (8 * rb + s) * 64 + lane;
+                    sg[rb] = mfma32(s_hi[bi], gb[s], sg[rb]);
+                    sg[rb] = mfma32(s_lo[bi], gb[s], sg[rb]);
+                }
+            }
+        }
+        // fq = rho(f) and dout . O_un = fq . sg
+        float2 cs[NR][8];
+        lrm_pairs_cs<NR>(a, crd, hf, cs);
+        f32x16_t fq[NR];
+        float dsum = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float f0 = f[rb][2 * j], f1 = f[rb][2 * j + 1];
+                fq[rb][2 * j] = f0 * cs[rb][j].x - f1 * cs[rb][j].y;
+                fq[rb][2 * j + 1] = f0 * cs[rb][j].y + f1 * cs[rb][j].x;
+                dsum += fq[rb][2 * j] * sg[rb][2 * j] + fq[rb][2 * j + 1] * sg[rb][2 * j + 1];
+            }
+        const float n = SILU ? (float)L : sum_xor32(nz) + a.eps;
+        const float invn = 1.f / n;
+        const float dot = valid ? sum_xor32(dsum) * invn : 0.f;
+        const float dn = SILU ? 0.f : -gh * dot * invn;
+        const float sc = valid ? gh * invn : 0.f;
+        if (hf == 0) accg += dot;
+        // dz terms; dpq = (rho^T(sg sc) + dn z) phi' in place in sg; fq sc in place in fq
+#pragma unroll
+        for (int rb = 0; rb < NR; ++rb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                accz[rb][v] += dn * f[rb][v];
+                fq[rb][v] *= sc;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float4 z4 = lrm_z4(z_s, rb, j >> 1, hf);
+                const float za = (j & 1) ? z4.z : z4.x, zb = (j & 1) ? z4.w : z4.y;
+                float y0 = sg[rb][2 * j] * sc, y1 = sg[rb][2 * j + 1] * sc;
+                rot_t(y0, y1, cs[rb][j]);
+                sg[rb][2 * j] = (y0 + dn * za) * df[rb][2 * j];
+                sg[rb][2 * j + 1] = (y1 + dn * zb) * df[rb][2 * j + 1];
+            }
+        }
+        if (valid) {
+            lrm_store_rank<NR>(sg, a.y1h + row * R, a.y1l + row * R, hf);
+            lrm_store_rank<NR>(fq, a.y2h + row * R, a.y2l + row * R, hf);
+        }
+        // dq_lr = W_q dpq
+        u32x4_t bh_[KS], bl_[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) lrm_bop(sg[ks >> 1], ks & 1, bh_[ks], bl_[ks]);
+        lrm_apply_store<KS, false>(w_dr, nullptr, bh_, bl_, lane, a.dq_lr + row * D, hf, valid);
+    }
+    // workgroup sums: dz over the 32 tokens of each lane half, then the waves in order; dg
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            float x = accz[rb][v];
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o, 64);
+            if ((lane & 31) == 0) red[wave][32 * rb + 8 * (v >> 2) + 4 * hf + (v & 3)] = x;
+        }
+    float g = accg;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) g += __shfl_xor(g, o, 64);
+    if (lane == 0) red[wave][R] = g;
+    __syncthreads();
+    float* part = a.part + (bh * a.nsplit + split) * (long)(2 * D * R + R + 4);
+    if (tid <= R) part[2 * D * R + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+}
+
+template <int R, bool SILU>
+__global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
+    constexpr int D = 128, NR = R / 32, NB = R / 4, KS = R / 16;
+    __shared__ u32x4_t w_rd[NB * 64], w_dr[NB * 64], s_rd_hi[NB * 64], s_rd_lo[NB * 64], s_dr_hi[NB * 64],
+        s_dr_lo[NB * 64];
+    __shared__ __attribute__((aligned(16))) float z_s[R];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
+    const int split = blockIdx.x;
+    const long bh = blockIdx.y;
+    const int head = (int)(bh % a.H);
+    const long L = a.L;
+    const long t_lo = (long)split * a.chunk;
+    const long t_hi = t_lo + a.chunk < L ? t_lo + a.chunk : L;
+    const float* W = a.Wk + (long)head * D * R;
+    const float* dS = a.dSz + bh * (long)(R * D + R);
+    lrm_build<R, false, false>(w_rd, nullptr, [&](int r, int d) { return W[d * R + r]; }, tid);
+    lrm_build<R, true, false>(w_dr, nullptr, [&](int r, int d) { return W[d * R + r]; }, tid);
+    lrm_build<R, false, true>(s_rd_hi, s_rd_lo, [&](int r, int d) { return dS[r * D + d]; }, tid);
+    lrm_build<R, true, true>(s_dr_hi, s_dr_lo, [&](int r, int d) { return dS[r * D + d]; }, tid);
+    for (int e = tid; e < R; e += 256) z_s[e] = dS[R * D + e];
+    __syncthreads();
+
+    for (long t0 = t_lo + 32 * wave; t0 < t_hi; t0 += 128) {
+        const long t = t0 + (lane & 31);
+        const bool valid = t < t_hi;
+        const long row = bh * L + (valid ? t : t_lo);
+        int crd[3];
+        token_coords(valid ? t : 0, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
+        float2 cs[NR][8];
+        lrm_pairs_cs<NR>(a, crd, hf, cs);
+        // u = phi(k W_k), phi', fk = rho(u)
+        f32x16_t fk[NR], du[NR];
+        {
+            u32x4_t xb[8];
+            lrm_rowops(xb, a.k + row * D, valid, hf);
+#pragma unroll
+            for (int rb = 0; rb < NR; ++rb) {
+                f32x16_t p;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) p[i] = 0.f;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) p = mfma32(w_rd[(8 * rb + s) * 64 + lane], xb[s], p);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    float f0, f1, d0, d1;
+                    lrm_phi<SILU>(p[2 * j], f0, d0);
+                    lrm_phi<SILU>(p[2 * j + 1], f1, d1);
+                    du[rb][2 * j] = d0;
+                    du[rb][2 * j + 1] = d1;
+                    fk[rb][2 * j] = valid ? f0 * cs[rb][j].x - f1 * cs[rb][j].y : 0.f;
+                    fk[rb][2 * j + 1] = valid ? f0 * cs[rb][j].y + f1 * cs[rb][j].x : 0.f;
+                }
+            }
+        }
+        // dv_lr = dS^T fk
+        {
+            u32x4_t bh_[KS], bl_[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) lrm_bop(fk[ks >> 1], ks & 1, bh_[ks], bl_[ks]);
+            lrm_apply_store<KS, true>(s_dr_hi, s_dr_lo, bh_, bl_, lane, a.dv_lr + row * D, hf, valid);
+        }
+        // dpk = (rho^T(dS v) + dz) phi'
+        f32x16_t sv[NR];
+        {
+            u32x4_t vb[8];
+            lrm_rowops(vb, a.v + row * D, valid, hf);
+#pragma unroll
+            for (int rb = 0; rb < NR; ++rb) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sv[rb][i] = 0.f;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const int bi = (8 * rb + s) * 64 + lane;
+                    sv[rb] = mfma32(s_rd_hi[bi], vb[s], sv[rb]);
+                    sv[rb] = mfma32(s_rd_lo[bi], vb[s], sv[rb]);
+                }
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float4 z4 = lrm_z4(z_s, rb, j >> 1, hf);
+                const float za = (j & 1) ? z4.z : z4.x, zb = (j & 1) ? z4.w : z4.y;
+                float y0 = sv[rb][2 * j], y1 = sv[rb][2 * j + 1];
+                rot_t(y0, y1, cs[rb][j]);
+                sv[rb][2 * j] = valid ? (y0 + za) * du[rb][2 * j] : 0.f;
+                sv[rb][2 * j + 1] = valid ? (y1 + zb) * du[rb][2 * j + 1] : 0.f;
+            }
+        if (valid) lrm_store_rank<NR>(sv, a.y1h + row * R, a.y1l + row * R, hf);
+        // dk_lr = W_k dpk
+        u32x4_t bh_[KS], bl_[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) lrm_bop(sv[ks >> 1], ks & 1, bh_[ks], bl_[ks]);
+        lrm_apply_store<KS, false>(w_dr, nullptr, bh_, bl_, lane, a.dk_lr + row * D, hf, valid);
+    }
+}
+
+// out[d][r] = sum over the split's tokens t of x[t][d] y[t][r] (y = yh + yl),
+// written to part + (slice * nsplit + split) * stride + off as [128][R], or
+// as [R][128] when `trans`. Wave w owns rows d = 32w ..; 64-token stages go
+// through LDS (rows padded to 288 / (2R + 32) bytes: the transposing reads
+// of 4 rows x 16 columns per 16 lanes hit distinct banks), loaded one stage
+// ahead into registers.
+template <int R>
+__global__ __launch_bounds__(256) void k_bwd_lrm_red(const uint16_t* __restrict__ x, const uint16_t* __restrict__ yh,
+                                                     const uint16_t* __restrict__ yl, long L, int chunk, int nsplit,
+                                                     float* __restrict__ part, long stride, long off, int trans) {
+    constexpr int D = 128, NR = R / 32, XP = D + 16, YP = R + 16, YC = R / 8;
+    constexpr int NY = (2 * 64 * YC + 255) / 256;   // 16-byte pieces of y per thread
+    __shared__ __attribute__((aligned(16))) uint16_t xs[64 * XP];
+    __shared__ __attribute__((aligned(16))) uint16_t ys[2][64 * YP];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int split = blockIdx.x;
+    const long bh = blockIdx.y;
+    const long t_lo = (long)split * chunk;
+    const long t_hi = t_lo + chunk < L ? t_lo + chunk : L;
+    const uint16_t* xb = x + bh * L * D;
+    const uint16_t* yhb = yh + bh * L * R;
+    const uint16_t* ylb = yl + bh * L * R;
+    f32x16_t acc[NR];
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
+    u32x4_t rx[4], ry[NY];
+    auto load = [&](long t0) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int it = tid + 256 * m, r = it >> 4, c = it & 15;
+            const long t = t0 + r;
+            const u32x4_t w = ldg16(xb + (t < t_hi ? t : t_lo) * D + 8 * c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rx[m][i] = t < t_hi ? w[i] : 0u;
+        }
+#pragma unroll
+        for (int m = 0; m < NY; ++m) {
+            const int it = tid + 256 * m;
+            const int which = it / (64 * YC), r = (it % (64 * YC)) / YC, c = it % YC;
+            const long t = t0 + r;
+            if (it < 2 * 64 * YC) {
+                const u32x4_t w = ldg16((which ? ylb : yhb) + (t < t_hi ? t : t_lo) * R + 8 * c);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ry[m][i] = t < t_hi ? w[i] : 0u;
+            }
+        }
+    };
+    // transposing-read addresses: lane c of group g reads row 4x + c/4 (+ 16ks + 8(l/32)) at
+    // columns 16(g % 2) + 4(c % 4) .. +3 (+ 32 * column block)
+    const int g = lane >> 4, c = lane & 15, hf = lane >> 5;
+    const int xr = (8 * hf + (c >> 2)) * XP + 32 * wave + 16 * (g & 1) + 4 * (c & 3);
+    const int yr = (8 * hf + (c >> 2)) * YP + 16 * (g & 1) + 4 * (c & 3);
+    if (t_lo < t_hi) load(t_lo);
+    for (long t0 = t_lo; t0 < t_hi; t0 += 64) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int it = tid + 256 * m;
+            *reinterpret_cast<u32x4_t*>(xs + (it >> 4) * XP + 8 * (it & 15)) = rx[m];
+        }
+#pragma unroll
+        for (int m = 0; m < NY; ++m) {
+            const int it = tid + 256 * m;
+            if (it < 2 * 64 * YC) {
+                const int which = it / (64 * YC), r = (it % (64 * YC)) / YC, cc = it % YC;
+                *reinterpret_cast<u32x4_t*>(ys[which] + r * YP + 8 * cc) = ry[m];
+            }
+        }
+        __syncthreads();
+        if (t0 + 64 < t_hi) load(t0 + 64);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const u32x2_t a0 = lds_tr8(xs + xr + 16 * ks * XP), a1 = lds_tr8(xs + xr + (16 * ks + 4) * XP);
+            const u32x4_t av = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+#pragma unroll
+            for (int rb = 0; rb < NR; ++rb) {
+                const int o = 16 * ks * YP + 32 * rb;
+                const u32x2_t h0 = lds_tr8(ys[0] + yr + o), h1 = lds_tr8(ys[0] + yr + o + 4 * YP);
+                const u32x2_t l0 = lds_tr8(ys[1] + yr + o), l1 = lds_tr8(ys[1] + yr + o + 4 * YP);
+                acc[rb] = mfma32(av, u32x4_t{h0[0], h0[1], h1[0], h1[1]}, acc[rb]);
+                acc[rb] = mfma32(av, u32x4_t{l0[0], l0[1], l1[0], l1[1]}, acc[rb]);
+            }
+        }
+        __syncthreads();
+    }
+    float* dst = part + (bh * nsplit + split) * stride + off;
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int d = 32 * wave + 8 * (v >> 2) + 4 * hf + (v & 3), r = 32 * rb + (lane & 31);
+            dst[trans ? r * D + d : d * R + r] = acc[rb][v];
+        }
+}
+
 // Per-axis sums for the absolute-PE tables: workgroup (c, bh) adds dpre over
 // the tokens of slice bh whose coordinate on `axis` is c, in a fixed order
 // (thread (j, r) takes every (256/R)-th such token from j, then the j's are
@@ -1832,7 +2326,33 @@ static hipError_t bwd_lr_d(int R, bool key_side, const LrBwdArgs& a, long BH, hi
     }
 }
 
+template <int R, bool SILU>
+static hipError_t bwd_lrm(bool key_side, const LrBwdArgs& a, long BH, hipStream_t st) {
+    constexpr int D = 128;
+    const dim3 grid((unsigned)a.nsplit, (unsigned)BH);
+    if (!key_side) {
+        // per token, then the [dW_q | dS | dz | dg] partials' dW_q and dS (stored transposed)
+        const long qs = 2l * D * R + R + 4;
+        hipLaunchKernelGGL((k_bwd_lrm_q<R, SILU>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_bwd_lrm_red<R>), grid, dim3(256), 0, st, a.q, a.y1h, a.y1l, a.L, a.chunk, a.nsplit,
+                           a.part, qs, 0l, 0);
+        hipLaunchKernelGGL((k_bwd_lrm_red<R>), grid, dim3(256), 0, st, a.dout, a.y2h, a.y2l, a.L, a.chunk, a.nsplit,
+                           a.part, qs, (long)D * R, 1);
+    } else {
+        hipLaunchKernelGGL((k_bwd_lrm_k<R, SILU>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_bwd_lrm_red<R>), grid, dim3(256), 0, st, a.k, a.y1h, a.y1l, a.L, a.chunk, a.nsplit,
+                           a.part, (long)D * R, 0l, 0);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_bwd_lr(int dtype_bf16, int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st) {
+    if (lr_bwd_on_mfma(dtype_bf16, D, R, a.abspe != 0, a.token != 0)) {
+        if (!a.y1h || !a.y1l || !a.y2h || !a.y2l) return hipErrorInvalidValue;
+        if (a.g.fmap != 0)
+            return R == 32 ? bwd_lrm<32, true>(key_side, a, BH, st) : bwd_lrm<64, true>(key_side, a, BH, st);
+        return R == 32 ? bwd_lrm<32, false>(key_side, a, BH, st) : bwd_lrm<64, false>(key_side, a, BH, st);
+    }
     if (dtype_bf16)
         return D == 64 ? bwd_lr_d<64, true>(R, key_side, a, BH, st) : bwd_lr_d<128, true>(R, key_side, a, BH, st);
     return D == 64 ? bwd_lr_d<64, false>(R, key_side, a, BH, st) : bwd_lr_d<128, false>(R, key_side, a, BH, st);

@@ -163,6 +163,7 @@ struct Layout {
     size_t wqo_hi, wqo_lo, wko_hi, wko_lo, eo;
     // backward
     size_t lse, delta, dqlr, dklr, dvlr, lrpart, dsz, bits, cnt, off, list, order, dpre, epart, dosp, gpart, dqt, qtt;
+    size_t lry;   // MFMA low-rank backward: 4 bf16 [BH][L][R] per-token rank vectors
     bool tiled;
 };
 
@@ -215,6 +216,7 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         int chunk, nsplit;
         lr_bwd_split(d, &chunk, &nsplit);
         w.lrpart = take(4ul * d.BH * nsplit * (2ul * d.D * R + R + 4));
+        if (lr_bwd_on_mfma(d.bf16, d.D, R, abspe, token)) w.lry = take(8ul * d.BH * d.L * R);
         w.dsz = take(4ul * d.BH * ((size_t)R * d.D + R));
         if (abspe) {
             // per-token gradient of x W + E and the per-slice axis sums of it
@@ -755,6 +757,13 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     la.wg = lowrank->Wg; la.bg = lowrank->bg; la.o_sp = o_sparse;
     la.dosp = token ? at<void>(ws, w.dosp) : nullptr;
     la.gpart = token ? at<float>(ws, w.gpart) : nullptr;
+    if (lr_bwd_on_mfma(d.bf16, d.D, R, abspe, token)) {
+        const size_t n = (size_t)d.BH * d.L * R;
+        la.y1h = at<uint16_t>(ws, w.lry);
+        la.y1l = la.y1h + n;
+        la.y2h = la.y1l + n;
+        la.y2l = la.y2h + n;
+    }
     const long qstride = 2l * d.D * R + R + 4;   // [dW_q | dS | dz | dg | pad]
     SLR_TRY(launch_bwd_lr(d.bf16, (int)d.D, R, false, la, d.BH, s));
     // [dW_q | dS | dz | dg] partials -> dS, dz per slice; dW_q, dg per head

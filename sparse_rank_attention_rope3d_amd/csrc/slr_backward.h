@@ -69,7 +69,17 @@ struct LrBwdArgs {
     const void* o_sp;                   // [BH][L][D] the forward's O_sparse (layer dtype)
     void* dosp;                         // [BH][L][D] (layer dtype): the sparse branch's upstream gradient
     float* gpart;                       // [BH][nsplit][D + 4]: dW_g, db_g partials
+    // MFMA path (lr_bwd_on_mfma): per-token rank vectors as bf16 hi + lo pairs, [BH][L][R] each:
+    // y1 = dpq (query side) or dpk (key side), y2 = fq g / n (query side)
+    uint16_t *y1h, *y1l, *y2h, *y2l;
 };
+
+// The low-rank backward runs on MFMA for bf16 layers with D = 128, rank 32
+// or 64, rotary low-rank features and the per-head gate; the absolute-PE
+// variant, the token gate, fp32 layers and other shapes take the VALU kernels.
+inline bool lr_bwd_on_mfma(int dtype_bf16, long D, int R, bool abspe, bool token) {
+    return dtype_bf16 && D == 128 && (R == 32 || R == 64) && !abspe && !token;
+}
 
 hipError_t launch_bwd_lr(int dtype_bf16, int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st);
 // out[o][e] = sum over (b < nb, split < nsplit) of part[((b*H + h)*nsplit + split)*stride + off + e]:

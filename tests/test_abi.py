@@ -234,13 +234,16 @@ def test_backward_absolute_pe_needs_the_table_gradients():
 def test_backward_token_gate_outputs():
     """The token gate's backward returns dW_g, db_g (required) instead of
     dgate (ignored), and needs room for the sparse branch's upstream
-    gradient."""
+    gradient (bf16 [B,H,L,D]); the per-head gate's bf16 rank-32 layout
+    instead holds the MFMA low-rank path's four bf16 [B,H,L,R] per-token
+    rank vectors, which the token gate (VALU path) does without."""
     shape, rope, sparse, lr = _cfgs()
     n_head = B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lr)
     lr.gate_mode, lr.gate, lr.Wg, lr.bg = B.SLR_GATE_TOKEN, None, FAKE, FAKE
     n_tok = B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lr)
     layer = synth.wan13b()
-    assert n_tok - n_head >= 2 * layer.B * layer.H * layer.L * layer.D
+    bhl = layer.B * layer.H * layer.L
+    assert n_tok - (n_head - 4 * 2 * bhl * layer.rank) >= 2 * bhl * layer.D
     assert _bwd(shape, rope, sparse, lr, dg=None) == B.SLR_EWORKSPACE
     assert _bwd(shape, rope, sparse, lr, dwg=None) == B.SLR_EINVAL
     assert _bwd(shape, rope, sparse, lr, dbg=None) == B.SLR_EINVAL
