@@ -1941,6 +1941,8 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
     float accg = 0.f;
 
     for (long t0 = t_lo + 32 * wave; t0 < t_hi; t0 += 128) {
+        // the operand copies are re-read from LDS each step rather than held in registers
+        asm volatile("" ::: "memory");
         const long t = t0 + (lane & 31);
         const bool valid = t < t_hi;
         const long row = bh * L + (valid ? t : t_lo);
@@ -2081,6 +2083,8 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
     __syncthreads();
 
     for (long t0 = t_lo + 32 * wave; t0 < t_hi; t0 += 128) {
+        // the operand copies are re-read from LDS each step rather than held in registers
+        asm volatile("" ::: "memory");
         const long t = t0 + (lane & 31);
         const bool valid = t < t_hi;
         const long row = bh * L + (valid ? t : t_lo);
