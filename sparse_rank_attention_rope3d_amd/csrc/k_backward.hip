@@ -1760,7 +1760,9 @@ __global__ __launch_bounds__(256) void k_bwd_lr_k(LrBwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Low-rank branch on MFMA (lr_bwd_on_mfma: bf16, D = 128, R = 32 or 64,
-// rotary features, per-head gate). Tokens sit on the MFMA column axis: lane
+// per-head gate; rotary or absolute-PE features: with absolute PE,
+// p = x W + E_t[t] + E_h[h] + E_w[w], rho is the identity, and each token's
+// dp is also stored (dpre) for the tables' sums). Tokens sit on the MFMA column axis: lane
 // l owns token l % 32 of its wave's 32, and a product over d leaves rank
 // r = 32rb + 8(v/4) + 4(l/32) + v%4 in register v of block rb (the slot16
 // order), which is the B operand layout of a product over r, and keeps each
@@ -1869,9 +1871,41 @@ __device__ __forceinline__ void lrm_phi(float x, float& f, float& df) {
     }
 }
 
+// fp32 rank vector in accumulator layout -> dst [R] (ADD: dst += it)
+template <int NR, bool ADD>
+__device__ __forceinline__ void lrm_store_dpre(const f32x16_t* y, float* dst, int hf) {
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            float4* p = reinterpret_cast<float4*>(dst + 32 * rb + 8 * g4 + 4 * hf);
+            float4 x = make_float4(y[rb][4 * g4], y[rb][4 * g4 + 1], y[rb][4 * g4 + 2], y[rb][4 * g4 + 3]);
+            if constexpr (ADD) {
+                const float4 o = *p;
+                x.x += o.x; x.y += o.y; x.z += o.z; x.w += o.w;
+            }
+            *p = x;
+        }
+}
+
 // z (or dz) at the ranks register v of block rb holds: 4 consecutive floats per group v / 4
 __device__ __forceinline__ float4 lrm_z4(const float* z_s, int rb, int g4, int hf) {
     return *reinterpret_cast<const float4*>(z_s + 32 * rb + 8 * g4 + 4 * hf);
+}
+
+// Absolute PE: E_t[t] + E_h[h] + E_w[w] at the ranks register v of block rb holds (the tables
+// are only 4-byte aligned)
+template <int NR>
+__device__ __forceinline__ void lrm_add_e(const LrBwdArgs& a, const int* crd, int hf, f32x16_t& p, int rb) {
+    constexpr int R = NR * 32;
+    const float* et = a.Et + crd[0] * R;
+    const float* eh = a.Eh + crd[1] * R;
+    const float* ew = a.Ew + crd[2] * R;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int r = 32 * rb + 8 * (v >> 2) + 4 * hf + (v & 3);
+        p[v] += et[r] + eh[r] + ew[r];
+    }
 }
 
 // (cos, sin) of the rank pairs (v, v + 1), v even, of block rb at token coordinates crd
@@ -1912,7 +1946,7 @@ __device__ __forceinline__ void lrm_apply_store(const u32x4_t* ahi, const u32x4_
     }
 }
 
-template <int R, bool SILU>
+template <int R, bool SILU, bool ABSPE>
 __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
     constexpr int D = 128, NR = R / 32, NB = R / 4, KS = R / 16;
     __shared__ u32x4_t w_rd[NB * 64], w_dr[NB * 64], s_hi[NB * 64], s_lo[NB * 64];
@@ -1961,6 +1995,7 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
                 for (int i = 0; i < 16; ++i) p[i] = 0.f;
 #pragma unroll
                 for (int s = 0; s < 8; ++s) p = mfma32(w_rd[(8 * rb + s) * 64 + lane], xb[s], p);
+                if constexpr (ABSPE) lrm_add_e<NR>(a, crd, hf, p, rb);
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     float fv, dv;
@@ -1993,9 +2028,9 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
                 }
             }
         }
-        // fq = rho(f) and dout . O_un = fq . sg
+        // fq = rho(f) (f itself for absolute PE) and dout . O_un = fq . sg
         float2 cs[NR][8];
-        lrm_pairs_cs<NR>(a, crd, hf, cs);
+        if constexpr (!ABSPE) lrm_pairs_cs<NR>(a, crd, hf, cs);
         f32x16_t fq[NR];
         float dsum = 0.f;
 #pragma unroll
@@ -2003,8 +2038,8 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float f0 = f[rb][2 * j], f1 = f[rb][2 * j + 1];
-                fq[rb][2 * j] = f0 * cs[rb][j].x - f1 * cs[rb][j].y;
-                fq[rb][2 * j + 1] = f0 * cs[rb][j].y + f1 * cs[rb][j].x;
+                fq[rb][2 * j] = ABSPE ? f0 : f0 * cs[rb][j].x - f1 * cs[rb][j].y;
+                fq[rb][2 * j + 1] = ABSPE ? f1 : f0 * cs[rb][j].y + f1 * cs[rb][j].x;
                 dsum += fq[rb][2 * j] * sg[rb][2 * j] + fq[rb][2 * j + 1] * sg[rb][2 * j + 1];
             }
         const float n = SILU ? (float)L : sum_xor32(nz) + a.eps;
@@ -2026,7 +2061,7 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
                 const float4 z4 = lrm_z4(z_s, rb, j >> 1, hf);
                 const float za = (j & 1) ? z4.z : z4.x, zb = (j & 1) ? z4.w : z4.y;
                 float y0 = sg[rb][2 * j] * sc, y1 = sg[rb][2 * j + 1] * sc;
-                rot_t(y0, y1, cs[rb][j]);
+                if constexpr (!ABSPE) rot_t(y0, y1, cs[rb][j]);
                 sg[rb][2 * j] = (y0 + dn * za) * df[rb][2 * j];
                 sg[rb][2 * j + 1] = (y1 + dn * zb) * df[rb][2 * j + 1];
             }
@@ -2034,6 +2069,8 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
         if (valid) {
             lrm_store_rank<NR>(sg, a.y1h + row * R, a.y1l + row * R, hf);
             lrm_store_rank<NR>(fq, a.y2h + row * R, a.y2l + row * R, hf);
+            // absolute PE: each token's gradient of q W_q + E (the query side's share of the E sums)
+            if constexpr (ABSPE) lrm_store_dpre<NR, false>(sg, a.dpre + row * R, hf);
         }
         // dq_lr = W_q dpq
         u32x4_t bh_[KS], bl_[KS];
@@ -2060,7 +2097,7 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
     if (tid <= R) part[2 * D * R + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
 }
 
-template <int R, bool SILU>
+template <int R, bool SILU, bool ABSPE>
 __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
     constexpr int D = 128, NR = R / 32, NB = R / 4, KS = R / 16;
     __shared__ u32x4_t w_rd[NB * 64], w_dr[NB * 64], s_rd_hi[NB * 64], s_rd_lo[NB * 64], s_dr_hi[NB * 64],
@@ -2091,8 +2128,8 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
         int crd[3];
         token_coords(valid ? t : 0, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
         float2 cs[NR][8];
-        lrm_pairs_cs<NR>(a, crd, hf, cs);
-        // u = phi(k W_k), phi', fk = rho(u)
+        if constexpr (!ABSPE) lrm_pairs_cs<NR>(a, crd, hf, cs);
+        // u = phi(k W_k), phi', fk = rho(u) (u itself for absolute PE)
         f32x16_t fk[NR], du[NR];
         {
             u32x4_t xb[8];
@@ -2104,6 +2141,7 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
                 for (int i = 0; i < 16; ++i) p[i] = 0.f;
 #pragma unroll
                 for (int s = 0; s < 8; ++s) p = mfma32(w_rd[(8 * rb + s) * 64 + lane], xb[s], p);
+                if constexpr (ABSPE) lrm_add_e<NR>(a, crd, hf, p, rb);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     float f0, f1, d0, d1;
@@ -2111,8 +2149,8 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
                     lrm_phi<SILU>(p[2 * j + 1], f1, d1);
                     du[rb][2 * j] = d0;
                     du[rb][2 * j + 1] = d1;
-                    fk[rb][2 * j] = valid ? f0 * cs[rb][j].x - f1 * cs[rb][j].y : 0.f;
-                    fk[rb][2 * j + 1] = valid ? f0 * cs[rb][j].y + f1 * cs[rb][j].x : 0.f;
+                    fk[rb][2 * j] = !valid ? 0.f : ABSPE ? f0 : f0 * cs[rb][j].x - f1 * cs[rb][j].y;
+                    fk[rb][2 * j + 1] = !valid ? 0.f : ABSPE ? f1 : f0 * cs[rb][j].y + f1 * cs[rb][j].x;
                 }
             }
         }
@@ -2147,11 +2185,15 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
                 const float4 z4 = lrm_z4(z_s, rb, j >> 1, hf);
                 const float za = (j & 1) ? z4.z : z4.x, zb = (j & 1) ? z4.w : z4.y;
                 float y0 = sv[rb][2 * j], y1 = sv[rb][2 * j + 1];
-                rot_t(y0, y1, cs[rb][j]);
+                if constexpr (!ABSPE) rot_t(y0, y1, cs[rb][j]);
                 sv[rb][2 * j] = valid ? (y0 + za) * du[rb][2 * j] : 0.f;
                 sv[rb][2 * j + 1] = valid ? (y1 + zb) * du[rb][2 * j + 1] : 0.f;
             }
-        if (valid) lrm_store_rank<NR>(sv, a.y1h + row * R, a.y1l + row * R, hf);
+        if (valid) {
+            lrm_store_rank<NR>(sv, a.y1h + row * R, a.y1l + row * R, hf);
+            // absolute PE: adds the key side's share (the query side wrote its own first)
+            if constexpr (ABSPE) lrm_store_dpre<NR, true>(sv, a.dpre + row * R, hf);
+        }
         // dk_lr = W_k dpk
         u32x4_t bh_[KS], bl_[KS];
 #pragma unroll
@@ -2330,20 +2372,20 @@ static hipError_t bwd_lr_d(int R, bool key_side, const LrBwdArgs& a, long BH, hi
     }
 }
 
-template <int R, bool SILU>
+template <int R, bool SILU, bool ABSPE>
 static hipError_t bwd_lrm(bool key_side, const LrBwdArgs& a, long BH, hipStream_t st) {
     constexpr int D = 128;
     const dim3 grid((unsigned)a.nsplit, (unsigned)BH);
     if (!key_side) {
         // per token, then the [dW_q | dS | dz | dg] partials' dW_q and dS (stored transposed)
         const long qs = 2l * D * R + R + 4;
-        hipLaunchKernelGGL((k_bwd_lrm_q<R, SILU>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_bwd_lrm_q<R, SILU, ABSPE>), grid, dim3(256), 0, st, a);
         hipLaunchKernelGGL((k_bwd_lrm_red<R>), grid, dim3(256), 0, st, a.q, a.y1h, a.y1l, a.L, a.chunk, a.nsplit,
                            a.part, qs, 0l, 0);
         hipLaunchKernelGGL((k_bwd_lrm_red<R>), grid, dim3(256), 0, st, a.dout, a.y2h, a.y2l, a.L, a.chunk, a.nsplit,
                            a.part, qs, (long)D * R, 1);
     } else {
-        hipLaunchKernelGGL((k_bwd_lrm_k<R, SILU>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_bwd_lrm_k<R, SILU, ABSPE>), grid, dim3(256), 0, st, a);
         hipLaunchKernelGGL((k_bwd_lrm_red<R>), grid, dim3(256), 0, st, a.k, a.y1h, a.y1l, a.L, a.chunk, a.nsplit,
                            a.part, (long)D * R, 0l, 0);
     }
@@ -2353,9 +2395,14 @@ static hipError_t bwd_lrm(bool key_side, const LrBwdArgs& a, long BH, hipStream_
 hipError_t launch_bwd_lr(int dtype_bf16, int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st) {
     if (lr_bwd_on_mfma(dtype_bf16, D, R, a.abspe != 0, a.token != 0)) {
         if (!a.y1h || !a.y1l || !a.y2h || !a.y2l) return hipErrorInvalidValue;
-        if (a.g.fmap != 0)
-            return R == 32 ? bwd_lrm<32, true>(key_side, a, BH, st) : bwd_lrm<64, true>(key_side, a, BH, st);
-        return R == 32 ? bwd_lrm<32, false>(key_side, a, BH, st) : bwd_lrm<64, false>(key_side, a, BH, st);
+        const bool silu = a.g.fmap != 0;
+        if (a.abspe) {
+            if (!a.dpre) return hipErrorInvalidValue;
+            if (silu) return R == 32 ? bwd_lrm<32, true, true>(key_side, a, BH, st) : bwd_lrm<64, true, true>(key_side, a, BH, st);
+            return R == 32 ? bwd_lrm<32, false, true>(key_side, a, BH, st) : bwd_lrm<64, false, true>(key_side, a, BH, st);
+        }
+        if (silu) return R == 32 ? bwd_lrm<32, true, false>(key_side, a, BH, st) : bwd_lrm<64, true, false>(key_side, a, BH, st);
+        return R == 32 ? bwd_lrm<32, false, false>(key_side, a, BH, st) : bwd_lrm<64, false, false>(key_side, a, BH, st);
     }
     if (dtype_bf16)
         return D == 64 ? bwd_lr_d<64, true>(R, key_side, a, BH, st) : bwd_lr_d<128, true>(R, key_side, a, BH, st);

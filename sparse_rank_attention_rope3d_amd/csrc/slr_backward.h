@@ -75,10 +75,11 @@ struct LrBwdArgs {
 };
 
 // The low-rank backward runs on MFMA for bf16 layers with D = 128, rank 32
-// or 64, rotary low-rank features and the per-head gate; the absolute-PE
-// variant, the token gate, fp32 layers and other shapes take the VALU kernels.
+// or 64 and the per-head gate (rotary or absolute-PE features); the token
+// gate, fp32 layers and other shapes take the VALU kernels.
 inline bool lr_bwd_on_mfma(int dtype_bf16, long D, int R, bool abspe, bool token) {
-    return dtype_bf16 && D == 128 && (R == 32 || R == 64) && !abspe && !token;
+    (void)abspe;
+    return dtype_bf16 && D == 128 && (R == 32 || R == 64) && !token;
 }
 
 hipError_t launch_bwd_lr(int dtype_bf16, int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st);

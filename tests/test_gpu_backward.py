@@ -166,6 +166,8 @@ SMALL = [
     ("absolute PE", dict(B=2, H=2, T=4, Hg=9, Wg=13, keep=3, lr_mode="abspe", lr_pairs=(0, 0, 0))),
     ("absolute PE silu D64 block32", dict(B=1, H=2, D=64, pairs=(12, 10, 10), T=3, Hg=10, Wg=11, block=32, keep=4,
                                           rank=16, lr_mode="abspe", lr_pairs=(0, 0, 0), fmap="silu")),
+    ("absolute PE silu rank 64", dict(B=1, H=2, T=3, Hg=10, Wg=11, keep=4, rank=64, lr_mode="abspe",
+                                      lr_pairs=(0, 0, 0), fmap="silu")),
 ]
 
 
