@@ -21,8 +21,10 @@
 // (each pair turned by the opposite angle) in the epilogues, where the
 // low-rank parts are added.
 //
-// Low-rank branch (RoLA §4.1-4.3, App. A): fp32 VALU kernels over token
-// tiles, split along L with fixed-order reductions of the partial sums.
+// Low-rank branch (RoLA §4.1-4.3, App. A): per-token kernels and sums over
+// tokens, split along L with fixed-order reductions of the partial sums; on
+// bf16 MFMA for the per-head gate at rank 32 or 64 with D = 128, fp32 VALU
+// kernels for the other settings.
 #include "slr_common.h"
 #include "slr_launch.h"
 #include "slr_backward.h"

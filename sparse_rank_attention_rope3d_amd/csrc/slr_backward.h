@@ -94,7 +94,7 @@ hipError_t launch_bwd_e_sum(const float* dpre, long BH, long L, int T, int Hg, i
 // Inverse of the kept-block lists, deterministic: bits [BH][nblk][ceil(nblk/32)] scratch.
 hipError_t launch_bwd_inverse(const int32_t* idx, long BH, int nblk, int keep, uint32_t* bits, int32_t* cnt,
                               int32_t* off, int32_t* list, int32_t* order, hipStream_t st);
-// [K | V | K^T] operand-order tiles of every key block for the streaming dQ kernel, from the
+// [K | V] operand-order tiles of every key block for the streaming dQ kernel, from the
 // zero-padded rotated k copy kr [BH][nblk*64][128] and v [BH][L][128] (bf16); grid (nblk, BH).
 hipError_t launch_bwd_dq_tiles(const uint16_t* kr, const uint16_t* v, long BH, long L, int nblk, uint16_t* tiles,
                                hipStream_t st);
