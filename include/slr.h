@@ -264,7 +264,8 @@ int slr_dense_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, co
  * dEw [Wg,r] fp32 (overwritten; sums over batch, heads and tokens; required,
  * 4-byte aligned); for SLR_LR_ROPE_OUTSIDE they are ignored (may be NULL).
  * Every setting of the forward is covered (either gate, either low-rank
- * variant, either feature map, bf16 or fp32). Workspace:
+ * variant, bf16 or fp32) with the elu + 1 and SiLU feature maps; FAVOR+
+ * layers return SLR_EUNSUPPORTED. Workspace:
  * slr_workspace_bytes(SLR_OP_ATTENTION_BWD, ...). Results are bitwise
  * reproducible (fixed reduction orders, no floating-point atomics).
  */
