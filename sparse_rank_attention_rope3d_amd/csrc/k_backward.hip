@@ -1839,14 +1839,15 @@ __device__ __forceinline__ void lrm_rowops(u32x4_t* b, const uint16_t* row, bool
     }
 }
 
-// Stores of a rank vector in accumulator layout to y [t][R] as bf16 hi + lo
+// Stores of a rank vector in accumulator layout to y [t][rv] as bf16 hi + lo (ranks < rv)
 template <int NR>
-__device__ __forceinline__ void lrm_store_rank(const f32x16_t* y, uint16_t* dh, uint16_t* dl, int hf) {
+__device__ __forceinline__ void lrm_store_rank(const f32x16_t* y, uint16_t* dh, uint16_t* dl, int hf, int rv) {
 #pragma unroll
     for (int rb = 0; rb < NR; ++rb)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             const int r0 = 32 * rb + 8 * g4 + 4 * hf;
+            if (r0 >= rv) continue;
             uint32_t h[2], l[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -1873,13 +1874,14 @@ __device__ __forceinline__ void lrm_phi(float x, float& f, float& df) {
     }
 }
 
-// fp32 rank vector in accumulator layout -> dst [R] (ADD: dst += it)
+// fp32 rank vector in accumulator layout -> dst [rv] (ADD: dst += it; ranks < rv)
 template <int NR, bool ADD>
-__device__ __forceinline__ void lrm_store_dpre(const f32x16_t* y, float* dst, int hf) {
+__device__ __forceinline__ void lrm_store_dpre(const f32x16_t* y, float* dst, int hf, int rv) {
 #pragma unroll
     for (int rb = 0; rb < NR; ++rb)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
+            if (32 * rb + 8 * g4 + 4 * hf >= rv) continue;
             float4* p = reinterpret_cast<float4*>(dst + 32 * rb + 8 * g4 + 4 * hf);
             float4 x = make_float4(y[rb][4 * g4], y[rb][4 * g4 + 1], y[rb][4 * g4 + 2], y[rb][4 * g4 + 3]);
             if constexpr (ADD) {
@@ -1895,29 +1897,30 @@ __device__ __forceinline__ float4 lrm_z4(const float* z_s, int rb, int g4, int h
     return *reinterpret_cast<const float4*>(z_s + 32 * rb + 8 * g4 + 4 * hf);
 }
 
-// Absolute PE: E_t[t] + E_h[h] + E_w[w] at the ranks register v of block rb holds (the tables
-// are only 4-byte aligned)
-template <int NR>
-__device__ __forceinline__ void lrm_add_e(const LrBwdArgs& a, const int* crd, int hf, f32x16_t& p, int rb) {
-    constexpr int R = NR * 32;
-    const float* et = a.Et + crd[0] * R;
-    const float* eh = a.Eh + crd[1] * R;
-    const float* ew = a.Ew + crd[2] * R;
+// Absolute PE: E_t[t] + E_h[h] + E_w[w] ([.][rv] tables, only 4-byte aligned) at the ranks
+// register v of block rb holds (ranks < rv)
+__device__ __forceinline__ void lrm_add_e(const LrBwdArgs& a, const int* crd, int hf, f32x16_t& p, int rb, int rv) {
+    const float* et = a.Et + crd[0] * rv;
+    const float* eh = a.Eh + crd[1] * rv;
+    const float* ew = a.Ew + crd[2] * rv;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         const int r = 32 * rb + 8 * (v >> 2) + 4 * hf + (v & 3);
-        p[v] += et[r] + eh[r] + ew[r];
+        if (r < rv) p[v] += et[r] + eh[r] + ew[r];
     }
 }
 
 // (cos, sin) of the rank pairs (v, v + 1), v even, of block rb at token coordinates crd
+// (the identity for the padding pairs past rv / 2)
 template <int NR>
-__device__ __forceinline__ void lrm_pairs_cs(const LrBwdArgs& a, const int* crd, int hf, float2 (*cs)[8]) {
+__device__ __forceinline__ void lrm_pairs_cs(const LrBwdArgs& a, const int* crd, int hf, float2 (*cs)[8], int rv) {
 #pragma unroll
     for (int rb = 0; rb < NR; ++rb)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            cs[rb][j] = lowrank_cs(a.tab, a.g, 16 * rb + 4 * (j >> 1) + 2 * hf + (j & 1), crd);
+        for (int j = 0; j < 8; ++j) {
+            const int pr = 16 * rb + 4 * (j >> 1) + 2 * hf + (j & 1);
+            cs[rb][j] = 2 * pr < rv ? lowrank_cs(a.tab, a.g, pr, crd) : make_float2(1.f, 0.f);
+        }
 }
 
 // y = W dpq (or dS^T fk ...): the 4 column blocks of a [128] x [R] product over r, one at a
@@ -1962,12 +1965,14 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
     const long t_lo = (long)split * a.chunk;
     const long t_hi = t_lo + a.chunk < L ? t_lo + a.chunk : L;
     const float gh = a.gate[head];
-    const float* W = a.Wq + (long)head * D * R;
-    const float* S = a.S + bh * R * D;
-    lrm_build<R, false, false>(w_rd, nullptr, [&](int r, int d) { return W[d * R + r]; }, tid);
-    lrm_build<R, true, false>(w_dr, nullptr, [&](int r, int d) { return W[d * R + r]; }, tid);
-    lrm_build<R, false, true>(s_hi, s_lo, [&](int r, int d) { return S[r * D + d]; }, tid);
-    for (int e = tid; e < R; e += 256) z_s[e] = a.z[bh * R + e];
+    // rv = the layer's rank (8, 16, 32 or 64); ranks rv .. R - 1 are padding with zero weights
+    const int rv = a.g.R;
+    const float* W = a.Wq + (long)head * D * rv;
+    const float* S = a.S + bh * rv * D;
+    lrm_build<R, false, false>(w_rd, nullptr, [&](int r, int d) { return r < rv ? W[d * rv + r] : 0.f; }, tid);
+    lrm_build<R, true, false>(w_dr, nullptr, [&](int r, int d) { return r < rv ? W[d * rv + r] : 0.f; }, tid);
+    lrm_build<R, false, true>(s_hi, s_lo, [&](int r, int d) { return r < rv ? S[r * D + d] : 0.f; }, tid);
+    for (int e = tid; e < R; e += 256) z_s[e] = e < rv ? a.z[bh * rv + e] : 0.f;
     __syncthreads();
     float accz[NR][16];
 #pragma unroll
@@ -1997,13 +2002,14 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
                 for (int i = 0; i < 16; ++i) p[i] = 0.f;
 #pragma unroll
                 for (int s = 0; s < 8; ++s) p = mfma32(w_rd[(8 * rb + s) * 64 + lane], xb[s], p);
-                if constexpr (ABSPE) lrm_add_e<NR>(a, crd, hf, p, rb);
+                if constexpr (ABSPE) lrm_add_e(a, crd, hf, p, rb, rv);
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     float fv, dv;
                     lrm_phi<SILU>(p[v], fv, dv);
-                    f[rb][v] = fv;
-                    df[rb][v] = dv;
+                    const bool rok = 32 * rb + 8 * (v >> 2) + 4 * hf + (v & 3) < rv;
+                    f[rb][v] = rok ? fv : 0.f;
+                    df[rb][v] = rok ? dv : 0.f;
                 }
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
@@ -2032,7 +2038,7 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
         }
         // fq = rho(f) (f itself for absolute PE) and dout . O_un = fq . sg
         float2 cs[NR][8];
-        if constexpr (!ABSPE) lrm_pairs_cs<NR>(a, crd, hf, cs);
+        if constexpr (!ABSPE) lrm_pairs_cs<NR>(a, crd, hf, cs, rv);
         f32x16_t fq[NR];
         float dsum = 0.f;
 #pragma unroll
@@ -2069,10 +2075,10 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
             }
         }
         if (valid) {
-            lrm_store_rank<NR>(sg, a.y1h + row * R, a.y1l + row * R, hf);
-            lrm_store_rank<NR>(fq, a.y2h + row * R, a.y2l + row * R, hf);
+            lrm_store_rank<NR>(sg, a.y1h + row * rv, a.y1l + row * rv, hf, rv);
+            lrm_store_rank<NR>(fq, a.y2h + row * rv, a.y2l + row * rv, hf, rv);
             // absolute PE: each token's gradient of q W_q + E (the query side's share of the E sums)
-            if constexpr (ABSPE) lrm_store_dpre<NR, false>(sg, a.dpre + row * R, hf);
+            if constexpr (ABSPE) lrm_store_dpre<NR, false>(sg, a.dpre + row * rv, hf, rv);
         }
         // dq_lr = W_q dpq
         u32x4_t bh_[KS], bl_[KS];
@@ -2095,8 +2101,12 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
     for (int o = 1; o < 64; o <<= 1) g += __shfl_xor(g, o, 64);
     if (lane == 0) red[wave][R] = g;
     __syncthreads();
-    float* part = a.part + (bh * a.nsplit + split) * (long)(2 * D * R + R + 4);
-    if (tid <= R) part[2 * D * R + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    // [dW_q | dS | dz | dg | pad] partials of rank rv: dz (rv), then dg
+    float* part = a.part + (bh * a.nsplit + split) * (long)(2 * D * rv + rv + 4);
+    if (tid <= rv) {
+        const int j = tid < rv ? tid : R;
+        part[2 * D * rv + tid] = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
+    }
 }
 
 template <int R, bool SILU, bool ABSPE>
@@ -2112,13 +2122,15 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
     const long L = a.L;
     const long t_lo = (long)split * a.chunk;
     const long t_hi = t_lo + a.chunk < L ? t_lo + a.chunk : L;
-    const float* W = a.Wk + (long)head * D * R;
-    const float* dS = a.dSz + bh * (long)(R * D + R);
-    lrm_build<R, false, false>(w_rd, nullptr, [&](int r, int d) { return W[d * R + r]; }, tid);
-    lrm_build<R, true, false>(w_dr, nullptr, [&](int r, int d) { return W[d * R + r]; }, tid);
-    lrm_build<R, false, true>(s_rd_hi, s_rd_lo, [&](int r, int d) { return dS[r * D + d]; }, tid);
-    lrm_build<R, true, true>(s_dr_hi, s_dr_lo, [&](int r, int d) { return dS[r * D + d]; }, tid);
-    for (int e = tid; e < R; e += 256) z_s[e] = dS[R * D + e];
+    // rv = the layer's rank (8, 16, 32 or 64); ranks rv .. R - 1 are padding with zero weights
+    const int rv = a.g.R;
+    const float* W = a.Wk + (long)head * D * rv;
+    const float* dS = a.dSz + bh * (long)(rv * D + rv);
+    lrm_build<R, false, false>(w_rd, nullptr, [&](int r, int d) { return r < rv ? W[d * rv + r] : 0.f; }, tid);
+    lrm_build<R, true, false>(w_dr, nullptr, [&](int r, int d) { return r < rv ? W[d * rv + r] : 0.f; }, tid);
+    lrm_build<R, false, true>(s_rd_hi, s_rd_lo, [&](int r, int d) { return r < rv ? dS[r * D + d] : 0.f; }, tid);
+    lrm_build<R, true, true>(s_dr_hi, s_dr_lo, [&](int r, int d) { return r < rv ? dS[r * D + d] : 0.f; }, tid);
+    for (int e = tid; e < R; e += 256) z_s[e] = e < rv ? dS[rv * D + e] : 0.f;
     __syncthreads();
 
     for (long t0 = t_lo + 32 * wave; t0 < t_hi; t0 += 128) {
@@ -2130,8 +2142,8 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
         int crd[3];
         token_coords(valid ? t : 0, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
         float2 cs[NR][8];
-        if constexpr (!ABSPE) lrm_pairs_cs<NR>(a, crd, hf, cs);
-        // u = phi(k W_k), phi', fk = rho(u) (u itself for absolute PE)
+        if constexpr (!ABSPE) lrm_pairs_cs<NR>(a, crd, hf, cs, rv);
+        // u = phi(k W_k), phi', fk = rho(u) (u itself for absolute PE); zero past rank rv
         f32x16_t fk[NR], du[NR];
         {
             u32x4_t xb[8];
@@ -2143,12 +2155,14 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
                 for (int i = 0; i < 16; ++i) p[i] = 0.f;
 #pragma unroll
                 for (int s = 0; s < 8; ++s) p = mfma32(w_rd[(8 * rb + s) * 64 + lane], xb[s], p);
-                if constexpr (ABSPE) lrm_add_e<NR>(a, crd, hf, p, rb);
+                if constexpr (ABSPE) lrm_add_e(a, crd, hf, p, rb, rv);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     float f0, f1, d0, d1;
                     lrm_phi<SILU>(p[2 * j], f0, d0);
                     lrm_phi<SILU>(p[2 * j + 1], f1, d1);
+                    // ranks 2j, 2j + 1 of this lane's group: both valid or both padding (rv % 8 == 0)
+                    if (32 * rb + 8 * (j >> 1) + 4 * hf + 2 * (j & 1) >= rv) f0 = f1 = d0 = d1 = 0.f;
                     du[rb][2 * j] = d0;
                     du[rb][2 * j + 1] = d1;
                     fk[rb][2 * j] = !valid ? 0.f : ABSPE ? f0 : f0 * cs[rb][j].x - f1 * cs[rb][j].y;
@@ -2192,9 +2206,9 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
                 sv[rb][2 * j + 1] = valid ? (y1 + zb) * du[rb][2 * j + 1] : 0.f;
             }
         if (valid) {
-            lrm_store_rank<NR>(sv, a.y1h + row * R, a.y1l + row * R, hf);
+            lrm_store_rank<NR>(sv, a.y1h + row * rv, a.y1l + row * rv, hf, rv);
             // absolute PE: adds the key side's share (the query side wrote its own first)
-            if constexpr (ABSPE) lrm_store_dpre<NR, true>(sv, a.dpre + row * R, hf);
+            if constexpr (ABSPE) lrm_store_dpre<NR, true>(sv, a.dpre + row * rv, hf, rv);
         }
         // dk_lr = W_k dpk
         u32x4_t bh_[KS], bl_[KS];
@@ -2204,16 +2218,18 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
     }
 }
 
-// out[d][r] = sum over the split's tokens t of x[t][d] y[t][r] (y = yh + yl),
-// written to part + (slice * nsplit + split) * stride + off as [128][R], or
-// as [R][128] when `trans`. Wave w owns rows d = 32w ..; 64-token stages go
+// out[d][r] = sum over the split's tokens t of x[t][d] y[t][r] (y = yh + yl,
+// [t][rv], rv <= R: the columns past rv are zero in LDS), written to
+// part + (slice * nsplit + split) * stride + off as [128][rv], or as
+// [rv][128] when `trans`. Wave w owns rows d = 32w ..; 64-token stages go
 // through LDS (rows padded to 288 / (2R + 32) bytes: the transposing reads
 // of 4 rows x 16 columns per 16 lanes hit distinct banks), loaded one stage
 // ahead into registers.
 template <int R>
 __global__ __launch_bounds__(256) void k_bwd_lrm_red(const uint16_t* __restrict__ x, const uint16_t* __restrict__ yh,
-                                                     const uint16_t* __restrict__ yl, long L, int chunk, int nsplit,
-                                                     float* __restrict__ part, long stride, long off, int trans) {
+                                                     const uint16_t* __restrict__ yl, int rv, long L, int chunk,
+                                                     int nsplit, float* __restrict__ part, long stride, long off,
+                                                     int trans) {
     constexpr int D = 128, NR = R / 32, XP = D + 16, YP = R + 16, YC = R / 8;
     constexpr int NY = (2 * 64 * YC + 255) / 256;   // 16-byte pieces of y per thread
     __shared__ __attribute__((aligned(16))) uint16_t xs[64 * XP];
@@ -2224,8 +2240,8 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_red(const uint16_t* __restrict_
     const long t_lo = (long)split * chunk;
     const long t_hi = t_lo + chunk < L ? t_lo + chunk : L;
     const uint16_t* xb = x + bh * L * D;
-    const uint16_t* yhb = yh + bh * L * R;
-    const uint16_t* ylb = yl + bh * L * R;
+    const uint16_t* yhb = yh + bh * L * rv;
+    const uint16_t* ylb = yl + bh * L * rv;
     f32x16_t acc[NR];
 #pragma unroll
     for (int rb = 0; rb < NR; ++rb)
@@ -2247,9 +2263,10 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_red(const uint16_t* __restrict_
             const int which = it / (64 * YC), r = (it % (64 * YC)) / YC, c = it % YC;
             const long t = t0 + r;
             if (it < 2 * 64 * YC) {
-                const u32x4_t w = ldg16((which ? ylb : yhb) + (t < t_hi ? t : t_lo) * R + 8 * c);
+                const bool ok = t < t_hi && 8 * c < rv;
+                const u32x4_t w = ok ? ldg16((which ? ylb : yhb) + t * rv + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ry[m][i] = t < t_hi ? w[i] : 0u;
+                for (int i = 0; i < 4; ++i) ry[m][i] = w[i];
             }
         }
     };
@@ -2296,7 +2313,7 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_red(const uint16_t* __restrict_
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int d = 32 * wave + 8 * (v >> 2) + 4 * hf + (v & 3), r = 32 * rb + (lane & 31);
-            dst[trans ? r * D + d : d * R + r] = acc[rb][v];
+            if (r < rv) dst[trans ? r * D + d : d * rv + r] = acc[rb][v];
         }
 }
 
@@ -2378,18 +2395,19 @@ template <int R, bool SILU, bool ABSPE>
 static hipError_t bwd_lrm(bool key_side, const LrBwdArgs& a, long BH, hipStream_t st) {
     constexpr int D = 128;
     const dim3 grid((unsigned)a.nsplit, (unsigned)BH);
+    const int rv = a.g.R;   // the layer's rank; R is its padded width (32 or 64)
     if (!key_side) {
         // per token, then the [dW_q | dS | dz | dg] partials' dW_q and dS (stored transposed)
-        const long qs = 2l * D * R + R + 4;
+        const long qs = 2l * D * rv + rv + 4;
         hipLaunchKernelGGL((k_bwd_lrm_q<R, SILU, ABSPE>), grid, dim3(256), 0, st, a);
-        hipLaunchKernelGGL((k_bwd_lrm_red<R>), grid, dim3(256), 0, st, a.q, a.y1h, a.y1l, a.L, a.chunk, a.nsplit,
-                           a.part, qs, 0l, 0);
-        hipLaunchKernelGGL((k_bwd_lrm_red<R>), grid, dim3(256), 0, st, a.dout, a.y2h, a.y2l, a.L, a.chunk, a.nsplit,
-                           a.part, qs, (long)D * R, 1);
+        hipLaunchKernelGGL((k_bwd_lrm_red<R>), grid, dim3(256), 0, st, a.q, a.y1h, a.y1l, rv, a.L, a.chunk,
+                           a.nsplit, a.part, qs, 0l, 0);
+        hipLaunchKernelGGL((k_bwd_lrm_red<R>), grid, dim3(256), 0, st, a.dout, a.y2h, a.y2l, rv, a.L, a.chunk,
+                           a.nsplit, a.part, qs, (long)D * rv, 1);
     } else {
         hipLaunchKernelGGL((k_bwd_lrm_k<R, SILU, ABSPE>), grid, dim3(256), 0, st, a);
-        hipLaunchKernelGGL((k_bwd_lrm_red<R>), grid, dim3(256), 0, st, a.k, a.y1h, a.y1l, a.L, a.chunk, a.nsplit,
-                           a.part, (long)D * R, 0l, 0);
+        hipLaunchKernelGGL((k_bwd_lrm_red<R>), grid, dim3(256), 0, st, a.k, a.y1h, a.y1l, rv, a.L, a.chunk,
+                           a.nsplit, a.part, (long)D * rv, 0l, 0);
     }
     return hipGetLastError();
 }
@@ -2397,14 +2415,15 @@ static hipError_t bwd_lrm(bool key_side, const LrBwdArgs& a, long BH, hipStream_
 hipError_t launch_bwd_lr(int dtype_bf16, int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st) {
     if (lr_bwd_on_mfma(dtype_bf16, D, R, a.abspe != 0, a.token != 0)) {
         if (!a.y1h || !a.y1l || !a.y2h || !a.y2l) return hipErrorInvalidValue;
-        const bool silu = a.g.fmap != 0;
+        if (a.g.R != R) return hipErrorInvalidValue;
+        const bool silu = a.g.fmap != 0, w32 = R <= 32;   // ranks 8, 16 run padded to 32
         if (a.abspe) {
             if (!a.dpre) return hipErrorInvalidValue;
-            if (silu) return R == 32 ? bwd_lrm<32, true, true>(key_side, a, BH, st) : bwd_lrm<64, true, true>(key_side, a, BH, st);
-            return R == 32 ? bwd_lrm<32, false, true>(key_side, a, BH, st) : bwd_lrm<64, false, true>(key_side, a, BH, st);
+            if (silu) return w32 ? bwd_lrm<32, true, true>(key_side, a, BH, st) : bwd_lrm<64, true, true>(key_side, a, BH, st);
+            return w32 ? bwd_lrm<32, false, true>(key_side, a, BH, st) : bwd_lrm<64, false, true>(key_side, a, BH, st);
         }
-        if (silu) return R == 32 ? bwd_lrm<32, true, false>(key_side, a, BH, st) : bwd_lrm<64, true, false>(key_side, a, BH, st);
-        return R == 32 ? bwd_lrm<32, false, false>(key_side, a, BH, st) : bwd_lrm<64, false, false>(key_side, a, BH, st);
+        if (silu) return w32 ? bwd_lrm<32, true, false>(key_side, a, BH, st) : bwd_lrm<64, true, false>(key_side, a, BH, st);
+        return w32 ? bwd_lrm<32, false, false>(key_side, a, BH, st) : bwd_lrm<64, false, false>(key_side, a, BH, st);
     }
     if (dtype_bf16)
         return D == 64 ? bwd_lr_d<64, true>(R, key_side, a, BH, st) : bwd_lr_d<128, true>(R, key_side, a, BH, st);

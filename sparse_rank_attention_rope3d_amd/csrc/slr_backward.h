@@ -74,12 +74,13 @@ struct LrBwdArgs {
     uint16_t *y1h, *y1l, *y2h, *y2l;
 };
 
-// The low-rank backward runs on MFMA for bf16 layers with D = 128, rank 32
-// or 64 and the per-head gate (rotary or absolute-PE features); the token
-// gate, fp32 layers and other shapes take the VALU kernels.
+// The low-rank backward runs on MFMA for bf16 layers with D = 128, rank 8,
+// 16, 32 or 64 (8 and 16 padded to 32 with zero weights) and the per-head
+// gate (rotary or absolute-PE features); the token gate, fp32 layers and
+// D = 64 take the VALU kernels.
 inline bool lr_bwd_on_mfma(int dtype_bf16, long D, int R, bool abspe, bool token) {
     (void)abspe;
-    return dtype_bf16 && D == 128 && (R == 32 || R == 64) && !token;
+    return dtype_bf16 && D == 128 && (R == 8 || R == 16 || R == 32 || R == 64) && !token;
 }
 
 hipError_t launch_bwd_lr(int dtype_bf16, int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st);

@@ -168,6 +168,8 @@ SMALL = [
                                           rank=16, lr_mode="abspe", lr_pairs=(0, 0, 0), fmap="silu")),
     ("absolute PE silu rank 64", dict(B=1, H=2, T=3, Hg=10, Wg=11, keep=4, rank=64, lr_mode="abspe",
                                       lr_pairs=(0, 0, 0), fmap="silu")),
+    ("rank 16 silu", dict(B=2, H=1, T=4, Hg=9, Wg=13, keep=3, rank=16, lr_pairs=(4, 2, 2), fmap="silu")),
+    ("absolute PE rank 8", dict(B=1, H=2, T=3, Hg=10, Wg=11, keep=2, rank=8, lr_mode="abspe", lr_pairs=(0, 0, 0))),
 ]
 
 
