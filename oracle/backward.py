@@ -18,6 +18,9 @@ states them. Readings:
   (each 2x2 pair turned by the opposite angle);
 - the low-rank branch's gradient follows phi, the rotation after phi, the
   summary S, z and the normaliser w . z + eps (or the token count for SiLU);
+  FAVOR+ features u_c(p) = exp(omega_c . p - |p|^2 / 2) / sqrt(r) (RoPeSLR
+  appendix) are not elementwise: du_c / dp = u_c (omega_c - p), so
+  dp = omega^T (du * u) - p sum_c du_c u_c;
 - the per-head gate's gradient is sum over rows of dout . O_lowrank;
 - with RoLA's token-wise gate (§4.4; the forward's reading is that of
   ``oracle.token_gate``) the gradient flows through the gate's logistic of
@@ -150,6 +153,19 @@ def query_blocks_keeping(idx, kblocks) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # low-rank branch
 
+def _favor(p, omega):
+    """FAVOR+ features of the rows of p [n, r]: exp(p omega^T - |p|^2 / 2) / sqrt(r)."""
+    om = _d(omega)
+    r = om.shape[0]
+    return np.exp(p @ om.T - 0.5 * (p * p).sum(axis=1, keepdims=True)) / np.sqrt(r)
+
+
+def _favor_back(p, u, du, omega):
+    """Gradient w.r.t. p of sum(du * u(p)) for FAVOR+ features u of p."""
+    g = du * u
+    return g @ _d(omega) - p * g.sum(axis=1, keepdims=True)
+
+
 def _phi_and_grad(x, fmap):
     """phi(x) and phi'(x): elu + 1 (x + 1 | exp x), or SiLU (x sigma(x))."""
     if fmap == "elu1":
@@ -170,7 +186,7 @@ def _axis_scatter(g, grid, r):
     return tuple(out)
 
 
-def lowrank_bwd(cfg, q, k, v, wq, wk, dolr, E=None, origin=(0, 0, 0)) -> Dict[str, np.ndarray]:
+def lowrank_bwd(cfg, q, k, v, wq, wk, dolr, E=None, origin=(0, 0, 0), omega=None) -> Dict[str, np.ndarray]:
     """Gradient of the low-rank branch O_lr (RoLA §4.1-4.3, App. A; the
     forward is ``oracle.lowrank_features`` / ``lowrank_rotate`` /
     ``lowrank_summary`` / ``lowrank_readout``) given dL/dO_lr = ``dolr`` [L, D].
@@ -184,7 +200,9 @@ def lowrank_bwd(cfg, q, k, v, wq, wk, dolr, E=None, origin=(0, 0, 0)) -> Dict[st
     dw_l = rho_l^T dfq_l + dn_l z,  dpq_l = dw_l * phi'(.),
     dW_q = q^T dpq,  dq = dpq W_q^T;  dfk_m = dS v_m,  dv_m = dS^T fk_m,
     du_m = rho_m^T dfk_m + dz,  dpk_m = du_m * phi'(.),  dW_k = k^T dpk,
-    dk = dpk W_k^T; the E tables take the per-axis sums of dpq + dpk."""
+    dk = dpk W_k^T; the E tables take the per-axis sums of dpq + dpk.
+    FAVOR+ (cfg.fmap "favor", ``omega`` [r, r] the head's directions): dpq and
+    dpk go through the features' full Jacobian (``_favor_back``)."""
     q, k, v, wq, wk, dolr = _d(q), _d(k), _d(v), _d(wq), _d(wk), _d(dolr)
     grid = (cfg.T, cfg.Hg, cfg.Wg)
     L = q.shape[0]
@@ -196,8 +214,12 @@ def lowrank_bwd(cfg, q, k, v, wq, wk, dolr, E=None, origin=(0, 0, 0)) -> Dict[st
         et, eh, ew = (_d(e) for e in E)
         add = et[c[:, 0]] + eh[c[:, 1]] + ew[c[:, 2]]
         pq, pk = pq + add, pk + add
-    w, dphq = _phi_and_grad(pq, fmap)
-    u, dphk = _phi_and_grad(pk, fmap)
+    favor = fmap == "favor"
+    if favor:
+        w, u = _favor(pq, omega), _favor(pk, omega)
+    else:
+        w, dphq = _phi_and_grad(pq, fmap)
+        u, dphk = _phi_and_grad(pk, fmap)
     if cfg.lr_mode == "rola":
         ang = _pair_angles(grid, cfg.base, cfg.pairs, cfg.lr_pairs, origin)
         cs, sn = np.cos(ang), np.sin(ang)
@@ -232,10 +254,10 @@ def lowrank_bwd(cfg, q, k, v, wq, wk, dolr, E=None, origin=(0, 0, 0)) -> Dict[st
         dn = -(dolr * o).sum(axis=1) / n
         dz = (dn[:, None] * w).sum(axis=0)
     dw = rho_t(dfq) + dn[:, None] * z[None, :]
-    dpq = dw * dphq
+    dpq = _favor_back(pq, w, dw, omega) if favor else dw * dphq
     dfk = v @ dS.T
     du = rho_t(dfk) + dz[None, :]
-    dpk = du * dphk
+    dpk = _favor_back(pk, u, du, omega) if favor else du * dphk
     res = {"dq": dpq @ wq.T, "dk": dpk @ wk.T, "dv": fk @ dS, "dWq": q.T @ dpq, "dWk": k.T @ dpk,
            "o_lr": o, "dS": dS, "dz": dz}
     if E is not None:
@@ -277,7 +299,7 @@ def token_gate_bwd(q, wg, bg, o_sp, o_lr, eps, dout) -> Dict[str, np.ndarray]:
 
 
 def layer_slice_bwd(cfg, q, k, v, wq, wk, gate_h, dout, E=None, idx=None,
-                    o_sp: Optional[np.ndarray] = None, token_gate_wb=None) -> Dict[str, np.ndarray]:
+                    o_sp: Optional[np.ndarray] = None, token_gate_wb=None, omega=None) -> Dict[str, np.ndarray]:
     """Gradients of one (b, h) slice of the layer (per-head gate):
     out = O_sparse + g_h O_lowrank, so dO_sparse = dout, dO_lowrank = g_h dout
     and dg_h = sum over rows of dout . O_lowrank. ``idx`` fixes the kept blocks
@@ -285,12 +307,13 @@ def layer_slice_bwd(cfg, q, k, v, wq, wk, gate_h, dout, E=None, idx=None,
     output used for dO . o (the saved forward output). Returns dq, dk, dv
     [L, D], dWq, dWk [D, r], dg (scalar), dE (absolute PE), idx and the parts.
     ``token_gate_wb = (wg [D], bg)`` uses RoLA's token-wise gate instead of
-    g_h (then dWg [D] and dbg replace dg)."""
+    g_h (then dWg [D] and dbg replace dg). ``omega`` [r, r]: the head's FAVOR+
+    directions when cfg.fmap is "favor"."""
     grid = (cfg.T, cfg.Hg, cfg.Wg)
     dout = _d(dout)
     L = dout.shape[0]
     if idx is None:
-        idx = oracle.layer_slice(cfg, q, k, v, wq, wk, gate_h, E=E)["idx_ref"]
+        idx = oracle.layer_slice(cfg, q, k, v, wq, wk, gate_h, E=E, omega=omega)["idx_ref"]
     qr = oracle.rope3d(q, grid, cfg.base, cfg.pairs)
     kr = oracle.rope3d(k, grid, cfg.base, cfg.pairs)
     tg = None
@@ -300,11 +323,11 @@ def layer_slice_bwd(cfg, q, k, v, wq, wk, gate_h, dout, E=None, idx=None,
         # the gate reads both branch outputs: the forward's O_sparse and O_lowrank
         L, D = dout.shape
         osp = oracle.block_sparse_attention(qr, kr, v, cfg.block, idx).reshape(-1, D)[:L] if o_sp is None else _d(o_sp)
-        olr = lowrank_bwd(cfg, q, k, v, wq, wk, np.zeros_like(dout), E=E)["o_lr"]
+        olr = lowrank_bwd(cfg, q, k, v, wq, wk, np.zeros_like(dout), E=E, omega=omega)["o_lr"]
         tg = token_gate_bwd(q, token_gate_wb[0], token_gate_wb[1], osp, olr, cfg.eps, dout)
         d_sp, d_lr, o_sp = tg["d_osp"], tg["d_olr"], osp
     sp = sparse_attention_bwd(qr, kr, v, cfg.block, idx, d_sp, o=o_sp)
-    lr = lowrank_bwd(cfg, q, k, v, wq, wk, d_lr, E=E)
+    lr = lowrank_bwd(cfg, q, k, v, wq, wk, d_lr, E=E, omega=omega)
     res = {
         "dq": rope3d_transpose(sp["dq"], grid, cfg.base, cfg.pairs) + lr["dq"],
         "dk": rope3d_transpose(sp["dk"], grid, cfg.base, cfg.pairs) + lr["dk"],

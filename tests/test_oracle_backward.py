@@ -45,19 +45,25 @@ def _inputs(cfg, h=0):
     return q, k, v, np.asarray(p["wq"][h], np.float64), np.asarray(p["wk"][h], np.float64), float(p["gate"][h]), E, dout
 
 
-def _loss(cfg, q, k, v, wq, wk, g, E, dout, idx):
-    res = oracle.layer_slice(cfg, q, k, v, wq, wk, g, E=E, idx=idx)
+def _omega(cfg, h=0):
+    p = synth.lowrank_params(cfg)
+    return np.asarray(p["omega"][h], np.float64) if "omega" in p else None
+
+
+def _loss(cfg, q, k, v, wq, wk, g, E, dout, idx, omega=None):
+    res = oracle.layer_slice(cfg, q, k, v, wq, wk, g, E=E, idx=idx, omega=omega)
     out = res["out"].reshape(-1, q.shape[1])[: q.shape[0]]
     return float((dout * out).sum())
 
 
 def _fd_check(cfg, seed, token=False):
     q, k, v, wq, wk, g, E, dout = _inputs(cfg)
+    om = _omega(cfg)
     tg = None
     if token:
         rng0 = np.random.default_rng(seed + 100)
         tg = (rng0.standard_normal(cfg.D) * 0.2, -0.3)
-    grads = OB.layer_slice_bwd(cfg, q, k, v, wq, wk, g, dout, E=E, token_gate_wb=tg)
+    grads = OB.layer_slice_bwd(cfg, q, k, v, wq, wk, g, dout, E=E, token_gate_wb=tg, omega=om)
     idx = grads["idx"]
     rng = np.random.default_rng(seed)
     args = {"q": q, "k": k, "v": v, "wq": wq, "wk": wk}
@@ -76,9 +82,9 @@ def _fd_check(cfg, seed, token=False):
         EE = (a["et"], a["eh"], a["ew"]) if E is not None else None
         if token:
             res = oracle.layer_slice(cfg, a["q"], a["k"], a["v"], a["wq"], a["wk"], 0.0, E=EE, idx=idx,
-                                     token_gate_wb=(a["wg"], float(a["bg"])))
+                                     token_gate_wb=(a["wg"], float(a["bg"])), omega=om)
             return float((dout * res["out"].reshape(-1, cfg.D)[: cfg.L]).sum())
-        return _loss(cfg, a["q"], a["k"], a["v"], a["wq"], a["wk"], float(a["g"]), EE, dout, idx)
+        return _loss(cfg, a["q"], a["k"], a["v"], a["wq"], a["wk"], float(a["g"]), EE, dout, idx, omega=om)
 
     h = 1e-5
     for name in args:
@@ -109,6 +115,43 @@ def test_finite_differences_token_gate():
 
 def test_finite_differences_token_gate_silu_absolute_pe():
     _fd_check(_abspe_cfg(fmap="silu"), 6, token=True)
+
+
+def test_finite_differences_rotary_favor():
+    """FAVOR+ features (RoPeSLR appendix): the full Jacobian of
+    exp(omega p - |p|^2 / 2) / sqrt(r) w.r.t. p, rotation after the features."""
+    _fd_check(_cfg(fmap="favor"), 7)
+
+
+def test_finite_differences_absolute_pe_favor():
+    _fd_check(_abspe_cfg(fmap="favor"), 8)
+
+
+def test_finite_differences_token_gate_favor():
+    _fd_check(_cfg(fmap="favor"), 9, token=True)
+
+
+def test_favor_feature_gradient_is_not_elementwise():
+    """A planted elementwise gradient (phi' = u, the derivative of exp along
+    one coordinate only) misses the finite differences of FAVOR+ features:
+    the pin above is sensitive to the omega^T and |p|^2 terms."""
+    rng = np.random.default_rng(10)
+    r = 8
+    om = rng.standard_normal((r, r))
+    p = rng.standard_normal((3, r)) * 0.5
+    du = rng.standard_normal((3, r))
+    u = OB._favor(p, om)
+    good = OB._favor_back(p, u, du, om)
+    bad = du * u
+    h = 1e-6
+    fd = np.zeros_like(p)
+    for i in range(3):
+        for j in range(r):
+            e = np.zeros_like(p)
+            e[i, j] = h
+            fd[i, j] = ((du * OB._favor(p + e, om)).sum() - (du * OB._favor(p - e, om)).sum()) / (2 * h)
+    np.testing.assert_allclose(good, fd, rtol=1e-6, atol=1e-9)
+    assert np.abs(bad - fd).max() > 1e-2
 
 
 def test_finite_differences_ragged_tail_and_one_kept_block():
