@@ -275,7 +275,8 @@ def cpu_backward_baseline(cfg, blocks: int):
     qblocks = np.sort(rng.choice(cfg.nblk, size=min(blocks, cfg.nblk), replace=False))
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        OB.lowrank_bwd(cfg, q, k, v, p["wq"][0], p["wk"][0], float(p["gate"][0]) * dout, E=E)
+        OB.lowrank_bwd(cfg, q, k, v, p["wq"][0], p["wk"][0], float(p["gate"][0]) * dout, E=E,
+                       omega=p["omega"][0] if cfg.fmap == "favor" else None)
         t1 = time.perf_counter()
         OB.sparse_attention_bwd(qr, kr, v, cfg.block, idx, dout, qblocks=qblocks)
         t2 = time.perf_counter()
@@ -579,7 +580,8 @@ def main() -> int:
     cfg = workload(args.workload)
     head, dev = measure_forward(cfg, args, torch, B, hip, dense_reps=args.dense_reps)
     backward = None
-    if args.bwd_reps > 0 and cfg.dtype == "bf16" and cfg.fmap != "favor":   # FAVOR+ has no backward
+    # (FAVOR+ layers have a backward only with the per-head gate)
+    if args.bwd_reps > 0 and cfg.dtype == "bf16" and not (cfg.fmap == "favor" and cfg.gate == "token"):
         backward = measure_backward(cfg, args, torch, B, dev)
     del dev
     torch.cuda.empty_cache()

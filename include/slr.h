@@ -77,7 +77,9 @@ extern "C" {
                                   of the exponential kernel, feature c of p = x W [+ E]:
                                   exp(omega_c . p - |p|^2 / 2) / sqrt(r), omega from
                                   slr_lowrank_cfg.omega; readout / (w . z + eps).
-                                  Forward only (slr_attention_bwd: SLR_EUNSUPPORTED) */
+                                  slr_attention_bwd covers it for bf16 layers with
+                                  D = 128 and the per-head gate (else
+                                  SLR_EUNSUPPORTED) */
 
 /* Gate of the combine (slr_lowrank_cfg.gate_mode) */
 #define SLR_GATE_HEAD 0        /* one scalar g_h per head: gate[H]                 */
@@ -265,7 +267,8 @@ int slr_dense_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, co
  * 4-byte aligned); for SLR_LR_ROPE_OUTSIDE they are ignored (may be NULL).
  * Every setting of the forward is covered (either gate, either low-rank
  * variant, bf16 or fp32) with the elu + 1 and SiLU feature maps; FAVOR+
- * layers return SLR_EUNSUPPORTED. Workspace:
+ * layers are covered for bf16 with D = 128 and the per-head gate (other
+ * FAVOR+ layers: SLR_EUNSUPPORTED). Workspace:
  * slr_workspace_bytes(SLR_OP_ATTENTION_BWD, ...). Results are bitwise
  * reproducible (fixed reduction orders, no floating-point atomics).
  */

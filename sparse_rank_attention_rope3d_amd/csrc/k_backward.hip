@@ -1860,6 +1860,99 @@ __device__ __forceinline__ void lrm_store_rank(const f32x16_t* y, uint16_t* dh, 
         }
 }
 
+// Operand-order LDS copies of the head's FAVOR+ directions omega [rv][rv]
+// (zero past rv), hi and lo parts, blocks (cb, ks) = cb (R/16) + ks:
+//   !TR: A[row c][k = j]: lane l: omega[32cb + l%32][16ks + 8(e/4) + 4(l/32) + e%4]  (y = omega p)
+//    TR: A[row j][k = c]: lane l: omega[16ks + 8(e/4) + 4(l/32) + e%4][32cb + l%32]  (omega^T g)
+template <int R, bool TR>
+__device__ __forceinline__ void lrm_build_omega(u32x4_t* hi, u32x4_t* lo, const float* om, int rv, int tid) {
+    constexpr int KS = R / 16, NBLK = (R / 32) * KS;
+    for (int it = tid; it < NBLK * 64; it += 256) {
+        const int blk = it >> 6, l = it & 63, h = l >> 5, cb = blk / KS, ks = blk % KS;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int a = 32 * cb + (l & 31), b = 16 * ks + 8 * (e >> 2) + 4 * h + (e & 3);
+            const int c = TR ? b : a, j = TR ? a : b;
+            x[e] = c < rv && j < rv ? om[c * rv + j] : 0.f;
+        }
+        u32x4_t u, v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u[i] = pack_bf2(x[2 * i], x[2 * i + 1]);
+            v[i] = pack_bf2(x[2 * i] - bf_lo(u[i]), x[2 * i + 1] - bf_hi(u[i]));
+        }
+        hi[it] = u;
+        lo[it] = v;
+    }
+}
+
+// out = M x over ranks (M an R x R operand copy in hi / lo parts, x a rank
+// vector in accumulator layout): three products per k-step (hi hi, lo hi, hi lo)
+template <int NR>
+__device__ __forceinline__ void lrm_rank_mat(const u32x4_t* mhi, const u32x4_t* mlo, const f32x16_t* x, int lane,
+                                             f32x16_t* out) {
+    constexpr int KS = NR * 2;
+    u32x4_t xh[KS], xl[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) lrm_bop(x[ks >> 1], ks & 1, xh[ks], xl[ks]);
+#pragma unroll
+    for (int cb = 0; cb < NR; ++cb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) out[cb][i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int bi = (cb * KS + ks) * 64 + lane;
+            const u32x4_t h = mhi[bi];
+            out[cb] = mfma32(h, xh[ks], out[cb]);
+            out[cb] = mfma32(mlo[bi], xh[ks], out[cb]);
+            out[cb] = mfma32(h, xl[ks], out[cb]);
+        }
+    }
+}
+
+// FAVOR+ features of p (rank layout, zero past rv): u = exp(omega p - |p|^2 / 2) / sqrt(rv)
+template <int NR>
+__device__ __forceinline__ void lrm_favor(const u32x4_t* oh, const u32x4_t* ol, const f32x16_t* p, int lane, int hf,
+                                          int rv, f32x16_t* u) {
+    float sq = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sq += p[rb][v] * p[rb][v];
+    sq = sum_xor32(sq);
+    lrm_rank_mat<NR>(oh, ol, p, lane, u);
+    const float rs = 1.f / sqrtf((float)rv);
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const bool rok = 32 * rb + 8 * (v >> 2) + 4 * hf + (v & 3) < rv;
+            u[rb][v] = rok ? __builtin_amdgcn_exp2f((u[rb][v] - 0.5f * sq) * kLog2e) * rs : 0.f;
+        }
+}
+
+// Gradient w.r.t. p of sum(du * u(p)) for FAVOR+ features: omega^T (du * u) - p sum(du * u); in place in du
+template <int NR>
+__device__ __forceinline__ void lrm_favor_back(const u32x4_t* th, const u32x4_t* tl, const f32x16_t* p,
+                                               const f32x16_t* u, int lane, f32x16_t* du) {
+    float gs = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            du[rb][v] *= u[rb][v];
+            gs += du[rb][v];
+        }
+    gs = sum_xor32(gs);
+    f32x16_t og[NR];
+    lrm_rank_mat<NR>(th, tl, du, lane, og);
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) du[rb][v] = og[rb][v] - p[rb][v] * gs;
+}
+
 // phi and phi' without branches: elu + 1 or SiLU
 template <bool SILU>
 __device__ __forceinline__ void lrm_phi(float x, float& f, float& df) {
@@ -1951,10 +2044,13 @@ __device__ __forceinline__ void lrm_apply_store(const u32x4_t* ahi, const u32x4_
     }
 }
 
-template <int R, bool SILU, bool ABSPE>
+template <int R, int FM, bool ABSPE>
 __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
     constexpr int D = 128, NR = R / 32, NB = R / 4, KS = R / 16;
+    constexpr bool SILU = FM == 1, FAV = FM == 2;   // feature map: elu + 1, SiLU, FAVOR+
+    constexpr int OB = FAV ? NR * KS * 64 : 1;
     __shared__ u32x4_t w_rd[NB * 64], w_dr[NB * 64], s_hi[NB * 64], s_lo[NB * 64];
+    __shared__ u32x4_t om_hi[OB], om_lo[OB], omt_hi[OB], omt_lo[OB];   // FAVOR+: omega, omega^T
     __shared__ __attribute__((aligned(16))) float z_s[R];
     __shared__ float red[4][R + 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
@@ -1972,6 +2068,10 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
     lrm_build<R, false, false>(w_rd, nullptr, [&](int r, int d) { return r < rv ? W[d * rv + r] : 0.f; }, tid);
     lrm_build<R, true, false>(w_dr, nullptr, [&](int r, int d) { return r < rv ? W[d * rv + r] : 0.f; }, tid);
     lrm_build<R, false, true>(s_hi, s_lo, [&](int r, int d) { return r < rv ? S[r * D + d] : 0.f; }, tid);
+    if constexpr (FAV) {
+        lrm_build_omega<R, false>(om_hi, om_lo, a.g.omega + (long)head * rv * rv, rv, tid);
+        lrm_build_omega<R, true>(omt_hi, omt_lo, a.g.omega + (long)head * rv * rv, rv, tid);
+    }
     for (int e = tid; e < R; e += 256) z_s[e] = e < rv ? a.z[bh * rv + e] : 0.f;
     __syncthreads();
     float accz[NR][16];
@@ -1989,8 +2089,8 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
         const long row = bh * L + (valid ? t : t_lo);
         int crd[3];
         token_coords(valid ? t : 0, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
-        // f = phi(q W_q), phi', n
-        f32x16_t f[NR], df[NR];
+        // p = q W_q (+ E), f = phi(p), phi' (FAVOR+: f from all of p, p kept for the backward), n
+        f32x16_t f[NR], df[NR], pp[FAV ? NR : 1];
         float nz = 0.f;
         {
             u32x4_t xb[8];
@@ -2003,22 +2103,29 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
 #pragma unroll
                 for (int s = 0; s < 8; ++s) p = mfma32(w_rd[(8 * rb + s) * 64 + lane], xb[s], p);
                 if constexpr (ABSPE) lrm_add_e(a, crd, hf, p, rb, rv);
+                if constexpr (FAV) {
+                    pp[rb] = p;
+                } else {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    float fv, dv;
-                    lrm_phi<SILU>(p[v], fv, dv);
-                    const bool rok = 32 * rb + 8 * (v >> 2) + 4 * hf + (v & 3) < rv;
-                    f[rb][v] = rok ? fv : 0.f;
-                    df[rb][v] = rok ? dv : 0.f;
-                }
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const float4 z4 = lrm_z4(z_s, rb, g4, hf);
-                    nz += f[rb][4 * g4] * z4.x + f[rb][4 * g4 + 1] * z4.y + f[rb][4 * g4 + 2] * z4.z +
-                          f[rb][4 * g4 + 3] * z4.w;
+                    for (int v = 0; v < 16; ++v) {
+                        float fv, dv;
+                        lrm_phi<SILU>(p[v], fv, dv);
+                        const bool rok = 32 * rb + 8 * (v >> 2) + 4 * hf + (v & 3) < rv;
+                        f[rb][v] = rok ? fv : 0.f;
+                        df[rb][v] = rok ? dv : 0.f;
+                    }
                 }
             }
         }
+        if constexpr (FAV) lrm_favor<NR>(om_hi, om_lo, pp, lane, hf, rv, f);
+#pragma unroll
+        for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const float4 z4 = lrm_z4(z_s, rb, g4, hf);
+                nz += f[rb][4 * g4] * z4.x + f[rb][4 * g4 + 1] * z4.y + f[rb][4 * g4 + 2] * z4.z +
+                      f[rb][4 * g4 + 3] * z4.w;
+            }
         // sg = S dout
         f32x16_t sg[NR];
         {
@@ -2070,10 +2177,12 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
                 const float za = (j & 1) ? z4.z : z4.x, zb = (j & 1) ? z4.w : z4.y;
                 float y0 = sg[rb][2 * j] * sc, y1 = sg[rb][2 * j + 1] * sc;
                 if constexpr (!ABSPE) rot_t(y0, y1, cs[rb][j]);
-                sg[rb][2 * j] = (y0 + dn * za) * df[rb][2 * j];
-                sg[rb][2 * j + 1] = (y1 + dn * zb) * df[rb][2 * j + 1];
+                sg[rb][2 * j] = (y0 + dn * za) * (FAV ? 1.f : df[rb][2 * j]);
+                sg[rb][2 * j + 1] = (y1 + dn * zb) * (FAV ? 1.f : df[rb][2 * j + 1]);
             }
         }
+        // FAVOR+: dw -> dp through the features' Jacobian
+        if constexpr (FAV) lrm_favor_back<NR>(omt_hi, omt_lo, pp, f, lane, sg);
         if (valid) {
             lrm_store_rank<NR>(sg, a.y1h + row * rv, a.y1l + row * rv, hf, rv);
             lrm_store_rank<NR>(fq, a.y2h + row * rv, a.y2l + row * rv, hf, rv);
@@ -2109,11 +2218,14 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
     }
 }
 
-template <int R, bool SILU, bool ABSPE>
+template <int R, int FM, bool ABSPE>
 __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
     constexpr int D = 128, NR = R / 32, NB = R / 4, KS = R / 16;
+    constexpr bool SILU = FM == 1, FAV = FM == 2;   // feature map: elu + 1, SiLU, FAVOR+
+    constexpr int OB = FAV ? NR * KS * 64 : 1;
     __shared__ u32x4_t w_rd[NB * 64], w_dr[NB * 64], s_rd_hi[NB * 64], s_rd_lo[NB * 64], s_dr_hi[NB * 64],
         s_dr_lo[NB * 64];
+    __shared__ u32x4_t om_hi[OB], om_lo[OB], omt_hi[OB], omt_lo[OB];   // FAVOR+: omega, omega^T
     __shared__ __attribute__((aligned(16))) float z_s[R];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
     const int split = blockIdx.x;
@@ -2130,6 +2242,10 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
     lrm_build<R, true, false>(w_dr, nullptr, [&](int r, int d) { return r < rv ? W[d * rv + r] : 0.f; }, tid);
     lrm_build<R, false, true>(s_rd_hi, s_rd_lo, [&](int r, int d) { return r < rv ? dS[r * D + d] : 0.f; }, tid);
     lrm_build<R, true, true>(s_dr_hi, s_dr_lo, [&](int r, int d) { return r < rv ? dS[r * D + d] : 0.f; }, tid);
+    if constexpr (FAV) {
+        lrm_build_omega<R, false>(om_hi, om_lo, a.g.omega + (long)head * rv * rv, rv, tid);
+        lrm_build_omega<R, true>(omt_hi, omt_lo, a.g.omega + (long)head * rv * rv, rv, tid);
+    }
     for (int e = tid; e < R; e += 256) z_s[e] = e < rv ? dS[rv * D + e] : 0.f;
     __syncthreads();
 
@@ -2143,8 +2259,9 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
         token_coords(valid ? t : 0, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
         float2 cs[NR][8];
         if constexpr (!ABSPE) lrm_pairs_cs<NR>(a, crd, hf, cs, rv);
-        // u = phi(k W_k), phi', fk = rho(u) (u itself for absolute PE); zero past rank rv
-        f32x16_t fk[NR], du[NR];
+        // p = k W_k (+ E), u = phi(p) and phi' (FAVOR+: u from all of p, kept in du, and p kept),
+        // fk = rho(u) (u itself for absolute PE); zero past rank rv
+        f32x16_t fk[NR], du[NR], pp[FAV ? NR : 1];
         {
             u32x4_t xb[8];
             lrm_rowops(xb, a.k + row * D, valid, hf);
@@ -2156,19 +2273,34 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
 #pragma unroll
                 for (int s = 0; s < 8; ++s) p = mfma32(w_rd[(8 * rb + s) * 64 + lane], xb[s], p);
                 if constexpr (ABSPE) lrm_add_e(a, crd, hf, p, rb, rv);
+                if constexpr (FAV) {
+                    pp[rb] = p;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        float f0, f1, d0, d1;
+                        lrm_phi<SILU>(p[2 * j], f0, d0);
+                        lrm_phi<SILU>(p[2 * j + 1], f1, d1);
+                        // ranks 2j, 2j + 1 of this lane's group: both valid or both padding (rv % 8 == 0)
+                        if (32 * rb + 8 * (j >> 1) + 4 * hf + 2 * (j & 1) >= rv) f0 = f1 = d0 = d1 = 0.f;
+                        du[rb][2 * j] = d0;
+                        du[rb][2 * j + 1] = d1;
+                        fk[rb][2 * j] = !valid ? 0.f : ABSPE ? f0 : f0 * cs[rb][j].x - f1 * cs[rb][j].y;
+                        fk[rb][2 * j + 1] = !valid ? 0.f : ABSPE ? f1 : f0 * cs[rb][j].y + f1 * cs[rb][j].x;
+                    }
+                }
+            }
+        }
+        if constexpr (FAV) {
+            lrm_favor<NR>(om_hi, om_lo, pp, lane, hf, rv, du);   // du holds u
+#pragma unroll
+            for (int rb = 0; rb < NR; ++rb)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    float f0, f1, d0, d1;
-                    lrm_phi<SILU>(p[2 * j], f0, d0);
-                    lrm_phi<SILU>(p[2 * j + 1], f1, d1);
-                    // ranks 2j, 2j + 1 of this lane's group: both valid or both padding (rv % 8 == 0)
-                    if (32 * rb + 8 * (j >> 1) + 4 * hf + 2 * (j & 1) >= rv) f0 = f1 = d0 = d1 = 0.f;
-                    du[rb][2 * j] = d0;
-                    du[rb][2 * j + 1] = d1;
+                    const float f0 = du[rb][2 * j], f1 = du[rb][2 * j + 1];
                     fk[rb][2 * j] = !valid ? 0.f : ABSPE ? f0 : f0 * cs[rb][j].x - f1 * cs[rb][j].y;
                     fk[rb][2 * j + 1] = !valid ? 0.f : ABSPE ? f1 : f0 * cs[rb][j].y + f1 * cs[rb][j].x;
                 }
-            }
         }
         // dv_lr = dS^T fk
         {
@@ -2202,9 +2334,11 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
                 const float za = (j & 1) ? z4.z : z4.x, zb = (j & 1) ? z4.w : z4.y;
                 float y0 = sv[rb][2 * j], y1 = sv[rb][2 * j + 1];
                 if constexpr (!ABSPE) rot_t(y0, y1, cs[rb][j]);
-                sv[rb][2 * j] = valid ? (y0 + za) * du[rb][2 * j] : 0.f;
-                sv[rb][2 * j + 1] = valid ? (y1 + zb) * du[rb][2 * j + 1] : 0.f;
+                sv[rb][2 * j] = valid ? (y0 + za) * (FAV ? 1.f : du[rb][2 * j]) : 0.f;
+                sv[rb][2 * j + 1] = valid ? (y1 + zb) * (FAV ? 1.f : du[rb][2 * j + 1]) : 0.f;
             }
+        // FAVOR+: du -> dp through the features' Jacobian (u in du)
+        if constexpr (FAV) lrm_favor_back<NR>(omt_hi, omt_lo, pp, du, lane, sv);
         if (valid) {
             lrm_store_rank<NR>(sv, a.y1h + row * rv, a.y1l + row * rv, hf, rv);
             // absolute PE: adds the key side's share (the query side wrote its own first)
@@ -2391,7 +2525,7 @@ static hipError_t bwd_lr_d(int R, bool key_side, const LrBwdArgs& a, long BH, hi
     }
 }
 
-template <int R, bool SILU, bool ABSPE>
+template <int R, int FM, bool ABSPE>
 static hipError_t bwd_lrm(bool key_side, const LrBwdArgs& a, long BH, hipStream_t st) {
     constexpr int D = 128;
     const dim3 grid((unsigned)a.nsplit, (unsigned)BH);
@@ -2399,13 +2533,13 @@ static hipError_t bwd_lrm(bool key_side, const LrBwdArgs& a, long BH, hipStream_
     if (!key_side) {
         // per token, then the [dW_q | dS | dz | dg] partials' dW_q and dS (stored transposed)
         const long qs = 2l * D * rv + rv + 4;
-        hipLaunchKernelGGL((k_bwd_lrm_q<R, SILU, ABSPE>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_bwd_lrm_q<R, FM, ABSPE>), grid, dim3(256), 0, st, a);
         hipLaunchKernelGGL((k_bwd_lrm_red<R>), grid, dim3(256), 0, st, a.q, a.y1h, a.y1l, rv, a.L, a.chunk,
                            a.nsplit, a.part, qs, 0l, 0);
         hipLaunchKernelGGL((k_bwd_lrm_red<R>), grid, dim3(256), 0, st, a.dout, a.y2h, a.y2l, rv, a.L, a.chunk,
                            a.nsplit, a.part, qs, (long)D * rv, 1);
     } else {
-        hipLaunchKernelGGL((k_bwd_lrm_k<R, SILU, ABSPE>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_bwd_lrm_k<R, FM, ABSPE>), grid, dim3(256), 0, st, a);
         hipLaunchKernelGGL((k_bwd_lrm_red<R>), grid, dim3(256), 0, st, a.k, a.y1h, a.y1l, rv, a.L, a.chunk,
                            a.nsplit, a.part, (long)D * rv, 0l, 0);
     }
@@ -2415,15 +2549,20 @@ static hipError_t bwd_lrm(bool key_side, const LrBwdArgs& a, long BH, hipStream_
 hipError_t launch_bwd_lr(int dtype_bf16, int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st) {
     if (lr_bwd_on_mfma(dtype_bf16, D, R, a.abspe != 0, a.token != 0)) {
         if (!a.y1h || !a.y1l || !a.y2h || !a.y2l) return hipErrorInvalidValue;
-        if (a.g.R != R) return hipErrorInvalidValue;
-        const bool silu = a.g.fmap != 0, w32 = R <= 32;   // ranks 8, 16 run padded to 32
-        if (a.abspe) {
-            if (!a.dpre) return hipErrorInvalidValue;
-            if (silu) return w32 ? bwd_lrm<32, true, true>(key_side, a, BH, st) : bwd_lrm<64, true, true>(key_side, a, BH, st);
-            return w32 ? bwd_lrm<32, false, true>(key_side, a, BH, st) : bwd_lrm<64, false, true>(key_side, a, BH, st);
+        if (a.g.R != R || (a.g.fmap == 2 && !a.g.omega)) return hipErrorInvalidValue;
+        if (a.abspe && !a.dpre) return hipErrorInvalidValue;
+        const bool w32 = R <= 32;   // ranks 8, 16 run padded to 32
+#define SLR_LRM(FM_, AB_) \
+    return w32 ? bwd_lrm<32, FM_, AB_>(key_side, a, BH, st) : bwd_lrm<64, FM_, AB_>(key_side, a, BH, st)
+        switch (a.g.fmap * 2 + (a.abspe ? 1 : 0)) {
+            case 0: SLR_LRM(0, false);
+            case 1: SLR_LRM(0, true);
+            case 2: SLR_LRM(1, false);
+            case 3: SLR_LRM(1, true);
+            case 4: SLR_LRM(2, false);
+            default: SLR_LRM(2, true);
         }
-        if (silu) return w32 ? bwd_lrm<32, true, false>(key_side, a, BH, st) : bwd_lrm<64, true, false>(key_side, a, BH, st);
-        return w32 ? bwd_lrm<32, false, false>(key_side, a, BH, st) : bwd_lrm<64, false, false>(key_side, a, BH, st);
+#undef SLR_LRM
     }
     if (dtype_bf16)
         return D == 64 ? bwd_lr_d<64, true>(R, key_side, a, BH, st) : bwd_lr_d<128, true>(R, key_side, a, BH, st);

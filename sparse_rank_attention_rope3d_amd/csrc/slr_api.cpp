@@ -205,6 +205,12 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         w.qr = take((size_t)d.es * d.BH * rows * d.D);
         w.kr = take((size_t)d.es * d.BH * rows * d.D);
         w.wkt = take(2ul * d.H * RP * d.D);
+        if (favor && d.bf16) {
+            // FAVOR+: the summary's (W_k omega^T) parts and, for absolute PE, the projected axis tables
+            w.wko_hi = take(2ul * d.H * RP * d.D);
+            w.wko_lo = take(2ul * d.H * RP * d.D);
+            if (abspe) w.eo = take(4ul * d.H * ((long)d.T + d.Hg + d.Wg) * R);
+        }
         w.part = take(4ul * d.BH * summary_split_cap(d) * (RP * d.D + RP));
         w.S = take(4ul * d.BH * R * d.D);
         w.z = take(4ul * d.BH * R);
@@ -363,8 +369,11 @@ int slr_workspace_bytes(int op, const slr_shape* shape, const slr_rope_cfg* rope
     }
     if (op == SLR_OP_ATTENTION || op == SLR_OP_LOWRANK_SUMMARY || op == SLR_OP_ATTENTION_BWD) {
         if (!lowrank) return SLR_EINVAL;
-        // the backward covers elu + 1 and SiLU features, not FAVOR+
-        if (op == SLR_OP_ATTENTION_BWD && lowrank->feature_map == SLR_FMAP_FAVOR) return SLR_EUNSUPPORTED;
+        // the backward of FAVOR+ features runs on the MFMA low-rank kernels only
+        if (op == SLR_OP_ATTENTION_BWD && lowrank->feature_map == SLR_FMAP_FAVOR &&
+            !lr_bwd_on_mfma(d.bf16, d.D, lowrank->rank, lowrank->mode == SLR_LR_ABS_PE,
+                            lowrank->gate_mode == SLR_GATE_TOKEN))
+            return SLR_EUNSUPPORTED;
         LrGeom lg;
         // pointer fields are not needed for sizing
         slr_lowrank_cfg probe = *lowrank;
@@ -695,7 +704,11 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     if ((st = check_rope(rope, d, &g))) return st;
     if ((st = check_sparse(sparse, d, &nblk))) return st;
     if ((st = check_lowrank(lowrank, rope, d, true, &lg, &RP))) return st;
-    if (lowrank->feature_map == SLR_FMAP_FAVOR) return SLR_EUNSUPPORTED;   // forward only
+    const bool favor = lowrank->feature_map == SLR_FMAP_FAVOR;
+    // FAVOR+: bf16, D = 128, per-head gate only (the MFMA low-rank kernels)
+    if (favor && !lr_bwd_on_mfma(d.bf16, d.D, lowrank->rank, lowrank->mode == SLR_LR_ABS_PE,
+                                 lowrank->gate_mode == SLR_GATE_TOKEN))
+        return SLR_EUNSUPPORTED;
     if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o_sparse) || !tensor_ok(dout)) return SLR_EINVAL;
     if (!tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv) || !idx || !aligned(idx, 4)) return SLR_EINVAL;
     if (!lse || !aligned(lse, 4)) return SLR_EINVAL;
@@ -721,7 +734,7 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     }
     lg.rope = g;
     const int bs = sparse->block, keep = sparse->keep, R = lowrank->rank;
-    Layout w = layout(SLR_OP_ATTENTION_BWD, d, g, bs, nblk, keep, R, RP, abspe, token);
+    Layout w = layout(SLR_OP_ATTENTION_BWD, d, g, bs, nblk, keep, R, RP, abspe, token, favor);
     if ((st = check_ws(ws, ws_bytes, w.total))) return st;
     hipStream_t s = (hipStream_t)stream;
     float2* tab = at<float2>(ws, w.tab);
@@ -737,6 +750,7 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
     SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, qr, kr, nullptr, nullptr, tab, g, d.BH, d.L, (long)nblk * bs, bs,
                              nblk, s, tiled_fwd ? tiled_qscale(d.D) : 1.f));
+    if ((st = favor_tables(d, &lg, lowrank, ws, w, s))) return st;
     if ((st = run_summary(d, g, lg, RP, lowrank, k, v, nullptr, 0, ws, w, S, z, false, s))) return st;
 
     // low-rank branch: query side, reductions, key side

@@ -269,10 +269,11 @@ def test_training_forward_requires_its_outputs():
     assert call(lse=FAKE + 2) == B.SLR_EINVAL
 
 
-def test_favor_feature_map_needs_omega_and_has_no_backward():
+def test_favor_feature_map_needs_omega_and_backward_coverage():
     """FAVOR+ features (SLR_FMAP_FAVOR) need the random directions; the
-    backward does not cover them (SLR_EUNSUPPORTED, before any other check
-    of its outputs)."""
+    backward covers them on the MFMA low-rank kernels (bf16, D = 128,
+    per-head gate) and returns SLR_EUNSUPPORTED for the token gate and fp32
+    layers, before any other check of its outputs."""
     shape, rope, sparse, lr = _cfgs()
     lr.feature_map = B.SLR_FMAP_FAVOR
     assert _attn(shape, rope, sparse, lr) == B.SLR_EINVAL          # omega missing
@@ -283,14 +284,26 @@ def test_favor_feature_map_needs_omega_and_has_no_backward():
     n_fav = B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lr)
     lr.feature_map = B.SLR_FMAP_ELU1
     n_elu = B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lr)
+    nb_elu = B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lr)
     layer = synth.wan13b()
     # four (W omega^T)^T bf16 parts [H, 32, D] on top
     assert n_fav - n_elu >= 4 * 2 * layer.H * 32 * layer.D
     lr.feature_map = B.SLR_FMAP_FAVOR
+    # the backward recomputes the summary: two (W_k omega^T)^T parts on top
+    nb_fav = B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lr)
+    assert nb_fav - nb_elu >= 2 * 2 * layer.H * 32 * layer.D
+    assert _bwd(shape, rope, sparse, lr) == B.SLR_EWORKSPACE
+    lr.gate_mode, lr.gate, lr.Wg, lr.bg = B.SLR_GATE_TOKEN, None, FAKE, FAKE
     with pytest.raises(B.SlrError) as e:
         B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lr)
     assert e.value.code == B.SLR_EUNSUPPORTED
     assert _bwd(shape, rope, sparse, lr) == B.SLR_EUNSUPPORTED
+    small = synth.tiny()   # fp32
+    lr32 = B.SlrLowrankCfg(small.rank, 0, *small.lr_pairs, 1e-6, FAKE, FAKE, FAKE, None, None, None)
+    lr32.feature_map, lr32.omega = B.SLR_FMAP_FAVOR, FAKE
+    with pytest.raises(B.SlrError) as e:
+        B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, B.shape_of(small), B.rope_of(small), B.sparse_of(small), lr32)
+    assert e.value.code == B.SLR_EUNSUPPORTED
     lr.feature_map = 3
     assert _attn(shape, rope, sparse, lr) == B.SLR_EINVAL
 

@@ -64,11 +64,16 @@ def _tables(cfg, p):
     return (p["et"], p["eh"], p["ew"]) if cfg.lr_mode == "abspe" else None
 
 
+def _omega(p, h):
+    return p["omega"][h] if "omega" in p else None
+
+
 def _oracle_lowrank(cfg, inp, b, h):
     qs, ks, vs = synth.qkv_slice(cfg, b, h)
     ds = np.asarray(synth.dout_slice(cfg, b, h), np.float64)
     p = inp.params_np
-    return OB.lowrank_bwd(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], float(p["gate"][h]) * ds, E=_tables(cfg, p))
+    return OB.lowrank_bwd(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], float(p["gate"][h]) * ds, E=_tables(cfg, p),
+                          omega=_omega(p, h))
 
 
 def _oracle_slice(cfg, inp, b, h, ig, qblocks=None, kblocks=None):
@@ -78,7 +83,7 @@ def _oracle_slice(cfg, inp, b, h, ig, qblocks=None, kblocks=None):
     p = inp.params_np
     grid = (cfg.T, cfg.Hg, cfg.Wg)
     res = oracle.layer_slice(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], p["gate"][h], E=_tables(cfg, p), qblocks=[0],
-                             idx=ig)
+                             idx=ig, omega=_omega(p, h))
     T.check_selection(ig, res["scores"], res["thr"], cfg.keep)
     qr, kr = res["q_rot"], res["k_rot"]
     lr = _oracle_lowrank(cfg, inp, b, h)
@@ -170,6 +175,10 @@ SMALL = [
                                       lr_pairs=(0, 0, 0), fmap="silu")),
     ("rank 16 silu", dict(B=2, H=1, T=4, Hg=9, Wg=13, keep=3, rank=16, lr_pairs=(4, 2, 2), fmap="silu")),
     ("absolute PE rank 8", dict(B=1, H=2, T=3, Hg=10, Wg=11, keep=2, rank=8, lr_mode="abspe", lr_pairs=(0, 0, 0))),
+    ("favor", dict(B=2, H=2, T=4, Hg=9, Wg=13, keep=3, fmap="favor")),
+    ("favor absolute PE rank 64", dict(B=1, H=2, T=3, Hg=10, Wg=11, keep=4, rank=64, lr_mode="abspe",
+                                       lr_pairs=(0, 0, 0), fmap="favor")),
+    ("favor rank 16", dict(B=1, H=2, T=4, Hg=9, Wg=13, keep=3, rank=16, lr_pairs=(4, 2, 2), fmap="favor")),
 ]
 
 
@@ -252,6 +261,13 @@ def test_backward_wan13b_sampled():
     full)."""
     cfg = synth.wan13b()
     _check(cfg, slices=[(0, 0), (1, 7)], qsample=4, ksample=4)
+
+
+def test_backward_favor_wan13b_sampled():
+    """FAVOR+ features (RoPeSLR appendix) at the full Wan2.1-1.3B shape,
+    sampled as above."""
+    cfg = dataclasses.replace(synth.wan13b(), fmap="favor")
+    _check(cfg, slices=[(0, 3), (1, 10)], qsample=2, ksample=2)
 
 
 def test_backward_wan14b_sampled():
