@@ -580,8 +580,7 @@ def main() -> int:
     cfg = workload(args.workload)
     head, dev = measure_forward(cfg, args, torch, B, hip, dense_reps=args.dense_reps)
     backward = None
-    # (FAVOR+ layers have a backward only with the per-head gate)
-    if args.bwd_reps > 0 and cfg.dtype == "bf16" and not (cfg.fmap == "favor" and cfg.gate == "token"):
+    if args.bwd_reps > 0 and cfg.dtype == "bf16":
         backward = measure_backward(cfg, args, torch, B, dev)
     del dev
     torch.cuda.empty_cache()

@@ -76,10 +76,7 @@ extern "C" {
 #define SLR_FMAP_FAVOR 2       /* RoPeSLR appendix: positive random features (FAVOR+)
                                   of the exponential kernel, feature c of p = x W [+ E]:
                                   exp(omega_c . p - |p|^2 / 2) / sqrt(r), omega from
-                                  slr_lowrank_cfg.omega; readout / (w . z + eps).
-                                  slr_attention_bwd covers it for bf16 layers with
-                                  D = 128 and the per-head gate (else
-                                  SLR_EUNSUPPORTED) */
+                                  slr_lowrank_cfg.omega; readout / (w . z + eps) */
 
 /* Gate of the combine (slr_lowrank_cfg.gate_mode) */
 #define SLR_GATE_HEAD 0        /* one scalar g_h per head: gate[H]                 */
@@ -265,10 +262,10 @@ int slr_dense_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, co
  * SLR_LR_ABS_PE layers also get the tables' gradients dEt [T,r], dEh [Hg,r],
  * dEw [Wg,r] fp32 (overwritten; sums over batch, heads and tokens; required,
  * 4-byte aligned); for SLR_LR_ROPE_OUTSIDE they are ignored (may be NULL).
- * Every setting of the forward is covered (either gate, either low-rank
- * variant, bf16 or fp32) with the elu + 1 and SiLU feature maps; FAVOR+
- * layers are covered for bf16 with D = 128 and the per-head gate (other
- * FAVOR+ layers: SLR_EUNSUPPORTED). Workspace:
+ * Every setting of the forward is covered: either gate, either low-rank
+ * variant, bf16 or fp32, and each feature map (elu + 1, SiLU, FAVOR+; the
+ * FAVOR+ gradient takes the features' full Jacobian, du_c/dp =
+ * u_c (omega_c - p), with omega held fixed). Workspace:
  * slr_workspace_bytes(SLR_OP_ATTENTION_BWD, ...). Results are bitwise
  * reproducible (fixed reduction orders, no floating-point atomics).
  */

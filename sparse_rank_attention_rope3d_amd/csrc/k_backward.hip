@@ -1248,9 +1248,10 @@ __global__ void k_inv_fill(const uint32_t* __restrict__ bits, const int32_t* __r
 }
 
 // ---------------------------------------------------------------------------
-// Low-rank branch. phi and its derivative: elu + 1 (x + 1 | e^x) or SiLU.
-__device__ __forceinline__ void phi_grad(int fmap, float x, float& f, float& df) {
-    if (fmap) {
+// Low-rank branch. phi and its derivative: elu + 1 (x + 1 | e^x) or SiLU
+// (FAVOR+ features depend on the whole projected row: lr_features_favor).
+__device__ __forceinline__ void phi_grad(bool silu, float x, float& f, float& df) {
+    if (silu) {
         const float sg = 1.f / (1.f + expf(-x));
         f = x * sg;
         df = sg * (1.f + x * (1.f - sg));
@@ -1375,10 +1376,11 @@ __device__ __forceinline__ void lr_features(const LrBwdArgs& a, const float* x, 
             p.w += et[3] + eh[3] + ew[3];
         }
         float f[4], df[4];
-        phi_grad(a.g.fmap, p.x, f[0], df[0]);
-        phi_grad(a.g.fmap, p.y, f[1], df[1]);
-        phi_grad(a.g.fmap, p.z, f[2], df[2]);
-        phi_grad(a.g.fmap, p.w, f[3], df[3]);
+        const bool silu = a.g.fmap == 1;
+        phi_grad(silu, p.x, f[0], df[0]);
+        phi_grad(silu, p.y, f[1], df[1]);
+        phi_grad(silu, p.z, f[2], df[2]);
+        phi_grad(silu, p.w, f[3], df[3]);
         *reinterpret_cast<float4*>(wt + t * Tl::RLD + 4 * g) = make_float4(f[0], f[1], f[2], f[3]);
         *reinterpret_cast<float4*>(dt + t * Tl::RLD + 4 * g) = make_float4(df[0], df[1], df[2], df[3]);
         // rotation after phi of the two pairs (4g, 4g+1), (4g+2, 4g+3) (rotary variant)
@@ -1429,6 +1431,89 @@ __device__ __forceinline__ void lr_back_features(const LrBwdArgs& a, const float
     }
 }
 
+// FAVOR+ features of a token tile (RoPeSLR appendix): p = x W (+ E) -> pt,
+// u_c = exp(omega_c . p - |p|^2 / 2) / sqrt(R) -> wt, and u also -> dt (the
+// elementwise factor lr_back_features multiplies by; lr_favor_back then
+// applies the rest of du/dp), the rotation after the features -> ft. om_s
+// holds the head's omega [R][R + 4]. One (token, 4 ranks) item per thread;
+// called by every thread of the workgroup.
+template <int D, int R>
+__device__ __forceinline__ void lr_features_favor(const LrBwdArgs& a, const float* x, const float* w_s,
+                                                  const float* om_s, float* pt, float* wt, float* ft, float* dt,
+                                                  long t0, long t_hi, int tid) {
+    using Tl = LrTile<D, R>;
+    static_assert(Tl::TT * (R / 4) <= 256, "one item per thread");
+    const bool own = tid < Tl::TT * (R / 4);
+    const int t = tid % Tl::TT, g = tid / Tl::TT;
+    const long l = t0 + t;
+    int crd[3] = {0, 0, 0};
+    if (l < t_hi) token_coords(l, a.g.rope.Hg, a.g.rope.Wg, crd[0], crd[1], crd[2]);
+    if (own) {
+        float4 p = vecmat4<D>(x + t * Tl::XLD, w_s, Tl::RW, g);
+        if (a.abspe && l < t_hi) {
+            const float* et = a.Et + crd[0] * R + 4 * g;
+            const float* eh = a.Eh + crd[1] * R + 4 * g;
+            const float* ew = a.Ew + crd[2] * R + 4 * g;
+            p.x += et[0] + eh[0] + ew[0];
+            p.y += et[1] + eh[1] + ew[1];
+            p.z += et[2] + eh[2] + ew[2];
+            p.w += et[3] + eh[3] + ew[3];
+        }
+        *reinterpret_cast<float4*>(pt + t * Tl::RLD + 4 * g) = p;
+    }
+    __syncthreads();
+    if (own) {
+        const float* pr = pt + t * Tl::RLD;
+        const float4 y = rowdot4<R>(pr, om_s, Tl::RW, g);   // omega_c . p for c = 4g .. 4g + 3
+        float sq = 0.f;
+#pragma unroll 4
+        for (int j = 0; j < R; j += 4) {
+            const float4 v = ld4(pr + j);
+            sq += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        }
+        const float h = 0.5f * sq, isr = 1.f / sqrtf((float)R);
+        float f[4] = {expf(y.x - h) * isr, expf(y.y - h) * isr, expf(y.z - h) * isr, expf(y.w - h) * isr};
+        *reinterpret_cast<float4*>(wt + t * Tl::RLD + 4 * g) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(dt + t * Tl::RLD + 4 * g) = make_float4(f[0], f[1], f[2], f[3]);
+        if (!a.abspe && l < t_hi) {
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const float2 cs = lowrank_cs(a.tab, a.g, 2 * g + q2, crd);
+                const float f0 = f[2 * q2], f1 = f[2 * q2 + 1];
+                f[2 * q2] = f0 * cs.x - f1 * cs.y;
+                f[2 * q2 + 1] = f0 * cs.y + f1 * cs.x;
+            }
+        }
+        *reinterpret_cast<float4*>(ft + t * Tl::RLD + 4 * g) = make_float4(f[0], f[1], f[2], f[3]);
+    }
+}
+
+// The rest of the FAVOR+ Jacobian: with e = du * u in dt (du/dp_j = u_c
+// (omega_cj - p_j)), dp_j = sum_c omega_cj e_c - p_j sum_c e_c -> dt. Called
+// by every thread of the workgroup after the barrier that follows
+// lr_back_features; ends with dt written (a barrier must follow).
+template <int D, int R>
+__device__ __forceinline__ void lr_favor_back(const float* om_s, const float* pt, float* dt, int tid) {
+    using Tl = LrTile<D, R>;
+    const bool own = tid < Tl::TT * (R / 4);
+    const int t = tid % Tl::TT, g = tid / Tl::TT;
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (own) {
+        const float* er = dt + t * Tl::RLD;
+        y = vecmat4<R>(er, om_s, Tl::RW, g);   // (omega^T e)_j for j = 4g .. 4g + 3
+        float se = 0.f;
+#pragma unroll 4
+        for (int c = 0; c < R; c += 4) {
+            const float4 v = ld4(er + c);
+            se += v.x + v.y + v.z + v.w;
+        }
+        const float4 p = ld4(pt + t * Tl::RLD + 4 * g);
+        y.x -= p.x * se; y.y -= p.y * se; y.z -= p.z * se; y.w -= p.w * se;
+    }
+    __syncthreads();
+    if (own) *reinterpret_cast<float4*>(dt + t * Tl::RLD + 4 * g) = y;
+}
+
 // Query side, per token l (O_l = rho_l(w_l)^T S / n_l, w_l = phi(q_l W_q),
 // n_l = w_l . z + eps, or L for SiLU), given dO_lr = g_h dout:
 //   dfq = S dO / n, dn = -(dO . O) / n, dw = rho^T dfq + dn z, dpq = dw phi',
@@ -1436,11 +1521,14 @@ __device__ __forceinline__ void lr_back_features(const LrBwdArgs& a, const float
 //   dz = dn w and dg = dout . O over the workgroup's tokens.
 // Partial layout per (slice, split): [dW_q D*R | dS R*D | dz R | dg 1 | pad 3]
 // (a stride of 2DR + R + 4 floats keeps every block 16-byte aligned).
-template <int D, int R, bool BF>
+template <int D, int R, bool BF, bool FV>
 __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
     using Tl = LrTile<D, R>;
     constexpr int TT = Tl::TT, XLD = Tl::XLD, RW = Tl::RW, RLD = Tl::RLD, NB16 = Tl::NB16;
     __shared__ __attribute__((aligned(16))) float w_s[D * RW];
+    // FAVOR+: the head's omega and the tile's projected rows p
+    __shared__ __attribute__((aligned(16))) float om_s[FV ? R * RW : 4];
+    __shared__ __attribute__((aligned(16))) float p_t[FV ? TT * RLD : 4];
     __shared__ __attribute__((aligned(16))) float s_s[R * D];
     __shared__ float z_s[R];
     __shared__ __attribute__((aligned(16))) float x_s[TT * XLD];
@@ -1464,11 +1552,13 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
     const bool token = a.token != 0;
     // the per-head gate exists only in head mode (the token gate passes no gate array)
     const float gh = token ? 0.f : a.gate[head];
-    const bool silu = a.g.fmap != 0;
+    const bool silu = a.g.fmap == 1;   // SiLU's readout divides by L
     for (int e = tid; e < D * R; e += 256) {
         const float x = a.Wq[(long)head * D * R + e];
         w_s[(e / R) * RW + e % R] = BF ? round_bf(x) : x;
     }
+    if constexpr (FV)
+        for (int e = tid; e < R * R; e += 256) om_s[(e / R) * RW + e % R] = a.g.omega[(long)head * R * R + e];
     for (int e = tid; e < R * D; e += 256) s_s[e] = a.S[bh * R * D + e];
     for (int e = tid; e < R; e += 256) z_s[e] = a.z[bh * R + e];
     float4 accW[NB16][4], accS[NB16][4];
@@ -1500,7 +1590,10 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
         __syncthreads();
         lr_load_rows<D, R, BF>(qs, gs, t0, t_hi, x_s, g_s, tid);
         __syncthreads();
-        lr_features<D, R>(a, x_s, w_s, w_t, f_t, d_t, t0, t_hi, tid);
+        if constexpr (FV)
+            lr_features_favor<D, R>(a, x_s, w_s, om_s, p_t, w_t, f_t, d_t, t0, t_hi, tid);
+        else
+            lr_features<D, R>(a, x_s, w_s, w_t, f_t, d_t, t0, t_hi, tid);
         __syncthreads();
         if (tid < TT) {
             float n = 0.f;
@@ -1591,6 +1684,10 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
         // dfq = S (g dout) / n -> rho^T, + dn z, * phi'  (d_t becomes dpq)
         lr_back_features<D, R>(a, g_s, s_s, z_s, sc_s, dn_s, d_t, t0, t_hi, tid);
         __syncthreads();
+        if constexpr (FV) {
+            lr_favor_back<D, R>(om_s, p_t, d_t, tid);
+            __syncthreads();
+        }
         if (a.abspe) {
             // gradient w.r.t. q W_q + E of each valid token (the E tables' share)
             for (int e = tid; e < TT * R; e += 256) {
@@ -1668,11 +1765,13 @@ __global__ __launch_bounds__(256) void k_bwd_lr_q(LrBwdArgs a) {
 // Key side, per token m (S = sum rho_m(u_m) v_m^T, z = sum u_m, u = phi(k W_k)),
 // given the reduced dS, dz: dv_lr = dS^T fk, dfk = dS v, du = rho^T dfk + dz,
 // dpk = du phi', dk_lr = W_k dpk; partial sums of dW_k = k^T dpk [D*R].
-template <int D, int R, bool BF>
+template <int D, int R, bool BF, bool FV>
 __global__ __launch_bounds__(256) void k_bwd_lr_k(LrBwdArgs a) {
     using Tl = LrTile<D, R>;
     constexpr int TT = Tl::TT, XLD = Tl::XLD, RW = Tl::RW, RLD = Tl::RLD, NB16 = Tl::NB16;
     __shared__ __attribute__((aligned(16))) float w_s[D * RW];
+    __shared__ __attribute__((aligned(16))) float om_s[FV ? R * RW : 4];
+    __shared__ __attribute__((aligned(16))) float p_t[FV ? TT * RLD : 4];
     __shared__ __attribute__((aligned(16))) float s_s[R * D];
     __shared__ float z_s[R];
     __shared__ __attribute__((aligned(16))) float x_s[TT * XLD];
@@ -1692,6 +1791,8 @@ __global__ __launch_bounds__(256) void k_bwd_lr_k(LrBwdArgs a) {
         const float x = a.Wk[(long)head * D * R + e];
         w_s[(e / R) * RW + e % R] = BF ? round_bf(x) : x;
     }
+    if constexpr (FV)
+        for (int e = tid; e < R * R; e += 256) om_s[(e / R) * RW + e % R] = a.g.omega[(long)head * R * R + e];
     for (int e = tid; e < R * D; e += 256) s_s[e] = dsz[e];
     for (int e = tid; e < R; e += 256) z_s[e] = dsz[R * D + e];
     float4 accW[NB16][4];
@@ -1707,7 +1808,10 @@ __global__ __launch_bounds__(256) void k_bwd_lr_k(LrBwdArgs a) {
         __syncthreads();
         lr_load_rows<D, R, BF>(ks, vs, t0, t_hi, x_s, v_s, tid);
         __syncthreads();
-        lr_features<D, R>(a, x_s, w_s, u_t, f_t, d_t, t0, t_hi, tid);
+        if constexpr (FV)
+            lr_features_favor<D, R>(a, x_s, w_s, om_s, p_t, u_t, f_t, d_t, t0, t_hi, tid);
+        else
+            lr_features<D, R>(a, x_s, w_s, u_t, f_t, d_t, t0, t_hi, tid);
         __syncthreads();
         // dv_lr = dS^T fk per (token, 4 dims)
         for (int e = tid; e < TT * (D / 4); e += 256) {
@@ -1719,6 +1823,10 @@ __global__ __launch_bounds__(256) void k_bwd_lr_k(LrBwdArgs a) {
         // dfk = dS v -> rho^T, + dz, * phi'  (d_t becomes dpk)
         lr_back_features<D, R>(a, v_s, s_s, z_s, nullptr, nullptr, d_t, t0, t_hi, tid);
         __syncthreads();
+        if constexpr (FV) {
+            lr_favor_back<D, R>(om_s, p_t, d_t, tid);
+            __syncthreads();
+        }
         if (a.abspe) {
             // adds the key side's share (the query side wrote its own first)
             for (int e = tid; e < TT * R; e += 256) {
@@ -2508,10 +2616,14 @@ static unsigned grid_for(long n) {
 template <int D, int R, bool BF>
 static hipError_t bwd_lr_t(bool key_side, const LrBwdArgs& a, long BH, hipStream_t st) {
     dim3 grid((unsigned)a.nsplit, (unsigned)BH);
-    if (key_side)
-        hipLaunchKernelGGL((k_bwd_lr_k<D, R, BF>), grid, dim3(256), 0, st, a);
-    else
-        hipLaunchKernelGGL((k_bwd_lr_q<D, R, BF>), grid, dim3(256), 0, st, a);
+    const bool fv = a.g.fmap == 2;
+    if (key_side) {
+        if (fv) hipLaunchKernelGGL((k_bwd_lr_k<D, R, BF, true>), grid, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_lr_k<D, R, BF, false>), grid, dim3(256), 0, st, a);
+    } else {
+        if (fv) hipLaunchKernelGGL((k_bwd_lr_q<D, R, BF, true>), grid, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_lr_q<D, R, BF, false>), grid, dim3(256), 0, st, a);
+    }
     return hipGetLastError();
 }
 
@@ -2564,6 +2676,7 @@ hipError_t launch_bwd_lr(int dtype_bf16, int D, int R, bool key_side, const LrBw
         }
 #undef SLR_LRM
     }
+    if (a.g.fmap == 2 && !a.g.omega) return hipErrorInvalidValue;
     if (dtype_bf16)
         return D == 64 ? bwd_lr_d<64, true>(R, key_side, a, BH, st) : bwd_lr_d<128, true>(R, key_side, a, BH, st);
     return D == 64 ? bwd_lr_d<64, false>(R, key_side, a, BH, st) : bwd_lr_d<128, false>(R, key_side, a, BH, st);

@@ -369,11 +369,6 @@ int slr_workspace_bytes(int op, const slr_shape* shape, const slr_rope_cfg* rope
     }
     if (op == SLR_OP_ATTENTION || op == SLR_OP_LOWRANK_SUMMARY || op == SLR_OP_ATTENTION_BWD) {
         if (!lowrank) return SLR_EINVAL;
-        // the backward of FAVOR+ features runs on the MFMA low-rank kernels only
-        if (op == SLR_OP_ATTENTION_BWD && lowrank->feature_map == SLR_FMAP_FAVOR &&
-            !lr_bwd_on_mfma(d.bf16, d.D, lowrank->rank, lowrank->mode == SLR_LR_ABS_PE,
-                            lowrank->gate_mode == SLR_GATE_TOKEN))
-            return SLR_EUNSUPPORTED;
         LrGeom lg;
         // pointer fields are not needed for sizing
         slr_lowrank_cfg probe = *lowrank;
@@ -705,10 +700,6 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     if ((st = check_sparse(sparse, d, &nblk))) return st;
     if ((st = check_lowrank(lowrank, rope, d, true, &lg, &RP))) return st;
     const bool favor = lowrank->feature_map == SLR_FMAP_FAVOR;
-    // FAVOR+: bf16, D = 128, per-head gate only (the MFMA low-rank kernels)
-    if (favor && !lr_bwd_on_mfma(d.bf16, d.D, lowrank->rank, lowrank->mode == SLR_LR_ABS_PE,
-                                 lowrank->gate_mode == SLR_GATE_TOKEN))
-        return SLR_EUNSUPPORTED;
     if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o_sparse) || !tensor_ok(dout)) return SLR_EINVAL;
     if (!tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv) || !idx || !aligned(idx, 4)) return SLR_EINVAL;
     if (!lse || !aligned(lse, 4)) return SLR_EINVAL;

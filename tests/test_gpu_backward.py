@@ -9,7 +9,10 @@ error <= 1e-2 and max-abs error <= 3e-2 x max |reference| for dq, dk, dv,
 dW_q, dW_k, the gate gradient and the E tables' gradients (the gradients are
 ~0.05 RMS, so the forward's absolute 3e-2 is stated relative to the
 gradient's own scale); for fp32 layers 1e-5 relative Frobenius and 1e-5 x
-max |reference|.
+max |reference|. The per-head gate's gradient dg_h = sum_l dout_l . O_lr,l
+is a sum whose terms cancel (by up to ~130x in these layers), and the
+rounding error of a sum scales with the sum of its terms' magnitudes, so its
+error is measured against sum_l |dout_l . O_lr,l| instead of |dg_h|.
 """
 import dataclasses
 
@@ -30,10 +33,14 @@ BAR = {"bf16": (1e-2, 3e-2), "f32": (1e-5, 1e-5)}
 _dtype = ["bf16"]
 
 
-def _close(name, got, ref):
+def _close(name, got, ref, scale=None):
+    """scale: the magnitude errors are measured against (default |ref|)."""
     rel, maxrel = BAR[_dtype[0]]
-    rf = T.rel_fro(got, ref)
-    scale = float(np.abs(ref).max()) if ref.size else 1.0
+    if scale is None:
+        rf = T.rel_fro(got, ref)
+        scale = float(np.abs(ref).max()) if ref.size else 1.0
+    else:
+        rf = T.max_abs(got, ref) / scale
     ma = T.max_abs(got, ref) / (scale if scale > 0 else 1.0)
     T.log(f"    {name}: rel_fro={rf:.3e} max_abs/max|ref|={ma:.3e}")
     assert rf <= rel, f"{name}: relative Frobenius error {rf:.3e} > {rel}"
@@ -97,6 +104,7 @@ def _oracle_slice(cfg, inp, b, h, ig, qblocks=None, kblocks=None):
         "dk": OB.rope3d_transpose(spk["dk"], grid, cfg.base, cfg.pairs) + lr["dk"],
         "dv": spk["dv"] + lr["dv"],
         "dWq": lr["dWq"], "dWk": lr["dWk"], "dg": float((ds * lr["o_lr"]).sum()),
+        "dg_abs": float(np.abs((ds * lr["o_lr"]).sum(axis=1)).sum()),
         "q_rot": qr, "k_rot": kr, "dE": lr.get("dE"),
     }
     return ref
@@ -153,7 +161,8 @@ def _check(cfg, slices=None, qsample=None, ksample=None, heads=None):
     for h in heads:
         _close(f"dWq[{h}]", T.to_host(dWq[h]), sum(dW[b, h]["dWq"] for b in range(cfg.B)))
         _close(f"dWk[{h}]", T.to_host(dWk[h]), sum(dW[b, h]["dWk"] for b in range(cfg.B)))
-        _close(f"dgate[{h}]", T.to_host(dg[h:h + 1]), np.array([sum(dW[b, h]["dg"] for b in range(cfg.B))]))
+        _close(f"dgate[{h}]", T.to_host(dg[h:h + 1]), np.array([sum(dW[b, h]["dg"] for b in range(cfg.B))]),
+               scale=sum(dW[b, h]["dg_abs"] for b in range(cfg.B)))
 
 
 SMALL = [
@@ -179,6 +188,10 @@ SMALL = [
     ("favor absolute PE rank 64", dict(B=1, H=2, T=3, Hg=10, Wg=11, keep=4, rank=64, lr_mode="abspe",
                                        lr_pairs=(0, 0, 0), fmap="favor")),
     ("favor rank 16", dict(B=1, H=2, T=4, Hg=9, Wg=13, keep=3, rank=16, lr_pairs=(4, 2, 2), fmap="favor")),
+    ("favor D64 block32", dict(B=1, H=2, D=64, pairs=(12, 10, 10), T=3, Hg=10, Wg=11, block=32, keep=4, rank=16,
+                               lr_pairs=(4, 2, 2), fmap="favor")),
+    ("favor absolute PE D64 rank 32", dict(B=1, H=2, D=64, pairs=(12, 10, 10), T=3, Hg=10, Wg=11, block=32, keep=4,
+                                           rank=32, lr_mode="abspe", lr_pairs=(0, 0, 0), fmap="favor")),
 ]
 
 
@@ -194,6 +207,10 @@ F32 = [
                                                      Hg=9, Wg=13, keep=3)),
     ("fp32 absolute PE silu", dataclasses.replace(synth.tiny(), name="fp32 abspe silu", lr_mode="abspe",
                                                   lr_pairs=(0, 0, 0), fmap="silu", T=3, Hg=5, Wg=7)),
+    ("fp32 favor", dataclasses.replace(synth.tiny(), name="fp32 favor", fmap="favor")),
+    ("fp32 favor ragged D128 absolute PE", dataclasses.replace(synth.wan13b(), name="fp32 favor abspe", dtype="f32",
+                                                               B=1, H=2, T=4, Hg=9, Wg=13, keep=3, lr_mode="abspe",
+                                                               lr_pairs=(0, 0, 0), fmap="favor")),
 ]
 
 
@@ -209,6 +226,13 @@ TOKEN = [
                                                              Hg=10, Wg=11, keep=4, gate="token", lr_mode="abspe",
                                                              lr_pairs=(0, 0, 0), fmap="silu")),
     ("token gate fp32", dataclasses.replace(synth.tiny(), name="token fp32", gate="token")),
+    ("token gate bf16 favor", dataclasses.replace(synth.wan13b(), name="token favor", B=2, H=2, T=4, Hg=9, Wg=13,
+                                                  keep=3, gate="token", fmap="favor")),
+    ("token gate bf16 absolute PE favor rank 64", dataclasses.replace(synth.wan13b(), name="token abspe favor", B=1,
+                                                                      H=2, T=3, Hg=10, Wg=11, keep=4, gate="token",
+                                                                      rank=64, lr_mode="abspe", lr_pairs=(0, 0, 0),
+                                                                      fmap="favor")),
+    ("token gate fp32 favor", dataclasses.replace(synth.tiny(), name="token fp32 favor", gate="token", fmap="favor")),
 ]
 
 
@@ -229,11 +253,12 @@ def test_backward_token_gate(name, cfg):
         for h in range(cfg.H):
             qs, ks, vs = synth.qkv_slice(cfg, b, h)
             ig = idx[b, h].cpu().numpy()
-            ref_f = oracle.layer_slice(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], 0.0, E=E, qblocks=[0], idx=ig)
+            ref_f = oracle.layer_slice(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], 0.0, E=E, qblocks=[0], idx=ig,
+                                       omega=_omega(p, h))
             T.check_selection(ig, ref_f["scores"], ref_f["thr"], cfg.keep)
             ds = np.asarray(synth.dout_slice(cfg, b, h), np.float64)
             ref = OB.layer_slice_bwd(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], 0.0, ds, E=E, idx=ig,
-                                     token_gate_wb=(p["wg"][h], float(p["bg"][h])))
+                                     token_gate_wb=(p["wg"][h], float(p["bg"][h])), omega=_omega(p, h))
             for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
                 got[n].append(T.to_host(t[b, h]))
                 want[n].append(ref[n])
