@@ -337,19 +337,22 @@ def run_sweep(args, torch, B, synth):
                "layer_ms": round(ms, 4), "dense_ms": round(dense_ms, 3), "speedup_vs_dense": round(dense_ms / ms, 2),
                "effective_tflops": round((F["sparse"] + F["lowrank"] + F["select"]) / (ms * 1e-3) / 1e12, 1)}
         if args.bwd_reps > 0:
-            # the layer backward at this point (the training forward saves what it needs)
-            saved = B.slr_attention_fwd_train(q, k, v, shape, rope, sparse, lowrank, ws=ws)
+            # the layer backward at this point (the training forward saves what it needs, the summary included)
+            summ = (torch.empty((cfg.B, cfg.H, cfg.rank, cfg.D), dtype=torch.float32, device="cuda"),
+                    torch.empty((cfg.B, cfg.H, cfg.rank), dtype=torch.float32, device="cuda"))
+            saved = B.slr_attention_fwd_train(q, k, v, shape, rope, sparse, lowrank, ws=ws, summary=summ)
             wsb = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lowrank), "cuda")
             dout = torch.ones_like(q)
             grads = B.slr_attention_bwd(q, k, v, saved[1], saved[2], saved[3], dout, shape, rope, sparse, lowrank,
-                                        ws=wsb)
+                                        ws=wsb, summary=summ)
             bms = _time_ms(torch, lambda: B.slr_attention_bwd(q, k, v, saved[1], saved[2], saved[3], dout, shape,
-                                                              rope, sparse, lowrank, ws=wsb, grads=grads),
+                                                              rope, sparse, lowrank, ws=wsb, grads=grads,
+                                                              summary=summ),
                            args.bwd_reps)
             row["backward_ms"] = round(bms, 3)
             row["backward_tflops"] = round((2.5 * F["sparse"] + 22.0 * cfg.B * cfg.H * cfg.L * cfg.D * cfg.rank)
                                            / (bms * 1e-3) / 1e12, 1)
-            del saved, wsb, grads, dout
+            del saved, wsb, grads, dout, summ
         with open(args.sweep, "a") as f:
             f.write(json.dumps(row) + "\n")
         print(f"[sweep] {row}", file=sys.stderr, flush=True)
@@ -486,22 +489,28 @@ def args_key(cfg) -> str:
 
 def measure_backward(cfg, args, torch, B, dev):
     """The layer backward (bf16): the training forward saves the selection,
-    O_sparse and the row normalisers once, then the backward is timed on a
-    seeded N(0, 1) output gradient."""
+    O_sparse, the row normalisers and the low-rank summary S, z once, then
+    the backward is timed on a seeded N(0, 1) output gradient (and once
+    more recomputing the summary itself)."""
     q, k, v, params, shape, rope, sparse, lowrank = dev
     print(f"[bench] {cfg.name}: layer backward", file=sys.stderr, flush=True)
     gen = torch.Generator(device="cuda").manual_seed(1234)
     dout = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
     ws = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lowrank), "cuda")
-    saved = B.slr_attention_fwd_train(q, k, v, shape, rope, sparse, lowrank, ws=ws)
+    summ = (torch.empty((cfg.B, cfg.H, cfg.rank, cfg.D), dtype=torch.float32, device="cuda"),
+            torch.empty((cfg.B, cfg.H, cfg.rank), dtype=torch.float32, device="cuda"))
+    saved = B.slr_attention_fwd_train(q, k, v, shape, rope, sparse, lowrank, ws=ws, summary=summ)
     fwd_train_ms = _time_ms(torch, lambda: B.slr_attention_fwd_train(q, k, v, shape, rope, sparse, lowrank, ws=ws,
-                                                                     outs=saved), args.bwd_reps)
+                                                                     outs=saved, summary=summ), args.bwd_reps)
     del ws
     _, idx_s, osp_s, lse_s = saved
     wsb = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lowrank), "cuda")
-    grads = B.slr_attention_bwd(q, k, v, idx_s, osp_s, lse_s, dout, shape, rope, sparse, lowrank, ws=wsb)
+    grads = B.slr_attention_bwd(q, k, v, idx_s, osp_s, lse_s, dout, shape, rope, sparse, lowrank, ws=wsb,
+                                summary=summ)
     bms = _time_ms(torch, lambda: B.slr_attention_bwd(q, k, v, idx_s, osp_s, lse_s, dout, shape, rope, sparse,
-                                                      lowrank, ws=wsb, grads=grads), args.bwd_reps)
+                                                      lowrank, ws=wsb, grads=grads, summary=summ), args.bwd_reps)
+    bms_re = _time_ms(torch, lambda: B.slr_attention_bwd(q, k, v, idx_s, osp_s, lse_s, dout, shape, rope, sparse,
+                                                         lowrank, ws=wsb, grads=grads), args.bwd_reps)
     F = cfg.flops()
     # algorithmic: S recomputed once, dP, dV, dK, dQ = 5 products of the
     # forward's 2 over the kept tiles; low-rank: 11 (D x r) products per token
@@ -511,9 +520,10 @@ def measure_backward(cfg, args, torch, B, dev):
     rec = {"ms": round(bms, 3), "TFLOP/s (algorithmic)": round(btf, 1),
            "frac_bf16_peak": round(btf / PEAK_BF16_TFLOPS, 4),
            "algorithmic_flops": {"sparse": f_bsp, "lowrank": f_blr},
+           "ms_recomputing_summary": round(bms_re, 3),
            "training_forward_ms": round(fwd_train_ms, 3),
            "training_step_ms": round(fwd_train_ms + bms, 3)}
-    del wsb, grads, saved, dout
+    del wsb, grads, saved, dout, summ
     return rec
 
 

@@ -215,12 +215,17 @@ int slr_attention_fwd_staged(const slr_shape *shape, const slr_rope_cfg *rope, c
  * needs. idx_out, o_sparse_out (as in slr_attention_fwd) and lse_out are
  * required: lse_out [B,H,L] fp32 receives, per query row, log2 of the
  * softmax normaliser over its kept keys, sum_j 2^(s_j) with s_j the row's
- * scores in log2 units (q.k / sqrt(D) * log2(e)). Same results otherwise.
+ * scores in log2 units (q.k / sqrt(D) * log2(e)). S_out [B,H,r,D] and
+ * z_out [B,H,r] fp32 (optional: both or neither, 4-byte aligned, else
+ * SLR_EINVAL) receive the low-rank summary the layer used (RoLA App. A
+ * Algorithm 1: S = sum over tokens of rho(phi(k W_k)) v^T, z = sum of
+ * phi(k W_k)), so that slr_attention_bwd need not recompute it. Same results
+ * otherwise.
  */
 int slr_attention_fwd_train(const slr_shape *shape, const slr_rope_cfg *rope, const slr_sparse_cfg *sparse,
                             const slr_lowrank_cfg *lowrank, const void *q, const void *k, const void *v, void *out,
-                            int32_t *idx_out, void *o_sparse_out, float *lse_out, void *ws, size_t ws_bytes,
-                            void *stream);
+                            int32_t *idx_out, void *o_sparse_out, float *lse_out, float *S_out, float *z_out,
+                            void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Dense softmax attention with 3D RoPE applied inside (RoLA §3 "Full
@@ -252,7 +257,10 @@ int slr_dense_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, co
  * lists a block twice gives undefined gradients (the forward's selection
  * never does). o_sparse [B,H,L,D] and lse [B,H,L] fp32 are that call's
  * o_sparse_out and lse_out (the softmax normalisers are reused, not
- * recomputed), for the same q, k, v and configuration. dout, dq, dk, dv:
+ * recomputed), for the same q, k, v and configuration. S [B,H,r,D] and z
+ * [B,H,r] fp32 are that call's S_out, z_out (optional: both or neither;
+ * with neither, the summary is recomputed from k and v; the workspace size
+ * does not depend on the choice). dout, dq, dk, dv:
  * [B,H,L,D] of shape->dtype (bf16 or fp32, like q, k, v); the byte ranges
  * of dq, dk and dv may not overlap each other or those of q, k, v,
  * o_sparse, dout (SLR_EINVAL). dWq, dWk: [H,D,r]
@@ -271,9 +279,10 @@ int slr_dense_attention_fwd(const slr_shape *shape, const slr_rope_cfg *rope, co
  */
 int slr_attention_bwd(const slr_shape *shape, const slr_rope_cfg *rope, const slr_sparse_cfg *sparse,
                       const slr_lowrank_cfg *lowrank, const void *q, const void *k, const void *v,
-                      const int32_t *idx, const void *o_sparse, const float *lse, const void *dout, void *dq,
-                      void *dk, void *dv, float *dWq, float *dWk, float *dgate, float *dWg, float *dbg,
-                      float *dEt, float *dEh, float *dEw, void *ws, size_t ws_bytes, void *stream);
+                      const int32_t *idx, const void *o_sparse, const float *lse, const float *S, const float *z,
+                      const void *dout, void *dq, void *dk, void *dv, float *dWq, float *dWk, float *dgate,
+                      float *dWg, float *dbg, float *dEt, float *dEh, float *dEw, void *ws, size_t ws_bytes,
+                      void *stream);
 
 /* Static text for a status code. */
 const char *slr_status_string(int status);

@@ -84,8 +84,8 @@ def lib() -> ctypes.CDLL:
         L.slr_attention_fwd_staged.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg), vp,
                                                vp, vp, vp, vp, vp, vp, vp, sz, P(vp), vp]
         L.slr_dense_attention_fwd.argtypes = [P(SlrShape), P(SlrRopeCfg), vp, vp, vp, vp, vp, sz, vp]
-        L.slr_attention_bwd.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg)] + [vp] * 19 + [sz, vp]
-        L.slr_attention_fwd_train.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg)] + [vp] * 8 + [sz, vp]
+        L.slr_attention_bwd.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg)] + [vp] * 21 + [sz, vp]
+        L.slr_attention_fwd_train.argtypes = [P(SlrShape), P(SlrRopeCfg), P(SlrSparseCfg), P(SlrLowrankCfg)] + [vp] * 10 + [sz, vp]
         for f in EXPORTS[:-1]:
             getattr(L, f).restype = ctypes.c_int
         L.slr_status_string.argtypes = [ctypes.c_int]
@@ -231,9 +231,11 @@ def slr_attention_fwd(q, k, v, shape: SlrShape, rope: SlrRopeCfg, sparse: SlrSpa
 
 
 def slr_attention_fwd_train(q, k, v, shape: SlrShape, rope: SlrRopeCfg, sparse: SlrSparseCfg,
-                            lowrank: SlrLowrankCfg, ws: Optional[torch.Tensor] = None, outs=None):
+                            lowrank: SlrLowrankCfg, ws: Optional[torch.Tensor] = None, outs=None, summary=None):
     """Training forward: returns (out, idx, o_sparse, lse [B, H, L] fp32);
-    ``outs`` may supply those four tensors."""
+    ``outs`` may supply those four tensors. ``summary`` = (S [B, H, r, D],
+    z [B, H, r]) fp32 tensors receive the low-rank summary for
+    slr_attention_bwd (None: not saved)."""
     if outs is None:
         L = shape.T * shape.Hg * shape.Wg
         nblk = -(-L // sparse.block)
@@ -245,19 +247,21 @@ def slr_attention_fwd_train(q, k, v, shape: SlrShape, rope: SlrRopeCfg, sparse: 
     ws = _ws(SLR_OP_ATTENTION, shape, rope, sparse, lowrank, ws, q.device)
     _check(lib().slr_attention_fwd_train(ctypes.byref(shape), ctypes.byref(rope), ctypes.byref(sparse),
                                          ctypes.byref(lowrank), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(idx),
-                                         _ptr(o_sp), _ptr(lse), _ptr(ws), ws.numel(), _stream()),
+                                         _ptr(o_sp), _ptr(lse), *(_ptr(t) for t in (summary or (None, None))),
+                                         _ptr(ws), ws.numel(), _stream()),
            "slr_attention_fwd_train")
     return out, idx, o_sp, lse
 
 
 def slr_attention_bwd(q, k, v, idx, o_sparse, lse, dout, shape: SlrShape, rope: SlrRopeCfg, sparse: SlrSparseCfg,
-                      lowrank: SlrLowrankCfg, ws: Optional[torch.Tensor] = None, grads=None):
+                      lowrank: SlrLowrankCfg, ws: Optional[torch.Tensor] = None, grads=None, summary=None):
     """Backward of the layer given dout (idx, o_sparse and lse saved by
     slr_attention_fwd_train). Returns (dq, dk, dv, dWq [H, D, r] fp32, dWk,
     dgate, dE): dgate is [H] fp32 for the per-head gate, (dWg [H, D], dbg [H])
     fp32 for the token gate; dE = (dEt [T, r], dEh [Hg, r], dEw [Wg, r]) fp32
     for the absolute-PE variant, else None; ``grads`` may supply those
-    outputs."""
+    outputs; ``summary`` = the (S, z) slr_attention_fwd_train saved (None:
+    recomputed)."""
     if grads is None:
         dev = q.device
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -275,7 +279,8 @@ def slr_attention_bwd(q, k, v, idx, o_sparse, lse, dout, shape: SlrShape, rope: 
     ws = _ws(SLR_OP_ATTENTION_BWD, shape, rope, sparse, lowrank, ws, q.device)
     _check(lib().slr_attention_bwd(ctypes.byref(shape), ctypes.byref(rope), ctypes.byref(sparse),
                                    ctypes.byref(lowrank), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(o_sparse),
-                                   _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dWq), _ptr(dWk),
+                                   _ptr(lse), *(_ptr(t) for t in (summary or (None, None))), _ptr(dout), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), _ptr(dWq), _ptr(dWk),
                                    *((None, _ptr(dg[0]), _ptr(dg[1])) if isinstance(dg, tuple) else (_ptr(dg), None, None)),
                                    *(_ptr(t) for t in (dE or (None, None, None))),
                                    _ptr(ws), ws.numel(), _stream()), "slr_attention_bwd")

@@ -531,8 +531,8 @@ namespace {
 
 static int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
                   const slr_lowrank_cfg* lowrank, const void* q, const void* k, const void* v, void* out,
-                  int32_t* idx_out, void* o_sparse_out, void* o_lowrank_out, float* lse_out, void* ws,
-                  size_t ws_bytes, void* const* events, void* stream) {
+                  int32_t* idx_out, void* o_sparse_out, void* o_lowrank_out, float* lse_out, float* S_out,
+                  float* z_out, void* ws, size_t ws_bytes, void* const* events, void* stream) {
     Dims d;
     RopeGeom g;
     LrGeom lg;
@@ -562,8 +562,9 @@ static int attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const
     float* qbar = at<float>(ws, w.qbar);
     float* kbar = at<float>(ws, w.kbar);
     int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, w.idx);
-    float* S = at<float>(ws, w.S);
-    float* z = at<float>(ws, w.z);
+    // the summary goes to the caller's S_out, z_out when given (training forward)
+    float* S = S_out ? S_out : at<float>(ws, w.S);
+    float* z = z_out ? z_out : at<float>(ws, w.z);
 
     auto mark = [&](int i) { return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess; };
     SLR_TRY(mark(0));
@@ -626,16 +627,18 @@ int slr_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
                       int32_t* idx_out, void* o_sparse_out, void* o_lowrank_out, void* ws, size_t ws_bytes,
                       void* stream) {
     return attention_fwd(shape, rope, sparse, lowrank, q, k, v, out, idx_out, o_sparse_out, o_lowrank_out, nullptr,
-                         ws, ws_bytes, nullptr, stream);
+                         nullptr, nullptr, ws, ws_bytes, nullptr, stream);
 }
 
 int slr_attention_fwd_train(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
                             const slr_lowrank_cfg* lowrank, const void* q, const void* k, const void* v, void* out,
-                            int32_t* idx_out, void* o_sparse_out, float* lse_out, void* ws, size_t ws_bytes,
-                            void* stream) {
+                            int32_t* idx_out, void* o_sparse_out, float* lse_out, float* S_out, float* z_out,
+                            void* ws, size_t ws_bytes, void* stream) {
     if (!idx_out || !o_sparse_out || !lse_out) return SLR_EINVAL;
-    return attention_fwd(shape, rope, sparse, lowrank, q, k, v, out, idx_out, o_sparse_out, nullptr, lse_out, ws,
-                         ws_bytes, nullptr, stream);
+    if ((S_out == nullptr) != (z_out == nullptr) || (S_out && (!aligned(S_out, 4) || !aligned(z_out, 4))))
+        return SLR_EINVAL;
+    return attention_fwd(shape, rope, sparse, lowrank, q, k, v, out, idx_out, o_sparse_out, nullptr, lse_out, S_out,
+                         z_out, ws, ws_bytes, nullptr, stream);
 }
 
 int slr_attention_fwd_staged(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
@@ -646,7 +649,7 @@ int slr_attention_fwd_staged(const slr_shape* shape, const slr_rope_cfg* rope, c
     for (int i = 0; i < 5; ++i)
         if (!events[i]) return SLR_EINVAL;
     return attention_fwd(shape, rope, sparse, lowrank, q, k, v, out, idx_out, o_sparse_out, o_lowrank_out, nullptr,
-                         ws, ws_bytes, events, stream);
+                         nullptr, nullptr, ws, ws_bytes, events, stream);
 }
 
 int slr_dense_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, const void* q, const void* k,
@@ -687,7 +690,8 @@ int slr_dense_attention_fwd(const slr_shape* shape, const slr_rope_cfg* rope, co
 
 int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const slr_sparse_cfg* sparse,
                       const slr_lowrank_cfg* lowrank, const void* q, const void* k, const void* v, const int32_t* idx,
-                      const void* o_sparse, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      const void* o_sparse, const float* lse, const float* S_in, const float* z_in, const void* dout,
+                      void* dq, void* dk, void* dv,
                       float* dWq, float* dWk, float* dgate, float* dWg, float* dbg, float* dEt, float* dEh,
                       float* dEw, void* ws, size_t ws_bytes, void* stream) {
     Dims d;
@@ -703,6 +707,8 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o_sparse) || !tensor_ok(dout)) return SLR_EINVAL;
     if (!tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv) || !idx || !aligned(idx, 4)) return SLR_EINVAL;
     if (!lse || !aligned(lse, 4)) return SLR_EINVAL;
+    if ((S_in == nullptr) != (z_in == nullptr) || (S_in && (!aligned(S_in, 4) || !aligned(z_in, 4))))
+        return SLR_EINVAL;
     const bool token = lowrank->gate_mode == SLR_GATE_TOKEN;
     if (!dWq || !dWk || !aligned(dWq, 4) || !aligned(dWk, 4)) return SLR_EINVAL;
     if (!token && (!dgate || !aligned(dgate, 4))) return SLR_EINVAL;
@@ -731,8 +737,9 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     float2* tab = at<float2>(ws, w.tab);
     uint16_t* qr = at<uint16_t>(ws, w.qr);
     uint16_t* kr = at<uint16_t>(ws, w.kr);
-    float* S = at<float>(ws, w.S);
-    float* z = at<float>(ws, w.z);
+    // the forward's summary when the caller saved it, else recomputed here
+    const float* S = S_in ? S_in : at<float>(ws, w.S);
+    const float* z = z_in ? z_in : at<float>(ws, w.z);
 
     // q scaled exactly as the forward scored it (pre-scaled into log2 units on
     // the tiled path), so the saved normalisers match the recomputed scores
@@ -741,8 +748,12 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     SLR_TRY(launch_rope_tables(tab, g, rope->base, s));
     SLR_TRY(launch_rope_pool(d.bf16, (int)d.D, q, k, qr, kr, nullptr, nullptr, tab, g, d.BH, d.L, (long)nblk * bs, bs,
                              nblk, s, tiled_fwd ? tiled_qscale(d.D) : 1.f));
-    if ((st = favor_tables(d, &lg, lowrank, ws, w, s))) return st;
-    if ((st = run_summary(d, g, lg, RP, lowrank, k, v, nullptr, 0, ws, w, S, z, false, s))) return st;
+    if (!S_in) {
+        if ((st = favor_tables(d, &lg, lowrank, ws, w, s))) return st;
+        if ((st = run_summary(d, g, lg, RP, lowrank, k, v, nullptr, 0, ws, w, at<float>(ws, w.S), at<float>(ws, w.z),
+                              false, s)))
+            return st;
+    }
 
     // low-rank branch: query side, reductions, key side
     LrBwdArgs la;

@@ -181,12 +181,13 @@ GIB = 2 ** 30   # the [B,H,L,D] fakes below sit 1 GiB apart: their byte ranges d
 
 
 def _bwd(shape, rope, sparse, lr, q=FAKE, k=FAKE + GIB, v=FAKE + 2 * GIB, idx=FAKE + 8 * GIB + 0x3000,
-         osp=FAKE + 3 * GIB, lse=FAKE + 8 * GIB + 0xc000, dout=FAKE + 4 * GIB, dq=FAKE + 5 * GIB, dk=FAKE + 6 * GIB,
+         osp=FAKE + 3 * GIB, lse=FAKE + 8 * GIB + 0xc000, S=None, z=None, dout=FAKE + 4 * GIB, dq=FAKE + 5 * GIB,
+         dk=FAKE + 6 * GIB,
          dv=FAKE + 7 * GIB, dwq=FAKE + 8 * GIB + 0x9000, dwk=FAKE + 8 * GIB + 0xa000, dg=FAKE + 8 * GIB + 0xb000,
          dwg=FAKE + 8 * GIB + 0x10000, dbg=FAKE + 8 * GIB + 0x11000, det=FAKE + 8 * GIB + 0xd000,
          deh=FAKE + 8 * GIB + 0xe000, dew=FAKE + 8 * GIB + 0xf000, ws=None, ws_bytes=0):
     r = ctypes.byref
-    return B.lib().slr_attention_bwd(r(shape), r(rope), r(sparse), r(lr), q, k, v, idx, osp, lse, dout, dq, dk, dv,
+    return B.lib().slr_attention_bwd(r(shape), r(rope), r(sparse), r(lr), q, k, v, idx, osp, lse, S, z, dout, dq, dk, dv,
                                      dwq, dwk, dg, dwg, dbg, det, deh, dew, ws, ws_bytes, None)
 
 
@@ -202,6 +203,12 @@ def test_backward_validates_before_launching():
         assert _bwd(shape, rope, sparse, lr, **{bad: None}) == B.SLR_EINVAL, bad
     assert _bwd(shape, rope, sparse, lr, idx=FAKE + 2) == B.SLR_EINVAL
     assert _bwd(shape, rope, sparse, lr, dk=MISALIGNED) == B.SLR_EINVAL
+    # the forward's saved summary: both or neither, 4-byte aligned
+    S, z = FAKE + 8 * GIB + 0x20000, FAKE + 8 * GIB + 0x30000
+    assert _bwd(shape, rope, sparse, lr, S=S, z=z) == B.SLR_EWORKSPACE
+    assert _bwd(shape, rope, sparse, lr, S=S) == B.SLR_EINVAL
+    assert _bwd(shape, rope, sparse, lr, z=z) == B.SLR_EINVAL
+    assert _bwd(shape, rope, sparse, lr, S=S + 2, z=z) == B.SLR_EINVAL
     # outputs may not share a byte with an input or with each other
     nbytes = 2 * layer.B * layer.H * layer.L * layer.D
     assert _bwd(shape, rope, sparse, lr, dq=FAKE) == B.SLR_EINVAL
@@ -259,14 +266,19 @@ def test_training_forward_requires_its_outputs():
     r = ctypes.byref
     L = B.lib()
 
-    def call(idx=FAKE + 0x1000, osp=FAKE + 0x2000, lse=FAKE + 0x3000):
+    def call(idx=FAKE + 0x1000, osp=FAKE + 0x2000, lse=FAKE + 0x3000, S=None, z=None):
         return L.slr_attention_fwd_train(r(shape), r(rope), r(sparse), r(lr), FAKE, FAKE, FAKE, FAKE + 0x4000, idx,
-                                         osp, lse, None, 0, None)
+                                         osp, lse, S, z, None, 0, None)
     assert call() == B.SLR_EWORKSPACE
     assert call(idx=None) == B.SLR_EINVAL
     assert call(osp=None) == B.SLR_EINVAL
     assert call(lse=None) == B.SLR_EINVAL
     assert call(lse=FAKE + 2) == B.SLR_EINVAL
+    # the saved summary: both or neither, 4-byte aligned
+    assert call(S=FAKE + 0x5000, z=FAKE + 0x6000) == B.SLR_EWORKSPACE
+    assert call(S=FAKE + 0x5000) == B.SLR_EINVAL
+    assert call(z=FAKE + 0x6000) == B.SLR_EINVAL
+    assert call(S=FAKE + 0x5002, z=FAKE + 0x6000) == B.SLR_EINVAL
 
 
 def test_favor_feature_map_needs_omega_and_backward_coverage():

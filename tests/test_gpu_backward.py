@@ -56,13 +56,22 @@ def _dout(cfg):
     return g
 
 
-def _run_gpu(cfg):
+def _summary_buffers(cfg):
+    S = torch.empty((cfg.B, cfg.H, cfg.rank, cfg.D), dtype=torch.float32, device="cuda")
+    return S, torch.empty((cfg.B, cfg.H, cfg.rank), dtype=torch.float32, device="cuda")
+
+
+def _run_gpu(cfg, saved_summary=True):
+    """Training forward then backward; the backward is given the summary the
+    forward saved (a training step's path) unless saved_summary is False."""
     inp = T.make_inputs(cfg)
     dout = _dout(cfg)
     shape, rope, sparse = B.shape_of(cfg), B.rope_of(cfg), B.sparse_of(cfg)
     lowrank = B.lowrank_of(cfg, inp.params)
-    _, idx, o_sp, lse = B.slr_attention_fwd_train(inp.q, inp.k, inp.v, shape, rope, sparse, lowrank)
-    grads = B.slr_attention_bwd(inp.q, inp.k, inp.v, idx, o_sp, lse, dout, shape, rope, sparse, lowrank)
+    summ = _summary_buffers(cfg) if saved_summary else None
+    _, idx, o_sp, lse = B.slr_attention_fwd_train(inp.q, inp.k, inp.v, shape, rope, sparse, lowrank, summary=summ)
+    grads = B.slr_attention_bwd(inp.q, inp.k, inp.v, idx, o_sp, lse, dout, shape, rope, sparse, lowrank,
+                                summary=summ)
     torch.cuda.synchronize()
     return inp, idx, grads, lse
 
@@ -277,6 +286,55 @@ def test_backward_token_gate(name, cfg):
     if E is not None:
         for i, n in enumerate(("dEt", "dEh", "dEw")):
             _close(n, T.to_host(dE[i]), sums["dE", i])
+
+
+SAVED = [
+    ("bf16 rotary", dataclasses.replace(synth.wan13b(), name="saved bf16", B=2, H=2, T=4, Hg=9, Wg=13, keep=3)),
+    ("bf16 FAVOR+ absolute PE rank 64", dataclasses.replace(synth.wan13b(), name="saved favor abspe", B=1, H=2, T=3,
+                                                            Hg=10, Wg=11, keep=4, rank=64, lr_mode="abspe",
+                                                            lr_pairs=(0, 0, 0), fmap="favor")),
+    ("bf16 token gate SiLU", dataclasses.replace(synth.wan13b(), name="saved token silu", B=1, H=2, T=4, Hg=9, Wg=13,
+                                                 keep=3, gate="token", fmap="silu")),
+    ("fp32 tiny", synth.tiny()),
+]
+
+
+@pytest.mark.parametrize("name,cfg", SAVED, ids=[s[0] for s in SAVED])
+def test_backward_saved_summary(name, cfg):
+    """slr_attention_fwd_train's S_out, z_out hold the summary the layer
+    used (against the oracle's S, z of every slice), and the backward given
+    them agrees with the backward that recomputes them (the two summaries
+    differ only in the split-L partition of their sums: within 1e-5)."""
+    T.log(f"  case {cfg.name}: L={cfg.L} D={cfg.D} r={cfg.rank} fmap={cfg.fmap} {cfg.lr_mode} {cfg.gate} {cfg.dtype}")
+    inp = T.make_inputs(cfg)
+    dout = _dout(cfg)
+    shape, rope, sparse = B.shape_of(cfg), B.rope_of(cfg), B.sparse_of(cfg)
+    lowrank = B.lowrank_of(cfg, inp.params)
+    S, z = _summary_buffers(cfg)
+    _, idx, o_sp, lse = B.slr_attention_fwd_train(inp.q, inp.k, inp.v, shape, rope, sparse, lowrank, summary=(S, z))
+    g_saved = B.slr_attention_bwd(inp.q, inp.k, inp.v, idx, o_sp, lse, dout, shape, rope, sparse, lowrank,
+                                  summary=(S, z))
+    g_re = B.slr_attention_bwd(inp.q, inp.k, inp.v, idx, o_sp, lse, dout, shape, rope, sparse, lowrank)
+    torch.cuda.synchronize()
+    p = inp.params_np
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            qs, ks, vs = synth.qkv_slice(cfg, b, h)
+            tg = (p["wg"][h], float(p["bg"][h])) if cfg.gate == "token" else None
+            res = oracle.layer_slice(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], p["gate"][h], _tables(cfg, p),
+                                     qblocks=[0], idx=idx[b, h].cpu().numpy(), token_gate_wb=tg, omega=_omega(p, h))
+            T.assert_close(f"S[{b},{h}]", T.to_host(S[b, h]), res["S"], cfg.dtype, branch=True)
+            T.assert_close(f"z[{b},{h}]", T.to_host(z[b, h]), res["z"], cfg.dtype, branch=True)
+
+    def flat(g):
+        out = list(g[:5])
+        out += list(g[5]) if isinstance(g[5], tuple) else [g[5]]
+        out += list(g[6] or ())
+        return out
+    for i, (a, c) in enumerate(zip(flat(g_saved), flat(g_re))):
+        rf = T.rel_fro(T.to_host(a), T.to_host(c))
+        T.log(f"    gradient {i}: saved vs recomputed summary rel_fro={rf:.3e}")
+        assert rf <= 1e-5, f"gradient {i}: saved vs recomputed summary differ by {rf:.3e}"
 
 
 def test_backward_wan13b_sampled():

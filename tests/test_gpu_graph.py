@@ -48,10 +48,12 @@ def test_layer_forward_replays_in_a_graph(gate):
         assert torch.equal(out, want), f"replay {rep} differs from the eager result"
 
 
-def test_training_step_replays_in_a_graph():
+@pytest.mark.parametrize("keep_summary", [False, True], ids=["recomputed summary", "saved summary"])
+def test_training_step_replays_in_a_graph(keep_summary):
     """The training forward and the backward capture together: the backward
     allocates nothing either and clears its scratch with a kernel (no memset
-    nodes); every replay equals the eager gradients bit for bit."""
+    nodes); every replay equals the eager gradients bit for bit, with the
+    backward recomputing the low-rank summary or taking the forward's."""
     cfg = T.custom(synth.wan13b(), name="graph training step", B=1, H=2, T=4, Hg=9, Wg=13, keep=3)
     inp = T.make_inputs(cfg)
     dout = torch.empty_like(inp.q)
@@ -62,9 +64,13 @@ def test_training_step_replays_in_a_graph():
     lowrank = B.lowrank_of(cfg, inp.params)
     wsf = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lowrank), "cuda")
     wsb = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lowrank), "cuda")
-    saved = B.slr_attention_fwd_train(inp.q, inp.k, inp.v, shape, rope, sparse, lowrank, ws=wsf)
+    summ = None
+    if keep_summary:
+        summ = (torch.empty((cfg.B, cfg.H, cfg.rank, cfg.D), dtype=torch.float32, device="cuda"),
+                torch.empty((cfg.B, cfg.H, cfg.rank), dtype=torch.float32, device="cuda"))
+    saved = B.slr_attention_fwd_train(inp.q, inp.k, inp.v, shape, rope, sparse, lowrank, ws=wsf, summary=summ)
     want = B.slr_attention_bwd(inp.q, inp.k, inp.v, saved[1], saved[2], saved[3], dout, shape, rope, sparse, lowrank,
-                               ws=wsb)
+                               ws=wsb, summary=summ)
     want = [t.clone() for t in want[:6]]
     torch.cuda.synchronize()
 
@@ -72,9 +78,10 @@ def test_training_step_replays_in_a_graph():
     grads = tuple(torch.empty_like(t) for t in want) + (None,)
 
     def step():
-        B.slr_attention_fwd_train(inp.q, inp.k, inp.v, shape, rope, sparse, lowrank, ws=wsf, outs=outs)
+        B.slr_attention_fwd_train(inp.q, inp.k, inp.v, shape, rope, sparse, lowrank, ws=wsf, outs=outs,
+                                  summary=summ)
         B.slr_attention_bwd(inp.q, inp.k, inp.v, outs[1], outs[2], outs[3], dout, shape, rope, sparse, lowrank,
-                            ws=wsb, grads=grads)
+                            ws=wsb, grads=grads, summary=summ)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
