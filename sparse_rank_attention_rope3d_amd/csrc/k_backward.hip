@@ -1,4 +1,5 @@
-// Backward pass of the hybrid layer (per-head gate; bf16 on MFMA, fp32 on VALU).
+// Backward pass of the hybrid layer (either gate, every feature map; bf16 on
+// MFMA, fp32 on VALU).
 //
 // The pages fine-tune this layer (RoLA, arXiv 2609.06712v3, §4.4 and
 // App. E.2: the low-rank projections and the gate are trained), so its
@@ -21,10 +22,13 @@
 // (each pair turned by the opposite angle) in the epilogues, where the
 // low-rank parts are added.
 //
-// Low-rank branch (RoLA §4.1-4.3, App. A): per-token kernels and sums over
-// tokens, split along L with fixed-order reductions of the partial sums; on
-// bf16 MFMA for the per-head gate at rank 32 or 64 with D = 128, fp32 VALU
-// kernels for the other settings.
+// Low-rank branch (RoLA §4.1-4.3, App. A; RoPeSLR abstract and appendix):
+// per-token kernels and sums over tokens, split along L with fixed-order
+// reductions of the partial sums; on bf16 MFMA for the per-head gate at
+// ranks 8-64 with D = 128, fp32 VALU kernels for the other settings (the
+// token gate, D = 64, fp32 layers). elu + 1 and SiLU features are
+// elementwise; FAVOR+ features take their full Jacobian, du_c/dp =
+// u_c (omega_c - p).
 #include "slr_common.h"
 #include "slr_launch.h"
 #include "slr_backward.h"

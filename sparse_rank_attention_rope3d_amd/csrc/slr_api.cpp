@@ -198,7 +198,8 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
     }
     w.tiled = false;
     if (op == SLR_OP_ATTENTION_BWD) {
-        // rotated q, k (rows padded to whole blocks), the recomputed summary,
+        // rotated q, k (rows padded to whole blocks), the summary (recomputed when
+        // the caller does not pass the forward's),
         // per-row softmax statistics, the low-rank gradient parts and the
         // inverse of the kept lists
         const size_t rows = (size_t)nblk * bs;
