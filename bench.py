@@ -118,8 +118,43 @@ def achievable_peaks(torch) -> dict:
     torch.cuda.synchronize()
     copy_gbs = 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
-    return {"gemm_bf16_TFLOP/s": round(gemm_tf, 1), "copy_GB/s": round(copy_gbs, 1),
-            "what": "8192^3 bf16 torch.matmul on random operands; 1 GiB device copy, read + write bytes"}
+    out = {"gemm_bf16_TFLOP/s": round(gemm_tf, 1), "copy_GB/s": round(copy_gbs, 1),
+           "what": "8192^3 bf16 torch.matmul on random operands; 1 GiB device copy, read + write bytes"}
+    mf = mfma_loop_rate(torch)
+    if mf is not None:
+        out["mfma_loop_bf16_TFLOP/s"] = mf
+        out["what"] += ("; an MFMA-only loop (libslr_probe.so: eight independent 32x32x16 bf16 chains per wave on "
+                        "register operands of varying non-zero values)")
+    return out
+
+
+def mfma_loop_rate(torch):
+    """The bf16 MFMA issue rate with operands in registers (no memory, no
+    other instructions in the loop), at the clock the part holds under
+    that load."""
+    path = os.path.join(ROOT, "sparse_rank_attention_rope3d_amd", "libslr_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.slrprobe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.slrprobe_mfma_loop.restype = ctypes.c_int
+    nwg, iters = 2048, 2000
+    sink = torch.empty(nwg * 256, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    call = lambda: lib.slrprobe_mfma_loop(nwg, iters, ctypes.c_void_p(sink.data_ptr()), stream)
+    for _ in range(3):
+        assert call() == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        assert call() == 0
+    e1.record()
+    torch.cuda.synchronize()
+    flops = 32768.0 * 8 * iters * 4 * nwg * reps
+    del sink
+    return round(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
 
 
 def memory_read_probe(torch) -> dict:
@@ -379,22 +414,32 @@ def measure_forward(cfg, args, torch, B, hip, ach=None, dense_reps=0):
         fwd()
     torch.cuda.synchronize()
     print(f"[bench] {cfg.name}: timing {args.steps} steps", file=sys.stderr, flush=True)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # between timed calls a 512 MB buffer is written (outside the timed
+    # region), so no call starts with the previous call's data in the 256 MB
+    # memory-side cache
+    scrub = None if args.no_scrub else torch.empty(512 * 2 ** 20, dtype=torch.uint8, device="cuda")
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t0 = time.perf_counter()
-    ev[0].record()
     for i in range(args.steps):
+        ev0[i].record()
         fwd()
-        ev[i + 1].record()
+        ev1[i].record()
+        if scrub is not None:
+            scrub.fill_(i & 0xFF)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    step_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    step_ms = np.array([ev0[i].elapsed_time(ev1[i]) for i in range(args.steps)])
     wall_ms = (t1 - t0) * 1e3 / args.steps
     # stage times from the same number of staged calls (their event records
     # add a few microseconds between stages, so they are not the headline)
     events = [[_event(hip) for _ in range(5)] for _ in range(args.steps)]
     for i in range(args.steps):
         B.slr_attention_fwd_staged(q, k, v, shape, rope, sparse, lowrank, out, ws, events[i])
+        if scrub is not None:
+            scrub.fill_(i & 0xFF)
     torch.cuda.synchronize()
+    del scrub
     stage_names = ["rope_pool", "select", "lowrank_summary", "sparse_flash"]
     stages = {n: [] for n in stage_names}
     for evs in events:
@@ -442,7 +487,8 @@ def measure_forward(cfg, args, torch, B, hip, ach=None, dense_reps=0):
                    "parallelism": "single GPU"},
         "ms_per_layer": {"mean": round(ms_mean, 4), "median": round(float(np.median(step_ms)), 4),
                          "min": round(float(step_ms.min()), 4), "max": round(float(step_ms.max()), 4),
-                         "wall_clock_mean": round(wall_ms, 4), "steps": args.steps},
+                         ("wall_clock_mean" if args.no_scrub else "wall_clock_mean_incl_scrub"): round(wall_ms, 4),
+                         "steps": args.steps, "scrub_between_calls_MB": 0 if args.no_scrub else 512},
         "effective_TFLOP/s": round(f_total / (ms_mean * 1e-3) / 1e12, 2),
         "effective_TFLOP/s_at_median": round(f_total / (float(np.median(step_ms)) * 1e-3) / 1e12, 2),
         "dense_equivalent_TFLOP/s": round(F["dense"] / (ms_mean * 1e-3) / 1e12, 1),
@@ -463,6 +509,8 @@ def measure_forward(cfg, args, torch, B, hip, ach=None, dense_reps=0):
     }
     if ach:
         rec["roofline"]["frac_of_achievable_gemm"] = round(flash_tf / ach["gemm_bf16_TFLOP/s"], 4)
+        if "mfma_loop_bf16_TFLOP/s" in ach:
+            rec["roofline"]["frac_of_achievable_mfma"] = round(flash_tf / ach["mfma_loop_bf16_TFLOP/s"], 4)
     if dense_reps > 0:
         print(f"[bench] {cfg.name}: dense flash baseline", file=sys.stderr, flush=True)
         wsd = B.workspace(B.slr_workspace_bytes(B.SLR_OP_DENSE, shape, rope), "cuda")
@@ -536,6 +584,8 @@ def main() -> int:
                     help="headline workload (default: the Wan2.1-14B layer, L = 75600)")
     ap.add_argument("--sub", default="wan13b,hunyuan13b",
                     help="comma-separated workloads timed as sub-records ('' for none)")
+    ap.add_argument("--no-scrub", action="store_true",
+                    help="do not write the 512 MB scratch buffer between timed forward calls")
     ap.add_argument("--gate", default="head", choices=["head", "token"],
                     help="combine gate: one scalar per head (the workloads' default) or the token-wise gate")
     ap.add_argument("--fmap", default="elu1", choices=["elu1", "silu", "favor"],
@@ -610,6 +660,9 @@ def main() -> int:
         for rec in [head] + subs:
             rec["roofline"]["frac_of_achievable_gemm"] = round(rec["roofline"]["achieved"] / ach["gemm_bf16_TFLOP/s"],
                                                                4)
+            if "mfma_loop_bf16_TFLOP/s" in ach:
+                rec["roofline"]["frac_of_achievable_mfma"] = round(
+                    rec["roofline"]["achieved"] / ach["mfma_loop_bf16_TFLOP/s"], 4)
             for st in rec["hbm_stages"].values():
                 if isinstance(st, dict):
                     st["frac_of_copy"] = round(st["GB/s"] / ach["copy_GB/s"], 4)

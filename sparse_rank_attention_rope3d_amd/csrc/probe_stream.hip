@@ -1,7 +1,9 @@
-// Read-bandwidth probe of the memory hierarchy (a measurement utility of the
-// bench, built as its own small library, libslr_probe.so; not part of the
-// layer's ABI).
+// Probes of what the part sustains (a measurement utility of the bench, built
+// as its own small library, libslr_probe.so; not part of the layer's ABI):
+// the read bandwidth of the memory hierarchy, and the issue rate of the
+// 32x32x16 bf16 MFMA with operands in registers.
 //
+// Read bandwidth:
 // Each workgroup streams 16-byte vectors of a device buffer, `passes` times
 // over, either into registers (ordinary vector loads, folded into one value
 // per thread so none is dead) or straight into LDS with the direct
@@ -61,6 +63,49 @@ __global__ __launch_bounds__(256) void k_stream_read(const u32x4_t* __restrict__
     sink[(long)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// MFMA issue rate: each wave runs `iters` rounds of eight independent
+// 32x32x16 bf16 accumulation chains on register operands (non-zero bf16
+// values that vary by lane, so the multipliers toggle as on real data); the
+// accumulators are folded into one value per thread at the end so no chain
+// is dead. 32768 flops per MFMA.
+__global__ __launch_bounds__(256) void k_mfma_loop(int iters, float* __restrict__ sink) {
+    const uint32_t lane = threadIdx.x;
+    u32x4_t a[8], b[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // two bf16 values in [0.5, 2): exponent 126 or 127, mantissa from a hash
+            uint32_t h = (lane * 2654435761u) ^ ((uint32_t)(s * 4 + i) * 40503u) ^ (blockIdx.x * 97u);
+            h ^= h >> 13;
+            h *= 0x5bd1e995u;
+            const uint32_t lo = 0x3f00u | (h & 0xffu) | ((h >> 8) & 0x80u);
+            const uint32_t hi = 0x3f00u | ((h >> 16) & 0xffu) | ((h >> 24) & 0x80u);
+            a[s][i] = lo | (hi << 16);
+            b[s][i] = hi | (lo << 16);
+        }
+    f32x16_t c[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c[s][i] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            c[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(__attribute__((ext_vector_type(8))) __bf16, a[s]),
+                __builtin_bit_cast(__attribute__((ext_vector_type(8))) __bf16, b[s ^ 1]), c[s], 0, 0, 0);
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc += c[s][i];
+    sink[(long)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -80,6 +125,15 @@ int slrprobe_stream_read(const void* buf, size_t bytes, int passes, int to_lds, 
         hipLaunchKernelGGL(k_stream_read<true>, dim3(nwg), dim3(256), 0, s, (const u32x4_t*)buf, nvec, passes, sink);
     else
         hipLaunchKernelGGL(k_stream_read<false>, dim3(nwg), dim3(256), 0, s, (const u32x4_t*)buf, nvec, passes, sink);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// Launches the MFMA probe on `stream`: `nwg` workgroups of 256 threads, each
+// wave `iters` rounds of 8 MFMAs; sink receives nwg * 256 floats. Returns 0,
+// or -1 for bad arguments, -4 when the launch fails.
+int slrprobe_mfma_loop(int nwg, int iters, float* sink, void* stream) {
+    if (!sink || nwg < 1 || nwg > 65536 || iters < 1) return -1;
+    hipLaunchKernelGGL(k_mfma_loop, dim3(nwg), dim3(256), 0, (hipStream_t)stream, iters, sink);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
