@@ -2663,7 +2663,7 @@ static hipError_t bwd_lrm(bool key_side, const LrBwdArgs& a, long BH, hipStream_
 }
 
 hipError_t launch_bwd_lr(int dtype_bf16, int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st) {
-    if (lr_bwd_on_mfma(dtype_bf16, D, R, a.abspe != 0, a.token != 0)) {
+    if (lr_bwd_on_mfma(dtype_bf16, D, R, key_side, a.token != 0)) {
         if (!a.y1h || !a.y1l || !a.y2h || !a.y2l) return hipErrorInvalidValue;
         if (a.g.R != R || (a.g.fmap == 2 && !a.g.omega)) return hipErrorInvalidValue;
         if (a.abspe && !a.dpre) return hipErrorInvalidValue;

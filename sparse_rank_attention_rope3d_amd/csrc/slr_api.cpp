@@ -223,7 +223,7 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         int chunk, nsplit;
         lr_bwd_split(d, &chunk, &nsplit);
         w.lrpart = take(4ul * d.BH * nsplit * (2ul * d.D * R + R + 4));
-        if (lr_bwd_on_mfma(d.bf16, d.D, R, abspe, token)) w.lry = take(8ul * d.BH * d.L * R);
+        if (lr_bwd_key_on_mfma(d.bf16, d.D, R)) w.lry = take(8ul * d.BH * d.L * R);
         w.dsz = take(4ul * d.BH * ((size_t)R * d.D + R));
         if (abspe) {
             // per-token gradient of x W + E and the per-slice axis sums of it
@@ -774,7 +774,7 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     la.wg = lowrank->Wg; la.bg = lowrank->bg; la.o_sp = o_sparse;
     la.dosp = token ? at<void>(ws, w.dosp) : nullptr;
     la.gpart = token ? at<float>(ws, w.gpart) : nullptr;
-    if (lr_bwd_on_mfma(d.bf16, d.D, R, abspe, token)) {
+    if (lr_bwd_key_on_mfma(d.bf16, d.D, R)) {
         const size_t n = (size_t)d.BH * d.L * R;
         la.y1h = at<uint16_t>(ws, w.lry);
         la.y1l = la.y1h + n;

@@ -69,18 +69,22 @@ struct LrBwdArgs {
     const void* o_sp;                   // [BH][L][D] the forward's O_sparse (layer dtype)
     void* dosp;                         // [BH][L][D] (layer dtype): the sparse branch's upstream gradient
     float* gpart;                       // [BH][nsplit][D + 4]: dW_g, db_g partials
-    // MFMA path (lr_bwd_on_mfma): per-token rank vectors as bf16 hi + lo pairs, [BH][L][R] each:
+    // MFMA kernels (lr_bwd_on_mfma): per-token rank vectors as bf16 hi + lo pairs, [BH][L][R] each:
     // y1 = dpq (query side) or dpk (key side), y2 = fq g / n (query side)
     uint16_t *y1h, *y1l, *y2h, *y2l;
 };
 
-// The low-rank backward runs on MFMA for bf16 layers with D = 128, rank 8,
-// 16, 32 or 64 (8 and 16 padded to 32 with zero weights) and the per-head
-// gate (rotary or absolute-PE features); the token gate, fp32 layers and
-// D = 64 take the VALU kernels.
-inline bool lr_bwd_on_mfma(int dtype_bf16, long D, int R, bool abspe, bool token) {
-    (void)abspe;
-    return dtype_bf16 && D == 128 && (R == 8 || R == 16 || R == 32 || R == 64) && !token;
+// The low-rank backward runs on MFMA for bf16 layers with D = 128 and rank
+// 8, 16, 32 or 64 (8 and 16 padded to 32 with zero weights), rotary or
+// absolute-PE features, any feature map: both sides with the per-head gate;
+// with the token gate only the key side (the gate changes only the query
+// side's upstream gradient), the query side taking the VALU kernel. fp32
+// layers and D = 64 take the VALU kernels on both sides.
+inline bool lr_bwd_key_on_mfma(int dtype_bf16, long D, int R) {
+    return dtype_bf16 && D == 128 && (R == 8 || R == 16 || R == 32 || R == 64);
+}
+inline bool lr_bwd_on_mfma(int dtype_bf16, long D, int R, bool key_side, bool token) {
+    return lr_bwd_key_on_mfma(dtype_bf16, D, R) && (key_side || !token);
 }
 
 hipError_t launch_bwd_lr(int dtype_bf16, int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st);
