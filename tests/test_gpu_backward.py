@@ -353,6 +353,63 @@ def test_backward_favor_wan13b_sampled():
     _check(cfg, slices=[(0, 3), (1, 10)], qsample=2, ksample=2)
 
 
+@pytest.mark.timeout(600)
+def test_backward_token_gate_wan13b_sampled():
+    """RoLA's token gate at the full Wan2.1-1.3B shape (its query side on the
+    VALU kernel, the key side on MFMA). The gate reads each row's RMS of
+    O_sparse, so the oracle computes O_sparse for every row of head 0 in both
+    batches; dq is compared on sampled query blocks, dk and dv on sampled key
+    blocks, dW_q, dW_k, dW_g and db_g of head 0 summed over the batch."""
+    cfg = dataclasses.replace(synth.wan13b(), name="token gate wan13b", gate="token")
+    T.log(f"  case {cfg.name}: L={cfg.L} nblk={cfg.nblk} keep={cfg.keep} r={cfg.rank}")
+    _dtype[0] = cfg.dtype
+    inp, idx, (dq, dk, dv, dWq, dWk, (dWg, dbg), _), lse = _run_gpu(cfg)
+    p = inp.params_np
+    grid = (cfg.T, cfg.Hg, cfg.Wg)
+    h = 0
+    got = {n: [] for n in ("dq", "dk", "dv")}
+    want = {n: [] for n in ("dq", "dk", "dv")}
+    sums = {}
+    for b in range(cfg.B):
+        qs, ks, vs = synth.qkv_slice(cfg, b, h)
+        ig = idx[b, h].cpu().numpy()
+        res = oracle.layer_slice(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], 0.0, qblocks=[0], idx=ig)
+        T.check_selection(ig, res["scores"], res["thr"], cfg.keep)
+        qr, kr = res["q_rot"], res["k_rot"]
+        ds = np.asarray(synth.dout_slice(cfg, b, h), np.float64)
+        osp = oracle.block_sparse_attention(qr, kr, vs, cfg.block, ig).reshape(-1, cfg.D)[:cfg.L]
+        olr = OB.lowrank_bwd(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], np.zeros_like(ds))["o_lr"]
+        tg = OB.token_gate_bwd(qs, p["wg"][h], float(p["bg"][h]), osp, olr, cfg.eps, ds)
+        lr = OB.lowrank_bwd(cfg, qs, ks, vs, p["wq"][h], p["wk"][h], tg["d_olr"])
+        qb = synth.sample_query_blocks(cfg, b, h, 3)
+        kb = synth.sample_query_blocks(cfg, b, h + 1000, 3)
+        spq = OB.sparse_attention_bwd(qr, kr, vs, cfg.block, ig, tg["d_osp"], qblocks=qb, o=osp)
+        spk = OB.sparse_attention_bwd(qr, kr, vs, cfg.block, ig, tg["d_osp"], qblocks=OB.query_blocks_keeping(ig, kb),
+                                      o=osp)
+        ref = {
+            "dq": OB.rope3d_transpose(spq["dq"], grid, cfg.base, cfg.pairs) + lr["dq"] + tg["dq"],
+            "dk": OB.rope3d_transpose(spk["dk"], grid, cfg.base, cfg.pairs) + lr["dk"],
+            "dv": spk["dv"] + lr["dv"],
+        }
+        rq, rk = _rows(cfg, qb), _rows(cfg, kb)
+        got_l = T.to_host(lse[b, h])[rq]
+        want_l = OB.row_log2_normaliser(qr, kr, cfg.block, ig, qb)
+        err = float(np.abs(got_l - want_l).max())
+        T.log(f"    lse[{b},{h}]: max_abs={err:.3e}")
+        assert err <= 3e-2, f"saved log2 normaliser off by {err:.3e}"
+        for name, t, rows in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rk)):
+            got[name].append(T.to_host(t[b, h])[rows])
+            want[name].append(ref[name][rows])
+        for n, val in (("dWq", lr["dWq"]), ("dWk", lr["dWk"]), ("dWg", tg["dwg"]), ("dbg", tg["dbg"])):
+            sums[n] = sums.get(n, 0.0) + np.asarray(val)
+    for n in ("dq", "dk", "dv"):
+        _close(n, np.concatenate(got[n]), np.concatenate(want[n]))
+    _close("dWq[0]", T.to_host(dWq[h]), sums["dWq"])
+    _close("dWk[0]", T.to_host(dWk[h]), sums["dWk"])
+    _close("dWg[0]", T.to_host(dWg[h]), sums["dWg"])
+    _close("dbg[0]", T.to_host(dbg[h:h + 1]), np.atleast_1d(sums["dbg"]))
+
+
 def test_backward_wan14b_sampled():
     """Full Wan2.1-14B shape (1182 blocks, 119 kept: long kept and inverse
     lists through the two-slot rings of the streaming kernels): sampled rows
