@@ -459,7 +459,7 @@ def measure_forward(cfg, args, torch, B, hip, ach=None, dense_reps=0):
     BHLD = cfg.B * cfg.H * cfg.L * cfg.D
     rows_pad = cfg.B * cfg.H * cfg.nblk * cfg.block * cfg.D
     idx_bytes = 4 * cfg.B * cfg.H * cfg.nblk * cfg.keep
-    # algorithmic bytes (the survey's roofline table): rotate + pool + select
+    # algorithmic bytes of the HBM-bound stages: rotate + pool + select
     # read q, k and write the rotated q, k (+ the kept indices); the summary
     # reads k, v; the low-rank apply + combine is fused into the flash kernel
     k1_bytes = 4 * BHLD * es + idx_bytes
