@@ -395,6 +395,31 @@ def run_sweep(args, torch, B, synth):
     return 0
 
 
+def layer_roofline(cfg, F, es, ms) -> dict:
+    """Ideal layer time at the published peaks: for each stage the larger of
+    its algorithmic FLOPs at the bf16 MFMA peak and its algorithmic bytes at
+    the HBM peak, summed over rotate + pool + select (read q, k, write the
+    rotated copies and the kept indices), the low-rank summary (read k, v),
+    the sparse flash attention (F_sparse) and the low-rank apply + combine
+    (read q and O_sparse, write O; fused into the flash kernel here, counted
+    as its own stage so the ideal does not depend on the fusion); and the
+    measured time's fraction of it."""
+    BHLD = cfg.B * cfg.H * cfg.L * cfg.D
+    idx_bytes = 4 * cfg.B * cfg.H * cfg.nblk * cfg.keep
+    f_lr_half = 4.0 * cfg.B * cfg.H * cfg.L * cfg.rank * cfg.D
+    stages = {
+        "rotate_pool_select": (F["select"], 4 * BHLD * es + idx_bytes),
+        "lowrank_summary": (f_lr_half, 2 * BHLD * es),
+        "sparse_flash": (F["sparse"], 0),
+        "lowrank_apply_combine": (f_lr_half, 3 * BHLD * es),
+    }
+    terms = {n: max(f / (PEAK_BF16_TFLOPS * 1e12), b / (PEAK_HBM_GBS * 1e9)) * 1e3 for n, (f, b) in stages.items()}
+    ideal = sum(terms.values())
+    return {"ideal_ms": round(ideal, 4), "frac": round(ideal / ms, 4),
+            "stage_ideal_ms": {n: round(v, 4) for n, v in terms.items()},
+            "peaks": {"bf16_TFLOP/s": PEAK_BF16_TFLOPS, "hbm_GB/s": PEAK_HBM_GBS}}
+
+
 def measure_forward(cfg, args, torch, B, hip, ach=None, dense_reps=0):
     """Time the layer forward of one workload: per-step times (hipEvents on
     the stream the library launches on) over `args.steps` plain forward
@@ -506,6 +531,7 @@ def measure_forward(cfg, args, torch, B, hip, ach=None, dense_reps=0):
             "rotate_pool_kernel_own_traffic": hbm(own_bytes, stage_ms["rope_pool"]),
         },
         "select": {"TFLOP/s": round(F["select"] / (stage_ms["select"] * 1e-3) / 1e12, 2)},
+        "layer_roofline": layer_roofline(cfg, F, es, ms_mean),
     }
     if ach:
         rec["roofline"]["frac_of_achievable_gemm"] = round(flash_tf / ach["gemm_bf16_TFLOP/s"], 4)
