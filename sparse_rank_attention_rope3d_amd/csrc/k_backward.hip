@@ -447,6 +447,54 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiles(const uint16_t* __restrict
 // the K part by transposing reads. The two key halves' dQ^T are added through
 // LDS at the end. The tiled path scores with q pre-multiplied by
 // log2(e)/sqrt(D), so p = exp2(score - lse2).
+// Low-rank part of a streaming kernel's output rows, formed in its epilogue
+// instead of read back from fp32 copies: y[db] (the accumulator layout of the
+// wave's 32 rows: lane row l % 32, register i = dim 32db + 8(i/4) + 4hf + i%4)
+// = A x, with x the row's rank vector stored by the low-rank kernels (bf16
+// hi + lo at xh / xl + row * rv; in the slot16 order of a product over r,
+// lane half hf takes ranks 16ks + 4hf + 0..3 and 16ks + 8 + 4hf + 0..3 of
+// k-step ks) and A [128][R] given as operand blocks (block (db, ks) =
+// db * KS + ks, 64 lanes x 16 bytes, KS = R / 16; as k_bwd_lr_opblocks lays
+// them out): W rounded to bf16 (alo null), or dS^T as hi + lo parts (three
+// products), as the low-rank kernels form them. Called by the whole wave
+// (each lane supplies its A row); rows with valid false add zero.
+__device__ __forceinline__ void lr_rows_product(const u32x4_t* __restrict__ ahi, const u32x4_t* __restrict__ alo,
+                                                const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl,
+                                                long row, bool valid, int rv, int lane, int hf, f32x16_t* y) {
+    const int KS = rv <= 32 ? 2 : 4;   // rank padded to 32 or 64
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[db][i] = 0.f;
+#pragma unroll 1
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4_t bh = {0u, 0u, 0u, 0u}, bl = {0u, 0u, 0u, 0u};
+        const int r0 = 16 * ks + 4 * hf, r1 = r0 + 8;
+        if (valid && r0 < rv) {
+            const u32x2_t h = *reinterpret_cast<const u32x2_t*>(xh + row * rv + r0);
+            const u32x2_t l = *reinterpret_cast<const u32x2_t*>(xl + row * rv + r0);
+            bh[0] = h[0]; bh[1] = h[1]; bl[0] = l[0]; bl[1] = l[1];
+        }
+        if (valid && r1 < rv) {
+            const u32x2_t h = *reinterpret_cast<const u32x2_t*>(xh + row * rv + r1);
+            const u32x2_t l = *reinterpret_cast<const u32x2_t*>(xl + row * rv + r1);
+            bh[2] = h[0]; bh[3] = h[1]; bl[2] = l[0]; bl[3] = l[1];
+        }
+        u32x4_t wh[4], wl[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            wh[db] = ahi[(db * KS + ks) * 64 + lane];
+            wl[db] = alo ? alo[(db * KS + ks) * 64 + lane] : u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            y[db] = mfma32(wh[db], bh, y[db]);
+            y[db] = mfma32(wh[db], bl, y[db]);
+            if (alo) y[db] = mfma32(wl[db], bh, y[db]);
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* __restrict__ idx_all,
                                                       const uint16_t* __restrict__ tiles_all) {
     constexpr int D = 128, BS = 64, PART = kDqPart, PLOADS = PART * 2 / (256 * 16);
@@ -588,17 +636,24 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* 
             for (int i = 0; i < 16; ++i) mrg[(16 * db + i) * 64 + lane] = dqacc[db][i];
     }
     __syncthreads();
-    if (kh == 1 || !qval) return;
+    if (kh == 1) return;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) dqacc[db][i] += mrg[(16 * db + i) * 64 + lane];
+    // the low-rank part W_q dpq of the wave's rows (whole wave), unless it was stored in fp32
+    const bool fused = a.lr_ph != nullptr;
+    f32x16_t lrp[4];
+    if (fused)
+        lr_rows_product(reinterpret_cast<const u32x4_t*>(a.lr_w) + (bh % a.H) * (a.lr_rv <= 32 ? 512 : 1024), nullptr,
+                        a.lr_ph, a.lr_pl, bh * L + (qval ? qrow : 0), qval, a.lr_rv, lane, hf, lrp);
+    if (!qval) return;
 
     // ---- epilogue: dq = R^T (dQ_rot / sqrt(D)) + dq_lowrank; lane owns row qrow,
     // dims 32db + 8g4 + 4hf + 0..3
     int crd[3];
     token_coords(qrow, a.g.Hg, a.g.Wg, crd[0], crd[1], crd[2]);
-    const float* lr = a.dq_lr + (bh * L + qrow) * D;
+    const float* lr = fused ? nullptr : a.dq_lr + (bh * L + qrow) * D;
     uint16_t* out = a.dq + (bh * L + qrow) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -610,7 +665,9 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* 
             for (int i = 0; i < 4; ++i) y[i] = dqacc[db][4 * g4 + i] * a.scale;
             rot_t(y[0], y[1], rope_cs(a.tab, a.g, d0 >> 1, crd));
             rot_t(y[2], y[3], rope_cs(a.tab, a.g, (d0 >> 1) + 1, crd));
-            const float4 l4 = *reinterpret_cast<const float4*>(lr + d0);
+            const float4 l4 = fused ? make_float4(lrp[db][4 * g4], lrp[db][4 * g4 + 1], lrp[db][4 * g4 + 2],
+                                                  lrp[db][4 * g4 + 3])
+                                    : *reinterpret_cast<const float4*>(lr + d0);
             *reinterpret_cast<u32x2_t*>(out + d0) =
                 u32x2_t{pack_bf2(y[0] + l4.x, y[1] + l4.y), pack_bf2(y[2] + l4.z, y[3] + l4.w)};
         }
@@ -782,11 +839,27 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_tiled(BwdArgs a, const int32_t
             for (int i = 0; i < 16; ++i) mrg[(16 * db + i) * 64 + lane] = acc[db][i];
     }
     __syncthreads();
-    if (qh == 1 || !kval) return;
+    if (qh == 1) return;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] += mrg[(16 * db + i) * 64 + lane];
+    // the low-rank parts of the wave's keys (whole wave), unless they were stored in fp32:
+    // dS^T fk (dV waves), W_k dpk (dK waves)
+    const bool fused = a.lr_ph != nullptr;
+    f32x16_t lrp[4];
+    if (fused) {
+        const long krow = bh * L + (kval ? key : 0);
+        const long nb = a.lr_rv <= 32 ? 512 : 1024;   // 16-byte entries of one operand matrix
+        if (role == 0)
+            lr_rows_product(reinterpret_cast<const u32x4_t*>(a.lr_sh) + bh * nb,
+                            reinterpret_cast<const u32x4_t*>(a.lr_sl) + bh * nb, a.lr_fh, a.lr_fl, krow, kval, a.lr_rv,
+                            lane, hf, lrp);
+        else
+            lr_rows_product(reinterpret_cast<const u32x4_t*>(a.lr_w) + (bh % a.H) * nb, nullptr, a.lr_ph, a.lr_pl, krow,
+                            kval, a.lr_rv, lane, hf, lrp);
+    }
+    if (!kval) return;
 
     // ---- epilogue: dv = dV + dv_lowrank (dV waves); dk = R^T (kscale dK_rot) + dk_lowrank (dK
     // waves); lane owns key `key`, dims 32db + 8g4 + 4hf + 0..3
@@ -797,7 +870,9 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_tiled(BwdArgs a, const int32_t
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int d0 = 32 * db + 8 * g4 + 4 * hf;
-                const float4 vl = *reinterpret_cast<const float4*>(a.dv_lr + ro + d0);
+                const float4 vl = fused ? make_float4(lrp[db][4 * g4], lrp[db][4 * g4 + 1], lrp[db][4 * g4 + 2],
+                                                      lrp[db][4 * g4 + 3])
+                                        : *reinterpret_cast<const float4*>(a.dv_lr + ro + d0);
                 *reinterpret_cast<u32x2_t*>(a.dv + ro + d0) =
                     u32x2_t{pack_bf2(acc[db][4 * g4] + vl.x, acc[db][4 * g4 + 1] + vl.y),
                             pack_bf2(acc[db][4 * g4 + 2] + vl.z, acc[db][4 * g4 + 3] + vl.w)};
@@ -816,7 +891,9 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_tiled(BwdArgs a, const int32_t
             for (int i = 0; i < 4; ++i) y[i] = acc[db][4 * g4 + i] * a.kscale;
             rot_t(y[0], y[1], rope_cs(a.tab, a.g, d0 >> 1, crd));
             rot_t(y[2], y[3], rope_cs(a.tab, a.g, (d0 >> 1) + 1, crd));
-            const float4 kl = *reinterpret_cast<const float4*>(a.dk_lr + ro + d0);
+            const float4 kl = fused ? make_float4(lrp[db][4 * g4], lrp[db][4 * g4 + 1], lrp[db][4 * g4 + 2],
+                                                  lrp[db][4 * g4 + 3])
+                                    : *reinterpret_cast<const float4*>(a.dk_lr + ro + d0);
             *reinterpret_cast<u32x2_t*>(a.dk + ro + d0) =
                 u32x2_t{pack_bf2(y[0] + kl.x, y[1] + kl.y), pack_bf2(y[2] + kl.z, y[3] + kl.w)};
         }
@@ -2301,11 +2378,13 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_q(LrBwdArgs a) {
             // absolute PE: each token's gradient of q W_q + E (the query side's share of the E sums)
             if constexpr (ABSPE) lrm_store_dpre<NR, false>(sg, a.dpre + row * rv, hf, rv);
         }
-        // dq_lr = W_q dpq
-        u32x4_t bh_[KS], bl_[KS];
+        // dq_lr = W_q dpq (unless the streaming dQ kernel forms it from dpq)
+        if (a.dq_lr) {
+            u32x4_t bh_[KS], bl_[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) lrm_bop(sg[ks >> 1], ks & 1, bh_[ks], bl_[ks]);
-        lrm_apply_store<KS, false>(w_dr, nullptr, bh_, bl_, lane, a.dq_lr + row * D, hf, valid);
+            for (int ks = 0; ks < KS; ++ks) lrm_bop(sg[ks >> 1], ks & 1, bh_[ks], bl_[ks]);
+            lrm_apply_store<KS, false>(w_dr, nullptr, bh_, bl_, lane, a.dq_lr + row * D, hf, valid);
+        }
     }
     // workgroup sums: dz over the 32 tokens of each lane half, then the waves in order; dg
 #pragma unroll
@@ -2414,12 +2493,14 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
                     fk[rb][2 * j + 1] = !valid ? 0.f : ABSPE ? f1 : f0 * cs[rb][j].y + f1 * cs[rb][j].x;
                 }
         }
-        // dv_lr = dS^T fk
-        {
+        // dv_lr = dS^T fk, or fk stored for the streaming dK/dV kernel to form it
+        if (a.dv_lr) {
             u32x4_t bh_[KS], bl_[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) lrm_bop(fk[ks >> 1], ks & 1, bh_[ks], bl_[ks]);
             lrm_apply_store<KS, true>(s_dr_hi, s_dr_lo, bh_, bl_, lane, a.dv_lr + row * D, hf, valid);
+        } else if (valid) {
+            lrm_store_rank<NR>(fk, a.y2h + row * rv, a.y2l + row * rv, hf, rv);
         }
         // dpk = (rho^T(dS v) + dz) phi'
         f32x16_t sv[NR];
@@ -2456,11 +2537,13 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_k(LrBwdArgs a) {
             // absolute PE: adds the key side's share (the query side wrote its own first)
             if constexpr (ABSPE) lrm_store_dpre<NR, true>(sv, a.dpre + row * rv, hf, rv);
         }
-        // dk_lr = W_k dpk
-        u32x4_t bh_[KS], bl_[KS];
+        // dk_lr = W_k dpk (unless the streaming dK/dV kernel forms it from dpk)
+        if (a.dk_lr) {
+            u32x4_t bh_[KS], bl_[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) lrm_bop(sv[ks >> 1], ks & 1, bh_[ks], bl_[ks]);
-        lrm_apply_store<KS, false>(w_dr, nullptr, bh_, bl_, lane, a.dk_lr + row * D, hf, valid);
+            for (int ks = 0; ks < KS; ++ks) lrm_bop(sv[ks >> 1], ks & 1, bh_[ks], bl_[ks]);
+            lrm_apply_store<KS, false>(w_dr, nullptr, bh_, bl_, lane, a.dk_lr + row * D, hf, valid);
+        }
     }
 }
 
@@ -2567,6 +2650,27 @@ __global__ __launch_bounds__(256) void k_bwd_lrm_red(const uint16_t* __restrict_
 // the tokens of slice bh whose coordinate on `axis` is c, in a fixed order
 // (thread (j, r) takes every (256/R)-th such token from j, then the j's are
 // added in order).
+// Operand blocks of the streaming kernels' low-rank epilogue products, laid
+// out as the low-rank kernels hold them in LDS (lrm_build, A[row d][k = r],
+// R = 32 or 64 padded with zeros): W [D][rv] of each head rounded to bf16
+// (DS false), or dS^T of each slice as hi + lo parts (DS: dS [rv][D] at
+// src + g (rv D + rv)). Grid = matrices.
+template <int R, bool DS>
+__global__ __launch_bounds__(256) void k_bwd_lr_opblocks(const float* __restrict__ src, int rv, u32x4_t* __restrict__ hi,
+                                                         u32x4_t* __restrict__ lo) {
+    constexpr int D = 128, NB = R / 4 * 64;
+    const long g = blockIdx.x;
+    if constexpr (DS) {
+        const float* dS = src + g * (long)(rv * D + rv);
+        lrm_build<R, true, true>(hi + g * NB, lo + g * NB, [&](int r, int d) { return r < rv ? dS[r * D + d] : 0.f; },
+                                 (int)threadIdx.x);
+    } else {
+        const float* W = src + g * (long)D * rv;
+        lrm_build<R, true, false>(hi + g * NB, nullptr, [&](int r, int d) { return r < rv ? W[d * rv + r] : 0.f; },
+                                  (int)threadIdx.x);
+    }
+}
+
 __global__ __launch_bounds__(256) void k_bwd_e_sum(const float* __restrict__ dpre, long L, int Hg, int Wg, int axis,
                                                    int R, float* __restrict__ part) {
     __shared__ float red[256];
@@ -2684,6 +2788,21 @@ hipError_t launch_bwd_lr(int dtype_bf16, int D, int R, bool key_side, const LrBw
     if (dtype_bf16)
         return D == 64 ? bwd_lr_d<64, true>(R, key_side, a, BH, st) : bwd_lr_d<128, true>(R, key_side, a, BH, st);
     return D == 64 ? bwd_lr_d<64, false>(R, key_side, a, BH, st) : bwd_lr_d<128, false>(R, key_side, a, BH, st);
+}
+
+hipError_t launch_bwd_lr_opblocks(bool ds, int rv, const float* src, long n, uint16_t* hi, uint16_t* lo,
+                                  hipStream_t st) {
+    u32x4_t* h = reinterpret_cast<u32x4_t*>(hi);
+    u32x4_t* l = reinterpret_cast<u32x4_t*>(lo);
+    const dim3 grid((unsigned)n);
+    if (rv <= 32) {
+        if (ds) hipLaunchKernelGGL((k_bwd_lr_opblocks<32, true>), grid, dim3(256), 0, st, src, rv, h, l);
+        else hipLaunchKernelGGL((k_bwd_lr_opblocks<32, false>), grid, dim3(256), 0, st, src, rv, h, l);
+    } else {
+        if (ds) hipLaunchKernelGGL((k_bwd_lr_opblocks<64, true>), grid, dim3(256), 0, st, src, rv, h, l);
+        else hipLaunchKernelGGL((k_bwd_lr_opblocks<64, false>), grid, dim3(256), 0, st, src, rv, h, l);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_bwd_sum_parts(const float* part, int B, int H, int nsplit, long stride, long off, long n,

@@ -161,6 +161,7 @@ struct Layout {
     size_t tab, qr, kr, kvt, qbar, kbar, scores, idx, wqt, wkt, part, S, z, sthi, stlo, zp, total;
     // FAVOR+ (bf16 layers): (W omega^T)^T hi/lo parts of both sides, the projected axis tables
     size_t wqo_hi, wqo_lo, wko_hi, wko_lo, eo;
+    size_t opwq, opwk, opsh, opsl;   // backward: operand blocks of the fused low-rank products
     // backward
     size_t lse, delta, dqlr, dklr, dvlr, lrpart, dsz, bits, cnt, off, list, order, dpre, epart, dosp, gpart, dqt, qtt;
     size_t lry;   // MFMA low-rank backward: 4 bf16 [BH][L][R] per-token rank vectors
@@ -217,9 +218,19 @@ Layout layout(int op, const Dims& d, const RopeGeom& g, int bs, int nblk, int ke
         w.z = take(4ul * d.BH * R);
         w.lse = take(4ul * d.BH * rows);
         w.delta = take(4ul * d.BH * rows);
-        w.dqlr = take(4ul * d.BH * d.L * d.D);
-        w.dklr = take(4ul * d.BH * d.L * d.D);
-        w.dvlr = take(4ul * d.BH * d.L * d.D);
+        // fp32 low-rank gradient parts, unless the streaming sparse kernels form them
+        if (!lr_fused_in_sparse(use_tiles(d, bs), d.bf16, d.D, R, false, token)) w.dqlr = take(4ul * d.BH * d.L * d.D);
+        if (!lr_fused_in_sparse(use_tiles(d, bs), d.bf16, d.D, R, true, token)) {
+            w.dklr = take(4ul * d.BH * d.L * d.D);
+            w.dvlr = take(4ul * d.BH * d.L * d.D);
+        }
+        if (lr_fused_in_sparse(use_tiles(d, bs), d.bf16, d.D, R, true, token)) {
+            // operand blocks of the fused products: W_q, W_k per head; dS^T hi, lo per slice
+            w.opwq = take(kBwdLrOpBytes(R) * d.H);
+            w.opwk = take(kBwdLrOpBytes(R) * d.H);
+            w.opsh = take(kBwdLrOpBytes(R) * d.BH);
+            w.opsl = take(kBwdLrOpBytes(R) * d.BH);
+        }
         int chunk, nsplit;
         lr_bwd_split(d, &chunk, &nsplit);
         w.lrpart = take(4ul * d.BH * nsplit * (2ul * d.D * R + R + 4));
@@ -765,7 +776,13 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     la.dSz = dsz;
     la.tab = tab; la.g = lg; la.eps = lowrank->eps; la.L = d.L; la.H = (int)d.H;
     lr_bwd_split(d, &la.chunk, &la.nsplit);
-    la.dq_lr = at<float>(ws, w.dqlr); la.dk_lr = at<float>(ws, w.dklr); la.dv_lr = at<float>(ws, w.dvlr);
+    // the streaming dQ (dK/dV) kernel forms the low-rank part of its rows itself when that side
+    // runs on the MFMA low-rank kernels; they then store only the rank vectors
+    const bool fuse_q = lr_fused_in_sparse(tiled_fwd, d.bf16, d.D, R, false, token);
+    const bool fuse_k = lr_fused_in_sparse(tiled_fwd, d.bf16, d.D, R, true, token);
+    la.dq_lr = fuse_q ? nullptr : at<float>(ws, w.dqlr);
+    la.dk_lr = fuse_k ? nullptr : at<float>(ws, w.dklr);
+    la.dv_lr = fuse_k ? nullptr : at<float>(ws, w.dvlr);
     la.part = at<float>(ws, w.lrpart);
     la.abspe = abspe ? 1 : 0;
     la.Et = lowrank->Et; la.Eh = lowrank->Eh; la.Ew = lowrank->Ew;
@@ -795,20 +812,8 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
         SLR_TRY(launch_bwd_sum_parts(la.gpart, (int)d.B, (int)d.H, la.nsplit, d.D + 4, 0, d.D, true, dWg, s));
         SLR_TRY(launch_bwd_sum_parts(la.gpart, (int)d.B, (int)d.H, la.nsplit, d.D + 4, d.D, 1, true, dbg, s));
     }
-    SLR_TRY(launch_bwd_lr(d.bf16, (int)d.D, R, true, la, d.BH, s));
-    SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, d.D * R, 0, d.D * R, true, dWk, s));
-    if (abspe) {
-        // E tables: per-axis sums of the per-token gradient, per slice, then over the slices
-        float* ep = at<float>(ws, w.epart);
-        const int na[3] = {d.T, d.Hg, d.Wg};
-        float* outs[3] = {dEt, dEh, dEw};
-        for (int ax = 0; ax < 3; ++ax) {
-            SLR_TRY(launch_bwd_e_sum(la.dpre, d.BH, d.L, d.T, d.Hg, d.Wg, ax, R, ep, s));
-            SLR_TRY(launch_bwd_sum_parts(ep, (int)d.BH, 1, 1, (long)na[ax] * R, 0, (long)na[ax] * R, true, outs[ax], s));
-        }
-    }
-
-    // sparse branch: dQ (and the row statistics), the inverse lists, dK and dV
+    // sparse branch, dQ first (and the row statistics): with fuse_q it forms W_q dpq from the
+    // query side's rank vectors, which the key side's overwrite next
     BwdArgs a;
     std::memset(&a, 0, sizeof(a));
     a.qr = qr; a.kr = kr; a.v = (const uint16_t*)v; a.o_sp = (const uint16_t*)o_sparse;
@@ -823,6 +828,13 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
     a.tab = tab; a.g = g; a.L = d.L; a.nblk = nblk; a.keep = keep;
     a.scale = (float)(1.0 / std::sqrt((double)d.D));
     a.nwg = d.BH * nblk;
+    a.lr_rv = R; a.H = (int)d.H;
+    if (fuse_q) {
+        a.lr_ph = la.y1h; a.lr_pl = la.y1l;
+        uint16_t* opw = at<uint16_t>(ws, w.opwq);
+        SLR_TRY(launch_bwd_lr_opblocks(false, R, lowrank->Wq, d.H, opw, nullptr, s));
+        a.lr_w = opw;
+    }
     if (tiled_fwd) {
         uint16_t* dqt = at<uint16_t>(ws, w.dqt);
         SLR_TRY(launch_bwd_dq_tiles(kr, (const uint16_t*)v, d.BH, d.L, nblk, dqt, s));
@@ -830,6 +842,32 @@ int slr_attention_bwd(const slr_shape* shape, const slr_rope_cfg* rope, const sl
         a.qtt = at<uint16_t>(ws, w.qtt);   // written by the dQ kernel for the dK/dV kernel
     }
     SLR_TRY(launch_bwd_dq(d.bf16, (int)d.D, bs, a, s));
+
+    // low-rank key side (with fuse_k it stores dpk and fk for the dK/dV kernel), its sums
+    SLR_TRY(launch_bwd_lr(d.bf16, (int)d.D, R, true, la, d.BH, s));
+    SLR_TRY(launch_bwd_sum_parts(la.part, (int)d.B, (int)d.H, la.nsplit, d.D * R, 0, d.D * R, true, dWk, s));
+    if (abspe) {
+        // E tables: per-axis sums of the per-token gradient, per slice, then over the slices
+        float* ep = at<float>(ws, w.epart);
+        const int na[3] = {d.T, d.Hg, d.Wg};
+        float* outs[3] = {dEt, dEh, dEw};
+        for (int ax = 0; ax < 3; ++ax) {
+            SLR_TRY(launch_bwd_e_sum(la.dpre, d.BH, d.L, d.T, d.Hg, d.Wg, ax, R, ep, s));
+            SLR_TRY(launch_bwd_sum_parts(ep, (int)d.BH, 1, 1, (long)na[ax] * R, 0, (long)na[ax] * R, true, outs[ax], s));
+        }
+    }
+
+    // the inverse lists, dK and dV
+    a.lr_ph = a.lr_pl = a.lr_fh = a.lr_fl = a.lr_w = a.lr_sh = a.lr_sl = nullptr;
+    if (fuse_k) {
+        a.lr_ph = la.y1h; a.lr_pl = la.y1l; a.lr_fh = la.y2h; a.lr_fl = la.y2l;
+        uint16_t* opw = at<uint16_t>(ws, w.opwk);
+        uint16_t* osh = at<uint16_t>(ws, w.opsh);
+        uint16_t* osl = at<uint16_t>(ws, w.opsl);
+        SLR_TRY(launch_bwd_lr_opblocks(false, R, lowrank->Wk, d.H, opw, nullptr, s));
+        SLR_TRY(launch_bwd_lr_opblocks(true, R, dsz, d.BH, osh, osl, s));
+        a.lr_w = opw; a.lr_sh = osh; a.lr_sl = osl;
+    }
     a.order = at<int32_t>(ws, w.order);
     SLR_TRY(launch_bwd_inverse(idx, d.BH, nblk, keep, at<uint32_t>(ws, w.bits), at<int32_t>(ws, w.cnt),
                                at<int32_t>(ws, w.off), at<int32_t>(ws, w.list), at<int32_t>(ws, w.order), s));

@@ -33,9 +33,17 @@ struct BwdArgs {
                                // when q_rot already carries that factor
     float kscale;              // dk_rot = kscale * sum dS q_rot: 1/sqrt(D), or ln 2 for scaled q
     float* delta;              // [BH][nblk*BS] dO . O_sparse per row
-    const float* dq_lr;        // [BH][L][D] low-rank parts of the gradients (fp32)
-    const float* dk_lr;
+    const float* dq_lr;        // [BH][L][D] low-rank parts of the gradients (fp32), read when the
+    const float* dk_lr;        // streaming kernel does not form them itself (lr_ph null)
     const float* dv_lr;
+    // Streaming kernels (dqt / qtt set): the low-rank parts formed in the epilogue from the
+    // per-token rank vectors the MFMA low-rank kernels stored (bf16 hi + lo, [BH][L][lr_rv]):
+    // dq_lr = W_q dpq (dQ kernel), dk_lr = W_k dpk and dv_lr = dS^T fk (dK/dV kernel).
+    const uint16_t *lr_ph, *lr_pl;   // dpq or dpk (null: read dq_lr / dk_lr, dv_lr)
+    const uint16_t *lr_fh, *lr_fl;   // fk (dK/dV kernel)
+    const uint16_t* lr_w;            // [H] operand blocks of W_q or W_k (launch_bwd_lr_opblocks)
+    const uint16_t *lr_sh, *lr_sl;   // [BH] operand blocks of dS^T, hi and lo (dK/dV kernel)
+    int lr_rv, H;
     uint16_t* dq;              // [BH][L][D] outputs
     uint16_t* dk;
     uint16_t* dv;
@@ -59,7 +67,8 @@ struct LrBwdArgs {
     float eps;
     long L;
     int H, chunk, nsplit;
-    float *dq_lr, *dk_lr, *dv_lr;       // [BH][L][D]
+    float *dq_lr, *dk_lr, *dv_lr;       // [BH][L][D] (MFMA kernels: null when the streaming
+                                        // sparse kernels form them; the key side then stores fk in y2)
     float* part;                        // split partials
     int abspe;                          // absolute-PE variant: E added before phi, no rotation
     const float *Et, *Eh, *Ew;          // [T|Hg|Wg][R] (absolute PE)
@@ -87,7 +96,20 @@ inline bool lr_bwd_on_mfma(int dtype_bf16, long D, int R, bool key_side, bool to
     return lr_bwd_key_on_mfma(dtype_bf16, D, R) && (key_side || !token);
 }
 
+// The streaming dQ (dK/dV) kernel forms the low-rank part itself when its
+// side of the low-rank backward runs on MFMA (whose kernels then store only
+// the rank vectors, not the [B,H,L,D] fp32 parts).
+inline bool lr_fused_in_sparse(bool tiled, int dtype_bf16, long D, int R, bool key_side, bool token) {
+    return tiled && lr_bwd_on_mfma(dtype_bf16, D, R, key_side, token);
+}
+
 hipError_t launch_bwd_lr(int dtype_bf16, int D, int R, bool key_side, const LrBwdArgs& a, long BH, hipStream_t st);
+// Operand blocks of the streaming kernels' low-rank products (bf16, D = 128, rank padded to 32
+// or 64: kBwdLrOpBytes(rv) bytes per matrix): n heads' W [D][rv] (ds false; lo unused) or n
+// slices' dS^T from the reduced [rv*D + rv] records (ds: hi and lo parts); grid n.
+constexpr size_t kBwdLrOpBytes(int rv) { return (rv <= 32 ? 512ul : 1024ul) * 16; }
+hipError_t launch_bwd_lr_opblocks(bool ds, int rv, const float* src, long n, uint16_t* hi, uint16_t* lo,
+                                  hipStream_t st);
 // out[o][e] = sum over (b < nb, split < nsplit) of part[((b*H + h)*nsplit + split)*stride + off + e]:
 // per_head sums the batches into [H][n], else [BH][n] (nb = 1, h = slice).
 hipError_t launch_bwd_sum_parts(const float* part, int B, int H, int nsplit, long stride, long off, long n,

@@ -180,6 +180,13 @@ def test_other_entry_points_validate():
 GIB = 2 ** 30   # the [B,H,L,D] fakes below sit 1 GiB apart: their byte ranges do not overlap
 
 
+def ctypes_copy(st):
+    """A field-by-field copy of a ctypes structure."""
+    out = type(st)()
+    ctypes.pointer(out)[0] = st
+    return out
+
+
 def _bwd(shape, rope, sparse, lr, q=FAKE, k=FAKE + GIB, v=FAKE + 2 * GIB, idx=FAKE + 8 * GIB + 0x3000,
          osp=FAKE + 3 * GIB, lse=FAKE + 8 * GIB + 0xc000, S=None, z=None, dout=FAKE + 4 * GIB, dq=FAKE + 5 * GIB,
          dk=FAKE + 6 * GIB,
@@ -195,8 +202,14 @@ def test_backward_validates_before_launching():
     shape, rope, sparse, lr = _cfgs()
     need = B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, lr)
     layer = synth.wan13b()
-    # rotated q, k plus three fp32 low-rank gradient parts
-    assert need > (2 * 2 + 3 * 4) * layer.B * layer.H * layer.L * layer.D
+    bhld = layer.B * layer.H * layer.L * layer.D
+    # rotated q, k; no fp32 low-rank gradient parts: the streaming dQ and dK/dV
+    # kernels form them from the MFMA low-rank kernels' rank vectors
+    assert 2 * 2 * bhld < need < (2 * 2 + 3 * 4) * bhld
+    # the token gate's query side runs on the VALU kernel, which stores dq_lr in fp32
+    tok = ctypes_copy(lr)
+    tok.gate_mode, tok.gate, tok.Wg, tok.bg = B.SLR_GATE_TOKEN, None, FAKE, FAKE
+    assert B.slr_workspace_bytes(B.SLR_OP_ATTENTION_BWD, shape, rope, sparse, tok) > need + 4 * bhld
     assert _bwd(shape, rope, sparse, lr) == B.SLR_EWORKSPACE
     assert _bwd(shape, rope, sparse, lr, ws=FAKE, ws_bytes=need - 1) == B.SLR_EWORKSPACE
     for bad in ("q", "osp", "lse", "dout", "dq", "dv", "dwq", "dg"):
