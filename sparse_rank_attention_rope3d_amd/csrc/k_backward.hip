@@ -439,14 +439,6 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiles(const uint16_t* __restrict
     }
 }
 
-// Workgroup = 4 waves = one 64-row query block; wave (rh, kh) owns query rows
-// 32rh .. and keys 32kh .. of every kept tile: S^T = K Q^T and dP^T = V dO^T
-// (a lane owns one query row), dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.
-// The tiles stream through a two-slot LDS ring (64 KB: two workgroups per
-// CU), each requested one tile ahead, one barrier per tile; K^T comes from
-// the K part by transposing reads. The two key halves' dQ^T are added through
-// LDS at the end. The tiled path scores with q pre-multiplied by
-// log2(e)/sqrt(D), so p = exp2(score - lse2).
 // Low-rank part of a streaming kernel's output rows, formed in its epilogue
 // instead of read back from fp32 copies: y[db] (the accumulator layout of the
 // wave's 32 rows: lane row l % 32, register i = dim 32db + 8(i/4) + 4hf + i%4)
@@ -456,45 +448,79 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiles(const uint16_t* __restrict
 // k-step ks) and A [128][R] given as operand blocks (block (db, ks) =
 // db * KS + ks, 64 lanes x 16 bytes, KS = R / 16; as k_bwd_lr_opblocks lays
 // them out): W rounded to bf16 (alo null), or dS^T as hi + lo parts (three
-// products), as the low-rank kernels form them. Called by the whole wave
-// (each lane supplies its A row); rows with valid false add zero.
-__device__ __forceinline__ void lr_rows_product(const u32x4_t* __restrict__ ahi, const u32x4_t* __restrict__ alo,
-                                                const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl,
-                                                long row, bool valid, int rv, int lane, int hf, f32x16_t* y) {
-    const int KS = rv <= 32 ? 2 : 4;   // rank padded to 32 or 64
+// products), as the low-rank kernels form them. Run by the whole wave (each
+// lane supplies its A row); rows with valid false add zero. The operands of
+// two k-steps are loaded together (LrOps), so that a kernel can request the
+// first pair before the barriers of its partial-sum merge and the load
+// latency overlaps them.
+struct LrOps {
+    u32x4_t bh[2], bl[2], wh[2][4], wl[2][4];   // wl used only with the lo part (LO)
+};
+struct LrSrc {
+    const u32x4_t* ahi;
+    const u32x4_t* alo;
+    const uint16_t* xh;
+    const uint16_t* xl;
+    long row;
+    bool valid;
+    int rv;
+};
+template <bool LO>
+__device__ __forceinline__ void lr_rows_load(const LrSrc& src, int ks0, int lane, int hf, LrOps& o) {
+    const int KS = src.rv <= 32 ? 2 : 4;   // rank padded to 32 or 64
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) y[db][i] = 0.f;
-#pragma unroll 1
-    for (int ks = 0; ks < KS; ++ks) {
-        u32x4_t bh = {0u, 0u, 0u, 0u}, bl = {0u, 0u, 0u, 0u};
+    for (int k = 0; k < 2; ++k) {
+        const int ks = ks0 + k;
+        o.bh[k] = u32x4_t{0u, 0u, 0u, 0u};
+        o.bl[k] = u32x4_t{0u, 0u, 0u, 0u};
         const int r0 = 16 * ks + 4 * hf, r1 = r0 + 8;
-        if (valid && r0 < rv) {
-            const u32x2_t h = *reinterpret_cast<const u32x2_t*>(xh + row * rv + r0);
-            const u32x2_t l = *reinterpret_cast<const u32x2_t*>(xl + row * rv + r0);
-            bh[0] = h[0]; bh[1] = h[1]; bl[0] = l[0]; bl[1] = l[1];
+        if (src.valid && r0 < src.rv) {
+            const u32x2_t h = *reinterpret_cast<const u32x2_t*>(src.xh + src.row * src.rv + r0);
+            const u32x2_t l = *reinterpret_cast<const u32x2_t*>(src.xl + src.row * src.rv + r0);
+            o.bh[k][0] = h[0]; o.bh[k][1] = h[1]; o.bl[k][0] = l[0]; o.bl[k][1] = l[1];
         }
-        if (valid && r1 < rv) {
-            const u32x2_t h = *reinterpret_cast<const u32x2_t*>(xh + row * rv + r1);
-            const u32x2_t l = *reinterpret_cast<const u32x2_t*>(xl + row * rv + r1);
-            bh[2] = h[0]; bh[3] = h[1]; bl[2] = l[0]; bl[3] = l[1];
-        }
-        u32x4_t wh[4], wl[4];
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            wh[db] = ahi[(db * KS + ks) * 64 + lane];
-            wl[db] = alo ? alo[(db * KS + ks) * 64 + lane] : u32x4_t{0u, 0u, 0u, 0u};
+        if (src.valid && r1 < src.rv) {
+            const u32x2_t h = *reinterpret_cast<const u32x2_t*>(src.xh + src.row * src.rv + r1);
+            const u32x2_t l = *reinterpret_cast<const u32x2_t*>(src.xl + src.row * src.rv + r1);
+            o.bh[k][2] = h[0]; o.bh[k][3] = h[1]; o.bl[k][2] = l[0]; o.bl[k][3] = l[1];
         }
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-            y[db] = mfma32(wh[db], bh, y[db]);
-            y[db] = mfma32(wh[db], bl, y[db]);
-            if (alo) y[db] = mfma32(wl[db], bh, y[db]);
+            o.wh[k][db] = src.ahi[(db * KS + ks) * 64 + lane];
+            if (LO) o.wl[k][db] = src.alo[(db * KS + ks) * 64 + lane];
         }
     }
 }
+template <bool LO>
+__device__ __forceinline__ void lr_rows_mfma(const LrOps& o, f32x16_t* y) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            y[db] = mfma32(o.wh[k][db], o.bh[k], y[db]);
+            y[db] = mfma32(o.wh[k][db], o.bl[k], y[db]);
+            if (LO) y[db] = mfma32(o.wl[k][db], o.bh[k], y[db]);
+        }
+}
+// Adds the product to y given the operands of k-steps 0 and 1 (loaded by the
+// caller); loads the rest at rank 64.
+template <bool LO>
+__device__ __forceinline__ void lr_rows_finish(const LrSrc& src, LrOps& o, int lane, int hf, f32x16_t* y) {
+    lr_rows_mfma<LO>(o, y);
+    if (src.rv > 32) {
+        lr_rows_load<LO>(src, 2, lane, hf, o);
+        lr_rows_mfma<LO>(o, y);
+    }
+}
 
+// Workgroup = 4 waves = one 64-row query block; wave (rh, kh) owns query rows
+// 32rh .. and keys 32kh .. of every kept tile: S^T = K Q^T and dP^T = V dO^T
+// (a lane owns one query row), dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.
+// The tiles stream through a two-slot LDS ring (64 KB: two workgroups per
+// CU), each requested one tile ahead, one barrier per tile; K^T comes from
+// the K part by transposing reads. The two key halves' dQ^T are added through
+// LDS at the end. The tiled path scores with q pre-multiplied by
+// log2(e)/sqrt(D), so p = exp2(score - lse2).
 __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* __restrict__ idx_all,
                                                       const uint16_t* __restrict__ tiles_all) {
     constexpr int D = 128, BS = 64, PART = kDqPart, PLOADS = PART * 2 / (256 * 16);
@@ -626,6 +652,14 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* 
         for (int i = 0; i < 8; ++i) dqacc[i >> 1] = mfma32(at[i], dsop[i & 1], dqacc[i >> 1]);
     }
 
+    // the low-rank part W_q dpq of the wave's rows, unless it was stored in fp32: the key-half-0
+    // waves request its first operands now (whole wave)
+    const bool fused = a.lr_ph != nullptr;
+    const LrSrc lrs{reinterpret_cast<const u32x4_t*>(a.lr_w) + (bh % a.H) * (a.lr_rv <= 32 ? 512 : 1024), nullptr,
+                    a.lr_ph, a.lr_pl, bh * L + (qval ? qrow : 0), qval, a.lr_rv};
+    LrOps lro;
+    if (fused && kh == 0) lr_rows_load<false>(lrs, 0, lane, hf, lro);
+
     // ---- add the key halves through LDS (no copy is in flight: the last tile waited for all)
     __syncthreads();
     float* mrg = reinterpret_cast<float*>(lds) + rh * (64 * 64);
@@ -641,12 +675,14 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* 
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) dqacc[db][i] += mrg[(16 * db + i) * 64 + lane];
-    // the low-rank part W_q dpq of the wave's rows (whole wave), unless it was stored in fp32
-    const bool fused = a.lr_ph != nullptr;
     f32x16_t lrp[4];
-    if (fused)
-        lr_rows_product(reinterpret_cast<const u32x4_t*>(a.lr_w) + (bh % a.H) * (a.lr_rv <= 32 ? 512 : 1024), nullptr,
-                        a.lr_ph, a.lr_pl, bh * L + (qval ? qrow : 0), qval, a.lr_rv, lane, hf, lrp);
+    if (fused) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) lrp[db][i] = 0.f;
+        lr_rows_finish<false>(lrs, lro, lane, hf, lrp);
+    }
     if (!qval) return;
 
     // ---- epilogue: dq = R^T (dQ_rot / sqrt(D)) + dq_lowrank; lane owns row qrow,
@@ -778,6 +814,94 @@ __device__ __forceinline__ void dkdv_tiled_loop(const BwdArgs& a, uint16_t* lds,
     }
 }
 
+// The end of k_bwd_dkdv_tiled for the waves of one role: the query halves'
+// partial sums added through LDS, then dv = dV + dv_lowrank (dV waves) or
+// dk = R^T (kscale dK_rot) + dk_lowrank (dK waves); the lane owns key `key`,
+// dims 32db + 8g4 + 4hf + 0..3. The low-rank part (unless it was stored in
+// fp32) is dS^T fk, accumulated onto dV by the MFMAs, or W_k dpk; the
+// query-half-0 waves request the operands of its first two k-steps before
+// the merge, so that their latency overlaps it.
+template <int ROLE>
+__device__ __forceinline__ void dkdv_tiled_tail(const BwdArgs& a, uint16_t* lds, f32x16_t* acc, long bh, long key,
+                                                bool kval, int kw, int qh, int lane, int hf) {
+    constexpr int D = 128;
+    const long L = a.L;
+    const bool fused = a.lr_ph != nullptr;
+    const long nb = a.lr_rv <= 32 ? 512 : 1024;   // 16-byte entries of one operand matrix
+    const long lrow = bh * L + (kval ? key : 0);
+    const LrSrc lrs = ROLE == 0 ? LrSrc{reinterpret_cast<const u32x4_t*>(a.lr_sh) + bh * nb,
+                                        reinterpret_cast<const u32x4_t*>(a.lr_sl) + bh * nb, a.lr_fh, a.lr_fl,
+                                        lrow, kval, a.lr_rv}
+                                : LrSrc{reinterpret_cast<const u32x4_t*>(a.lr_w) + (bh % a.H) * nb, nullptr, a.lr_ph,
+                                        a.lr_pl, lrow, kval, a.lr_rv};
+    LrOps lro;
+    if (fused && qh == 0) lr_rows_load<ROLE == 0>(lrs, 0, lane, hf, lro);
+
+    // ---- add the query halves through LDS (no copy is in flight: the last tile waited for all)
+    __syncthreads();
+    float* mrg = reinterpret_cast<float*>(lds) + (ROLE * 2 + kw) * (64 * 64);
+    if (qh == 1) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mrg[(16 * db + i) * 64 + lane] = acc[db][i];
+    }
+    __syncthreads();
+    if (qh == 1) return;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] += mrg[(16 * db + i) * 64 + lane];
+
+    const long ro = (bh * L + key) * D;
+    if (ROLE == 0) {
+        if (fused) lr_rows_finish<true>(lrs, lro, lane, hf, acc);   // whole wave
+        if (!kval) return;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = 32 * db + 8 * g4 + 4 * hf;
+                float y[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] = acc[db][4 * g4 + i];
+                if (!fused) {
+                    const float4 vl = *reinterpret_cast<const float4*>(a.dv_lr + ro + d0);
+                    y[0] += vl.x; y[1] += vl.y; y[2] += vl.z; y[3] += vl.w;
+                }
+                *reinterpret_cast<u32x2_t*>(a.dv + ro + d0) = u32x2_t{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])};
+            }
+        return;
+    }
+    f32x16_t lrp[4];
+    if (fused) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) lrp[db][i] = 0.f;
+        lr_rows_finish<false>(lrs, lro, lane, hf, lrp);   // whole wave
+    }
+    if (!kval) return;
+    int crd[3];
+    token_coords(key, a.g.Hg, a.g.Wg, crd[0], crd[1], crd[2]);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int d0 = 32 * db + 8 * g4 + 4 * hf;
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = acc[db][4 * g4 + i] * a.kscale;
+            rot_t(y[0], y[1], rope_cs(a.tab, a.g, d0 >> 1, crd));
+            rot_t(y[2], y[3], rope_cs(a.tab, a.g, (d0 >> 1) + 1, crd));
+            const float4 kl = fused ? make_float4(lrp[db][4 * g4], lrp[db][4 * g4 + 1], lrp[db][4 * g4 + 2],
+                                                  lrp[db][4 * g4 + 3])
+                                    : *reinterpret_cast<const float4*>(a.dk_lr + ro + d0);
+            *reinterpret_cast<u32x2_t*>(a.dk + ro + d0) =
+                u32x2_t{pack_bf2(y[0] + kl.x, y[1] + kl.y), pack_bf2(y[2] + kl.z, y[3] + kl.w)};
+        }
+}
+
 __global__ __launch_bounds__(512) void k_bwd_dkdv_tiled(BwdArgs a, const int32_t* __restrict__ inv_off,
                                                         const int32_t* __restrict__ inv_list,
                                                         const int32_t* __restrict__ order,
@@ -829,74 +953,10 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_tiled(BwdArgs a, const int32_t
     else
         dkdv_tiled_loop<1>(a, lds, qt, list, n0, n1, tid, wave, lane, qh, hf, op, pex, acc);
 
-    // ---- add the query halves through LDS (no copy is in flight: the last tile waited for all)
-    __syncthreads();
-    float* mrg = reinterpret_cast<float*>(lds) + (role * 2 + kw) * (64 * 64);
-    if (qh == 1) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mrg[(16 * db + i) * 64 + lane] = acc[db][i];
-    }
-    __syncthreads();
-    if (qh == 1) return;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] += mrg[(16 * db + i) * 64 + lane];
-    // the low-rank parts of the wave's keys (whole wave), unless they were stored in fp32:
-    // dS^T fk (dV waves), W_k dpk (dK waves)
-    const bool fused = a.lr_ph != nullptr;
-    f32x16_t lrp[4];
-    if (fused) {
-        const long krow = bh * L + (kval ? key : 0);
-        const long nb = a.lr_rv <= 32 ? 512 : 1024;   // 16-byte entries of one operand matrix
-        if (role == 0)
-            lr_rows_product(reinterpret_cast<const u32x4_t*>(a.lr_sh) + bh * nb,
-                            reinterpret_cast<const u32x4_t*>(a.lr_sl) + bh * nb, a.lr_fh, a.lr_fl, krow, kval, a.lr_rv,
-                            lane, hf, lrp);
-        else
-            lr_rows_product(reinterpret_cast<const u32x4_t*>(a.lr_w) + (bh % a.H) * nb, nullptr, a.lr_ph, a.lr_pl, krow,
-                            kval, a.lr_rv, lane, hf, lrp);
-    }
-    if (!kval) return;
-
-    // ---- epilogue: dv = dV + dv_lowrank (dV waves); dk = R^T (kscale dK_rot) + dk_lowrank (dK
-    // waves); lane owns key `key`, dims 32db + 8g4 + 4hf + 0..3
-    const long ro = (bh * L + key) * D;
-    if (role == 0) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int d0 = 32 * db + 8 * g4 + 4 * hf;
-                const float4 vl = fused ? make_float4(lrp[db][4 * g4], lrp[db][4 * g4 + 1], lrp[db][4 * g4 + 2],
-                                                      lrp[db][4 * g4 + 3])
-                                        : *reinterpret_cast<const float4*>(a.dv_lr + ro + d0);
-                *reinterpret_cast<u32x2_t*>(a.dv + ro + d0) =
-                    u32x2_t{pack_bf2(acc[db][4 * g4] + vl.x, acc[db][4 * g4 + 1] + vl.y),
-                            pack_bf2(acc[db][4 * g4 + 2] + vl.z, acc[db][4 * g4 + 3] + vl.w)};
-            }
-        return;
-    }
-    int crd[3];
-    token_coords(key, a.g.Hg, a.g.Wg, crd[0], crd[1], crd[2]);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const int d0 = 32 * db + 8 * g4 + 4 * hf;
-            float y[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = acc[db][4 * g4 + i] * a.kscale;
-            rot_t(y[0], y[1], rope_cs(a.tab, a.g, d0 >> 1, crd));
-            rot_t(y[2], y[3], rope_cs(a.tab, a.g, (d0 >> 1) + 1, crd));
-            const float4 kl = fused ? make_float4(lrp[db][4 * g4], lrp[db][4 * g4 + 1], lrp[db][4 * g4 + 2],
-                                                  lrp[db][4 * g4 + 3])
-                                    : *reinterpret_cast<const float4*>(a.dk_lr + ro + d0);
-            *reinterpret_cast<u32x2_t*>(a.dk + ro + d0) =
-                u32x2_t{pack_bf2(y[0] + kl.x, y[1] + kl.y), pack_bf2(y[2] + kl.z, y[3] + kl.w)};
-        }
+    if (role == 0)
+        dkdv_tiled_tail<0>(a, lds, acc, bh, key, kval, kw, qh, lane, hf);
+    else
+        dkdv_tiled_tail<1>(a, lds, acc, bh, key, kval, kw, qh, lane, hf);
 }
 
 // ---------------------------------------------------------------------------
