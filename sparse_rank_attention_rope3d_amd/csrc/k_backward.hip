@@ -394,17 +394,107 @@ __device__ __forceinline__ u32x2_t lds_tr8(const uint16_t* p) {
     return __builtin_bit_cast(u32x2_t, r);
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// LDS accesses inside the streaming loops, whose next tile is being copied
+// into the other ring slot meanwhile. The compiler cannot tell that such an
+// access stays clear of the copy's slot, so before any LDS access it can see
+// it waits for all copies in flight (the prefetch would then have to land
+// before the current tile's math); these helpers issue their accesses in one
+// asm block, and the reads wait for themselves inside it.
+//
 // The eight A operand chunks (h, db, h2), i = 2db + h2, of X^T from a part
 // holding X: lane l gets X[rows 32h + 16h2 + 8(e / 4) + 4(l / 32) + e % 4,
 // e = 0 .. 7][dim 32db + l % 32], the row order in which a 32x32 score
 // accumulator holds its rows; t0 / t1 = part + 4096h + tr_lane_off(lane, 0 / 1).
+// Chunk i takes the transposing reads at element offset 1024(i / 2) +
+// 128(i % 2) from t0 (its first four rows) and from t1.
 __device__ __forceinline__ void lds_read_t8(u32x4_t* at, const uint16_t* t0, const uint16_t* t1) {
+    u32x2_t r[16];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %17 offset:0\n\t"
+        "ds_read_b64_tr_b16 %2, %16 offset:256\n\t"
+        "ds_read_b64_tr_b16 %3, %17 offset:256\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %5, %17 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %6, %16 offset:2304\n\t"
+        "ds_read_b64_tr_b16 %7, %17 offset:2304\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %9, %17 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %10, %16 offset:4352\n\t"
+        "ds_read_b64_tr_b16 %11, %17 offset:4352\n\t"
+        "ds_read_b64_tr_b16 %12, %16 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %13, %17 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %14, %16 offset:6400\n\t"
+        "ds_read_b64_tr_b16 %15, %17 offset:6400\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+        : "v"(lds_addr(t0)), "v"(lds_addr(t1))
+        : "memory");
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int o = (i >> 1) * 1024 + (i & 1) * 128;
-        const u32x2_t lo = lds_tr8(t0 + o), hi = lds_tr8(t1 + o);
-        at[i] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    for (int i = 0; i < 8; ++i) at[i] = u32x4_t{r[2 * i][0], r[2 * i][1], r[2 * i + 1][0], r[2 * i + 1][1]};
+}
+
+// Four float4 at p, p + 8, p + 16, p + 24 (p 16-byte aligned).
+__device__ __forceinline__ void lds_read_f4x4(float4* v, const float* p) {
+    u32x4_t r[4];
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:0\n\t"
+        "ds_read_b128 %1, %4 offset:32\n\t"
+        "ds_read_b128 %2, %4 offset:64\n\t"
+        "ds_read_b128 %3, %4 offset:96\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(lds_addr(p))
+        : "memory");
+#pragma unroll
+    for (int g = 0; g < 4; ++g) v[g] = __builtin_bit_cast(float4, r[g]);
+}
+
+// v[e] = p[64 e], e = 0 .. 15. (The pairs come out as float2: taking the
+// second word of an integer pair output and bit-casting it to float compiles
+// to the first word.)
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void lds_read_col16(float* v, const float* p) {
+    f32x2_t r[8];
+    asm volatile(
+        "ds_read2st64_b32 %0, %8 offset0:0 offset1:1\n\t"
+        "ds_read2st64_b32 %1, %8 offset0:2 offset1:3\n\t"
+        "ds_read2st64_b32 %2, %8 offset0:4 offset1:5\n\t"
+        "ds_read2st64_b32 %3, %8 offset0:6 offset1:7\n\t"
+        "ds_read2st64_b32 %4, %8 offset0:8 offset1:9\n\t"
+        "ds_read2st64_b32 %5, %8 offset0:10 offset1:11\n\t"
+        "ds_read2st64_b32 %6, %8 offset0:12 offset1:13\n\t"
+        "ds_read2st64_b32 %7, %8 offset0:14 offset1:15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(lds_addr(p))
+        : "memory");
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        v[2 * k] = r[k][0];
+        v[2 * k + 1] = r[k][1];
     }
+}
+
+// p[64 e] = v[e], e = 0 .. 15 (the caller waits for the stores before it
+// signals them to other waves).
+__device__ __forceinline__ void lds_write_col16(float* p, const float* v) {
+    asm volatile(
+        "ds_write2st64_b32 %0, %1, %2 offset0:0 offset1:1\n\t"
+        "ds_write2st64_b32 %0, %3, %4 offset0:2 offset1:3\n\t"
+        "ds_write2st64_b32 %0, %5, %6 offset0:4 offset1:5\n\t"
+        "ds_write2st64_b32 %0, %7, %8 offset0:6 offset1:7\n\t"
+        "ds_write2st64_b32 %0, %9, %10 offset0:8 offset1:9\n\t"
+        "ds_write2st64_b32 %0, %11, %12 offset0:10 offset1:11\n\t"
+        "ds_write2st64_b32 %0, %13, %14 offset0:12 offset1:13\n\t"
+        "ds_write2st64_b32 %0, %15, %16 offset0:14 offset1:15"
+        :
+        : "v"(lds_addr(p)), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15])
+        : "memory");
 }
 
 // The dQ kernel's tile [K | V] of every key block, from the rotated k rows
@@ -636,12 +726,18 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* 
         for (int s = 0; s < 8; ++s) dpacc = mfma32(vop[s], doop[s], dpacc);
         u32x4_t at[8];   // K^T chunks (kh, db, h2) = (kh, i / 2, i % 2)
         lds_read_t8(at, kp + tr0, kp + tr1);
-        const long key0 = (long)jraw * BS + 32 * kh + 4 * hf;
+        // entry i of this lane is key 64 jraw + 32 kh + 4 hf + 8(i / 4) + i % 4: the number of
+        // keys from the first one that lie in the layer (0 .. 64)
+        const int kleft =
+            ragged ? (int)max(0l, min(L - ((long)jraw * BS + 32 * kh + 4 * hf), (long)BS)) : BS;
         float ds[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const bool off = !jok || (ragged && key0 + 8 * (i >> 2) + (i & 3) >= L);
-            ds[i] = off ? 0.f : __builtin_amdgcn_exp2f(sacc[i] - lse2) * (dpacc[i] - dl);
+            // computed for every entry and then selected (the tile's entries are finite: a
+            // skipped entry streams tile 0), so that no entry takes a branch of its own
+            const float v = __builtin_amdgcn_exp2f(sacc[i] - lse2) * (dpacc[i] - dl);
+            const bool off = !jok || 8 * (i >> 2) + (i & 3) >= kleft;
+            ds[i] = off ? 0.f : v;
         }
         u32x4_t dsop[2];
 #pragma unroll
@@ -774,16 +870,16 @@ __device__ __forceinline__ void dkdv_tiled_loop(const BwdArgs& a, uint16_t* lds,
         u32x4_t bop[2];   // P (dV waves) or dS (dK waves): the keys' B operand of the second product
         if constexpr (ROLE == 0) {
             float p[16];
+            float4 l4[4];   // the rows' log2 normalisers
+            lds_read_f4x4(l4, st);
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float4 l4 = *reinterpret_cast<const float4*>(st + 8 * g);
-                p[4 * g + 0] = __builtin_amdgcn_exp2f(sacc[4 * g + 0] * a.qmul - l4.x);
-                p[4 * g + 1] = __builtin_amdgcn_exp2f(sacc[4 * g + 1] * a.qmul - l4.y);
-                p[4 * g + 2] = __builtin_amdgcn_exp2f(sacc[4 * g + 2] * a.qmul - l4.z);
-                p[4 * g + 3] = __builtin_amdgcn_exp2f(sacc[4 * g + 3] * a.qmul - l4.w);
+                p[4 * g + 0] = __builtin_amdgcn_exp2f(sacc[4 * g + 0] * a.qmul - l4[g].x);
+                p[4 * g + 1] = __builtin_amdgcn_exp2f(sacc[4 * g + 1] * a.qmul - l4[g].y);
+                p[4 * g + 2] = __builtin_amdgcn_exp2f(sacc[4 * g + 2] * a.qmul - l4[g].z);
+                p[4 * g + 3] = __builtin_amdgcn_exp2f(sacc[4 * g + 3] * a.qmul - l4[g].w);
             }
-#pragma unroll
-            for (int e = 0; e < 16; ++e) pex[e * 64 + lane] = p[e];
+            lds_write_col16(pex + lane, p);
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -793,14 +889,16 @@ __device__ __forceinline__ void dkdv_tiled_loop(const BwdArgs& a, uint16_t* lds,
         __builtin_amdgcn_s_barrier();   // P is in LDS
         asm volatile("" ::: "memory");
         if constexpr (ROLE == 1) {
-            float ds[16];
+            float ds[16], pv[16];
+            float4 d4[4];   // the rows' delta = dO . O
+            lds_read_f4x4(d4, st + 64);
+            lds_read_col16(pv, pex + lane);
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float4 d4 = *reinterpret_cast<const float4*>(st + 64 + 8 * g);
-                ds[4 * g + 0] = pex[(4 * g + 0) * 64 + lane] * (sacc[4 * g + 0] - d4.x);
-                ds[4 * g + 1] = pex[(4 * g + 1) * 64 + lane] * (sacc[4 * g + 1] - d4.y);
-                ds[4 * g + 2] = pex[(4 * g + 2) * 64 + lane] * (sacc[4 * g + 2] - d4.z);
-                ds[4 * g + 3] = pex[(4 * g + 3) * 64 + lane] * (sacc[4 * g + 3] - d4.w);
+                ds[4 * g + 0] = pv[4 * g + 0] * (sacc[4 * g + 0] - d4[g].x);
+                ds[4 * g + 1] = pv[4 * g + 1] * (sacc[4 * g + 1] - d4[g].y);
+                ds[4 * g + 2] = pv[4 * g + 2] * (sacc[4 * g + 2] - d4[g].z);
+                ds[4 * g + 3] = pv[4 * g + 3] * (sacc[4 * g + 3] - d4[g].w);
             }
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
