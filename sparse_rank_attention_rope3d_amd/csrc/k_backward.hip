@@ -35,23 +35,26 @@
 
 namespace slr {
 
-// (cos, sin) of backbone rotary pair p (0 .. D/2-1) at token coordinates crd
+// (cos, sin) of backbone rotary pair p (0 .. D/2-1) at token coordinates crd.
+// The axis is picked by selects over the three candidate entries rather than
+// by indexing the geometry with it: a lane-dependent index into the kernel
+// arguments turns into a memory load per call, ahead of the table load.
 __device__ __forceinline__ float2 rope_cs(const float2* __restrict__ tab, const RopeGeom& g, int p, const int* crd) {
-    int a, j;
-    if (p < g.np[0]) { a = 0; j = p; }
-    else if (p < g.np[0] + g.np[1]) { a = 1; j = p - g.np[0]; }
-    else { a = 2; j = p - g.np[0] - g.np[1]; }
-    return tab[g.tab_off[a] + crd[a] * g.np[a] + j];
+    const int n0 = g.np[0], n01 = g.np[0] + g.np[1];
+    const int i0 = g.tab_off[0] + crd[0] * g.np[0] + p;
+    const int i1 = g.tab_off[1] + crd[1] * g.np[1] + (p - n0);
+    const int i2 = g.tab_off[2] + crd[2] * g.np[2] + (p - n01);
+    return tab[p < n0 ? i0 : (p < n01 ? i1 : i2)];
 }
 
 // (cos, sin) of low-rank pair pr: the axis chunks hold lp[] pairs that reuse
-// the backbone's schedule of their axis
+// the backbone's schedule of their axis (axis picked as in rope_cs)
 __device__ __forceinline__ float2 lowrank_cs(const float2* __restrict__ tab, const LrGeom& g, int pr, const int* crd) {
-    int a, j;
-    if (pr < g.lp[0]) { a = 0; j = pr; }
-    else if (pr < g.lp[0] + g.lp[1]) { a = 1; j = pr - g.lp[0]; }
-    else { a = 2; j = pr - g.lp[0] - g.lp[1]; }
-    return tab[g.rope.tab_off[a] + crd[a] * g.rope.np[a] + j];
+    const int n0 = g.lp[0], n01 = g.lp[0] + g.lp[1];
+    const int i0 = g.rope.tab_off[0] + crd[0] * g.rope.np[0] + pr;
+    const int i1 = g.rope.tab_off[1] + crd[1] * g.rope.np[1] + (pr - n0);
+    const int i2 = g.rope.tab_off[2] + crd[2] * g.rope.np[2] + (pr - n01);
+    return tab[pr < n0 ? i0 : (pr < n01 ? i1 : i2)];
 }
 
 // y -> R^T y for one pair: turned by minus its angle
@@ -60,6 +63,45 @@ __device__ __forceinline__ void rot_t(float& y0, float& y1, float2 cs) {
     const float x1 = -y0 * cs.y + y1 * cs.x;
     y0 = x0;
     y1 = x1;
+}
+
+// Epilogue of the streaming dQ and dK/dV kernels for one lane's row: out[d] =
+// bf16((R^T (scale acc))[d] + lr[d]) over dims 32db + 8g4 + 4hf + 0..3
+// (group q = 4db + g4), the low-rank part taken from lrp (the accumulator
+// layout) when FUSED, else read from the fp32 row lr. The loads of NB
+// groups are issued before their stores: the compiler keeps loads behind
+// earlier stores that might alias them, so group by group each would wait
+// for its own loads.
+template <bool FUSED, int NB>
+__device__ __forceinline__ void rotate_store_row(const float2* __restrict__ tab, const RopeGeom& g, const int* crd,
+                                                 const f32x16_t* acc, float scale, const f32x16_t* lrp,
+                                                 const float* __restrict__ lr, uint16_t* __restrict__ out, int hf) {
+#pragma unroll
+    for (int h = 0; h < 16 / NB; ++h) {
+        float2 cs[2 * NB];
+        float4 l[FUSED ? 1 : NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int q = NB * h + k, d0 = 32 * (q >> 2) + 8 * (q & 3) + 4 * hf;
+            cs[2 * k] = rope_cs(tab, g, d0 >> 1, crd);
+            cs[2 * k + 1] = rope_cs(tab, g, (d0 >> 1) + 1, crd);
+            if (!FUSED) l[FUSED ? 0 : k] = *reinterpret_cast<const float4*>(lr + d0);
+        }
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int q = NB * h + k, d0 = 32 * (q >> 2) + 8 * (q & 3) + 4 * hf, e = 4 * (q & 3);
+            const float4 lk = FUSED ? make_float4(lrp[q >> 2][e], lrp[q >> 2][e + 1], lrp[q >> 2][e + 2],
+                                                  lrp[q >> 2][e + 3])
+                                    : l[FUSED ? 0 : k];
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = acc[q >> 2][e + i] * scale;
+            rot_t(y[0], y[1], cs[2 * k]);
+            rot_t(y[2], y[3], cs[2 * k + 1]);
+            *reinterpret_cast<u32x2_t*>(out + d0) =
+                u32x2_t{pack_bf2(y[0] + lk.x, y[1] + lk.y), pack_bf2(y[2] + lk.z, y[3] + lk.w)};
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -611,7 +653,7 @@ __device__ __forceinline__ void lr_rows_finish(const LrSrc& src, LrOps& o, int l
 // the K part by transposing reads. The two key halves' dQ^T are added through
 // LDS at the end. The tiled path scores with q pre-multiplied by
 // log2(e)/sqrt(D), so p = exp2(score - lse2).
-__global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* __restrict__ idx_all,
+__global__ __launch_bounds__(256, 2) void k_bwd_dq_tiled(BwdArgs a, const int32_t* __restrict__ idx_all,
                                                       const uint16_t* __restrict__ tiles_all) {
     constexpr int D = 128, BS = 64, PART = kDqPart, PLOADS = PART * 2 / (256 * 16);
     __shared__ __attribute__((aligned(16))) uint16_t lds[4 * PART];
@@ -781,28 +823,14 @@ __global__ __launch_bounds__(256) void k_bwd_dq_tiled(BwdArgs a, const int32_t* 
     }
     if (!qval) return;
 
-    // ---- epilogue: dq = R^T (dQ_rot / sqrt(D)) + dq_lowrank; lane owns row qrow,
-    // dims 32db + 8g4 + 4hf + 0..3
+    // ---- epilogue: dq = R^T (dQ_rot / sqrt(D)) + dq_lowrank; lane owns row qrow
     int crd[3];
     token_coords(qrow, a.g.Hg, a.g.Wg, crd[0], crd[1], crd[2]);
-    const float* lr = fused ? nullptr : a.dq_lr + (bh * L + qrow) * D;
     uint16_t* out = a.dq + (bh * L + qrow) * D;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const int d0 = 32 * db + 8 * g4 + 4 * hf;
-            float y[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = dqacc[db][4 * g4 + i] * a.scale;
-            rot_t(y[0], y[1], rope_cs(a.tab, a.g, d0 >> 1, crd));
-            rot_t(y[2], y[3], rope_cs(a.tab, a.g, (d0 >> 1) + 1, crd));
-            const float4 l4 = fused ? make_float4(lrp[db][4 * g4], lrp[db][4 * g4 + 1], lrp[db][4 * g4 + 2],
-                                                  lrp[db][4 * g4 + 3])
-                                    : *reinterpret_cast<const float4*>(lr + d0);
-            *reinterpret_cast<u32x2_t*>(out + d0) =
-                u32x2_t{pack_bf2(y[0] + l4.x, y[1] + l4.y), pack_bf2(y[2] + l4.z, y[3] + l4.w)};
-        }
+    if (fused)
+        rotate_store_row<true, 8>(a.tab, a.g, crd, dqacc, a.scale, lrp, nullptr, out, hf);
+    else
+        rotate_store_row<false, 8>(a.tab, a.g, crd, dqacc, a.scale, lrp, a.dq_lr + (bh * L + qrow) * D, out, hf);
 }
 
 // ---------------------------------------------------------------------------
@@ -982,22 +1010,10 @@ __device__ __forceinline__ void dkdv_tiled_tail(const BwdArgs& a, uint16_t* lds,
     if (!kval) return;
     int crd[3];
     token_coords(key, a.g.Hg, a.g.Wg, crd[0], crd[1], crd[2]);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const int d0 = 32 * db + 8 * g4 + 4 * hf;
-            float y[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = acc[db][4 * g4 + i] * a.kscale;
-            rot_t(y[0], y[1], rope_cs(a.tab, a.g, d0 >> 1, crd));
-            rot_t(y[2], y[3], rope_cs(a.tab, a.g, (d0 >> 1) + 1, crd));
-            const float4 kl = fused ? make_float4(lrp[db][4 * g4], lrp[db][4 * g4 + 1], lrp[db][4 * g4 + 2],
-                                                  lrp[db][4 * g4 + 3])
-                                    : *reinterpret_cast<const float4*>(a.dk_lr + ro + d0);
-            *reinterpret_cast<u32x2_t*>(a.dk + ro + d0) =
-                u32x2_t{pack_bf2(y[0] + kl.x, y[1] + kl.y), pack_bf2(y[2] + kl.z, y[3] + kl.w)};
-        }
+    if (fused)
+        rotate_store_row<true, 4>(a.tab, a.g, crd, acc, a.kscale, lrp, nullptr, a.dk + ro, hf);
+    else
+        rotate_store_row<false, 4>(a.tab, a.g, crd, acc, a.kscale, lrp, a.dk_lr + ro, a.dk + ro, hf);
 }
 
 __global__ __launch_bounds__(512) void k_bwd_dkdv_tiled(BwdArgs a, const int32_t* __restrict__ inv_off,
