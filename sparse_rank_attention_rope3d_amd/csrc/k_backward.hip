@@ -775,11 +775,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq_tiled(BwdArgs a, const int32_
         float ds[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            // computed for every entry and then selected (the tile's entries are finite: a
-            // skipped entry streams tile 0), so that no entry takes a branch of its own
-            const float v = __builtin_amdgcn_exp2f(sacc[i] - lse2) * (dpacc[i] - dl);
+            // an entry off the layer or of a skipped block gets exp2(-inf) = 0 (its dP is
+            // finite: a skipped entry streams tile 0): the select sits before the exp, so the
+            // compiler has no reason to branch around the exp of each entry
             const bool off = !jok || 8 * (i >> 2) + (i & 3) >= kleft;
-            ds[i] = off ? 0.f : v;
+            ds[i] = __builtin_amdgcn_exp2f(off ? -__builtin_inff() : sacc[i] - lse2) * (dpacc[i] - dl);
         }
         u32x4_t dsop[2];
 #pragma unroll
