@@ -42,7 +42,7 @@ METRIC = "SLR attn fwd ms/layer + effective TFLOP/s at L=32760/75600/118800, 1 G
 # on, identified by the sha256 of its files; any other source reports null.
 FLASH_TRAFFIC_SOURCES = ["k_flash.hip", "slr_common.h", "slr_launch.h"]
 FLASH_TRAFFIC = {
-    "sha256": "cf0508e80607d6cccdb3a8e7f8f8e1b9358c2c484292572488efd6e75dc2c32f",
+    "sha256": "c5d34a9a56f37494d5ba0a4dfc70b6437c38dc85473e3a3387bcf7494e636513",
     "bytes_per_launch": {"wan13b": 8203.9e6 + 201.3e6, "wan14b": 229030.0e6 + 1549.1e6,
                          "hunyuan13b": 195059.5e6 + 730.2e6},
 }

@@ -101,28 +101,84 @@ __device__ __forceinline__ float2 lr_cossin(const float2* __restrict__ tab, cons
 // wave's B operand in this kernel's token-slot order, so no LDS transpose is
 // needed (the tail block's padded keys are zero there).
 //
+// PF (TILEDV, rotary variant, rank <= 32, rotation table of at most kLrTabMax
+// entries; the FAVOR+ instance would spill, so only elu + 1 / SiLU use it):
+// each wave keeps its next sub-tile in flight while it works on the current
+// one. The V^T chunks go straight from memory into a two-slot LDS ring of the
+// wave (direct global -> LDS copies, no registers), the next K rows into the
+// registers the U MFMAs just released, and the cos/sin rows of the low-rank
+// pairs sit in LDS, so no global load is issued between the prefetch and the
+// next sub-tile (vector loads complete in issue order: waiting for a later
+// load would also wait for the prefetch). The ring aliases the reduction
+// buffer, which is used only after the loop. (Copying the K rows into LDS as
+// well, one slot each for K and V^T, measured 1% slower.)
+//
 // FAV (FAVOR+ features): besides U = K W_k (the exponent's |p|^2 term, per
 // token a sum over the r lanes of a 32-lane half), Y = K (W_k omega^T) on
 // MFMA with bf16 hi + lo weights gives omega_c . p; u_c = exp(y_c -
 // |p|^2 / 2) / sqrt(R).
-template <int D, int RP, bool ABSPE, bool TILEDV, bool FAV = false>
-__global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restrict__ k,
-                                                         const uint16_t* __restrict__ v,
-                                                         const uint16_t* __restrict__ kv_tiles, int nblk,
-                                                         const uint16_t* __restrict__ wkt,
-                                                         const float* __restrict__ Et,
-                                                         const float* __restrict__ Eh,
-                                                         const float* __restrict__ Ew,
-                                                         const float2* __restrict__ tab, LrGeom g, long L,
-                                                         int H, int chunk, int nsplit, float* __restrict__ part,
-                                                         const uint16_t* __restrict__ wkot_hi,
-                                                         const uint16_t* __restrict__ wkot_lo) {
+// Largest rotation table (float2 entries) the prefetching summary stages in LDS.
+constexpr int kLrTabMax = 1920;
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Eight 16-byte LDS reads at 1 KB spacing (the chunks of one operand-order
+// sub-tile), waiting for their own completion only. Written as one asm block
+// so the compiler does not first wait for every copy still landing in LDS.
+__device__ __forceinline__ void lds_read8_1k(u32x4_t* r, const uint16_t* lds_base) {
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds_base;
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %4, %8 offset:4096\n\t"
+        "ds_read_b128 %5, %8 offset:5120\n\t"
+        "ds_read_b128 %6, %8 offset:6144\n\t"
+        "ds_read_b128 %7, %8 offset:7168\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a)
+        : "memory");
+}
+
+// Eight 8-byte LDS reads at per-lane byte addresses a[0..7], same waiting rule.
+__device__ __forceinline__ void lds_gather8(f32x2_t* r, const uint32_t* a) {
+    asm volatile(
+        "ds_read_b64 %0, %8\n\t"
+        "ds_read_b64 %1, %9\n\t"
+        "ds_read_b64 %2, %10\n\t"
+        "ds_read_b64 %3, %11\n\t"
+        "ds_read_b64 %4, %12\n\t"
+        "ds_read_b64 %5, %13\n\t"
+        "ds_read_b64 %6, %14\n\t"
+        "ds_read_b64 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+}
+
+#define SLR_SUMMARY_PARAMS                                                                                      \
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const uint16_t *__restrict__ kv_tiles, int nblk, \
+        const uint16_t *__restrict__ wkt, const float *__restrict__ Et, const float *__restrict__ Eh,            \
+        const float *__restrict__ Ew, const float2 *__restrict__ tab, LrGeom g, long L, int H, int chunk,        \
+        int nsplit, float *__restrict__ part, const uint16_t *__restrict__ wkot_hi,                              \
+        const uint16_t *__restrict__ wkot_lo
+#define SLR_SUMMARY_ARGS k, v, kv_tiles, nblk, wkt, Et, Eh, Ew, tab, g, L, H, chunk, nsplit, part, wkot_hi, wkot_lo
+
+template <int D, int RP, bool ABSPE, bool TILEDV, bool FAV, bool PF>
+__device__ __forceinline__ void lr_summary_bf16_body(SLR_SUMMARY_PARAMS) {
     constexpr int NRB = RP / 32;   // r blocks
     constexpr int NDB = D / 32;    // d blocks
     constexpr int NKS = D / 16;    // k steps over d
     constexpr int VLD = 32 + 8;    // LDS row stride (elements) of V^T
+    static_assert(!PF || (TILEDV && !ABSPE && D == 128), "prefetching summary: tiled V^T, rotary variant");
+    constexpr int RED_N = RP * D + RP;
+    constexpr int RING_F = PF ? 4 * 2 * 4096 / 2 : 0;   // 4 waves x 2 slots x 8 KB, in floats
     __shared__ __attribute__((aligned(16))) uint16_t vt[TILEDV ? 1 : 4][TILEDV ? 8 : D * VLD];
-    __shared__ float red[RP * D + RP];
+    __shared__ __attribute__((aligned(16))) float red[RING_F > RED_N ? RING_F : RED_N];
+    __shared__ __attribute__((aligned(16))) float2 ltab[PF ? kLrTabMax : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
@@ -175,16 +231,75 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
         rbase[rb] = (a == 0 ? g.rope.tab_off[0] : a == 1 ? g.rope.tab_off[1] : g.rope.tab_off[2]) + j;
         rstride[rb] = a == 0 ? g.rope.np[0] : a == 1 ? g.rope.np[1] : g.rope.np[2];
     }
+    u32x4_t kop[NKS];
+    // K rows of sub-tile t0 (rows past the chunk clamped to its last token)
+    auto load_k = [&](long t0) {
+        const long tk = t0 + l32;
+        const long tkc = tk < tok_hi ? tk : tok_hi - 1;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) kop[s] = ldg16(ks + tkc * D + 16 * s + 8 * hf);
+    };
+    // PF: V^T chunks of sub-tile t0 -> ring slot sl of this wave (the LDS
+    // image equals the memory image: chunk i at 1 KB * i, lane at 16 B * lane)
+    uint16_t* const vring = reinterpret_cast<uint16_t*>(red) + (PF ? wave * 8192 : 0);
+    auto issue_v = [&](long t0, int sl) {
+        const uint16_t* vp = tiles + (t0 >> 6) * (long)kTileElems + 64 * 128 + ((((t0 >> 5) & 1) * 8) * 64 + lane) * 8;
+        uint16_t* dst = vring + sl * 4096;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vp + i * 512),
+                                             (__attribute__((address_space(3))) void*)(dst + i * 512), 16, 0, 0);
+    };
+    // PF: LDS rotation table, entry (axis a, coordinate c, pair j < lp[a]) at
+    // loff[a] + c lp[a] + j; the lanes of padding features (r >= R) read entry 0
+    int lbase[NRB], lstride[NRB];
+    const uint32_t tbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float2*)ltab;
+    if constexpr (PF) {
+        const int n0 = g.rope.T * g.lp[0], n1 = g.rope.Hg * g.lp[1], n2 = g.rope.Wg * g.lp[2];
+        for (int e = tid; e < n0 + n1 + n2; e += 256) {
+            const int a = e < n0 ? 0 : (e < n0 + n1 ? 1 : 2);
+            const int r = e - (a == 0 ? 0 : (a == 1 ? n0 : n0 + n1));
+            const int c = r / g.lp[a], j = r - c * g.lp[a];
+            ltab[e] = tab[g.rope.tab_off[a] + c * g.rope.np[a] + j];
+        }
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            const int r = 32 * rb + l32, pr = r >> 1, a = rax[rb];
+            const int j = pr - (a == 0 ? 0 : (a == 1 ? g.lp[0] : g.lp[0] + g.lp[1]));
+            const bool live = r < g.R;
+            lbase[rb] = live ? (a == 0 ? 0 : (a == 1 ? n0 : n0 + n1)) + j : 0;
+            lstride[rb] = live ? g.lp[a] : 0;
+        }
+        __syncthreads();
+        const long tf = tok_lo + 32 * wave;
+        if (tf < tok_hi) {
+            issue_v(tf, 0);
+            load_k(tf);
+        }
+    }
+    int slot = 0;   // PF: ring slot of the current sub-tile
+    // PF: cos/sin of this lane's pair for the 16 tokens of sub-tile t0 from LDS
+    auto lds_cs = [&](int rb, const int* ca, long t0, float2* cs) {
+        uint32_t ad[16];
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+            const bool okt = t0 + 4 * hf + 8 * (vv >> 2) + (vv & 3) < tok_hi;
+            ad[vv] = tbase + 8u * (uint32_t)(lbase[rb] + (okt ? ca[vv] : 0) * lstride[rb]);
+        }
+        f32x2_t cv[16];
+        lds_gather8(cv, ad);
+        lds_gather8(cv + 8, ad + 8);
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) cs[vv] = make_float2(cv[vv].x, cv[vv].y);
+    };
     // Every load below is unconditional: rows past the chunk are clamped to
     // its last token (their features are zeroed), so the loads of a sub-tile
     // issue back to back instead of one predicated round trip each.
     for (long t0 = tok_lo + 32 * wave; t0 < tok_hi; t0 += 128) {
-        // ---- U = K_sub W_k
-        const long tk = t0 + l32;
-        const long tkc = tk < tok_hi ? tk : tok_hi - 1;
-        u32x4_t kop[NKS];
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) kop[s] = ldg16(ks + tkc * D + 16 * s + 8 * hf);
+        // ---- U = K_sub W_k (PF: K rows and the V^T chunks were requested one
+        // sub-tile earlier, and nothing else is in flight)
+        if constexpr (PF) wait_vmcnt<0>();
+        else load_k(t0);
         f32x16_t uacc[NRB];
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
@@ -211,13 +326,22 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
                     yacc[rb] = mfma32(kop[s], ldg16(wkot_lo + wo), yacc[rb]);
                 }
         }
+        // PF: the next sub-tile's requests, now that kop is free
+        if constexpr (PF) {
+            if (t0 + 128 < tok_hi) {
+                issue_v(t0 + 128, slot ^ 1);
+                load_k(t0 + 128);
+            }
+        }
         // ---- V sub-tile -> this wave's LDS area, transposed to [d][slot16(tok)]
         u32x4_t vop[TILEDV ? 8 : 1];
         if (TILEDV) {
             // sub-tile = key half ((t0 / 32) & 1) of block t0 / 64; chunk (kh, db, h2)
-            const uint16_t* vp = tiles + (t0 >> 6) * (long)kTileElems + 64 * 128 + ((((t0 >> 5) & 1) * 8) * 64 + lane) * 8;
+            if constexpr (!PF) {
+                const uint16_t* vp = tiles + (t0 >> 6) * (long)kTileElems + 64 * 128 + ((((t0 >> 5) & 1) * 8) * 64 + lane) * 8;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) vop[i] = ldg16(vp + i * 512);
+                for (int i = 0; i < 8; ++i) vop[i] = ldg16(vp + i * 512);
+            }
         } else if (vg < 4) {
             uint32_t rows[8][4];
 #pragma unroll
@@ -303,6 +427,7 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
                 const int r = 32 * rb + l32;
                 float2 cs[16];
                 float eo[16];
+                if constexpr (PF) lds_cs(rb, cA[rb], t0, cs);
 #pragma unroll
                 for (int vv = 0; vv < 16; ++vv) {
                     const bool ok = t0 + 4 * hf + 8 * (vv >> 2) + (vv & 3) < tok_hi && r < g.R;
@@ -311,7 +436,7 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
                         const int it = ok ? cT[vv] : 0, ih = ok ? cH[vv] : 0, iw = ok ? cW[vv] : 0;
                         const float* eoh = g.eo + (long)head * na * g.R + rr;
                         eo[vv] = eoh[it * g.R] + eoh[(g.rope.T + ih) * g.R] + eoh[(g.rope.T + g.rope.Hg + iw) * g.R];
-                    } else {
+                    } else if (!PF) {
                         cs[vv] = tab[rbase[rb] + (ok ? cA[rb][vv] : 0) * rstride[rb]];
                     }
                 }
@@ -336,6 +461,7 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
             // gathers first (all independent), arithmetic after
             float2 cs[16];
             float ev[16];
+            if constexpr (PF) lds_cs(rb, cA[rb], t0, cs);
 #pragma unroll
             for (int vv = 0; vv < 16; ++vv) {
                 const bool ok = t0 + 4 * hf + 8 * (vv >> 2) + (vv & 3) < tok_hi && r < g.R;
@@ -343,7 +469,7 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
                     const int rr = r < g.R ? r : 0;
                     const int it = ok ? cT[vv] : 0, ih = ok ? cH[vv] : 0, iw = ok ? cW[vv] : 0;
                     ev[vv] = Et[it * g.R + rr] + Eh[ih * g.R + rr] + Ew[iw * g.R + rr];
-                } else {
+                } else if (!PF) {
                     cs[vv] = tab[rbase[rb] + (ok ? cA[rb][vv] : 0) * rstride[rb]];
                 }
             }
@@ -381,6 +507,7 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
         // ---- S += F^T V
+        if constexpr (PF) lds_read8_1k(vop, vring + slot * 4096 + lane * 8);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -399,7 +526,10 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
+        slot ^= 1;
     }
+    // PF: the ring aliases red; no copy is requested past the last sub-tile
+    if constexpr (PF) wait_vmcnt<0>();
     __syncthreads();
 
     // ---- reduce the 4 waves in a fixed order, then write the partial
@@ -430,6 +560,18 @@ __global__ __launch_bounds__(256) void k_lr_summary_bf16(const uint16_t* __restr
     }
     float* dst = part + (bh * nsplit + split) * (long)(RP * D + RP);
     for (int e = tid; e < RP * D + RP; e += 256) dst[e] = red[e];
+}
+
+template <int D, int RP, bool ABSPE, bool TILEDV, bool FAV = false>
+__global__ __launch_bounds__(256) void k_lr_summary_bf16(SLR_SUMMARY_PARAMS) {
+    lr_summary_bf16_body<D, RP, ABSPE, TILEDV, FAV, false>(SLR_SUMMARY_ARGS);
+}
+
+// The prefetching instance (elu + 1 or SiLU features, rank <= 32), held to
+// two waves per SIMD: two workgroups per CU with its 79 KB of LDS.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_lr_summary_bf16_pf(
+    SLR_SUMMARY_PARAMS) {
+    lr_summary_bf16_body<128, 32, false, true, false, true>(SLR_SUMMARY_ARGS);
 }
 
 // fp32 layers: the same sums on fp32 VALU (tokens staged through LDS).
@@ -605,21 +747,32 @@ static hipError_t summary_bf16_t(bool abspe, const void* k, const void* v, const
                                  float* part, hipStream_t st, const uint16_t* woh, const uint16_t* wol) {
     dim3 grid((unsigned)nsplit, (unsigned)BH);
     const bool fav = g.fmap == 2;
-#define SLR_SUMB(AB, FV)                                                                                            \
-    hipLaunchKernelGGL((k_lr_summary_bf16<D, RP, AB, TILEDV, FV>), grid, dim3(256), 0, st, (const uint16_t*)k,      \
-                       (const uint16_t*)v, kvt, nblk, wkt, Et, Eh, Ew, tab, g, L, H, chunk, nsplit, part, woh, wol)
+    const bool pf = lr_summary_prefetch(1, D, abspe, TILEDV, g);
+#define SLR_SUMB(KERNEL)                                                                                    \
+    hipLaunchKernelGGL((KERNEL), grid, dim3(256), 0, st, (const uint16_t*)k, (const uint16_t*)v, kvt, nblk, wkt, \
+                       Et, Eh, Ew, tab, g, L, H, chunk, nsplit, part, woh, wol)
     if (abspe) {
-        if (fav) SLR_SUMB(true, true); else SLR_SUMB(true, false);
+        if (fav) SLR_SUMB((k_lr_summary_bf16<D, RP, true, TILEDV, true>));
+        else SLR_SUMB((k_lr_summary_bf16<D, RP, true, TILEDV, false>));
+    } else if (pf) {
+        if constexpr (TILEDV && D == 128 && RP == 32) SLR_SUMB(k_lr_summary_bf16_pf);
     } else {
-        if (fav) SLR_SUMB(false, true); else SLR_SUMB(false, false);
+        if (fav) SLR_SUMB((k_lr_summary_bf16<D, RP, false, TILEDV, true>));
+        else SLR_SUMB((k_lr_summary_bf16<D, RP, false, TILEDV, false>));
     }
 #undef SLR_SUMB
     return hipGetLastError();
 }
 
+bool lr_summary_prefetch(int dtype_bf16, int D, bool abspe, bool tiled, const LrGeom& g) {
+    const long n = (long)g.rope.T * g.lp[0] + (long)g.rope.Hg * g.lp[1] + (long)g.rope.Wg * g.lp[2];
+    return dtype_bf16 && D == 128 && tiled && !abspe && g.R <= 32 && g.fmap != 2 && n <= kLrTabMax;
+}
+
 // The kernel instance launch_lr_summary picks for these arguments.
-static const void* summary_kernel(int dtype_bf16, int D, int RP, bool abspe, bool tiled, bool favor) {
+static const void* summary_kernel(int dtype_bf16, int D, int RP, bool abspe, bool tiled, bool favor, bool pf) {
 #define SLR_PICK(...) return reinterpret_cast<const void*>(&__VA_ARGS__)
+    if (pf) SLR_PICK(k_lr_summary_bf16_pf);
     if (dtype_bf16 && favor) {
         // FAVOR+ instances (their occupancy is what sizes the split)
         if (tiled && D == 128) {
@@ -652,21 +805,22 @@ static const void* summary_kernel(int dtype_bf16, int D, int RP, bool abspe, boo
 #undef SLR_PICK
 }
 
-hipError_t lr_summary_slots(int dtype_bf16, int D, int RP, bool abspe, bool tiled, int* slots, bool favor) {
+hipError_t lr_summary_slots(int dtype_bf16, int D, int RP, bool abspe, bool tiled, int* slots, bool favor, bool pf) {
     constexpr int kMaxDev = 64;
-    static std::atomic<int> cache[kMaxDev][64];
+    static std::atomic<int> cache[kMaxDev][128];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    const int key = (favor && dtype_bf16 ? 32 : 0) | (dtype_bf16 ? 16 : 0) | (D == 128 ? 8 : 0) | (RP == 64 ? 4 : 0) |
-                    (abspe ? 2 : 0) | (tiled ? 1 : 0);
+    pf = pf && dtype_bf16 && D == 128 && RP == 32 && tiled && !abspe && !favor;
+    const int key = (pf ? 64 : 0) | (favor && dtype_bf16 ? 32 : 0) | (dtype_bf16 ? 16 : 0) | (D == 128 ? 8 : 0) |
+                    (RP == 64 ? 4 : 0) | (abspe ? 2 : 0) | (tiled ? 1 : 0);
     if (dev >= 0 && dev < kMaxDev) {
         const int c = cache[dev][key].load(std::memory_order_relaxed);
         if (c > 0) { *slots = c; return hipSuccess; }
     }
     int cus = 0, per = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, summary_kernel(dtype_bf16, D, RP, abspe, tiled, favor), 256,
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, summary_kernel(dtype_bf16, D, RP, abspe, tiled, favor, pf), 256,
                                                           0)) != hipSuccess)
         return e;
     const int n = (cus > 0 ? cus : 1) * (per > 0 ? per : 1);

@@ -463,7 +463,8 @@ static int run_summary(const Dims& d, const RopeGeom& g, const LrGeom& lg, int R
     const bool abspe = lr->mode == SLR_LR_ABS_PE;
     const bool favor = lr->feature_map == SLR_FMAP_FAVOR;
     int slots = 0, chunk, nsplit;
-    SLR_TRY(lr_summary_slots(d.bf16, (int)d.D, RP, abspe, kvt != nullptr, &slots, favor));
+    SLR_TRY(lr_summary_slots(d.bf16, (int)d.D, RP, abspe, kvt != nullptr, &slots, favor,
+                             lr_summary_prefetch(d.bf16, (int)d.D, abspe, kvt != nullptr, lg)));
     summary_split(d, slots, &chunk, &nsplit, max_split);
     const float2* tab = at<float2>(ws, w.tab);
     uint16_t* wkt = d.bf16 ? at<uint16_t>(ws, w.wkt) : nullptr;

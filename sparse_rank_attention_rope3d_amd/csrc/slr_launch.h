@@ -75,9 +75,14 @@ hipError_t launch_lr_prep(const float* W, uint16_t* Wt, int H, int D, int R, int
 hipError_t launch_lr_prep_favor(const float* W, const float* omega, int round_bf16, int H, int D, int R, int RP,
                                 uint16_t* wot_hi, uint16_t* wot_lo, const float* Et, const float* Eh, const float* Ew,
                                 int T, int Hg, int Wg, float* eo, hipStream_t st);
+// Whether the summary runs its prefetching instance for these arguments
+// (bf16, D = 128, tiled V^T, rotary variant, rank <= 32, elu + 1 or SiLU features,
+// rotation table fits its LDS copy).
+bool lr_summary_prefetch(int dtype_bf16, int D, bool abspe, bool tiled, const LrGeom& g);
 // Workgroups of the summary kernel chosen for these arguments that the
 // current device holds at once (CUs x resident workgroups per CU; cached).
-hipError_t lr_summary_slots(int dtype_bf16, int D, int RP, bool abspe, bool tiled, int* slots, bool favor = false);
+hipError_t lr_summary_slots(int dtype_bf16, int D, int RP, bool abspe, bool tiled, int* slots, bool favor = false,
+                            bool pf = false);
 
 // kvt: when non-null (bf16, D = 128, 64-token blocks), V operands come from the [K | V^T] tiles
 // wkot_hi / wkot_lo: FAVOR+ on bf16 layers, (W_k omega^T)^T from launch_lr_prep_favor (else null)
