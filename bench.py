@@ -43,7 +43,7 @@ METRIC = "SLR attn fwd ms/layer + effective TFLOP/s at L=32760/75600/118800, 1 G
 FLASH_TRAFFIC_SOURCES = ["k_flash.hip", "slr_common.h", "slr_launch.h"]
 FLASH_TRAFFIC = {
     "sha256": "c5d34a9a56f37494d5ba0a4dfc70b6437c38dc85473e3a3387bcf7494e636513",
-    "bytes_per_launch": {"wan13b": 8203.9e6 + 201.3e6, "wan14b": 229030.0e6 + 1549.1e6,
+    "bytes_per_launch": {"wan13b": 8203.9e6 + 201.3e6, "wan14b": 218434.0e6 + 1548.4e6,
                          "hunyuan13b": 195059.5e6 + 730.2e6},
 }
 GEN_THREADS = 8   # input generation: numpy fills each slice's arrays without the GIL
@@ -742,6 +742,7 @@ def main() -> int:
         "stages_ms": head["stages_ms"],
         "hbm_stages": head["hbm_stages"],
         "select": head["select"],
+        "layer_roofline": head["layer_roofline"],
         "dense_flash": head.get("dense_flash"),
         "dense_equivalent_TFLOP/s": head["dense_equivalent_TFLOP/s"],
         "backward": backward,
