@@ -65,6 +65,78 @@ def flash_traffic(workload: str):
     return FLASH_TRAFFIC["bytes_per_launch"].get(workload)
 
 
+def live_traffic(workload: str, timeout_s: int = 150):
+    """HBM bytes per launch of the headline's flash kernel, counted in this
+    run: two child processes of this script (`--pmc-probe`: 1 + 2 layer
+    forwards of the workload, then three 1 GiB device copies) under
+    `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE`, each counter scaled
+    by what it reads for the copies in the same process. Returns
+    (bytes, detail) or (None, reason)."""
+    import csv
+    import shutil
+    import subprocess
+    import tempfile
+    prof = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
+    if not os.path.exists(prof):
+        return None, "rocprofv3 not found"
+    tmp = os.environ.get("TMPDIR") or "/tmp"
+    env = dict(os.environ, TMPDIR=tmp)
+    copy_kib = 2 ** 30 / 1024
+    per = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        out = tempfile.mkdtemp(prefix="slr_pmc_", dir=tmp)
+        cmd = ["timeout", "-s", "KILL", str(timeout_s), prof, "--pmc", counter, "--output-format", "csv", "-d", out,
+               "-o", "run", "--", sys.executable, os.path.abspath(__file__), "--pmc-probe", workload]
+        try:
+            r = subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=timeout_s + 30)
+        except (OSError, subprocess.TimeoutExpired) as e:
+            return None, f"{counter} run failed: {e}"
+        path = os.path.join(out, "run_counter_collection.csv")
+        if not os.path.exists(path):
+            return None, f"{counter} run wrote no counters (exit {r.returncode})"
+        flash, copies = [], []
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                name = row["Kernel_Name"]
+                if name.startswith("void slr::k_flash_tiled<") and ", false, false>" in name:
+                    flash.append(float(row["Counter_Value"]))
+                elif name.startswith("__amd_rocclr_copyBuffer"):
+                    copies.append(float(row["Counter_Value"]))
+        shutil.rmtree(out, ignore_errors=True)
+        if not flash or len(copies) < 3:
+            return None, f"{counter}: flash or copy dispatches missing in the counters"
+        cal = copy_kib / (sum(sorted(copies)[-3:]) / 3)   # bytes moved per counted KiB, in KiB
+        per[counter] = {"KiB_per_launch": round(sum(flash) / len(flash), 1), "scale": round(cal, 4),
+                        "bytes": sum(flash) / len(flash) * cal * 1024}
+    total = per["FETCH_SIZE"]["bytes"] + per["WRITE_SIZE"]["bytes"]
+    return total, {"source": "rocprofv3 --pmc child runs of this script (3 launches each; 1 GiB copies calibrate)",
+                   "fetch_bytes": round(per["FETCH_SIZE"]["bytes"]), "write_bytes": round(per["WRITE_SIZE"]["bytes"]),
+                   "counters": per}
+
+
+def pmc_probe(workload: str, torch, B) -> int:
+    """The counted child of live_traffic: 1 + 2 layer forwards of the
+    workload, then three 1 GiB device copies."""
+    from sparse_rank_attention_rope3d_amd import synth
+    cfg = synth.by_name(workload)
+    q, k, v, params = make_device_inputs(cfg, torch)
+    shape, rope, sparse = B.shape_of(cfg), B.rope_of(cfg), B.sparse_of(cfg)
+    lowrank = B.lowrank_of(cfg, params)
+    ws = B.workspace(B.slr_workspace_bytes(B.SLR_OP_ATTENTION, shape, rope, sparse, lowrank), "cuda")
+    out = torch.empty_like(q)
+    for _ in range(3):
+        B.slr_attention_fwd(q, k, v, shape, rope, sparse, lowrank, out=out, ws=ws)
+    torch.cuda.synchronize()
+    del q, k, v, ws, out
+    src = torch.ones(2 ** 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_probe": workload}))
+    return 0
+
+
 def host_cpu() -> dict:
     model = platform.processor() or "unknown"
     try:
@@ -627,6 +699,10 @@ def main() -> int:
                     help="time every keep-fraction x rank point of the Wan2.1-1.3B sweep against the dense "
                          "kernel, append one JSON object per point to JSONL (resuming after the points it "
                          "holds) and exit")
+    ap.add_argument("--no-live-traffic", action="store_true",
+                    help="report the flash kernel's stored HBM byte counts instead of counting them in two "
+                         "rocprofv3 --pmc child runs")
+    ap.add_argument("--pmc-probe", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; used to scale "
                          "the FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -641,6 +717,9 @@ def main() -> int:
     import torch
     from sparse_rank_attention_rope3d_amd import binding as B
     from sparse_rank_attention_rope3d_amd import synth
+
+    if args.pmc_probe:
+        return pmc_probe(args.pmc_probe, torch, B)
 
     if args.calibrate_copy:
         n = args.calibrate_copy * 2 ** 20
@@ -721,6 +800,21 @@ def main() -> int:
                 "sample": f"one (b,h) slice of {cfg.B * cfg.H}: the whole low-rank backward and the sparse backward "
                           f"of {binfo['sampled_blocks']} of {cfg.nblk} query blocks, numpy fp64 with BLAS on one "
                           f"thread, {binfo['measured_s']} s measured, extrapolated linearly to the layer"}
+
+    # the headline flash kernel's HBM bytes, counted now (else the stored counts for this source)
+    key = args_key(cfg)
+    if key is not None and not args.no_live_traffic:
+        print("[bench] HBM counters of the flash kernel (two rocprofv3 --pmc child runs)", file=sys.stderr,
+              flush=True)
+        tb, detail = live_traffic(key)
+        if tb is not None:
+            head["roofline"]["traffic"] = round(tb)
+            head["roofline"]["traffic_detail"] = detail
+        else:
+            head["roofline"]["traffic_detail"] = {"source": "stored counts for this kernel source "
+                                                            f"(live counting unavailable: {detail})"}
+    elif head["roofline"]["traffic"] is not None:
+        head["roofline"]["traffic_detail"] = {"source": "stored counts for this kernel source"}
 
     ms = head["ms_per_layer"]["mean"]
     line = {
