@@ -65,57 +65,92 @@ def flash_traffic(workload: str):
     return FLASH_TRAFFIC["bytes_per_launch"].get(workload)
 
 
-def live_traffic(workload: str, timeout_s: int = 150):
-    """HBM bytes per launch of the headline's flash kernel, counted in this
-    run: two child processes of this script (`--pmc-probe`: 1 + 2 layer
-    forwards of the workload, then three 1 GiB device copies) under
-    `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE`, each counter scaled
-    by what it reads for the copies in the same process. Returns
-    (bytes, detail) or (None, reason)."""
+def _pmc_child(counters, workload: str, timeout_s: int):
+    """Rows of run_counter_collection.csv of this script's `--pmc-probe`
+    child under `rocprofv3 --pmc <counters>`, or an error string."""
     import csv
     import shutil
     import subprocess
     import tempfile
     prof = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
     if not os.path.exists(prof):
-        return None, "rocprofv3 not found"
+        return "rocprofv3 not found"
     tmp = os.environ.get("TMPDIR") or "/tmp"
-    env = dict(os.environ, TMPDIR=tmp)
+    out = tempfile.mkdtemp(prefix="slr_pmc_", dir=tmp)
+    cmd = ["timeout", "-s", "KILL", str(timeout_s), prof, "--pmc", *counters, "--output-format", "csv", "-d", out,
+           "-o", "run", "--", sys.executable, os.path.abspath(__file__), "--pmc-probe", workload]
+    try:
+        r = subprocess.run(cmd, cwd=ROOT, env=dict(os.environ, TMPDIR=tmp), capture_output=True, text=True,
+                           timeout=timeout_s + 30)
+    except (OSError, subprocess.TimeoutExpired) as e:
+        shutil.rmtree(out, ignore_errors=True)
+        return f"{' '.join(counters)} run failed: {e}"
+    path = os.path.join(out, "run_counter_collection.csv")
+    rows = None
+    if os.path.exists(path):
+        with open(path) as f:
+            rows = list(csv.DictReader(f))
+    shutil.rmtree(out, ignore_errors=True)
+    return rows if rows else f"{' '.join(counters)} run wrote no counters (exit {r.returncode})"
+
+
+def _is_flash(name: str) -> bool:
+    # the layer's sparse instance (not the dense one): k_flash_tiled<RP, LR, false, FAV>
+    return name.startswith("void slr::k_flash_tiled<") and ", false, false>" in name
+
+
+def live_counters(workload: str, timeout_s: int = 150):
+    """The headline flash kernel, counted in this run by child processes of
+    this script (`--pmc-probe`: 1 + 2 layer forwards of the workload, then
+    three 1 GiB device copies) under rocprofv3 --pmc:
+      traffic: FETCH_SIZE and WRITE_SIZE (one run each), each scaled by what
+        it reads for the copies in the same process -> HBM bytes per launch;
+      MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x shader cycles),
+        shader cycles = GRBM_COUNT / 8 XCDs (duration x clock).
+    Returns (traffic bytes or None, traffic detail, mfma dict or None)."""
     copy_kib = 2 ** 30 / 1024
     per = {}
+    tb, tdetail = None, None
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-        out = tempfile.mkdtemp(prefix="slr_pmc_", dir=tmp)
-        cmd = ["timeout", "-s", "KILL", str(timeout_s), prof, "--pmc", counter, "--output-format", "csv", "-d", out,
-               "-o", "run", "--", sys.executable, os.path.abspath(__file__), "--pmc-probe", workload]
-        try:
-            r = subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=timeout_s + 30)
-        except (OSError, subprocess.TimeoutExpired) as e:
-            return None, f"{counter} run failed: {e}"
-        path = os.path.join(out, "run_counter_collection.csv")
-        if not os.path.exists(path):
-            return None, f"{counter} run wrote no counters (exit {r.returncode})"
-        flash, copies = [], []
-        with open(path) as f:
-            for row in csv.DictReader(f):
-                name = row["Kernel_Name"]
-                if name.startswith("void slr::k_flash_tiled<") and ", false, false>" in name:
-                    flash.append(float(row["Counter_Value"]))
-                elif name.startswith("__amd_rocclr_copyBuffer"):
-                    copies.append(float(row["Counter_Value"]))
-        shutil.rmtree(out, ignore_errors=True)
+        rows = _pmc_child([counter], workload, timeout_s)
+        if isinstance(rows, str):
+            tdetail = rows
+            break
+        flash = [float(r["Counter_Value"]) for r in rows if _is_flash(r["Kernel_Name"])]
+        copies = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")]
         if not flash or len(copies) < 3:
-            return None, f"{counter}: flash or copy dispatches missing in the counters"
+            tdetail = f"{counter}: flash or copy dispatches missing in the counters"
+            break
         cal = copy_kib / (sum(sorted(copies)[-3:]) / 3)   # bytes moved per counted KiB, in KiB
         per[counter] = {"KiB_per_launch": round(sum(flash) / len(flash), 1), "scale": round(cal, 4),
                         "bytes": sum(flash) / len(flash) * cal * 1024}
-    total = per["FETCH_SIZE"]["bytes"] + per["WRITE_SIZE"]["bytes"]
-    return total, {"source": "rocprofv3 --pmc child runs of this script (3 launches each; 1 GiB copies calibrate)",
+    if len(per) == 2:
+        tb = per["FETCH_SIZE"]["bytes"] + per["WRITE_SIZE"]["bytes"]
+        tdetail = {"source": "rocprofv3 --pmc child runs of this script (3 launches each; 1 GiB copies calibrate)",
                    "fetch_bytes": round(per["FETCH_SIZE"]["bytes"]), "write_bytes": round(per["WRITE_SIZE"]["bytes"]),
                    "counters": per}
+    mfma = None
+    rows = _pmc_child(["SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_COUNT"], workload, timeout_s)
+    if not isinstance(rows, str):
+        disp = {}
+        for r in rows:
+            if _is_flash(r["Kernel_Name"]):
+                d = disp.setdefault(r["Dispatch_Id"], {})
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+                d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+        fr = [(d["SQ_VALU_MFMA_BUSY_CYCLES"] * 8 / (1024 * d["GRBM_COUNT"]), d["GRBM_COUNT"] / 8 / d["ns"] * 1e3)
+              for d in disp.values() if d.get("GRBM_COUNT") and "SQ_VALU_MFMA_BUSY_CYCLES" in d and d["ns"] > 0]
+        if fr:
+            mfma = {"busy_frac": round(sum(f for f, _ in fr) / len(fr), 4),
+                    "clock_MHz": round(sum(c for _, c in fr) / len(fr)),
+                    "what": "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_COUNT / 8): the fraction of SIMD "
+                            "cycles the matrix cores were busy, at the shader clock the kernel ran at "
+                            "(rocprofv3 --pmc child run, 3 launches)"}
+    return tb, tdetail, mfma
 
 
 def pmc_probe(workload: str, torch, B) -> int:
-    """The counted child of live_traffic: 1 + 2 layer forwards of the
+    """The counted child of live_counters: 1 + 2 layer forwards of the
     workload, then three 1 GiB device copies."""
     from sparse_rank_attention_rope3d_amd import synth
     cfg = synth.by_name(workload)
@@ -700,8 +735,8 @@ def main() -> int:
                          "kernel, append one JSON object per point to JSONL (resuming after the points it "
                          "holds) and exit")
     ap.add_argument("--no-live-traffic", action="store_true",
-                    help="report the flash kernel's stored HBM byte counts instead of counting them in two "
-                         "rocprofv3 --pmc child runs")
+                    help="report the flash kernel's stored HBM byte counts and skip its MFMA busy fraction "
+                         "instead of counting both in three rocprofv3 --pmc child runs")
     ap.add_argument("--pmc-probe", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; used to scale "
@@ -804,15 +839,17 @@ def main() -> int:
     # the headline flash kernel's HBM bytes, counted now (else the stored counts for this source)
     key = args_key(cfg)
     if key is not None and not args.no_live_traffic:
-        print("[bench] HBM counters of the flash kernel (two rocprofv3 --pmc child runs)", file=sys.stderr,
-              flush=True)
-        tb, detail = live_traffic(key)
+        print("[bench] HBM and MFMA counters of the flash kernel (three rocprofv3 --pmc child runs)",
+              file=sys.stderr, flush=True)
+        tb, detail, mfma = live_counters(key)
         if tb is not None:
             head["roofline"]["traffic"] = round(tb)
             head["roofline"]["traffic_detail"] = detail
         else:
             head["roofline"]["traffic_detail"] = {"source": "stored counts for this kernel source "
                                                             f"(live counting unavailable: {detail})"}
+        if mfma is not None:
+            head["roofline"]["mfma_busy"] = mfma
     elif head["roofline"]["traffic"] is not None:
         head["roofline"]["traffic_detail"] = {"source": "stored counts for this kernel source"}
 
