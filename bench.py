@@ -110,6 +110,7 @@ def live_counters(workload: str, timeout_s: int = 150):
     Returns (traffic bytes or None, traffic detail, mfma dict or None)."""
     copy_kib = 2 ** 30 / 1024
     per = {}
+    stage_bytes = {}   # HBM-bound stage kernels: counted bytes per launch, read + written
     tb, tdetail = None, None
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         rows = _pmc_child([counter], workload, timeout_s)
@@ -124,6 +125,11 @@ def live_counters(workload: str, timeout_s: int = 150):
         cal = copy_kib / (sum(sorted(copies)[-3:]) / 3)   # bytes moved per counted KiB, in KiB
         per[counter] = {"KiB_per_launch": round(sum(flash) / len(flash), 1), "scale": round(cal, 4),
                         "bytes": sum(flash) / len(flash) * cal * 1024}
+        for stage, prefix in (("rope_pool", "slr::k_rope_pool<"), ("lowrank_summary", "slr::k_lr_summary_bf16")):
+            # template instances are listed as "void slr::...", plain kernels as "slr::..."
+            v = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"].removeprefix("void ").startswith(prefix)]
+            if v:
+                stage_bytes[stage] = stage_bytes.get(stage, 0.0) + sum(v) / len(v) * cal * 1024
     if len(per) == 2:
         tb = per["FETCH_SIZE"]["bytes"] + per["WRITE_SIZE"]["bytes"]
         tdetail = {"source": "rocprofv3 --pmc child runs of this script (3 launches each; 1 GiB copies calibrate)",
@@ -146,7 +152,7 @@ def live_counters(workload: str, timeout_s: int = 150):
                     "what": "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_COUNT / 8): the fraction of SIMD "
                             "cycles the matrix cores were busy, at the shader clock the kernel ran at "
                             "(rocprofv3 --pmc child run, 3 launches)"}
-    return tb, tdetail, mfma
+    return tb, tdetail, mfma, (stage_bytes if len(per) == 2 else None)
 
 
 def pmc_probe(workload: str, torch, B) -> int:
@@ -841,7 +847,7 @@ def main() -> int:
     if key is not None and not args.no_live_traffic:
         print("[bench] HBM and MFMA counters of the flash kernel (three rocprofv3 --pmc child runs)",
               file=sys.stderr, flush=True)
-        tb, detail, mfma = live_counters(key)
+        tb, detail, mfma, stage_bytes = live_counters(key)
         if tb is not None:
             head["roofline"]["traffic"] = round(tb)
             head["roofline"]["traffic_detail"] = detail
@@ -850,6 +856,12 @@ def main() -> int:
                                                             f"(live counting unavailable: {detail})"}
         if mfma is not None:
             head["roofline"]["mfma_busy"] = mfma
+        # counted bytes of the HBM-bound stage kernels (rotate + pool moves more than the survey's
+        # algorithmic bytes by design: the V read and the [K | V^T] tile write)
+        for stage, nb in (stage_bytes or {}).items():
+            rec_key = "rotate_pool_kernel_own_traffic" if stage == "rope_pool" else "lowrank_summary"
+            if isinstance(head["hbm_stages"].get(rec_key), dict):
+                head["hbm_stages"][rec_key]["counted_bytes"] = round(nb)
     elif head["roofline"]["traffic"] is not None:
         head["roofline"]["traffic_detail"] = {"source": "stored counts for this kernel source"}
 
