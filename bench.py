@@ -99,21 +99,16 @@ def _is_flash(name: str) -> bool:
     return name.startswith("void slr::k_flash_tiled<") and ", false, false>" in name
 
 
-def live_counters(workload: str, timeout_s: int = 150):
-    """The headline flash kernel, counted in this run by child processes of
-    this script (`--pmc-probe`: 1 + 2 layer forwards of the workload, then
-    three 1 GiB device copies) under rocprofv3 --pmc:
-      traffic: FETCH_SIZE and WRITE_SIZE (one run each), each scaled by what
-        it reads for the copies in the same process -> HBM bytes per launch;
-      MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x shader cycles),
-        shader cycles = GRBM_COUNT / 8 XCDs (duration x clock).
-    Returns (traffic bytes or None, traffic detail, mfma dict or None)."""
+def counters_from_rows(fetch_rows, write_rows, sq_rows):
+    """Numbers of live_counters from the counter rows of its three child
+    runs (each a list of run_counter_collection.csv rows, or an error
+    string): (traffic bytes or None, traffic detail, mfma dict or None,
+    counted bytes of the HBM-bound stage kernels or None)."""
     copy_kib = 2 ** 30 / 1024
     per = {}
     stage_bytes = {}   # HBM-bound stage kernels: counted bytes per launch, read + written
-    tb, tdetail = None, None
-    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-        rows = _pmc_child([counter], workload, timeout_s)
+    tdetail = None
+    for counter, rows in (("FETCH_SIZE", fetch_rows), ("WRITE_SIZE", write_rows)):
         if isinstance(rows, str):
             tdetail = rows
             break
@@ -130,16 +125,16 @@ def live_counters(workload: str, timeout_s: int = 150):
             v = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"].removeprefix("void ").startswith(prefix)]
             if v:
                 stage_bytes[stage] = stage_bytes.get(stage, 0.0) + sum(v) / len(v) * cal * 1024
+    tb = None
     if len(per) == 2:
         tb = per["FETCH_SIZE"]["bytes"] + per["WRITE_SIZE"]["bytes"]
         tdetail = {"source": "rocprofv3 --pmc child runs of this script (3 launches each; 1 GiB copies calibrate)",
                    "fetch_bytes": round(per["FETCH_SIZE"]["bytes"]), "write_bytes": round(per["WRITE_SIZE"]["bytes"]),
                    "counters": per}
     mfma = None
-    rows = _pmc_child(["SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_COUNT"], workload, timeout_s)
-    if not isinstance(rows, str):
+    if not isinstance(sq_rows, str):
         disp = {}
-        for r in rows:
+        for r in sq_rows:
             if _is_flash(r["Kernel_Name"]):
                 d = disp.setdefault(r["Dispatch_Id"], {})
                 d[r["Counter_Name"]] = float(r["Counter_Value"])
@@ -153,6 +148,20 @@ def live_counters(workload: str, timeout_s: int = 150):
                             "cycles the matrix cores were busy, at the shader clock the kernel ran at "
                             "(rocprofv3 --pmc child run, 3 launches)"}
     return tb, tdetail, mfma, (stage_bytes if len(per) == 2 else None)
+
+
+def live_counters(workload: str, timeout_s: int = 150):
+    """The headline flash kernel, counted in this run by child processes of
+    this script (`--pmc-probe`: 1 + 2 layer forwards of the workload, then
+    three 1 GiB device copies) under rocprofv3 --pmc:
+      traffic: FETCH_SIZE and WRITE_SIZE (one run each), each scaled by what
+        it reads for the copies in the same process -> HBM bytes per launch;
+      MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x shader cycles),
+        shader cycles = GRBM_COUNT / 8 XCDs (duration x clock)."""
+    fetch = _pmc_child(["FETCH_SIZE"], workload, timeout_s)
+    write = _pmc_child(["WRITE_SIZE"], workload, timeout_s) if not isinstance(fetch, str) else fetch
+    sq = _pmc_child(["SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_COUNT"], workload, timeout_s)
+    return counters_from_rows(fetch, write, sq)
 
 
 def pmc_probe(workload: str, torch, B) -> int:
