@@ -150,7 +150,7 @@ def counters_from_rows(fetch_rows, write_rows, sq_rows):
     return tb, tdetail, mfma, (stage_bytes if len(per) == 2 else None)
 
 
-def live_counters(workload: str, timeout_s: int = 150):
+def live_counters(workload: str, timeout_s: int = 90):
     """The headline flash kernel, counted in this run by child processes of
     this script (`--pmc-probe`: 1 + 2 layer forwards of the workload, then
     three 1 GiB device copies) under rocprofv3 --pmc:
@@ -158,9 +158,11 @@ def live_counters(workload: str, timeout_s: int = 150):
         it reads for the copies in the same process -> HBM bytes per launch;
       MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x shader cycles),
         shader cycles = GRBM_COUNT / 8 XCDs (duration x clock)."""
+    # after any failed run the rest are skipped (a profiler that fails once costs one time limit at most)
     fetch = _pmc_child(["FETCH_SIZE"], workload, timeout_s)
     write = _pmc_child(["WRITE_SIZE"], workload, timeout_s) if not isinstance(fetch, str) else fetch
-    sq = _pmc_child(["SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_COUNT"], workload, timeout_s)
+    sq = (_pmc_child(["SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_COUNT"], workload, timeout_s)
+          if not isinstance(write, str) else write)
     return counters_from_rows(fetch, write, sq)
 
 
