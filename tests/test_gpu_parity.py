@@ -76,6 +76,10 @@ SMALL = [
     (64, 64, 16, "abspe", (3, 6, 7), 2, "f32"),
     (128, 64, 32, "rola", (20, 7, 2), 2, "bf16"),     # grid rows of 2 tokens (coordinate steps wrap often)
     (128, 64, 32, "abspe", (9, 4, 3), 2, "bf16"),
+    # the layer forward's summary stages the low-rank rotation rows in LDS when they fit (at most 1920
+    # entries: 8 T + 4 Hg + 4 Wg at rank 32); these two sit just below and just above that limit
+    (128, 64, 32, "rola", (236, 2, 4), 3, "bf16"),    # 1912 entries, 30 blocks, tail 32
+    (128, 64, 32, "rola", (250, 2, 2), 3, "bf16"),    # 2016 entries: the summary without the LDS copy
 ]
 
 
