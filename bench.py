@@ -637,7 +637,8 @@ def measure_forward(cfg, args, torch, B, hip, ach=None, dense_reps=0):
         "ms_per_layer": {"mean": round(ms_mean, 4), "median": round(float(np.median(step_ms)), 4),
                          "min": round(float(step_ms.min()), 4), "max": round(float(step_ms.max()), 4),
                          ("wall_clock_mean" if args.no_scrub else "wall_clock_mean_incl_scrub"): round(wall_ms, 4),
-                         "steps": args.steps, "scrub_between_calls_MB": 0 if args.no_scrub else 512},
+                         "steps": args.steps, "scrub_between_calls_MB": 0 if args.no_scrub else 512,
+                         "each_ms": [round(float(x), 3) for x in step_ms]},
         "effective_TFLOP/s": round(f_total / (ms_mean * 1e-3) / 1e12, 2),
         "effective_TFLOP/s_at_median": round(f_total / (float(np.median(step_ms)) * 1e-3) / 1e12, 2),
         "dense_equivalent_TFLOP/s": round(F["dense"] / (ms_mean * 1e-3) / 1e12, 1),
