@@ -868,7 +868,7 @@ def main() -> int:
                                                             f"(live counting unavailable: {detail})"}
         if mfma is not None:
             head["roofline"]["mfma_busy"] = mfma
-        # counted bytes of the HBM-bound stage kernels (rotate + pool moves more than the survey's
+        # counted bytes of the HBM-bound stage kernels (rotate + pool moves more than the stage's
         # algorithmic bytes by design: the V read and the [K | V^T] tile write)
         for stage, nb in (stage_bytes or {}).items():
             rec_key = "rotate_pool_kernel_own_traffic" if stage == "rope_pool" else "lowrank_summary"
